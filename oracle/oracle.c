@@ -1,0 +1,745 @@
+/*
+ * oracle.c — plain, sequential CPU definition of deterministic packing.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load or call this file.  The GPU library
+ * never links it, includes it or calls it, and shares no code, header, table
+ * or constant generator with it.
+ *
+ * Each function follows one step of the method, in the order the pages give
+ * it, written for a reader to check by eye: one loop per step, no blocking,
+ * no fusion, no parallel reformulation.  Where the pages leave a step open,
+ * the reading taken is stated at the function.  Pages cited:
+ *   [NS]  NeuronSpark-Trainer README — "Concepts" (data lines, mixture,
+ *         strata, hold-out, shuffling) and "Training" (updates, cycles,
+ *         determinism, checkpoints).
+ *   [ZE]  "Zephon: deterministic data loading" (aixai.ru blog) — the 16→8/32/64
+ *         GPU resume section (SHA-256 of every global batch), "three
+ *         decisions" and the TorchTitan integration section (fail-fast
+ *         divisibility checks).
+ *   [LI]  Linnet "Training" docs — "Supervised fine-tuning" (pack to exactly
+ *         T positions, completion-only loss, learned-position counts),
+ *         "Other trainers" (position ids restart at 0 per sequence).
+ *
+ * Parity status of each part (what pins it is in the test suite):
+ *   - doc hash (C1): the pages name no hash function, so the function itself
+ *     is our definition.  Pinned by closed forms of the definition and by the
+ *     published SplitMix64 output for state 0; "parity unpinned" by the pages.
+ *   - Philox4x32-10: Salmon et al., SC'11; pinned against rocRAND's open
+ *     implementation.
+ *   - SHA-256: FIPS 180-4; pinned against Python's hashlib.
+ *   - the sort uses the C library's qsort with a total order as comparator.
+ *
+ * All integers are unsigned unless stated; products that can exceed 64 bits
+ * are taken in unsigned __int128.
+ */
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+typedef unsigned __int128 u128;
+
+#if defined(__BYTE_ORDER__) && __BYTE_ORDER__ != __ORDER_LITTLE_ENDIAN__
+#error "the oracle writes records in host byte order and assumes little-endian"
+#endif
+
+enum {
+    OR_OK = 0,
+    OR_E_INVAL = -2,
+    OR_E_NOMEM = -3,
+    OR_E_EXHAUSTED = -5,
+    OR_E_STATE = -6,
+    OR_E_RANGE = -7,
+};
+
+/* ------------------------------------------------------------------------ */
+/* C1. Per-document content hash.                                           */
+/*                                                                          */
+/* [NS] Concepts: documents are held out by a hash of their text that is     */
+/* the same in every data line.  Reading: the input is token ids, so hash    */
+/* the token sequence and its length; not keyed by seed, cycle or rank.      */
+/*                                                                          */
+/* Definition: position keys k_i = (i+1)·0x9E3779B1 mod 2^32.  Pair tokens   */
+/* (t_{2j}, t_{2j+1}); an odd length gets a virtual t_L = 0 (with its key).  */
+/* S = Σ_j ((t_{2j}+k_{2j}) mod 2^32)·((t_{2j+1}+k_{2j+1}) mod 2^32) mod 2^64 */
+/* (the NH compression of Black et al., CRYPTO'99, with fixed keys), then    */
+/* h = mix64(S xor (L·0x9E3779B97F4A7C15 mod 2^64)), where mix64 is the      */
+/* SplitMix64 output function (Steele, Lea & Flood, OOPSLA 2014).            */
+/* ------------------------------------------------------------------------ */
+
+uint64_t or_mix64(uint64_t z)
+{
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+
+static uint32_t position_key(uint64_t i)
+{
+    return (uint32_t)((i + 1) * 0x9E3779B1ull);
+}
+
+uint64_t or_doc_hash(const uint32_t *t, uint64_t L)
+{
+    uint64_t S = 0;
+    for (uint64_t i = 0; i < L; i += 2) {
+        uint32_t a = t[i] + position_key(i);
+        uint32_t second = (i + 1 < L) ? t[i + 1] : 0u;
+        uint32_t b = second + position_key(i + 1);
+        S += (uint64_t)a * (uint64_t)b;
+    }
+    return or_mix64(S ^ (L * 0x9E3779B97F4A7C15ull));
+}
+
+/* C2. Hold-out decision: held iff floor(h·10000 / 2^64) < bp, i.e. the hash
+ * read as a fraction of 2^64 falls below bp basis points.  [NS] Concepts:
+ * 1 % of a file's documents (5 % for one source) by that hash; each source
+ * applies its own rate to the same unsalted hash. */
+int or_held(uint64_t h, uint32_t bp)
+{
+    uint64_t q = (uint64_t)(((u128)h * 10000u) >> 64);
+    return q < (uint64_t)bp;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Philox4x32-10 (Salmon, Moraes, Dror & Shaw, SC'11): ten rounds of the     */
+/* 4x32 S-box with multipliers 0xD2511F53 (applied to word 0) and            */
+/* 0xCD9E8D57 (word 2), key bumped by the Weyl increments 0x9E3779B9 and     */
+/* 0xBB67AE85 between rounds.                                               */
+/* ------------------------------------------------------------------------ */
+
+void or_philox4x32_10(const uint32_t ctr_in[4], const uint32_t key_in[2], uint32_t out[4])
+{
+    uint32_t c0 = ctr_in[0], c1 = ctr_in[1], c2 = ctr_in[2], c3 = ctr_in[3];
+    uint32_t k0 = key_in[0], k1 = key_in[1];
+    for (int round = 0; round < 10; round++) {
+        if (round > 0) {
+            k0 += 0x9E3779B9u;
+            k1 += 0xBB67AE85u;
+        }
+        uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+        uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+        uint32_t hi0 = (uint32_t)(p0 >> 32), lo0 = (uint32_t)p0;
+        uint32_t hi1 = (uint32_t)(p1 >> 32), lo1 = (uint32_t)p1;
+        uint32_t n0 = hi1 ^ c1 ^ k0;
+        uint32_t n1 = lo1;
+        uint32_t n2 = hi0 ^ c3 ^ k1;
+        uint32_t n3 = lo0;
+        c0 = n0; c1 = n1; c2 = n2; c3 = n3;
+    }
+    out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
+}
+
+/* C3. Shuffle key of document d: the first two words of
+ * Philox4x32-10(counter = (d mod 2^32, d div 2^32, 0x53485546, 0),
+ *               key = (seed mod 2^32, seed div 2^32)),
+ * key64 = x1·2^32 + x0.  Keyed only by the seed and the input document index,
+ * never by rank, world or worker count. */
+uint64_t or_shuffle_key(uint64_t seed, uint64_t d)
+{
+    uint32_t ctr[4] = {(uint32_t)d, (uint32_t)(d >> 32), 0x53485546u, 0u};
+    uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+    uint32_t x[4];
+    or_philox4x32_10(ctr, key, x);
+    return ((uint64_t)x[1] << 32) | x[0];
+}
+
+/* ------------------------------------------------------------------------ */
+/* SHA-256 (FIPS 180-4, section 6.2).                                        */
+/* ------------------------------------------------------------------------ */
+
+static const uint32_t SHA_K[64] = {
+    0x428a2f98, 0x71374491, 0xb5c0fbcf, 0xe9b5dba5, 0x3956c25b, 0x59f111f1, 0x923f82a4, 0xab1c5ed5,
+    0xd807aa98, 0x12835b01, 0x243185be, 0x550c7dc3, 0x72be5d74, 0x80deb1fe, 0x9bdc06a7, 0xc19bf174,
+    0xe49b69c1, 0xefbe4786, 0x0fc19dc6, 0x240ca1cc, 0x2de92c6f, 0x4a7484aa, 0x5cb0a9dc, 0x76f988da,
+    0x983e5152, 0xa831c66d, 0xb00327c8, 0xbf597fc7, 0xc6e00bf3, 0xd5a79147, 0x06ca6351, 0x14292967,
+    0x27b70a85, 0x2e1b2138, 0x4d2c6dfc, 0x53380d13, 0x650a7354, 0x766a0abb, 0x81c2c92e, 0x92722c85,
+    0xa2bfe8a1, 0xa81a664b, 0xc24b8b70, 0xc76c51a3, 0xd192e819, 0xd6990624, 0xf40e3585, 0x106aa070,
+    0x19a4c116, 0x1e376c08, 0x2748774c, 0x34b0bcb5, 0x391c0cb3, 0x4ed8aa4a, 0x5b9cca4f, 0x682e6ff3,
+    0x748f82ee, 0x78a5636f, 0x84c87814, 0x8cc70208, 0x90befffa, 0xa4506ceb, 0xbef9a3f7, 0xc67178f2,
+};
+
+static uint32_t rotr(uint32_t x, int n) { return (x >> n) | (x << (32 - n)); }
+
+static void sha_block(uint32_t H[8], const uint8_t blk[64])
+{
+    uint32_t W[64];
+    for (int t = 0; t < 16; t++)
+        W[t] = ((uint32_t)blk[4 * t] << 24) | ((uint32_t)blk[4 * t + 1] << 16) |
+               ((uint32_t)blk[4 * t + 2] << 8) | (uint32_t)blk[4 * t + 3];
+    for (int t = 16; t < 64; t++) {
+        uint32_t s0 = rotr(W[t - 15], 7) ^ rotr(W[t - 15], 18) ^ (W[t - 15] >> 3);
+        uint32_t s1 = rotr(W[t - 2], 17) ^ rotr(W[t - 2], 19) ^ (W[t - 2] >> 10);
+        W[t] = W[t - 16] + s0 + W[t - 7] + s1;
+    }
+    uint32_t a = H[0], b = H[1], c = H[2], d = H[3], e = H[4], f = H[5], g = H[6], h = H[7];
+    for (int t = 0; t < 64; t++) {
+        uint32_t S1 = rotr(e, 6) ^ rotr(e, 11) ^ rotr(e, 25);
+        uint32_t ch = (e & f) ^ (~e & g);
+        uint32_t T1 = h + S1 + ch + SHA_K[t] + W[t];
+        uint32_t S0 = rotr(a, 2) ^ rotr(a, 13) ^ rotr(a, 22);
+        uint32_t maj = (a & b) ^ (a & c) ^ (b & c);
+        uint32_t T2 = S0 + maj;
+        h = g; g = f; f = e; e = d + T1;
+        d = c; c = b; b = a; a = T1 + T2;
+    }
+    H[0] += a; H[1] += b; H[2] += c; H[3] += d;
+    H[4] += e; H[5] += f; H[6] += g; H[7] += h;
+}
+
+void or_sha256(const uint8_t *msg, uint64_t len, uint8_t out[32])
+{
+    uint32_t H[8] = {0x6a09e667, 0xbb67ae85, 0x3c6ef372, 0xa54ff53a,
+                     0x510e527f, 0x9b05688c, 0x1f83d9ab, 0x5be0cd19};
+    uint64_t full = len / 64;
+    for (uint64_t i = 0; i < full; i++)
+        sha_block(H, msg + 64 * i);
+    uint8_t tail[128];
+    memset(tail, 0, sizeof tail);
+    uint64_t rem = len - 64 * full;
+    memcpy(tail, msg + 64 * full, rem);
+    tail[rem] = 0x80;
+    uint64_t tail_len = (rem + 1 + 8 <= 64) ? 64 : 128;
+    uint64_t bits = len * 8;
+    for (int i = 0; i < 8; i++)
+        tail[tail_len - 1 - i] = (uint8_t)(bits >> (8 * i));
+    for (uint64_t off = 0; off < tail_len; off += 64)
+        sha_block(H, tail + off);
+    for (int i = 0; i < 8; i++) {
+        out[4 * i] = (uint8_t)(H[i] >> 24);
+        out[4 * i + 1] = (uint8_t)(H[i] >> 16);
+        out[4 * i + 2] = (uint8_t)(H[i] >> 8);
+        out[4 * i + 3] = (uint8_t)H[i];
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* C6 (recipe part). Largest-remainder apportionment of the B windows of an  */
+/* update over the sources: n_s = floor(B·w_s/W), the B − Σn_s leftover      */
+/* seats one each to the largest remainders (B·w_s mod W), ties to the lower */
+/* source.  The same n_s holds for every update, so each update holds each   */
+/* source within one window of its share ([NS] Concepts asks for two).       */
+/* ------------------------------------------------------------------------ */
+
+int or_apportion(uint32_t B, uint32_t S, const uint64_t *w, uint32_t *n)
+{
+    u128 W = 0;
+    for (uint32_t s = 0; s < S; s++) W += w[s];
+    if (W == 0 || W >> 64) return OR_E_INVAL;
+    uint64_t *rem = (uint64_t *)malloc(sizeof(uint64_t) * (S ? S : 1));
+    uint8_t *got = (uint8_t *)calloc(S ? S : 1, 1);
+    if (!rem || !got) { free(rem); free(got); return OR_E_NOMEM; }
+    uint64_t given = 0;
+    for (uint32_t s = 0; s < S; s++) {
+        u128 q = (u128)B * w[s];
+        n[s] = (uint32_t)(q / W);
+        rem[s] = (uint64_t)(q % W);
+        given += n[s];
+    }
+    for (uint64_t left = B - given; left > 0; left--) {
+        int best = -1;
+        for (uint32_t s = 0; s < S; s++) {
+            if (got[s]) continue;
+            if (best < 0 || rem[s] > rem[best]) best = (int)s;
+        }
+        got[best] = 1;
+        n[best] += 1;
+    }
+    free(rem);
+    free(got);
+    return OR_OK;
+}
+
+/* C6 (interleave). The update's slots hold items (s, k), k < n_s, ordered by
+ * (2k+1)/(2·n_s) ascending (Sainte-Laguë/Webster order), ties to the lower
+ * source: the sources are spread through the update rather than in blocks. */
+typedef struct { uint32_t s, k, n; } slot_item;
+
+static int cmp_slot(const void *pa, const void *pb)
+{
+    const slot_item *a = (const slot_item *)pa, *b = (const slot_item *)pb;
+    uint64_t lhs = (2ull * a->k + 1) * (uint64_t)b->n;
+    uint64_t rhs = (2ull * b->k + 1) * (uint64_t)a->n;
+    if (lhs != rhs) return lhs < rhs ? -1 : 1;
+    if (a->s != b->s) return a->s < b->s ? -1 : 1;
+    return 0;
+}
+
+int or_slot_table(uint32_t B, uint32_t S, const uint32_t *n, uint32_t *slot_src, uint32_t *slot_k)
+{
+    slot_item *it = (slot_item *)malloc(sizeof(slot_item) * (B ? B : 1));
+    if (!it) return OR_E_NOMEM;
+    uint32_t m = 0;
+    for (uint32_t s = 0; s < S; s++)
+        for (uint32_t k = 0; k < n[s]; k++) {
+            it[m].s = s; it[m].k = k; it[m].n = n[s];
+            m++;
+        }
+    if (m != B) { free(it); return OR_E_INVAL; }
+    qsort(it, m, sizeof(slot_item), cmp_slot);
+    for (uint32_t j = 0; j < m; j++) { slot_src[j] = it[j].s; slot_k[j] = it[j].k; }
+    free(it);
+    return OR_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* The plan of a corpus: C1–C6 over every document.                          */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+    const uint32_t *tokens;
+    uint64_t n_tokens;
+    const uint64_t *offsets;     /* [n_docs+1] */
+    uint64_t n_docs;
+    const uint16_t *source;      /* [n_docs] */
+    const uint16_t *stratum;     /* [n_docs] */
+    const uint32_t *prompt_len;  /* [n_docs] or NULL (all 0) */
+    uint32_t n_sources;
+    const uint32_t *n_strata;    /* [S] */
+    const uint64_t *weight;      /* [S] */
+    const uint32_t *bp;          /* [S] */
+    uint32_t T, B;
+    uint64_t seed;
+    uint32_t pad_token;
+} or_corpus;
+
+typedef struct {
+    or_corpus c;
+    uint64_t *hash;              /* [D] */
+    uint8_t *keep;               /* [D] */
+    uint64_t n_kept;
+    uint32_t *order;             /* [n_kept]: source by source, merged order */
+    uint64_t *src_doc_start;     /* [S+1] */
+    uint64_t n_pieces;
+    uint32_t *pc_doc, *pc_off, *pc_len, *pc_woff;   /* [n_pieces] */
+    uint64_t *src_piece_start;   /* [S+1] */
+    uint64_t n_windows;
+    uint64_t *win_first;         /* [n_windows+1] first piece of each window */
+    uint64_t *src_win_start;     /* [S+1] */
+    uint64_t *win_real;          /* [n_windows] real (non-padding) positions */
+    uint64_t *win_learn;         /* [n_windows] learned positions */
+    uint32_t *n_upd;             /* [S] windows per update */
+    uint32_t *slot_src, *slot_k; /* [B] */
+    uint64_t *kept_docs, *kept_tokens, *held_docs, *held_tokens; /* [S] */
+    uint64_t order_check, hash_check;
+    /* cycle state */
+    int64_t cycle;               /* -1 before the first cycle */
+    uint32_t U;                  /* updates in the current cycle */
+    uint64_t *cyc_start;         /* [S] first window of the current cycle */
+    uint64_t *cyc_next;          /* [S] first window of the next cycle */
+} or_plan;
+
+typedef struct { uint32_t group; uint32_t d; uint64_t key; } sort_item;
+
+static int cmp_sort(const void *pa, const void *pb)
+{
+    const sort_item *a = (const sort_item *)pa, *b = (const sort_item *)pb;
+    if (a->group != b->group) return a->group < b->group ? -1 : 1;
+    if (a->key != b->key) return a->key < b->key ? -1 : 1;
+    if (a->d != b->d) return a->d < b->d ? -1 : 1;
+    return 0;
+}
+
+static uint64_t doc_len(const or_corpus *c, uint64_t d) { return c->offsets[d + 1] - c->offsets[d]; }
+static uint32_t doc_prompt(const or_corpus *c, uint64_t d) { return c->prompt_len ? c->prompt_len[d] : 0u; }
+
+void or_plan_free(or_plan *p);
+
+#define ALLOC(ptr, count) do { (ptr) = calloc((count) ? (count) : 1, sizeof(*(ptr))); if (!(ptr)) goto nomem; } while (0)
+
+or_plan *or_plan_build(const or_corpus *cin, int *err)
+{
+    *err = OR_OK;
+    or_plan *p = (or_plan *)calloc(1, sizeof(or_plan));
+    if (!p) { *err = OR_E_NOMEM; return NULL; }
+    p->c = *cin;
+    const or_corpus *c = &p->c;
+    const uint64_t D = c->n_docs;
+    const uint32_t S = c->n_sources, T = c->T;
+    sort_item *items = NULL;
+    uint32_t *gbase = NULL;
+
+    if (T == 0 || c->B == 0 || S == 0) { *err = OR_E_INVAL; free(p); return NULL; }
+    ALLOC(p->hash, D); ALLOC(p->keep, D);
+    ALLOC(p->src_doc_start, S + 1); ALLOC(p->src_piece_start, S + 1); ALLOC(p->src_win_start, S + 1);
+    ALLOC(p->n_upd, S); ALLOC(p->slot_src, c->B); ALLOC(p->slot_k, c->B);
+    ALLOC(p->kept_docs, S); ALLOC(p->kept_tokens, S); ALLOC(p->held_docs, S); ALLOC(p->held_tokens, S);
+    ALLOC(p->cyc_start, S); ALLOC(p->cyc_next, S);
+    ALLOC(gbase, S + 1);
+
+    /* C1 + C2: hash every document, decide hold-out; a kept document is one
+     * that is not held out and has at least one token. */
+    p->n_kept = 0;
+    for (uint64_t d = 0; d < D; d++) {
+        uint64_t L = doc_len(c, d);
+        uint32_t s = c->source[d];
+        p->hash[d] = or_doc_hash(c->tokens + c->offsets[d], L);
+        int held = or_held(p->hash[d], c->bp[s]);
+        p->keep[d] = (uint8_t)(!held && L > 0);
+        if (held) { p->held_docs[s]++; p->held_tokens[s] += L; }
+        if (p->keep[d]) { p->kept_docs[s]++; p->kept_tokens[s] += L; p->n_kept++; p->hash_check += p->hash[d]; }
+    }
+
+    /* C3: per (source, stratum) group, kept documents ordered by
+     * (shuffle key, input index).  Groups are numbered source-major. */
+    gbase[0] = 0;
+    for (uint32_t s = 0; s < S; s++) gbase[s + 1] = gbase[s] + c->n_strata[s];
+    ALLOC(items, p->n_kept);
+    {
+        uint64_t m = 0;
+        for (uint64_t d = 0; d < D; d++) {
+            if (!p->keep[d]) continue;
+            items[m].group = gbase[c->source[d]] + c->stratum[d];
+            items[m].d = (uint32_t)d;
+            items[m].key = or_shuffle_key(c->seed, d);
+            m++;
+        }
+        qsort(items, p->n_kept, sizeof(sort_item), cmp_sort);
+    }
+
+    /* C4: within each source, interleave its strata by least consumed token
+     * fraction.  Sequential greedy: among strata with documents left, take
+     * the head of the stratum k with the smallest a_k / A_k (a_k = tokens
+     * already taken from k, A_k = kept tokens of k), ties to the smaller k.
+     * [NS] Concepts: every segment holds every stratum at its share of the
+     * source's tokens, cut at document ends; shares in proportion to sizes. */
+    ALLOC(p->order, p->n_kept);
+    {
+        uint64_t out = 0, gi = 0;
+        for (uint32_t s = 0; s < S; s++) {
+            uint32_t K = c->n_strata[s];
+            uint64_t *head = calloc(K ? K : 1, sizeof(uint64_t));
+            uint64_t *end = calloc(K ? K : 1, sizeof(uint64_t));
+            uint64_t *a = calloc(K ? K : 1, sizeof(uint64_t));
+            uint64_t *A = calloc(K ? K : 1, sizeof(uint64_t));
+            if (!head || !end || !a || !A) { free(head); free(end); free(a); free(A); goto nomem; }
+            p->src_doc_start[s] = out;
+            for (uint32_t k = 0; k < K; k++) {
+                head[k] = gi;
+                while (gi < p->n_kept && items[gi].group == gbase[s] + k) {
+                    A[k] += doc_len(c, items[gi].d);
+                    gi++;
+                }
+                end[k] = gi;
+            }
+            for (;;) {
+                int best = -1;
+                for (uint32_t k = 0; k < K; k++) {
+                    if (head[k] == end[k]) continue;
+                    if (best < 0) { best = (int)k; continue; }
+                    /* a_k / A_k < a_best / A_best  <=>  a_k·A_best < a_best·A_k */
+                    u128 lhs = (u128)a[k] * A[best];
+                    u128 rhs = (u128)a[best] * A[k];
+                    if (lhs < rhs) best = (int)k;
+                }
+                if (best < 0) break;
+                uint32_t d = items[head[best]].d;
+                p->order[out++] = d;
+                a[best] += doc_len(c, d);
+                head[best]++;
+            }
+            free(head); free(end); free(a); free(A);
+        }
+        p->src_doc_start[S] = out;
+    }
+    for (uint64_t i = 0; i < p->n_kept; i++)
+        p->order_check += or_mix64((i << 32) ^ (uint64_t)p->order[i]);
+
+    /* C5a: split documents into pieces: a document of L ≤ T tokens is one
+     * piece; a longer one is floor(L/T) pieces of T tokens plus a tail piece
+     * of the rest, if any.  Count first, then fill. */
+    {
+        uint64_t P = 0;
+        for (uint64_t i = 0; i < p->n_kept; i++) {
+            uint64_t L = doc_len(c, p->order[i]);
+            P += (L <= T) ? 1 : (L / T + (L % T != 0));
+        }
+        p->n_pieces = P;
+        ALLOC(p->pc_doc, P); ALLOC(p->pc_off, P); ALLOC(p->pc_len, P); ALLOC(p->pc_woff, P);
+        uint64_t q = 0;
+        for (uint32_t s = 0; s < S; s++) {
+            p->src_piece_start[s] = q;
+            for (uint64_t i = p->src_doc_start[s]; i < p->src_doc_start[s + 1]; i++) {
+                uint32_t d = p->order[i];
+                uint64_t L = doc_len(c, d);
+                for (uint64_t o = 0; o < L; o += T) {
+                    uint64_t len = (L - o < T) ? (L - o) : T;
+                    p->pc_doc[q] = d; p->pc_off[q] = (uint32_t)o; p->pc_len[q] = (uint32_t)len;
+                    q++;
+                }
+            }
+        }
+        p->src_piece_start[S] = q;
+    }
+
+    /* C5b: next-fit, per source, in order: a piece joins the open window if
+     * it still fits in T positions, else the window is closed (its rest is
+     * padding) and the piece opens a new one.  [LI] Supervised fine-tuning:
+     * batches of exactly T positions, padding the rest; [NS] Concepts:
+     * windows cut at document ends. */
+    {
+        uint64_t M = 0;
+        for (uint32_t s = 0; s < S; s++) {
+            uint64_t fill = 0; int open = 0;
+            for (uint64_t q = p->src_piece_start[s]; q < p->src_piece_start[s + 1]; q++) {
+                if (!(open && fill + p->pc_len[q] <= T)) { M++; open = 1; fill = 0; }
+                fill += p->pc_len[q];
+            }
+        }
+        p->n_windows = M;
+        ALLOC(p->win_first, M + 1); ALLOC(p->win_real, M); ALLOC(p->win_learn, M);
+        uint64_t w = 0;
+        for (uint32_t s = 0; s < S; s++) {
+            p->src_win_start[s] = w;
+            uint64_t fill = 0; int open = 0;
+            for (uint64_t q = p->src_piece_start[s]; q < p->src_piece_start[s + 1]; q++) {
+                if (!(open && fill + p->pc_len[q] <= T)) {
+                    p->win_first[w] = q; w++; open = 1; fill = 0;
+                }
+                p->pc_woff[q] = (uint32_t)fill;
+                fill += p->pc_len[q];
+            }
+        }
+        p->src_win_start[S] = w;
+        p->win_first[M] = p->src_piece_start[S];
+    }
+
+    /* Real and learned positions of each window.  A position is learned when
+     * its token lies at or after the document's prompt ([LI] Supervised
+     * fine-tuning: a prompted example learns only its completion). */
+    for (uint64_t w = 0; w < p->n_windows; w++) {
+        uint64_t real = 0, learn = 0;
+        for (uint64_t q = p->win_first[w]; q < p->win_first[w + 1]; q++) {
+            uint64_t o = p->pc_off[q], len = p->pc_len[q];
+            uint64_t pl = doc_prompt(c, p->pc_doc[q]);
+            uint64_t from = o > pl ? o : pl;
+            real += len;
+            if (o + len > from) learn += o + len - from;
+        }
+        p->win_real[w] = real;
+        p->win_learn[w] = learn;
+    }
+
+    /* C6: per-update counts and the slot table. */
+    *err = or_apportion(c->B, S, c->weight, p->n_upd);
+    if (*err) goto fail;
+    *err = or_slot_table(c->B, S, p->n_upd, p->slot_src, p->slot_k);
+    if (*err) goto fail;
+
+    p->cycle = -1;
+    p->U = 0;
+    free(items);
+    free(gbase);
+    return p;
+nomem:
+    *err = OR_E_NOMEM;
+fail:
+    free(items);
+    free(gbase);
+    or_plan_free(p);
+    return NULL;
+}
+
+void or_plan_free(or_plan *p)
+{
+    if (!p) return;
+    free(p->hash); free(p->keep); free(p->order); free(p->src_doc_start);
+    free(p->pc_doc); free(p->pc_off); free(p->pc_len); free(p->pc_woff);
+    free(p->src_piece_start); free(p->win_first); free(p->src_win_start);
+    free(p->win_real); free(p->win_learn); free(p->n_upd); free(p->slot_src); free(p->slot_k);
+    free(p->kept_docs); free(p->kept_tokens); free(p->held_docs); free(p->held_tokens);
+    free(p->cyc_start); free(p->cyc_next);
+    free(p);
+}
+
+/* ------------------------------------------------------------------------ */
+/* C6 (cycles). Cycle c takes U_c·n_s consecutive windows of each source's   */
+/* stream, starting where cycle c−1 ended.  U_c is the configured number of  */
+/* updates, or (when 0) the most that every source with n_s > 0 supports.    */
+/* Running out is an error, not a second pass ([NS] Concepts: max_epochs 1); */
+/* a cycle is a whole number of updates ([NS] Training: updates never span a */
+/* cycle end).                                                               */
+/* ------------------------------------------------------------------------ */
+
+int or_cycle(or_plan *p, uint32_t cyc, uint32_t updates_cfg)
+{
+    const uint32_t S = p->c.n_sources;
+    if ((int64_t)cyc != p->cycle + 1) return OR_E_STATE;
+    uint64_t *start = calloc(S, sizeof(uint64_t));
+    if (!start) return OR_E_NOMEM;
+    for (uint32_t s = 0; s < S; s++) start[s] = (cyc == 0) ? 0 : p->cyc_next[s];
+    uint64_t U;
+    if (updates_cfg > 0) {
+        U = updates_cfg;
+    } else {
+        U = UINT64_MAX;
+        for (uint32_t s = 0; s < S; s++) {
+            if (p->n_upd[s] == 0) continue;
+            uint64_t M = p->src_win_start[s + 1] - p->src_win_start[s];
+            uint64_t u = (M - start[s]) / p->n_upd[s];
+            if (u < U) U = u;
+        }
+    }
+    int ok = (U > 0 && U <= 0xFFFFFFFFull);
+    for (uint32_t s = 0; ok && s < S; s++) {
+        uint64_t M = p->src_win_start[s + 1] - p->src_win_start[s];
+        if ((u128)U * p->n_upd[s] > (u128)(M - start[s])) ok = 0;
+    }
+    if (!ok) { free(start); return OR_E_EXHAUSTED; }   /* cycle state unchanged */
+    p->U = (uint32_t)U;
+    for (uint32_t s = 0; s < S; s++) {
+        p->cyc_start[s] = start[s];
+        p->cyc_next[s] = start[s] + U * p->n_upd[s];
+    }
+    p->cycle = cyc;
+    free(start);
+    return OR_OK;
+}
+
+/* Global window index of slot j of update b of the current cycle. */
+uint64_t or_window_of(const or_plan *p, uint64_t b, uint32_t j)
+{
+    uint32_t s = p->slot_src[j];
+    return p->src_win_start[s] + p->cyc_start[s] + b * p->n_upd[s] + p->slot_k[j];
+}
+
+/* C7. Emission of one window of T positions.  For a position inside piece
+ * (d, o, len) placed at window offset f, with u = position − f: the token
+ * tokens[off[d] + o + u], position id u (0 starts each piece: [LI] Other
+ * trainers), document id d, mask 1 iff o + u ≥ prompt_len(d).  Other
+ * positions are padding: pad token, position 0, document −1, mask 0. */
+void or_emit_window(const or_plan *p, uint64_t gw, uint32_t *tok, int32_t *pos, int32_t *doc, uint8_t *mask)
+{
+    const or_corpus *c = &p->c;
+    for (uint32_t t = 0; t < c->T; t++) { tok[t] = c->pad_token; pos[t] = 0; doc[t] = -1; mask[t] = 0; }
+    for (uint64_t q = p->win_first[gw]; q < p->win_first[gw + 1]; q++) {
+        uint32_t d = p->pc_doc[q], o = p->pc_off[q], len = p->pc_len[q], f = p->pc_woff[q];
+        uint32_t pl = doc_prompt(c, d);
+        for (uint32_t u = 0; u < len; u++) {
+            tok[f + u] = c->tokens[c->offsets[d] + o + u];
+            pos[f + u] = (int32_t)u;
+            doc[f + u] = (int32_t)d;
+            mask[f + u] = (uint8_t)((uint64_t)o + u >= pl);
+        }
+    }
+}
+
+/* C8. Window digest: SHA-256 over tok ‖ pos ‖ doc ‖ mask of the window, the
+ * first three as 4-byte little-endian words, the mask as bytes.  [ZE] the
+ * SHA-256 of every global batch matches byte for byte across GPU counts;
+ * reading: hash per window, then the batch as the SHA-256 of its B window
+ * digests in slot order, so each rank hashes its own slice. */
+void or_window_digest(uint32_t T, const uint32_t *tok, const int32_t *pos, const int32_t *doc,
+                      const uint8_t *mask, uint8_t out[32])
+{
+    uint8_t *rec = (uint8_t *)malloc(13ull * T);
+    memcpy(rec, tok, 4ull * T);
+    memcpy(rec + 4ull * T, pos, 4ull * T);
+    memcpy(rec + 8ull * T, doc, 4ull * T);
+    memcpy(rec + 12ull * T, mask, T);
+    or_sha256(rec, 13ull * T, out);
+    free(rec);
+}
+
+/* One call of the batch entry: updates [step, step+n_steps) of the current
+ * cycle, rank `rank` of `world` owning slots [rank·B/world, (rank+1)·B/world).
+ * Outputs are [n_steps][B/world][T]; learned is the global per-update count;
+ * digests (optional) are [n_steps][B/world][32]. */
+int or_batch(const or_plan *p, uint32_t step, uint32_t n_steps, uint32_t rank, uint32_t world,
+             uint32_t *tok, int32_t *pos, int32_t *doc, uint8_t *mask, int64_t *learned,
+             uint8_t *digests)
+{
+    const uint32_t B = p->c.B, T = p->c.T;
+    if (p->cycle < 0) return OR_E_STATE;
+    if (world == 0 || rank >= world || B % world) return OR_E_INVAL;
+    if ((uint64_t)step + n_steps > p->U) return OR_E_RANGE;
+    const uint32_t per = B / world;
+    for (uint32_t i = 0; i < n_steps; i++) {
+        uint64_t b = (uint64_t)step + i;
+        for (uint32_t jj = 0; jj < per; jj++) {
+            uint32_t j = rank * per + jj;
+            uint64_t gw = or_window_of(p, b, j);
+            uint64_t at = ((uint64_t)i * per + jj) * T;
+            or_emit_window(p, gw, tok + at, pos + at, doc + at, mask + at);
+            if (digests)
+                or_window_digest(T, tok + at, pos + at, doc + at, mask + at,
+                                 digests + ((uint64_t)i * per + jj) * 32);
+        }
+        if (learned) {
+            int64_t sum = 0;
+            for (uint32_t j = 0; j < B; j++) sum += (int64_t)p->win_learn[or_window_of(p, b, j)];
+            learned[i] = sum;
+        }
+    }
+    return OR_OK;
+}
+
+/* Plan digest of the current cycle: SHA-256 over a little-endian byte string
+ * of the recipe, the per-source stream sizes and cycle ranges, and two
+ * order-free sums that change with the document order and content.  A resume
+ * whose digest differs was planned from another recipe or order ([NS]
+ * Training: a resume with another sample order is refused). */
+static void put(uint8_t **w, uint64_t v, int bytes)
+{
+    for (int i = 0; i < bytes; i++) *(*w)++ = (uint8_t)(v >> (8 * i));
+}
+
+int or_plan_digest(const or_plan *p, uint8_t out[32])
+{
+    const or_corpus *c = &p->c;
+    const uint32_t S = c->n_sources;
+    if (p->cycle < 0) return OR_E_STATE;
+    uint64_t bytes = 8 + 4 + 4 + 8 + 4 + 4 + (uint64_t)S * (8 + 4 + 4 + 4 + 8 + 8 + 8) + 4 + 4 + 8ull * S + 8 + 8;
+    uint8_t *buf = (uint8_t *)malloc(bytes), *w = buf;
+    if (!buf) return OR_E_NOMEM;
+    memcpy(w, "DPACKPD1", 8); w += 8;
+    put(&w, c->T, 4); put(&w, c->B, 4); put(&w, c->seed, 8); put(&w, S, 4); put(&w, c->pad_token, 4);
+    for (uint32_t s = 0; s < S; s++) {
+        put(&w, c->weight[s], 8); put(&w, c->bp[s], 4); put(&w, c->n_strata[s], 4);
+        put(&w, p->n_upd[s], 4);
+        put(&w, p->src_win_start[s + 1] - p->src_win_start[s], 8);
+        put(&w, p->kept_docs[s], 8); put(&w, p->kept_tokens[s], 8);
+    }
+    put(&w, (uint64_t)p->cycle, 4); put(&w, p->U, 4);
+    for (uint32_t s = 0; s < S; s++) put(&w, p->cyc_start[s], 8);
+    put(&w, p->order_check, 8); put(&w, p->hash_check, 8);
+    or_sha256(buf, (uint64_t)(w - buf), out);
+    free(buf);
+    return OR_OK;
+}
+
+/* ---- accessors for the Python wrapper (sizes, arrays, cycle state) ---- */
+uint64_t or_plan_sizes(const or_plan *p, uint64_t *n_kept, uint64_t *n_pieces, uint64_t *n_windows)
+{
+    *n_kept = p->n_kept; *n_pieces = p->n_pieces; *n_windows = p->n_windows;
+    return p->c.n_docs;
+}
+
+void or_plan_export(const or_plan *p, uint64_t *hash, uint8_t *keep, uint32_t *order,
+                    uint64_t *src_doc_start, uint32_t *pc_doc, uint32_t *pc_off, uint32_t *pc_len,
+                    uint32_t *pc_woff, uint64_t *src_piece_start, uint64_t *win_first,
+                    uint64_t *src_win_start, uint64_t *win_real, uint64_t *win_learn,
+                    uint32_t *n_upd, uint32_t *slot_src, uint32_t *slot_k, uint64_t *stats /*[4][S]*/,
+                    uint64_t *checks /*[2]*/)
+{
+    const uint64_t D = p->c.n_docs, S = p->c.n_sources, B = p->c.B;
+    memcpy(hash, p->hash, 8 * D); memcpy(keep, p->keep, D);
+    memcpy(order, p->order, 4 * p->n_kept); memcpy(src_doc_start, p->src_doc_start, 8 * (S + 1));
+    memcpy(pc_doc, p->pc_doc, 4 * p->n_pieces); memcpy(pc_off, p->pc_off, 4 * p->n_pieces);
+    memcpy(pc_len, p->pc_len, 4 * p->n_pieces); memcpy(pc_woff, p->pc_woff, 4 * p->n_pieces);
+    memcpy(src_piece_start, p->src_piece_start, 8 * (S + 1));
+    memcpy(win_first, p->win_first, 8 * (p->n_windows + 1));
+    memcpy(src_win_start, p->src_win_start, 8 * (S + 1));
+    memcpy(win_real, p->win_real, 8 * p->n_windows); memcpy(win_learn, p->win_learn, 8 * p->n_windows);
+    memcpy(n_upd, p->n_upd, 4 * S); memcpy(slot_src, p->slot_src, 4 * B); memcpy(slot_k, p->slot_k, 4 * B);
+    memcpy(stats, p->kept_docs, 8 * S); memcpy(stats + S, p->kept_tokens, 8 * S);
+    memcpy(stats + 2 * S, p->held_docs, 8 * S); memcpy(stats + 3 * S, p->held_tokens, 8 * S);
+    checks[0] = p->order_check; checks[1] = p->hash_check;
+}
+
+uint32_t or_cycle_state(const or_plan *p, int64_t *cycle, uint64_t *start /*[S]*/)
+{
+    *cycle = p->cycle;
+    memcpy(start, p->cyc_start, 8 * p->c.n_sources);
+    return p->U;
+}
