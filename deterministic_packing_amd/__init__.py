@@ -1,0 +1,283 @@
+"""Deterministic, elastically reproducible packing on MI355X — Python binding.
+
+A thin ctypes layer over the C ABI in ``include/dpack.h`` (libdpack.so, built
+from ``csrc/`` with hipcc for gfx950).  Functions keep the C names
+(``pack_init``, ``pack_cycle``, ``pack_batch``, ``pack_fingerprint``,
+``pack_inspect``, ``pack_destroy``); :class:`Packer` bundles them with torch
+device tensors.  Only argument marshalling happens here: every step of the
+path runs in the library's HIP kernels.  There is no CPU fallback — when the
+library is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional
+
+import numpy as np
+
+__all__ = [
+    "DpackError", "load_library", "pack_init", "pack_cycle", "pack_batch", "pack_fingerprint",
+    "pack_inspect", "pack_destroy", "pack_strerror", "Packer", "INSPECT", "SYMBOLS",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdpack.so")
+ABI_VERSION = 1
+
+PACK_OK, PACK_E_ABI, PACK_E_INVAL, PACK_E_NOMEM, PACK_E_HIP = 0, -1, -2, -3, -4
+PACK_E_EXHAUSTED, PACK_E_STATE, PACK_E_RANGE = -5, -6, -7
+
+SYMBOLS = ("pack_init", "pack_cycle", "pack_batch", "pack_fingerprint", "pack_inspect",
+           "pack_destroy", "pack_strerror", "pack_last_error")
+
+# what -> (numpy dtype, length key)
+INSPECT = {
+    "hash": (1, np.uint64), "keep": (2, np.uint8), "order": (3, np.uint32),
+    "src_doc_start": (4, np.uint64), "piece_doc": (5, np.uint32), "piece_off": (6, np.uint32),
+    "piece_len": (7, np.uint32), "piece_woff": (8, np.uint32), "src_piece_start": (9, np.uint64),
+    "win_first": (10, np.uint64), "src_win_start": (11, np.uint64), "win_real": (12, np.uint64),
+    "win_learn": (13, np.uint64), "per_update": (14, np.uint32), "slot_src": (15, np.uint32),
+    "slot_k": (16, np.uint32), "counts": (17, np.uint64),
+}
+
+
+class DpackError(RuntimeError):
+    def __init__(self, code: int, call: str, msg: str = ""):
+        super().__init__(f"{call} failed: {code} ({_strerror(code)}){': ' + msg if msg else ''}")
+        self.code = code
+
+
+class PackConfig(C.Structure):
+    _fields_ = [
+        ("abi_version", C.c_uint32), ("flags", C.c_uint32),
+        ("tokens", C.c_void_p), ("n_tokens", C.c_uint64),
+        ("doc_offsets", C.c_void_p), ("n_docs", C.c_uint64),
+        ("doc_source", C.c_void_p), ("doc_stratum", C.c_void_p), ("doc_prompt_len", C.c_void_p),
+        ("n_sources", C.c_uint32), ("n_strata", C.c_void_p), ("share_weight", C.c_void_p),
+        ("holdout_bp", C.c_void_p), ("window_tokens", C.c_uint32), ("global_batch", C.c_uint32),
+        ("updates_per_cycle", C.c_uint32), ("pad_token", C.c_uint32), ("seed", C.c_uint64),
+        ("rank", C.c_uint32), ("world", C.c_uint32), ("stream", C.c_void_p),
+    ]
+
+
+class PackCycleInfo(C.Structure):
+    _fields_ = [
+        ("cycle", C.c_uint32), ("n_updates", C.c_uint32), ("real_tokens", C.c_uint64),
+        ("learned_tokens", C.c_uint64), ("positions", C.c_uint64), ("plan_digest", C.c_uint8 * 32),
+        ("windows_start", C.c_void_p), ("windows_taken", C.c_void_p), ("windows_remaining", C.c_void_p),
+        ("kept_docs", C.c_void_p), ("kept_tokens", C.c_void_p), ("held_docs", C.c_void_p),
+        ("held_tokens", C.c_void_p), ("per_update", C.c_void_p),
+    ]
+
+
+class PackOut(C.Structure):
+    _fields_ = [
+        ("tokens", C.c_void_p), ("pos", C.c_void_p), ("doc", C.c_void_p), ("mask", C.c_void_p),
+        ("learned", C.c_void_p), ("digests", C.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def load_library(path: Optional[str] = None):
+    """Load libdpack.so; raises if it has not been built."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"libdpack.so not found at {p}: build it with "
+                           "`python -m deterministic_packing_amd.build` (hipcc, gfx950)")
+    lib = C.CDLL(p)
+    vp, i32, u32 = C.c_void_p, C.c_int, C.c_uint32
+    lib.pack_init.restype = i32
+    lib.pack_init.argtypes = [C.POINTER(PackConfig), C.POINTER(vp)]
+    lib.pack_cycle.restype = i32
+    lib.pack_cycle.argtypes = [vp, u32, C.POINTER(PackCycleInfo)]
+    lib.pack_batch.restype = i32
+    lib.pack_batch.argtypes = [vp, u32, u32, C.POINTER(PackOut)]
+    lib.pack_fingerprint.restype = i32
+    lib.pack_fingerprint.argtypes = [vp, vp, u32, vp]
+    lib.pack_inspect.restype = i32
+    lib.pack_inspect.argtypes = [vp, u32, vp, C.c_uint64, C.POINTER(C.c_uint64)]
+    lib.pack_destroy.restype = None
+    lib.pack_destroy.argtypes = [vp]
+    lib.pack_strerror.restype = C.c_char_p
+    lib.pack_strerror.argtypes = [i32]
+    lib.pack_last_error.restype = C.c_char_p
+    lib.pack_last_error.argtypes = [vp]
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _strerror(code: int) -> str:
+    try:
+        return load_library().pack_strerror(code).decode()
+    except Exception:
+        return "unknown"
+
+
+def pack_strerror(code: int) -> str:
+    return load_library().pack_strerror(code).decode()
+
+
+def _check(rc: int, call: str, ctx=None):
+    if rc != PACK_OK:
+        msg = load_library().pack_last_error(ctx).decode()
+        raise DpackError(rc, call, msg)
+
+
+def pack_init(cfg: PackConfig) -> int:
+    ctx = C.c_void_p()
+    _check(load_library().pack_init(C.byref(cfg), C.byref(ctx)), "pack_init")
+    return ctx.value
+
+
+def pack_cycle(ctx: int, cycle: int, info: Optional[PackCycleInfo] = None) -> PackCycleInfo:
+    info = info or PackCycleInfo()
+    _check(load_library().pack_cycle(ctx, cycle, C.byref(info)), "pack_cycle", ctx)
+    return info
+
+
+def pack_batch(ctx: int, step: int, n_steps: int, out: PackOut) -> None:
+    _check(load_library().pack_batch(ctx, step, n_steps, C.byref(out)), "pack_batch", ctx)
+
+
+def pack_fingerprint(ctx: int, digests_ptr: int, n_batches: int, out_ptr: int) -> None:
+    _check(load_library().pack_fingerprint(ctx, digests_ptr, n_batches, out_ptr), "pack_fingerprint", ctx)
+
+
+def pack_inspect(ctx: int, what: str) -> np.ndarray:
+    code, dtype = INSPECT[what]
+    lib = load_library()
+    need = C.c_uint64(0)
+    rc = lib.pack_inspect(ctx, code, None, 0, C.byref(need))
+    if rc not in (PACK_OK, PACK_E_RANGE):
+        _check(rc, "pack_inspect", ctx)
+    out = np.zeros(max(1, need.value // np.dtype(dtype).itemsize), dtype=dtype)
+    _check(lib.pack_inspect(ctx, code, out.ctypes.data, out.nbytes, C.byref(need)), "pack_inspect", ctx)
+    return out[: need.value // np.dtype(dtype).itemsize]
+
+
+def pack_destroy(ctx: int) -> None:
+    if ctx:
+        load_library().pack_destroy(ctx)
+
+
+class Packer:
+    """One packing context over a corpus held in torch device tensors.
+
+    ``corpus`` provides numpy arrays (tokens, offsets, source, stratum,
+    prompt_len) and the recipe (n_strata, weight, holdout_bp, T, B,
+    updates_per_cycle, seed, pad_token); they are copied to ``device`` once
+    (or pass ``device_tensors`` to reuse resident ones)."""
+
+    def __init__(self, corpus, rank: int = 0, world: int = 1, device: str = "cuda",
+                 device_tensors: Optional[dict] = None, stream=None):
+        import torch
+
+        self.torch = torch
+        self.corpus = corpus
+        self.rank, self.world = rank, world
+        if device_tensors is None:
+            device_tensors = upload_corpus(corpus, device)
+        self.dev = device_tensors
+        self.stream = stream if stream is not None else torch.cuda.current_stream(device=self.dev["tokens"].device)
+        S = corpus.n_sources
+        self._host = dict(
+            n_strata=np.ascontiguousarray(corpus.n_strata, np.uint32),
+            weight=np.ascontiguousarray(corpus.weight, np.uint64),
+            bp=np.ascontiguousarray(corpus.holdout_bp, np.uint32),
+        )
+        assert self._host["weight"].shape[0] == S
+        d = self.dev
+        self.cfg = PackConfig(
+            ABI_VERSION, 0,
+            d["tokens"].data_ptr() if d["tokens"].numel() else None, int(d["tokens"].numel()),
+            d["offsets"].data_ptr(), int(d["source"].numel()),
+            d["source"].data_ptr(), d["stratum"].data_ptr() if d.get("stratum") is not None else None,
+            d["prompt_len"].data_ptr() if d.get("prompt_len") is not None else None,
+            S, self._host["n_strata"].ctypes.data, self._host["weight"].ctypes.data,
+            self._host["bp"].ctypes.data, corpus.T, corpus.B, corpus.updates_per_cycle,
+            corpus.pad_token, corpus.seed & 0xFFFFFFFFFFFFFFFF, rank, world, self.stream.cuda_stream)
+        self.ctx = pack_init(self.cfg)
+        self.per = corpus.B // world
+
+    def close(self):
+        if getattr(self, "ctx", None):
+            pack_destroy(self.ctx)
+            self.ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def cycle(self, c: int) -> dict:
+        S = self.corpus.n_sources
+        arrs = {k: np.zeros(S, np.uint64) for k in ("windows_start", "windows_taken", "windows_remaining",
+                                                     "kept_docs", "kept_tokens", "held_docs", "held_tokens")}
+        arrs["per_update"] = np.zeros(S, np.uint32)
+        info = PackCycleInfo()
+        for k, v in arrs.items():
+            setattr(info, k, v.ctypes.data)
+        pack_cycle(self.ctx, c, info)
+        out = dict(cycle=info.cycle, n_updates=info.n_updates, real_tokens=info.real_tokens,
+                   learned_tokens=info.learned_tokens, positions=info.positions,
+                   plan_digest=bytes(info.plan_digest))
+        out.update(arrs)
+        return out
+
+    def alloc_out(self, n_steps: int, digests: bool = True, learned: bool = True) -> dict:
+        t = self.torch
+        dev = self.dev["tokens"].device
+        shape = (n_steps, self.per, self.corpus.T)
+        return dict(
+            tokens=t.empty(shape, dtype=t.int32, device=dev),  # uint32 bits
+            pos=t.empty(shape, dtype=t.int32, device=dev),
+            doc=t.empty(shape, dtype=t.int32, device=dev),
+            mask=t.empty(shape, dtype=t.uint8, device=dev),
+            learned=t.empty((n_steps,), dtype=t.int64, device=dev) if learned else None,
+            digests=t.empty((n_steps, self.per, 32), dtype=t.uint8, device=dev) if digests else None,
+        )
+
+    def batch_into(self, step: int, n_steps: int, out: dict) -> dict:
+        po = PackOut(out["tokens"].data_ptr(), out["pos"].data_ptr(), out["doc"].data_ptr(),
+                     out["mask"].data_ptr(),
+                     out["learned"].data_ptr() if out.get("learned") is not None else None,
+                     out["digests"].data_ptr() if out.get("digests") is not None else None)
+        pack_batch(self.ctx, step, n_steps, po)
+        return out
+
+    def batch(self, step: int, n_steps: int = 1, digests: bool = True, learned: bool = True) -> dict:
+        return self.batch_into(step, n_steps, self.alloc_out(n_steps, digests, learned))
+
+    def fingerprint(self, digests) -> "torch.Tensor":
+        """digests: device uint8 [n][B][32] (all ranks' slices in rank order)."""
+        t = self.torch
+        n = int(digests.shape[0])
+        out = t.empty((n, 32), dtype=t.uint8, device=digests.device)
+        pack_fingerprint(self.ctx, digests.data_ptr(), n, out.data_ptr())
+        return out
+
+    def inspect(self, what: str) -> np.ndarray:
+        return pack_inspect(self.ctx, what)
+
+
+def upload_corpus(corpus, device: str = "cuda") -> dict:
+    """Copy a corpus's arrays to the device as torch tensors (uint16/uint32/uint64
+    carried in same-width signed dtypes: only the bits matter to the library)."""
+    import torch
+
+    def t(a, dt):
+        if a is None:
+            return None
+        return torch.from_numpy(np.ascontiguousarray(a).view(dt)).to(device)
+
+    return dict(tokens=t(corpus.tokens, np.int32), offsets=t(corpus.offsets, np.int64),
+                source=t(corpus.source, np.int16), stratum=t(corpus.stratum, np.int16),
+                prompt_len=t(corpus.prompt_len, np.int32))

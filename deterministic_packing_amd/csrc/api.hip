@@ -1,0 +1,622 @@
+// api.hip — the C ABI declared in include/dpack.h: context, workspace, the
+// synchronous plan (pack_init), cycles, and asynchronous batch emission.
+#include <cstring>
+#include <mutex>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "dp_common.h"
+#include "dpack.h"
+
+namespace {
+
+constexpr size_t ALIGN = 256;
+
+// One cached workspace per device: pack_destroy parks its arena here and the
+// next pack_init on that device reuses it when large enough, so a loop of
+// init/destroy does not pay hipMalloc/hipFree each time.
+struct ArenaCache {
+    std::mutex mu;
+    std::vector<std::pair<void*, size_t>> per_device;  // index = device
+};
+ArenaCache& arena_cache() {
+    static ArenaCache c;
+    return c;
+}
+
+void* arena_take(int dev, size_t bytes, size_t* got) {
+    auto& c = arena_cache();
+    std::lock_guard<std::mutex> lk(c.mu);
+    if ((size_t)dev < c.per_device.size()) {
+        auto& e = c.per_device[dev];
+        if (e.first && e.second >= bytes) {
+            void* p = e.first;
+            *got = e.second;
+            e = {nullptr, 0};
+            return p;
+        }
+    }
+    return nullptr;
+}
+
+void arena_give(int dev, void* ptr, size_t bytes) {
+    auto& c = arena_cache();
+    std::lock_guard<std::mutex> lk(c.mu);
+    if ((size_t)dev >= c.per_device.size()) c.per_device.resize(dev + 1, {nullptr, 0});
+    auto& e = c.per_device[dev];
+    if (e.first == nullptr || e.second < bytes) {
+        if (e.first) (void)hipFree(e.first);
+        e = {ptr, bytes};
+    } else {
+        (void)hipFree(ptr);
+    }
+}
+
+thread_local std::string g_init_error;
+
+uint32_t bitlen(uint64_t x) {
+    uint32_t n = 0;
+    while (x) {
+        ++n;
+        x >>= 1;
+    }
+    return n;
+}
+
+struct InvalError {
+    std::string msg;
+};
+
+}  // namespace
+
+struct pack_ctx {
+    pack_config cfg{};
+    std::vector<uint32_t> n_strata, gbase, bp;
+    std::vector<uint64_t> weight;
+    uint64_t W = 0;
+    hipStream_t st = nullptr;
+    int device = 0;
+    dp::Plan p{};
+    char* arena = nullptr;
+    size_t arena_bytes = 0;
+    uint32_t* nstart = nullptr;
+    uint8_t* dig_buf = nullptr;
+    size_t dig_cap = 0;
+    std::vector<uint64_t> src_win_start, stats, checks, src_piece_start;
+    std::vector<uint32_t> n_upd;
+    int64_t cycle = -1;
+    uint32_t U = 0;
+    std::vector<uint64_t> cyc_start, cyc_next;
+    std::string err;
+};
+
+namespace {
+
+struct Carver {
+    char* base;
+    size_t off = 0;
+    template <typename T>
+    T* take(uint64_t count) {
+        off = (off + ALIGN - 1) / ALIGN * ALIGN;
+        T* p = reinterpret_cast<T*>(base ? base + off : nullptr);
+        off += sizeof(T) * (count ? count : 1);
+        return p;
+    }
+};
+
+// Lay out (or size, when base == nullptr) every device array of the plan.
+size_t carve(pack_ctx& c, char* base) {
+    dp::Plan& p = c.p;
+    const uint64_t D = p.n_docs, S = p.S, G = p.G, B = p.B, P = p.cap_pieces;
+    Carver k{base};
+    p.gbase = k.take<uint32_t>(S + 1);
+    p.n_strata = k.take<uint32_t>(S);
+    p.weight = k.take<uint64_t>(S);
+    p.bp = k.take<uint32_t>(S);
+    p.group = k.take<uint32_t>(D);
+    p.hash = k.take<uint64_t>(D);
+    p.keep = k.take<uint8_t>(D);
+    p.kept_pos = k.take<uint32_t>(D + 1);
+    p.stats = k.take<uint64_t>(4 * S);
+    p.err = k.take<uint32_t>(1);
+    p.key[0] = k.take<uint64_t>(D);
+    p.key[1] = k.take<uint64_t>(D);
+    p.val[0] = k.take<uint32_t>(D);
+    p.val[1] = k.take<uint32_t>(D);
+    p.hist = k.take<uint32_t>(dp::sort_hist_words(D));
+    p.group_start = k.take<uint32_t>(G + 1);
+    p.gpre = k.take<uint64_t>(D + 1);
+    p.order = k.take<uint32_t>(D);
+    p.src_doc_start = k.take<uint64_t>(S + 1);
+    p.piece_start = k.take<uint32_t>(D + 1);
+    p.opre = k.take<uint64_t>(D + 1);
+    p.pc_doc = k.take<uint32_t>(P);
+    p.pc_off = k.take<uint32_t>(P);
+    p.pc_len = k.take<uint32_t>(P);
+    p.pc_woff = k.take<uint32_t>(P);
+    p.pc_pre = k.take<uint64_t>(P + 1);
+    p.src_piece_start = k.take<uint64_t>(S + 1);
+    p.jump = k.take<uint32_t>((uint64_t)bitlen(P) * P);
+    p.src_win_start = k.take<uint64_t>(S + 1);
+    p.win_first = k.take<uint32_t>(P + 1);
+    p.win_real = k.take<uint32_t>(P);
+    p.win_learn = k.take<uint32_t>(P);
+    p.n_upd = k.take<uint32_t>(S);
+    p.slot_src = k.take<uint32_t>(B);
+    p.slot_k = k.take<uint32_t>(B);
+    p.cyc_start = k.take<uint64_t>(S);
+    p.checks = k.take<uint64_t>(2);
+    p.cyc_sums = k.take<uint64_t>(2);
+    c.nstart = k.take<uint32_t>(S + 1);
+    c.dig_cap = 128 + 48 * S;
+    c.dig_buf = k.take<uint8_t>(c.dig_cap + 32);
+    return k.off + ALIGN;
+}
+
+template <typename T>
+void d2h(T* dst, const T* src, uint64_t count, hipStream_t st) {
+    if (count) DP_HIP(hipMemcpyAsync(dst, src, sizeof(T) * count, hipMemcpyDeviceToHost, st));
+}
+template <typename T>
+void h2d(T* dst, const T* src, uint64_t count, hipStream_t st) {
+    if (count) DP_HIP(hipMemcpyAsync(dst, src, sizeof(T) * count, hipMemcpyHostToDevice, st));
+}
+
+void check_config(const pack_config* cfg) {
+    auto bad = [](const char* m) { throw InvalError{m}; };
+    if (cfg->flags != 0) bad("flags must be 0");
+    if (cfg->n_docs < 1 || cfg->n_docs >= (1ull << 31)) bad("n_docs must be in [1, 2^31)");
+    if (!cfg->doc_offsets || !cfg->doc_source) bad("doc_offsets and doc_source are required");
+    if (cfg->n_tokens && !cfg->tokens) bad("tokens is NULL with n_tokens > 0");
+    if (cfg->n_sources < 1 || cfg->n_sources > 4096) bad("n_sources must be in [1, 4096]");
+    if (!cfg->share_weight || !cfg->holdout_bp) bad("share_weight and holdout_bp are required");
+    const uint32_t T = cfg->window_tokens, B = cfg->global_batch;
+    if (T < 64 || T > (1u << 20) || T % 64) bad("window_tokens must be a multiple of 64 in [64, 2^20]");
+    if (B < 1 || B > (1u << 20)) bad("global_batch must be in [1, 2^20]");
+    if (cfg->world < 1 || cfg->rank >= cfg->world) bad("need world >= 1 and rank < world");
+    if (B % cfg->world) bad("world must divide global_batch");
+    uint64_t G = 0;
+    for (uint32_t s = 0; s < cfg->n_sources; ++s) {
+        const uint32_t k = cfg->n_strata ? cfg->n_strata[s] : 1u;
+        if (k < 1) bad("every source needs at least one stratum");
+        G += k;
+        if (cfg->holdout_bp[s] > 10000) bad("holdout_bp must be <= 10000");
+    }
+    if (G > 65536) bad("at most 65536 (source, stratum) groups");
+    unsigned __int128 W = 0;
+    for (uint32_t s = 0; s < cfg->n_sources; ++s) W += cfg->share_weight[s];
+    if (W == 0 || (W >> 64) != 0) bad("share weights must sum to [1, 2^64)");
+}
+
+int fail_hip(pack_ctx* c, const dp::HipError& e) {
+    const std::string m = std::string(e.what) + ": " + hipGetErrorString(e.code);
+    if (c) c->err = m;
+    else g_init_error = m;
+    return PACK_E_HIP;
+}
+
+void release(pack_ctx* c) {
+    if (!c) return;
+    if (c->arena) {
+        (void)hipStreamSynchronize(c->st);
+        arena_give(c->device, c->arena, c->arena_bytes);
+    }
+    delete c;
+}
+
+void build_plan(pack_ctx& c) {
+    dp::Plan& p = c.p;
+    hipStream_t st = c.st;
+    // recipe to the device
+    h2d(p.gbase, c.gbase.data(), p.S + 1, st);
+    h2d(p.n_strata, c.n_strata.data(), p.S, st);
+    h2d(p.weight, c.weight.data(), p.S, st);
+    h2d(p.bp, c.bp.data(), p.S, st);
+    dp::launch_zero_u32(p.err, 1, st);
+    dp::launch_zero_u64(p.stats, 4ull * p.S, st);
+
+    // validation first: no kernel reads the corpus through unchecked offsets
+    dp::launch_validate(p, st);
+    uint32_t err = 0;
+    d2h(&err, p.err, 1, st);
+    DP_HIP(hipStreamSynchronize(st));
+    if (err) {
+        std::string m = "invalid corpus:";
+        if (err & 1u) m += " offsets decrease;";
+        if (err & 2u) m += " a document has 2^32 or more tokens;";
+        if (err & 4u) m += " a source id >= n_sources;";
+        if (err & 8u) m += " a stratum id >= n_strata of its source;";
+        if (err & 16u) m += " doc_offsets[n_docs] > n_tokens;";
+        throw InvalError{m};
+    }
+
+    // A1 hash + hold-out, A2 compaction, A3 keys
+    dp::launch_hash(p, st);
+    dp::launch_keep_scan(p, st);
+    uint32_t n_kept = 0;
+    d2h(&n_kept, p.kept_pos + p.n_docs, 1, st);
+    DP_HIP(hipStreamSynchronize(st));
+    p.n_kept = n_kept;
+
+    // A3 sort, A4 merge, A5 piece counts
+    dp::launch_sort(p, st);
+    dp::launch_merge(p, st);
+    dp::launch_piece_count(p, st);
+    uint32_t n_pieces = 0;
+    d2h(&n_pieces, p.piece_start + p.n_kept, 1, st);
+    DP_HIP(hipStreamSynchronize(st));
+    p.n_pieces = n_pieces;
+    if (p.n_pieces > p.cap_pieces) throw InvalError{"internal: piece bound exceeded"};
+    p.levels = bitlen(p.n_pieces) ? bitlen(p.n_pieces) : 1;
+
+    // A5 pieces, next-fit by lifting, windows per source
+    dp::launch_pieces(p, st);
+    dp::launch_lifting(p, st);
+    dp::launch_window_count(p, st);
+    c.src_win_start.assign(p.S + 1, 0);
+    d2h(c.src_win_start.data(), p.src_win_start, p.S + 1, st);
+    DP_HIP(hipStreamSynchronize(st));
+    p.n_windows = c.src_win_start[p.S];
+
+    // window table, A6 mixture, checks
+    dp::launch_zero_u32(p.win_first, 1, st);  // an empty plan still has win_first[0] = 0
+    dp::launch_windows(p, st);
+    dp::launch_mixture_w(p, c.W, c.nstart, st);
+    dp::launch_checks(p, st);
+    c.n_upd.assign(p.S, 0);
+    c.stats.assign(4ull * p.S, 0);
+    c.checks.assign(2, 0);
+    c.src_piece_start.assign(p.S + 1, 0);
+    d2h(c.n_upd.data(), p.n_upd, p.S, st);
+    d2h(c.stats.data(), p.stats, 4ull * p.S, st);
+    d2h(c.checks.data(), p.checks, 2, st);
+    d2h(c.src_piece_start.data(), p.src_piece_start, p.S + 1, st);
+    d2h(&err, p.err, 1, st);
+    DP_HIP(hipStreamSynchronize(st));
+    if (err) throw dp::HipError{hipErrorUnknown, "internal plan consistency check (library bug)"};
+}
+
+void put(std::vector<uint8_t>& b, uint64_t v, int bytes) {
+    for (int i = 0; i < bytes; ++i) b.push_back((uint8_t)(v >> (8 * i)));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pack_strerror(int code) {
+    switch (code) {
+        case PACK_OK: return "ok";
+        case PACK_E_ABI: return "ABI version mismatch";
+        case PACK_E_INVAL: return "invalid argument or corpus";
+        case PACK_E_NOMEM: return "out of memory";
+        case PACK_E_HIP: return "HIP runtime error";
+        case PACK_E_EXHAUSTED: return "a source cannot supply the cycle (data exhausted)";
+        case PACK_E_STATE: return "call out of order";
+        case PACK_E_RANGE: return "step range outside the current cycle";
+        default: return "unknown error";
+    }
+}
+
+const char* pack_last_error(const pack_ctx* ctx) {
+    return ctx ? ctx->err.c_str() : g_init_error.c_str();
+}
+
+int pack_init(const pack_config* cfg, pack_ctx** out) {
+    g_init_error.clear();
+    if (!out) {
+        g_init_error = "out is NULL";
+        return PACK_E_INVAL;
+    }
+    *out = nullptr;
+    if (!cfg) {
+        g_init_error = "cfg is NULL";
+        return PACK_E_INVAL;
+    }
+    if (cfg->abi_version != DPACK_ABI_VERSION) {
+        g_init_error = "abi_version mismatch";
+        return PACK_E_ABI;
+    }
+    pack_ctx* c = nullptr;
+    try {
+        check_config(cfg);
+        c = new (std::nothrow) pack_ctx;
+        if (!c) {
+            g_init_error = "host allocation failed";
+            return PACK_E_NOMEM;
+        }
+        c->cfg = *cfg;
+        c->st = static_cast<hipStream_t>(cfg->stream);
+        const uint32_t S = cfg->n_sources;
+        c->n_strata.resize(S);
+        c->gbase.resize(S + 1);
+        c->bp.assign(cfg->holdout_bp, cfg->holdout_bp + S);
+        c->weight.assign(cfg->share_weight, cfg->share_weight + S);
+        uint32_t G = 0;
+        for (uint32_t s = 0; s < S; ++s) {
+            c->n_strata[s] = cfg->n_strata ? cfg->n_strata[s] : 1u;
+            c->gbase[s] = G;
+            G += c->n_strata[s];
+            c->W += c->weight[s];
+        }
+        c->gbase[S] = G;
+        DP_HIP(hipGetDevice(&c->device));
+
+        dp::Plan& p = c->p;
+        p.tokens = cfg->tokens;
+        p.offsets = cfg->doc_offsets;
+        p.source = cfg->doc_source;
+        p.stratum = cfg->doc_stratum;
+        p.prompt_len = cfg->doc_prompt_len;
+        p.n_tokens = cfg->n_tokens;
+        p.n_docs = cfg->n_docs;
+        p.S = S;
+        p.G = G;
+        p.T = cfg->window_tokens;
+        p.B = cfg->global_batch;
+        p.seed = cfg->seed;
+        p.pad_token = cfg->pad_token;
+        p.cap_pieces = cfg->n_docs + cfg->n_tokens / cfg->window_tokens;
+        if (p.cap_pieces >= 0xFFFFFFFFull) throw InvalError{"too many pieces for 32-bit piece indices"};
+
+        const size_t bytes = carve(*c, nullptr);
+        size_t got = 0;
+        void* mem = arena_take(c->device, bytes, &got);
+        if (!mem) {
+            if (hipMalloc(&mem, bytes) != hipSuccess) {
+                (void)hipGetLastError();
+                g_init_error = "device workspace allocation failed (" + std::to_string(bytes) + " bytes)";
+                delete c;
+                return PACK_E_NOMEM;
+            }
+            got = bytes;
+        }
+        c->arena = static_cast<char*>(mem);
+        c->arena_bytes = got;
+        carve(*c, c->arena);
+        build_plan(*c);
+        c->cyc_start.assign(S, 0);
+        c->cyc_next.assign(S, 0);
+        *out = c;
+        return PACK_OK;
+    } catch (const InvalError& e) {
+        g_init_error = e.msg;
+        release(c);
+        return PACK_E_INVAL;
+    } catch (const dp::HipError& e) {
+        fail_hip(nullptr, e);
+        release(c);
+        return PACK_E_HIP;
+    } catch (const std::bad_alloc&) {
+        g_init_error = "host allocation failed";
+        release(c);
+        return PACK_E_NOMEM;
+    }
+}
+
+int pack_cycle(pack_ctx* c, uint32_t cycle, pack_cycle_info* info) {
+    if (!c) return PACK_E_INVAL;
+    c->err.clear();
+    const uint32_t S = c->p.S;
+    if ((int64_t)cycle != c->cycle + 1) {
+        c->err = "cycles must be planned in order 0, 1, 2, ...";
+        return PACK_E_STATE;
+    }
+    try {
+        std::vector<uint64_t> start(S);
+        for (uint32_t s = 0; s < S; ++s) start[s] = cycle == 0 ? 0 : c->cyc_next[s];
+        uint64_t U = c->cfg.updates_per_cycle;
+        if (U == 0) {
+            U = ~0ull;
+            for (uint32_t s = 0; s < S; ++s) {
+                if (c->n_upd[s] == 0) continue;
+                const uint64_t M = c->src_win_start[s + 1] - c->src_win_start[s];
+                const uint64_t u = (M - start[s]) / c->n_upd[s];
+                if (u < U) U = u;
+            }
+        }
+        bool ok = U > 0 && U <= 0xFFFFFFFFull;
+        for (uint32_t s = 0; ok && s < S; ++s) {
+            const uint64_t M = c->src_win_start[s + 1] - c->src_win_start[s];
+            if ((unsigned __int128)U * c->n_upd[s] > (unsigned __int128)(M - start[s])) ok = false;
+        }
+        if (!ok) {
+            c->err = "a source cannot supply the cycle's windows";
+            return PACK_E_EXHAUSTED;
+        }
+        c->U = (uint32_t)U;
+        c->cyc_start = start;
+        for (uint32_t s = 0; s < S; ++s) c->cyc_next[s] = start[s] + U * c->n_upd[s];
+        c->cycle = cycle;
+        dp::Plan& p = c->p;
+        h2d(p.cyc_start, c->cyc_start.data(), S, c->st);
+        dp::launch_cycle_sums(p, c->U, c->st);
+        uint64_t sums[2] = {0, 0};
+        d2h(sums, p.cyc_sums, 2, c->st);
+
+        // plan digest: SHA-256 of a little-endian description of the recipe,
+        // stream sizes, cycle start and two order-free sums over the plan
+        std::vector<uint8_t> msg;
+        const char magic[8] = {'D', 'P', 'A', 'C', 'K', 'P', 'D', '1'};
+        msg.insert(msg.end(), magic, magic + 8);
+        put(msg, p.T, 4);
+        put(msg, p.B, 4);
+        put(msg, p.seed, 8);
+        put(msg, S, 4);
+        put(msg, p.pad_token, 4);
+        for (uint32_t s = 0; s < S; ++s) {
+            put(msg, c->weight[s], 8);
+            put(msg, c->bp[s], 4);
+            put(msg, c->n_strata[s], 4);
+            put(msg, c->n_upd[s], 4);
+            put(msg, c->src_win_start[s + 1] - c->src_win_start[s], 8);
+            put(msg, c->stats[0 * S + s], 8);
+            put(msg, c->stats[1 * S + s], 8);
+        }
+        put(msg, cycle, 4);
+        put(msg, c->U, 4);
+        for (uint32_t s = 0; s < S; ++s) put(msg, c->cyc_start[s], 8);
+        put(msg, c->checks[0], 8);
+        put(msg, c->checks[1], 8);
+        if (msg.size() > c->dig_cap) throw InvalError{"internal: digest buffer"};
+        h2d(c->dig_buf, msg.data(), msg.size(), c->st);
+        dp::launch_sha_bytes(c->dig_buf, msg.size(), c->dig_buf + c->dig_cap, c->st);
+        uint8_t digest[32];
+        d2h(digest, c->dig_buf + c->dig_cap, 32, c->st);
+        DP_HIP(hipStreamSynchronize(c->st));
+
+        if (info) {
+            info->cycle = cycle;
+            info->n_updates = c->U;
+            info->real_tokens = sums[0];
+            info->learned_tokens = sums[1];
+            info->positions = (uint64_t)c->U * p.B * p.T;
+            std::memcpy(info->plan_digest, digest, 32);
+            for (uint32_t s = 0; s < S; ++s) {
+                const uint64_t M = c->src_win_start[s + 1] - c->src_win_start[s];
+                const uint64_t taken = (uint64_t)c->U * c->n_upd[s];
+                if (info->windows_start) info->windows_start[s] = c->cyc_start[s];
+                if (info->windows_taken) info->windows_taken[s] = taken;
+                if (info->windows_remaining) info->windows_remaining[s] = M - c->cyc_start[s] - taken;
+                if (info->kept_docs) info->kept_docs[s] = c->stats[0 * S + s];
+                if (info->kept_tokens) info->kept_tokens[s] = c->stats[1 * S + s];
+                if (info->held_docs) info->held_docs[s] = c->stats[2 * S + s];
+                if (info->held_tokens) info->held_tokens[s] = c->stats[3 * S + s];
+                if (info->per_update) info->per_update[s] = c->n_upd[s];
+            }
+        }
+        return PACK_OK;
+    } catch (const InvalError& e) {
+        c->err = e.msg;
+        return PACK_E_INVAL;
+    } catch (const dp::HipError& e) {
+        return fail_hip(c, e);
+    } catch (const std::bad_alloc&) {
+        c->err = "host allocation failed";
+        return PACK_E_NOMEM;
+    }
+}
+
+int pack_batch(pack_ctx* c, uint32_t step, uint32_t n_steps, const pack_out* out) {
+    if (!c) return PACK_E_INVAL;
+    c->err.clear();
+    if (c->cycle < 0) {
+        c->err = "no cycle planned";
+        return PACK_E_STATE;
+    }
+    if (n_steps == 0 || (uint64_t)step + n_steps > c->U) {
+        c->err = "step range outside the current cycle";
+        return PACK_E_RANGE;
+    }
+    if (!out || !out->tokens || !out->pos || !out->doc || !out->mask) {
+        c->err = "tokens, pos, doc and mask outputs are required";
+        return PACK_E_INVAL;
+    }
+    if (((uintptr_t)out->tokens | (uintptr_t)out->pos | (uintptr_t)out->doc | (uintptr_t)out->digests) % 16 ||
+        (uintptr_t)out->mask % 4 || (uintptr_t)out->learned % 8) {
+        c->err = "outputs must be 16-byte aligned (mask 4-byte, learned 8-byte)";
+        return PACK_E_INVAL;
+    }
+    try {
+        dp::EmitArgs a{};
+        a.tok = out->tokens;
+        a.pos = out->pos;
+        a.doc = out->doc;
+        a.mask = out->mask;
+        a.learned = out->learned;
+        a.digests = out->digests;
+        a.step = step;
+        a.n_steps = n_steps;
+        a.rank = c->cfg.rank;
+        a.per = c->p.B / c->cfg.world;
+        if ((uint64_t)n_steps * a.per >= (1ull << 31)) {
+            c->err = "too many windows in one call";
+            return PACK_E_RANGE;
+        }
+        dp::launch_emit(c->p, a, c->st);
+        if (a.learned) dp::launch_learned(c->p, a, c->st);
+        if (a.digests) dp::launch_window_sha(c->p, a, c->st);
+        return PACK_OK;
+    } catch (const dp::HipError& e) {
+        return fail_hip(c, e);
+    }
+}
+
+int pack_fingerprint(pack_ctx* c, const uint8_t* digests, uint32_t n_batches, uint8_t* out) {
+    if (!c) return PACK_E_INVAL;
+    c->err.clear();
+    if (!digests || !out) {
+        c->err = "digests and out are required";
+        return PACK_E_INVAL;
+    }
+    if ((uintptr_t)digests % 4) {
+        c->err = "digests must be 4-byte aligned";
+        return PACK_E_INVAL;
+    }
+    if (n_batches == 0) return PACK_OK;
+    try {
+        dp::launch_batch_fp(digests, c->p.B, n_batches, out, c->st);
+        return PACK_OK;
+    } catch (const dp::HipError& e) {
+        return fail_hip(c, e);
+    }
+}
+
+int pack_inspect(const pack_ctx* cc, uint32_t what, void* host_dst, uint64_t capacity, uint64_t* needed) {
+    if (!cc) return PACK_E_INVAL;
+    pack_ctx* c = const_cast<pack_ctx*>(cc);
+    const dp::Plan& p = c->p;
+    const void* src = nullptr;
+    uint64_t count = 0;
+    int width = 0;      // bytes per element on the device
+    int out_width = 0;  // bytes per element in the host copy
+    switch (what) {
+        case PACK_INSPECT_HASH: src = p.hash; count = p.n_docs; width = out_width = 8; break;
+        case PACK_INSPECT_KEEP: src = p.keep; count = p.n_docs; width = out_width = 1; break;
+        case PACK_INSPECT_ORDER: src = p.order; count = p.n_kept; width = out_width = 4; break;
+        case PACK_INSPECT_SRC_DOC_START: src = p.src_doc_start; count = p.S + 1; width = out_width = 8; break;
+        case PACK_INSPECT_PIECE_DOC: src = p.pc_doc; count = p.n_pieces; width = out_width = 4; break;
+        case PACK_INSPECT_PIECE_OFF: src = p.pc_off; count = p.n_pieces; width = out_width = 4; break;
+        case PACK_INSPECT_PIECE_LEN: src = p.pc_len; count = p.n_pieces; width = out_width = 4; break;
+        case PACK_INSPECT_PIECE_WOFF: src = p.pc_woff; count = p.n_pieces; width = out_width = 4; break;
+        case PACK_INSPECT_SRC_PIECE_START: src = p.src_piece_start; count = p.S + 1; width = out_width = 8; break;
+        case PACK_INSPECT_WIN_FIRST: src = p.win_first; count = p.n_windows + 1; width = 4; out_width = 8; break;
+        case PACK_INSPECT_SRC_WIN_START: src = p.src_win_start; count = p.S + 1; width = out_width = 8; break;
+        case PACK_INSPECT_WIN_REAL: src = p.win_real; count = p.n_windows; width = 4; out_width = 8; break;
+        case PACK_INSPECT_WIN_LEARN: src = p.win_learn; count = p.n_windows; width = 4; out_width = 8; break;
+        case PACK_INSPECT_PER_UPDATE: src = p.n_upd; count = p.S; width = out_width = 4; break;
+        case PACK_INSPECT_SLOT_SRC: src = p.slot_src; count = p.B; width = out_width = 4; break;
+        case PACK_INSPECT_SLOT_K: src = p.slot_k; count = p.B; width = out_width = 4; break;
+        case PACK_INSPECT_COUNTS: count = 3; width = out_width = 8; break;
+        default: c->err = "unknown inspect code"; return PACK_E_INVAL;
+    }
+    const uint64_t bytes = count * out_width;
+    if (needed) *needed = bytes;
+    if (capacity < bytes) return PACK_E_RANGE;
+    if (!host_dst && bytes) return PACK_E_INVAL;
+    try {
+        if (what == PACK_INSPECT_COUNTS) {
+            uint64_t v[3] = {p.n_kept, p.n_pieces, p.n_windows};
+            std::memcpy(host_dst, v, sizeof v);
+            return PACK_OK;
+        }
+        if (width == out_width) {
+            if (bytes) DP_HIP(hipMemcpyAsync(host_dst, src, bytes, hipMemcpyDeviceToHost, c->st));
+            DP_HIP(hipStreamSynchronize(c->st));
+        } else {
+            std::vector<uint32_t> tmp(count);
+            if (count) DP_HIP(hipMemcpyAsync(tmp.data(), src, count * 4, hipMemcpyDeviceToHost, c->st));
+            DP_HIP(hipStreamSynchronize(c->st));
+            uint64_t* o = static_cast<uint64_t*>(host_dst);
+            for (uint64_t i = 0; i < count; ++i) o[i] = tmp[i];
+        }
+        return PACK_OK;
+    } catch (const dp::HipError& e) {
+        return fail_hip(c, e);
+    }
+}
+
+void pack_destroy(pack_ctx* c) { release(c); }
+
+}  // extern "C"

@@ -1,0 +1,234 @@
+// dp_common.h — device primitives and the plan workspace shared by the
+// library's HIP translation units.  Written for gfx950 (wave64, CDNA4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dp {
+
+constexpr int WAVE = 64;
+constexpr uint32_t END = 0xFFFFFFFFu;  // "past the end of the source" in jump tables
+// error bit set by a kernel that finds the plan inconsistent (a library bug):
+// the access is skipped and pack_init reports the failure instead
+constexpr uint32_t ERR_INTERNAL = 0x100u;
+
+// ---------------------------------------------------------------- errors
+struct HipError {
+    hipError_t code;
+    const char* what;
+};
+
+#define DP_HIP(call)                                                    \
+    do {                                                                \
+        hipError_t e_ = (call);                                         \
+        if (e_ != hipSuccess) throw ::dp::HipError{e_, #call};          \
+    } while (0)
+
+// ---------------------------------------------------------------- hashing primitives
+
+// SplitMix64 output function (Steele, Lea & Flood, OOPSLA 2014).
+__host__ __device__ inline uint64_t mix64(uint64_t z) {
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+
+constexpr uint32_t PHI32 = 0x9E3779B1u;
+constexpr uint64_t PHI64 = 0x9E3779B97F4A7C15ull;
+
+// Philox4x32-10 (Salmon, Moraes, Dror & Shaw, SC'11).  Returns the first two
+// output words as x1·2^32 + x0, which is all the shuffle key needs.
+__device__ inline uint64_t philox_key64(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                        uint32_t k0, uint32_t k1) {
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        const uint32_t lo0 = 0xD2511F53u * c0, hi0 = __umulhi(0xD2511F53u, c0);
+        const uint32_t lo1 = 0xCD9E8D57u * c2, hi1 = __umulhi(0xCD9E8D57u, c2);
+        const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+        c0 = n0; c1 = lo1; c2 = n2; c3 = lo0;
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+    return ((uint64_t)c1 << 32) | c0;
+}
+
+// 128-bit compare of a·b against c·d for 64-bit operands: -1, 0, +1.
+__host__ __device__ inline int cmp_mul128(uint64_t a, uint64_t b, uint64_t c, uint64_t d) {
+    const unsigned __int128 x = (unsigned __int128)a * b;
+    const unsigned __int128 y = (unsigned __int128)c * d;
+    return x < y ? -1 : (x > y ? 1 : 0);
+}
+
+// ---------------------------------------------------------------- wave helpers
+__device__ inline uint64_t wave_sum_u64(uint64_t v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);
+    return v;
+}
+
+__device__ inline uint32_t lane_id() { return __lane_id(); }
+
+// ---------------------------------------------------------------- plan workspace
+// Device arrays of the plan; sizes in the comments (D docs, K kept, P pieces,
+// M windows, S sources, G groups, L lifting levels).
+struct Plan {
+    // inputs (borrowed)
+    const uint32_t* tokens;
+    const uint64_t* offsets;
+    const uint16_t* source;
+    const uint16_t* stratum;      // may be null
+    const uint32_t* prompt_len;   // may be null
+    uint64_t n_tokens, n_docs;
+    uint32_t S, G, T, B;
+    uint64_t seed;
+    uint32_t pad_token;
+
+    // recipe on device
+    uint32_t* gbase;              // [S+1] first group of each source
+    uint32_t* n_strata;           // [S]
+    uint64_t* weight;             // [S]
+    uint32_t* bp;                 // [S]
+
+    // A1/A2
+    uint32_t* group;              // [D] group of each doc
+    uint64_t* hash;               // [D]
+    uint8_t* keep;                // [D]
+    uint32_t* kept_pos;           // [D+1] exclusive scan of keep
+    uint64_t* stats;              // [4][S] kept docs, kept tokens, held docs, held tokens
+    uint32_t* err;                // [1] validation error flags
+
+    // A3 sort
+    uint64_t* key[2];             // [D]
+    uint32_t* val[2];             // [D]
+    uint32_t* hist;               // [256 * NB + 1]
+    uint32_t sort_buf;            // which buffer holds the sorted result
+
+    // A4
+    uint32_t* group_start;        // [G+1]
+    uint64_t* gpre;               // [D+1] length prefix in sorted order
+    uint32_t* order;              // [D] merged order (kept docs)
+    uint64_t* src_doc_start;      // [S+1]
+
+    // A5
+    uint32_t* piece_start;        // [D+1] exclusive scan of piece counts over the order
+    uint64_t* opre;               // [D+1] length prefix over the order
+    uint32_t* pc_doc;             // [P]
+    uint32_t* pc_off;             // [P]
+    uint32_t* pc_len;             // [P]
+    uint32_t* pc_woff;            // [P]
+    uint64_t* pc_pre;             // [P+1] token prefix over pieces
+    uint64_t* src_piece_start;    // [S+1]
+    uint32_t* jump;               // [L][P] lifting table
+    uint32_t levels;
+    uint64_t* src_win_start;      // [S+1]
+    uint32_t* win_first;          // [M+1]
+    uint32_t* win_real;           // [M]
+    uint32_t* win_learn;          // [M]
+
+    // A6
+    uint32_t* n_upd;              // [S]
+    uint32_t* slot_src;           // [B]
+    uint32_t* slot_k;             // [B]
+    uint64_t* cyc_start;          // [S] first window of the current cycle per source
+    uint64_t* checks;             // [2] order check, hash check
+    uint64_t* cyc_sums;           // [2] real, learned over the current cycle
+
+    // sizes known after the corresponding step (host copies)
+    uint64_t n_kept, n_pieces, n_windows;
+    uint64_t cap_pieces;          // allocation bound for pieces
+};
+
+// ---------------------------------------------------------------- SHA-256 (FIPS 180-4)
+__host__ __device__ inline uint32_t sha_k(int t) {
+    constexpr uint32_t K[64] = {
+        0x428a2f98u, 0x71374491u, 0xb5c0fbcfu, 0xe9b5dba5u, 0x3956c25bu, 0x59f111f1u, 0x923f82a4u, 0xab1c5ed5u,
+        0xd807aa98u, 0x12835b01u, 0x243185beu, 0x550c7dc3u, 0x72be5d74u, 0x80deb1feu, 0x9bdc06a7u, 0xc19bf174u,
+        0xe49b69c1u, 0xefbe4786u, 0x0fc19dc6u, 0x240ca1ccu, 0x2de92c6fu, 0x4a7484aau, 0x5cb0a9dcu, 0x76f988dau,
+        0x983e5152u, 0xa831c66du, 0xb00327c8u, 0xbf597fc7u, 0xc6e00bf3u, 0xd5a79147u, 0x06ca6351u, 0x14292967u,
+        0x27b70a85u, 0x2e1b2138u, 0x4d2c6dfcu, 0x53380d13u, 0x650a7354u, 0x766a0abbu, 0x81c2c92eu, 0x92722c85u,
+        0xa2bfe8a1u, 0xa81a664bu, 0xc24b8b70u, 0xc76c51a3u, 0xd192e819u, 0xd6990624u, 0xf40e3585u, 0x106aa070u,
+        0x19a4c116u, 0x1e376c08u, 0x2748774cu, 0x34b0bcb5u, 0x391c0cb3u, 0x4ed8aa4au, 0x5b9cca4fu, 0x682e6ff3u,
+        0x748f82eeu, 0x78a5636fu, 0x84c87814u, 0x8cc70208u, 0x90befffau, 0xa4506cebu, 0xbef9a3f7u, 0xc67178f2u};
+    return K[t];
+}
+
+__device__ inline uint32_t rotr32(uint32_t x, uint32_t n) { return __builtin_amdgcn_alignbit(x, x, n); }
+
+// One compression of a 64-byte block given as 16 big-endian words.  On
+// gfx950 the rotates map to v_alignbit_b32, the 3-input xors, Ch and Maj to
+// v_bitop3_b32, and the sums to v_add3_u32.
+__device__ inline void sha256_compress(uint32_t H[8], uint32_t W[16]) {
+    uint32_t a = H[0], b = H[1], c = H[2], d = H[3], e = H[4], f = H[5], g = H[6], h = H[7];
+#pragma unroll
+    for (int t = 0; t < 64; ++t) {
+        uint32_t w;
+        if (t < 16) {
+            w = W[t];
+        } else {
+            const uint32_t w15 = W[(t + 1) & 15], w2 = W[(t + 14) & 15];
+            const uint32_t s0 = __builtin_amdgcn_bitop3_b32(rotr32(w15, 7), rotr32(w15, 18), w15 >> 3, 0x96);
+            const uint32_t s1 = __builtin_amdgcn_bitop3_b32(rotr32(w2, 17), rotr32(w2, 19), w2 >> 10, 0x96);
+            w = W[t & 15] + s0 + W[(t + 9) & 15] + s1;
+            W[t & 15] = w;
+        }
+        const uint32_t S1 = __builtin_amdgcn_bitop3_b32(rotr32(e, 6), rotr32(e, 11), rotr32(e, 25), 0x96);
+        const uint32_t ch = __builtin_amdgcn_bitop3_b32(e, f, g, 0xCA);   // (e & f) | (~e & g)
+        const uint32_t T1 = h + S1 + ch + sha_k(t) + w;
+        const uint32_t S0 = __builtin_amdgcn_bitop3_b32(rotr32(a, 2), rotr32(a, 13), rotr32(a, 22), 0x96);
+        const uint32_t mj = __builtin_amdgcn_bitop3_b32(a, b, c, 0xE8);   // majority
+        h = g; g = f; f = e; e = d + T1;
+        d = c; c = b; b = a; a = T1 + S0 + mj;
+    }
+    H[0] += a; H[1] += b; H[2] += c; H[3] += d;
+    H[4] += e; H[5] += f; H[6] += g; H[7] += h;
+}
+
+__device__ inline void sha256_init(uint32_t H[8]) {
+    H[0] = 0x6a09e667u; H[1] = 0xbb67ae85u; H[2] = 0x3c6ef372u; H[3] = 0xa54ff53au;
+    H[4] = 0x510e527fu; H[5] = 0x9b05688cu; H[6] = 0x1f83d9abu; H[7] = 0x5be0cd19u;
+}
+
+__device__ inline uint32_t bswap32(uint32_t x) { return __builtin_bswap32(x); }
+
+// ---------------------------------------------------------------- launchers
+// (each defined in the translation unit that holds the kernels)
+void launch_validate(const Plan& p, hipStream_t st);
+void launch_hash(const Plan& p, hipStream_t st);
+void launch_keep_scan(Plan& p, hipStream_t st);       // kept_pos + compaction into val[0], keys
+void launch_sort(Plan& p, hipStream_t st);            // LSD radix by (group, key64); sets sort_buf
+void launch_merge(Plan& p, hipStream_t st);           // group_start, gpre, order, src_doc_start
+void launch_piece_count(Plan& p, hipStream_t st);     // piece_start, opre
+void launch_pieces(Plan& p, hipStream_t st);          // piece table, pc_pre, src_piece_start
+void launch_lifting(Plan& p, hipStream_t st);         // jump tables
+void launch_window_count(Plan& p, hipStream_t st);    // src_win_start
+void launch_windows(Plan& p, hipStream_t st);         // win_first, pc_woff, win_real, win_learn
+void launch_mixture_w(Plan& p, uint64_t W, uint32_t* nstart, hipStream_t st);  // n_upd, slot table
+void launch_zero_u64(uint64_t* a, uint64_t n, hipStream_t st);
+void launch_zero_u32(uint32_t* a, uint64_t n, hipStream_t st);
+uint64_t sort_hist_words(uint64_t n_docs);
+void launch_checks(Plan& p, hipStream_t st);          // order / hash checks
+void launch_cycle_sums(Plan& p, uint32_t U, hipStream_t st);
+
+struct EmitArgs {
+    uint32_t* tok; int32_t* pos; int32_t* doc; uint8_t* mask;
+    int64_t* learned; uint8_t* digests;
+    uint32_t step, n_steps, rank, per;
+};
+void launch_emit(const Plan& p, const EmitArgs& a, hipStream_t st);
+void launch_learned(const Plan& p, const EmitArgs& a, hipStream_t st);
+void launch_window_sha(const Plan& p, const EmitArgs& a, hipStream_t st);
+void launch_batch_fp(const uint8_t* digests, uint32_t B, uint32_t n_batches, uint8_t* out, hipStream_t st);
+void launch_sha_bytes(const uint8_t* msg, uint64_t len, uint8_t* out, hipStream_t st);
+
+// scans (scan.hip)
+size_t scan_temp_bytes(uint64_t n);
+// exclusive scans writing out[0..n] (out[n] = total)
+void scan_keep_u32(const uint8_t* flags, uint64_t n, uint32_t* out, void* tmp, hipStream_t st);
+void scan_u32(const uint32_t* in, uint64_t n, uint32_t* out, void* tmp, hipStream_t st);
+void scan_len_u64(const uint32_t* ids, const uint64_t* offsets, uint64_t n, uint64_t* out, void* tmp,
+                  hipStream_t st);
+void scan_pieces_u32(const uint32_t* ids, const uint64_t* offsets, uint32_t T, uint64_t n, uint32_t* out,
+                     void* tmp, hipStream_t st);
+
+}  // namespace dp

@@ -1,0 +1,159 @@
+// emit.hip — emission of a rank's slice of updates [step, step+n) and the
+// per-update learned-position counts.
+//
+// Linnet Training, Supervised fine-tuning: rows of exactly T positions with
+// the rest padded, a prompted example learns only its completion, updates
+// weighed by their count of learned positions; Other trainers: a position id
+// 0 starts a new sequence within a row.  For a position t inside piece
+// (d, o, len) placed at window offset f, u = t − f: token tokens[off[d]+o+u],
+// position id u, document id d, mask 1 iff o + u ≥ prompt_len(d).  Padding:
+// pad token, position 0, document −1, mask 0.
+//
+// One workgroup per window.  The window's piece table is staged in LDS; each
+// thread produces 4 consecutive positions and writes them with one 16-byte
+// store per int32 array and one 4-byte store of the mask.
+#include "dp_common.h"
+
+namespace dp {
+namespace {
+
+constexpr int EB = 256;      // threads per window
+constexpr int ECAP = 512;    // pieces staged in LDS
+
+__device__ inline uint64_t window_of(const Plan& p, uint64_t b, uint32_t j) {
+    const uint32_t s = p.slot_src[j];
+    return p.src_win_start[s] + p.cyc_start[s] + b * p.n_upd[s] + p.slot_k[j];
+}
+
+struct PieceView {
+    uint32_t woff, doc, mfrom;
+    uint64_t src;
+};
+
+__global__ __launch_bounds__(EB) void k_emit(Plan p, EmitArgs a) {
+    __shared__ uint32_t s_woff[ECAP];
+    __shared__ uint32_t s_doc[ECAP];
+    __shared__ uint32_t s_mfrom[ECAP];
+    __shared__ uint64_t s_src[ECAP];
+
+    const uint32_t widx = blockIdx.x;                  // window of this launch
+    const uint32_t i = widx / a.per, jj = widx % a.per;
+    const uint64_t gw = window_of(p, (uint64_t)a.step + i, a.rank * a.per + jj);
+    const uint32_t q0 = p.win_first[gw], q1 = p.win_first[gw + 1];
+    const uint32_t np = q1 - q0;
+    const uint32_t real = p.win_real[gw];
+    const bool staged = np <= ECAP;
+
+    auto piece = [&](uint32_t q) -> PieceView {  // q relative to q0
+        const uint32_t g = q0 + q;
+        const uint32_t d = p.pc_doc[g], o = p.pc_off[g], f = p.pc_woff[g];
+        const uint32_t pl = p.prompt_len ? p.prompt_len[d] : 0u;
+        PieceView v;
+        v.woff = f;
+        v.doc = d;
+        v.mfrom = pl > o ? f + (pl - o < 0x7FFFFFFFu ? pl - o : 0x7FFFFFFFu) : f;
+        v.src = p.offsets[d] + o;
+        return v;
+    };
+    if (staged) {
+        for (uint32_t q = threadIdx.x; q < np; q += EB) {
+            const PieceView v = piece(q);
+            s_woff[q] = v.woff;
+            s_doc[q] = v.doc;
+            s_mfrom[q] = v.mfrom;
+            s_src[q] = v.src;
+        }
+        __syncthreads();
+    }
+    // last piece whose window offset is ≤ t
+    auto find = [&](uint32_t t) -> uint32_t {
+        uint32_t lo = 0, hi = np;  // woff[lo] ≤ t < woff[hi]
+        while (hi - lo > 1) {
+            const uint32_t mid = (lo + hi) >> 1;
+            const uint32_t w = staged ? s_woff[mid] : p.pc_woff[q0 + mid];
+            if (w <= t) lo = mid;
+            else hi = mid;
+        }
+        return lo;
+    };
+    auto get = [&](uint32_t q) -> PieceView {
+        if (staged) return PieceView{s_woff[q], s_doc[q], s_mfrom[q], s_src[q]};
+        return piece(q);
+    };
+
+    const uint64_t out0 = (uint64_t)widx * p.T;
+    uint4* tok4 = reinterpret_cast<uint4*>(a.tok + out0);
+    int4* pos4 = reinterpret_cast<int4*>(a.pos + out0);
+    int4* doc4 = reinterpret_cast<int4*>(a.doc + out0);
+    uint32_t* mask4 = reinterpret_cast<uint32_t*>(a.mask + out0);
+    const uint32_t pad = p.pad_token;
+
+    for (uint32_t g = threadIdx.x; g < p.T / 4; g += EB) {
+        const uint32_t t0 = 4 * g;
+        uint32_t tk[4];
+        int32_t ps[4], dc[4];
+        uint32_t mk = 0;
+        if (t0 >= real) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { tk[e] = pad; ps[e] = 0; dc[e] = -1; }
+        } else {
+            uint32_t q = find(t0);
+            PieceView v = get(q);
+            uint32_t next_woff = (q + 1 < np) ? (staged ? s_woff[q + 1] : p.pc_woff[q0 + q + 1]) : real;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t t = t0 + e;
+                if (t >= real) {
+                    tk[e] = pad; ps[e] = 0; dc[e] = -1;
+                    continue;
+                }
+                while (t >= next_woff && q + 1 < np) {  // next piece (contiguous up to `real`)
+                    ++q;
+                    v = get(q);
+                    next_woff = (q + 1 < np) ? (staged ? s_woff[q + 1] : p.pc_woff[q0 + q + 1]) : real;
+                }
+                const uint32_t u = t - v.woff;
+                tk[e] = (v.src + u < p.n_tokens) ? p.tokens[v.src + u] : pad;  // guard: never read past the corpus
+                ps[e] = (int32_t)u;
+                dc[e] = (int32_t)v.doc;
+                mk |= (t >= v.mfrom ? 1u : 0u) << (8 * e);
+            }
+        }
+        tok4[g] = make_uint4(tk[0], tk[1], tk[2], tk[3]);
+        pos4[g] = make_int4(ps[0], ps[1], ps[2], ps[3]);
+        doc4[g] = make_int4(dc[0], dc[1], dc[2], dc[3]);
+        mask4[g] = mk;
+    }
+}
+
+// learned[i] = Σ over all B slots of the window's learned positions (global,
+// the same on every rank).
+__global__ __launch_bounds__(256) void k_learned(Plan p, EmitArgs a) {
+    __shared__ uint64_t part[256 / WAVE];
+    const uint64_t b = (uint64_t)a.step + blockIdx.x;
+    uint64_t s = 0;
+    for (uint32_t j = threadIdx.x; j < p.B; j += blockDim.x) s += p.win_learn[window_of(p, b, j)];
+    s = wave_sum_u64(s);
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x / WAVE] = s;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint64_t t = 0;
+        for (int w = 0; w < 256 / WAVE; ++w) t += part[w];
+        a.learned[blockIdx.x] = (int64_t)t;
+    }
+}
+
+}  // namespace
+
+void launch_emit(const Plan& p, const EmitArgs& a, hipStream_t st) {
+    const uint64_t windows = (uint64_t)a.n_steps * a.per;
+    hipLaunchKernelGGL(k_emit, dim3((uint32_t)windows), dim3(EB), 0, st, p, a);
+    DP_HIP(hipGetLastError());
+}
+
+void launch_learned(const Plan& p, const EmitArgs& a, hipStream_t st) {
+    hipLaunchKernelGGL(k_learned, dim3(a.n_steps), dim3(256), 0, st, p, a);
+    DP_HIP(hipGetLastError());
+}
+
+}  // namespace dp

@@ -1,0 +1,456 @@
+// plan.hip — strata merge, pieces, next-fit window cut, mixture slots and the
+// plan's order checks.  Every step here computes its result as a closed-form
+// rank or a function composition, so the output is independent of thread
+// scheduling and equal to the sequential definition.
+#include "dp_common.h"
+
+namespace dp {
+namespace {
+
+__device__ inline uint32_t upper_bound_u64(const uint64_t* a, uint32_t n, uint64_t x) {
+    // first index i in [0, n) with a[i] > x (n if none)
+    uint32_t lo = 0, hi = n;
+    while (lo < hi) {
+        const uint32_t mid = (lo + hi) >> 1;
+        if (a[mid] <= x) lo = mid + 1;
+        else hi = mid;
+    }
+    return lo;
+}
+
+// ------------------------------------------------------------------ A4 strata merge
+// NeuronSpark-Trainer README, Concepts: every segment of a cycle holds each
+// stratum of a source at its share of the source's tokens, cut at document
+// ends, in proportion to the strata's sizes.  Sequential reading: repeatedly
+// take the head of the stratum with the least consumed fraction a_k/A_k, ties
+// to the lower stratum.  Each stratum's fractions increase strictly, so the
+// result is the merge of the strata by (a/A, k) and the output position of
+// element (k, j) is j plus, for every other stratum k', the number of its
+// elements ordered before it — counted by binary search with exact 128-bit
+// cross-multiplication.
+
+__global__ __launch_bounds__(256) void k_fill_u32(uint32_t* a, uint64_t n, uint32_t v) {
+    const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) a[i] = v;
+}
+
+__global__ __launch_bounds__(256) void k_zero_u64(uint64_t* a, uint64_t n) {
+    const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) a[i] = 0;
+}
+
+__global__ __launch_bounds__(256) void k_group_bounds(const uint32_t* val, const uint32_t* group, uint64_t n,
+                                                      uint32_t* gs) {
+    const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    const uint32_t g = group[val[i]];
+    if (i == 0 || group[val[i - 1]] != g) gs[g] = (uint32_t)i;
+}
+
+// gs[g] = min(gs[g], gs[g+1], …): empty groups start where the next non-empty
+// one does.  One block, chunks from the top.
+__global__ __launch_bounds__(1024) void k_group_suffix_min(uint32_t* gs, uint32_t G) {
+    __shared__ uint32_t lw[16];
+    __shared__ uint32_t carry_s;
+    if (threadIdx.x == 0) carry_s = gs[G];
+    __syncthreads();
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    for (int64_t top = (int64_t)G - 1; top >= 0; top -= 1024) {
+        const int64_t i = top - (int64_t)threadIdx.x;  // thread 0 takes the highest index
+        uint32_t x = i >= 0 ? gs[i] : 0xFFFFFFFFu;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const uint32_t y = __shfl_up(x, o, 64);
+            if (lane >= o) x = min(x, y);
+        }
+        if (lane == 63) lw[wid] = x;
+        __syncthreads();
+        uint32_t before = carry_s;
+        for (int w = 0; w < wid; ++w) before = min(before, lw[w]);
+        x = min(x, before);
+        if (i >= 0) gs[i] = x;
+        __syncthreads();
+        if (threadIdx.x == 1023) carry_s = x;
+        __syncthreads();
+    }
+}
+
+__global__ __launch_bounds__(256) void k_merge(Plan p, const uint32_t* val) {
+    const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= p.n_kept) return;
+    const uint32_t d = val[i];
+    const uint32_t g = p.group[d];
+    const uint32_t s = p.source[d];
+    const uint32_t g0 = p.gbase[s], K = p.n_strata[s], k = g - g0;
+    const uint32_t b0 = p.group_start[g];
+    const uint64_t a = p.gpre[i] - p.gpre[b0];
+    const uint64_t A = p.gpre[p.group_start[g + 1]] - p.gpre[b0];
+    uint64_t rank = i - b0;
+    for (uint32_t k2 = 0; k2 < K; ++k2) {
+        if (k2 == k) continue;
+        const uint32_t c0 = p.group_start[g0 + k2], c1 = p.group_start[g0 + k2 + 1];
+        if (c0 == c1) continue;
+        const uint64_t base = p.gpre[c0];
+        const uint64_t A2 = p.gpre[c1] - base;
+        // elements (k2, j2) before (k, j):  a2/A2 < a/A, or equal and k2 < k
+        uint32_t lo = 0, hi = c1 - c0;
+        while (lo < hi) {
+            const uint32_t mid = (lo + hi) >> 1;
+            const uint64_t a2 = p.gpre[c0 + mid] - base;
+            const int c = cmp_mul128(a2, A, a, A2);
+            const bool before = (k2 < k) ? (c <= 0) : (c < 0);
+            if (before) lo = mid + 1;
+            else hi = mid;
+        }
+        rank += lo;
+    }
+    const uint64_t at = p.group_start[g0] + rank;
+    if (at < p.n_kept) p.order[at] = d;
+    else atomicOr(p.err, ERR_INTERNAL);
+}
+
+__global__ void k_src_doc_start(Plan p) {
+    const uint32_t s = blockIdx.x * blockDim.x + threadIdx.x;
+    if (s <= p.S) p.src_doc_start[s] = p.group_start[p.gbase[s]];
+}
+
+// ------------------------------------------------------------------ A5 pieces
+// A document of L ≤ T tokens is one piece; a longer one is ⌊L/T⌋ pieces of T
+// and a tail piece (config "long-context branch": split at T).
+__global__ __launch_bounds__(256) void k_pieces(Plan p) {
+    const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= p.n_kept) return;
+    const uint32_t d = p.order[i];
+    const uint32_t q0 = p.piece_start[i];
+    if (d >= p.n_docs || p.piece_start[i + 1] > p.n_pieces) {
+        atomicOr(p.err, ERR_INTERNAL);
+        return;
+    }
+    const uint64_t L = p.offsets[d + 1] - p.offsets[d];
+    const uint32_t np = p.piece_start[i + 1] - q0;
+    const uint64_t pre = p.opre[i];
+    for (uint32_t r = 0; r < np; ++r) {
+        const uint64_t o = (uint64_t)r * p.T;
+        const uint32_t q = q0 + r;
+        p.pc_doc[q] = d;
+        p.pc_off[q] = (uint32_t)o;
+        p.pc_len[q] = (uint32_t)((L - o) < p.T ? (L - o) : p.T);
+        p.pc_pre[q] = pre + o;
+    }
+    if (i == p.n_kept - 1) p.pc_pre[p.n_pieces] = p.opre[p.n_kept];
+}
+
+__global__ void k_src_piece_start(Plan p) {
+    const uint32_t s = blockIdx.x * blockDim.x + threadIdx.x;
+    if (s <= p.S) p.src_piece_start[s] = p.piece_start[p.src_doc_start[s]];
+}
+
+// ------------------------------------------------------------------ A5 next-fit
+// Linnet Training, Supervised fine-tuning: windows of exactly T positions,
+// padding the rest; NeuronSpark-Trainer README, Concepts: cut at document
+// ends.  Next-fit in order: a window that starts at piece q holds pieces
+// q … next(q)−1 with next(q) = max{ j : pre[j] − pre[q] ≤ T }.  Window starts
+// of a source are next^w(first piece), w = 0, 1, …; they are found by binary
+// lifting: jump[l][q] = next^(2^l)(q), END once past the source.
+__global__ __launch_bounds__(256) void k_next(Plan p) {
+    const uint64_t q = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (q >= p.n_pieces) return;
+    const uint32_t s = upper_bound_u64(p.src_piece_start, p.S + 1, q) - 1;
+    const uint64_t pe = p.src_piece_start[s + 1];
+    const uint64_t base = p.pc_pre[q];
+    uint64_t lo = q + 1, hi = q + p.T;  // a window holds at most T pieces
+    if (hi > pe) hi = pe;
+    // largest j in [lo, hi] with pre[j] − base ≤ T  (pre[q+1] − base ≤ T always)
+    while (lo < hi) {
+        const uint64_t mid = (lo + hi + 1) >> 1;
+        if (p.pc_pre[mid] - base <= p.T) lo = mid;
+        else hi = mid - 1;
+    }
+    p.jump[q] = (lo == pe) ? END : (uint32_t)lo;
+}
+
+__global__ __launch_bounds__(256) void k_lift(const uint32_t* prev, uint32_t* next, uint64_t n) {
+    const uint64_t q = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (q >= n) return;
+    const uint32_t x = prev[q];
+    next[q] = (x == END) ? END : prev[x];
+}
+
+// windows per source by lifting from its first piece, then their prefix
+__global__ __launch_bounds__(1024) void k_window_count(Plan p) {
+    extern __shared__ uint64_t m[];  // [S]
+    for (uint32_t s = threadIdx.x; s < p.S; s += blockDim.x) {
+        const uint64_t a = p.src_piece_start[s], b = p.src_piece_start[s + 1];
+        uint64_t M = 0;
+        if (a < b) {
+            uint32_t cur = (uint32_t)a;
+            M = 1;
+            for (int l = (int)p.levels - 1; l >= 0; --l) {
+                const uint32_t nx = p.jump[(uint64_t)l * p.cap_pieces + cur];
+                if (nx != END) {
+                    cur = nx;
+                    M += 1ull << l;
+                }
+            }
+        }
+        m[s] = M;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint64_t run = 0;
+        for (uint32_t s = 0; s < p.S; ++s) {
+            p.src_win_start[s] = run;
+            run += m[s];
+        }
+        p.src_win_start[p.S] = run;
+    }
+}
+
+__global__ __launch_bounds__(256) void k_windows(Plan p) {
+    const uint64_t gw = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (gw >= p.n_windows) return;
+    const uint32_t s = upper_bound_u64(p.src_win_start, p.S + 1, gw) - 1;
+    const uint64_t w = gw - p.src_win_start[s];
+    uint32_t cur = (uint32_t)p.src_piece_start[s];
+    for (uint32_t l = 0; l < p.levels; ++l)
+        if ((w >> l) & 1) cur = p.jump[(uint64_t)l * p.cap_pieces + cur];
+    p.win_first[gw] = cur;
+    if (gw == p.n_windows - 1) p.win_first[p.n_windows] = (uint32_t)p.n_pieces;
+}
+
+// offsets of pieces in their window; real and learned positions per window
+// (Linnet Training: a prompted example learns only its completion).
+__global__ __launch_bounds__(256) void k_window_stats(Plan p) {
+    const uint64_t gw = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (gw >= p.n_windows) return;
+    const uint32_t q0 = p.win_first[gw], q1 = p.win_first[gw + 1];
+    if (q0 >= q1 || q1 > p.n_pieces) {
+        atomicOr(p.err, ERR_INTERNAL);
+        p.win_real[gw] = 0;
+        p.win_learn[gw] = 0;
+        return;
+    }
+    uint32_t f = 0, learn = 0;
+    for (uint32_t q = q0; q < q1; ++q) {
+        p.pc_woff[q] = f;
+        const uint32_t o = p.pc_off[q], len = p.pc_len[q];
+        const uint32_t pl = p.prompt_len ? p.prompt_len[p.pc_doc[q]] : 0u;
+        const uint64_t from = o > pl ? o : pl;
+        if ((uint64_t)o + len > from) learn += (uint32_t)((uint64_t)o + len - from);
+        f += len;
+    }
+    p.win_real[gw] = f;
+    p.win_learn[gw] = learn;
+}
+
+// ------------------------------------------------------------------ A6 mixture
+// NeuronSpark-Trainer README, Concepts: every update holds each source within
+// two samples of its recipe share.  Largest remainder: n_s = ⌊B·w_s/W⌋, the
+// leftover seats one each to the largest remainders B·w_s mod W, ties to the
+// lower source; the same n_s for every update (within one of the quota).
+
+// floor and remainder of (hi:lo) / W for hi < W (so the quotient fits 64 bits)
+__device__ inline uint64_t div128(uint64_t hi, uint64_t lo, uint64_t W, uint64_t* rem) {
+    uint64_t q = 0, r = hi;
+    for (int b = 63; b >= 0; --b) {
+        const bool carry = (r >> 63) != 0;
+        r = (r << 1) | ((lo >> b) & 1ull);
+        q <<= 1;
+        if (carry || r >= W) {
+            r -= W;
+            q |= 1ull;
+        }
+    }
+    *rem = r;
+    return q;
+}
+
+__global__ __launch_bounds__(1024) void k_apportion(Plan p, uint64_t W, uint32_t* nstart) {
+    extern __shared__ uint64_t sh[];  // rem[S] then n[S] (32-bit)
+    uint64_t* rem = sh;
+    uint32_t* nn = reinterpret_cast<uint32_t*>(sh + p.S);
+    __shared__ uint64_t given_s;
+    if (threadIdx.x == 0) given_s = 0;
+    __syncthreads();
+    for (uint32_t s = threadIdx.x; s < p.S; s += blockDim.x) {
+        const uint64_t w = p.weight[s];
+        const uint64_t hi = __umul64hi((uint64_t)p.B, w), lo = (uint64_t)p.B * w;
+        uint64_t r;
+        const uint64_t n = div128(hi, lo, W, &r);  // hi < W since B·w < B·W
+        rem[s] = r;
+        nn[s] = (uint32_t)n;
+        atomicAdd((unsigned long long*)&given_s, (unsigned long long)n);
+    }
+    __syncthreads();
+    const uint64_t left = (uint64_t)p.B - given_s;
+    for (uint32_t s = threadIdx.x; s < p.S; s += blockDim.x) {
+        uint64_t rank = 0;
+        for (uint32_t t = 0; t < p.S; ++t)
+            rank += (rem[t] > rem[s] || (rem[t] == rem[s] && t < s)) ? 1 : 0;
+        p.n_upd[s] = (uint32_t)(nn[s] + (rank < left ? 1 : 0));
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t run = 0;
+        for (uint32_t s = 0; s < p.S; ++s) {
+            nstart[s] = run;
+            run += p.n_upd[s];
+        }
+        nstart[p.S] = run;
+    }
+}
+
+// Slot order inside an update: items (s, k), k < n_s, by (2k+1)/(2n_s), ties
+// to the lower source (Sainte-Laguë order), so the sources are spread over
+// the update.  Position of (s, k) = number of items ordered before it,
+// counted in closed form per source.
+__global__ __launch_bounds__(256) void k_slots(Plan p, const uint32_t* nstart) {
+    const uint32_t u = blockIdx.x * blockDim.x + threadIdx.x;
+    if (u >= p.B) return;
+    uint32_t lo = 0, hi = p.S;  // source s with nstart[s] ≤ u < nstart[s+1]
+    while (hi - lo > 1) {
+        const uint32_t mid = (lo + hi) >> 1;
+        if (nstart[mid] <= u) lo = mid;
+        else hi = mid;
+    }
+    uint32_t s = lo;
+    while (nstart[s + 1] <= u) ++s;  // skip sources with n = 0
+    const uint32_t k = u - nstart[s];
+    const uint64_t ns = p.n_upd[s];
+    uint64_t pos = k;
+    for (uint32_t s2 = 0; s2 < p.S; ++s2) {
+        const uint64_t n2 = p.n_upd[s2];
+        if (s2 == s || n2 == 0) continue;
+        const uint64_t X = (2ull * k + 1) * n2;   // compare (2k'+1)·n_s against X
+        const uint64_t F = (s2 < s) ? X / ns : (X - 1) / ns;  // largest admissible odd bound
+        uint64_t c = (F + 1) / 2;
+        if (c > n2) c = n2;
+        pos += c;
+    }
+    if (pos < p.B) {
+        p.slot_src[pos] = s;
+        p.slot_k[pos] = k;
+    } else {
+        atomicOr(p.err, ERR_INTERNAL);
+    }
+}
+
+// ------------------------------------------------------------------ checks
+__global__ __launch_bounds__(256) void k_checks(Plan p) {
+    const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    uint64_t oc = 0, hc = 0;
+    if (i < p.n_kept) oc = mix64((i << 32) ^ (uint64_t)p.order[i]);
+    if (i < p.n_docs && p.keep[i]) hc = p.hash[i];
+    oc = wave_sum_u64(oc);
+    hc = wave_sum_u64(hc);
+    if ((threadIdx.x & 63) == 0) {
+        if (oc) atomicAdd((unsigned long long*)&p.checks[0], (unsigned long long)oc);
+        if (hc) atomicAdd((unsigned long long*)&p.checks[1], (unsigned long long)hc);
+    }
+}
+
+__device__ inline uint64_t window_of(const Plan& p, uint64_t b, uint32_t j) {
+    const uint32_t s = p.slot_src[j];
+    return p.src_win_start[s] + p.cyc_start[s] + b * p.n_upd[s] + p.slot_k[j];
+}
+
+__global__ __launch_bounds__(256) void k_cycle_sums(Plan p, uint64_t total) {
+    const uint64_t idx = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    uint64_t real = 0, learn = 0;
+    if (idx < total) {
+        const uint64_t gw = window_of(p, idx / p.B, (uint32_t)(idx % p.B));
+        real = p.win_real[gw];
+        learn = p.win_learn[gw];
+    }
+    real = wave_sum_u64(real);
+    learn = wave_sum_u64(learn);
+    if ((threadIdx.x & 63) == 0) {
+        if (real) atomicAdd((unsigned long long*)&p.cyc_sums[0], (unsigned long long)real);
+        if (learn) atomicAdd((unsigned long long*)&p.cyc_sums[1], (unsigned long long)learn);
+    }
+}
+
+inline uint32_t blocks_for(uint64_t n, uint32_t b = 256) { return (uint32_t)((n + b - 1) / b); }
+
+}  // namespace
+
+void launch_merge(Plan& p, hipStream_t st) {
+    const uint32_t* val = p.val[p.sort_buf];
+    hipLaunchKernelGGL(k_fill_u32, dim3(blocks_for(p.G + 1)), dim3(256), 0, st, p.group_start, (uint64_t)p.G + 1,
+                       (uint32_t)p.n_kept);
+    if (p.n_kept)
+        hipLaunchKernelGGL(k_group_bounds, dim3(blocks_for(p.n_kept)), dim3(256), 0, st, val, p.group, p.n_kept,
+                           p.group_start);
+    hipLaunchKernelGGL(k_group_suffix_min, dim3(1), dim3(1024), 0, st, p.group_start, p.G);
+    scan_len_u64(val, p.offsets, p.n_kept, p.gpre, p.hist, st);
+    // holes (which a correct merge never leaves) would read document 0
+    if (p.n_kept) hipLaunchKernelGGL(k_fill_u32, dim3(blocks_for(p.n_kept)), dim3(256), 0, st, p.order, p.n_kept, 0u);
+    if (p.n_kept) hipLaunchKernelGGL(k_merge, dim3(blocks_for(p.n_kept)), dim3(256), 0, st, p, val);
+    hipLaunchKernelGGL(k_src_doc_start, dim3(blocks_for(p.S + 1)), dim3(256), 0, st, p);
+    DP_HIP(hipGetLastError());
+}
+
+void launch_piece_count(Plan& p, hipStream_t st) {
+    scan_pieces_u32(p.order, p.offsets, p.T, p.n_kept, p.piece_start, p.hist, st);
+    scan_len_u64(p.order, p.offsets, p.n_kept, p.opre, p.hist, st);
+}
+
+void launch_pieces(Plan& p, hipStream_t st) {
+    if (p.n_kept) hipLaunchKernelGGL(k_pieces, dim3(blocks_for(p.n_kept)), dim3(256), 0, st, p);
+    hipLaunchKernelGGL(k_src_piece_start, dim3(blocks_for(p.S + 1)), dim3(256), 0, st, p);
+    DP_HIP(hipGetLastError());
+}
+
+void launch_lifting(Plan& p, hipStream_t st) {
+    if (p.n_pieces == 0) return;
+    hipLaunchKernelGGL(k_next, dim3(blocks_for(p.n_pieces)), dim3(256), 0, st, p);
+    for (uint32_t l = 1; l < p.levels; ++l)
+        hipLaunchKernelGGL(k_lift, dim3(blocks_for(p.n_pieces)), dim3(256), 0, st,
+                           (const uint32_t*)(p.jump + (uint64_t)(l - 1) * p.cap_pieces),
+                           p.jump + (uint64_t)l * p.cap_pieces, p.n_pieces);
+    DP_HIP(hipGetLastError());
+}
+
+void launch_window_count(Plan& p, hipStream_t st) {
+    hipLaunchKernelGGL(k_window_count, dim3(1), dim3(1024), (size_t)p.S * sizeof(uint64_t), st, p);
+    DP_HIP(hipGetLastError());
+}
+
+void launch_windows(Plan& p, hipStream_t st) {
+    if (p.n_windows == 0) return;
+    hipLaunchKernelGGL(k_windows, dim3(blocks_for(p.n_windows)), dim3(256), 0, st, p);
+    hipLaunchKernelGGL(k_window_stats, dim3(blocks_for(p.n_windows)), dim3(256), 0, st, p);
+    DP_HIP(hipGetLastError());
+}
+
+void launch_mixture_w(Plan& p, uint64_t W, uint32_t* nstart, hipStream_t st) {
+    hipLaunchKernelGGL(k_apportion, dim3(1), dim3(1024), (size_t)p.S * 12, st, p, W, nstart);
+    hipLaunchKernelGGL(k_slots, dim3(blocks_for(p.B)), dim3(256), 0, st, p, (const uint32_t*)nstart);
+    DP_HIP(hipGetLastError());
+}
+
+void launch_checks(Plan& p, hipStream_t st) {
+    hipLaunchKernelGGL(k_zero_u64, dim3(1), dim3(256), 0, st, p.checks, (uint64_t)2);
+    const uint64_t n = p.n_docs > p.n_kept ? p.n_docs : p.n_kept;
+    hipLaunchKernelGGL(k_checks, dim3(blocks_for(n)), dim3(256), 0, st, p);
+    DP_HIP(hipGetLastError());
+}
+
+void launch_cycle_sums(Plan& p, uint32_t U, hipStream_t st) {
+    hipLaunchKernelGGL(k_zero_u64, dim3(1), dim3(256), 0, st, p.cyc_sums, (uint64_t)2);
+    const uint64_t total = (uint64_t)U * p.B;
+    if (total) hipLaunchKernelGGL(k_cycle_sums, dim3(blocks_for(total)), dim3(256), 0, st, p, total);
+    DP_HIP(hipGetLastError());
+}
+
+void launch_zero_u64(uint64_t* a, uint64_t n, hipStream_t st) {
+    if (n) hipLaunchKernelGGL(k_zero_u64, dim3(blocks_for(n)), dim3(256), 0, st, a, n);
+    DP_HIP(hipGetLastError());
+}
+
+void launch_zero_u32(uint32_t* a, uint64_t n, hipStream_t st) {
+    if (n) hipLaunchKernelGGL(k_fill_u32, dim3(blocks_for(n)), dim3(256), 0, st, a, n, 0u);
+    DP_HIP(hipGetLastError());
+}
+
+}  // namespace dp

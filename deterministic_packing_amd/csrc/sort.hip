@@ -1,0 +1,156 @@
+// sort.hip — compaction of kept documents, Philox4x32-10 shuffle keys, and a
+// stable LSD radix sort of the kept documents by (group, key64).
+//
+// NeuronSpark-Trainer README, Concepts: a file's documents are shuffled.  The
+// shuffle here is counter-based: key64(d) = x1·2^32 + x0 of
+// Philox4x32-10(counter = (d lo, d hi, 0x53485546, 0), key = (seed lo, seed hi))
+// (Salmon et al., SC'11), so it depends only on the seed and the input index d,
+// never on rank, world or launch shape.  Kept documents enter the sort in
+// input order and every pass is stable, so ties of key64 fall back to d.
+#include "dp_common.h"
+
+namespace dp {
+namespace {
+
+constexpr int RB = 256;             // threads per block
+constexpr int RI = 8;               // rounds per tile
+constexpr int RTILE = RB * RI;      // elements per tile
+
+__global__ __launch_bounds__(256) void k_compact_keys(Plan p, uint64_t* key, uint32_t* val) {
+    const uint64_t d = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (d >= p.n_docs || !p.keep[d]) return;
+    const uint32_t at = p.kept_pos[d];
+    val[at] = (uint32_t)d;
+    key[at] = philox_key64((uint32_t)d, (uint32_t)(d >> 32), 0x53485546u, 0u, (uint32_t)p.seed,
+                           (uint32_t)(p.seed >> 32));
+}
+
+template <bool GROUP>
+__device__ inline uint32_t digit_of(uint64_t key, uint32_t val, const uint32_t* group, int shift) {
+    if (GROUP) return (group[val] >> shift) & 0xFFu;
+    return (uint32_t)(key >> shift) & 0xFFu;
+}
+
+template <bool GROUP>
+__global__ __launch_bounds__(RB) void k_hist(const uint64_t* key, const uint32_t* val, const uint32_t* group,
+                                             uint64_t n, int shift, uint32_t* hist, uint32_t nb) {
+    __shared__ uint32_t h[256];
+    h[threadIdx.x] = 0;
+    __syncthreads();
+    const uint64_t base = (uint64_t)blockIdx.x * RTILE;
+    for (int r = 0; r < RI; ++r) {
+        const uint64_t i = base + (uint64_t)r * RB + threadIdx.x;
+        if (i < n) atomicAdd(&h[digit_of<GROUP>(GROUP ? 0 : key[i], GROUP ? val[i] : 0, group, shift)], 1u);
+    }
+    __syncthreads();
+    hist[(uint64_t)threadIdx.x * nb + blockIdx.x] = h[threadIdx.x];
+}
+
+// Stable scatter: element i of the tile lands at
+//   offset[digit][tile] + (# earlier elements of the tile with the same digit).
+// Within a round of 256 elements the earlier same-digit lanes of a wave come
+// from ballots over the 8 digit bits; earlier waves and rounds from LDS counts.
+template <bool GROUP>
+__global__ __launch_bounds__(RB) void k_scatter(const uint64_t* key_in, const uint32_t* val_in,
+                                                const uint32_t* group, uint64_t n, int shift,
+                                                const uint32_t* hofs, uint32_t nb, uint64_t* key_out,
+                                                uint32_t* val_out, uint32_t* err) {
+    __shared__ uint32_t running[256];
+    __shared__ uint32_t wcount[RB / WAVE][256];
+    const int t = threadIdx.x, wid = t / WAVE, lane = t & (WAVE - 1);
+    running[t] = hofs[(uint64_t)t * nb + blockIdx.x];
+#pragma unroll
+    for (int w = 0; w < RB / WAVE; ++w) wcount[w][t] = 0;
+    __syncthreads();
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (WAVE - lane));
+    const uint64_t base = (uint64_t)blockIdx.x * RTILE;
+    for (int r = 0; r < RI; ++r) {
+        const uint64_t i = base + (uint64_t)r * RB + t;
+        const bool valid = i < n;
+        uint64_t k = 0;
+        uint32_t v = 0, dg = 0;
+        if (valid) {
+            k = key_in[i];
+            v = val_in[i];
+            dg = digit_of<GROUP>(k, v, group, shift);
+        }
+        uint64_t peers = __ballot(valid);
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+            const bool bit = (dg >> b) & 1u;
+            const uint64_t m = __ballot(bit);
+            peers &= bit ? m : ~m;
+        }
+        const uint32_t rank = (uint32_t)__popcll(peers & lt_mask);
+        if (valid && rank == 0) wcount[wid][dg] = (uint32_t)__popcll(peers);
+        __syncthreads();
+        if (valid) {
+            uint32_t dst = running[dg] + rank;
+            for (int w = 0; w < wid; ++w) dst += wcount[w][dg];
+            if (dst < n) {
+                key_out[dst] = k;
+                val_out[dst] = v;
+            } else {
+                atomicOr(err, ERR_INTERNAL);
+            }
+        }
+        __syncthreads();
+        uint32_t add = 0;
+#pragma unroll
+        for (int w = 0; w < RB / WAVE; ++w) {
+            add += wcount[w][t];
+            wcount[w][t] = 0;
+        }
+        running[t] += add;
+        __syncthreads();
+    }
+}
+
+}  // namespace
+
+void launch_keep_scan(Plan& p, hipStream_t st) {
+    scan_keep_u32(p.keep, p.n_docs, p.kept_pos, p.hist, st);
+    const uint64_t blocks = (p.n_docs + 255) / 256;
+    hipLaunchKernelGGL(k_compact_keys, dim3((uint32_t)blocks), dim3(256), 0, st, p, p.key[0], p.val[0]);
+    DP_HIP(hipGetLastError());
+}
+
+// requires p.n_kept (host) to be set
+void launch_sort(Plan& p, hipStream_t st) {
+    const uint64_t n = p.n_kept;
+    const uint32_t nb = (uint32_t)((n + RTILE - 1) / RTILE);
+    // hist holds [256·nb] counts followed by [256·nb + 1] scanned offsets and the scan's temp
+    uint32_t* hist = p.hist;
+    uint32_t* hofs = p.hist + 256ull * nb + 1;
+    void* tmp = hofs + 256ull * nb + 2;
+    int cur = 0;
+    auto pass = [&](bool group_pass, int shift) {
+        if (nb == 0) return;
+        if (group_pass)
+            hipLaunchKernelGGL(k_hist<true>, dim3(nb), dim3(RB), 0, st, p.key[cur], p.val[cur], p.group, n, shift,
+                               hist, nb);
+        else
+            hipLaunchKernelGGL(k_hist<false>, dim3(nb), dim3(RB), 0, st, p.key[cur], p.val[cur], p.group, n, shift,
+                               hist, nb);
+        scan_u32(hist, 256ull * nb, hofs, tmp, st);
+        if (group_pass)
+            hipLaunchKernelGGL(k_scatter<true>, dim3(nb), dim3(RB), 0, st, p.key[cur], p.val[cur], p.group, n,
+                               shift, hofs, nb, p.key[cur ^ 1], p.val[cur ^ 1], p.err);
+        else
+            hipLaunchKernelGGL(k_scatter<false>, dim3(nb), dim3(RB), 0, st, p.key[cur], p.val[cur], p.group, n,
+                               shift, hofs, nb, p.key[cur ^ 1], p.val[cur ^ 1], p.err);
+        DP_HIP(hipGetLastError());
+        cur ^= 1;
+    };
+    for (int shift = 0; shift < 64; shift += 8) pass(false, shift);
+    for (int shift = 0; p.G > 1 && shift < 32 && ((p.G - 1) >> shift) != 0; shift += 8) pass(true, shift);
+    p.sort_buf = (uint32_t)cur;
+}
+
+// workspace for the sort's histogram, offsets and scan temp, in uint32 words
+uint64_t sort_hist_words(uint64_t n_docs) {
+    const uint64_t nb = (n_docs + RTILE - 1) / RTILE + 1;
+    return 256ull * nb * 2 + 4 + (scan_temp_bytes(256ull * nb) + 3) / 4 + 16;
+}
+
+}  // namespace dp

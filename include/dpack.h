@@ -1,0 +1,196 @@
+/*
+ * dpack.h — C ABI of the deterministic packing library for MI355X (gfx950).
+ *
+ * The library turns pre-tokenized documents resident in GPU memory into
+ * training batches of fixed T-position windows that are byte-identical at any
+ * rank count:
+ *   hash hold-out → (source, stratum) grouping → counter-based shuffle →
+ *   strata merge → window cut (next-fit) → mixture slots → emission of token
+ *   ids, position ids, document ids and loss masks → per-window SHA-256.
+ *
+ * Pages the operations follow (cited per call below):
+ *   - NeuronSpark-Trainer README, "Concepts": data lines consumed in cycles,
+ *     every token trained once (running out is an error), each update within
+ *     two samples of each source's recipe share, strata at their share of the
+ *     source's tokens cut at document ends, documents shuffled, 1 % (5 % for
+ *     one source) held out by a hash of the text that is the same in every
+ *     line; "Training": updates never span a cycle end, a resume with another
+ *     sample order is refused.
+ *   - Zephon blog post (aixai.ru), resume of a 16-GPU run on 8/32/64 GPUs: the
+ *     SHA-256 of every global batch is equal byte for byte; TorchTitan
+ *     integration: configuration errors (divisibility) fail at start.
+ *   - Linnet "Training" docs, "Supervised fine-tuning": batches of exactly T
+ *     positions padded, a prompted example learns only its completion, updates
+ *     weighed by the count of learned positions; "Other trainers": a position
+ *     id 0 starts a new sequence within a row.
+ *
+ * Conventions for every call:
+ *   - Return 0 (PACK_OK) on success, a negative PACK_E_* code on failure. No
+ *     exception or signal crosses the ABI. pack_last_error() gives a message.
+ *   - "device" pointers are GPU memory of the current HIP device; "host"
+ *     pointers are CPU memory.  Device inputs are borrowed (caller-owned,
+ *     read-only, must outlive the context); the context owns its workspace.
+ *   - All work is ordered on cfg->stream (NULL = the default stream).
+ *   - One context must not be used by two host threads at once.
+ *   - No environment variable changes any output byte.
+ */
+#ifndef DPACK_H
+#define DPACK_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DPACK_ABI_VERSION 1u
+
+enum {
+    PACK_OK = 0,
+    PACK_E_ABI = -1,       /* cfg->abi_version differs from DPACK_ABI_VERSION */
+    PACK_E_INVAL = -2,     /* an argument or the corpus violates a stated precondition */
+    PACK_E_NOMEM = -3,     /* a host or device allocation failed */
+    PACK_E_HIP = -4,       /* a HIP runtime call failed (message in pack_last_error) */
+    PACK_E_EXHAUSTED = -5, /* a source cannot supply the cycle's windows */
+    PACK_E_STATE = -6,     /* calls out of order (cycle skipped, batch before cycle) */
+    PACK_E_RANGE = -7,     /* step range beyond the current cycle */
+};
+
+typedef struct pack_ctx pack_ctx;
+
+/* Configuration of a packing context.  Limits (PACK_E_INVAL otherwise):
+ * 1 ≤ n_docs < 2^31; every document shorter than 2^32 tokens; offsets
+ * monotone with doc_offsets[n_docs] ≤ n_tokens; 1 ≤ n_sources ≤ 4096;
+ * source < n_sources; stratum < n_strata[source]; Σ n_strata ≤ 65536;
+ * Σ share_weight in [1, 2^64); holdout_bp ≤ 10000; T a multiple of 64 in
+ * [64, 2^20]; 1 ≤ B ≤ 2^20; world ≥ 1 divides B; rank < world. */
+typedef struct pack_config {
+    uint32_t abi_version;          /* DPACK_ABI_VERSION */
+    uint32_t flags;                /* reserved, must be 0 */
+    const uint32_t *tokens;        /* device [n_tokens] token ids */
+    uint64_t n_tokens;
+    const uint64_t *doc_offsets;   /* device [n_docs+1]: document d is tokens[off[d], off[d+1]) */
+    uint64_t n_docs;
+    const uint16_t *doc_source;    /* device [n_docs] */
+    const uint16_t *doc_stratum;   /* device [n_docs]; NULL = stratum 0 for all */
+    const uint32_t *doc_prompt_len;/* device [n_docs]; NULL = no prompt (every token learned) */
+    uint32_t n_sources;
+    const uint32_t *n_strata;      /* host [n_sources]; NULL = one stratum each */
+    const uint64_t *share_weight;  /* host [n_sources] integer recipe weights */
+    const uint32_t *holdout_bp;    /* host [n_sources] hold-out rate in basis points */
+    uint32_t window_tokens;        /* T: positions per window */
+    uint32_t global_batch;         /* B: windows per update (all ranks) */
+    uint32_t updates_per_cycle;    /* updates in each cycle; 0 = the most the data support */
+    uint32_t pad_token;            /* token id written at padding positions */
+    uint64_t seed;                 /* shuffle seed */
+    uint32_t rank, world;          /* this context emits slots [rank·B/world, (rank+1)·B/world) */
+    void *stream;                  /* hipStream_t for all work; NULL = default stream */
+} pack_config;
+
+/* pack_init — build the plan of a corpus (hash and hold-out of every
+ * document, grouping, shuffle keys and sort, strata merge, pieces, next-fit
+ * windows, per-update apportionment and slot table) on cfg->stream.
+ * Synchronous: returns once the plan is on the device; reads back only the
+ * per-source window counts and statistics.  The plan is independent of rank
+ * and world, which only select the emitted slice.
+ * Errors: PACK_E_ABI, PACK_E_INVAL (limits above, checked on the host and,
+ * for device arrays, by a validation kernel), PACK_E_NOMEM, PACK_E_HIP.
+ * On error *out is NULL and nothing is leaked. */
+int pack_init(const pack_config *cfg, pack_ctx **out);
+
+/* Per-cycle information, filled by pack_cycle.  The per-source arrays are
+ * optional host buffers of n_sources entries owned by the caller. */
+typedef struct pack_cycle_info {
+    uint32_t cycle;
+    uint32_t n_updates;            /* U of this cycle */
+    uint64_t real_tokens;          /* non-padding positions in the cycle (all ranks) */
+    uint64_t learned_tokens;       /* positions with loss mask 1 in the cycle (all ranks) */
+    uint64_t positions;            /* U·B·T */
+    uint8_t plan_digest[32];       /* SHA-256 identifying recipe, stream sizes, cycle start and order */
+    uint64_t *windows_start;       /* first window of the cycle in each source's stream */
+    uint64_t *windows_taken;       /* U·n_s */
+    uint64_t *windows_remaining;   /* windows left after the cycle */
+    uint64_t *kept_docs, *kept_tokens, *held_docs, *held_tokens;
+    uint32_t *per_update;          /* n_s: windows of each source in every update */
+} pack_cycle_info;
+
+/* pack_cycle — plan cycle `cycle` (must be 0, then 1, 2, …): U updates, each
+ * of B windows of which n_s come from source s, taking the next U·n_s windows
+ * of each source's stream.  U = updates_per_cycle, or when that is 0 the most
+ * every source with n_s > 0 supports.  Synchronous.  info may be NULL.
+ * Errors: PACK_E_STATE (out of order), PACK_E_EXHAUSTED (some source cannot
+ * supply U·n_s windows, or U would be 0: an error, never a second pass; the
+ * cycle state is unchanged), PACK_E_HIP. */
+int pack_cycle(pack_ctx *ctx, uint32_t cycle, pack_cycle_info *info);
+
+/* Outputs of pack_batch: device buffers owned by the caller, each laid out
+ * [n_steps][B/world][T] in slot order (row-major, contiguous). */
+typedef struct pack_out {
+    uint32_t *tokens;    /* token id, pad_token at padding */
+    int32_t *pos;        /* offset within the piece (0 starts each piece), 0 at padding */
+    int32_t *doc;        /* global input document index, −1 at padding */
+    uint8_t *mask;       /* 1 iff the token is learned (at or after the prompt) */
+    int64_t *learned;    /* device [n_steps]: global learned positions of each update; NULL = skip */
+    uint8_t *digests;    /* device [n_steps][B/world][32]: SHA-256 of each window's record
+                            tok‖pos‖doc‖mask (little-endian, 13·T bytes); NULL = skip */
+} pack_out;
+
+/* pack_batch — emit updates [step, step+n_steps) of the current cycle for
+ * this context's rank.  Asynchronous on cfg->stream; a pure function of
+ * (corpus, config, cycle, step), so re-emitting a step reproduces it exactly.
+ * Errors: PACK_E_STATE (no cycle planned), PACK_E_RANGE (step + n_steps > U
+ * or n_steps = 0), PACK_E_INVAL (a NULL output array), PACK_E_HIP. */
+int pack_batch(pack_ctx *ctx, uint32_t step, uint32_t n_steps, const pack_out *out);
+
+/* pack_fingerprint — batch fingerprints: for each of n_batches, SHA-256 over
+ * its B window digests (B·32 bytes, slot order) from the device array
+ * digests [n_batches][B][32], into the device array out [n_batches][32].
+ * For world > 1 the caller first gathers every rank's digests in rank order.
+ * Asynchronous on the context's stream.  Errors: PACK_E_INVAL (NULL), PACK_E_HIP. */
+int pack_fingerprint(pack_ctx *ctx, const uint8_t *digests, uint32_t n_batches, uint8_t *out);
+
+/* Plan arrays that pack_inspect copies to the host (for checking the plan
+ * against an independent implementation).  Types and lengths: */
+enum {
+    PACK_INSPECT_HASH = 1,          /* uint64 [n_docs] content hash */
+    PACK_INSPECT_KEEP = 2,          /* uint8  [n_docs] 1 = kept */
+    PACK_INSPECT_ORDER = 3,         /* uint32 [n_kept] kept docs, source by source, merged order */
+    PACK_INSPECT_SRC_DOC_START = 4, /* uint64 [n_sources+1] */
+    PACK_INSPECT_PIECE_DOC = 5,     /* uint32 [n_pieces] */
+    PACK_INSPECT_PIECE_OFF = 6,     /* uint32 [n_pieces] offset of the piece in its document */
+    PACK_INSPECT_PIECE_LEN = 7,     /* uint32 [n_pieces] */
+    PACK_INSPECT_PIECE_WOFF = 8,    /* uint32 [n_pieces] offset of the piece in its window */
+    PACK_INSPECT_SRC_PIECE_START = 9,  /* uint64 [n_sources+1] */
+    PACK_INSPECT_WIN_FIRST = 10,    /* uint64 [n_windows+1] first piece of each window */
+    PACK_INSPECT_SRC_WIN_START = 11,/* uint64 [n_sources+1] */
+    PACK_INSPECT_WIN_REAL = 12,     /* uint64 [n_windows] real positions */
+    PACK_INSPECT_WIN_LEARN = 13,    /* uint64 [n_windows] learned positions */
+    PACK_INSPECT_PER_UPDATE = 14,   /* uint32 [n_sources] n_s */
+    PACK_INSPECT_SLOT_SRC = 15,     /* uint32 [B] */
+    PACK_INSPECT_SLOT_K = 16,       /* uint32 [B] */
+    PACK_INSPECT_COUNTS = 17,       /* uint64 [3]: n_kept, n_pieces, n_windows */
+};
+
+/* pack_inspect — copy plan array `what` to host memory (synchronous).
+ * *needed receives its size in bytes; nothing is copied when
+ * capacity_bytes < *needed.  Errors: PACK_E_INVAL (unknown what, NULL ctx),
+ * PACK_E_RANGE (capacity too small), PACK_E_HIP. */
+int pack_inspect(const pack_ctx *ctx, uint32_t what, void *host_dst, uint64_t capacity_bytes,
+                 uint64_t *needed);
+
+/* pack_destroy — free the context and its device workspace (synchronizes
+ * its stream first).  NULL is a no-op. */
+void pack_destroy(pack_ctx *ctx);
+
+/* Static description of an error code. */
+const char *pack_strerror(int code);
+
+/* Message of the last error on this context (or of the last failed
+ * pack_init on this thread when ctx is NULL); never NULL. */
+const char *pack_last_error(const pack_ctx *ctx);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DPACK_H */

@@ -1,0 +1,95 @@
+"""The C-ABI library loads, exports every function include/dpack.h declares,
+and rejects bad configurations on the host (no GPU call is made)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import deterministic_packing_amd as dp
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = set()
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names |= set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(pack_\w+)\s*\(", text, flags=re.M))
+    return names
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(dp.LIB_PATH):
+        pytest.fail("libdpack.so is not built (run __graft_entry__.build())")
+    return dp.load_library()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    declared = _declared_functions()
+    assert declared == set(dp.SYMBOLS), declared
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_strerror_covers_every_code(lib):
+    for code in range(-7, 1):
+        assert dp.pack_strerror(code) not in ("", "unknown error")
+    assert dp.pack_strerror(-99) == "unknown error"
+
+
+def _cfg(**kw):
+    import numpy as np
+    keep = dict(w=np.array([1, 1], np.uint64), bp=np.array([0, 0], np.uint32))
+    c = dp.PackConfig()
+    c.abi_version = dp.ABI_VERSION
+    c.tokens, c.n_tokens = 16, 100            # never dereferenced: host checks fail first
+    c.doc_offsets, c.n_docs = 16, 3
+    c.doc_source = 16
+    c.n_sources = 2
+    c.share_weight = keep["w"].ctypes.data
+    c.holdout_bp = keep["bp"].ctypes.data
+    c.window_tokens, c.global_batch = 128, 8
+    c.world, c.rank = 1, 0
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c, keep
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("abi_version", 99, dp.PACK_E_ABI),
+    ("world", 3, dp.PACK_E_INVAL),          # world must divide B (fail fast, as the pages require)
+    ("rank", 5, dp.PACK_E_INVAL),
+    ("window_tokens", 100, dp.PACK_E_INVAL),
+    ("global_batch", 0, dp.PACK_E_INVAL),
+    ("n_docs", 0, dp.PACK_E_INVAL),
+    ("flags", 1, dp.PACK_E_INVAL),
+    ("n_sources", 0, dp.PACK_E_INVAL),
+])
+def test_init_rejects_bad_config_on_host(lib, field, value, code):
+    cfg, keep = _cfg(**{field: value})
+    ctx = C.c_void_p()
+    rc = lib.pack_init(C.byref(cfg), C.byref(ctx))
+    assert rc == code
+    assert ctx.value is None
+    assert lib.pack_last_error(None).decode()
+
+
+def test_init_rejects_zero_weights_and_bad_holdout(lib):
+    import numpy as np
+    for w, bp in [([0, 0], [0, 0]), ([1, 1], [0, 10001]), ([2**63, 2**63], [0, 0])]:
+        cfg, keep = _cfg()
+        wa, ba = np.array(w, np.uint64), np.array(bp, np.uint32)
+        cfg.share_weight, cfg.holdout_bp = wa.ctypes.data, ba.ctypes.data
+        ctx = C.c_void_p()
+        assert lib.pack_init(C.byref(cfg), C.byref(ctx)) == dp.PACK_E_INVAL
+
+
+def test_null_arguments_are_errors(lib):
+    assert lib.pack_init(None, None) == dp.PACK_E_INVAL
+    assert lib.pack_cycle(None, 0, None) == dp.PACK_E_INVAL
+    assert lib.pack_batch(None, 0, 1, None) == dp.PACK_E_INVAL
+    lib.pack_destroy(None)

@@ -1,0 +1,252 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle, bit for bit,
+on seeded corpora of every workload shape, plus error paths and determinism."""
+import numpy as np
+import pytest
+
+import deterministic_packing_amd as dp
+import oracle
+from synth import make_corpus, random_small
+from synth.corpus import Corpus
+
+from _gpu_parity import compare_batch, compare_cycle, compare_plan, say, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    dp.load_library()
+    yield
+    torch.cuda.synchronize()
+
+
+SMALL_CASES = [("small", s) for s in range(8)] + [
+    ("tiny", 1.0), ("sft", 0.004), ("long", 0.01), ("pretrain", 0.006), ("full", 0.002)]
+
+
+def _corpus(kind, arg):
+    if kind == "small":
+        s = int(arg)
+        return random_small(s, n_docs=60 + 40 * s, n_sources=1 + s % 4, max_strata=1 + s % 3, T=64 * (1 + s % 2),
+                            B=[1, 2, 4, 6, 8, 3, 5, 7][s], max_len=[40, 150, 300, 90, 64, 200, 20, 500][s],
+                            prompts=bool(s % 2), bp_max=2000)
+    c = make_corpus(kind, arg)
+    if kind == "pretrain":
+        c = c.replace(updates_per_cycle=0)  # a scaled-down corpus cannot supply 200 updates
+    return c
+
+
+@pytest.mark.parametrize("kind,arg", SMALL_CASES)
+def test_plan_cycle_batch_parity(kind, arg):
+    c = _corpus(kind, arg)
+    say("plan/cycle/batch", kind, arg, "docs", c.n_docs, "T", c.T, "B", c.B)
+    op = oracle.Plan(c)
+    pk = dp.Packer(c)
+    compare_plan(pk, op)
+    try:
+        oi = op.cycle(0)
+    except oracle.OracleError as e:
+        with pytest.raises(dp.DpackError) as ge:
+            pk.cycle(0)
+        assert ge.value.code == e.code
+        return
+    gi = pk.cycle(0)
+    compare_cycle(gi, oi, op)
+    U = oi.n_updates
+    steps = list(range(0, U, max(1, U // 6)))[:6]
+    for st in steps:
+        n = min(3, U - st)
+        say("batch", kind, arg, "step", st, "n", n)
+        o = op.batch(st, n)
+        g = to_np(pk.batch(st, n))
+        compare_batch(g, o, f"{kind}{arg} step {st}")
+        fp = pk.fingerprint(pk.batch(st, n)["digests"]).cpu().numpy()
+        for i in range(n):
+            assert fp[i].tobytes() == oracle.batch_fingerprint(o["digests"][i])
+    pk.close()
+
+
+@pytest.mark.parametrize("kind,arg,worlds", [("tiny", 0.5, [1, 2, 4, 8]), ("pretrain", 0.006, [1, 8, 16, 32, 64]),
+                                             ("small", 4, [1, 2, 4, 8])])
+def test_elastic_rank_counts_identical(kind, arg, worlds):
+    c = _corpus(kind, arg)
+    if kind == "small":
+        c = c.replace(B=8)
+    if kind == "pretrain":
+        c = c.replace(updates_per_cycle=2)
+    op = oracle.Plan(c)
+    op.cycle(0)
+    n = min(2, op.cycle_info.n_updates)
+    ref = op.batch(0, n)
+    ref_fp = [oracle.batch_fingerprint(ref["digests"][i]) for i in range(n)]
+    tensors = dp.upload_corpus(c)
+    for R in worlds:
+        say("elastic", kind, arg, "world", R)
+        parts = []
+        for r in range(R):
+            pk = dp.Packer(c, rank=r, world=R, device_tensors=tensors)  # an independent context per rank
+            pk.cycle(0)
+            parts.append(to_np(pk.batch(0, n)))
+            pk.close()
+        cat = {k: np.concatenate([p[k] for p in parts], axis=1) for k in ("tokens", "pos", "doc", "mask", "digests")}
+        cat["learned"] = parts[0]["learned"]
+        for p in parts:
+            assert np.array_equal(p["learned"], ref["learned"])
+        compare_batch(cat, ref, f"world {R}")
+        fps = [oracle.batch_fingerprint(cat["digests"][i]) for i in range(n)]
+        assert fps == ref_fp
+
+
+def test_world_not_dividing_batch_fails_at_init():
+    c = make_corpus("tiny", 0.2)
+    for R in (3, 16, 64):
+        with pytest.raises(dp.DpackError) as e:
+            dp.Packer(c, rank=0, world=R)
+        assert e.value.code == dp.PACK_E_INVAL
+
+
+def test_cycles_until_exhausted_match_oracle():
+    c = random_small(40, n_docs=400, n_sources=3, T=64, B=6, max_len=100, prompts=True, updates_per_cycle=2)
+    op = oracle.Plan(c)
+    pk = dp.Packer(c)
+    compare_plan(pk, op)
+    for cyc in range(100):
+        try:
+            oi = op.cycle(cyc)
+        except oracle.OracleError as e:
+            assert e.code == oracle.OR_E_EXHAUSTED
+            with pytest.raises(dp.DpackError) as ge:
+                pk.cycle(cyc)
+            assert ge.value.code == dp.PACK_E_EXHAUSTED
+            break
+        say("cycle", cyc)
+        compare_cycle(pk.cycle(cyc), oi, op)
+        compare_batch(to_np(pk.batch(0, oi.n_updates)), op.batch(0, oi.n_updates), f"cycle {cyc}")
+    else:
+        pytest.fail("never exhausted")
+    pk.close()
+
+
+def test_call_order_errors():
+    c = random_small(41, n_docs=200, T=64, B=4, max_len=80)
+    pk = dp.Packer(c)
+    with pytest.raises(dp.DpackError) as e:
+        pk.batch(0, 1)
+    assert e.value.code == dp.PACK_E_STATE
+    with pytest.raises(dp.DpackError) as e:
+        pk.cycle(1)
+    assert e.value.code == dp.PACK_E_STATE
+    info = pk.cycle(0)
+    with pytest.raises(dp.DpackError) as e:
+        pk.batch(info["n_updates"], 1)
+    assert e.value.code == dp.PACK_E_RANGE
+    with pytest.raises(dp.DpackError) as e:
+        pk.batch(0, 0)
+    assert e.value.code == dp.PACK_E_RANGE
+    pk.close()
+
+
+def _bad_corpus(kind):
+    c = random_small(42, n_docs=50, T=64, B=2, max_len=40, zero_len_frac=0.0)
+    if kind == "offsets":
+        off = c.offsets.copy()
+        off[11] = off[10] - 1  # document 10 gets a negative length
+        return c.replace(offsets=off)
+    if kind == "source":
+        src = c.source.copy()
+        src[7] = c.n_sources
+        return c.replace(source=src)
+    if kind == "stratum":
+        st = c.stratum.copy()
+        st[5] = c.n_strata[c.source[5]]
+        return c.replace(stratum=st)
+    if kind == "tokens":
+        return c.replace(tokens=c.tokens[:-5].copy())
+    raise ValueError(kind)
+
+
+@pytest.mark.parametrize("kind", ["offsets", "source", "stratum", "tokens"])
+def test_invalid_corpus_rejected_by_validation_kernel(kind):
+    c = _bad_corpus(kind)
+    say("invalid corpus", kind)
+    with pytest.raises(dp.DpackError) as e:
+        dp.Packer(c)
+    assert e.value.code == dp.PACK_E_INVAL
+
+
+def test_all_held_out_is_exhausted_not_a_fault():
+    c = random_small(43, n_docs=100, T=64, B=2, max_len=50)
+    c = c.replace(holdout_bp=np.full(c.n_sources, 10000, np.uint32))
+    op = oracle.Plan(c)
+    assert op.order.size == 0
+    pk = dp.Packer(c)
+    compare_plan(pk, op)
+    with pytest.raises(dp.DpackError) as e:
+        pk.cycle(0)
+    assert e.value.code == dp.PACK_E_EXHAUSTED
+
+
+def _explicit(lengths, T, B, sources=None, strata=None, n_strata=None, weights=None, prompts=None, bp=None):
+    L = np.asarray(lengths, np.int64)
+    D = L.shape[0]
+    off = np.zeros(D + 1, np.uint64)
+    np.cumsum(L, out=off[1:])
+    r = np.random.default_rng(D)
+    src = np.zeros(D, np.uint16) if sources is None else np.asarray(sources, np.uint16)
+    S = int(src.max()) + 1 if D else 1
+    st = np.zeros(D, np.uint16) if strata is None else np.asarray(strata, np.uint16)
+    ns = np.ones(S, np.uint32) if n_strata is None else np.asarray(n_strata, np.uint32)
+    w = np.ones(S, np.uint64) if weights is None else np.asarray(weights, np.uint64)
+    return Corpus("edge", r.integers(0, 50000, size=int(off[-1]), dtype=np.uint32), off, src, st,
+                  None if prompts is None else np.asarray(prompts, np.uint32), ns, w,
+                  np.zeros(S, np.uint32) if bp is None else np.asarray(bp, np.uint32), T=T, B=B,
+                  updates_per_cycle=0, seed=7, pad_token=99)
+
+
+EDGE = {
+    "exact_T": lambda: _explicit([64] * 10 + [128, 192, 1], 64, 2),
+    "one_token_docs": lambda: _explicit([1] * 300, 64, 1),
+    "one_long_doc": lambda: _explicit([64 * 37 + 5], 64, 1),
+    "ragged_many_pieces": lambda: _explicit([1, 2, 3, 600, 1, 63, 65, 2] * 40, 64, 4),
+    "empty_docs_and_source": lambda: _explicit([0, 5, 0, 70, 3, 0] * 20, 64, 2,
+                                              sources=[0, 0, 2, 2, 0, 2] * 20, weights=[3, 0, 5]),
+    "empty_stratum": lambda: _explicit([10, 20, 30, 40] * 30, 64, 2, strata=[0, 2, 0, 2] * 30, n_strata=[3]),
+    "tiny_share_zero_seats": lambda: _explicit([30] * 200, 64, 4, sources=[0, 1] * 100, weights=[1000, 1]),
+    "prompt_beyond_doc": lambda: _explicit([10, 100, 200] * 30, 64, 2, prompts=[50, 3, 150] * 30),
+    "many_pieces_window": lambda: _explicit([1] * 5000, 4096, 1),
+}
+
+
+@pytest.mark.parametrize("name", sorted(EDGE))
+def test_edge_cases(name):
+    c = EDGE[name]()
+    say("edge", name)
+    op = oracle.Plan(c)
+    pk = dp.Packer(c)
+    compare_plan(pk, op)
+    try:
+        oi = op.cycle(0)
+    except oracle.OracleError as e:
+        with pytest.raises(dp.DpackError) as ge:
+            pk.cycle(0)
+        assert ge.value.code == e.code
+        return
+    gi = pk.cycle(0)
+    compare_cycle(gi, oi, op)
+    n = min(oi.n_updates, 8)
+    compare_batch(to_np(pk.batch(0, n)), op.batch(0, n), name)
+
+
+def test_reemission_and_reinit_are_bytewise_identical():
+    c = make_corpus("sft", 0.002)
+    a = dp.Packer(c)
+    a.cycle(0)
+    x = to_np(a.batch(1, 3))
+    y = to_np(a.batch(1, 3))
+    b = dp.Packer(c)
+    b.cycle(0)
+    z = to_np(b.batch(1, 3))
+    for k in x:
+        assert np.array_equal(x[k], y[k]) and np.array_equal(x[k], z[k]), k
