@@ -1,0 +1,265 @@
+#!/usr/bin/env python3
+"""Packed tokens/s of the whole deterministic-packing path on one MI355X.
+
+One step = one pass of the whole path over the resident synthetic corpus:
+pack_init (validation, hash + hold-out, keys, radix sort, strata merge,
+pieces, next-fit cut, window table, mixture) + pack_cycle(0) + pack_batch of
+every update of the cycle with learned counts and per-window SHA-256 digests
++ pack_destroy.  The corpus is in HBM and the output buffers are allocated
+before the timed region.  value = real (non-padding) tokens emitted per second.
+
+Per-kernel times come from HIP events the library records on its stream
+(PACK_FLAG_TIMING) inside the timed steps; the roofline object is reported for
+the kernel that takes the most time, and every phase is listed under
+"kernels".  The CPU baseline is the oracle (plain sequential C) timed on this
+host on a bounded sample of the same workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0                      # MI355X HBM3E, 8 TB/s
+VALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12  # 256 CUs x 4 SIMD x 16 lanes x 2.4 GHz = 39.3 T int32 ops/s
+SHA_OPS_PER_BLOCK = 1400                    # int32 VALU ops per SHA-256 compression on gfx950
+METRIC = "packed tokens/s and achieved HBM GB/s (% of peak), 1 MI355X, bit-exact vs oracle"
+
+WORKLOAD_TEXT = {
+    "pretrain": "pre-train mix: 15 sources x 4 strata, 1M docs, lognormal lengths (median 600, sigma 1.2, "
+                "max 65536), Zipf(1.1) ids over 65,536, hold-out 1% (5% source 14), T=4096, B=256, 200 updates",
+    "tiny": "tiny: 2 sources x 2,000 docs, geometric lengths mean 300, T=2048, B=8, max updates",
+    "sft": "SFT: 500k prompt/completion pairs, T=4096, B=8, completion-only mask, max updates",
+    "long": "long-context: 8 sources, 200k Pareto(1.3) docs 1k-200k, T=32768, B=32, max updates",
+    "full": "full cycle: 2B tokens, 15 sources x 8 strata, T=4096, B=1024, max updates",
+}
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def traffic_from_profile(kernel: str, workload: str):
+    """HBM bytes per launch measured by rocprofv3 PMC runs, if a committed
+    summary exists for this kernel and workload and the kernel's source is
+    unchanged since (else None)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_pmc.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if line.startswith("- ") and ":" in line:
+            k, v = line[2:].split(":", 1)
+            fields[k.strip()] = v.strip().strip("`")
+    src = fields.get("source file")
+    if not src or "traffic bytes per launch" not in fields:
+        return None
+    cur = hashlib.sha256(open(os.path.join(ROOT, src), "rb").read()).hexdigest()
+    if cur != fields.get("source sha256"):
+        return None
+    return float(fields["traffic bytes per launch"])
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="pretrain", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--scale", type=float, default=1.0, help="fraction of the workload (1.0 = as specified)")
+    ap.add_argument("--cpu-sample-updates", type=int, default=10,
+                    help="updates the oracle emits for the CPU baseline (the plan is always whole)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-copy", action="store_true", help="skip the plain D2D copy used as calibration/ceiling")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}); "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import deterministic_packing_amd as dp
+    from synth import make_corpus
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    dp.load_library()
+
+    t0 = time.time()
+    corpus = make_corpus(args.workload, args.scale)
+    log(f"corpus {args.workload} scale {args.scale}: {corpus.n_docs} docs, {corpus.n_tokens} tokens "
+        f"({time.time() - t0:.1f}s)")
+    tensors = dp.upload_corpus(corpus)
+    torch.cuda.synchronize()
+    log("corpus resident in HBM")
+
+    probe = dp.Packer(corpus, device_tensors=tensors)
+    try:
+        U = probe.cycle(0)["n_updates"]
+    except dp.DpackError as e:
+        if e.code != dp.PACK_E_EXHAUSTED or args.scale == 1.0:
+            raise
+        # a scaled-down corpus cannot supply the configured updates: take the most it supports
+        probe.close()
+        corpus = corpus.replace(updates_per_cycle=0)
+        probe = dp.Packer(corpus, device_tensors=tensors)
+        U = probe.cycle(0)["n_updates"]
+    probe.close()
+    B, T = corpus.B, corpus.T
+    out = dp.Packer.alloc_out(probe, U)  # output buffers outside the timed region
+    torch.cuda.synchronize()
+    log(f"cycle 0: {U} updates x {B} windows x {T} positions")
+
+    def one_step():
+        pk = dp.Packer(corpus, device_tensors=tensors, timing=True)
+        info = pk.cycle(0)
+        pk.batch_into(0, info["n_updates"], out)
+        tm = pk.timings(reset=True)
+        pk.close()
+        return info, tm
+
+    for w in range(args.warmup):
+        one_step()
+        log(f"warmup {w + 1}/{args.warmup} done")
+    torch.cuda.synchronize()
+    phase_ms = {}
+    phase_calls = {}
+    t_start = time.perf_counter()
+    for s in range(args.steps):
+        info, tm = one_step()
+        for k, (ms, n) in tm.items():
+            phase_ms[k] = phase_ms.get(k, 0.0) + ms
+            phase_calls[k] = phase_calls.get(k, 0) + n
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    ms_per_step = elapsed * 1e3 / args.steps
+    real = info["real_tokens"]
+    positions = info["positions"]
+    value = real / (ms_per_step / 1e3)
+    log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step, {value:.4g} packed tokens/s")
+
+    # per-kernel figures (averaged per launch over the timed steps)
+    n_windows = U * B
+    algo = {
+        # emission: read every real token once, write 13 bytes per position
+        "emit": ("hbm", 4.0 * real + 13.0 * positions, "GB/s"),
+        # hash: read every token once + per document offsets/source in, hash/keep out
+        "hash": ("hbm", 4.0 * corpus.n_tokens + 19.0 * corpus.n_docs, "GB/s"),
+        # window SHA-256: (13T/64 + 1) compressions per window
+        "digest": ("alu", SHA_OPS_PER_BLOCK * n_windows * (13 * T // 64 + 1), "TOP/s"),
+    }
+    kernels = {}
+    for k in phase_ms:
+        if phase_calls[k] == 0:
+            continue
+        per_step = phase_ms[k] / args.steps
+        entry = {"ms_per_step": round(per_step, 4), "launch_groups_per_step": phase_calls[k] / args.steps}
+        if k in algo:
+            bound, work, unit = algo[k]
+            per_launch_ms = phase_ms[k] / phase_calls[k]
+            ach = work / (per_launch_ms / 1e3) / 1e9 if unit == "GB/s" else work / (per_launch_ms / 1e3) / 1e12
+            peak = HBM_PEAK_GBPS if unit == "GB/s" else VALU_PEAK_TOPS
+            entry.update(bound=bound, achieved=round(ach, 2), peak=round(peak, 1), unit=unit,
+                         frac=round(ach / peak, 4), work_per_launch=work)
+        kernels[k] = entry
+    dominant = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
+    dom = kernels[dominant]
+    roofline = None
+    if "bound" in dom:
+        traffic = traffic_from_profile(dominant, args.workload)
+        roofline = {"kernel": dominant, "bound": dom["bound"], "achieved": dom["achieved"], "peak": dom["peak"],
+                    "unit": dom["unit"], "frac": dom["frac"], "traffic": traffic}
+    emit_k = kernels.get("emit", {})
+    emit_roofline = None
+    if "achieved" in emit_k:
+        emit_roofline = {"kernel": "emit", "bound": "hbm", "achieved": emit_k["achieved"], "peak": HBM_PEAK_GBPS,
+                         "unit": "GB/s", "frac": emit_k["frac"], "traffic": traffic_from_profile("emit", args.workload)}
+
+    # plain device-to-device copy of 1 GiB: practical HBM ceiling and the
+    # known-size kernel the PMC byte counters are calibrated against
+    copy = None
+    if not args.no_copy:
+        n = 1 << 28
+        a = torch.empty(n, dtype=torch.int32, device="cuda")
+        b = torch.empty_like(a)
+        a.fill_(1)
+        b.copy_(a)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(5):
+            b.copy_(a)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 5
+        copy = {"bytes_per_copy": 2 * 4 * n, "ms": round(ms, 4), "GBps": round(2 * 4 * n / (ms / 1e3) / 1e9, 1)}
+        del a, b
+
+    # CPU baseline: the oracle on this host (whole plan, sampled updates)
+    cpu = None
+    sample_check = None
+    if not args.no_cpu_baseline:
+        import oracle
+        oracle.build()
+        n_s = max(1, min(args.cpu_sample_updates, U))
+        t_a = time.perf_counter()
+        op = oracle.Plan(corpus)
+        t_b = time.perf_counter()
+        oi = op.cycle(0)
+        t_c = time.perf_counter()
+        ob = op.batch(0, n_s, digests=True)
+        t_d = time.perf_counter()
+        est = (t_b - t_a) + (t_c - t_b) + (t_d - t_c) * U / n_s
+        cpu = {"value": round(real / est, 1), "unit": "packed tokens/s", "cores": 1, "kind": "oracle",
+               "sample": (f"whole plan of the corpus ({t_b - t_a:.2f}s) + cycle ({t_c - t_b:.2f}s) + emission "
+                          f"with SHA-256 of updates 0..{n_s - 1} of {U} ({t_d - t_c:.2f}s), scaled to {U} "
+                          f"updates: {est:.2f}s per step; single-threaded C")}
+        log(f"cpu baseline {cpu['value']:.4g} tokens/s ({est:.1f}s per step)")
+        # bit-exactness on the sample: GPU outputs of the last timed step vs the oracle
+        mism = 0
+        for key in ("tokens", "pos", "doc", "mask", "digests"):
+            g = out[key][:n_s].cpu().numpy()
+            if key == "tokens":
+                g = g.view(np.uint32)
+            mism += int((g != ob[key]).sum())
+        mism += int((out["learned"][:n_s].cpu().numpy() != ob["learned"]).sum())
+        mism += int(oi.plan_digest != info["plan_digest"])
+        sample_check = {"updates_compared": n_s, "windows_compared": n_s * B, "mismatches": mism}
+        log(f"bit-exact check on {n_s} updates: {mism} mismatches")
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "packed tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u32",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD_TEXT[args.workload] + ("" if args.scale == 1.0 else f" (scale {args.scale})"),
+                   "docs": corpus.n_docs, "tokens": corpus.n_tokens, "T": T, "B": B, "updates": U,
+                   "real_tokens_per_step": real, "positions_per_step": positions,
+                   "step": "pack_init + pack_cycle + pack_batch(all updates, learned, digests) + pack_destroy"},
+        "roofline": roofline,
+        "roofline_emit": emit_roofline,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+        "copy_ceiling": copy,
+        "bit_exact_sample": sample_check,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

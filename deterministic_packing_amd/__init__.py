@@ -18,7 +18,7 @@ import numpy as np
 
 __all__ = [
     "DpackError", "load_library", "pack_init", "pack_cycle", "pack_batch", "pack_fingerprint",
-    "pack_inspect", "pack_destroy", "pack_strerror", "Packer", "INSPECT", "SYMBOLS",
+    "pack_inspect", "pack_get_timings", "pack_destroy", "pack_strerror", "Packer", "INSPECT", "SYMBOLS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -29,7 +29,11 @@ PACK_OK, PACK_E_ABI, PACK_E_INVAL, PACK_E_NOMEM, PACK_E_HIP = 0, -1, -2, -3, -4
 PACK_E_EXHAUSTED, PACK_E_STATE, PACK_E_RANGE = -5, -6, -7
 
 SYMBOLS = ("pack_init", "pack_cycle", "pack_batch", "pack_fingerprint", "pack_inspect",
-           "pack_destroy", "pack_strerror", "pack_last_error")
+           "pack_get_timings", "pack_destroy", "pack_strerror", "pack_last_error")
+
+PACK_FLAG_TIMING = 1
+PHASES = ("validate", "hash", "keys", "sort", "merge", "pieces", "cut", "windows", "mixture",
+          "cycle", "emit", "learned", "digest", "fingerprint")
 
 # what -> (numpy dtype, length key)
 INSPECT = {
@@ -71,6 +75,10 @@ class PackCycleInfo(C.Structure):
     ]
 
 
+class PackTimings(C.Structure):
+    _fields_ = [("ms", C.c_double * len(PHASES)), ("calls", C.c_uint64 * len(PHASES))]
+
+
 class PackOut(C.Structure):
     _fields_ = [
         ("tokens", C.c_void_p), ("pos", C.c_void_p), ("doc", C.c_void_p), ("mask", C.c_void_p),
@@ -102,6 +110,8 @@ def load_library(path: Optional[str] = None):
     lib.pack_fingerprint.argtypes = [vp, vp, u32, vp]
     lib.pack_inspect.restype = i32
     lib.pack_inspect.argtypes = [vp, u32, vp, C.c_uint64, C.POINTER(C.c_uint64)]
+    lib.pack_get_timings.restype = i32
+    lib.pack_get_timings.argtypes = [vp, C.POINTER(PackTimings), i32]
     lib.pack_destroy.restype = None
     lib.pack_destroy.argtypes = [vp]
     lib.pack_strerror.restype = C.c_char_p
@@ -162,6 +172,13 @@ def pack_inspect(ctx: int, what: str) -> np.ndarray:
     return out[: need.value // np.dtype(dtype).itemsize]
 
 
+def pack_get_timings(ctx: int, reset: bool = False) -> dict:
+    """Phase -> (milliseconds summed, intervals) since the last reset."""
+    t = PackTimings()
+    _check(load_library().pack_get_timings(ctx, C.byref(t), 1 if reset else 0), "pack_get_timings", ctx)
+    return {name: (t.ms[i], int(t.calls[i])) for i, name in enumerate(PHASES)}
+
+
 def pack_destroy(ctx: int) -> None:
     if ctx:
         load_library().pack_destroy(ctx)
@@ -176,7 +193,7 @@ class Packer:
     (or pass ``device_tensors`` to reuse resident ones)."""
 
     def __init__(self, corpus, rank: int = 0, world: int = 1, device: str = "cuda",
-                 device_tensors: Optional[dict] = None, stream=None):
+                 device_tensors: Optional[dict] = None, stream=None, timing: bool = False):
         import torch
 
         self.torch = torch
@@ -195,7 +212,7 @@ class Packer:
         assert self._host["weight"].shape[0] == S
         d = self.dev
         self.cfg = PackConfig(
-            ABI_VERSION, 0,
+            ABI_VERSION, PACK_FLAG_TIMING if timing else 0,
             d["tokens"].data_ptr() if d["tokens"].numel() else None, int(d["tokens"].numel()),
             d["offsets"].data_ptr(), int(d["source"].numel()),
             d["source"].data_ptr(), d["stratum"].data_ptr() if d.get("stratum") is not None else None,
@@ -266,6 +283,9 @@ class Packer:
 
     def inspect(self, what: str) -> np.ndarray:
         return pack_inspect(self.ctx, what)
+
+    def timings(self, reset: bool = False) -> dict:
+        return pack_get_timings(self.ctx, reset)
 
 
 def upload_corpus(corpus, device: str = "cuda") -> dict:

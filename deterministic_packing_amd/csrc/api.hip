@@ -70,8 +70,71 @@ struct InvalError {
 
 }  // namespace
 
+// HIP events around kernel phases, recorded on the context's stream when the
+// context is made with PACK_FLAG_TIMING; resolved in pack_get_timings.
+struct PhaseTimer {
+    bool on = false;
+    std::vector<hipEvent_t> pool;
+    struct Pending {
+        int phase;
+        hipEvent_t a, b;
+    };
+    std::vector<Pending> pending;
+    int open_phase = -1;
+    hipEvent_t open_a = nullptr;
+    double ms[PACK_N_PHASES] = {};
+    uint64_t calls[PACK_N_PHASES] = {};
+
+    hipEvent_t get() {
+        if (!pool.empty()) {
+            hipEvent_t e = pool.back();
+            pool.pop_back();
+            return e;
+        }
+        hipEvent_t e;
+        DP_HIP(hipEventCreate(&e));
+        return e;
+    }
+    void begin(int phase, hipStream_t st) {
+        if (!on) return;
+        open_phase = phase;
+        open_a = get();
+        DP_HIP(hipEventRecord(open_a, st));
+    }
+    void end(hipStream_t st) {
+        if (!on || open_phase < 0) return;
+        hipEvent_t b = get();
+        DP_HIP(hipEventRecord(b, st));
+        pending.push_back({open_phase, open_a, b});
+        open_phase = -1;
+    }
+    void resolve() {
+        for (auto& q : pending) {
+            DP_HIP(hipEventSynchronize(q.b));
+            float t = 0.f;
+            DP_HIP(hipEventElapsedTime(&t, q.a, q.b));
+            ms[q.phase] += t;
+            calls[q.phase] += 1;
+            pool.push_back(q.a);
+            pool.push_back(q.b);
+        }
+        pending.clear();
+    }
+    void destroy() {
+        for (auto& q : pending) {
+            pool.push_back(q.a);
+            pool.push_back(q.b);
+        }
+        pending.clear();
+        if (open_phase >= 0) pool.push_back(open_a);
+        for (hipEvent_t e : pool) (void)hipEventDestroy(e);
+        pool.clear();
+    }
+};
+
 struct pack_ctx {
     pack_config cfg{};
+    PhaseTimer timer;
     std::vector<uint32_t> n_strata, gbase, bp;
     std::vector<uint64_t> weight;
     uint64_t W = 0;
@@ -165,7 +228,7 @@ void h2d(T* dst, const T* src, uint64_t count, hipStream_t st) {
 
 void check_config(const pack_config* cfg) {
     auto bad = [](const char* m) { throw InvalError{m}; };
-    if (cfg->flags != 0) bad("flags must be 0");
+    if (cfg->flags & ~PACK_FLAG_TIMING) bad("unknown flags");
     if (cfg->n_docs < 1 || cfg->n_docs >= (1ull << 31)) bad("n_docs must be in [1, 2^31)");
     if (!cfg->doc_offsets || !cfg->doc_source) bad("doc_offsets and doc_source are required");
     if (cfg->n_tokens && !cfg->tokens) bad("tokens is NULL with n_tokens > 0");
@@ -202,6 +265,7 @@ void release(pack_ctx* c) {
         (void)hipStreamSynchronize(c->st);
         arena_give(c->device, c->arena, c->arena_bytes);
     }
+    c->timer.destroy();
     delete c;
 }
 
@@ -217,7 +281,9 @@ void build_plan(pack_ctx& c) {
     dp::launch_zero_u64(p.stats, 4ull * p.S, st);
 
     // validation first: no kernel reads the corpus through unchecked offsets
+    c.timer.begin(PACK_PHASE_VALIDATE, st);
     dp::launch_validate(p, st);
+    c.timer.end(st);
     uint32_t err = 0;
     d2h(&err, p.err, 1, st);
     DP_HIP(hipStreamSynchronize(st));
@@ -232,17 +298,27 @@ void build_plan(pack_ctx& c) {
     }
 
     // A1 hash + hold-out, A2 compaction, A3 keys
+    c.timer.begin(PACK_PHASE_HASH, st);
     dp::launch_hash(p, st);
+    c.timer.end(st);
+    c.timer.begin(PACK_PHASE_KEYS, st);
     dp::launch_keep_scan(p, st);
+    c.timer.end(st);
     uint32_t n_kept = 0;
     d2h(&n_kept, p.kept_pos + p.n_docs, 1, st);
     DP_HIP(hipStreamSynchronize(st));
     p.n_kept = n_kept;
 
     // A3 sort, A4 merge, A5 piece counts
+    c.timer.begin(PACK_PHASE_SORT, st);
     dp::launch_sort(p, st);
+    c.timer.end(st);
+    c.timer.begin(PACK_PHASE_MERGE, st);
     dp::launch_merge(p, st);
+    c.timer.end(st);
+    c.timer.begin(PACK_PHASE_PIECES, st);
     dp::launch_piece_count(p, st);
+    c.timer.end(st);
     uint32_t n_pieces = 0;
     d2h(&n_pieces, p.piece_start + p.n_kept, 1, st);
     DP_HIP(hipStreamSynchronize(st));
@@ -251,19 +327,27 @@ void build_plan(pack_ctx& c) {
     p.levels = bitlen(p.n_pieces) ? bitlen(p.n_pieces) : 1;
 
     // A5 pieces, next-fit by lifting, windows per source
+    c.timer.begin(PACK_PHASE_PIECES, st);
     dp::launch_pieces(p, st);
+    c.timer.end(st);
+    c.timer.begin(PACK_PHASE_CUT, st);
     dp::launch_lifting(p, st);
     dp::launch_window_count(p, st);
+    c.timer.end(st);
     c.src_win_start.assign(p.S + 1, 0);
     d2h(c.src_win_start.data(), p.src_win_start, p.S + 1, st);
     DP_HIP(hipStreamSynchronize(st));
     p.n_windows = c.src_win_start[p.S];
 
     // window table, A6 mixture, checks
+    c.timer.begin(PACK_PHASE_WINDOWS, st);
     dp::launch_zero_u32(p.win_first, 1, st);  // an empty plan still has win_first[0] = 0
     dp::launch_windows(p, st);
+    c.timer.end(st);
+    c.timer.begin(PACK_PHASE_MIXTURE, st);
     dp::launch_mixture_w(p, c.W, c.nstart, st);
     dp::launch_checks(p, st);
+    c.timer.end(st);
     c.n_upd.assign(p.S, 0);
     c.stats.assign(4ull * p.S, 0);
     c.checks.assign(2, 0);
@@ -328,6 +412,7 @@ int pack_init(const pack_config* cfg, pack_ctx** out) {
         }
         c->cfg = *cfg;
         c->st = static_cast<hipStream_t>(cfg->stream);
+        c->timer.on = (cfg->flags & PACK_FLAG_TIMING) != 0;
         const uint32_t S = cfg->n_sources;
         c->n_strata.resize(S);
         c->gbase.resize(S + 1);
@@ -430,6 +515,7 @@ int pack_cycle(pack_ctx* c, uint32_t cycle, pack_cycle_info* info) {
         for (uint32_t s = 0; s < S; ++s) c->cyc_next[s] = start[s] + U * c->n_upd[s];
         c->cycle = cycle;
         dp::Plan& p = c->p;
+        c->timer.begin(PACK_PHASE_CYCLE, c->st);
         h2d(p.cyc_start, c->cyc_start.data(), S, c->st);
         dp::launch_cycle_sums(p, c->U, c->st);
         uint64_t sums[2] = {0, 0};
@@ -462,6 +548,7 @@ int pack_cycle(pack_ctx* c, uint32_t cycle, pack_cycle_info* info) {
         if (msg.size() > c->dig_cap) throw InvalError{"internal: digest buffer"};
         h2d(c->dig_buf, msg.data(), msg.size(), c->st);
         dp::launch_sha_bytes(c->dig_buf, msg.size(), c->dig_buf + c->dig_cap, c->st);
+        c->timer.end(c->st);
         uint8_t digest[32];
         d2h(digest, c->dig_buf + c->dig_cap, 32, c->st);
         DP_HIP(hipStreamSynchronize(c->st));
@@ -534,9 +621,19 @@ int pack_batch(pack_ctx* c, uint32_t step, uint32_t n_steps, const pack_out* out
             c->err = "too many windows in one call";
             return PACK_E_RANGE;
         }
+        c->timer.begin(PACK_PHASE_EMIT, c->st);
         dp::launch_emit(c->p, a, c->st);
-        if (a.learned) dp::launch_learned(c->p, a, c->st);
-        if (a.digests) dp::launch_window_sha(c->p, a, c->st);
+        c->timer.end(c->st);
+        if (a.learned) {
+            c->timer.begin(PACK_PHASE_LEARNED, c->st);
+            dp::launch_learned(c->p, a, c->st);
+            c->timer.end(c->st);
+        }
+        if (a.digests) {
+            c->timer.begin(PACK_PHASE_DIGEST, c->st);
+            dp::launch_window_sha(c->p, a, c->st);
+            c->timer.end(c->st);
+        }
         return PACK_OK;
     } catch (const dp::HipError& e) {
         return fail_hip(c, e);
@@ -556,7 +653,9 @@ int pack_fingerprint(pack_ctx* c, const uint8_t* digests, uint32_t n_batches, ui
     }
     if (n_batches == 0) return PACK_OK;
     try {
+        c->timer.begin(PACK_PHASE_FINGERPRINT, c->st);
         dp::launch_batch_fp(digests, c->p.B, n_batches, out, c->st);
+        c->timer.end(c->st);
         return PACK_OK;
     } catch (const dp::HipError& e) {
         return fail_hip(c, e);
@@ -610,6 +709,25 @@ int pack_inspect(const pack_ctx* cc, uint32_t what, void* host_dst, uint64_t cap
             DP_HIP(hipStreamSynchronize(c->st));
             uint64_t* o = static_cast<uint64_t*>(host_dst);
             for (uint64_t i = 0; i < count; ++i) o[i] = tmp[i];
+        }
+        return PACK_OK;
+    } catch (const dp::HipError& e) {
+        return fail_hip(c, e);
+    }
+}
+
+int pack_get_timings(pack_ctx* c, pack_timings* out, int reset) {
+    if (!c || !out) return PACK_E_INVAL;
+    try {
+        DP_HIP(hipStreamSynchronize(c->st));
+        c->timer.resolve();
+        for (int i = 0; i < PACK_N_PHASES; ++i) {
+            out->ms[i] = c->timer.ms[i];
+            out->calls[i] = c->timer.calls[i];
+            if (reset) {
+                c->timer.ms[i] = 0;
+                c->timer.calls[i] = 0;
+            }
         }
         return PACK_OK;
     } catch (const dp::HipError& e) {

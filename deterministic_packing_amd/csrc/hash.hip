@@ -41,9 +41,31 @@ __global__ __launch_bounds__(256) void k_validate(Plan p) {
     if (err) atomicOr(p.err, err);
 }
 
+// four tokens starting at a 4-byte aligned address: one global_load_dwordx4
+// (multi-dword global loads need dword alignment only)
+typedef uint32_t u32x4a4 __attribute__((ext_vector_type(4), aligned(4)));
+
+__device__ inline uint64_t quad_terms(const uint32_t* t, uint64_t base, uint64_t L) {
+    uint32_t t0, t1 = 0, t2 = 0, t3 = 0;
+    if (base + 4 <= L) {
+        const u32x4a4 v = *reinterpret_cast<const u32x4a4*>(t + base);
+        t0 = v.x; t1 = v.y; t2 = v.z; t3 = v.w;
+    } else {
+        t0 = t[base];
+        if (base + 1 < L) t1 = t[base + 1];
+        if (base + 2 < L) t2 = t[base + 2];
+    }
+    const uint32_t k0 = (uint32_t)(base + 1) * PHI32;
+    const uint32_t k1 = k0 + PHI32, k2 = k1 + PHI32, k3 = k2 + PHI32;
+    uint64_t S = (uint64_t)(t0 + k0) * (uint64_t)(t1 + k1);
+    if (base + 2 < L) S += (uint64_t)(t2 + k2) * (uint64_t)(t3 + k3);
+    return S;
+}
+
 // One wavefront per document (grid-stride).  Lane l takes the 4-token groups
 // at document-relative indices 4l, 4l+256, …, i.e. two whole pairs each; an
-// odd last token pairs with the virtual token 0 and its key.
+// odd last token pairs with the virtual token 0 and its key.  Two groups per
+// lane are loaded before either is used.
 __global__ __launch_bounds__(256) void k_hash(Plan p, uint32_t lds_bins) {
     extern __shared__ unsigned long long bins[];  // [4][S] when lds_bins
     if (lds_bins) {
@@ -58,19 +80,13 @@ __global__ __launch_bounds__(256) void k_hash(Plan p, uint32_t lds_bins) {
         const uint64_t L = p.offsets[d + 1] - o;
         const uint32_t* t = p.tokens + o;
         uint64_t S = 0;
-        for (uint64_t base = 4ull * lane; base < L; base += 4ull * WAVE) {
-            uint32_t t0 = t[base], t1 = 0, t2 = 0, t3 = 0;
-            if (base + 4 <= L) {
-                t1 = t[base + 1]; t2 = t[base + 2]; t3 = t[base + 3];
-            } else {
-                if (base + 1 < L) t1 = t[base + 1];
-                if (base + 2 < L) t2 = t[base + 2];
-            }
-            const uint32_t k0 = (uint32_t)(base + 1) * PHI32;
-            const uint32_t k1 = k0 + PHI32, k2 = k1 + PHI32, k3 = k2 + PHI32;
-            S += (uint64_t)(t0 + k0) * (uint64_t)(t1 + k1);
-            if (base + 2 < L) S += (uint64_t)(t2 + k2) * (uint64_t)(t3 + k3);
+        uint64_t base = 4ull * lane;
+        for (; base + 4ull * WAVE < L; base += 8ull * WAVE) {
+            const uint64_t s0 = quad_terms(t, base, L);
+            const uint64_t s1 = quad_terms(t, base + 4ull * WAVE, L);
+            S += s0 + s1;
         }
+        if (base < L) S += quad_terms(t, base, L);
         S = wave_sum_u64(S);
         if (lane == 0) {
             const uint64_t h = mix64(S ^ (L * PHI64));
@@ -110,7 +126,7 @@ void launch_hash(const Plan& p, hipStream_t st) {
     const uint32_t lds_bins = p.S <= 256 ? 1u : 0u;
     const size_t lds = lds_bins ? 4ull * p.S * sizeof(uint64_t) : 0;
     uint64_t blocks = (p.n_docs + 3) / 4;
-    if (blocks > 8192) blocks = 8192;
+    if (blocks > 8192) blocks = 8192;  // more blocks than resident slots: finished slots take new blocks
     hipLaunchKernelGGL(k_hash, dim3((uint32_t)blocks), dim3(256), lds, st, p, lds_bins);
     DP_HIP(hipGetLastError());
 }

@@ -2,6 +2,8 @@
 // plan's order checks.  Every step here computes its result as a closed-form
 // rank or a function composition, so the output is independent of thread
 // scheduling and equal to the sequential definition.
+#include <algorithm>
+
 #include "dp_common.h"
 
 namespace dp {
@@ -336,17 +338,36 @@ __global__ __launch_bounds__(256) void k_slots(Plan p, const uint32_t* nstart) {
 }
 
 // ------------------------------------------------------------------ checks
-__global__ __launch_bounds__(256) void k_checks(Plan p) {
-    const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    uint64_t oc = 0, hc = 0;
-    if (i < p.n_kept) oc = mix64((i << 32) ^ (uint64_t)p.order[i]);
-    if (i < p.n_docs && p.keep[i]) hc = p.hash[i];
-    oc = wave_sum_u64(oc);
-    hc = wave_sum_u64(hc);
+// two 64-bit sums for the plan digest; integer sums are order-free, so a
+// grid-stride loop with one atomic per block gives the exact value
+__device__ inline void block_add2(uint64_t x, uint64_t y, uint64_t* dst) {
+    __shared__ uint64_t part[2][256 / WAVE];
+    x = wave_sum_u64(x);
+    y = wave_sum_u64(y);
     if ((threadIdx.x & 63) == 0) {
-        if (oc) atomicAdd((unsigned long long*)&p.checks[0], (unsigned long long)oc);
-        if (hc) atomicAdd((unsigned long long*)&p.checks[1], (unsigned long long)hc);
+        part[0][threadIdx.x / WAVE] = x;
+        part[1][threadIdx.x / WAVE] = y;
     }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint64_t a = 0, b = 0;
+        for (int w = 0; w < 256 / WAVE; ++w) {
+            a += part[0][w];
+            b += part[1][w];
+        }
+        if (a) atomicAdd((unsigned long long*)&dst[0], (unsigned long long)a);
+        if (b) atomicAdd((unsigned long long*)&dst[1], (unsigned long long)b);
+    }
+}
+
+__global__ __launch_bounds__(256) void k_checks(Plan p) {
+    uint64_t oc = 0, hc = 0;
+    const uint64_t n = p.n_docs > p.n_kept ? p.n_docs : p.n_kept;
+    for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (uint64_t)gridDim.x * blockDim.x) {
+        if (i < p.n_kept) oc += mix64((i << 32) ^ (uint64_t)p.order[i]);
+        if (i < p.n_docs && p.keep[i]) hc += p.hash[i];
+    }
+    block_add2(oc, hc, p.checks);
 }
 
 __device__ inline uint64_t window_of(const Plan& p, uint64_t b, uint32_t j) {
@@ -355,19 +376,14 @@ __device__ inline uint64_t window_of(const Plan& p, uint64_t b, uint32_t j) {
 }
 
 __global__ __launch_bounds__(256) void k_cycle_sums(Plan p, uint64_t total) {
-    const uint64_t idx = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
     uint64_t real = 0, learn = 0;
-    if (idx < total) {
+    for (uint64_t idx = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+         idx += (uint64_t)gridDim.x * blockDim.x) {
         const uint64_t gw = window_of(p, idx / p.B, (uint32_t)(idx % p.B));
-        real = p.win_real[gw];
-        learn = p.win_learn[gw];
+        real += p.win_real[gw];
+        learn += p.win_learn[gw];
     }
-    real = wave_sum_u64(real);
-    learn = wave_sum_u64(learn);
-    if ((threadIdx.x & 63) == 0) {
-        if (real) atomicAdd((unsigned long long*)&p.cyc_sums[0], (unsigned long long)real);
-        if (learn) atomicAdd((unsigned long long*)&p.cyc_sums[1], (unsigned long long)learn);
-    }
+    block_add2(real, learn, p.cyc_sums);
 }
 
 inline uint32_t blocks_for(uint64_t n, uint32_t b = 256) { return (uint32_t)((n + b - 1) / b); }
@@ -432,14 +448,15 @@ void launch_mixture_w(Plan& p, uint64_t W, uint32_t* nstart, hipStream_t st) {
 void launch_checks(Plan& p, hipStream_t st) {
     hipLaunchKernelGGL(k_zero_u64, dim3(1), dim3(256), 0, st, p.checks, (uint64_t)2);
     const uint64_t n = p.n_docs > p.n_kept ? p.n_docs : p.n_kept;
-    hipLaunchKernelGGL(k_checks, dim3(blocks_for(n)), dim3(256), 0, st, p);
+    hipLaunchKernelGGL(k_checks, dim3(std::min<uint32_t>(blocks_for(n), 512)), dim3(256), 0, st, p);
     DP_HIP(hipGetLastError());
 }
 
 void launch_cycle_sums(Plan& p, uint32_t U, hipStream_t st) {
     hipLaunchKernelGGL(k_zero_u64, dim3(1), dim3(256), 0, st, p.cyc_sums, (uint64_t)2);
     const uint64_t total = (uint64_t)U * p.B;
-    if (total) hipLaunchKernelGGL(k_cycle_sums, dim3(blocks_for(total)), dim3(256), 0, st, p, total);
+    if (total)
+        hipLaunchKernelGGL(k_cycle_sums, dim3(std::min<uint32_t>(blocks_for(total), 512)), dim3(256), 0, st, p, total);
     DP_HIP(hipGetLastError());
 }
 

@@ -58,6 +58,34 @@ enum {
 
 typedef struct pack_ctx pack_ctx;
 
+/* pack_config.flags: record HIP events around every kernel phase on the
+ * context's stream (read with pack_get_timings).  Changes no output byte. */
+#define PACK_FLAG_TIMING 1u
+
+/* Kernel phases timed under PACK_FLAG_TIMING. */
+enum {
+    PACK_PHASE_VALIDATE = 0, /* corpus validation kernel */
+    PACK_PHASE_HASH,         /* per-document hash and hold-out */
+    PACK_PHASE_KEYS,         /* compaction of kept documents and Philox keys */
+    PACK_PHASE_SORT,         /* radix sort by (group, key) */
+    PACK_PHASE_MERGE,        /* strata merge */
+    PACK_PHASE_PIECES,       /* piece counts, prefix sums and piece table */
+    PACK_PHASE_CUT,          /* next-fit: next pointers, lifting, windows per source */
+    PACK_PHASE_WINDOWS,      /* window table, real and learned positions per window */
+    PACK_PHASE_MIXTURE,      /* apportionment, slot table, order checks */
+    PACK_PHASE_CYCLE,        /* cycle sums and plan digest */
+    PACK_PHASE_EMIT,         /* emission kernel of pack_batch */
+    PACK_PHASE_LEARNED,      /* per-update learned counts of pack_batch */
+    PACK_PHASE_DIGEST,       /* per-window SHA-256 of pack_batch */
+    PACK_PHASE_FINGERPRINT,  /* pack_fingerprint */
+    PACK_N_PHASES
+};
+
+typedef struct pack_timings {
+    double ms[PACK_N_PHASES];      /* summed event-to-event time of each phase */
+    uint64_t calls[PACK_N_PHASES]; /* number of timed intervals summed */
+} pack_timings;
+
 /* Configuration of a packing context.  Limits (PACK_E_INVAL otherwise):
  * 1 ≤ n_docs < 2^31; every document shorter than 2^32 tokens; offsets
  * monotone with doc_offsets[n_docs] ≤ n_tokens; 1 ≤ n_sources ≤ 4096;
@@ -66,7 +94,7 @@ typedef struct pack_ctx pack_ctx;
  * [64, 2^20]; 1 ≤ B ≤ 2^20; world ≥ 1 divides B; rank < world. */
 typedef struct pack_config {
     uint32_t abi_version;          /* DPACK_ABI_VERSION */
-    uint32_t flags;                /* reserved, must be 0 */
+    uint32_t flags;                /* 0, or PACK_FLAG_TIMING */
     const uint32_t *tokens;        /* device [n_tokens] token ids */
     uint64_t n_tokens;
     const uint64_t *doc_offsets;   /* device [n_docs+1]: document d is tokens[off[d], off[d+1]) */
@@ -177,6 +205,12 @@ enum {
  * PACK_E_RANGE (capacity too small), PACK_E_HIP. */
 int pack_inspect(const pack_ctx *ctx, uint32_t what, void *host_dst, uint64_t capacity_bytes,
                  uint64_t *needed);
+
+/* pack_get_timings — synchronize the context's stream and return the phase
+ * times recorded since the last reset (all zero unless the context was made
+ * with PACK_FLAG_TIMING).  reset != 0 clears them afterwards.
+ * Errors: PACK_E_INVAL (NULL), PACK_E_HIP. */
+int pack_get_timings(pack_ctx *ctx, pack_timings *out, int reset);
 
 /* pack_destroy — free the context and its device workspace (synchronizes
  * its stream first).  NULL is a no-op. */
