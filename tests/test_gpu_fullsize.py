@@ -1,0 +1,98 @@
+"""Parity at the workloads' full sizes, in the launch configuration bench.py
+times (every update of the cycle emitted by one pack_batch call with learned
+counts and digests).  The oracle computes the whole plan; outputs are compared
+on sampled windows (content and digests), whole sampled batches
+(fingerprints), every learned count, and checked on the GPU for properties that
+hold everywhere (padding at the end, position ids, masks agreeing with the
+learned counts)."""
+import numpy as np
+import pytest
+
+import deterministic_packing_amd as dp
+import oracle
+from synth import make_corpus
+
+from _gpu_parity import compare_cycle, compare_plan, say
+
+pytestmark = pytest.mark.gpu
+
+_CACHE = {}
+
+
+def _setup(name):
+    if name not in _CACHE:
+        _CACHE.clear()  # one workload's buffers at a time
+        import torch
+        torch.cuda.empty_cache()
+        say("generate", name)
+        c = make_corpus(name)
+        say("oracle plan", name, c.n_docs, "docs", c.n_tokens, "tokens")
+        op = oracle.Plan(c)
+        oi = op.cycle(0)
+        say("gpu plan", name)
+        tensors = dp.upload_corpus(c)
+        pk = dp.Packer(c, device_tensors=tensors)
+        gi = pk.cycle(0)
+        _CACHE[name] = (c, op, oi, tensors, pk, gi)
+    return _CACHE[name]
+
+
+# (workload, max updates emitted in one call: the bench's whole cycle where it fits)
+FULL = [("tiny", None), ("pretrain", None), ("sft", None), ("long", None), ("full", 48)]
+
+
+@pytest.mark.parametrize("name,cap", FULL)
+def test_full_size_parity(name, cap):
+    import torch
+    c, op, oi, tensors, pk, gi = _setup(name)
+    say("compare plan", name)
+    compare_plan(pk, op)
+    compare_cycle(gi, oi, op)
+    U = oi.n_updates
+    n = U if cap is None else min(cap, U)
+    B, T = c.B, c.T
+    r = np.random.default_rng(7)
+    # emit in one call per contiguous range (bench: the whole cycle in one call)
+    ranges = [(0, n)] if cap is None else [(0, n // 2), (U - n // 2, n // 2)]
+    outs = []
+    for s0, cnt in ranges:
+        say("emit", name, "steps", s0, "+", cnt)
+        outs.append((s0, pk.batch(s0, cnt)))
+    torch.cuda.synchronize()
+    for s0, g in outs:
+        cnt = g["tokens"].shape[0]
+        # learned counts of every update in the call
+        learned = g["learned"].cpu().numpy()
+        for i in range(cnt):
+            exp = sum(int(op.win_learn[op.window_of(s0 + i, j)]) for j in range(B))
+            assert learned[i] == exp, (name, s0 + i)
+        # properties of every window of the call, on the GPU
+        doc = g["doc"]
+        real = doc >= 0
+        n_real = real.sum(dim=2)
+        idx = torch.arange(T, device=doc.device).view(1, 1, T)
+        assert bool((real == (idx < n_real.unsqueeze(2))).all()), "padding only at the end of a window"
+        assert bool((g["pos"][~real] == 0).all()) and bool((g["mask"][~real] == 0).all())
+        assert bool(((g["tokens"] == c.pad_token) | real).all())
+        assert bool((g["mask"].sum(dim=(1, 2)).cpu() == g["learned"].cpu()).all()), "learned = sum of mask"
+        exp_real = np.array([[int(op.win_real[op.window_of(s0 + i, j)]) for j in range(B)] for i in range(cnt)])
+        assert np.array_equal(n_real.cpu().numpy(), exp_real)
+        # sampled windows: whole content and digest vs the oracle
+        picks = [(int(r.integers(cnt)), int(r.integers(B))) for _ in range(48)] + [(0, 0), (cnt - 1, B - 1)]
+        for i, j in picks:
+            gw = op.window_of(s0 + i, j)
+            tok, pos, dc, mask = op.emit_window(gw)
+            assert np.array_equal(g["tokens"][i, j].cpu().numpy().view(np.uint32), tok), (name, s0 + i, j)
+            assert np.array_equal(g["pos"][i, j].cpu().numpy(), pos)
+            assert np.array_equal(g["doc"][i, j].cpu().numpy(), dc)
+            assert np.array_equal(g["mask"][i, j].cpu().numpy(), mask)
+            assert g["digests"][i, j].cpu().numpy().tobytes() == oracle.window_digest(tok, pos, dc, mask)
+        # whole sampled batches: every window digest and the batch fingerprint
+        for i in sorted({0, cnt - 1}):
+            o = op.batch(s0 + i, 1)
+            assert np.array_equal(g["digests"][i].cpu().numpy(), o["digests"][0]), (name, s0 + i)
+            fp = pk.fingerprint(g["digests"][i:i + 1]).cpu().numpy()[0].tobytes()
+            assert fp == oracle.batch_fingerprint(o["digests"][0])
+    outs.clear()
+    _CACHE.clear()
+    torch.cuda.empty_cache()
