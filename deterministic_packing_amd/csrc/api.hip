@@ -144,6 +144,7 @@ struct pack_ctx {
     char* arena = nullptr;
     size_t arena_bytes = 0;
     uint32_t* nstart = nullptr;
+    uint32_t* hash_first = nullptr;  // tile -> first document table of the hash
     uint8_t* dig_buf = nullptr;
     size_t dig_cap = 0;
     std::vector<uint64_t> src_win_start, stats, checks, src_piece_start;
@@ -179,6 +180,7 @@ size_t carve(pack_ctx& c, char* base) {
     p.bp = k.take<uint32_t>(S);
     p.group = k.take<uint32_t>(D);
     p.hash = k.take<uint64_t>(D);
+    c.hash_first = k.take<uint32_t>(dp::hash_tile_count(p.n_tokens) + 2);
     p.keep = k.take<uint8_t>(D);
     p.kept_pos = k.take<uint32_t>(D + 1);
     p.stats = k.take<uint64_t>(4 * S);
@@ -285,7 +287,10 @@ void build_plan(pack_ctx& c) {
     dp::launch_validate(p, st);
     c.timer.end(st);
     uint32_t err = 0;
+    uint64_t span[2] = {0, 0};  // offsets[0] and offsets[n_docs]: the tokens the documents cover
     d2h(&err, p.err, 1, st);
+    d2h(&span[0], p.offsets, 1, st);
+    d2h(&span[1], p.offsets + p.n_docs, 1, st);
     DP_HIP(hipStreamSynchronize(st));
     if (err) {
         std::string m = "invalid corpus:";
@@ -299,7 +304,8 @@ void build_plan(pack_ctx& c) {
 
     // A1 hash + hold-out, A2 compaction, A3 keys
     c.timer.begin(PACK_PHASE_HASH, st);
-    dp::launch_hash(p, st);
+    dp::launch_hash(p, span[0], span[1], p.gpre /* per-document sums; gpre is free until the merge */,
+                    c.hash_first, st);
     c.timer.end(st);
     c.timer.begin(PACK_PHASE_KEYS, st);
     dp::launch_keep_scan(p, st);

@@ -9,6 +9,8 @@
 // SplitMix64 output function over S xor L·0x9E3779B97F4A7C15.  A document is
 // held iff floor(h·10000/2^64) < bp of its source, kept iff not held and
 // non-empty.
+#include <algorithm>
+
 #include "dp_common.h"
 
 namespace dp {
@@ -41,69 +43,143 @@ __global__ __launch_bounds__(256) void k_validate(Plan p) {
     if (err) atomicOr(p.err, err);
 }
 
-// four tokens starting at a 4-byte aligned address: one global_load_dwordx4
-// (multi-dword global loads need dword alignment only)
+// ------------------------------------------------------------------ flat hash
+// The tokens of all documents form one contiguous range [off[0], off[D]).  It
+// is cut into tiles of HT tokens; a thread takes 16 contiguous tokens, so the
+// whole corpus streams through once, coalesced and balanced whatever the
+// document lengths.  A token at document-relative index r (even) adds the NH
+// term (t_r + k_r)·(t_{r+1} + k_{r+1}) to its document's sum, with t_L = 0 for
+// an odd length L.  Per-document partial sums are combined inside a wavefront
+// by a segmented scan (documents are in token order) and added to S[d] with one
+// 64-bit atomic per document and wavefront: integer addition is order-free, so
+// the sum is exact.  k_hash_final then mixes and decides the hold-out.
+constexpr uint32_t HT = 4096;  // tokens per tile: 256 threads x 16
+
 typedef uint32_t u32x4a4 __attribute__((ext_vector_type(4), aligned(4)));
 
-__device__ inline uint64_t quad_terms(const uint32_t* t, uint64_t base, uint64_t L) {
-    uint32_t t0, t1 = 0, t2 = 0, t3 = 0;
-    if (base + 4 <= L) {
-        const u32x4a4 v = *reinterpret_cast<const u32x4a4*>(t + base);
-        t0 = v.x; t1 = v.y; t2 = v.z; t3 = v.w;
-    } else {
-        t0 = t[base];
-        if (base + 1 < L) t1 = t[base + 1];
-        if (base + 2 < L) t2 = t[base + 2];
+// first[t] = the document containing token base + t·HT (clamped to D−1)
+__global__ __launch_bounds__(256) void k_tile_first_doc(Plan p, uint64_t base, uint64_t ntiles, uint32_t* first) {
+    const uint64_t t = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t > ntiles) return;
+    const uint64_t x = base + t * HT;
+    // number of j in [1, D] with off[j] <= x: the containing document (empty ones skipped)
+    uint64_t lo = 1, hi = p.n_docs + 1;
+    while (lo < hi) {
+        const uint64_t mid = (lo + hi) >> 1;
+        if (p.offsets[mid] <= x) lo = mid + 1;
+        else hi = mid;
     }
-    const uint32_t k0 = (uint32_t)(base + 1) * PHI32;
-    const uint32_t k1 = k0 + PHI32, k2 = k1 + PHI32, k3 = k2 + PHI32;
-    uint64_t S = (uint64_t)(t0 + k0) * (uint64_t)(t1 + k1);
-    if (base + 2 < L) S += (uint64_t)(t2 + k2) * (uint64_t)(t3 + k3);
-    return S;
+    uint64_t d = lo - 1;
+    if (d > p.n_docs - 1) d = p.n_docs - 1;
+    first[t] = (uint32_t)d;
 }
 
-// One wavefront per document (grid-stride).  Lane l takes the 4-token groups
-// at document-relative indices 4l, 4l+256, …, i.e. two whole pairs each; an
-// odd last token pairs with the virtual token 0 and its key.  Two groups per
-// lane are loaded before either is used.
-__global__ __launch_bounds__(256) void k_hash(Plan p, uint32_t lds_bins) {
+__device__ inline uint64_t pair_term(uint32_t a, uint32_t b, uint64_t r) {
+    const uint32_t k0 = (uint32_t)(r + 1) * PHI32;
+    return (uint64_t)(a + k0) * (uint64_t)(b + k0 + PHI32);
+}
+
+__global__ __launch_bounds__(256) void k_hash_flat(Plan p, const uint32_t* first, uint64_t base, uint64_t end,
+                                                   uint64_t ntiles, uint64_t* S) {
+    const uint32_t lane = lane_id();
+    for (uint64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+        const uint64_t t0 = base + tile * HT + 16ull * threadIdx.x;  // this thread's first token
+        const bool active = t0 < end;
+        uint32_t fd = 0xFFFFFFFFu, ld = 0xFFFFFFFFu;
+        uint64_t v1 = 0, v2 = 0;
+        if (active) {
+            uint32_t x[17];
+            if (t0 + 16 <= end) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const u32x4a4 v = *reinterpret_cast<const u32x4a4*>(p.tokens + t0 + 4 * q);
+                    x[4 * q] = v.x; x[4 * q + 1] = v.y; x[4 * q + 2] = v.z; x[4 * q + 3] = v.w;
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 16; ++j) x[j] = (t0 + j < end) ? p.tokens[t0 + j] : 0u;
+            }
+            x[16] = (t0 + 16 < end) ? p.tokens[t0 + 16] : 0u;
+            // document of t0: search between the tile's first document and the next tile's
+            uint64_t lo = first[tile], hi = first[tile + 1] + 1;  // d in [lo, hi)
+            while (hi - lo > 1) {
+                const uint64_t mid = (lo + hi) >> 1;
+                if (p.offsets[mid] <= t0) lo = mid;
+                else hi = mid;
+            }
+            uint32_t cur = (uint32_t)lo;
+            while (p.offsets[cur + 1] <= t0) ++cur;  // skip empty documents
+            fd = cur;
+            uint64_t ob = p.offsets[cur], nb = p.offsets[cur + 1];
+            uint64_t acc = 0;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const uint64_t pos = t0 + j;
+                if (pos < end) {
+                    if (pos >= nb) {  // the next document starts: flush the finished one
+                        if (cur == fd) v1 = acc;
+                        else atomicAdd((unsigned long long*)&S[cur], (unsigned long long)acc);
+                        acc = 0;
+                        do {
+                            ++cur;
+                            ob = nb;
+                            nb = p.offsets[cur + 1];
+                        } while (pos >= nb);
+                    }
+                    const uint64_t r = pos - ob;
+                    if ((r & 1) == 0) acc += pair_term(x[j], pos + 1 < nb ? x[j + 1] : 0u, r);
+                }
+            }
+            if (cur == fd) v1 = acc;
+            else {
+                ld = cur;
+                v2 = acc;
+            }
+        }
+        // the last document's part joins the next lane's first document when they match
+        const uint32_t fd_next = __shfl_down(fd, 1, WAVE);
+        if (ld != 0xFFFFFFFFu && (lane == WAVE - 1 || fd_next != ld))
+            atomicAdd((unsigned long long*)&S[ld], (unsigned long long)v2);
+        const uint32_t ld_prev = __shfl_up(ld, 1, WAVE);
+        const uint64_t v2_prev = __shfl_up(v2, 1, WAVE);
+        if (lane > 0 && ld_prev != 0xFFFFFFFFu && ld_prev == fd) v1 += v2_prev;
+        // segmented inclusive scan of v1 by fd (fd is nondecreasing across lanes)
+#pragma unroll
+        for (int o = 1; o < WAVE; o <<= 1) {
+            const uint64_t y = __shfl_up(v1, o, WAVE);
+            const uint32_t fy = __shfl_up(fd, o, WAVE);
+            if (lane >= (uint32_t)o && fy == fd) v1 += y;
+        }
+        if (fd != 0xFFFFFFFFu && (lane == WAVE - 1 || fd_next != fd))
+            atomicAdd((unsigned long long*)&S[fd], (unsigned long long)v1);
+    }
+}
+
+// h = mix64(S xor L·φ64); held iff floor(h·10000/2^64) < bp; kept iff not held
+// and non-empty; per-source statistics in LDS, one atomic per block and bin.
+__global__ __launch_bounds__(256) void k_hash_final(Plan p, const uint64_t* S, uint32_t lds_bins) {
     extern __shared__ unsigned long long bins[];  // [4][S] when lds_bins
     if (lds_bins) {
         for (uint32_t i = threadIdx.x; i < 4 * p.S; i += blockDim.x) bins[i] = 0;
         __syncthreads();
     }
-    const uint32_t lane = lane_id();
-    const uint64_t w0 = (uint64_t)__builtin_amdgcn_readfirstlane(blockIdx.x * (blockDim.x / WAVE) + threadIdx.x / WAVE);
-    const uint64_t nw = (uint64_t)gridDim.x * (blockDim.x / WAVE);
-    for (uint64_t d = w0; d < p.n_docs; d += nw) {
-        const uint64_t o = p.offsets[d];
-        const uint64_t L = p.offsets[d + 1] - o;
-        const uint32_t* t = p.tokens + o;
-        uint64_t S = 0;
-        uint64_t base = 4ull * lane;
-        for (; base + 4ull * WAVE < L; base += 8ull * WAVE) {
-            const uint64_t s0 = quad_terms(t, base, L);
-            const uint64_t s1 = quad_terms(t, base + 4ull * WAVE, L);
-            S += s0 + s1;
-        }
-        if (base < L) S += quad_terms(t, base, L);
-        S = wave_sum_u64(S);
-        if (lane == 0) {
-            const uint64_t h = mix64(S ^ (L * PHI64));
-            const uint32_t s = p.source[d];
-            const bool held = __umul64hi(h, 10000ull) < (uint64_t)p.bp[s];
-            const bool keep = !held && L > 0;
-            p.hash[d] = h;
-            p.keep[d] = keep ? 1 : 0;
-            if (held || keep) {
-                const uint32_t slot = (held ? 2u : 0u) * p.S + s;
-                if (lds_bins) {
-                    atomicAdd(&bins[slot], 1ull);
-                    atomicAdd(&bins[slot + p.S], (unsigned long long)L);
-                } else {
-                    atomicAdd((unsigned long long*)&p.stats[slot], 1ull);
-                    atomicAdd((unsigned long long*)&p.stats[slot + p.S], (unsigned long long)L);
-                }
+    for (uint64_t d = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; d < p.n_docs;
+         d += (uint64_t)gridDim.x * blockDim.x) {
+        const uint64_t L = p.offsets[d + 1] - p.offsets[d];
+        const uint64_t h = mix64(S[d] ^ (L * PHI64));
+        const uint32_t s = p.source[d];
+        const bool held = __umul64hi(h, 10000ull) < (uint64_t)p.bp[s];
+        const bool keep = !held && L > 0;
+        p.hash[d] = h;
+        p.keep[d] = keep ? 1 : 0;
+        if (held || keep) {
+            const uint32_t slot = (held ? 2u : 0u) * p.S + s;
+            if (lds_bins) {
+                atomicAdd(&bins[slot], 1ull);
+                atomicAdd(&bins[slot + p.S], (unsigned long long)L);
+            } else {
+                atomicAdd((unsigned long long*)&p.stats[slot], 1ull);
+                atomicAdd((unsigned long long*)&p.stats[slot + p.S], (unsigned long long)L);
             }
         }
     }
@@ -114,6 +190,11 @@ __global__ __launch_bounds__(256) void k_hash(Plan p, uint32_t lds_bins) {
     }
 }
 
+__global__ __launch_bounds__(256) void k_zero(uint64_t* a, uint64_t n) {
+    for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (uint64_t)gridDim.x * blockDim.x)
+        a[i] = 0;
+}
+
 }  // namespace
 
 void launch_validate(const Plan& p, hipStream_t st) {
@@ -122,13 +203,25 @@ void launch_validate(const Plan& p, hipStream_t st) {
     DP_HIP(hipGetLastError());
 }
 
-void launch_hash(const Plan& p, hipStream_t st) {
+// base/end: offsets[0] and offsets[n_docs] (read back after validation);
+// S: [n_docs] sums, first: [ntiles + 1] tile table (workspace)
+void launch_hash(const Plan& p, uint64_t base, uint64_t end, uint64_t* S, uint32_t* first, hipStream_t st) {
+    const uint64_t ntiles = end > base ? (end - base + HT - 1) / HT : 0;
+    hipLaunchKernelGGL(k_zero, dim3((uint32_t)std::min<uint64_t>((p.n_docs + 255) / 256, 2048)), dim3(256), 0, st, S,
+                       p.n_docs);
+    if (ntiles) {
+        hipLaunchKernelGGL(k_tile_first_doc, dim3((uint32_t)((ntiles + 1 + 255) / 256)), dim3(256), 0, st, p, base,
+                           ntiles, first);
+        hipLaunchKernelGGL(k_hash_flat, dim3((uint32_t)std::min<uint64_t>(ntiles, 16384)), dim3(256), 0, st, p,
+                           (const uint32_t*)first, base, end, ntiles, S);
+    }
     const uint32_t lds_bins = p.S <= 256 ? 1u : 0u;
     const size_t lds = lds_bins ? 4ull * p.S * sizeof(uint64_t) : 0;
-    uint64_t blocks = (p.n_docs + 3) / 4;
-    if (blocks > 8192) blocks = 8192;  // more blocks than resident slots: finished slots take new blocks
-    hipLaunchKernelGGL(k_hash, dim3((uint32_t)blocks), dim3(256), lds, st, p, lds_bins);
+    hipLaunchKernelGGL(k_hash_final, dim3((uint32_t)std::min<uint64_t>((p.n_docs + 255) / 256, 1024)), dim3(256), lds,
+                       st, p, (const uint64_t*)S, lds_bins);
     DP_HIP(hipGetLastError());
 }
+
+uint64_t hash_tile_count(uint64_t n_tokens) { return (n_tokens + HT - 1) / HT; }
 
 }  // namespace dp
