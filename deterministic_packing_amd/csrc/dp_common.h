@@ -139,6 +139,14 @@ struct Plan {
     uint64_t cap_pieces;          // allocation bound for pieces
 };
 
+// Global window index of slot j of update b of the current cycle: source s
+// = slot_src[j] contributes its (slot_k[j])-th window of the update, i.e. window
+// cyc_start[s] + b·n_s + slot_k[j] of its stream.
+__device__ inline uint64_t window_of(const Plan& p, uint64_t b, uint32_t j) {
+    const uint32_t s = p.slot_src[j];
+    return p.src_win_start[s] + p.cyc_start[s] + b * p.n_upd[s] + p.slot_k[j];
+}
+
 // ---------------------------------------------------------------- SHA-256 (FIPS 180-4)
 __host__ __device__ inline uint32_t sha_k(int t) {
     constexpr uint32_t K[64] = {
@@ -219,6 +227,7 @@ struct EmitArgs {
 void launch_emit(const Plan& p, const EmitArgs& a, hipStream_t st);
 void launch_learned(const Plan& p, const EmitArgs& a, hipStream_t st);
 void launch_window_sha(const Plan& p, const EmitArgs& a, hipStream_t st);
+void launch_emit_sha(const Plan& p, const EmitArgs& a, hipStream_t st);
 void launch_batch_fp(const uint8_t* digests, uint32_t B, uint32_t n_batches, uint8_t* out, hipStream_t st);
 void launch_sha_bytes(const uint8_t* msg, uint64_t len, uint8_t* out, hipStream_t st);
 

@@ -20,11 +20,6 @@ namespace {
 constexpr int EB = 256;      // threads per window
 constexpr int ECAP = 512;    // pieces staged in LDS
 
-__device__ inline uint64_t window_of(const Plan& p, uint64_t b, uint32_t j) {
-    const uint32_t s = p.slot_src[j];
-    return p.src_win_start[s] + p.cyc_start[s] + b * p.n_upd[s] + p.slot_k[j];
-}
-
 struct PieceView {
     uint32_t woff, doc, mfrom;
     uint64_t src;

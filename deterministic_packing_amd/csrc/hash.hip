@@ -45,7 +45,7 @@ __global__ __launch_bounds__(256) void k_validate(Plan p) {
 
 // ------------------------------------------------------------------ flat hash
 // The tokens of all documents form one contiguous range [off[0], off[D]).  It
-// is cut into tiles of HT tokens; a thread takes 16 contiguous tokens, so the
+// is cut into tiles of HT tokens; a thread takes TPT contiguous tokens, so the
 // whole corpus streams through once, coalesced and balanced whatever the
 // document lengths.  A token at document-relative index r (even) adds the NH
 // term (t_r + k_r)·(t_{r+1} + k_{r+1}) to its document's sum, with t_L = 0 for
@@ -53,7 +53,8 @@ __global__ __launch_bounds__(256) void k_validate(Plan p) {
 // by a segmented scan (documents are in token order) and added to S[d] with one
 // 64-bit atomic per document and wavefront: integer addition is order-free, so
 // the sum is exact.  k_hash_final then mixes and decides the hold-out.
-constexpr uint32_t HT = 4096;  // tokens per tile: 256 threads x 16
+constexpr uint32_t TPT = 16;         // contiguous tokens per thread
+constexpr uint32_t HT = 256 * TPT;   // tokens per tile (one 256-thread block)
 
 typedef uint32_t u32x4a4 __attribute__((ext_vector_type(4), aligned(4)));
 
@@ -79,41 +80,60 @@ __device__ inline uint64_t pair_term(uint32_t a, uint32_t b, uint64_t r) {
     return (uint64_t)(a + k0) * (uint64_t)(b + k0 + PHI32);
 }
 
+// The document offsets a tile needs are staged in LDS once per tile, so no
+// thread waits on a dependent global load to find its documents (tiles with
+// more than OCAP documents read them from global memory instead).
+constexpr uint32_t OCAP = 1024;
+
+struct Offs {
+    const uint64_t* g;   // global offsets
+    const uint64_t* l;   // LDS copy of offsets[d0 .. d0 + n)
+    uint64_t d0;
+    bool staged;
+    __device__ inline uint64_t operator[](uint64_t d) const { return staged ? l[d - d0] : g[d]; }
+};
+
 __global__ __launch_bounds__(256) void k_hash_flat(Plan p, const uint32_t* first, uint64_t base, uint64_t end,
                                                    uint64_t ntiles, uint64_t* S) {
+    __shared__ uint64_t s_off[OCAP + 1];
     const uint32_t lane = lane_id();
     for (uint64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-        const uint64_t t0 = base + tile * HT + 16ull * threadIdx.x;  // this thread's first token
+        const uint64_t t0 = base + tile * HT + (uint64_t)TPT * threadIdx.x;  // this thread's first token
+        const uint64_t d_lo = first[tile], d_hi = first[tile + 1];  // documents of the tile
+        Offs off{p.offsets, s_off, d_lo, d_hi - d_lo + 2 <= OCAP + 1};
+        __syncthreads();  // the previous tile's readers are done with s_off
+        if (off.staged)
+            for (uint64_t i = threadIdx.x; i < d_hi - d_lo + 2; i += blockDim.x) s_off[i] = p.offsets[d_lo + i];
+        __syncthreads();
         const bool active = t0 < end;
         uint32_t fd = 0xFFFFFFFFu, ld = 0xFFFFFFFFu;
         uint64_t v1 = 0, v2 = 0;
         if (active) {
-            uint32_t x[17];
-            if (t0 + 16 <= end) {
+            uint32_t x[TPT + 1];
+            if (t0 + TPT <= end) {
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
+                for (uint32_t q = 0; q < TPT / 4; ++q) {
                     const u32x4a4 v = *reinterpret_cast<const u32x4a4*>(p.tokens + t0 + 4 * q);
                     x[4 * q] = v.x; x[4 * q + 1] = v.y; x[4 * q + 2] = v.z; x[4 * q + 3] = v.w;
                 }
             } else {
 #pragma unroll
-                for (int j = 0; j < 16; ++j) x[j] = (t0 + j < end) ? p.tokens[t0 + j] : 0u;
+                for (uint32_t j = 0; j < TPT; ++j) x[j] = (t0 + j < end) ? p.tokens[t0 + j] : 0u;
             }
-            x[16] = (t0 + 16 < end) ? p.tokens[t0 + 16] : 0u;
+            x[TPT] = (t0 + TPT < end) ? p.tokens[t0 + TPT] : 0u;
             // document of t0: search between the tile's first document and the next tile's
-            uint64_t lo = first[tile], hi = first[tile + 1] + 1;  // d in [lo, hi)
+            uint64_t lo = d_lo, hi = d_hi + 1;  // d in [lo, hi)
             while (hi - lo > 1) {
                 const uint64_t mid = (lo + hi) >> 1;
-                if (p.offsets[mid] <= t0) lo = mid;
+                if (off[mid] <= t0) lo = mid;
                 else hi = mid;
             }
             uint32_t cur = (uint32_t)lo;
-            while (p.offsets[cur + 1] <= t0) ++cur;  // skip empty documents
             fd = cur;
-            uint64_t ob = p.offsets[cur], nb = p.offsets[cur + 1];
+            uint64_t ob = off[cur], nb = off[cur + 1];
             uint64_t acc = 0;
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
+            for (uint32_t j = 0; j < TPT; ++j) {
                 const uint64_t pos = t0 + j;
                 if (pos < end) {
                     if (pos >= nb) {  // the next document starts: flush the finished one
@@ -123,7 +143,7 @@ __global__ __launch_bounds__(256) void k_hash_flat(Plan p, const uint32_t* first
                         do {
                             ++cur;
                             ob = nb;
-                            nb = p.offsets[cur + 1];
+                            nb = off[cur + 1];
                         } while (pos >= nb);
                     }
                     const uint64_t r = pos - ob;

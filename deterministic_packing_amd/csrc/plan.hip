@@ -370,11 +370,6 @@ __global__ __launch_bounds__(256) void k_checks(Plan p) {
     block_add2(oc, hc, p.checks);
 }
 
-__device__ inline uint64_t window_of(const Plan& p, uint64_t b, uint32_t j) {
-    const uint32_t s = p.slot_src[j];
-    return p.src_win_start[s] + p.cyc_start[s] + b * p.n_upd[s] + p.slot_k[j];
-}
-
 __global__ __launch_bounds__(256) void k_cycle_sums(Plan p, uint64_t total) {
     uint64_t real = 0, learn = 0;
     for (uint64_t idx = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
