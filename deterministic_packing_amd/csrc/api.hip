@@ -200,6 +200,7 @@ size_t carve(pack_ctx& c, char* base) {
     p.pc_off = k.take<uint32_t>(P);
     p.pc_len = k.take<uint32_t>(P);
     p.pc_woff = k.take<uint32_t>(P);
+    p.pc_emit = k.take<uint4>(P);
     p.pc_pre = k.take<uint64_t>(P + 1);
     p.src_piece_start = k.take<uint64_t>(S + 1);
     p.jump = k.take<uint32_t>((uint64_t)bitlen(P) * P);
@@ -627,17 +628,23 @@ int pack_batch(pack_ctx* c, uint32_t step, uint32_t n_steps, const pack_out* out
             c->err = "too many windows in one call";
             return PACK_E_RANGE;
         }
-        c->timer.begin(PACK_PHASE_EMIT, c->st);
-        dp::launch_emit(c->p, a, c->st);
-        c->timer.end(c->st);
+        if (a.digests && dp::emit_sha_fits(a)) {  // emission beside the digests, one kernel
+            c->timer.begin(PACK_PHASE_DIGEST, c->st);
+            dp::launch_emit_sha(c->p, a, c->st);
+            c->timer.end(c->st);
+        } else {
+            c->timer.begin(PACK_PHASE_EMIT, c->st);
+            dp::launch_emit(c->p, a, c->st);
+            c->timer.end(c->st);
+            if (a.digests) {
+                c->timer.begin(PACK_PHASE_DIGEST, c->st);
+                dp::launch_window_sha(c->p, a, c->st);
+                c->timer.end(c->st);
+            }
+        }
         if (a.learned) {
             c->timer.begin(PACK_PHASE_LEARNED, c->st);
             dp::launch_learned(c->p, a, c->st);
-            c->timer.end(c->st);
-        }
-        if (a.digests) {
-            c->timer.begin(PACK_PHASE_DIGEST, c->st);
-            dp::launch_window_sha(c->p, a, c->st);
             c->timer.end(c->st);
         }
         return PACK_OK;

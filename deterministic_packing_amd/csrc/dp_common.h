@@ -117,6 +117,7 @@ struct Plan {
     uint32_t* pc_off;             // [P]
     uint32_t* pc_len;             // [P]
     uint32_t* pc_woff;            // [P]
+    uint4* pc_emit;               // [P] emission view: (u64 token index of window position 0, doc, mask start)
     uint64_t* pc_pre;             // [P+1] token prefix over pieces
     uint64_t* src_piece_start;    // [S+1]
     uint32_t* jump;               // [L][P] lifting table
@@ -227,6 +228,7 @@ struct EmitArgs {
 void launch_emit(const Plan& p, const EmitArgs& a, hipStream_t st);
 void launch_learned(const Plan& p, const EmitArgs& a, hipStream_t st);
 void launch_window_sha(const Plan& p, const EmitArgs& a, hipStream_t st);
+bool emit_sha_fits(const EmitArgs& a);                 // launch_emit_sha applies (one workgroup per CU)
 void launch_emit_sha(const Plan& p, const EmitArgs& a, hipStream_t st);
 void launch_batch_fp(const uint8_t* digests, uint32_t B, uint32_t n_batches, uint8_t* out, hipStream_t st);
 void launch_sha_bytes(const uint8_t* msg, uint64_t len, uint8_t* out, hipStream_t st);

@@ -221,7 +221,11 @@ __global__ __launch_bounds__(256) void k_windows(Plan p) {
 }
 
 // offsets of pieces in their window; real and learned positions per window
-// (Linnet Training: a prompted example learns only its completion).
+// (Linnet Training: a prompted example learns only its completion).  Also the
+// emission view of each piece: window position t of the piece holds token
+// base + t (base = off[d] + o − f, modulo 2^64) and learns iff t ≥ mfrom
+// (mfrom = f + min(max(prompt_len − o, 0), len), so t < f + len never learns
+// when the prompt covers the piece).
 __global__ __launch_bounds__(256) void k_window_stats(Plan p) {
     const uint64_t gw = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (gw >= p.n_windows) return;
@@ -235,10 +239,13 @@ __global__ __launch_bounds__(256) void k_window_stats(Plan p) {
     uint32_t f = 0, learn = 0;
     for (uint32_t q = q0; q < q1; ++q) {
         p.pc_woff[q] = f;
-        const uint32_t o = p.pc_off[q], len = p.pc_len[q];
-        const uint32_t pl = p.prompt_len ? p.prompt_len[p.pc_doc[q]] : 0u;
+        const uint32_t o = p.pc_off[q], len = p.pc_len[q], d = p.pc_doc[q];
+        const uint32_t pl = p.prompt_len ? p.prompt_len[d] : 0u;
         const uint64_t from = o > pl ? o : pl;
         if ((uint64_t)o + len > from) learn += (uint32_t)((uint64_t)o + len - from);
+        const uint64_t base = p.offsets[d] + o - f;
+        const uint32_t lead = (uint32_t)(from - o < len ? from - o : len);  // prompt positions of the piece
+        p.pc_emit[q] = make_uint4((uint32_t)base, (uint32_t)(base >> 32), d, f + lead);
         f += len;
     }
     p.win_real[gw] = f;

@@ -63,6 +63,7 @@ constexpr uint32_t SPIECES = SCH * 4;    // 16-byte pieces per chunk per window
 constexpr uint32_t SGRP = 64 / SPIECES;  // windows per load instruction
 constexpr uint32_t SLOADS = 64 / SGRP;   // load instructions per chunk
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // native vector: stays in VGPRs
+typedef uint32_t u32x4a4 __attribute__((ext_vector_type(4), aligned(4)));  // 16-byte load, 4-byte aligned
 
 // Loads chunk c of windows w0 .. w0+63 for this lane's (group, piece).  Lanes
 // past the last window or past the record's last block load a clamped, valid
@@ -99,28 +100,50 @@ __device__ __forceinline__ void load_chunk(u32x4 (&stage)[SLOADS], const EmitArg
 // with more waves than SIMDs use the 64 KB variant instead.
 constexpr uint32_t SWAVES = 4;  // waves per workgroup
 
-template <bool SPREAD>
-__global__ __launch_bounds__(64 * SWAVES) void k_window_sha(uint32_t T, EmitArgs a, uint64_t n_windows) {
-    __shared__ u32x4 lds_all[(SPREAD ? 6 : 4) * 64 * SPIECES];  // 96 KB or 64 KB
-    const uint32_t wave = threadIdx.x / 64, lane = threadIdx.x % 64;
-    u32x4* lds = lds_all + wave * 64 * SPIECES;                 // this wave's 16 KB
-    const uint64_t w0 = ((uint64_t)blockIdx.x * SWAVES + wave) * 64;
-    if (w0 >= n_windows) return;                                // whole wave past the end
+// Waits until the emitting wave of the same workgroup has published at least
+// `need` record blocks of its 64 windows (workgroup-scope acquire).  The
+// emitting wave never waits on anything, so the wait ends; the spin limit is
+// a safety net only (the digests are then wrong and err is flagged).
+__device__ __forceinline__ void wait_progress(const uint32_t* prog, uint32_t need, uint32_t* err) {
+    uint32_t spins = 0;
+    while (__hip_atomic_load(prog, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < need) {
+        __builtin_amdgcn_s_sleep(2);
+        if (++spins == (1u << 24)) {
+            atomicOr(err, ERR_INTERNAL);
+            break;
+        }
+    }
+}
+
+// Hashes windows w0 .. w0+63 of the outputs (one lane per window), reading
+// each 256-byte chunk cooperatively and transposing it through this wave's
+// 16 KB of LDS.  With prog set, chunk c is read only once the emitting wave
+// has published its blocks.
+template <bool WAIT>
+__device__ __forceinline__ void hash_outputs(uint32_t T, const EmitArgs& a, uint64_t n_windows, uint64_t w0,
+                                             uint32_t lane, u32x4* lds, const uint32_t* prog, uint32_t* err) {
     const uint32_t nblk = 13 * (T / 64);   // blocks in the record
     const uint32_t nch = (nblk + SCH - 1) / SCH;
     const uint32_t my_piece = lane % SPIECES, my_grp = lane / SPIECES;
     u32x4 stage[SLOADS];
+    if (WAIT) wait_progress(prog, SCH < nblk ? SCH : nblk, err);
     load_chunk(stage, a, T, w0, n_windows, 0, my_grp, my_piece);
     uint32_t H[8];
     sha256_init(H);
 #pragma unroll 1
     for (uint32_t c = 0; c < nch; ++c) {
         // chunk c: registers -> LDS (swizzled); then chunk c+1 into registers
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();  // the previous chunk's LDS reads are done
 #pragma unroll
         for (uint32_t i = 0; i < SLOADS; ++i) {
             const uint32_t j = SGRP * i + my_grp;
             lds[j * SPIECES + (my_piece ^ (j % SPIECES))] = stage[i];
         }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        if (WAIT && c + 1 < nch) wait_progress(prog, (c + 2) * SCH < nblk ? (c + 2) * SCH : nblk, err);
         // the last iteration reloads its own chunk (harmless) so the loop has no branch around the loads
         load_chunk(stage, a, T, w0, n_windows, c + 1 < nch ? c + 1 : c, my_grp, my_piece);
         const uint32_t nb = (c + 1) * SCH <= nblk ? SCH : nblk - c * SCH;
@@ -148,6 +171,226 @@ __global__ __launch_bounds__(64 * SWAVES) void k_window_sha(uint32_t T, EmitArgs
     W[15] = (uint32_t)bits;
     sha256_compress(H, W);
     if (w0 + lane < n_windows) store_digest(H, a.digests + 32 * (w0 + lane));
+}
+
+template <bool SPREAD>
+__global__ __launch_bounds__(64 * SWAVES) void k_window_sha(uint32_t T, EmitArgs a, uint64_t n_windows) {
+    __shared__ u32x4 lds_all[(SPREAD ? 6 : 4) * 64 * SPIECES];  // 96 KB or 64 KB
+    const uint32_t wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+    const uint64_t w0 = ((uint64_t)blockIdx.x * SWAVES + wave) * 64;
+    if (w0 >= n_windows) return;  // whole wave past the end
+    hash_outputs<false>(T, a, n_windows, w0, lane, lds_all + wave * 64 * SPIECES, nullptr, nullptr);
+}
+
+// ---------------------------------------------------------------- emission beside the digest
+// With digests requested and at most one hashing wave per SIMD, pack_batch
+// runs one kernel whose workgroups pair four emitting waves with four hashing
+// waves (one per SIMD).  Emitting wave e writes the record of its 64 windows
+// (one lane per window) block by block in record order and publishes, in LDS,
+// how many blocks are complete; hashing wave e hashes the same windows from
+// the outputs exactly as k_window_sha does, reading a chunk only once it is
+// published.  Emission is memory traffic and a little integer work, so it
+// hides under the hashing waves' SHA-256 chains, the step's longest serial
+// dependency, instead of running as a kernel of its own before them.
+//
+// Piece view (plan array pc_emit, written with the window offsets): position
+// t of piece q holds token base_q + t, position id t − f_q, document id d_q,
+// and learns iff t ≥ mfrom_q.  After the window's real positions comes a
+// padding piece (pad token, position 0, document −1, mask 0), then a piece
+// that never starts.
+constexpr uint32_t NEVER = 0x7FFFFFFFu;  // above every window position, positive as int32
+constexpr uint32_t FWAVES = 8;           // waves per workgroup: 4 hashing, 4 emitting
+
+struct EPiece {
+    uint64_t base;   // token index of window position 0
+    uint32_t woff;   // first window position
+    uint32_t doc;    // document id (0xFFFFFFFF = −1 for padding)
+    uint32_t mfrom;  // first learned window position (NEVER for padding)
+    uint32_t pm;     // all ones for a real piece, 0 for padding
+};
+
+__device__ __forceinline__ EPiece fetch_piece(const Plan& p, uint32_t q, uint32_t q1, uint32_t real) {
+    const uint32_t qq = q < q1 ? q : q1 - 1;  // every window holds at least one piece
+    const uint4 e = p.pc_emit[qq];
+    const uint32_t wo = p.pc_woff[qq];
+    const bool in = q < q1;
+    EPiece r;
+    r.base = in ? ((uint64_t)e.y << 32) | e.x : 0;
+    r.woff = in ? wo : (q == q1 ? real : NEVER);
+    r.doc = in ? e.z : 0xFFFFFFFFu;
+    r.mfrom = in ? e.w : NEVER;
+    r.pm = in ? 0xFFFFFFFFu : 0u;
+    return r;
+}
+
+// The piece holding the current position, the next one, and a prefetched third.
+struct ECursor {
+    EPiece cur, nxt, nn;
+    uint32_t qn;  // piece index of nn
+    __device__ __forceinline__ void restart(const Plan& p, uint32_t q0, uint32_t q1, uint32_t real) {
+        cur = fetch_piece(p, q0, q1, real);
+        nxt = fetch_piece(p, q0 + 1, q1, real);
+        nn = fetch_piece(p, q0 + 2, q1, real);
+        qn = q0 + 2;
+    }
+    __device__ __forceinline__ void seek(const Plan& p, uint32_t t, uint32_t q1, uint32_t real) {
+        while (t >= nxt.woff) {
+            cur = nxt;
+            nxt = nn;
+            ++qn;
+            nn = fetch_piece(p, qn, q1, real);
+        }
+    }
+};
+
+__device__ __forceinline__ bool wave_any(bool c) { return __builtin_amdgcn_ballot_w64(c) != 0; }
+__device__ __forceinline__ int clamp4(int x) { return x < 0 ? 0 : (x > 4 ? 4 : x); }
+// little-endian mask word whose bytes j..3 are 1 (j in [0, 4])
+__device__ __forceinline__ uint32_t ones_le(int j) { return (uint32_t)(0x01010101ull << (8 * j)); }
+
+__device__ __forceinline__ void load16(uint32_t (&w)[16], const uint32_t* src) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const u32x4a4 v = reinterpret_cast<const u32x4a4*>(src)[i];
+        w[4 * i] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
+    }
+}
+
+__device__ __forceinline__ void store16(void* dst, const uint32_t (&w)[16]) {
+    u32x4* d = reinterpret_cast<u32x4*>(dst);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) d[i] = u32x4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
+}
+
+// Emits one record block of a lane's window: 16 positions of tokens (s = 0),
+// position ids (1) or document ids (2), or 64 mask bytes (3), starting at
+// window position t0.  Blocks with at most one piece boundary select per
+// element between the current and the next piece; others go element by element.
+__device__ __forceinline__ void emit_block(const Plan& p, const EmitArgs& a, ECursor& c, uint32_t s, uint32_t t0,
+                                           uint32_t q1, uint32_t real, uint64_t w, bool valid) {
+    const uint32_t T = p.T, n = s == 3 ? 64 : 16, pad = p.pad_token;
+    const uint64_t n_tokens = p.n_tokens;
+    c.seek(p, t0, q1, real);
+    const EPiece& A = c.cur;
+    const EPiece& B = c.nxt;
+    const uint32_t k = B.woff - t0 < n ? B.woff - t0 : n;  // elements in A (≥ 1)
+    const uint64_t lim = n_tokens >= 16 ? n_tokens - 16 : 0;
+    bool general = t0 + n > c.nn.woff;
+    if (s == 0) {
+        const bool okA = !A.pm || (n_tokens >= 16 && A.base + t0 <= lim);
+        const bool okB = k == 16 || !B.pm || (n_tokens >= 16 && B.base + t0 <= lim);
+        general = general || !okA || !okB;
+    }
+    uint8_t* dst = s == 0 ? reinterpret_cast<uint8_t*>(a.tok + w * T + t0)
+                 : s == 1 ? reinterpret_cast<uint8_t*>(a.pos + w * T + t0)
+                 : s == 2 ? reinterpret_cast<uint8_t*>(a.doc + w * T + t0)
+                          : a.mask + w * T + t0;
+    const bool boundary = wave_any(!general && k < n);
+    if (!general) {
+        uint32_t v[16];
+        if (s == 0) {
+            if (A.pm) load16(v, p.tokens + A.base + t0);
+            else
+#pragma unroll
+                for (int e = 0; e < 16; ++e) v[e] = pad;
+            if (k < 16) {
+                uint32_t u[16];
+                if (B.pm) load16(u, p.tokens + B.base + t0);
+                else
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) u[e] = pad;
+#pragma unroll
+                for (uint32_t e = 0; e < 16; ++e) v[e] = e < k ? v[e] : u[e];
+            }
+        } else if (s == 1) {
+            const uint32_t pa = t0 - A.woff, pb = t0 - B.woff;
+            if (!boundary) {
+#pragma unroll
+                for (uint32_t e = 0; e < 16; ++e) v[e] = (pa + e) & A.pm;
+            } else {
+#pragma unroll
+                for (uint32_t e = 0; e < 16; ++e) v[e] = e < k ? (pa + e) & A.pm : (pb + e) & B.pm;
+            }
+        } else if (s == 2) {
+#pragma unroll
+            for (uint32_t e = 0; e < 16; ++e) v[e] = boundary && e >= k ? B.doc : A.doc;
+        } else {
+            // learned positions of the block: [A.mfrom, B.woff) ∪ [B.mfrom, end)
+            const int ma = (int)A.mfrom - (int)t0;
+            if (!boundary) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) v[i] = ones_le(clamp4(ma - 4 * i));
+            } else {
+                const int wb = (int)B.woff - (int)t0, mb = (int)B.mfrom - (int)t0;
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    v[i] = __builtin_amdgcn_bitop3_b32(ones_le(clamp4(ma - 4 * i)), ones_le(clamp4(wb - 4 * i)),
+                                                       ones_le(clamp4(mb - 4 * i)), 0xBA);  // (x & ~y) | z
+            }
+        }
+        if (valid) store16(dst, v);
+    } else {
+#pragma unroll 1
+        for (uint32_t e = 0; e < n; ++e) {
+            const uint32_t t = t0 + e;
+            c.seek(p, t, q1, real);
+            const EPiece& P = c.cur;
+            if (!valid) continue;
+            if (s == 0) {
+                const uint64_t at = P.base + t;
+                reinterpret_cast<uint32_t*>(dst)[e] = P.pm && at < n_tokens ? p.tokens[at] : pad;
+            } else if (s == 1) {
+                reinterpret_cast<uint32_t*>(dst)[e] = (t - P.woff) & P.pm;
+            } else if (s == 2) {
+                reinterpret_cast<uint32_t*>(dst)[e] = P.doc;
+            } else {
+                dst[e] = t >= P.mfrom ? 1 : 0;
+            }
+        }
+    }
+}
+
+// Emits windows w0 .. w0+63 (one lane per window) in record order, publishing
+// the number of complete blocks after every chunk of SCH blocks.
+__device__ __forceinline__ void emit_lanes(const Plan& p, const EmitArgs& a, uint64_t n_windows, uint64_t w0,
+                                           uint32_t lane, uint32_t* prog) {
+    const bool valid = w0 + lane < n_windows;
+    const uint64_t w = valid ? w0 + lane : n_windows - 1;  // lanes past the end mirror the last window
+    const uint32_t i = (uint32_t)(w / a.per), jj = (uint32_t)(w % a.per);
+    const uint64_t gw = window_of(p, (uint64_t)a.step + i, a.rank * a.per + jj);
+    const uint32_t q0 = p.win_first[gw], q1 = p.win_first[gw + 1], real = p.win_real[gw];
+    const uint32_t T = p.T, nblk = 13 * (T / 64);
+    ECursor c;
+    uint32_t b = 0;
+#pragma unroll 1
+    for (uint32_t s = 0; s < 4; ++s) {
+        c.restart(p, q0, q1, real);
+        const uint32_t n = s == 3 ? 64 : 16;
+#pragma unroll 1
+        for (uint32_t t0 = 0; t0 < T; t0 += n) {
+            emit_block(p, a, c, s, t0, q1, real, w, valid);
+            ++b;
+            if (b % SCH == 0 || b == nblk) {
+                // every lane's stores of the chunk complete, then the count (workgroup-scope release)
+                if (lane == 0) __hip_atomic_store(prog, b, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+            }
+        }
+    }
+}
+
+__global__ __launch_bounds__(64 * FWAVES) void k_emit_sha(Plan p, EmitArgs a, uint64_t n_windows) {
+    // 64 KB of transposition buffers for the hashing waves, padded to 96 KB so
+    // that a CU holds one workgroup and each SIMD one hashing wave
+    __shared__ u32x4 lds_all[6 * 64 * SPIECES];
+    __shared__ uint32_t prog[4];
+    const uint32_t wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+    if (threadIdx.x < 4) prog[threadIdx.x] = 0;
+    __syncthreads();
+    const uint32_t e = wave & 3;
+    const uint64_t w0 = ((uint64_t)blockIdx.x * 4 + e) * 64;
+    if (w0 >= n_windows) return;
+    if (wave < 4) hash_outputs<true>(p.T, a, n_windows, w0, lane, lds_all + e * 64 * SPIECES, prog + e, p.err);
+    else emit_lanes(p, a, n_windows, w0, lane, prog + e);
 }
 
 // SHA-256 of an arbitrary byte string (4-byte aligned start), one lane.
@@ -215,6 +458,17 @@ void launch_window_sha(const Plan& p, const EmitArgs& a, hipStream_t st) {
         hipLaunchKernelGGL(k_window_sha<true>, dim3(groups), dim3(64 * SWAVES), 0, st, p.T, a, n);
     else
         hipLaunchKernelGGL(k_window_sha<false>, dim3(groups), dim3(64 * SWAVES), 0, st, p.T, a, n);
+    DP_HIP(hipGetLastError());
+}
+
+bool emit_sha_fits(const EmitArgs& a) {
+    const uint64_t n = (uint64_t)a.n_steps * a.per;
+    return (n + 255) / 256 <= 256;  // one workgroup (four hashing waves) per CU of MI355X's 256
+}
+
+void launch_emit_sha(const Plan& p, const EmitArgs& a, hipStream_t st) {
+    const uint64_t n = (uint64_t)a.n_steps * a.per;
+    hipLaunchKernelGGL(k_emit_sha, dim3((uint32_t)((n + 255) / 256)), dim3(64 * FWAVES), 0, st, p, a, n);
     DP_HIP(hipGetLastError());
 }
 

@@ -74,9 +74,10 @@ enum {
     PACK_PHASE_WINDOWS,      /* window table, real and learned positions per window */
     PACK_PHASE_MIXTURE,      /* apportionment, slot table, order checks */
     PACK_PHASE_CYCLE,        /* cycle sums and plan digest */
-    PACK_PHASE_EMIT,         /* emission kernel of pack_batch */
+    PACK_PHASE_EMIT,         /* emission kernel of pack_batch (when not timed under DIGEST) */
     PACK_PHASE_LEARNED,      /* per-update learned counts of pack_batch */
-    PACK_PHASE_DIGEST,       /* per-window SHA-256 of pack_batch */
+    PACK_PHASE_DIGEST,       /* per-window SHA-256 of pack_batch; with at most 65536 windows
+                              * in the call, emission runs inside the same kernel and is timed here */
     PACK_PHASE_FINGERPRINT,  /* pack_fingerprint */
     PACK_N_PHASES
 };

@@ -37,8 +37,11 @@ def _setup(name):
     return _CACHE[name]
 
 
-# (workload, max updates emitted in one call: the bench's whole cycle where it fits)
-FULL = [("tiny", None), ("pretrain", None), ("sft", None), ("long", None), ("full", 48)]
+# (workload, updates emitted per call: None = the whole cycle in one call, as the
+# bench does; else the first a and the last b updates of the cycle).  The full
+# workload's second call holds 67,584 windows, more than the one-kernel
+# emission-and-digest launch takes, so it covers the two-kernel path.
+FULL = [("tiny", None), ("pretrain", None), ("sft", None), ("long", None), ("full", (24, 66))]
 
 
 @pytest.mark.parametrize("name,cap", FULL)
@@ -49,11 +52,10 @@ def test_full_size_parity(name, cap):
     compare_plan(pk, op)
     compare_cycle(gi, oi, op)
     U = oi.n_updates
-    n = U if cap is None else min(cap, U)
     B, T = c.B, c.T
     r = np.random.default_rng(7)
     # emit in one call per contiguous range (bench: the whole cycle in one call)
-    ranges = [(0, n)] if cap is None else [(0, n // 2), (U - n // 2, n // 2)]
+    ranges = [(0, U)] if cap is None else [(0, min(cap[0], U)), (max(U - cap[1], 0), min(cap[1], U))]
     outs = []
     for s0, cnt in ranges:
         say("emit", name, "steps", s0, "+", cnt)
