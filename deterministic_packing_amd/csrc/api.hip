@@ -214,6 +214,7 @@ size_t carve(pack_ctx& c, char* base) {
     p.cyc_start = k.take<uint64_t>(S);
     p.checks = k.take<uint64_t>(2);
     p.cyc_sums = k.take<uint64_t>(2);
+    p.pad16 = k.take<uint32_t>(16);
     c.nstart = k.take<uint32_t>(S + 1);
     c.dig_cap = 128 + 48 * S;
     c.dig_buf = k.take<uint8_t>(c.dig_cap + 32);
@@ -282,6 +283,7 @@ void build_plan(pack_ctx& c) {
     h2d(p.bp, c.bp.data(), p.S, st);
     dp::launch_zero_u32(p.err, 1, st);
     dp::launch_zero_u64(p.stats, 4ull * p.S, st);
+    dp::launch_fill_u32(p.pad16, 16, p.pad_token, st);
 
     // validation first: no kernel reads the corpus through unchecked offsets
     c.timer.begin(PACK_PHASE_VALIDATE, st);

@@ -118,6 +118,7 @@ struct Plan {
     uint32_t* pc_len;             // [P]
     uint32_t* pc_woff;            // [P]
     uint4* pc_emit;               // [P] emission view: (u64 token index of window position 0, doc, mask start)
+    uint32_t* pad16;              // [16] the pad token, 16 times (a load source for padding)
     uint64_t* pc_pre;             // [P+1] token prefix over pieces
     uint64_t* src_piece_start;    // [S+1]
     uint32_t* jump;               // [L][P] lifting table
@@ -216,6 +217,7 @@ void launch_windows(Plan& p, hipStream_t st);         // win_first, pc_woff, win
 void launch_mixture_w(Plan& p, uint64_t W, uint32_t* nstart, hipStream_t st);  // n_upd, slot table
 void launch_zero_u64(uint64_t* a, uint64_t n, hipStream_t st);
 void launch_zero_u32(uint32_t* a, uint64_t n, hipStream_t st);
+void launch_fill_u32(uint32_t* a, uint64_t n, uint32_t v, hipStream_t st);
 uint64_t sort_hist_words(uint64_t n_docs);
 void launch_checks(Plan& p, hipStream_t st);          // order / hash checks
 void launch_cycle_sums(Plan& p, uint32_t U, hipStream_t st);

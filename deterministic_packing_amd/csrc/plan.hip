@@ -467,8 +467,10 @@ void launch_zero_u64(uint64_t* a, uint64_t n, hipStream_t st) {
     DP_HIP(hipGetLastError());
 }
 
-void launch_zero_u32(uint32_t* a, uint64_t n, hipStream_t st) {
-    if (n) hipLaunchKernelGGL(k_fill_u32, dim3(blocks_for(n)), dim3(256), 0, st, a, n, 0u);
+void launch_zero_u32(uint32_t* a, uint64_t n, hipStream_t st) { launch_fill_u32(a, n, 0u, st); }
+
+void launch_fill_u32(uint32_t* a, uint64_t n, uint32_t v, hipStream_t st) {
+    if (n) hipLaunchKernelGGL(k_fill_u32, dim3(blocks_for(n)), dim3(256), 0, st, a, n, v);
     DP_HIP(hipGetLastError());
 }
 

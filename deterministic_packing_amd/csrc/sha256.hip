@@ -262,96 +262,182 @@ __device__ __forceinline__ void store16(void* dst, const uint32_t (&w)[16]) {
     for (int i = 0; i < 4; ++i) d[i] = u32x4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
 }
 
-// Emits one record block of a lane's window: 16 positions of tokens (s = 0),
-// position ids (1) or document ids (2), or 64 mask bytes (3), starting at
-// window position t0.  Blocks with at most one piece boundary select per
-// element between the current and the next piece; others go element by element.
-__device__ __forceinline__ void emit_block(const Plan& p, const EmitArgs& a, ECursor& c, uint32_t s, uint32_t t0,
-                                           uint32_t q1, uint32_t real, uint64_t w, bool valid) {
-    const uint32_t T = p.T, n = s == 3 ? 64 : 16, pad = p.pad_token;
-    const uint64_t n_tokens = p.n_tokens;
-    c.seek(p, t0, q1, real);
-    const EPiece& A = c.cur;
-    const EPiece& B = c.nxt;
-    const uint32_t k = B.woff - t0 < n ? B.woff - t0 : n;  // elements in A (≥ 1)
-    const uint64_t lim = n_tokens >= 16 ? n_tokens - 16 : 0;
-    bool general = t0 + n > c.nn.woff;
-    if (s == 0) {
-        const bool okA = !A.pm || (n_tokens >= 16 && A.base + t0 <= lim);
-        const bool okB = k == 16 || !B.pm || (n_tokens >= 16 && B.base + t0 <= lim);
-        general = general || !okA || !okB;
+__device__ __forceinline__ uint32_t wave_min(uint32_t v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const uint32_t u = __shfl_xor(v, o, 64);
+        v = u < v ? u : v;
     }
-    uint8_t* dst = s == 0 ? reinterpret_cast<uint8_t*>(a.tok + w * T + t0)
-                 : s == 1 ? reinterpret_cast<uint8_t*>(a.pos + w * T + t0)
-                 : s == 2 ? reinterpret_cast<uint8_t*>(a.doc + w * T + t0)
-                          : a.mask + w * T + t0;
-    const bool boundary = wave_any(!general && k < n);
-    if (!general) {
-        uint32_t v[16];
-        if (s == 0) {
-            if (A.pm) load16(v, p.tokens + A.base + t0);
-            else
-#pragma unroll
-                for (int e = 0; e < 16; ++e) v[e] = pad;
-            if (k < 16) {
-                uint32_t u[16];
-                if (B.pm) load16(u, p.tokens + B.base + t0);
-                else
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) u[e] = pad;
-#pragma unroll
-                for (uint32_t e = 0; e < 16; ++e) v[e] = e < k ? v[e] : u[e];
-            }
-        } else if (s == 1) {
-            const uint32_t pa = t0 - A.woff, pb = t0 - B.woff;
-            if (!boundary) {
-#pragma unroll
-                for (uint32_t e = 0; e < 16; ++e) v[e] = (pa + e) & A.pm;
-            } else {
-#pragma unroll
-                for (uint32_t e = 0; e < 16; ++e) v[e] = e < k ? (pa + e) & A.pm : (pb + e) & B.pm;
-            }
-        } else if (s == 2) {
-#pragma unroll
-            for (uint32_t e = 0; e < 16; ++e) v[e] = boundary && e >= k ? B.doc : A.doc;
-        } else {
-            // learned positions of the block: [A.mfrom, B.woff) ∪ [B.mfrom, end)
-            const int ma = (int)A.mfrom - (int)t0;
-            if (!boundary) {
-#pragma unroll
-                for (int i = 0; i < 16; ++i) v[i] = ones_le(clamp4(ma - 4 * i));
-            } else {
-                const int wb = (int)B.woff - (int)t0, mb = (int)B.mfrom - (int)t0;
-#pragma unroll
-                for (int i = 0; i < 16; ++i)
-                    v[i] = __builtin_amdgcn_bitop3_b32(ones_le(clamp4(ma - 4 * i)), ones_le(clamp4(wb - 4 * i)),
-                                                       ones_le(clamp4(mb - 4 * i)), 0xBA);  // (x & ~y) | z
-            }
-        }
-        if (valid) store16(dst, v);
-    } else {
+    return v;
+}
+
+__device__ __forceinline__ void publish(uint32_t* prog, uint32_t blocks, uint32_t lane) {
+    // every lane's stores complete (the explicit wait makes the release's
+    // ordering of global stores before the LDS count independent of how the
+    // workgroup-scope release is lowered), then the count
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (lane == 0) __hip_atomic_store(prog, blocks, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// Emits array s (0 tokens, 1 position ids, 2 document ids) of a lane's window
+// in runs: a run writes 16 elements from the piece holding position t and
+// advances t by the run's length within that piece, min(16, end − t); the
+// elements past the piece end are rewritten by the next run of the same lane
+// (program order), so no run selects between pieces.  The window's last
+// positions, where 16 elements would cross into the next window, are written
+// one by one.  Record blocks [blk0, blk0 + T/16) are published as all lanes
+// complete them.
+template <uint32_t s>
+__device__ __forceinline__ void emit_runs(const Plan& p, const EmitArgs& a, ECursor& c, uint32_t q0, uint32_t q1,
+                                          uint32_t real, uint64_t w, bool valid, uint32_t* prog, uint32_t lane,
+                                          uint32_t blk0) {
+    const uint32_t T = p.T, pad = p.pad_token;
+    const uint64_t n_tokens = p.n_tokens;
+    c.restart(p, q0, q1, real);
+    uint32_t* out = (s == 0 ? a.tok : s == 1 ? reinterpret_cast<uint32_t*>(a.pos) : reinterpret_cast<uint32_t*>(a.doc)) +
+                    w * T;
+    uint32_t t = 0, published = 0, it = 0;
 #pragma unroll 1
-        for (uint32_t e = 0; e < n; ++e) {
-            const uint32_t t = t0 + e;
-            c.seek(p, t, q1, real);
+    while (wave_any(t < T)) {
+        if (t < T) {
             const EPiece& P = c.cur;
-            if (!valid) continue;
-            if (s == 0) {
-                const uint64_t at = P.base + t;
-                reinterpret_cast<uint32_t*>(dst)[e] = P.pm && at < n_tokens ? p.tokens[at] : pad;
-            } else if (s == 1) {
-                reinterpret_cast<uint32_t*>(dst)[e] = (t - P.woff) & P.pm;
-            } else if (s == 2) {
-                reinterpret_cast<uint32_t*>(dst)[e] = P.doc;
+            const uint32_t end = c.nxt.woff < T ? c.nxt.woff : T;  // the piece's end in the window
+            const uint32_t ne = end - t < 16 ? end - t : 16;
+            if (t + 16 <= T && (s != 0 || !P.pm || P.base + t + 16 <= n_tokens)) {
+                uint32_t v[16];
+                if (s == 0) {
+                    if (P.pm) load16(v, p.tokens + P.base + t);
+                    else
+#pragma unroll
+                        for (int e = 0; e < 16; ++e) v[e] = pad;
+                } else if (s == 1) {
+                    const uint32_t pa = (t - P.woff) & P.pm, inc = P.pm & 1u;  // padding: all 0
+#pragma unroll
+                    for (uint32_t e = 0; e < 16; ++e) v[e] = pa + e * inc;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) v[e] = P.doc;
+                }
+                if (valid) store16(out + t, v);
             } else {
-                dst[e] = t >= P.mfrom ? 1 : 0;
+#pragma unroll 1
+                for (uint32_t e = 0; e < ne; ++e) {
+                    const uint32_t te = t + e;
+                    const uint64_t at = P.base + te;
+                    const uint32_t v = s == 0 ? (P.pm && at < n_tokens ? p.tokens[at] : pad)
+                                     : s == 1 ? (te - P.woff) & P.pm
+                                              : P.doc;
+                    if (valid) out[te] = v;
+                }
+            }
+            t += ne;
+            if (t < T) c.seek(p, t, q1, real);
+        }
+        if ((++it & 7) == 0 || !wave_any(t < T)) {
+            const uint32_t done = wave_min(t) / 16;  // blocks complete in every lane
+            if (done > published) {
+                published = done;
+                publish(prog, blk0 + done, lane);
             }
         }
     }
 }
 
+// Token runs, RG at a time: the runs' positions come from the cursor first,
+// then all their loads are issued (padding reads pad16, so every load is
+// unconditional and no loaded value is merged across branches), then the
+// stores, in run order, so a run's tail past its piece end is rewritten by the
+// next run.  Runs that cannot load 16 tokens (the window's last positions, the
+// corpus end) are written element by element after the group's stores.
+constexpr uint32_t RG = 4;
+__device__ __forceinline__ void emit_token_runs(const Plan& p, const EmitArgs& a, ECursor& c, uint32_t q0,
+                                                uint32_t q1, uint32_t real, uint64_t w, bool valid, uint32_t* prog,
+                                                uint32_t lane) {
+    const uint32_t T = p.T, pad = p.pad_token;
+    const uint64_t n_tokens = p.n_tokens;
+    c.restart(p, q0, q1, real);
+    uint32_t* out = a.tok + w * T;
+    uint32_t t = 0, published = 0;
+#pragma unroll 1
+    while (wave_any(t < T)) {
+        uint32_t rt[RG], rn[RG], rpm[RG];
+        uint64_t rb[RG];
+        bool rv[RG];
+#pragma unroll
+        for (uint32_t r = 0; r < RG; ++r) {
+            const bool act = t < T;
+            const EPiece& P = c.cur;
+            const uint32_t end = c.nxt.woff < T ? c.nxt.woff : T;  // the piece's end in the window
+            const uint32_t ne = act ? (end - t < 16 ? end - t : 16) : 0;
+            rt[r] = t;
+            rn[r] = ne;
+            rb[r] = P.base;
+            rpm[r] = P.pm;
+            rv[r] = act && t + 16 <= T && (!P.pm || P.base + t + 16 <= n_tokens);
+            t += ne;
+            if (t < T) c.seek(p, t, q1, real);
+        }
+        uint32_t v[RG][16];
+#pragma unroll
+        for (uint32_t r = 0; r < RG; ++r)
+            load16(v[r], rv[r] && rpm[r] ? p.tokens + rb[r] + rt[r] : p.pad16);
+        if (valid) {
+#pragma unroll
+            for (uint32_t r = 0; r < RG; ++r)
+                if (rv[r]) store16(out + rt[r], v[r]);
+#pragma unroll
+            for (uint32_t r = 0; r < RG; ++r) {
+                if (rv[r]) continue;
+#pragma unroll 1
+                for (uint32_t e = 0; e < rn[r]; ++e) {
+                    const uint64_t at = rb[r] + rt[r] + e;
+                    out[rt[r] + e] = rpm[r] && at < n_tokens ? p.tokens[at] : pad;
+                }
+            }
+        }
+        const uint32_t done = wave_min(t) / 16;  // blocks complete in every lane
+        if (done > published) {
+            published = done;
+            publish(prog, done, lane);
+        }
+    }
+}
+
+// Emits mask block t0 .. t0+63 of a lane's window (64 bytes).  With at most
+// one piece boundary in the block, the learned positions are
+// [A.mfrom, B.woff) ∪ [B.mfrom, end), word by word; otherwise byte by byte.
+__device__ __forceinline__ void emit_mask_block(const Plan& p, const EmitArgs& a, ECursor& c, uint32_t t0,
+                                                uint32_t q1, uint32_t real, uint64_t w, bool valid) {
+    c.seek(p, t0, q1, real);
+    const EPiece& A = c.cur;
+    const EPiece& B = c.nxt;
+    uint8_t* dst = a.mask + w * p.T + t0;
+    if (t0 + 64 <= c.nn.woff) {
+        uint32_t v[16];
+        const int ma = (int)A.mfrom - (int)t0;
+        if (!wave_any(t0 + 64 > B.woff)) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) v[i] = ones_le(clamp4(ma - 4 * i));
+        } else {
+            const int wb = (int)B.woff - (int)t0, mb = (int)B.mfrom - (int)t0;
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                v[i] = __builtin_amdgcn_bitop3_b32(ones_le(clamp4(ma - 4 * i)), ones_le(clamp4(wb - 4 * i)),
+                                                   ones_le(clamp4(mb - 4 * i)), 0xBA);  // (x & ~y) | z
+        }
+        if (valid) store16(dst, v);
+    } else {
+#pragma unroll 1
+        for (uint32_t e = 0; e < 64; ++e) {
+            const uint32_t t = t0 + e;
+            c.seek(p, t, q1, real);
+            if (valid) dst[e] = t >= c.cur.mfrom ? 1 : 0;
+        }
+    }
+}
+
 // Emits windows w0 .. w0+63 (one lane per window) in record order, publishing
-// the number of complete blocks after every chunk of SCH blocks.
+// the number of record blocks complete in every lane.
 __device__ __forceinline__ void emit_lanes(const Plan& p, const EmitArgs& a, uint64_t n_windows, uint64_t w0,
                                            uint32_t lane, uint32_t* prog) {
     const bool valid = w0 + lane < n_windows;
@@ -359,22 +445,18 @@ __device__ __forceinline__ void emit_lanes(const Plan& p, const EmitArgs& a, uin
     const uint32_t i = (uint32_t)(w / a.per), jj = (uint32_t)(w % a.per);
     const uint64_t gw = window_of(p, (uint64_t)a.step + i, a.rank * a.per + jj);
     const uint32_t q0 = p.win_first[gw], q1 = p.win_first[gw + 1], real = p.win_real[gw];
-    const uint32_t T = p.T, nblk = 13 * (T / 64);
+    const uint32_t T = p.T, per = T / 16, nblk = 13 * (T / 64);
     ECursor c;
-    uint32_t b = 0;
+    emit_token_runs(p, a, c, q0, q1, real, w, valid, prog, lane);
+    emit_runs<1>(p, a, c, q0, q1, real, w, valid, prog, lane, per);
+    emit_runs<2>(p, a, c, q0, q1, real, w, valid, prog, lane, 2 * per);
+    c.restart(p, q0, q1, real);
+    uint32_t b = 3 * per;
 #pragma unroll 1
-    for (uint32_t s = 0; s < 4; ++s) {
-        c.restart(p, q0, q1, real);
-        const uint32_t n = s == 3 ? 64 : 16;
-#pragma unroll 1
-        for (uint32_t t0 = 0; t0 < T; t0 += n) {
-            emit_block(p, a, c, s, t0, q1, real, w, valid);
-            ++b;
-            if (b % SCH == 0 || b == nblk) {
-                // every lane's stores of the chunk complete, then the count (workgroup-scope release)
-                if (lane == 0) __hip_atomic_store(prog, b, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-            }
-        }
+    for (uint32_t t0 = 0; t0 < T; t0 += 64) {
+        emit_mask_block(p, a, c, t0, q1, real, w, valid);
+        ++b;
+        if (b % SCH == 0 || b == nblk) publish(prog, b, lane);
     }
 }
 
