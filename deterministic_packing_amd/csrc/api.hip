@@ -13,20 +13,27 @@ namespace {
 
 constexpr size_t ALIGN = 256;
 
-// One cached workspace per device: pack_destroy parks its arena here and the
-// next pack_init on that device reuses it when large enough, so a loop of
-// init/destroy does not pay hipMalloc/hipFree each time.
+// One cached device workspace and one pinned host staging area per device:
+// pack_destroy parks them here and the next pack_init on that device reuses
+// them when large enough, so a loop of init/destroy does not pay
+// hipMalloc/hipHostMalloc (and their frees) each time.
 struct ArenaCache {
     std::mutex mu;
     std::vector<std::pair<void*, size_t>> per_device;  // index = device
+    bool pinned;
 };
-ArenaCache& arena_cache() {
-    static ArenaCache c;
-    return c;
+ArenaCache& arena_cache(bool pinned = false) {
+    static ArenaCache dev{{}, {}, false}, host{{}, {}, true};
+    return pinned ? host : dev;
 }
 
-void* arena_take(int dev, size_t bytes, size_t* got) {
-    auto& c = arena_cache();
+void cache_free(const ArenaCache& c, void* p) {
+    if (c.pinned) (void)hipHostFree(p);
+    else (void)hipFree(p);
+}
+
+void* arena_take(int dev, size_t bytes, size_t* got, bool pinned = false) {
+    auto& c = arena_cache(pinned);
     std::lock_guard<std::mutex> lk(c.mu);
     if ((size_t)dev < c.per_device.size()) {
         auto& e = c.per_device[dev];
@@ -40,16 +47,16 @@ void* arena_take(int dev, size_t bytes, size_t* got) {
     return nullptr;
 }
 
-void arena_give(int dev, void* ptr, size_t bytes) {
-    auto& c = arena_cache();
+void arena_give(int dev, void* ptr, size_t bytes, bool pinned = false) {
+    auto& c = arena_cache(pinned);
     std::lock_guard<std::mutex> lk(c.mu);
     if ((size_t)dev >= c.per_device.size()) c.per_device.resize(dev + 1, {nullptr, 0});
     auto& e = c.per_device[dev];
     if (e.first == nullptr || e.second < bytes) {
-        if (e.first) (void)hipFree(e.first);
+        if (e.first) cache_free(c, e.first);
         e = {ptr, bytes};
     } else {
-        (void)hipFree(ptr);
+        cache_free(c, ptr);
     }
 }
 
@@ -147,6 +154,10 @@ struct pack_ctx {
     uint32_t* hash_first = nullptr;  // tile -> first document table of the hash
     uint8_t* dig_buf = nullptr;
     size_t dig_cap = 0;
+    // pinned host staging for every host<->device copy (asynchronous copies,
+    // no pageable bounce); a bump allocator reset after each synchronization
+    uint8_t* pin = nullptr;
+    size_t pin_bytes = 0, pin_off = 0;
     std::vector<uint64_t> src_win_start, stats, checks, src_piece_start;
     std::vector<uint32_t> n_upd;
     int64_t cycle = -1;
@@ -230,6 +241,40 @@ void h2d(T* dst, const T* src, uint64_t count, hipStream_t st) {
     if (count) DP_HIP(hipMemcpyAsync(dst, src, sizeof(T) * count, hipMemcpyHostToDevice, st));
 }
 
+// pinned staging: bytes for the largest set of copies between two synchronizations
+size_t pin_bytes_for(uint32_t S) { return 64ull * S + 2048; }
+
+template <typename T>
+T* pin_take(pack_ctx& c, uint64_t count) {
+    c.pin_off = (c.pin_off + 63) / 64 * 64;
+    T* p = reinterpret_cast<T*>(c.pin + c.pin_off);
+    c.pin_off += sizeof(T) * (count ? count : 1);
+    if (c.pin_off > c.pin_bytes) throw dp::HipError{hipErrorOutOfMemory, "internal: pinned staging exhausted"};
+    return p;
+}
+
+// host array -> pinned staging -> device (asynchronous)
+template <typename T>
+void h2d_staged(pack_ctx& c, T* dst, const T* src, uint64_t count) {
+    if (!count) return;
+    T* h = pin_take<T>(c, count);
+    std::memcpy(h, src, sizeof(T) * count);
+    h2d(dst, h, count, c.st);
+}
+
+// device -> pinned staging (asynchronous); read the returned pointer after a synchronization
+template <typename T>
+T* d2h_staged(pack_ctx& c, const T* src, uint64_t count) {
+    T* h = pin_take<T>(c, count);
+    d2h(h, src, count, c.st);
+    return h;
+}
+
+void sync_staged(pack_ctx& c) {
+    DP_HIP(hipStreamSynchronize(c.st));
+    c.pin_off = 0;
+}
+
 void check_config(const pack_config* cfg) {
     auto bad = [](const char* m) { throw InvalError{m}; };
     if (cfg->flags & ~PACK_FLAG_TIMING) bad("unknown flags");
@@ -265,10 +310,9 @@ int fail_hip(pack_ctx* c, const dp::HipError& e) {
 
 void release(pack_ctx* c) {
     if (!c) return;
-    if (c->arena) {
-        (void)hipStreamSynchronize(c->st);
-        arena_give(c->device, c->arena, c->arena_bytes);
-    }
+    if (c->arena || c->pin) (void)hipStreamSynchronize(c->st);
+    if (c->arena) arena_give(c->device, c->arena, c->arena_bytes);
+    if (c->pin) arena_give(c->device, c->pin, c->pin_bytes, true);
     c->timer.destroy();
     delete c;
 }
@@ -277,10 +321,11 @@ void build_plan(pack_ctx& c) {
     dp::Plan& p = c.p;
     hipStream_t st = c.st;
     // recipe to the device
-    h2d(p.gbase, c.gbase.data(), p.S + 1, st);
-    h2d(p.n_strata, c.n_strata.data(), p.S, st);
-    h2d(p.weight, c.weight.data(), p.S, st);
-    h2d(p.bp, c.bp.data(), p.S, st);
+    c.pin_off = 0;
+    h2d_staged(c, p.gbase, c.gbase.data(), p.S + 1);
+    h2d_staged(c, p.n_strata, c.n_strata.data(), p.S);
+    h2d_staged(c, p.weight, c.weight.data(), p.S);
+    h2d_staged(c, p.bp, c.bp.data(), p.S);
     dp::launch_zero_u32(p.err, 1, st);
     dp::launch_zero_u64(p.stats, 4ull * p.S, st);
     dp::launch_fill_u32(p.pad16, 16, p.pad_token, st);
@@ -289,12 +334,12 @@ void build_plan(pack_ctx& c) {
     c.timer.begin(PACK_PHASE_VALIDATE, st);
     dp::launch_validate(p, st);
     c.timer.end(st);
-    uint32_t err = 0;
-    uint64_t span[2] = {0, 0};  // offsets[0] and offsets[n_docs]: the tokens the documents cover
-    d2h(&err, p.err, 1, st);
-    d2h(&span[0], p.offsets, 1, st);
-    d2h(&span[1], p.offsets + p.n_docs, 1, st);
-    DP_HIP(hipStreamSynchronize(st));
+    const uint32_t* h_err = d2h_staged(c, p.err, 1);
+    const uint64_t* h_lo = d2h_staged(c, p.offsets, 1);  // offsets[0] and offsets[n_docs]:
+    const uint64_t* h_hi = d2h_staged(c, p.offsets + p.n_docs, 1);  // the tokens the documents cover
+    sync_staged(c);
+    uint32_t err = *h_err;
+    const uint64_t span[2] = {*h_lo, *h_hi};
     if (err) {
         std::string m = "invalid corpus:";
         if (err & 1u) m += " offsets decrease;";
@@ -313,10 +358,9 @@ void build_plan(pack_ctx& c) {
     c.timer.begin(PACK_PHASE_KEYS, st);
     dp::launch_keep_scan(p, st);
     c.timer.end(st);
-    uint32_t n_kept = 0;
-    d2h(&n_kept, p.kept_pos + p.n_docs, 1, st);
-    DP_HIP(hipStreamSynchronize(st));
-    p.n_kept = n_kept;
+    const uint32_t* h_kept = d2h_staged(c, p.kept_pos + p.n_docs, 1);
+    sync_staged(c);
+    p.n_kept = *h_kept;
 
     // A3 sort, A4 merge, A5 piece counts
     c.timer.begin(PACK_PHASE_SORT, st);
@@ -328,10 +372,9 @@ void build_plan(pack_ctx& c) {
     c.timer.begin(PACK_PHASE_PIECES, st);
     dp::launch_piece_count(p, st);
     c.timer.end(st);
-    uint32_t n_pieces = 0;
-    d2h(&n_pieces, p.piece_start + p.n_kept, 1, st);
-    DP_HIP(hipStreamSynchronize(st));
-    p.n_pieces = n_pieces;
+    const uint32_t* h_pieces = d2h_staged(c, p.piece_start + p.n_kept, 1);
+    sync_staged(c);
+    p.n_pieces = *h_pieces;
     if (p.n_pieces > p.cap_pieces) throw InvalError{"internal: piece bound exceeded"};
     p.levels = bitlen(p.n_pieces) ? bitlen(p.n_pieces) : 1;
 
@@ -343,9 +386,9 @@ void build_plan(pack_ctx& c) {
     dp::launch_lifting(p, st);
     dp::launch_window_count(p, st);
     c.timer.end(st);
-    c.src_win_start.assign(p.S + 1, 0);
-    d2h(c.src_win_start.data(), p.src_win_start, p.S + 1, st);
-    DP_HIP(hipStreamSynchronize(st));
+    const uint64_t* h_sws = d2h_staged(c, p.src_win_start, p.S + 1);
+    sync_staged(c);
+    c.src_win_start.assign(h_sws, h_sws + p.S + 1);
     p.n_windows = c.src_win_start[p.S];
 
     // window table, A6 mixture, checks
@@ -357,16 +400,17 @@ void build_plan(pack_ctx& c) {
     dp::launch_mixture_w(p, c.W, c.nstart, st);
     dp::launch_checks(p, st);
     c.timer.end(st);
-    c.n_upd.assign(p.S, 0);
-    c.stats.assign(4ull * p.S, 0);
-    c.checks.assign(2, 0);
-    c.src_piece_start.assign(p.S + 1, 0);
-    d2h(c.n_upd.data(), p.n_upd, p.S, st);
-    d2h(c.stats.data(), p.stats, 4ull * p.S, st);
-    d2h(c.checks.data(), p.checks, 2, st);
-    d2h(c.src_piece_start.data(), p.src_piece_start, p.S + 1, st);
-    d2h(&err, p.err, 1, st);
-    DP_HIP(hipStreamSynchronize(st));
+    const uint32_t* h_upd = d2h_staged(c, p.n_upd, p.S);
+    const uint64_t* h_stats = d2h_staged(c, p.stats, 4ull * p.S);
+    const uint64_t* h_checks = d2h_staged(c, p.checks, 2);
+    const uint64_t* h_sps = d2h_staged(c, p.src_piece_start, p.S + 1);
+    h_err = d2h_staged(c, p.err, 1);
+    sync_staged(c);
+    c.n_upd.assign(h_upd, h_upd + p.S);
+    c.stats.assign(h_stats, h_stats + 4ull * p.S);
+    c.checks.assign(h_checks, h_checks + 2);
+    c.src_piece_start.assign(h_sps, h_sps + p.S + 1);
+    err = *h_err;
     if (err) throw dp::HipError{hipErrorUnknown, "internal plan consistency check (library bug)"};
 }
 
@@ -469,6 +513,19 @@ int pack_init(const pack_config* cfg, pack_ctx** out) {
         c->arena = static_cast<char*>(mem);
         c->arena_bytes = got;
         carve(*c, c->arena);
+        const size_t pbytes = pin_bytes_for(S);
+        void* pin = arena_take(c->device, pbytes, &got, true);
+        if (!pin) {
+            if (hipHostMalloc(&pin, pbytes, hipHostMallocDefault) != hipSuccess) {
+                (void)hipGetLastError();
+                g_init_error = "pinned host staging allocation failed";
+                release(c);
+                return PACK_E_NOMEM;
+            }
+            got = pbytes;
+        }
+        c->pin = static_cast<uint8_t*>(pin);
+        c->pin_bytes = got;
         build_plan(*c);
         c->cyc_start.assign(S, 0);
         c->cyc_next.assign(S, 0);
@@ -525,10 +582,10 @@ int pack_cycle(pack_ctx* c, uint32_t cycle, pack_cycle_info* info) {
         c->cycle = cycle;
         dp::Plan& p = c->p;
         c->timer.begin(PACK_PHASE_CYCLE, c->st);
-        h2d(p.cyc_start, c->cyc_start.data(), S, c->st);
+        c->pin_off = 0;
+        h2d_staged(*c, p.cyc_start, c->cyc_start.data(), S);
         dp::launch_cycle_sums(p, c->U, c->st);
-        uint64_t sums[2] = {0, 0};
-        d2h(sums, p.cyc_sums, 2, c->st);
+        const uint64_t* h_sums = d2h_staged(*c, p.cyc_sums, 2);
 
         // plan digest: SHA-256 of a little-endian description of the recipe,
         // stream sizes, cycle start and two order-free sums over the plan
@@ -555,12 +612,15 @@ int pack_cycle(pack_ctx* c, uint32_t cycle, pack_cycle_info* info) {
         put(msg, c->checks[0], 8);
         put(msg, c->checks[1], 8);
         if (msg.size() > c->dig_cap) throw InvalError{"internal: digest buffer"};
-        h2d(c->dig_buf, msg.data(), msg.size(), c->st);
+        h2d_staged(*c, c->dig_buf, msg.data(), msg.size());
         dp::launch_sha_bytes(c->dig_buf, msg.size(), c->dig_buf + c->dig_cap, c->st);
         c->timer.end(c->st);
-        uint8_t digest[32];
-        d2h(digest, c->dig_buf + c->dig_cap, 32, c->st);
+        const uint8_t* h_digest = d2h_staged(*c, (const uint8_t*)(c->dig_buf + c->dig_cap), 32);
         DP_HIP(hipStreamSynchronize(c->st));
+        const uint64_t sums[2] = {h_sums[0], h_sums[1]};
+        uint8_t digest[32];
+        std::memcpy(digest, h_digest, 32);
+        c->pin_off = 0;
 
         if (info) {
             info->cycle = cycle;

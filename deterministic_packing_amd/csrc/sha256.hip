@@ -279,7 +279,7 @@ __device__ __forceinline__ void publish(uint32_t* prog, uint32_t blocks, uint32_
     if (lane == 0) __hip_atomic_store(prog, blocks, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
-// Emits array s (0 tokens, 1 position ids, 2 document ids) of a lane's window
+// Emits the position ids (s = 1) or document ids (s = 2) of a lane's window
 // in runs: a run writes 16 elements from the piece holding position t and
 // advances t by the run's length within that piece, min(16, end − t); the
 // elements past the piece end are rewritten by the next run of the same lane
@@ -291,11 +291,10 @@ template <uint32_t s>
 __device__ __forceinline__ void emit_runs(const Plan& p, const EmitArgs& a, ECursor& c, uint32_t q0, uint32_t q1,
                                           uint32_t real, uint64_t w, bool valid, uint32_t* prog, uint32_t lane,
                                           uint32_t blk0) {
-    const uint32_t T = p.T, pad = p.pad_token;
-    const uint64_t n_tokens = p.n_tokens;
+    static_assert(s == 1 || s == 2, "position or document ids");
+    const uint32_t T = p.T;
     c.restart(p, q0, q1, real);
-    uint32_t* out = (s == 0 ? a.tok : s == 1 ? reinterpret_cast<uint32_t*>(a.pos) : reinterpret_cast<uint32_t*>(a.doc)) +
-                    w * T;
+    uint32_t* out = reinterpret_cast<uint32_t*>(s == 1 ? a.pos : a.doc) + w * T;
     uint32_t t = 0, published = 0, it = 0;
 #pragma unroll 1
     while (wave_any(t < T)) {
@@ -303,14 +302,9 @@ __device__ __forceinline__ void emit_runs(const Plan& p, const EmitArgs& a, ECur
             const EPiece& P = c.cur;
             const uint32_t end = c.nxt.woff < T ? c.nxt.woff : T;  // the piece's end in the window
             const uint32_t ne = end - t < 16 ? end - t : 16;
-            if (t + 16 <= T && (s != 0 || !P.pm || P.base + t + 16 <= n_tokens)) {
+            if (t + 16 <= T) {
                 uint32_t v[16];
-                if (s == 0) {
-                    if (P.pm) load16(v, p.tokens + P.base + t);
-                    else
-#pragma unroll
-                        for (int e = 0; e < 16; ++e) v[e] = pad;
-                } else if (s == 1) {
+                if (s == 1) {
                     const uint32_t pa = (t - P.woff) & P.pm, inc = P.pm & 1u;  // padding: all 0
 #pragma unroll
                     for (uint32_t e = 0; e < 16; ++e) v[e] = pa + e * inc;
@@ -319,16 +313,9 @@ __device__ __forceinline__ void emit_runs(const Plan& p, const EmitArgs& a, ECur
                     for (int e = 0; e < 16; ++e) v[e] = P.doc;
                 }
                 if (valid) store16(out + t, v);
-            } else {
+            } else if (valid) {
 #pragma unroll 1
-                for (uint32_t e = 0; e < ne; ++e) {
-                    const uint32_t te = t + e;
-                    const uint64_t at = P.base + te;
-                    const uint32_t v = s == 0 ? (P.pm && at < n_tokens ? p.tokens[at] : pad)
-                                     : s == 1 ? (te - P.woff) & P.pm
-                                              : P.doc;
-                    if (valid) out[te] = v;
-                }
+                for (uint32_t e = 0; e < ne; ++e) out[t + e] = s == 1 ? (t + e - P.woff) & P.pm : P.doc;
             }
             t += ne;
             if (t < T) c.seek(p, t, q1, real);
@@ -476,7 +463,7 @@ __global__ __launch_bounds__(64 * FWAVES) void k_emit_sha(Plan p, EmitArgs a, ui
 }
 
 // SHA-256 of an arbitrary byte string (4-byte aligned start), one lane.
-__device__ void sha_bytes(const uint8_t* msg, uint64_t len, uint8_t* out) {
+__device__ __forceinline__ void sha_bytes(const uint8_t* msg, uint64_t len, uint8_t* out) {
     uint32_t H[8];
     sha256_init(H);
     const uint64_t full = len / 64;
