@@ -6,7 +6,11 @@
 // Philox4x32-10(counter = (d lo, d hi, 0x53485546, 0), key = (seed lo, seed hi))
 // (Salmon et al., SC'11), so it depends only on the seed and the input index d,
 // never on rank, world or launch shape.  Kept documents enter the sort in
-// input order and every pass is stable, so ties of key64 fall back to d.
+// input order and every pass is stable.  The radix passes order by
+// (group, key64 >> 32) only; runs that tie there (rare: about n²/2^33 pairs
+// for n documents of a group) are then ordered by the low 32 key bits with a
+// stable insertion sort, which leaves ties of key64 in input order, so the
+// result is the order by (group, key64, d).
 #include "dp_common.h"
 
 namespace dp {
@@ -106,6 +110,33 @@ __global__ __launch_bounds__(RB) void k_scatter(const uint64_t* key_in, const ui
     }
 }
 
+// Orders each run of equal (group, key64 >> 32) by the low 32 key bits; the
+// thread at a run's first element sorts the run (insertion sort, stable).
+// Other threads only read the high key bits and groups, which the sort of a
+// run does not change.
+__global__ __launch_bounds__(256) void k_tie_fix(uint64_t* key, uint32_t* val, const uint32_t* group, uint64_t n) {
+    const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    const uint32_t hi = (uint32_t)(key[i] >> 32), g = group[val[i]];
+    auto same = [&](uint64_t j) { return (uint32_t)(key[j] >> 32) == hi && group[val[j]] == g; };
+    if (i > 0 && same(i - 1)) return;     // not the first element of its run
+    if (i + 1 >= n || !same(i + 1)) return;  // a run of one
+    uint64_t end = i + 2;
+    while (end < n && same(end)) ++end;
+    for (uint64_t a = i + 1; a < end; ++a) {
+        const uint64_t k = key[a];
+        const uint32_t v = val[a];
+        uint64_t b = a;
+        while (b > i && (uint32_t)key[b - 1] > (uint32_t)k) {
+            key[b] = key[b - 1];
+            val[b] = val[b - 1];
+            --b;
+        }
+        key[b] = k;
+        val[b] = v;
+    }
+}
+
 }  // namespace
 
 void launch_keep_scan(Plan& p, hipStream_t st) {
@@ -142,8 +173,13 @@ void launch_sort(Plan& p, hipStream_t st) {
         DP_HIP(hipGetLastError());
         cur ^= 1;
     };
-    for (int shift = 0; shift < 64; shift += 8) pass(false, shift);
+    for (int shift = 32; shift < 64; shift += 8) pass(false, shift);
     for (int shift = 0; p.G > 1 && shift < 32 && ((p.G - 1) >> shift) != 0; shift += 8) pass(true, shift);
+    if (n > 1) {
+        hipLaunchKernelGGL(k_tie_fix, dim3((uint32_t)((n + 255) / 256)), dim3(256), 0, st, p.key[cur], p.val[cur],
+                           (const uint32_t*)p.group, n);
+        DP_HIP(hipGetLastError());
+    }
     p.sort_buf = (uint32_t)cur;
 }
 
