@@ -93,85 +93,119 @@ struct Offs {
     __device__ inline uint64_t operator[](uint64_t d) const { return staged ? l[d - d0] : g[d]; }
 };
 
-__global__ __launch_bounds__(256) void k_hash_flat(Plan p, const uint32_t* first, uint64_t base, uint64_t end,
-                                                   uint64_t ntiles, uint64_t* S) {
-    __shared__ uint64_t s_off[OCAP + 1];
+// Loads the TPT + 1 tokens from t0 (the last one is the pair partner of the
+// thread's last token), all in bounds: callers pass t0 + TPT + 1 <= end.
+// (Non-temporal loads measured 1.6x slower here.)
+__device__ __forceinline__ void load_tokens(const uint32_t* tokens, uint64_t t0, uint32_t (&x)[TPT + 1]) {
+#pragma unroll
+    for (uint32_t q = 0; q < TPT / 4; ++q) {
+        const u32x4a4 v = *reinterpret_cast<const u32x4a4*>(tokens + t0 + 4 * q);
+        x[4 * q] = v.x; x[4 * q + 1] = v.y; x[4 * q + 2] = v.z; x[4 * q + 3] = v.w;
+    }
+    x[TPT] = tokens[t0 + TPT];
+}
+
+// One tile: the tile's document offsets into LDS, each thread's documents and
+// NH terms, and the per-document sums into S (see above).  x holds the
+// thread's tokens from t0 (zeros past end).
+__device__ __forceinline__ void hash_tile(const Plan& p, const uint32_t* first, uint64_t base, uint64_t end,
+                                          uint64_t tile, const uint32_t (&x)[TPT + 1], uint64_t* s_off,
+                                          uint64_t* S) {
     const uint32_t lane = lane_id();
-    for (uint64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-        const uint64_t t0 = base + tile * HT + (uint64_t)TPT * threadIdx.x;  // this thread's first token
-        const uint64_t d_lo = first[tile], d_hi = first[tile + 1];  // documents of the tile
-        Offs off{p.offsets, s_off, d_lo, d_hi - d_lo + 2 <= OCAP + 1};
-        __syncthreads();  // the previous tile's readers are done with s_off
-        if (off.staged)
-            for (uint64_t i = threadIdx.x; i < d_hi - d_lo + 2; i += blockDim.x) s_off[i] = p.offsets[d_lo + i];
-        __syncthreads();
-        const bool active = t0 < end;
-        uint32_t fd = 0xFFFFFFFFu, ld = 0xFFFFFFFFu;
-        uint64_t v1 = 0, v2 = 0;
-        if (active) {
-            uint32_t x[TPT + 1];
-            if (t0 + TPT <= end) {
+    const uint64_t t0 = base + tile * HT + (uint64_t)TPT * threadIdx.x;  // this thread's first token
+    const uint64_t d_lo = first[tile], d_hi = first[tile + 1];  // documents of the tile
+    Offs off{p.offsets, s_off, d_lo, d_hi - d_lo + 2 <= OCAP + 1};
+    __syncthreads();  // the previous tile's readers are done with s_off
+    if (off.staged)
+        for (uint64_t i = threadIdx.x; i < d_hi - d_lo + 2; i += blockDim.x) s_off[i] = p.offsets[d_lo + i];
+    __syncthreads();
+    const bool active = t0 < end;
+    uint32_t fd = 0xFFFFFFFFu, ld = 0xFFFFFFFFu;
+    uint64_t v1 = 0, v2 = 0;
+    if (active) {
+        // document of t0: search between the tile's first document and the next tile's
+        uint64_t lo = d_lo, hi = d_hi + 1;  // d in [lo, hi)
+        while (hi - lo > 1) {
+            const uint64_t mid = (lo + hi) >> 1;
+            if (off[mid] <= t0) lo = mid;
+            else hi = mid;
+        }
+        uint32_t cur = (uint32_t)lo;
+        fd = cur;
+        uint64_t ob = off[cur], nb = off[cur + 1];
+        uint64_t acc = 0;
 #pragma unroll
-                for (uint32_t q = 0; q < TPT / 4; ++q) {
-                    const u32x4a4 v = *reinterpret_cast<const u32x4a4*>(p.tokens + t0 + 4 * q);
-                    x[4 * q] = v.x; x[4 * q + 1] = v.y; x[4 * q + 2] = v.z; x[4 * q + 3] = v.w;
+        for (uint32_t j = 0; j < TPT; ++j) {
+            const uint64_t pos = t0 + j;
+            if (pos < end) {
+                if (pos >= nb) {  // the next document starts: flush the finished one
+                    if (cur == fd) v1 = acc;
+                    else atomicAdd((unsigned long long*)&S[cur], (unsigned long long)acc);
+                    acc = 0;
+                    do {
+                        ++cur;
+                        ob = nb;
+                        nb = off[cur + 1];
+                    } while (pos >= nb);
                 }
-            } else {
-#pragma unroll
-                for (uint32_t j = 0; j < TPT; ++j) x[j] = (t0 + j < end) ? p.tokens[t0 + j] : 0u;
-            }
-            x[TPT] = (t0 + TPT < end) ? p.tokens[t0 + TPT] : 0u;
-            // document of t0: search between the tile's first document and the next tile's
-            uint64_t lo = d_lo, hi = d_hi + 1;  // d in [lo, hi)
-            while (hi - lo > 1) {
-                const uint64_t mid = (lo + hi) >> 1;
-                if (off[mid] <= t0) lo = mid;
-                else hi = mid;
-            }
-            uint32_t cur = (uint32_t)lo;
-            fd = cur;
-            uint64_t ob = off[cur], nb = off[cur + 1];
-            uint64_t acc = 0;
-#pragma unroll
-            for (uint32_t j = 0; j < TPT; ++j) {
-                const uint64_t pos = t0 + j;
-                if (pos < end) {
-                    if (pos >= nb) {  // the next document starts: flush the finished one
-                        if (cur == fd) v1 = acc;
-                        else atomicAdd((unsigned long long*)&S[cur], (unsigned long long)acc);
-                        acc = 0;
-                        do {
-                            ++cur;
-                            ob = nb;
-                            nb = off[cur + 1];
-                        } while (pos >= nb);
-                    }
-                    const uint64_t r = pos - ob;
-                    if ((r & 1) == 0) acc += pair_term(x[j], pos + 1 < nb ? x[j + 1] : 0u, r);
-                }
-            }
-            if (cur == fd) v1 = acc;
-            else {
-                ld = cur;
-                v2 = acc;
+                const uint64_t r = pos - ob;
+                if ((r & 1) == 0) acc += pair_term(x[j], pos + 1 < nb ? x[j + 1] : 0u, r);
             }
         }
-        // the last document's part joins the next lane's first document when they match
-        const uint32_t fd_next = __shfl_down(fd, 1, WAVE);
-        if (ld != 0xFFFFFFFFu && (lane == WAVE - 1 || fd_next != ld))
-            atomicAdd((unsigned long long*)&S[ld], (unsigned long long)v2);
-        const uint32_t ld_prev = __shfl_up(ld, 1, WAVE);
-        const uint64_t v2_prev = __shfl_up(v2, 1, WAVE);
-        if (lane > 0 && ld_prev != 0xFFFFFFFFu && ld_prev == fd) v1 += v2_prev;
-        // segmented inclusive scan of v1 by fd (fd is nondecreasing across lanes)
-#pragma unroll
-        for (int o = 1; o < WAVE; o <<= 1) {
-            const uint64_t y = __shfl_up(v1, o, WAVE);
-            const uint32_t fy = __shfl_up(fd, o, WAVE);
-            if (lane >= (uint32_t)o && fy == fd) v1 += y;
+        if (cur == fd) v1 = acc;
+        else {
+            ld = cur;
+            v2 = acc;
         }
-        if (fd != 0xFFFFFFFFu && (lane == WAVE - 1 || fd_next != fd))
-            atomicAdd((unsigned long long*)&S[fd], (unsigned long long)v1);
+    }
+    // the last document's part joins the next lane's first document when they match
+    const uint32_t fd_next = __shfl_down(fd, 1, WAVE);
+    if (ld != 0xFFFFFFFFu && (lane == WAVE - 1 || fd_next != ld))
+        atomicAdd((unsigned long long*)&S[ld], (unsigned long long)v2);
+    const uint32_t ld_prev = __shfl_up(ld, 1, WAVE);
+    const uint64_t v2_prev = __shfl_up(v2, 1, WAVE);
+    if (lane > 0 && ld_prev != 0xFFFFFFFFu && ld_prev == fd) v1 += v2_prev;
+    // segmented inclusive scan of v1 by fd (fd is nondecreasing across lanes)
+#pragma unroll
+    for (int o = 1; o < WAVE; o <<= 1) {
+        const uint64_t y = __shfl_up(v1, o, WAVE);
+        const uint32_t fy = __shfl_up(fd, o, WAVE);
+        if (lane >= (uint32_t)o && fy == fd) v1 += y;
+    }
+    if (fd != 0xFFFFFFFFu && (lane == WAVE - 1 || fd_next != fd))
+        atomicAdd((unsigned long long*)&S[fd], (unsigned long long)v1);
+}
+
+// Tiles [0, nfast) have every thread's TPT + 1 tokens inside [base, end):
+// they run two at a time, the next tile's loads issued (unconditionally, at a
+// clamped tile) before the current tile is hashed.  The last tiles load
+// element by element with bounds checks.
+__global__ __launch_bounds__(256) void k_hash_flat(Plan p, const uint32_t* first, uint64_t base, uint64_t end,
+                                                   uint64_t ntiles, uint64_t nfast, uint64_t* S) {
+    __shared__ uint64_t s_off[OCAP + 1];
+    const uint32_t* tok = p.tokens;
+    const uint64_t step = gridDim.x;
+    uint64_t ta = blockIdx.x;
+    if (ta < nfast) {
+        uint32_t xa[TPT + 1], xb[TPT + 1];
+        load_tokens(tok, base + ta * HT + (uint64_t)TPT * threadIdx.x, xa);
+        while (true) {
+            const uint64_t tb = ta + step;
+            load_tokens(tok, base + (tb < nfast ? tb : ta) * HT + (uint64_t)TPT * threadIdx.x, xb);
+            hash_tile(p, first, base, end, ta, xa, s_off, S);
+            if (tb >= nfast) break;
+            ta = tb + step;
+            load_tokens(tok, base + (ta < nfast ? ta : tb) * HT + (uint64_t)TPT * threadIdx.x, xa);
+            hash_tile(p, first, base, end, tb, xb, s_off, S);
+            if (ta >= nfast) break;
+        }
+    }
+    for (uint64_t tile = nfast + blockIdx.x; tile < ntiles; tile += step) {
+        const uint64_t t0 = base + tile * HT + (uint64_t)TPT * threadIdx.x;
+        uint32_t x[TPT + 1];
+#pragma unroll
+        for (uint32_t j = 0; j <= TPT; ++j) x[j] = (t0 + j < end) ? tok[t0 + j] : 0u;
+        hash_tile(p, first, base, end, tile, x, s_off, S);
     }
 }
 
@@ -232,8 +266,10 @@ void launch_hash(const Plan& p, uint64_t base, uint64_t end, uint64_t* S, uint32
     if (ntiles) {
         hipLaunchKernelGGL(k_tile_first_doc, dim3((uint32_t)((ntiles + 1 + 255) / 256)), dim3(256), 0, st, p, base,
                            ntiles, first);
+        // tiles whose every thread reads TPT + 1 tokens below end
+        const uint64_t nfast = (end - base - 1) / HT;
         hipLaunchKernelGGL(k_hash_flat, dim3((uint32_t)std::min<uint64_t>(ntiles, 16384)), dim3(256), 0, st, p,
-                           (const uint32_t*)first, base, end, ntiles, S);
+                           (const uint32_t*)first, base, end, ntiles, nfast, S);
     }
     const uint32_t lds_bins = p.S <= 256 ? 1u : 0u;
     const size_t lds = lds_bins ? 4ull * p.S * sizeof(uint64_t) : 0;
