@@ -171,11 +171,19 @@ __global__ __launch_bounds__(256) void k_next(Plan p) {
     p.jump[q] = (lo == pe) ? END : (uint32_t)lo;
 }
 
-__global__ __launch_bounds__(256) void k_lift(const uint32_t* prev, uint32_t* next, uint64_t n) {
+// Levels l+1 .. l+k (k <= 3) from level l in one launch: level l+i is
+// next^(2^(l+i)) = level l applied 2^i times, so a thread follows level l
+// from q and records every power-of-two step (2, 4, 8 lookups).
+__global__ __launch_bounds__(256) void k_lift(const uint32_t* lev, uint32_t* out, uint64_t stride, uint32_t k,
+                                              uint64_t n) {
     const uint64_t q = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (q >= n) return;
-    const uint32_t x = prev[q];
-    next[q] = (x == END) ? END : prev[x];
+    uint32_t x = (uint32_t)q;
+    uint32_t steps = 0;
+    for (uint32_t i = 1; i <= k; ++i) {
+        for (const uint32_t target = 1u << i; steps < target; ++steps) x = (x == END) ? END : lev[x];
+        out[(uint64_t)(i - 1) * stride + q] = x;
+    }
 }
 
 // windows per source by lifting from its first piece, then their prefix
@@ -422,10 +430,13 @@ void launch_pieces(Plan& p, hipStream_t st) {
 void launch_lifting(Plan& p, hipStream_t st) {
     if (p.n_pieces == 0) return;
     hipLaunchKernelGGL(k_next, dim3(blocks_for(p.n_pieces)), dim3(256), 0, st, p);
-    for (uint32_t l = 1; l < p.levels; ++l)
+    for (uint32_t l = 1; l < p.levels;) {  // levels l .. l+k-1 from level l-1
+        const uint32_t k = p.levels - l < 3 ? p.levels - l : 3;
         hipLaunchKernelGGL(k_lift, dim3(blocks_for(p.n_pieces)), dim3(256), 0, st,
                            (const uint32_t*)(p.jump + (uint64_t)(l - 1) * p.cap_pieces),
-                           p.jump + (uint64_t)l * p.cap_pieces, p.n_pieces);
+                           p.jump + (uint64_t)l * p.cap_pieces, p.cap_pieces, k, p.n_pieces);
+        l += k;
+    }
     DP_HIP(hipGetLastError());
 }
 
