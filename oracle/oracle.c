@@ -20,6 +20,8 @@
  *   [LI]  Linnet "Training" docs — "Supervised fine-tuning" (pack to exactly
  *         T positions, completion-only loss, learned-position counts),
  *         "Other trainers" (position ids restart at 0 per sequence).
+ *   [ZE'] the same Zephon post, its minimal example (a pipeline that packs
+ *         with pack_flat(max_length, algorithm="wrap")).
  *
  * Parity status of each part (what pins it is in the test suite):
  *   - doc hash (C1): the pages name no hash function, so the function itself
@@ -301,6 +303,7 @@ typedef struct {
     uint32_t T, B;
     uint64_t seed;
     uint32_t pad_token;
+    uint32_t wrap;               /* 0: next-fit cut at document ends; 1: wrap (C5w) */
 } or_corpus;
 
 typedef struct {
@@ -445,6 +448,51 @@ or_plan *or_plan_build(const or_corpus *cin, int *err)
     for (uint64_t i = 0; i < p->n_kept; i++)
         p->order_check += or_mix64((i << 32) ^ (uint64_t)p->order[i]);
 
+    /* C5w, wrap packing ([ZE'] pack_flat(..., algorithm="wrap"); the page
+     * gives only the name).  Reading: per source, the merged order's tokens
+     * are one stream, cut every T tokens into windows; a document that
+     * crosses a cut is split there and continues at the next window's first
+     * position (its pieces restart position ids at 0, [LI] Other trainers);
+     * only the stream's last window can be short, and its rest is padding.
+     * A piece is a maximal run of one document inside one window. */
+    if (c->wrap) {
+        uint64_t P = 0, M = 0;
+        for (uint32_t s = 0; s < S; s++) {
+            uint64_t x = 0;  /* stream position of the next token */
+            for (uint64_t i = p->src_doc_start[s]; i < p->src_doc_start[s + 1]; i++) {
+                uint64_t L = doc_len(c, p->order[i]);
+                for (uint64_t o = 0; o < L;) {
+                    uint64_t room = T - x % T, len = (L - o < room) ? (L - o) : room;
+                    P++; o += len; x += len;
+                }
+            }
+            M += (x + T - 1) / T;
+        }
+        p->n_pieces = P;
+        p->n_windows = M;
+        ALLOC(p->pc_doc, P); ALLOC(p->pc_off, P); ALLOC(p->pc_len, P); ALLOC(p->pc_woff, P);
+        ALLOC(p->win_first, M + 1); ALLOC(p->win_real, M); ALLOC(p->win_learn, M);
+        uint64_t q = 0, w = 0;
+        for (uint32_t s = 0; s < S; s++) {
+            p->src_piece_start[s] = q;
+            p->src_win_start[s] = w;
+            uint64_t x = 0;
+            for (uint64_t i = p->src_doc_start[s]; i < p->src_doc_start[s + 1]; i++) {
+                uint32_t d = p->order[i];
+                uint64_t L = doc_len(c, d);
+                for (uint64_t o = 0; o < L;) {
+                    uint64_t room = T - x % T, len = (L - o < room) ? (L - o) : room;
+                    if (x % T == 0) p->win_first[w++] = q;  /* the piece opens a window */
+                    p->pc_doc[q] = d; p->pc_off[q] = (uint32_t)o; p->pc_len[q] = (uint32_t)len;
+                    p->pc_woff[q] = (uint32_t)(x % T);
+                    q++; o += len; x += len;
+                }
+            }
+        }
+        p->src_piece_start[S] = q;
+        p->src_win_start[S] = w;
+        p->win_first[M] = q;
+    } else {
     /* C5a: split documents into pieces: a document of L ≤ T tokens is one
      * piece; a longer one is floor(L/T) pieces of T tokens plus a tail piece
      * of the rest, if any.  Count first, then fill. */
@@ -503,6 +551,7 @@ or_plan *or_plan_build(const or_corpus *cin, int *err)
         p->src_win_start[S] = w;
         p->win_first[M] = p->src_piece_start[S];
     }
+    }  /* next-fit */
 
     /* Real and learned positions of each window.  A position is learned when
      * its token lies at or after the document's prompt ([LI] Supervised
@@ -692,7 +741,7 @@ int or_plan_digest(const or_plan *p, uint8_t out[32])
     uint64_t bytes = 8 + 4 + 4 + 8 + 4 + 4 + (uint64_t)S * (8 + 4 + 4 + 4 + 8 + 8 + 8) + 4 + 4 + 8ull * S + 8 + 8;
     uint8_t *buf = (uint8_t *)malloc(bytes), *w = buf;
     if (!buf) return OR_E_NOMEM;
-    memcpy(w, "DPACKPD1", 8); w += 8;
+    memcpy(w, c->wrap ? "DPACKPW1" : "DPACKPD1", 8); w += 8;  /* the packing mode is part of the plan */
     put(&w, c->T, 4); put(&w, c->B, 4); put(&w, c->seed, 8); put(&w, S, 4); put(&w, c->pad_token, 4);
     for (uint32_t s = 0; s < S; s++) {
         put(&w, c->weight[s], 8); put(&w, c->bp[s], 4); put(&w, c->n_strata[s], 4);

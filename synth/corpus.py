@@ -45,6 +45,7 @@ class Corpus:
     seed: int = 0
     pad_token: int = 0
     meta: Dict = dataclasses.field(default_factory=dict)
+    wrap: bool = False          # packing: False = next-fit cut at document ends, True = wrap
 
     @property
     def n_docs(self) -> int:
