@@ -75,6 +75,7 @@ def main():
                     help="updates the oracle emits for the CPU baseline (the plan is always whole)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-copy", action="store_true", help="skip the plain D2D copy used as calibration/ceiling")
+    ap.add_argument("--wrap", action="store_true", help="wrap packing (PACK_FLAG_WRAP) instead of next-fit")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -93,7 +94,7 @@ def main():
     dp.load_library()
 
     t0 = time.time()
-    corpus = make_corpus(args.workload, args.scale)
+    corpus = make_corpus(args.workload, args.scale).replace(wrap=args.wrap)
     log(f"corpus {args.workload} scale {args.scale}: {corpus.n_docs} docs, {corpus.n_tokens} tokens "
         f"({time.time() - t0:.1f}s)")
     tensors = dp.upload_corpus(corpus)
@@ -255,7 +256,8 @@ def main():
         "vs_baseline": None,
         "dtype": "u32",
         "data": "synthetic",
-        "config": {"workload": WORKLOAD_TEXT[args.workload] + ("" if args.scale == 1.0 else f" (scale {args.scale})"),
+        "config": {"workload": WORKLOAD_TEXT[args.workload] + ("" if args.scale == 1.0 else f" (scale {args.scale})")
+                   + (", wrap packing" if args.wrap else ""),
                    "docs": corpus.n_docs, "tokens": corpus.n_tokens, "T": T, "B": B, "updates": U,
                    "real_tokens_per_step": real, "positions_per_step": positions,
                    "step": "pack_init + pack_cycle + pack_batch(all updates, learned, digests) + pack_destroy"},

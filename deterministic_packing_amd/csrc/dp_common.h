@@ -83,6 +83,7 @@ struct Plan {
     uint32_t S, G, T, B;
     uint64_t seed;
     uint32_t pad_token;
+    uint32_t wrap;                // 1: wrap packing (cut every T tokens), 0: next-fit
 
     // recipe on device
     uint32_t* gbase;              // [S+1] first group of each source
@@ -242,6 +243,9 @@ void scan_keep_u32(const uint8_t* flags, uint64_t n, uint32_t* out, void* tmp, h
 void scan_u32(const uint32_t* in, uint64_t n, uint32_t* out, void* tmp, hipStream_t st);
 void scan_len_u64(const uint32_t* ids, const uint64_t* offsets, uint64_t n, uint64_t* out, void* tmp,
                   hipStream_t st);
+void scan_wrap_pieces_u32(const uint32_t* ids, const uint64_t* offsets, const uint64_t* opre,
+                          const uint64_t* src_doc_start, const uint16_t* source, uint32_t T, uint64_t n,
+                          uint32_t* out, void* tmp, hipStream_t st);
 void scan_pieces_u32(const uint32_t* ids, const uint64_t* offsets, uint32_t T, uint64_t n, uint32_t* out,
                      void* tmp, hipStream_t st);
 

@@ -131,13 +131,31 @@ __global__ __launch_bounds__(256) void k_pieces(Plan p) {
     const uint64_t L = p.offsets[d + 1] - p.offsets[d];
     const uint32_t np = p.piece_start[i + 1] - q0;
     const uint64_t pre = p.opre[i];
-    for (uint32_t r = 0; r < np; ++r) {
-        const uint64_t o = (uint64_t)r * p.T;
-        const uint32_t q = q0 + r;
-        p.pc_doc[q] = d;
-        p.pc_off[q] = (uint32_t)o;
-        p.pc_len[q] = (uint32_t)((L - o) < p.T ? (L - o) : p.T);
-        p.pc_pre[q] = pre + o;
+    if (!p.wrap) {
+        for (uint32_t r = 0; r < np; ++r) {
+            const uint64_t o = (uint64_t)r * p.T;
+            const uint32_t q = q0 + r;
+            p.pc_doc[q] = d;
+            p.pc_off[q] = (uint32_t)o;
+            p.pc_len[q] = (uint32_t)((L - o) < p.T ? (L - o) : p.T);
+            p.pc_pre[q] = pre + o;
+        }
+    } else {
+        // wrap: cut where the source's stream crosses a multiple of T
+        uint64_t x = pre - p.opre[p.src_doc_start[p.source[d]]];  // stream position of the first token
+        uint64_t o = 0;
+        for (uint32_t r = 0; r < np; ++r) {
+            const uint64_t room = p.T - x % p.T;
+            const uint64_t len = (L - o) < room ? (L - o) : room;
+            const uint32_t q = q0 + r;
+            p.pc_doc[q] = d;
+            p.pc_off[q] = (uint32_t)o;
+            p.pc_len[q] = (uint32_t)len;
+            p.pc_pre[q] = pre + o;
+            o += len;
+            x += len;
+        }
+        if (o != L) atomicOr(p.err, ERR_INTERNAL);  // piece count and cut disagree
     }
     if (i == p.n_kept - 1) p.pc_pre[p.n_pieces] = p.opre[p.n_kept];
 }
@@ -226,6 +244,32 @@ __global__ __launch_bounds__(256) void k_windows(Plan p) {
         if ((w >> l) & 1) cur = p.jump[(uint64_t)l * p.cap_pieces + cur];
     p.win_first[gw] = cur;
     if (gw == p.n_windows - 1) p.win_first[p.n_windows] = (uint32_t)p.n_pieces;
+}
+
+// Wrap packing: source s has ceil(Λ_s / T) windows (Λ_s its kept tokens), and
+// window w of s starts at the piece whose stream position is w·T.
+__global__ __launch_bounds__(1024) void k_wrap_window_count(Plan p) {
+    if (threadIdx.x != 0) return;
+    uint64_t run = 0;
+    for (uint32_t s = 0; s < p.S; ++s) {
+        p.src_win_start[s] = run;
+        const uint64_t lam = p.opre[p.src_doc_start[s + 1]] - p.opre[p.src_doc_start[s]];
+        run += (lam + p.T - 1) / p.T;
+    }
+    p.src_win_start[p.S] = run;
+}
+
+__global__ __launch_bounds__(256) void k_wrap_windows(Plan p) {
+    const uint64_t q = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (q >= p.n_pieces) return;
+    const uint32_t s = upper_bound_u64(p.src_piece_start, p.S + 1, q) - 1;
+    const uint64_t y = p.pc_pre[q] - p.opre[p.src_doc_start[s]];  // stream position of the piece
+    if (y % p.T == 0) {
+        const uint64_t gw = p.src_win_start[s] + y / p.T;
+        if (gw < p.n_windows) p.win_first[gw] = (uint32_t)q;
+        else atomicOr(p.err, ERR_INTERNAL);
+    }
+    if (q == p.n_pieces - 1) p.win_first[p.n_windows] = (uint32_t)p.n_pieces;
 }
 
 // offsets of pieces in their window; real and learned positions per window
@@ -417,8 +461,12 @@ void launch_merge(Plan& p, hipStream_t st) {
 }
 
 void launch_piece_count(Plan& p, hipStream_t st) {
-    scan_pieces_u32(p.order, p.offsets, p.T, p.n_kept, p.piece_start, p.hist, st);
     scan_len_u64(p.order, p.offsets, p.n_kept, p.opre, p.hist, st);
+    if (p.wrap)
+        scan_wrap_pieces_u32(p.order, p.offsets, p.opre, p.src_doc_start, p.source, p.T, p.n_kept, p.piece_start,
+                             p.hist, st);
+    else
+        scan_pieces_u32(p.order, p.offsets, p.T, p.n_kept, p.piece_start, p.hist, st);
 }
 
 void launch_pieces(Plan& p, hipStream_t st) {
@@ -428,7 +476,7 @@ void launch_pieces(Plan& p, hipStream_t st) {
 }
 
 void launch_lifting(Plan& p, hipStream_t st) {
-    if (p.n_pieces == 0) return;
+    if (p.n_pieces == 0 || p.wrap) return;  // wrap packing cuts by position, no next-fit
     hipLaunchKernelGGL(k_next, dim3(blocks_for(p.n_pieces)), dim3(256), 0, st, p);
     for (uint32_t l = 1; l < p.levels;) {  // levels l .. l+k-1 from level l-1
         const uint32_t k = p.levels - l < 3 ? p.levels - l : 3;
@@ -441,13 +489,15 @@ void launch_lifting(Plan& p, hipStream_t st) {
 }
 
 void launch_window_count(Plan& p, hipStream_t st) {
-    hipLaunchKernelGGL(k_window_count, dim3(1), dim3(1024), (size_t)p.S * sizeof(uint64_t), st, p);
+    if (p.wrap) hipLaunchKernelGGL(k_wrap_window_count, dim3(1), dim3(64), 0, st, p);
+    else hipLaunchKernelGGL(k_window_count, dim3(1), dim3(1024), (size_t)p.S * sizeof(uint64_t), st, p);
     DP_HIP(hipGetLastError());
 }
 
 void launch_windows(Plan& p, hipStream_t st) {
     if (p.n_windows == 0) return;
-    hipLaunchKernelGGL(k_windows, dim3(blocks_for(p.n_windows)), dim3(256), 0, st, p);
+    if (p.wrap) hipLaunchKernelGGL(k_wrap_windows, dim3(blocks_for(p.n_pieces)), dim3(256), 0, st, p);
+    else hipLaunchKernelGGL(k_windows, dim3(blocks_for(p.n_windows)), dim3(256), 0, st, p);
     hipLaunchKernelGGL(k_window_stats, dim3(blocks_for(p.n_windows)), dim3(256), 0, st, p);
     DP_HIP(hipGetLastError());
 }

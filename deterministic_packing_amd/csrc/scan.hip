@@ -110,6 +110,24 @@ struct PieceCountIn {
     }
 };
 
+// wrap packing: pieces of the document at order position i = windows of its
+// source's stream that it touches; x = its first token's stream position
+struct WrapPieceCountIn {
+    const uint32_t* ids;
+    const uint64_t* off;
+    const uint64_t* opre;           // token prefix over the order
+    const uint64_t* src_doc_start;  // [S+1] first order position of each source
+    const uint16_t* source;
+    uint32_t T;
+    __device__ uint32_t operator()(uint64_t i) const {
+        const uint32_t d = ids[i];
+        const uint64_t L = off[d + 1] - off[d];
+        if (L == 0) return 0;
+        const uint64_t x = opre[i] - opre[src_doc_start[source[d]]];
+        return (uint32_t)((x + L - 1) / T - x / T + 1);
+    }
+};
+
 template <typename T, typename In>
 void scan_impl(In in, uint64_t n, T* out, void* tmp, hipStream_t st) {
     const uint64_t nb = (n + STILE - 1) / STILE;
@@ -144,6 +162,11 @@ void scan_len_u64(const uint32_t* ids, const uint64_t* offsets, uint64_t n, uint
 void scan_pieces_u32(const uint32_t* ids, const uint64_t* offsets, uint32_t T, uint64_t n, uint32_t* out,
                      void* tmp, hipStream_t st) {
     scan_impl<uint32_t>(PieceCountIn{ids, offsets, T}, n, out, tmp, st);
+}
+void scan_wrap_pieces_u32(const uint32_t* ids, const uint64_t* offsets, const uint64_t* opre,
+                          const uint64_t* src_doc_start, const uint16_t* source, uint32_t T, uint64_t n,
+                          uint32_t* out, void* tmp, hipStream_t st) {
+    scan_impl<uint32_t>(WrapPieceCountIn{ids, offsets, opre, src_doc_start, source, T}, n, out, tmp, st);
 }
 
 }  // namespace dp

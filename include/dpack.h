@@ -61,6 +61,14 @@ typedef struct pack_ctx pack_ctx;
 /* pack_config.flags: record HIP events around every kernel phase on the
  * context's stream (read with pack_get_timings).  Changes no output byte. */
 #define PACK_FLAG_TIMING 1u
+/* pack_config.flags: wrap packing instead of next-fit.  "Zephon:
+ * deterministic data loading" (aixai.ru), minimal example, packs with
+ * pack_flat(max_length, algorithm="wrap"); the page gives only the name.
+ * Reading taken: per source, the merged order's tokens are one stream cut
+ * every T tokens; a document crossing a cut continues at the next window's
+ * first position, its position ids restarting at 0; only each source's last
+ * window can be short (padded).  Every other output is as with next-fit. */
+#define PACK_FLAG_WRAP 2u
 
 /* Kernel phases timed under PACK_FLAG_TIMING. */
 enum {
@@ -95,7 +103,7 @@ typedef struct pack_timings {
  * [64, 2^20]; 1 ≤ B ≤ 2^20; world ≥ 1 divides B; rank < world. */
 typedef struct pack_config {
     uint32_t abi_version;          /* DPACK_ABI_VERSION */
-    uint32_t flags;                /* 0, or PACK_FLAG_TIMING */
+    uint32_t flags;                /* 0 or PACK_FLAG_TIMING | PACK_FLAG_WRAP */
     const uint32_t *tokens;        /* device [n_tokens] token ids */
     uint64_t n_tokens;
     const uint64_t *doc_offsets;   /* device [n_docs+1]: document d is tokens[off[d], off[d+1]) */

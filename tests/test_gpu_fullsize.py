@@ -25,7 +25,8 @@ def _setup(name):
         import torch
         torch.cuda.empty_cache()
         say("generate", name)
-        c = make_corpus(name)
+        wrap = name.startswith("wrap-")
+        c = make_corpus(name[5:] if wrap else name).replace(wrap=wrap)
         say("oracle plan", name, c.n_docs, "docs", c.n_tokens, "tokens")
         op = oracle.Plan(c)
         oi = op.cycle(0)
@@ -40,8 +41,10 @@ def _setup(name):
 # (workload, updates emitted per call: None = the whole cycle in one call, as the
 # bench does; else the first a and the last b updates of the cycle).  The full
 # workload's second call holds 67,584 windows, more than the one-kernel
-# emission-and-digest launch takes, so it covers the two-kernel path.
-FULL = [("tiny", None), ("pretrain", None), ("sft", None), ("long", None), ("full", (24, 66))]
+# emission-and-digest launch takes, so it covers the two-kernel path;
+# wrap-pretrain is the pre-train workload with wrap packing.
+FULL = [("tiny", None), ("pretrain", None), ("sft", None), ("long", None), ("full", (24, 66)),
+        ("wrap-pretrain", None)]
 
 
 @pytest.mark.parametrize("name,cap", FULL)

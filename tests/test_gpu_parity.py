@@ -40,7 +40,16 @@ def _corpus(kind, arg):
 
 @pytest.mark.parametrize("kind,arg", SMALL_CASES)
 def test_plan_cycle_batch_parity(kind, arg):
-    c = _corpus(kind, arg)
+    _parity_run(_corpus(kind, arg), kind, arg)
+
+
+@pytest.mark.parametrize("kind,arg", SMALL_CASES)
+def test_wrap_plan_cycle_batch_parity(kind, arg):
+    """The same cases with wrap packing (PACK_FLAG_WRAP)."""
+    _parity_run(_corpus(kind, arg).replace(wrap=True), "wrap-" + kind, arg)
+
+
+def _parity_run(c, kind, arg):
     say("plan/cycle/batch", kind, arg, "docs", c.n_docs, "T", c.T, "B", c.B)
     op = oracle.Plan(c)
     pk = dp.Packer(c)
@@ -69,9 +78,11 @@ def test_plan_cycle_batch_parity(kind, arg):
 
 
 @pytest.mark.parametrize("kind,arg,worlds", [("tiny", 0.5, [1, 2, 4, 8]), ("pretrain", 0.006, [1, 8, 16, 32, 64]),
-                                             ("small", 4, [1, 2, 4, 8])])
+                                             ("small", 4, [1, 2, 4, 8]), ("wrap-pretrain", 0.006, [1, 8, 64])])
 def test_elastic_rank_counts_identical(kind, arg, worlds):
-    c = _corpus(kind, arg)
+    wrap = kind.startswith("wrap-")
+    kind = kind[5:] if wrap else kind
+    c = _corpus(kind, arg).replace(wrap=wrap)
     if kind == "small":
         c = c.replace(B=8)
     if kind == "pretrain":
@@ -221,7 +232,15 @@ EDGE = {
 
 @pytest.mark.parametrize("name", sorted(EDGE))
 def test_edge_cases(name):
-    c = EDGE[name]()
+    _edge_run(EDGE[name](), name)
+
+
+@pytest.mark.parametrize("name", sorted(EDGE))
+def test_wrap_edge_cases(name):
+    _edge_run(EDGE[name]().replace(wrap=True), "wrap-" + name)
+
+
+def _edge_run(c, name):
     say("edge", name)
     op = oracle.Plan(c)
     pk = dp.Packer(c)
