@@ -304,6 +304,7 @@ typedef struct {
     uint64_t seed;
     uint32_t pad_token;
     uint32_t wrap;               /* 0: next-fit cut at document ends; 1: wrap (C5w) */
+    uint32_t heldout;            /* 1: the stream is the held-out documents (C2v) */
 } or_corpus;
 
 typedef struct {
@@ -371,14 +372,20 @@ or_plan *or_plan_build(const or_corpus *cin, int *err)
     ALLOC(gbase, S + 1);
 
     /* C1 + C2: hash every document, decide hold-out; a kept document is one
-     * that is not held out and has at least one token. */
+     * that is not held out and has at least one token.
+     * C2v (heldout): the validation stream.  [NS] Concepts: each source's
+     * validation rows come from its held-out documents of every stratum, and
+     * the validation mix weights the sources by the recipe.  Reading: the same
+     * plan (shuffle, strata merge, cut, mixture) over the non-empty held-out
+     * documents instead of the kept ones; kept_* then count the stream's
+     * documents, held_* still the documents the hash holds out. */
     p->n_kept = 0;
     for (uint64_t d = 0; d < D; d++) {
         uint64_t L = doc_len(c, d);
         uint32_t s = c->source[d];
         p->hash[d] = or_doc_hash(c->tokens + c->offsets[d], L);
         int held = or_held(p->hash[d], c->bp[s]);
-        p->keep[d] = (uint8_t)(!held && L > 0);
+        p->keep[d] = (uint8_t)((c->heldout ? held : !held) && L > 0);
         if (held) { p->held_docs[s]++; p->held_tokens[s] += L; }
         if (p->keep[d]) { p->kept_docs[s]++; p->kept_tokens[s] += L; p->n_kept++; p->hash_check += p->hash[d]; }
     }
@@ -741,7 +748,10 @@ int or_plan_digest(const or_plan *p, uint8_t out[32])
     uint64_t bytes = 8 + 4 + 4 + 8 + 4 + 4 + (uint64_t)S * (8 + 4 + 4 + 4 + 8 + 8 + 8) + 4 + 4 + 8ull * S + 8 + 8;
     uint8_t *buf = (uint8_t *)malloc(bytes), *w = buf;
     if (!buf) return OR_E_NOMEM;
-    memcpy(w, c->wrap ? "DPACKPW1" : "DPACKPD1", 8); w += 8;  /* the packing mode is part of the plan */
+    /* the packing mode and the stream (training / held-out) are part of the plan */
+    memcpy(w, "DPACKP", 6); w += 6;
+    *w++ = c->wrap ? 'W' : 'D';
+    *w++ = c->heldout ? 'V' : '1';
     put(&w, c->T, 4); put(&w, c->B, 4); put(&w, c->seed, 8); put(&w, S, 4); put(&w, c->pad_token, 4);
     for (uint32_t s = 0; s < S; s++) {
         put(&w, c->weight[s], 8); put(&w, c->bp[s], 4); put(&w, c->n_strata[s], 4);

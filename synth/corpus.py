@@ -46,6 +46,7 @@ class Corpus:
     pad_token: int = 0
     meta: Dict = dataclasses.field(default_factory=dict)
     wrap: bool = False          # packing: False = next-fit cut at document ends, True = wrap
+    heldout: bool = False       # stream: False = training documents, True = held-out (validation)
 
     @property
     def n_docs(self) -> int:

@@ -98,15 +98,16 @@ def test_every_update_within_two_samples_of_share():
 
 # --------------------------------------------------------------- hold-out, shuffle and strata merge by brute force
 
-def _brute_order(c: Corpus):
-    """Kept docs and their per-source order, from the pinned primitives with
-    Python big ints, Python's sorted and exact Fractions."""
+def _brute_order(c: Corpus, heldout: bool = False):
+    """Kept docs (with heldout, the non-empty held-out ones) and their
+    per-source order, from the pinned primitives with Python big ints,
+    Python's sorted and exact Fractions."""
     L = c.lengths()
     keep = []
     for d in range(c.n_docs):
         h = oracle.doc_hash(c.tokens[c.offsets[d]:c.offsets[d + 1]])
         held = ((h * 10000) >> 64) < int(c.holdout_bp[c.source[d]])
-        keep.append((not held) and L[d] > 0)
+        keep.append((held if heldout else not held) and L[d] > 0)
     order = []
     for s in range(c.n_sources):
         strata = []
