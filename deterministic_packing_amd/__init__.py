@@ -33,6 +33,7 @@ SYMBOLS = ("pack_init", "pack_cycle", "pack_batch", "pack_fingerprint", "pack_in
 
 PACK_FLAG_TIMING = 1
 PACK_FLAG_WRAP = 2
+PACK_FLAG_HELDOUT = 4
 PHASES = ("validate", "hash", "keys", "sort", "merge", "pieces", "cut", "windows", "mixture",
           "cycle", "emit", "learned", "digest", "fingerprint")
 
@@ -213,7 +214,8 @@ class Packer:
         assert self._host["weight"].shape[0] == S
         d = self.dev
         self.cfg = PackConfig(
-            ABI_VERSION, (PACK_FLAG_TIMING if timing else 0) | (PACK_FLAG_WRAP if getattr(corpus, "wrap", False) else 0),
+            ABI_VERSION, (PACK_FLAG_TIMING if timing else 0) | (PACK_FLAG_WRAP if getattr(corpus, "wrap", False) else 0)
+            | (PACK_FLAG_HELDOUT if getattr(corpus, "heldout", False) else 0),
             d["tokens"].data_ptr() if d["tokens"].numel() else None, int(d["tokens"].numel()),
             d["offsets"].data_ptr(), int(d["source"].numel()),
             d["source"].data_ptr(), d["stratum"].data_ptr() if d.get("stratum") is not None else None,

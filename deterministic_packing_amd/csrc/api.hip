@@ -277,7 +277,7 @@ void sync_staged(pack_ctx& c) {
 
 void check_config(const pack_config* cfg) {
     auto bad = [](const char* m) { throw InvalError{m}; };
-    if (cfg->flags & ~(PACK_FLAG_TIMING | PACK_FLAG_WRAP)) bad("unknown flags");
+    if (cfg->flags & ~(PACK_FLAG_TIMING | PACK_FLAG_WRAP | PACK_FLAG_HELDOUT)) bad("unknown flags");
     if (cfg->n_docs < 1 || cfg->n_docs >= (1ull << 31)) bad("n_docs must be in [1, 2^31)");
     if (!cfg->doc_offsets || !cfg->doc_source) bad("doc_offsets and doc_source are required");
     if (cfg->n_tokens && !cfg->tokens) bad("tokens is NULL with n_tokens > 0");
@@ -496,6 +496,7 @@ int pack_init(const pack_config* cfg, pack_ctx** out) {
         p.seed = cfg->seed;
         p.pad_token = cfg->pad_token;
         p.wrap = (cfg->flags & PACK_FLAG_WRAP) ? 1u : 0u;
+        p.heldout = (cfg->flags & PACK_FLAG_HELDOUT) ? 1u : 0u;
         p.cap_pieces = cfg->n_docs + cfg->n_tokens / cfg->window_tokens;
         if (p.cap_pieces >= 0xFFFFFFFFull) throw InvalError{"too many pieces for 32-bit piece indices"};
 
@@ -591,8 +592,8 @@ int pack_cycle(pack_ctx* c, uint32_t cycle, pack_cycle_info* info) {
         // plan digest: SHA-256 of a little-endian description of the recipe,
         // stream sizes, cycle start and two order-free sums over the plan
         std::vector<uint8_t> msg;
-        // the packing mode is part of the plan: "DPACKPD1" next-fit, "DPACKPW1" wrap
-        const char magic[8] = {'D', 'P', 'A', 'C', 'K', 'P', p.wrap ? 'W' : 'D', '1'};
+        // the packing mode (D next-fit, W wrap) and the stream (1 training, V held-out) are part of the plan
+        const char magic[8] = {'D', 'P', 'A', 'C', 'K', 'P', p.wrap ? 'W' : 'D', p.heldout ? 'V' : '1'};
         msg.insert(msg.end(), magic, magic + 8);
         put(msg, p.T, 4);
         put(msg, p.B, 4);

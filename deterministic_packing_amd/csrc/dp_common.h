@@ -84,6 +84,7 @@ struct Plan {
     uint64_t seed;
     uint32_t pad_token;
     uint32_t wrap;                // 1: wrap packing (cut every T tokens), 0: next-fit
+    uint32_t heldout;             // 1: the stream is the held-out documents (validation)
 
     // recipe on device
     uint32_t* gbase;              // [S+1] first group of each source

@@ -210,7 +210,8 @@ __global__ __launch_bounds__(256) void k_hash_flat(Plan p, const uint32_t* first
 }
 
 // h = mix64(S xor L·φ64); held iff floor(h·10000/2^64) < bp; kept iff not held
-// and non-empty; per-source statistics in LDS, one atomic per block and bin.
+// and non-empty (with the held-out stream: iff held and non-empty); per-source
+// statistics in LDS, one atomic per block and bin.
 __global__ __launch_bounds__(256) void k_hash_final(Plan p, const uint64_t* S, uint32_t lds_bins) {
     extern __shared__ unsigned long long bins[];  // [4][S] when lds_bins
     if (lds_bins) {
@@ -223,11 +224,12 @@ __global__ __launch_bounds__(256) void k_hash_final(Plan p, const uint64_t* S, u
         const uint64_t h = mix64(S[d] ^ (L * PHI64));
         const uint32_t s = p.source[d];
         const bool held = __umul64hi(h, 10000ull) < (uint64_t)p.bp[s];
-        const bool keep = !held && L > 0;
+        const bool keep = (p.heldout ? held : !held) && L > 0;  // the stream's documents
         p.hash[d] = h;
         p.keep[d] = keep ? 1 : 0;
-        if (held || keep) {
-            const uint32_t slot = (held ? 2u : 0u) * p.S + s;
+        for (uint32_t b = 0; b < 2; ++b) {  // bins 0: the stream's documents, 2: held out by the hash
+            if (!(b == 0 ? keep : held)) continue;
+            const uint32_t slot = 2u * b * p.S + s;
             if (lds_bins) {
                 atomicAdd(&bins[slot], 1ull);
                 atomicAdd(&bins[slot + p.S], (unsigned long long)L);

@@ -69,6 +69,14 @@ typedef struct pack_ctx pack_ctx;
  * first position, its position ids restarting at 0; only each source's last
  * window can be short (padded).  Every other output is as with next-fit. */
 #define PACK_FLAG_WRAP 2u
+/* pack_config.flags: plan the held-out documents, the validation stream,
+ * instead of the training ones.  NeuronSpark-Trainer README, Concepts: each
+ * source's validation rows come from its held-out documents of every
+ * stratum, and the validation mix weights the sources by the recipe.
+ * Reading taken: the same plan (shuffle, strata merge, cut, mixture) over the
+ * non-empty held-out documents; the cycle info's kept_* then count the
+ * stream's documents, held_* still the documents the hash holds out. */
+#define PACK_FLAG_HELDOUT 4u
 
 /* Kernel phases timed under PACK_FLAG_TIMING. */
 enum {
@@ -103,7 +111,7 @@ typedef struct pack_timings {
  * [64, 2^20]; 1 ≤ B ≤ 2^20; world ≥ 1 divides B; rank < world. */
 typedef struct pack_config {
     uint32_t abi_version;          /* DPACK_ABI_VERSION */
-    uint32_t flags;                /* 0 or PACK_FLAG_TIMING | PACK_FLAG_WRAP */
+    uint32_t flags;                /* 0 or PACK_FLAG_TIMING | PACK_FLAG_WRAP | PACK_FLAG_HELDOUT */
     const uint32_t *tokens;        /* device [n_tokens] token ids */
     uint64_t n_tokens;
     const uint64_t *doc_offsets;   /* device [n_docs+1]: document d is tokens[off[d], off[d+1]) */

@@ -25,8 +25,10 @@ def _setup(name):
         import torch
         torch.cuda.empty_cache()
         say("generate", name)
-        wrap = name.startswith("wrap-")
-        c = make_corpus(name[5:] if wrap else name).replace(wrap=wrap)
+        mode, _, base = name.partition("-") if "-" in name else ("", "", name)
+        c = make_corpus(base).replace(wrap=mode == "wrap", heldout=mode == "heldout")
+        if mode == "heldout":
+            c = c.replace(updates_per_cycle=0)  # the 1-5 % held out cannot supply 200 updates
         say("oracle plan", name, c.n_docs, "docs", c.n_tokens, "tokens")
         op = oracle.Plan(c)
         oi = op.cycle(0)
@@ -42,9 +44,10 @@ def _setup(name):
 # bench does; else the first a and the last b updates of the cycle).  The full
 # workload's second call holds 67,584 windows, more than the one-kernel
 # emission-and-digest launch takes, so it covers the two-kernel path;
-# wrap-pretrain is the pre-train workload with wrap packing.
+# wrap-pretrain is the pre-train workload with wrap packing, heldout-pretrain
+# its held-out (validation) stream.
 FULL = [("tiny", None), ("pretrain", None), ("sft", None), ("long", None), ("full", (24, 66)),
-        ("wrap-pretrain", None)]
+        ("wrap-pretrain", None), ("heldout-pretrain", None)]
 
 
 @pytest.mark.parametrize("name,cap", FULL)

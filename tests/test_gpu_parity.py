@@ -49,6 +49,17 @@ def test_wrap_plan_cycle_batch_parity(kind, arg):
     _parity_run(_corpus(kind, arg).replace(wrap=True), "wrap-" + kind, arg)
 
 
+HELDOUT_CASES = [(s, w) for s in range(6) for w in (False, True)]
+
+
+@pytest.mark.parametrize("seed,wrap", HELDOUT_CASES)
+def test_heldout_stream_parity(seed, wrap):
+    """The held-out (validation) stream, PACK_FLAG_HELDOUT, with both packings."""
+    c = random_small(1000 + seed, n_docs=300 + 100 * seed, n_sources=1 + seed % 3, max_strata=1 + seed % 3,
+                     T=64, B=1 + seed % 4, max_len=120, prompts=bool(seed % 2), bp_max=6000)
+    _parity_run(c.replace(heldout=True, wrap=wrap), "heldout" + ("-wrap" if wrap else ""), seed)
+
+
 def _parity_run(c, kind, arg):
     say("plan/cycle/batch", kind, arg, "docs", c.n_docs, "T", c.T, "B", c.B)
     op = oracle.Plan(c)
@@ -78,14 +89,17 @@ def _parity_run(c, kind, arg):
 
 
 @pytest.mark.parametrize("kind,arg,worlds", [("tiny", 0.5, [1, 2, 4, 8]), ("pretrain", 0.006, [1, 8, 16, 32, 64]),
-                                             ("small", 4, [1, 2, 4, 8]), ("wrap-pretrain", 0.006, [1, 8, 64])])
+                                             ("small", 4, [1, 2, 4, 8]), ("wrap-pretrain", 0.006, [1, 8, 64]),
+                                             ("heldout", 1100, [1, 2, 4, 8])])
 def test_elastic_rank_counts_identical(kind, arg, worlds):
-    wrap = kind.startswith("wrap-")
-    kind = kind[5:] if wrap else kind
-    c = _corpus(kind, arg).replace(wrap=wrap)
+    if kind == "heldout":  # a held-out stream large enough for B = 8
+        c = random_small(arg, n_docs=2000, n_sources=2, T=64, B=8, max_len=60, bp_max=6000).replace(heldout=True)
+    else:
+        mode, _, base = kind.partition("-") if "-" in kind else ("", "", kind)
+        c = _corpus(base, arg).replace(wrap=mode == "wrap")
     if kind == "small":
         c = c.replace(B=8)
-    if kind == "pretrain":
+    if kind.endswith("pretrain"):
         c = c.replace(updates_per_cycle=2)
     op = oracle.Plan(c)
     op.cycle(0)
