@@ -175,7 +175,7 @@ class _OrCorpus(C.Structure):
         ("source", C.c_void_p), ("stratum", C.c_void_p), ("prompt_len", C.c_void_p),
         ("n_sources", C.c_uint32), ("n_strata", C.c_void_p), ("weight", C.c_void_p),
         ("bp", C.c_void_p), ("T", C.c_uint32), ("B", C.c_uint32), ("seed", C.c_uint64),
-        ("pad_token", C.c_uint32), ("wrap", C.c_uint32), ("heldout", C.c_uint32),
+        ("pad_token", C.c_uint32), ("wrap", C.c_uint32), ("heldout", C.c_uint32), ("read_random", C.c_uint32),
     ]
 
 
@@ -224,7 +224,7 @@ class Plan:
             _ptr(k["offsets"]), D, _ptr(k["source"]) if D else None, _ptr(k["stratum"]) if D else None,
             _ptr(k["prompt_len"]), S, _ptr(k["n_strata"]), _ptr(k["weight"]), _ptr(k["bp"]),
             c.T, c.B, c.seed & 0xFFFFFFFFFFFFFFFF, c.pad_token, 1 if getattr(c, "wrap", False) else 0,
-            1 if getattr(c, "heldout", False) else 0)
+            1 if getattr(c, "heldout", False) else 0, 1 if getattr(c, "read_random", False) else 0)
         err = C.c_int(0)
         self._p = lib.or_plan_build(C.byref(self._cs), C.byref(err))
         if not self._p:

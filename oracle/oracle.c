@@ -137,6 +137,21 @@ void or_philox4x32_10(const uint32_t ctr_in[4], const uint32_t key_in[2], uint32
  *               key = (seed mod 2^32, seed div 2^32)),
  * key64 = x1·2^32 + x0.  Keyed only by the seed and the input document index,
  * never by rank, world or worker count. */
+/* C6r. Read order of a source's windows within a cycle ([NS] Concepts: the
+ * trainer reads each source's windows of a segment in a random order).
+ * Reading: a segment is a cycle; window i of source s's cycle range (i in
+ * [0, U·n_s)) gets key64 = x1·2^32 + x0 of Philox4x32-10(counter =
+ * (i, s, cycle, 0x57494E44), key = (seed lo, seed hi)), and the range is read
+ * in order of (key64, i). */
+uint64_t or_window_key(uint64_t seed, uint32_t s, uint32_t cycle, uint32_t i)
+{
+    uint32_t ctr[4] = {i, s, cycle, 0x57494E44u};
+    uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+    uint32_t x[4];
+    or_philox4x32_10(ctr, key, x);
+    return ((uint64_t)x[1] << 32) | x[0];
+}
+
 uint64_t or_shuffle_key(uint64_t seed, uint64_t d)
 {
     uint32_t ctr[4] = {(uint32_t)d, (uint32_t)(d >> 32), 0x53485546u, 0u};
@@ -305,6 +320,7 @@ typedef struct {
     uint32_t pad_token;
     uint32_t wrap;               /* 0: next-fit cut at document ends; 1: wrap (C5w) */
     uint32_t heldout;            /* 1: the stream is the held-out documents (C2v) */
+    uint32_t read_random;        /* 1: each cycle's windows of a source read in a random order (C6r) */
 } or_corpus;
 
 typedef struct {
@@ -331,6 +347,8 @@ typedef struct {
     uint32_t U;                  /* updates in the current cycle */
     uint64_t *cyc_start;         /* [S] first window of the current cycle */
     uint64_t *cyc_next;          /* [S] first window of the next cycle */
+    uint64_t *perm_start;        /* [S+1] with read_random: start of each source's part of perm */
+    uint32_t *perm;              /* [U·B] with read_random: read order within each source's cycle range */
 } or_plan;
 
 typedef struct { uint32_t group; uint32_t d; uint64_t key; } sort_item;
@@ -604,6 +622,7 @@ void or_plan_free(or_plan *p)
     free(p->src_piece_start); free(p->win_first); free(p->src_win_start);
     free(p->win_real); free(p->win_learn); free(p->n_upd); free(p->slot_src); free(p->slot_k);
     free(p->kept_docs); free(p->kept_tokens); free(p->held_docs); free(p->held_tokens);
+    free(p->perm); free(p->perm_start);
     free(p->cyc_start); free(p->cyc_next);
     free(p);
 }
@@ -642,6 +661,30 @@ int or_cycle(or_plan *p, uint32_t cyc, uint32_t updates_cfg)
         if ((u128)U * p->n_upd[s] > (u128)(M - start[s])) ok = 0;
     }
     if (!ok) { free(start); return OR_E_EXHAUSTED; }   /* cycle state unchanged */
+    if (p->c.read_random) {
+        /* C6r: for each source, its U·n_s cycle windows ordered by (key64, i) */
+        uint64_t total = 0;
+        for (uint32_t s = 0; s < S; s++) total += U * p->n_upd[s];
+        uint64_t *ps = calloc(S + 1, sizeof(uint64_t));
+        uint32_t *perm = calloc(total ? total : 1, sizeof(uint32_t));
+        sort_item *it = calloc(total ? total : 1, sizeof(sort_item));
+        if (!ps || !perm || !it) { free(ps); free(perm); free(it); free(start); return OR_E_NOMEM; }
+        uint64_t e = 0;
+        for (uint32_t s = 0; s < S; s++) {
+            ps[s] = e;
+            for (uint64_t i = 0; i < U * p->n_upd[s]; i++, e++) {
+                it[e].group = s;
+                it[e].d = (uint32_t)i;
+                it[e].key = or_window_key(p->c.seed, s, cyc, (uint32_t)i);
+            }
+        }
+        ps[S] = e;
+        qsort(it, total, sizeof(sort_item), cmp_sort);  /* by (source, key64, i) */
+        for (uint64_t r = 0; r < total; r++) perm[r] = it[r].d;
+        free(it);
+        free(p->perm); free(p->perm_start);
+        p->perm = perm; p->perm_start = ps;
+    }
     p->U = (uint32_t)U;
     for (uint32_t s = 0; s < S; s++) {
         p->cyc_start[s] = start[s];
@@ -656,7 +699,9 @@ int or_cycle(or_plan *p, uint32_t cyc, uint32_t updates_cfg)
 uint64_t or_window_of(const or_plan *p, uint64_t b, uint32_t j)
 {
     uint32_t s = p->slot_src[j];
-    return p->src_win_start[s] + p->cyc_start[s] + b * p->n_upd[s] + p->slot_k[j];
+    uint64_t i = b * p->n_upd[s] + p->slot_k[j];   /* the source's i-th window of the cycle */
+    if (p->c.read_random) i = p->perm[p->perm_start[s] + i];
+    return p->src_win_start[s] + p->cyc_start[s] + i;
 }
 
 /* C7. Emission of one window of T positions.  For a position inside piece
@@ -745,13 +790,15 @@ int or_plan_digest(const or_plan *p, uint8_t out[32])
     const or_corpus *c = &p->c;
     const uint32_t S = c->n_sources;
     if (p->cycle < 0) return OR_E_STATE;
-    uint64_t bytes = 8 + 4 + 4 + 8 + 4 + 4 + (uint64_t)S * (8 + 4 + 4 + 4 + 8 + 8 + 8) + 4 + 4 + 8ull * S + 8 + 8;
+    uint64_t bytes = 8 + 4 + 4 + 8 + 4 + 4 + (uint64_t)S * (8 + 4 + 4 + 4 + 8 + 8 + 8) + 4 + 4 + 8ull * S + 8 + 8
+                     + (c->read_random ? 4 : 0);
     uint8_t *buf = (uint8_t *)malloc(bytes), *w = buf;
     if (!buf) return OR_E_NOMEM;
     /* the packing mode and the stream (training / held-out) are part of the plan */
     memcpy(w, "DPACKP", 6); w += 6;
     *w++ = c->wrap ? 'W' : 'D';
     *w++ = c->heldout ? 'V' : '1';
+    if (c->read_random) put(&w, 0x444E4152u, 4);  /* "RAND": windows read in a random order */
     put(&w, c->T, 4); put(&w, c->B, 4); put(&w, c->seed, 8); put(&w, S, 4); put(&w, c->pad_token, 4);
     for (uint32_t s = 0; s < S; s++) {
         put(&w, c->weight[s], 8); put(&w, c->bp[s], 4); put(&w, c->n_strata[s], 4);

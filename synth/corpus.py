@@ -47,6 +47,7 @@ class Corpus:
     meta: Dict = dataclasses.field(default_factory=dict)
     wrap: bool = False          # packing: False = next-fit cut at document ends, True = wrap
     heldout: bool = False       # stream: False = training documents, True = held-out (validation)
+    read_random: bool = False   # each cycle's windows of a source read in a random order
 
     @property
     def n_docs(self) -> int:
