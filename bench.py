@@ -76,6 +76,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-copy", action="store_true", help="skip the plain D2D copy used as calibration/ceiling")
     ap.add_argument("--wrap", action="store_true", help="wrap packing (PACK_FLAG_WRAP) instead of next-fit")
+    ap.add_argument("--read-random", action="store_true",
+                    help="each cycle's windows of a source read in a random order (PACK_FLAG_READ_RANDOM)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -94,7 +96,7 @@ def main():
     dp.load_library()
 
     t0 = time.time()
-    corpus = make_corpus(args.workload, args.scale).replace(wrap=args.wrap)
+    corpus = make_corpus(args.workload, args.scale).replace(wrap=args.wrap, read_random=args.read_random)
     log(f"corpus {args.workload} scale {args.scale}: {corpus.n_docs} docs, {corpus.n_tokens} tokens "
         f"({time.time() - t0:.1f}s)")
     tensors = dp.upload_corpus(corpus)
@@ -257,7 +259,7 @@ def main():
         "dtype": "u32",
         "data": "synthetic",
         "config": {"workload": WORKLOAD_TEXT[args.workload] + ("" if args.scale == 1.0 else f" (scale {args.scale})")
-                   + (", wrap packing" if args.wrap else ""),
+                   + (", wrap packing" if args.wrap else "") + (", random read order" if args.read_random else ""),
                    "docs": corpus.n_docs, "tokens": corpus.n_tokens, "T": T, "B": B, "updates": U,
                    "real_tokens_per_step": real, "positions_per_step": positions,
                    "step": "pack_init + pack_cycle + pack_batch(all updates, learned, digests) + pack_destroy"},

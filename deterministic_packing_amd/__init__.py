@@ -34,6 +34,7 @@ SYMBOLS = ("pack_init", "pack_cycle", "pack_batch", "pack_fingerprint", "pack_in
 PACK_FLAG_TIMING = 1
 PACK_FLAG_WRAP = 2
 PACK_FLAG_HELDOUT = 4
+PACK_FLAG_READ_RANDOM = 8
 PHASES = ("validate", "hash", "keys", "sort", "merge", "pieces", "cut", "windows", "mixture",
           "cycle", "emit", "learned", "digest", "fingerprint")
 
@@ -215,7 +216,8 @@ class Packer:
         d = self.dev
         self.cfg = PackConfig(
             ABI_VERSION, (PACK_FLAG_TIMING if timing else 0) | (PACK_FLAG_WRAP if getattr(corpus, "wrap", False) else 0)
-            | (PACK_FLAG_HELDOUT if getattr(corpus, "heldout", False) else 0),
+            | (PACK_FLAG_HELDOUT if getattr(corpus, "heldout", False) else 0)
+            | (PACK_FLAG_READ_RANDOM if getattr(corpus, "read_random", False) else 0),
             d["tokens"].data_ptr() if d["tokens"].numel() else None, int(d["tokens"].numel()),
             d["offsets"].data_ptr(), int(d["source"].numel()),
             d["source"].data_ptr(), d["stratum"].data_ptr() if d.get("stratum") is not None else None,

@@ -200,7 +200,8 @@ size_t carve(pack_ctx& c, char* base) {
     p.key[1] = k.take<uint64_t>(D);
     p.val[0] = k.take<uint32_t>(D);
     p.val[1] = k.take<uint32_t>(D);
-    p.hist = k.take<uint32_t>(dp::sort_hist_words(D));
+    const uint64_t WR = p.read_random ? P : 0;  // cycle windows ≤ windows ≤ pieces
+    p.hist = k.take<uint32_t>(dp::sort_hist_words(D > WR ? D : WR));
     p.group_start = k.take<uint32_t>(G + 1);
     p.gpre = k.take<uint64_t>(D + 1);
     p.order = k.take<uint32_t>(D);
@@ -226,6 +227,13 @@ size_t carve(pack_ctx& c, char* base) {
     p.checks = k.take<uint64_t>(2);
     p.cyc_sums = k.take<uint64_t>(2);
     p.pad16 = k.take<uint32_t>(16);
+    p.perm_start = k.take<uint64_t>(S + 1);
+    p.perm = k.take<uint32_t>(WR);
+    p.wkey[0] = k.take<uint64_t>(WR);
+    p.wkey[1] = k.take<uint64_t>(WR);
+    p.wval[0] = k.take<uint32_t>(WR);
+    p.wval[1] = k.take<uint32_t>(WR);
+    p.wgroup = k.take<uint32_t>(WR);
     c.nstart = k.take<uint32_t>(S + 1);
     c.dig_cap = 128 + 48 * S;
     c.dig_buf = k.take<uint8_t>(c.dig_cap + 32);
@@ -277,7 +285,8 @@ void sync_staged(pack_ctx& c) {
 
 void check_config(const pack_config* cfg) {
     auto bad = [](const char* m) { throw InvalError{m}; };
-    if (cfg->flags & ~(PACK_FLAG_TIMING | PACK_FLAG_WRAP | PACK_FLAG_HELDOUT)) bad("unknown flags");
+    if (cfg->flags & ~(PACK_FLAG_TIMING | PACK_FLAG_WRAP | PACK_FLAG_HELDOUT | PACK_FLAG_READ_RANDOM))
+        bad("unknown flags");
     if (cfg->n_docs < 1 || cfg->n_docs >= (1ull << 31)) bad("n_docs must be in [1, 2^31)");
     if (!cfg->doc_offsets || !cfg->doc_source) bad("doc_offsets and doc_source are required");
     if (cfg->n_tokens && !cfg->tokens) bad("tokens is NULL with n_tokens > 0");
@@ -497,6 +506,7 @@ int pack_init(const pack_config* cfg, pack_ctx** out) {
         p.pad_token = cfg->pad_token;
         p.wrap = (cfg->flags & PACK_FLAG_WRAP) ? 1u : 0u;
         p.heldout = (cfg->flags & PACK_FLAG_HELDOUT) ? 1u : 0u;
+        p.read_random = (cfg->flags & PACK_FLAG_READ_RANDOM) ? 1u : 0u;
         p.cap_pieces = cfg->n_docs + cfg->n_tokens / cfg->window_tokens;
         if (p.cap_pieces >= 0xFFFFFFFFull) throw InvalError{"too many pieces for 32-bit piece indices"};
 
@@ -586,6 +596,12 @@ int pack_cycle(pack_ctx* c, uint32_t cycle, pack_cycle_info* info) {
         c->timer.begin(PACK_PHASE_CYCLE, c->st);
         c->pin_off = 0;
         h2d_staged(*c, p.cyc_start, c->cyc_start.data(), S);
+        if (p.read_random) {  // each source's U·n_s cycle windows in their random read order
+            std::vector<uint64_t> ps(S + 1, 0);
+            for (uint32_t s = 0; s < S; ++s) ps[s + 1] = ps[s] + (uint64_t)c->U * c->n_upd[s];
+            h2d_staged(*c, p.perm_start, ps.data(), S + 1);
+            dp::launch_read_order(p, cycle, ps[S], c->st);
+        }
         dp::launch_cycle_sums(p, c->U, c->st);
         const uint64_t* h_sums = d2h_staged(*c, p.cyc_sums, 2);
 
@@ -595,6 +611,7 @@ int pack_cycle(pack_ctx* c, uint32_t cycle, pack_cycle_info* info) {
         // the packing mode (D next-fit, W wrap) and the stream (1 training, V held-out) are part of the plan
         const char magic[8] = {'D', 'P', 'A', 'C', 'K', 'P', p.wrap ? 'W' : 'D', p.heldout ? 'V' : '1'};
         msg.insert(msg.end(), magic, magic + 8);
+        if (p.read_random) put(msg, 0x444E4152u, 4);  // "RAND": windows read in a random order
         put(msg, p.T, 4);
         put(msg, p.B, 4);
         put(msg, p.seed, 8);

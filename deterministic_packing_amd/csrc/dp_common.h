@@ -85,6 +85,7 @@ struct Plan {
     uint32_t pad_token;
     uint32_t wrap;                // 1: wrap packing (cut every T tokens), 0: next-fit
     uint32_t heldout;             // 1: the stream is the held-out documents (validation)
+    uint32_t read_random;         // 1: each cycle's windows of a source are read in a random order
 
     // recipe on device
     uint32_t* gbase;              // [S+1] first group of each source
@@ -137,6 +138,13 @@ struct Plan {
     uint64_t* cyc_start;          // [S] first window of the current cycle per source
     uint64_t* checks;             // [2] order check, hash check
     uint64_t* cyc_sums;           // [2] real, learned over the current cycle
+    // random read order (read_random): per cycle, source s reads its i-th cycle
+    // window from position perm[perm_start[s] + i] of its cycle range
+    uint64_t* perm_start;         // [S+1]
+    uint32_t* perm;               // [U·B]
+    uint64_t* wkey[2];            // sort workspace [cap windows]
+    uint32_t* wval[2];
+    uint32_t* wgroup;
 
     // sizes known after the corresponding step (host copies)
     uint64_t n_kept, n_pieces, n_windows;
@@ -144,11 +152,15 @@ struct Plan {
 };
 
 // Global window index of slot j of update b of the current cycle: source s
-// = slot_src[j] contributes its (slot_k[j])-th window of the update, i.e. window
-// cyc_start[s] + b·n_s + slot_k[j] of its stream.
+// = slot_src[j] contributes its (slot_k[j])-th window of the update, i.e. its
+// i-th window of the cycle, i = b·n_s + slot_k[j]: window cyc_start[s] + i of
+// its stream, or cyc_start[s] + perm[perm_start[s] + i] with the random read
+// order.
 __device__ inline uint64_t window_of(const Plan& p, uint64_t b, uint32_t j) {
     const uint32_t s = p.slot_src[j];
-    return p.src_win_start[s] + p.cyc_start[s] + b * p.n_upd[s] + p.slot_k[j];
+    uint64_t i = b * p.n_upd[s] + p.slot_k[j];  // the source's i-th window of the cycle
+    if (p.read_random) i = p.perm[p.perm_start[s] + i];
+    return p.src_win_start[s] + p.cyc_start[s] + i;
 }
 
 // ---------------------------------------------------------------- SHA-256 (FIPS 180-4)
@@ -210,6 +222,9 @@ void launch_hash(const Plan& p, uint64_t base, uint64_t end, uint64_t* S, uint32
 uint64_t hash_tile_count(uint64_t n_tokens);
 void launch_keep_scan(Plan& p, hipStream_t st);       // kept_pos + compaction into val[0], keys
 void launch_sort(Plan& p, hipStream_t st);            // LSD radix by (group, key64); sets sort_buf
+uint32_t sort_pairs(uint64_t* const key[2], uint32_t* const val[2], const uint32_t* group, uint64_t n, uint32_t G,
+                    uint32_t* hist_ws, uint32_t* err, hipStream_t st);
+void launch_read_order(Plan& p, uint32_t cycle, uint64_t total, hipStream_t st);  // perm of each source's cycle windows
 void launch_merge(Plan& p, hipStream_t st);           // group_start, gpre, order, src_doc_start
 void launch_piece_count(Plan& p, hipStream_t st);     // piece_start, opre
 void launch_pieces(Plan& p, hipStream_t st);          // piece table, pc_pre, src_piece_start

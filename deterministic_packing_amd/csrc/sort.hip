@@ -110,6 +110,34 @@ __global__ __launch_bounds__(RB) void k_scatter(const uint64_t* key_in, const ui
     }
 }
 
+// Random read order of each source's cycle windows (NeuronSpark-Trainer
+// README, Concepts: the trainer reads each source's windows of a segment in a
+// random order; a segment read as a cycle).  Element e of the cycle's windows
+// is source s's i-th window; key64 = x1·2^32 + x0 of Philox4x32-10(counter =
+// (i, s, cycle, 0x57494E44), key = seed); sorted by (s, key64, e).
+__global__ __launch_bounds__(256) void k_window_keys(Plan p, uint32_t cycle, uint64_t total) {
+    const uint64_t e = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (e >= total) return;
+    uint32_t lo = 0, hi = p.S;  // source: the last s with perm_start[s] <= e
+    while (lo < hi) {
+        const uint32_t mid = (lo + hi + 1) >> 1;
+        if (p.perm_start[mid] <= e) lo = mid;
+        else hi = mid - 1;
+    }
+    const uint32_t s = lo;
+    const uint32_t i = (uint32_t)(e - p.perm_start[s]);
+    p.wkey[0][e] = philox_key64(i, s, cycle, 0x57494E44u, (uint32_t)p.seed, (uint32_t)(p.seed >> 32));
+    p.wval[0][e] = (uint32_t)e;
+    p.wgroup[e] = s;
+}
+
+__global__ __launch_bounds__(256) void k_perm_out(Plan p, const uint32_t* sorted, uint64_t total) {
+    const uint64_t r = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (r >= total) return;
+    const uint32_t e = sorted[r];
+    p.perm[r] = (uint32_t)(e - p.perm_start[p.wgroup[e]]);
+}
+
 // Orders each run of equal (group, key64 >> 32) by the low 32 key bits; the
 // thread at a run's first element sorts the run (insertion sort, stable).
 // Other threads only read the high key bits and groups, which the sort of a
@@ -146,41 +174,58 @@ void launch_keep_scan(Plan& p, hipStream_t st) {
     DP_HIP(hipGetLastError());
 }
 
-// requires p.n_kept (host) to be set
-void launch_sort(Plan& p, hipStream_t st) {
-    const uint64_t n = p.n_kept;
+// Stable sort of n (key64, val) pairs by (group[val], key64, input order),
+// ping-ponging between buffers 0 and 1; returns the buffer that holds the
+// result.  group values are < G.
+uint32_t sort_pairs(uint64_t* const key[2], uint32_t* const val[2], const uint32_t* group, uint64_t n, uint32_t G,
+                    uint32_t* hist_ws, uint32_t* err, hipStream_t st) {
     const uint32_t nb = (uint32_t)((n + RTILE - 1) / RTILE);
     // hist holds [256·nb] counts followed by [256·nb + 1] scanned offsets and the scan's temp
-    uint32_t* hist = p.hist;
-    uint32_t* hofs = p.hist + 256ull * nb + 1;
+    uint32_t* hist = hist_ws;
+    uint32_t* hofs = hist_ws + 256ull * nb + 1;
     void* tmp = hofs + 256ull * nb + 2;
     int cur = 0;
     auto pass = [&](bool group_pass, int shift) {
         if (nb == 0) return;
         if (group_pass)
-            hipLaunchKernelGGL(k_hist<true>, dim3(nb), dim3(RB), 0, st, p.key[cur], p.val[cur], p.group, n, shift,
-                               hist, nb);
+            hipLaunchKernelGGL(k_hist<true>, dim3(nb), dim3(RB), 0, st, key[cur], val[cur], group, n, shift, hist, nb);
         else
-            hipLaunchKernelGGL(k_hist<false>, dim3(nb), dim3(RB), 0, st, p.key[cur], p.val[cur], p.group, n, shift,
-                               hist, nb);
+            hipLaunchKernelGGL(k_hist<false>, dim3(nb), dim3(RB), 0, st, key[cur], val[cur], group, n, shift, hist,
+                               nb);
         scan_u32(hist, 256ull * nb, hofs, tmp, st);
         if (group_pass)
-            hipLaunchKernelGGL(k_scatter<true>, dim3(nb), dim3(RB), 0, st, p.key[cur], p.val[cur], p.group, n,
-                               shift, hofs, nb, p.key[cur ^ 1], p.val[cur ^ 1], p.err);
+            hipLaunchKernelGGL(k_scatter<true>, dim3(nb), dim3(RB), 0, st, key[cur], val[cur], group, n, shift, hofs,
+                               nb, key[cur ^ 1], val[cur ^ 1], err);
         else
-            hipLaunchKernelGGL(k_scatter<false>, dim3(nb), dim3(RB), 0, st, p.key[cur], p.val[cur], p.group, n,
-                               shift, hofs, nb, p.key[cur ^ 1], p.val[cur ^ 1], p.err);
+            hipLaunchKernelGGL(k_scatter<false>, dim3(nb), dim3(RB), 0, st, key[cur], val[cur], group, n, shift, hofs,
+                               nb, key[cur ^ 1], val[cur ^ 1], err);
         DP_HIP(hipGetLastError());
         cur ^= 1;
     };
     for (int shift = 32; shift < 64; shift += 8) pass(false, shift);
-    for (int shift = 0; p.G > 1 && shift < 32 && ((p.G - 1) >> shift) != 0; shift += 8) pass(true, shift);
+    for (int shift = 0; G > 1 && shift < 32 && ((G - 1) >> shift) != 0; shift += 8) pass(true, shift);
     if (n > 1) {
-        hipLaunchKernelGGL(k_tie_fix, dim3((uint32_t)((n + 255) / 256)), dim3(256), 0, st, p.key[cur], p.val[cur],
-                           (const uint32_t*)p.group, n);
+        hipLaunchKernelGGL(k_tie_fix, dim3((uint32_t)((n + 255) / 256)), dim3(256), 0, st, key[cur], val[cur], group,
+                           n);
         DP_HIP(hipGetLastError());
     }
-    p.sort_buf = (uint32_t)cur;
+    return (uint32_t)cur;
+}
+
+// requires p.n_kept (host) to be set
+void launch_sort(Plan& p, hipStream_t st) {
+    p.sort_buf = sort_pairs(p.key, p.val, p.group, p.n_kept, p.G, p.hist, p.err, st);
+}
+
+// requires perm_start (device) for the cycle; total = U·B
+void launch_read_order(Plan& p, uint32_t cycle, uint64_t total, hipStream_t st) {
+    if (total == 0) return;
+    const uint32_t blocks = (uint32_t)((total + 255) / 256);
+    hipLaunchKernelGGL(k_window_keys, dim3(blocks), dim3(256), 0, st, p, cycle, total);
+    DP_HIP(hipGetLastError());
+    const uint32_t buf = sort_pairs(p.wkey, p.wval, p.wgroup, total, p.S, p.hist, p.err, st);
+    hipLaunchKernelGGL(k_perm_out, dim3(blocks), dim3(256), 0, st, p, (const uint32_t*)p.wval[buf], total);
+    DP_HIP(hipGetLastError());
 }
 
 // workspace for the sort's histogram, offsets and scan temp, in uint32 words

@@ -77,6 +77,14 @@ typedef struct pack_ctx pack_ctx;
  * non-empty held-out documents; the cycle info's kept_* then count the
  * stream's documents, held_* still the documents the hash holds out. */
 #define PACK_FLAG_HELDOUT 4u
+/* pack_config.flags: read each source's windows of a cycle in a random order.
+ * NeuronSpark-Trainer README, Concepts: the trainer reads each source's
+ * windows of a segment in a random order.  Reading taken: a segment is a
+ * cycle; source s's i-th window of the cycle (i < U·n_s) is ranked by
+ * key64 = x1·2^32 + x0 of Philox4x32-10(counter = (i, s, cycle, 0x57494E44),
+ * key = seed), ties by i, and update b's k-th window of s is the one of rank
+ * b·n_s + k.  Per-update counts, cycle ranges and sums are unchanged. */
+#define PACK_FLAG_READ_RANDOM 8u
 
 /* Kernel phases timed under PACK_FLAG_TIMING. */
 enum {
@@ -111,7 +119,7 @@ typedef struct pack_timings {
  * [64, 2^20]; 1 ≤ B ≤ 2^20; world ≥ 1 divides B; rank < world. */
 typedef struct pack_config {
     uint32_t abi_version;          /* DPACK_ABI_VERSION */
-    uint32_t flags;                /* 0 or PACK_FLAG_TIMING | PACK_FLAG_WRAP | PACK_FLAG_HELDOUT */
+    uint32_t flags;                /* 0 or an or of PACK_FLAG_TIMING, _WRAP, _HELDOUT, _READ_RANDOM */
     const uint32_t *tokens;        /* device [n_tokens] token ids */
     uint64_t n_tokens;
     const uint64_t *doc_offsets;   /* device [n_docs+1]: document d is tokens[off[d], off[d+1]) */

@@ -66,7 +66,7 @@ def _cfg(**kw):
     ("window_tokens", 100, dp.PACK_E_INVAL),
     ("global_batch", 0, dp.PACK_E_INVAL),
     ("n_docs", 0, dp.PACK_E_INVAL),
-    ("flags", 8, dp.PACK_E_INVAL),
+    ("flags", 16, dp.PACK_E_INVAL),
     ("n_sources", 0, dp.PACK_E_INVAL),
 ])
 def test_init_rejects_bad_config_on_host(lib, field, value, code):

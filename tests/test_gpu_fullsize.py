@@ -26,7 +26,7 @@ def _setup(name):
         torch.cuda.empty_cache()
         say("generate", name)
         mode, _, base = name.partition("-") if "-" in name else ("", "", name)
-        c = make_corpus(base).replace(wrap=mode == "wrap", heldout=mode == "heldout")
+        c = make_corpus(base).replace(wrap=mode == "wrap", heldout=mode == "heldout", read_random=mode == "random")
         if mode == "heldout":
             c = c.replace(updates_per_cycle=0)  # the 1-5 % held out cannot supply 200 updates
         say("oracle plan", name, c.n_docs, "docs", c.n_tokens, "tokens")
@@ -45,9 +45,10 @@ def _setup(name):
 # workload's second call holds 67,584 windows, more than the one-kernel
 # emission-and-digest launch takes, so it covers the two-kernel path;
 # wrap-pretrain is the pre-train workload with wrap packing, heldout-pretrain
-# its held-out (validation) stream.
+# its held-out (validation) stream, random-pretrain with each cycle's windows
+# read in a random order.
 FULL = [("tiny", None), ("pretrain", None), ("sft", None), ("long", None), ("full", (24, 66)),
-        ("wrap-pretrain", None), ("heldout-pretrain", None)]
+        ("wrap-pretrain", None), ("heldout-pretrain", None), ("random-pretrain", None)]
 
 
 @pytest.mark.parametrize("name,cap", FULL)

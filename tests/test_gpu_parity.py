@@ -49,6 +49,12 @@ def test_wrap_plan_cycle_batch_parity(kind, arg):
     _parity_run(_corpus(kind, arg).replace(wrap=True), "wrap-" + kind, arg)
 
 
+@pytest.mark.parametrize("kind,arg", SMALL_CASES)
+def test_read_random_parity(kind, arg):
+    """The same cases with each cycle's windows read in a random order (PACK_FLAG_READ_RANDOM)."""
+    _parity_run(_corpus(kind, arg).replace(read_random=True), "random-order-" + kind, arg)
+
+
 HELDOUT_CASES = [(s, w) for s in range(6) for w in (False, True)]
 
 
@@ -90,13 +96,13 @@ def _parity_run(c, kind, arg):
 
 @pytest.mark.parametrize("kind,arg,worlds", [("tiny", 0.5, [1, 2, 4, 8]), ("pretrain", 0.006, [1, 8, 16, 32, 64]),
                                              ("small", 4, [1, 2, 4, 8]), ("wrap-pretrain", 0.006, [1, 8, 64]),
-                                             ("heldout", 1100, [1, 2, 4, 8])])
+                                             ("heldout", 1100, [1, 2, 4, 8]), ("random-tiny", 0.5, [1, 2, 4, 8])])
 def test_elastic_rank_counts_identical(kind, arg, worlds):
     if kind == "heldout":  # a held-out stream large enough for B = 8
         c = random_small(arg, n_docs=2000, n_sources=2, T=64, B=8, max_len=60, bp_max=6000).replace(heldout=True)
     else:
         mode, _, base = kind.partition("-") if "-" in kind else ("", "", kind)
-        c = _corpus(base, arg).replace(wrap=mode == "wrap")
+        c = _corpus(base, arg).replace(wrap=mode == "wrap", read_random=mode == "random")
     if kind == "small":
         c = c.replace(B=8)
     if kind.endswith("pretrain"):
@@ -132,8 +138,10 @@ def test_world_not_dividing_batch_fails_at_init():
         assert e.value.code == dp.PACK_E_INVAL
 
 
-def test_cycles_until_exhausted_match_oracle():
+@pytest.mark.parametrize("read_random", [False, True])
+def test_cycles_until_exhausted_match_oracle(read_random):
     c = random_small(40, n_docs=400, n_sources=3, T=64, B=6, max_len=100, prompts=True, updates_per_cycle=2)
+    c = c.replace(read_random=read_random)
     op = oracle.Plan(c)
     pk = dp.Packer(c)
     compare_plan(pk, op)
