@@ -86,6 +86,8 @@ def _load():
         lib.or_window_digest.argtypes = [u32, vp, vp, vp, vp, vp]
         lib.or_batch.restype = i32
         lib.or_batch.argtypes = [vp, u32, u32, u32, u32, vp, vp, vp, vp, vp, vp]
+        lib.or_batch_packed.restype = i32
+        lib.or_batch_packed.argtypes = [vp, u32, u32, u32, u32, u32, vp, vp, vp, vp, vp, vp]
         lib.or_plan_digest.restype = i32
         lib.or_plan_digest.argtypes = [vp, vp]
         _lib = lib
@@ -325,3 +327,22 @@ class Plan:
         if rc:
             raise OracleError(rc, "batch")
         return dict(tokens=tok, pos=pos, doc=doc, mask=mask, learned=lrn, digests=dig)
+
+    def batch_packed(self, step: int, n_steps: int = 1, rank: int = 0, world: int = 1, bucket: int = 256) -> dict:
+        """Padding-free rows: one packed row per update of this rank's windows'
+        real positions, its length rounded up to a multiple of bucket."""
+        B, T = self.corpus.B, self.corpus.T
+        if world <= 0 or B % world:
+            raise OracleError(OR_E_INVAL, "batch world")
+        per = B // world
+        tok = np.zeros((n_steps, per * T), np.uint32)
+        pos = np.zeros((n_steps, per * T), np.int32)
+        doc = np.zeros((n_steps, per * T), np.int32)
+        mask = np.zeros((n_steps, per * T), np.uint8)
+        row_start = np.zeros((n_steps, per + 1), np.int64)
+        length = np.zeros(n_steps, np.int64)
+        rc = _load().or_batch_packed(self._p, step, n_steps, rank, world, bucket, _ptr(tok), _ptr(pos), _ptr(doc),
+                                     _ptr(mask), _ptr(row_start), _ptr(length))
+        if rc:
+            raise OracleError(rc, "batch_packed")
+        return dict(tokens=tok, pos=pos, doc=doc, mask=mask, row_start=row_start, length=length)

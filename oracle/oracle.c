@@ -775,6 +775,52 @@ int or_batch(const or_plan *p, uint32_t step, uint32_t n_steps, uint32_t rank, u
     return OR_OK;
 }
 
+/* C7p. Padding-free rows ([LI] Supervised fine-tuning, the transformers
+ * Trainer path: the padding is removed and the rows are packed into one
+ * sequence whose length rounds up to a multiple of bucket, 256, so few shapes
+ * compile; a position id 0 starts each sequence).  Reading: for each update,
+ * this rank's windows, in slot order, give their real positions (the window's
+ * first win_real positions) one after another in one row; row_start[jj] is
+ * where window jj begins, row_start[per] their total; the row's length is that
+ * total rounded up to a multiple of bucket (none for bucket ≤ 1), at most
+ * per·T, and its positions past the total are padding.  Positions of the
+ * row buffer past the length are left as padding here (callers use the length). */
+int or_batch_packed(const or_plan *p, uint32_t step, uint32_t n_steps, uint32_t rank, uint32_t world,
+                    uint32_t bucket, uint32_t *tok, int32_t *pos, int32_t *doc, uint8_t *mask,
+                    int64_t *row_start, int64_t *length)
+{
+    const uint32_t B = p->c.B, T = p->c.T;
+    if (p->cycle < 0) return OR_E_STATE;
+    if (world == 0 || rank >= world || B % world) return OR_E_INVAL;
+    if ((uint64_t)step + n_steps > p->U) return OR_E_RANGE;
+    const uint32_t per = B / world;
+    const uint64_t cap = (uint64_t)per * T;
+    uint32_t *wt = malloc(4ull * T); int32_t *wp = malloc(4ull * T), *wd = malloc(4ull * T); uint8_t *wm = malloc(T);
+    if (!wt || !wp || !wd || !wm) { free(wt); free(wp); free(wd); free(wm); return OR_E_NOMEM; }
+    for (uint32_t i = 0; i < n_steps; i++) {
+        uint32_t *rt = tok + i * cap; int32_t *rp = pos + i * cap, *rd = doc + i * cap; uint8_t *rm = mask + i * cap;
+        for (uint64_t x = 0; x < cap; x++) { rt[x] = p->c.pad_token; rp[x] = 0; rd[x] = -1; rm[x] = 0; }
+        uint64_t at = 0;
+        for (uint32_t jj = 0; jj < per; jj++) {
+            uint64_t gw = or_window_of(p, (uint64_t)step + i, rank * per + jj);
+            uint64_t real = p->win_real[gw];
+            row_start[(uint64_t)i * (per + 1) + jj] = (int64_t)at;
+            or_emit_window(p, gw, wt, wp, wd, wm);
+            for (uint64_t t = 0; t < real; t++) {
+                rt[at + t] = wt[t]; rp[at + t] = wp[t]; rd[at + t] = wd[t]; rm[at + t] = wm[t];
+            }
+            at += real;
+        }
+        row_start[(uint64_t)i * (per + 1) + per] = (int64_t)at;
+        uint64_t L = at;
+        if (bucket > 1) L = (at + bucket - 1) / bucket * bucket;
+        if (L > cap) L = cap;
+        length[i] = (int64_t)L;
+    }
+    free(wt); free(wp); free(wd); free(wm);
+    return OR_OK;
+}
+
 /* Plan digest of the current cycle: SHA-256 over a little-endian byte string
  * of the recipe, the per-source stream sizes and cycle ranges, and two
  * order-free sums that change with the document order and content.  A resume
