@@ -76,6 +76,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-copy", action="store_true", help="skip the plain D2D copy used as calibration/ceiling")
     ap.add_argument("--wrap", action="store_true", help="wrap packing (PACK_FLAG_WRAP) instead of next-fit")
+    ap.add_argument("--packed", action="store_true",
+                    help="emit padding-free rows (pack_batch_packed, bucket 256) instead of padded windows and digests")
     ap.add_argument("--read-random", action="store_true",
                     help="each cycle's windows of a source read in a random order (PACK_FLAG_READ_RANDOM)")
     args = ap.parse_args()
@@ -116,14 +118,18 @@ def main():
         U = probe.cycle(0)["n_updates"]
     probe.close()
     B, T = corpus.B, corpus.T
-    out = dp.Packer.alloc_out(probe, U)  # output buffers outside the timed region
+    # output buffers outside the timed region
+    out = dp.Packer.alloc_out_packed(probe, U) if args.packed else dp.Packer.alloc_out(probe, U)
     torch.cuda.synchronize()
     log(f"cycle 0: {U} updates x {B} windows x {T} positions")
 
     def one_step():
         pk = dp.Packer(corpus, device_tensors=tensors, timing=True)
         info = pk.cycle(0)
-        pk.batch_into(0, info["n_updates"], out)
+        if args.packed:
+            pk.batch_packed_into(0, info["n_updates"], out)
+        else:
+            pk.batch_into(0, info["n_updates"], out)
         tm = pk.timings(reset=True)
         pk.close()
         return info, tm
@@ -225,7 +231,7 @@ def main():
         t_b = time.perf_counter()
         oi = op.cycle(0)
         t_c = time.perf_counter()
-        ob = op.batch(0, n_s, digests=True)
+        ob = op.batch_packed(0, n_s) if args.packed else op.batch(0, n_s, digests=True)
         t_d = time.perf_counter()
         est = (t_b - t_a) + (t_c - t_b) + (t_d - t_c) * U / n_s
         cpu = {"value": round(real / est, 1), "unit": "packed tokens/s", "cores": 1, "kind": "oracle",
@@ -235,12 +241,23 @@ def main():
         log(f"cpu baseline {cpu['value']:.4g} tokens/s ({est:.1f}s per step)")
         # bit-exactness on the sample: GPU outputs of the last timed step vs the oracle
         mism = 0
-        for key in ("tokens", "pos", "doc", "mask", "digests"):
-            g = out[key][:n_s].cpu().numpy()
-            if key == "tokens":
-                g = g.view(np.uint32)
-            mism += int((g != ob[key]).sum())
-        mism += int((out["learned"][:n_s].cpu().numpy() != ob["learned"]).sum())
+        if args.packed:
+            lens = out["length"][:n_s].cpu().numpy()
+            mism += int((lens != ob["length"]).sum()) + int((out["row_start"][:n_s].cpu().numpy() != ob["row_start"]).sum())
+            for key in ("tokens", "pos", "doc", "mask"):
+                g = out[key][:n_s].cpu().numpy()
+                if key == "tokens":
+                    g = g.view(np.uint32)
+                mism += sum(int((g[i, :int(ob["length"][i])] != ob[key][i, :int(ob["length"][i])]).sum())
+                            for i in range(n_s))
+            mism += int((out["learned"][:n_s].cpu().numpy() != op.batch(0, n_s, digests=False)["learned"]).sum())
+        else:
+            for key in ("tokens", "pos", "doc", "mask", "digests"):
+                g = out[key][:n_s].cpu().numpy()
+                if key == "tokens":
+                    g = g.view(np.uint32)
+                mism += int((g != ob[key]).sum())
+            mism += int((out["learned"][:n_s].cpu().numpy() != ob["learned"]).sum())
         mism += int(oi.plan_digest != info["plan_digest"])
         sample_check = {"updates_compared": n_s, "windows_compared": n_s * B, "mismatches": mism}
         log(f"bit-exact check on {n_s} updates: {mism} mismatches")
@@ -259,10 +276,13 @@ def main():
         "dtype": "u32",
         "data": "synthetic",
         "config": {"workload": WORKLOAD_TEXT[args.workload] + ("" if args.scale == 1.0 else f" (scale {args.scale})")
-                   + (", wrap packing" if args.wrap else "") + (", random read order" if args.read_random else ""),
+                   + (", wrap packing" if args.wrap else "") + (", random read order" if args.read_random else "")
+                   + (", padding-free rows" if args.packed else ""),
                    "docs": corpus.n_docs, "tokens": corpus.n_tokens, "T": T, "B": B, "updates": U,
                    "real_tokens_per_step": real, "positions_per_step": positions,
-                   "step": "pack_init + pack_cycle + pack_batch(all updates, learned, digests) + pack_destroy"},
+                   "step": ("pack_init + pack_cycle + pack_batch_packed(all updates, learned, bucket 256) + pack_destroy"
+                            if args.packed else
+                            "pack_init + pack_cycle + pack_batch(all updates, learned, digests) + pack_destroy")},
         "roofline": roofline,
         "roofline_hash": side.get("hash"),
         "roofline_emit": side.get("emit"),

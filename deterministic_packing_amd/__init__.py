@@ -17,7 +17,7 @@ from typing import Optional
 import numpy as np
 
 __all__ = [
-    "DpackError", "load_library", "pack_init", "pack_cycle", "pack_batch", "pack_fingerprint",
+    "DpackError", "load_library", "pack_init", "pack_cycle", "pack_batch", "pack_batch_packed", "pack_fingerprint",
     "pack_inspect", "pack_get_timings", "pack_destroy", "pack_strerror", "Packer", "INSPECT", "SYMBOLS",
 ]
 
@@ -28,7 +28,7 @@ ABI_VERSION = 1
 PACK_OK, PACK_E_ABI, PACK_E_INVAL, PACK_E_NOMEM, PACK_E_HIP = 0, -1, -2, -3, -4
 PACK_E_EXHAUSTED, PACK_E_STATE, PACK_E_RANGE = -5, -6, -7
 
-SYMBOLS = ("pack_init", "pack_cycle", "pack_batch", "pack_fingerprint", "pack_inspect",
+SYMBOLS = ("pack_init", "pack_cycle", "pack_batch", "pack_batch_packed", "pack_fingerprint", "pack_inspect",
            "pack_get_timings", "pack_destroy", "pack_strerror", "pack_last_error")
 
 PACK_FLAG_TIMING = 1
@@ -89,6 +89,13 @@ class PackOut(C.Structure):
     ]
 
 
+class PackOutPacked(C.Structure):
+    _fields_ = [
+        ("tokens", C.c_void_p), ("pos", C.c_void_p), ("doc", C.c_void_p), ("mask", C.c_void_p),
+        ("row_start", C.c_void_p), ("length", C.c_void_p), ("learned", C.c_void_p), ("bucket", C.c_uint32),
+    ]
+
+
 _lib = None
 
 
@@ -109,6 +116,8 @@ def load_library(path: Optional[str] = None):
     lib.pack_cycle.argtypes = [vp, u32, C.POINTER(PackCycleInfo)]
     lib.pack_batch.restype = i32
     lib.pack_batch.argtypes = [vp, u32, u32, C.POINTER(PackOut)]
+    lib.pack_batch_packed.restype = i32
+    lib.pack_batch_packed.argtypes = [vp, u32, u32, C.POINTER(PackOutPacked)]
     lib.pack_fingerprint.restype = i32
     lib.pack_fingerprint.argtypes = [vp, vp, u32, vp]
     lib.pack_inspect.restype = i32
@@ -157,6 +166,10 @@ def pack_cycle(ctx: int, cycle: int, info: Optional[PackCycleInfo] = None) -> Pa
 
 def pack_batch(ctx: int, step: int, n_steps: int, out: PackOut) -> None:
     _check(load_library().pack_batch(ctx, step, n_steps, C.byref(out)), "pack_batch", ctx)
+
+
+def pack_batch_packed(ctx: int, step: int, n_steps: int, out: PackOutPacked) -> None:
+    _check(load_library().pack_batch_packed(ctx, step, n_steps, C.byref(out)), "pack_batch_packed", ctx)
 
 
 def pack_fingerprint(ctx: int, digests_ptr: int, n_batches: int, out_ptr: int) -> None:
@@ -277,6 +290,29 @@ class Packer:
 
     def batch(self, step: int, n_steps: int = 1, digests: bool = True, learned: bool = True) -> dict:
         return self.batch_into(step, n_steps, self.alloc_out(n_steps, digests, learned))
+
+    def alloc_out_packed(self, n_steps: int, learned: bool = True) -> dict:
+        t = self.torch
+        dev = self.dev["tokens"].device
+        cap = self.per * self.corpus.T
+        return dict(tokens=t.empty((n_steps, cap), dtype=t.int32, device=dev),
+                    pos=t.empty((n_steps, cap), dtype=t.int32, device=dev),
+                    doc=t.empty((n_steps, cap), dtype=t.int32, device=dev),
+                    mask=t.empty((n_steps, cap), dtype=t.uint8, device=dev),
+                    row_start=t.empty((n_steps, self.per + 1), dtype=t.int64, device=dev),
+                    length=t.empty(n_steps, dtype=t.int64, device=dev),
+                    learned=t.empty(n_steps, dtype=t.int64, device=dev) if learned else None)
+
+    def batch_packed_into(self, step: int, n_steps: int, out: dict, bucket: int = 256) -> dict:
+        po = PackOutPacked(out["tokens"].data_ptr(), out["pos"].data_ptr(), out["doc"].data_ptr(),
+                           out["mask"].data_ptr(), out["row_start"].data_ptr(), out["length"].data_ptr(),
+                           out["learned"].data_ptr() if out.get("learned") is not None else None, bucket)
+        pack_batch_packed(self.ctx, step, n_steps, po)
+        return out
+
+    def batch_packed(self, step: int, n_steps: int = 1, bucket: int = 256, learned: bool = True) -> dict:
+        """Padding-free rows: update i's windows' real positions in row i."""
+        return self.batch_packed_into(step, n_steps, self.alloc_out_packed(n_steps, learned), bucket)
 
     def fingerprint(self, digests) -> "torch.Tensor":
         """digests: device uint8 [n][B][32] (all ranks' slices in rank order)."""

@@ -735,6 +735,58 @@ int pack_batch(pack_ctx* c, uint32_t step, uint32_t n_steps, const pack_out* out
     }
 }
 
+int pack_batch_packed(pack_ctx* c, uint32_t step, uint32_t n_steps, const pack_out_packed* out) {
+    if (!c) return PACK_E_INVAL;
+    c->err.clear();
+    if (c->cycle < 0) {
+        c->err = "no cycle planned";
+        return PACK_E_STATE;
+    }
+    if (n_steps == 0 || (uint64_t)step + n_steps > c->U) {
+        c->err = "step range outside the current cycle";
+        return PACK_E_RANGE;
+    }
+    if (!out || !out->tokens || !out->pos || !out->doc || !out->mask || !out->row_start || !out->length) {
+        c->err = "tokens, pos, doc, mask, row_start and length outputs are required";
+        return PACK_E_INVAL;
+    }
+    if (((uintptr_t)out->tokens | (uintptr_t)out->pos | (uintptr_t)out->doc) % 4 ||
+        ((uintptr_t)out->row_start | (uintptr_t)out->length | (uintptr_t)out->learned) % 8) {
+        c->err = "tokens/pos/doc must be 4-byte aligned, row_start/length/learned 8-byte aligned";
+        return PACK_E_INVAL;
+    }
+    try {
+        dp::EmitArgs a{};
+        a.tok = out->tokens;
+        a.pos = out->pos;
+        a.doc = out->doc;
+        a.mask = out->mask;
+        a.learned = out->learned;
+        a.row_start = out->row_start;
+        a.length = out->length;
+        a.bucket = out->bucket;
+        a.step = step;
+        a.n_steps = n_steps;
+        a.rank = c->cfg.rank;
+        a.per = c->p.B / c->cfg.world;
+        if ((uint64_t)n_steps * a.per >= (1ull << 31)) {
+            c->err = "too many windows in one call";
+            return PACK_E_RANGE;
+        }
+        c->timer.begin(PACK_PHASE_EMIT, c->st);
+        dp::launch_emit_packed(c->p, a, c->st);
+        c->timer.end(c->st);
+        if (a.learned) {
+            c->timer.begin(PACK_PHASE_LEARNED, c->st);
+            dp::launch_learned(c->p, a, c->st);
+            c->timer.end(c->st);
+        }
+        return PACK_OK;
+    } catch (const dp::HipError& e) {
+        return fail_hip(c, e);
+    }
+}
+
 int pack_fingerprint(pack_ctx* c, const uint8_t* digests, uint32_t n_batches, uint8_t* out) {
     if (!c) return PACK_E_INVAL;
     c->err.clear();

@@ -243,8 +243,10 @@ struct EmitArgs {
     uint32_t* tok; int32_t* pos; int32_t* doc; uint8_t* mask;
     int64_t* learned; uint8_t* digests;
     uint32_t step, n_steps, rank, per;
+    int64_t* row_start; int64_t* length; uint32_t bucket;  // padding-free rows only
 };
 void launch_emit(const Plan& p, const EmitArgs& a, hipStream_t st);
+void launch_emit_packed(const Plan& p, const EmitArgs& a, hipStream_t st);  // padding-free rows
 void launch_learned(const Plan& p, const EmitArgs& a, hipStream_t st);
 void launch_window_sha(const Plan& p, const EmitArgs& a, hipStream_t st);
 bool emit_sha_fits(const EmitArgs& a);                 // launch_emit_sha applies (one workgroup per CU)

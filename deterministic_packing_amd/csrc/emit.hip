@@ -25,6 +25,10 @@ struct PieceView {
     uint64_t src;
 };
 
+// PACKED: padding-free rows (Linnet Training, the transformers Trainer path):
+// window jj of update i writes only its real positions, at row position
+// a.row_start[i][jj] of update i's row (stride B/world·T), one element at a time.
+template <bool PACKED>
 __global__ __launch_bounds__(EB) void k_emit(Plan p, EmitArgs a) {
     __shared__ uint32_t s_woff[ECAP];
     __shared__ uint32_t s_doc[ECAP];
@@ -76,7 +80,8 @@ __global__ __launch_bounds__(EB) void k_emit(Plan p, EmitArgs a) {
         return piece(q);
     };
 
-    const uint64_t out0 = (uint64_t)widx * p.T;
+    const uint64_t out0 = PACKED ? (uint64_t)i * a.per * p.T + (uint64_t)a.row_start[(uint64_t)i * (a.per + 1) + jj]
+                                 : (uint64_t)widx * p.T;
     uint4* tok4 = reinterpret_cast<uint4*>(a.tok + out0);
     int4* pos4 = reinterpret_cast<int4*>(a.pos + out0);
     int4* doc4 = reinterpret_cast<int4*>(a.doc + out0);
@@ -85,6 +90,7 @@ __global__ __launch_bounds__(EB) void k_emit(Plan p, EmitArgs a) {
 
     for (uint32_t g = threadIdx.x; g < p.T / 4; g += EB) {
         const uint32_t t0 = 4 * g;
+        if (PACKED && t0 >= real) break;  // no padding inside a packed row
         uint32_t tk[4];
         int32_t ps[4], dc[4];
         uint32_t mk = 0;
@@ -114,10 +120,69 @@ __global__ __launch_bounds__(EB) void k_emit(Plan p, EmitArgs a) {
                 mk |= (t >= v.mfrom ? 1u : 0u) << (8 * e);
             }
         }
-        tok4[g] = make_uint4(tk[0], tk[1], tk[2], tk[3]);
-        pos4[g] = make_int4(ps[0], ps[1], ps[2], ps[3]);
-        doc4[g] = make_int4(dc[0], dc[1], dc[2], dc[3]);
-        mask4[g] = mk;
+        if (PACKED) {
+#pragma unroll
+            for (uint32_t e = 0; e < 4; ++e) {
+                if (t0 + e >= real) break;
+                a.tok[out0 + t0 + e] = tk[e];
+                a.pos[out0 + t0 + e] = ps[e];
+                a.doc[out0 + t0 + e] = dc[e];
+                a.mask[out0 + t0 + e] = (uint8_t)(mk >> (8 * e));
+            }
+        } else {
+            tok4[g] = make_uint4(tk[0], tk[1], tk[2], tk[3]);
+            pos4[g] = make_int4(ps[0], ps[1], ps[2], ps[3]);
+            doc4[g] = make_int4(dc[0], dc[1], dc[2], dc[3]);
+            mask4[g] = mk;
+        }
+    }
+}
+
+// Row starts of the padding-free rows: per update (one workgroup), an
+// exclusive scan of its windows' real positions in slot order, chunk by chunk
+// with a carry; then the total and the length rounded up to the bucket.
+__global__ __launch_bounds__(256) void k_packed_starts(Plan p, EmitArgs a) {
+    __shared__ uint64_t part[256 / WAVE];
+    const uint32_t i = blockIdx.x, lane = threadIdx.x % WAVE, wid = threadIdx.x / WAVE;
+    int64_t* rs = a.row_start + (uint64_t)i * (a.per + 1);
+    uint64_t carry = 0;
+    for (uint32_t c0 = 0; c0 < a.per; c0 += 256) {
+        const uint32_t jj = c0 + threadIdx.x;
+        const uint64_t v = jj < a.per ? p.win_real[window_of(p, (uint64_t)a.step + i, a.rank * a.per + jj)] : 0;
+        uint64_t x = v;  // inclusive scan in the wave
+#pragma unroll
+        for (int o = 1; o < WAVE; o <<= 1) {
+            const uint64_t y = __shfl_up(x, o, WAVE);
+            if (lane >= (uint32_t)o) x += y;
+        }
+        if (lane == WAVE - 1) part[wid] = x;
+        __syncthreads();
+        uint64_t before = carry;
+        for (uint32_t w = 0; w < wid; ++w) before += part[w];
+        if (jj < a.per) rs[jj] = (int64_t)(before + x - v);
+        uint64_t chunk = 0;
+        for (uint32_t w = 0; w < 256 / WAVE; ++w) chunk += part[w];
+        __syncthreads();
+        carry += chunk;
+    }
+    if (threadIdx.x == 0) {
+        rs[a.per] = (int64_t)carry;
+        const uint64_t cap = (uint64_t)a.per * p.T;
+        uint64_t L = a.bucket > 1 ? (carry + a.bucket - 1) / a.bucket * a.bucket : carry;
+        a.length[i] = (int64_t)(L < cap ? L : cap);
+    }
+}
+
+// padding of each packed row between its total and its length
+__global__ __launch_bounds__(256) void k_packed_pad(Plan p, EmitArgs a) {
+    const uint32_t i = blockIdx.x;
+    const uint64_t base = (uint64_t)i * a.per * p.T;
+    const uint64_t from = (uint64_t)a.row_start[(uint64_t)i * (a.per + 1) + a.per], to = (uint64_t)a.length[i];
+    for (uint64_t x = from + threadIdx.x; x < to; x += blockDim.x) {
+        a.tok[base + x] = p.pad_token;
+        a.pos[base + x] = 0;
+        a.doc[base + x] = -1;
+        a.mask[base + x] = 0;
     }
 }
 
@@ -142,7 +207,15 @@ __global__ __launch_bounds__(256) void k_learned(Plan p, EmitArgs a) {
 
 void launch_emit(const Plan& p, const EmitArgs& a, hipStream_t st) {
     const uint64_t windows = (uint64_t)a.n_steps * a.per;
-    hipLaunchKernelGGL(k_emit, dim3((uint32_t)windows), dim3(EB), 0, st, p, a);
+    hipLaunchKernelGGL(k_emit<false>, dim3((uint32_t)windows), dim3(EB), 0, st, p, a);
+    DP_HIP(hipGetLastError());
+}
+
+void launch_emit_packed(const Plan& p, const EmitArgs& a, hipStream_t st) {
+    const uint64_t windows = (uint64_t)a.n_steps * a.per;
+    hipLaunchKernelGGL(k_packed_starts, dim3(a.n_steps), dim3(256), 0, st, p, a);
+    hipLaunchKernelGGL(k_emit<true>, dim3((uint32_t)windows), dim3(EB), 0, st, p, a);
+    hipLaunchKernelGGL(k_packed_pad, dim3(a.n_steps), dim3(256), 0, st, p, a);
     DP_HIP(hipGetLastError());
 }
 

@@ -195,6 +195,30 @@ typedef struct pack_out {
  * or n_steps = 0), PACK_E_INVAL (a NULL output array), PACK_E_HIP. */
 int pack_batch(pack_ctx *ctx, uint32_t step, uint32_t n_steps, const pack_out *out);
 
+/* Padding-free rows.  Linnet "Training", Supervised fine-tuning (the
+ * transformers Trainer path): the padding is removed and a batch's rows are
+ * packed into one sequence whose length rounds up to a multiple of a bucket
+ * (256) so that few shapes compile; a position id 0 starts each sequence.
+ * Device arrays, all required but learned: */
+typedef struct pack_out_packed {
+    uint32_t *tokens;    /* [n_steps][B/world · T]: update i's row; window jj's real positions
+                            (as in pack_batch) at row_start[i][jj] .. row_start[i][jj+1] */
+    int32_t *pos;        /* same layout; 0 starts each piece */
+    int32_t *doc;
+    uint8_t *mask;
+    int64_t *row_start;  /* [n_steps][B/world + 1]: where each window begins; [B/world] = the total */
+    int64_t *length;     /* [n_steps]: the total rounded up to a multiple of bucket, at most B/world · T;
+                            positions from the total to the length are padding, later ones are not written */
+    int64_t *learned;    /* [n_steps] or NULL: as in pack_batch */
+    uint32_t bucket;     /* the rounding multiple (256 in the pages); 0 or 1: none */
+} pack_out_packed;
+
+/* pack_batch_packed — pack_batch's windows as padding-free rows (no digests:
+ * window digests are defined over the padded records of pack_batch).
+ * tokens, pos and doc must be 4-byte aligned, row_start, length and learned
+ * 8-byte aligned.  Asynchronous on cfg->stream.  Errors as pack_batch. */
+int pack_batch_packed(pack_ctx *ctx, uint32_t step, uint32_t n_steps, const pack_out_packed *out);
+
 /* pack_fingerprint — batch fingerprints: for each of n_batches, SHA-256 over
  * its B window digests (B·32 bytes, slot order) from the device array
  * digests [n_batches][B][32], into the device array out [n_batches][32].

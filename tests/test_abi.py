@@ -92,4 +92,5 @@ def test_null_arguments_are_errors(lib):
     assert lib.pack_init(None, None) == dp.PACK_E_INVAL
     assert lib.pack_cycle(None, 0, None) == dp.PACK_E_INVAL
     assert lib.pack_batch(None, 0, 1, None) == dp.PACK_E_INVAL
+    assert lib.pack_batch_packed(None, 0, 1, None) == dp.PACK_E_INVAL
     lib.pack_destroy(None)

@@ -55,6 +55,39 @@ def test_read_random_parity(kind, arg):
     _parity_run(_corpus(kind, arg).replace(read_random=True), "random-order-" + kind, arg)
 
 
+PACKED_CASES = [("small", s, b, w) for s, b, w in [(0, 256, 1), (1, 64, 1), (3, 1, 2), (4, 256, 4), (5, 256, 1),
+                                                   (7, 0, 7)]] + [("sft", 0.004, 256, 1), ("pretrain", 0.006, 256, 8),
+                                                                  ("long", 0.01, 256, 2)]
+
+
+@pytest.mark.parametrize("kind,arg,bucket,world", PACKED_CASES)
+def test_padding_free_rows_parity(kind, arg, bucket, world):
+    """pack_batch_packed against the oracle's padding-free rows (rank 0 and the last rank)."""
+    c = _corpus(kind, arg)
+    if c.B % world:
+        c = c.replace(B=world * max(1, c.B // world))
+    op = oracle.Plan(c)
+    try:
+        oi = op.cycle(0)
+    except oracle.OracleError:
+        pytest.skip("corpus exhausted at this size")
+    n = min(3, oi.n_updates)
+    for rank in sorted({0, world - 1}):
+        say("packed", kind, arg, "bucket", bucket, "world", world, "rank", rank)
+        pk = dp.Packer(c, rank=rank, world=world)
+        pk.cycle(0)
+        g = {k: (v.cpu().numpy() if v is not None else None) for k, v in pk.batch_packed(0, n, bucket).items()}
+        o = op.batch_packed(0, n, rank=rank, world=world, bucket=bucket)
+        assert np.array_equal(g["row_start"], o["row_start"]) and np.array_equal(g["length"], o["length"])
+        for i in range(n):
+            L = int(o["length"][i])
+            for k in ("tokens", "pos", "doc", "mask"):
+                a = g[k][i, :L].view(np.uint32) if k == "tokens" else g[k][i, :L]
+                assert np.array_equal(a, o[k][i, :L]), (i, k)
+        assert np.array_equal(g["learned"], op.batch(0, n, digests=False)["learned"])
+        pk.close()
+
+
 HELDOUT_CASES = [(s, w) for s in range(6) for w in (False, True)]
 
 
