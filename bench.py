@@ -156,7 +156,10 @@ def main():
 
     # per-kernel figures (averaged per launch over the timed steps)
     n_windows = U * B
-    emit_bytes = 4.0 * real + 13.0 * positions  # read every real token once, write 13 bytes per position
+    # read every real token once, write 13 bytes per output position (padded
+    # windows: U·B·T; padding-free rows: the rows' lengths, bucket padding included)
+    row_positions = int(out["length"].sum().item()) if args.packed else positions
+    emit_bytes = 4.0 * real + 13.0 * row_positions
     fused = phase_calls.get("emit", 0) == 0     # emission ran inside the digest kernel
     algo = {
         "emit": ("hbm", emit_bytes, "GB/s"),
@@ -235,8 +238,9 @@ def main():
         t_d = time.perf_counter()
         est = (t_b - t_a) + (t_c - t_b) + (t_d - t_c) * U / n_s
         cpu = {"value": round(real / est, 1), "unit": "packed tokens/s", "cores": 1, "kind": "oracle",
-               "sample": (f"whole plan of the corpus ({t_b - t_a:.2f}s) + cycle ({t_c - t_b:.2f}s) + emission "
-                          f"with SHA-256 of updates 0..{n_s - 1} of {U} ({t_d - t_c:.2f}s), scaled to {U} "
+               "sample": (f"whole plan of the corpus ({t_b - t_a:.2f}s) + cycle ({t_c - t_b:.2f}s) + "
+                          + ("padding-free rows" if args.packed else "emission with SHA-256")
+                          + f" of updates 0..{n_s - 1} of {U} ({t_d - t_c:.2f}s), scaled to {U} "
                           f"updates: {est:.2f}s per step; single-threaded C")}
         log(f"cpu baseline {cpu['value']:.4g} tokens/s ({est:.1f}s per step)")
         # bit-exactness on the sample: GPU outputs of the last timed step vs the oracle
@@ -279,7 +283,7 @@ def main():
                    + (", wrap packing" if args.wrap else "") + (", random read order" if args.read_random else "")
                    + (", padding-free rows" if args.packed else ""),
                    "docs": corpus.n_docs, "tokens": corpus.n_tokens, "T": T, "B": B, "updates": U,
-                   "real_tokens_per_step": real, "positions_per_step": positions,
+                   "real_tokens_per_step": real, "positions_per_step": row_positions,
                    "step": ("pack_init + pack_cycle + pack_batch_packed(all updates, learned, bucket 256) + pack_destroy"
                             if args.packed else
                             "pack_init + pack_cycle + pack_batch(all updates, learned, digests) + pack_destroy")},

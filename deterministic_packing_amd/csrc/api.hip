@@ -750,9 +750,9 @@ int pack_batch_packed(pack_ctx* c, uint32_t step, uint32_t n_steps, const pack_o
         c->err = "tokens, pos, doc, mask, row_start and length outputs are required";
         return PACK_E_INVAL;
     }
-    if (((uintptr_t)out->tokens | (uintptr_t)out->pos | (uintptr_t)out->doc) % 4 ||
+    if (((uintptr_t)out->tokens | (uintptr_t)out->pos | (uintptr_t)out->doc) % 16 || (uintptr_t)out->mask % 4 ||
         ((uintptr_t)out->row_start | (uintptr_t)out->length | (uintptr_t)out->learned) % 8) {
-        c->err = "tokens/pos/doc must be 4-byte aligned, row_start/length/learned 8-byte aligned";
+        c->err = "tokens/pos/doc must be 16-byte aligned, mask 4-byte, row_start/length/learned 8-byte aligned";
         return PACK_E_INVAL;
     }
     try {

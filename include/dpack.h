@@ -215,8 +215,8 @@ typedef struct pack_out_packed {
 
 /* pack_batch_packed — pack_batch's windows as padding-free rows (no digests:
  * window digests are defined over the padded records of pack_batch).
- * tokens, pos and doc must be 4-byte aligned, row_start, length and learned
- * 8-byte aligned.  Asynchronous on cfg->stream.  Errors as pack_batch. */
+ * tokens, pos and doc must be 16-byte aligned, mask 4-byte aligned, row_start,
+ * length and learned 8-byte aligned.  Asynchronous on cfg->stream.  Errors as pack_batch. */
 int pack_batch_packed(pack_ctx *ctx, uint32_t step, uint32_t n_steps, const pack_out_packed *out);
 
 /* pack_fingerprint — batch fingerprints: for each of n_batches, SHA-256 over

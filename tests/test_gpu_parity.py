@@ -32,6 +32,10 @@ def _corpus(kind, arg):
         return random_small(s, n_docs=60 + 40 * s, n_sources=1 + s % 4, max_strata=1 + s % 3, T=64 * (1 + s % 2),
                             B=[1, 2, 4, 6, 8, 3, 5, 7][s], max_len=[40, 150, 300, 90, 64, 200, 20, 500][s],
                             prompts=bool(s % 2), bp_max=2000)
+    if kind == "tinydocs":  # documents of 1-5 tokens: windows of many pieces, short source tails
+        s = int(arg)
+        return random_small(50 + s, n_docs=40 + 30 * s, n_sources=1 + s % 3, max_strata=2, T=64, B=1 + s,
+                            max_len=5, prompts=bool(s % 2), bp_max=1000)
     c = make_corpus(kind, arg)
     if kind == "pretrain":
         c = c.replace(updates_per_cycle=0)  # a scaled-down corpus cannot supply 200 updates
@@ -55,15 +59,18 @@ def test_read_random_parity(kind, arg):
     _parity_run(_corpus(kind, arg).replace(read_random=True), "random-order-" + kind, arg)
 
 
-PACKED_CASES = [("small", s, b, w) for s, b, w in [(0, 256, 1), (1, 64, 1), (3, 1, 2), (4, 256, 4), (5, 256, 1),
-                                                   (7, 0, 7)]] + [("sft", 0.004, 256, 1), ("pretrain", 0.006, 256, 8),
-                                                                  ("long", 0.01, 256, 2)]
+PACKED_CASES = ([("small", s, b, w, False) for s, b, w in [(0, 256, 1), (1, 64, 1), (3, 1, 2), (4, 256, 4),
+                                                            (5, 256, 1), (7, 0, 7)]]
+                + [("tinydocs", s, b, 1, wr) for s, b in [(0, 1), (1, 256), (2, 3), (3, 0)] for wr in (False, True)]
+                + [("small", 2, 256, 1, True), ("sft", 0.004, 256, 1, False), ("pretrain", 0.006, 256, 8, False),
+                   ("long", 0.01, 256, 2, False)])
 
 
-@pytest.mark.parametrize("kind,arg,bucket,world", PACKED_CASES)
-def test_padding_free_rows_parity(kind, arg, bucket, world):
-    """pack_batch_packed against the oracle's padding-free rows (rank 0 and the last rank)."""
-    c = _corpus(kind, arg)
+@pytest.mark.parametrize("kind,arg,bucket,world,wrap", PACKED_CASES)
+def test_padding_free_rows_parity(kind, arg, bucket, world, wrap):
+    """pack_batch_packed against the oracle's padding-free rows (rank 0 and the last rank).
+    Row starts fall anywhere, so windows begin and end inside 16-byte store groups."""
+    c = _corpus(kind, arg).replace(wrap=wrap)
     if c.B % world:
         c = c.replace(B=world * max(1, c.B // world))
     op = oracle.Plan(c)
@@ -85,6 +92,38 @@ def test_padding_free_rows_parity(kind, arg, bucket, world):
                 a = g[k][i, :L].view(np.uint32) if k == "tokens" else g[k][i, :L]
                 assert np.array_equal(a, o[k][i, :L]), (i, k)
         assert np.array_equal(g["learned"], op.batch(0, n, digests=False)["learned"])
+        pk.close()
+
+
+PACKED_SHORT = {
+    # windows of 1-3 real positions, many of them inside one 16-byte store group of the row
+    "split_130": (lambda: _explicit([130] * 20, 64, 3), 1),
+    "split_66": (lambda: _explicit([66] * 31, 64, 5), 1),
+    "mixed_prompts": (lambda: _explicit([130, 3, 1, 2, 67] * 12, 64, 4, prompts=[5, 0, 1, 0, 70] * 12), 2),
+}
+
+
+@pytest.mark.parametrize("name", sorted(PACKED_SHORT))
+def test_padding_free_rows_short_windows(name):
+    """Every update of a cycle whose windows are shorter than a store group."""
+    make, world = PACKED_SHORT[name]
+    c = make()
+    op = oracle.Plan(c)
+    n = op.cycle(0).n_updates
+    for rank in sorted({0, world - 1}):
+        say("packed-short", name, "world", world, "rank", rank)
+        pk = dp.Packer(c, rank=rank, world=world)
+        pk.cycle(0)
+        g = {k: (v.cpu().numpy() if v is not None else None) for k, v in pk.batch_packed(0, n, 8).items()}
+        o = op.batch_packed(0, n, rank=rank, world=world, bucket=8)
+        lens = np.diff(o["row_start"], axis=1)
+        assert ((lens > 0) & (lens < 4)).any()
+        assert np.array_equal(g["row_start"], o["row_start"]) and np.array_equal(g["length"], o["length"])
+        for i in range(n):
+            L = int(o["length"][i])
+            for k in ("tokens", "pos", "doc", "mask"):
+                a = g[k][i, :L].view(np.uint32) if k == "tokens" else g[k][i, :L]
+                assert np.array_equal(a, o[k][i, :L]), (i, k)
         pk.close()
 
 
