@@ -77,7 +77,11 @@ def _load():
         lib.or_cycle.restype = i32
         lib.or_cycle.argtypes = [vp, u32, u32]
         lib.or_cycle_state.restype = u32
-        lib.or_cycle_state.argtypes = [vp, C.POINTER(C.c_int64), vp]
+        lib.or_cycle_state.argtypes = [vp, C.POINTER(C.c_int64), vp, vp]
+        lib.or_cum_export.restype = i32
+        lib.or_cum_export.argtypes = [vp, vp]
+        lib.or_cumulative.restype = i32
+        lib.or_cumulative.argtypes = [u32, u32, vp, vp, u64, u64, vp, C.POINTER(u64)]
         lib.or_window_of.restype = u64
         lib.or_window_of.argtypes = [vp, u64, u32]
         lib.or_emit_window.restype = None
@@ -141,6 +145,23 @@ def apportion(B: int, weights) -> np.ndarray:
     return n
 
 
+def cumulative(B: int, weights, remaining, updates: int = 0, cap: Optional[int] = None):
+    """C6c on its own: (U, A [U+1, S]) for B windows per update, integer
+    weights and each source's remaining windows; updates = 0 takes the most
+    that fit."""
+    w = np.ascontiguousarray(weights, np.uint64)
+    rem = np.ascontiguousarray(remaining, np.uint64)
+    S = w.shape[0]
+    if cap is None:
+        cap = updates if updates else int(rem.sum()) // B
+    A = np.zeros((cap + 1, S), np.uint32)
+    U = C.c_uint64()
+    rc = _load().or_cumulative(B, S, _ptr(w), _ptr(rem), updates, cap, _ptr(A), C.byref(U))
+    if rc:
+        raise OracleError(rc, "cumulative")
+    return int(U.value), A[:U.value + 1].copy()
+
+
 def slot_table(B: int, n) -> tuple:
     n = np.ascontiguousarray(n, dtype=np.uint32)
     ss = np.zeros(B, dtype=np.uint32)
@@ -178,6 +199,7 @@ class _OrCorpus(C.Structure):
         ("n_sources", C.c_uint32), ("n_strata", C.c_void_p), ("weight", C.c_void_p),
         ("bp", C.c_void_p), ("T", C.c_uint32), ("B", C.c_uint32), ("seed", C.c_uint64),
         ("pad_token", C.c_uint32), ("wrap", C.c_uint32), ("heldout", C.c_uint32), ("read_random", C.c_uint32),
+        ("cumulative", C.c_uint32),
     ]
 
 
@@ -226,7 +248,8 @@ class Plan:
             _ptr(k["offsets"]), D, _ptr(k["source"]) if D else None, _ptr(k["stratum"]) if D else None,
             _ptr(k["prompt_len"]), S, _ptr(k["n_strata"]), _ptr(k["weight"]), _ptr(k["bp"]),
             c.T, c.B, c.seed & 0xFFFFFFFFFFFFFFFF, c.pad_token, 1 if getattr(c, "wrap", False) else 0,
-            1 if getattr(c, "heldout", False) else 0, 1 if getattr(c, "read_random", False) else 0)
+            1 if getattr(c, "heldout", False) else 0, 1 if getattr(c, "read_random", False) else 0,
+            1 if getattr(c, "cumulative", False) else 0)
         err = C.c_int(0)
         self._p = lib.or_plan_build(C.byref(self._cs), C.byref(err))
         if not self._p:
@@ -279,9 +302,8 @@ class Plan:
         S = self.corpus.n_sources
         start = np.zeros(S, np.uint64)
         cyc = C.c_int64()
-        U = int(lib.or_cycle_state(self._p, C.byref(cyc), _ptr(start)))
-        n = self.n_per_update.astype(np.uint64)
-        taken = n * np.uint64(U)
+        taken = np.zeros(S, np.uint64)
+        U = int(lib.or_cycle_state(self._p, C.byref(cyc), _ptr(start), _ptr(taken)))
         remaining = self.windows_per_source - start - taken
         wins = [self.window_of(b, j) for b in range(U) for j in range(self.corpus.B)] if U * self.corpus.B <= 2_000_000 else None
         if wins is not None:
@@ -297,6 +319,16 @@ class Plan:
         self.cycle_info = CycleInfo(c, U, start, taken, remaining, real, learned,
                                     U * self.corpus.B * self.corpus.T, dig.tobytes())
         return self.cycle_info
+
+    def cumulative_taken(self) -> np.ndarray:
+        """With the cumulative mixture: A [U+1, S], windows of each source taken
+        before each update of the current cycle (row U: the cycle's totals)."""
+        S = self.corpus.n_sources
+        A = np.zeros((self.cycle_info.n_updates + 1, S), np.uint32)
+        rc = _load().or_cum_export(self._p, _ptr(A))
+        if rc:
+            raise OracleError(rc, "cum_export")
+        return A
 
     def window_of(self, b: int, j: int) -> int:
         return int(_load().or_window_of(self._p, b, j))

@@ -31,6 +31,10 @@
  *     implementation.
  *   - SHA-256: FIPS 180-4; pinned against Python's hashlib.
  *   - the sort uses the C library's qsort with a total order as comparator.
+ *   - cumulative mixture (C6c): pinned by its requirements in exact integers
+ *     (quota at every update boundary, monotone, B per update), by exhaustive
+ *     enumeration of every valid schedule on tiny cases, and by closed forms
+ *     (one source; whole-window shares equal the fixed apportionment).
  *
  * All integers are unsigned unless stated; products that can exceed 64 bits
  * are taken in unsigned __int128.
@@ -52,6 +56,7 @@ enum {
     OR_E_EXHAUSTED = -5,
     OR_E_STATE = -6,
     OR_E_RANGE = -7,
+    OR_E_INTERNAL = -9,  /* a step's own guarantee failed (never expected) */
 };
 
 /* ------------------------------------------------------------------------ */
@@ -299,6 +304,85 @@ int or_slot_table(uint32_t B, uint32_t S, const uint32_t *n, uint32_t *slot_src,
     return OR_OK;
 }
 
+/* C6c. Cumulative mixture of a cycle ([NS] Concepts: every update holds each
+ * source within two samples of its recipe share; max_epochs 1, so every
+ * source's windows are to be trained, small shares included).  Reading: the
+ * cycle's updates are one schedule; after u updates source s has taken
+ * A_s(u) windows with floor(u·B·w_s/W) ≤ A_s(u) ≤ ceil(u·B·w_s/W) and
+ * A_s(u) ≥ A_s(u−1).  Each update's count A_s(u+1) − A_s(u) is then within
+ * two of B·w_s/W, and a source whose share is below one window per update
+ * still gets its windows, spread over the cycle.
+ * Source s's j-th window of the cycle (j ≥ 1) is released in update
+ * floor((j−1)·W/(B·w_s)) (from there on taking it keeps A_s within the upper
+ * quota) and is due by update ceil(j·W/(B·w_s)) − 1 (the lower quota at the
+ * next boundary needs it).  Update u takes the B released, not yet taken
+ * windows with the earliest due updates, ties to the lower source, then the
+ * lower j: earliest deadline first.  A seat-by-seat schedule within quota at
+ * every house size exists (Balinski and Young's quota method, 1975), so one
+ * within quota at every update boundary does, and earliest deadline first
+ * meets every deadline of unit jobs whenever some schedule does: a missed
+ * deadline or an update with fewer than B released windows is an internal
+ * error here, never expected.
+ * The cycle has u_cfg updates, or (u_cfg = 0) the most after which no source
+ * has taken more than its rem_s remaining windows.  Writes A [(U+1)·S] (A must
+ * hold (cap+1)·S entries, cap ≥ the updates it can run) and returns U, or 0
+ * when even one update does not fit (the caller reports exhaustion). */
+typedef struct { u128 due; uint32_t s; uint32_t j; } due_item;
+
+static int cmp_due(const void *pa, const void *pb)
+{
+    const due_item *a = (const due_item *)pa, *b = (const due_item *)pb;
+    if (a->due != b->due) return a->due < b->due ? -1 : 1;
+    if (a->s != b->s) return a->s < b->s ? -1 : 1;
+    if (a->j != b->j) return a->j < b->j ? -1 : 1;
+    return 0;
+}
+
+int or_cumulative(uint32_t B, uint32_t S, const uint64_t *w, const uint64_t *rem, uint64_t u_cfg,
+                  uint64_t cap, uint32_t *A, uint64_t *U_out)
+{
+    u128 W = 0;
+    for (uint32_t s = 0; s < S; s++) W += w[s];
+    if (W == 0 || W >> 64 || B == 0) return OR_E_INVAL;
+    *U_out = 0;
+    for (uint32_t s = 0; s < S; s++) A[s] = 0;
+    due_item *it = (due_item *)malloc(sizeof(due_item) * ((uint64_t)B + S + 1));
+    if (!it) return OR_E_NOMEM;
+    uint64_t U = 0;
+    for (uint64_t u = 0; u < cap && (u_cfg == 0 || u < u_cfg); u++) {
+        const uint32_t *a = A + u * S;
+        uint32_t *an = A + (u + 1) * S;
+        /* released, not yet taken windows of every source with their due updates */
+        uint64_t m = 0;
+        for (uint32_t s = 0; s < S; s++) {
+            if (w[s] == 0) continue;
+            u128 q = (u128)(u + 1) * B * w[s];
+            u128 hi = (q + W - 1) / W;                    /* ceil((u+1)·B·w_s/W) */
+            for (u128 j = (u128)a[s] + 1; j <= hi; j++) {
+                u128 num = j * W, den = (u128)B * w[s];
+                it[m].due = (num + den - 1) / den - 1;      /* ceil(j·W/(B·w_s)) − 1 */
+                it[m].s = s;
+                it[m].j = (uint32_t)j;
+                m++;
+            }
+        }
+        if (m < B) { free(it); return OR_E_INTERNAL; }
+        qsort(it, m, sizeof(due_item), cmp_due);
+        for (uint32_t s = 0; s < S; s++) an[s] = a[s];
+        for (uint64_t r = 0; r < B; r++) an[it[r].s] += 1;
+        for (uint64_t r = B; r < m; r++)
+            if (it[r].due <= u) { free(it); return OR_E_INTERNAL; }  /* deadline missed */
+        int fits = 1;
+        for (uint32_t s = 0; s < S; s++)
+            if (an[s] > rem[s]) fits = 0;
+        if (!fits) break;
+        U = u + 1;
+    }
+    free(it);
+    *U_out = U;
+    return OR_OK;
+}
+
 /* ------------------------------------------------------------------------ */
 /* The plan of a corpus: C1–C6 over every document.                          */
 /* ------------------------------------------------------------------------ */
@@ -321,6 +405,7 @@ typedef struct {
     uint32_t wrap;               /* 0: next-fit cut at document ends; 1: wrap (C5w) */
     uint32_t heldout;            /* 1: the stream is the held-out documents (C2v) */
     uint32_t read_random;        /* 1: each cycle's windows of a source read in a random order (C6r) */
+    uint32_t cumulative;         /* 1: per-update counts from the cycle's cumulative quotas (C6c) */
 } or_corpus;
 
 typedef struct {
@@ -349,6 +434,9 @@ typedef struct {
     uint64_t *cyc_next;          /* [S] first window of the next cycle */
     uint64_t *perm_start;        /* [S+1] with read_random: start of each source's part of perm */
     uint32_t *perm;              /* [U·B] with read_random: read order within each source's cycle range */
+    uint64_t *taken;             /* [S] windows the current cycle takes from each source */
+    uint32_t *cum_A;             /* [(U+1)·S] with cumulative: windows of s taken before update u */
+    uint32_t *cum_src, *cum_k;   /* [U·B] with cumulative: slot table of every update */
 } or_plan;
 
 typedef struct { uint32_t group; uint32_t d; uint64_t key; } sort_item;
@@ -386,7 +474,7 @@ or_plan *or_plan_build(const or_corpus *cin, int *err)
     ALLOC(p->src_doc_start, S + 1); ALLOC(p->src_piece_start, S + 1); ALLOC(p->src_win_start, S + 1);
     ALLOC(p->n_upd, S); ALLOC(p->slot_src, c->B); ALLOC(p->slot_k, c->B);
     ALLOC(p->kept_docs, S); ALLOC(p->kept_tokens, S); ALLOC(p->held_docs, S); ALLOC(p->held_tokens, S);
-    ALLOC(p->cyc_start, S); ALLOC(p->cyc_next, S);
+    ALLOC(p->cyc_start, S); ALLOC(p->cyc_next, S); ALLOC(p->taken, S);
     ALLOC(gbase, S + 1);
 
     /* C1 + C2: hash every document, decide hold-out; a kept document is one
@@ -623,7 +711,8 @@ void or_plan_free(or_plan *p)
     free(p->win_real); free(p->win_learn); free(p->n_upd); free(p->slot_src); free(p->slot_k);
     free(p->kept_docs); free(p->kept_tokens); free(p->held_docs); free(p->held_tokens);
     free(p->perm); free(p->perm_start);
-    free(p->cyc_start); free(p->cyc_next);
+    free(p->cyc_start); free(p->cyc_next); free(p->taken);
+    free(p->cum_A); free(p->cum_src); free(p->cum_k);
     free(p);
 }
 
@@ -638,41 +727,71 @@ void or_plan_free(or_plan *p)
 
 int or_cycle(or_plan *p, uint32_t cyc, uint32_t updates_cfg)
 {
-    const uint32_t S = p->c.n_sources;
+    const uint32_t S = p->c.n_sources, B = p->c.B;
     if ((int64_t)cyc != p->cycle + 1) return OR_E_STATE;
-    uint64_t *start = calloc(S, sizeof(uint64_t));
-    if (!start) return OR_E_NOMEM;
-    for (uint32_t s = 0; s < S; s++) start[s] = (cyc == 0) ? 0 : p->cyc_next[s];
+    uint64_t *start = calloc(S, sizeof(uint64_t)), *take = calloc(S, sizeof(uint64_t));
+    uint64_t *rem = calloc(S, sizeof(uint64_t));
+    uint32_t *cA = NULL, *csrc = NULL, *ck = NULL, *cnt = NULL;
+    int rc = OR_OK;
+#define CYC_FAIL(code) do { rc = (code); goto out; } while (0)
+    if (!start || !take || !rem) CYC_FAIL(OR_E_NOMEM);
+    for (uint32_t s = 0; s < S; s++) {
+        start[s] = (cyc == 0) ? 0 : p->cyc_next[s];
+        rem[s] = p->src_win_start[s + 1] - p->src_win_start[s] - start[s];
+    }
     uint64_t U;
-    if (updates_cfg > 0) {
-        U = updates_cfg;
-    } else {
-        U = UINT64_MAX;
-        for (uint32_t s = 0; s < S; s++) {
-            if (p->n_upd[s] == 0) continue;
-            uint64_t M = p->src_win_start[s + 1] - p->src_win_start[s];
-            uint64_t u = (M - start[s]) / p->n_upd[s];
-            if (u < U) U = u;
-        }
-    }
-    int ok = (U > 0 && U <= 0xFFFFFFFFull);
-    for (uint32_t s = 0; ok && s < S; s++) {
-        uint64_t M = p->src_win_start[s + 1] - p->src_win_start[s];
-        if ((u128)U * p->n_upd[s] > (u128)(M - start[s])) ok = 0;
-    }
-    if (!ok) { free(start); return OR_E_EXHAUSTED; }   /* cycle state unchanged */
-    if (p->c.read_random) {
-        /* C6r: for each source, its U·n_s cycle windows ordered by (key64, i) */
+    if (p->c.cumulative) {
+        /* C6c: the cycle's schedule from its cumulative quotas */
         uint64_t total = 0;
-        for (uint32_t s = 0; s < S; s++) total += U * p->n_upd[s];
+        for (uint32_t s = 0; s < S; s++) total += rem[s];
+        uint64_t cap = total / B;                    /* every update takes B windows */
+        if (updates_cfg > cap || cap == 0) CYC_FAIL(OR_E_EXHAUSTED);
+        if (updates_cfg) cap = updates_cfg;
+        if (cap > 0xFFFFFFFFull) cap = 0xFFFFFFFFull;
+        cA = malloc(sizeof(uint32_t) * (cap + 1) * S);
+        if (!cA) CYC_FAIL(OR_E_NOMEM);
+        rc = or_cumulative(B, S, p->c.weight, rem, updates_cfg, cap, cA, &U);
+        if (rc) goto out;
+        if (U == 0 || (updates_cfg && U < updates_cfg)) CYC_FAIL(OR_E_EXHAUSTED);
+        for (uint32_t s = 0; s < S; s++) take[s] = cA[U * S + s];
+        csrc = malloc(sizeof(uint32_t) * U * B);
+        ck = malloc(sizeof(uint32_t) * U * B);
+        cnt = malloc(sizeof(uint32_t) * S);
+        if (!csrc || !ck || !cnt) CYC_FAIL(OR_E_NOMEM);
+        for (uint64_t u = 0; u < U; u++) {   /* each update's slots interleaved as in C6 */
+            for (uint32_t s = 0; s < S; s++) cnt[s] = cA[(u + 1) * S + s] - cA[u * S + s];
+            rc = or_slot_table(B, S, cnt, csrc + u * B, ck + u * B);
+            if (rc) goto out;
+        }
+    } else {
+        if (updates_cfg > 0) {
+            U = updates_cfg;
+        } else {
+            U = UINT64_MAX;
+            for (uint32_t s = 0; s < S; s++) {
+                if (p->n_upd[s] == 0) continue;
+                uint64_t u = rem[s] / p->n_upd[s];
+                if (u < U) U = u;
+            }
+        }
+        int ok = (U > 0 && U <= 0xFFFFFFFFull);
+        for (uint32_t s = 0; ok && s < S; s++)
+            if ((u128)U * p->n_upd[s] > (u128)rem[s]) ok = 0;
+        if (!ok) CYC_FAIL(OR_E_EXHAUSTED);   /* cycle state unchanged */
+        for (uint32_t s = 0; s < S; s++) take[s] = U * p->n_upd[s];
+    }
+    if (p->c.read_random) {
+        /* C6r: for each source, its cycle windows ordered by (key64, i) */
+        uint64_t total = 0;
+        for (uint32_t s = 0; s < S; s++) total += take[s];
         uint64_t *ps = calloc(S + 1, sizeof(uint64_t));
         uint32_t *perm = calloc(total ? total : 1, sizeof(uint32_t));
         sort_item *it = calloc(total ? total : 1, sizeof(sort_item));
-        if (!ps || !perm || !it) { free(ps); free(perm); free(it); free(start); return OR_E_NOMEM; }
+        if (!ps || !perm || !it) { free(ps); free(perm); free(it); CYC_FAIL(OR_E_NOMEM); }
         uint64_t e = 0;
         for (uint32_t s = 0; s < S; s++) {
             ps[s] = e;
-            for (uint64_t i = 0; i < U * p->n_upd[s]; i++, e++) {
+            for (uint64_t i = 0; i < take[s]; i++, e++) {
                 it[e].group = s;
                 it[e].d = (uint32_t)i;
                 it[e].key = or_window_key(p->c.seed, s, cyc, (uint32_t)i);
@@ -688,18 +807,33 @@ int or_cycle(or_plan *p, uint32_t cyc, uint32_t updates_cfg)
     p->U = (uint32_t)U;
     for (uint32_t s = 0; s < S; s++) {
         p->cyc_start[s] = start[s];
-        p->cyc_next[s] = start[s] + U * p->n_upd[s];
+        p->cyc_next[s] = start[s] + take[s];
+        p->taken[s] = take[s];
+    }
+    if (p->c.cumulative) {
+        free(p->cum_A); free(p->cum_src); free(p->cum_k);
+        p->cum_A = cA; p->cum_src = csrc; p->cum_k = ck;
+        cA = csrc = ck = NULL;
     }
     p->cycle = cyc;
-    free(start);
-    return OR_OK;
+out:
+#undef CYC_FAIL
+    free(start); free(take); free(rem); free(cA); free(csrc); free(ck); free(cnt);
+    return rc;
 }
 
 /* Global window index of slot j of update b of the current cycle. */
 uint64_t or_window_of(const or_plan *p, uint64_t b, uint32_t j)
 {
-    uint32_t s = p->slot_src[j];
-    uint64_t i = b * p->n_upd[s] + p->slot_k[j];   /* the source's i-th window of the cycle */
+    uint32_t s;
+    uint64_t i;                                    /* the source's i-th window of the cycle */
+    if (p->c.cumulative) {
+        s = p->cum_src[b * p->c.B + j];
+        i = (uint64_t)p->cum_A[b * p->c.n_sources + s] + p->cum_k[b * p->c.B + j];
+    } else {
+        s = p->slot_src[j];
+        i = b * p->n_upd[s] + p->slot_k[j];
+    }
     if (p->c.read_random) i = p->perm[p->perm_start[s] + i];
     return p->src_win_start[s] + p->cyc_start[s] + i;
 }
@@ -837,7 +971,7 @@ int or_plan_digest(const or_plan *p, uint8_t out[32])
     const uint32_t S = c->n_sources;
     if (p->cycle < 0) return OR_E_STATE;
     uint64_t bytes = 8 + 4 + 4 + 8 + 4 + 4 + (uint64_t)S * (8 + 4 + 4 + 4 + 8 + 8 + 8) + 4 + 4 + 8ull * S + 8 + 8
-                     + (c->read_random ? 4 : 0);
+                     + (c->read_random ? 4 : 0) + (c->cumulative ? 4 : 0);
     uint8_t *buf = (uint8_t *)malloc(bytes), *w = buf;
     if (!buf) return OR_E_NOMEM;
     /* the packing mode and the stream (training / held-out) are part of the plan */
@@ -845,6 +979,7 @@ int or_plan_digest(const or_plan *p, uint8_t out[32])
     *w++ = c->wrap ? 'W' : 'D';
     *w++ = c->heldout ? 'V' : '1';
     if (c->read_random) put(&w, 0x444E4152u, 4);  /* "RAND": windows read in a random order */
+    if (c->cumulative) put(&w, 0x554D5543u, 4);   /* "CUMU": per-update counts from cumulative quotas */
     put(&w, c->T, 4); put(&w, c->B, 4); put(&w, c->seed, 8); put(&w, S, 4); put(&w, c->pad_token, 4);
     for (uint32_t s = 0; s < S; s++) {
         put(&w, c->weight[s], 8); put(&w, c->bp[s], 4); put(&w, c->n_strata[s], 4);
@@ -889,9 +1024,18 @@ void or_plan_export(const or_plan *p, uint64_t *hash, uint8_t *keep, uint32_t *o
     checks[0] = p->order_check; checks[1] = p->hash_check;
 }
 
-uint32_t or_cycle_state(const or_plan *p, int64_t *cycle, uint64_t *start /*[S]*/)
+uint32_t or_cycle_state(const or_plan *p, int64_t *cycle, uint64_t *start /*[S]*/, uint64_t *taken /*[S]*/)
 {
     *cycle = p->cycle;
     memcpy(start, p->cyc_start, 8 * p->c.n_sources);
+    memcpy(taken, p->taken, 8 * p->c.n_sources);
     return p->U;
+}
+
+/* With the cumulative mixture: A [(U+1)·S] of the current cycle. */
+int or_cum_export(const or_plan *p, uint32_t *A)
+{
+    if (!p->c.cumulative || p->cycle < 0) return OR_E_STATE;
+    memcpy(A, p->cum_A, sizeof(uint32_t) * ((uint64_t)p->U + 1) * p->c.n_sources);
+    return OR_OK;
 }

@@ -48,6 +48,7 @@ class Corpus:
     wrap: bool = False          # packing: False = next-fit cut at document ends, True = wrap
     heldout: bool = False       # stream: False = training documents, True = held-out (validation)
     read_random: bool = False   # each cycle's windows of a source read in a random order
+    cumulative: bool = False    # per-update counts from the cycle's cumulative quotas
 
     @property
     def n_docs(self) -> int:
