@@ -78,6 +78,8 @@ def main():
     ap.add_argument("--wrap", action="store_true", help="wrap packing (PACK_FLAG_WRAP) instead of next-fit")
     ap.add_argument("--packed", action="store_true",
                     help="emit padding-free rows (pack_batch_packed, bucket 256) instead of padded windows and digests")
+    ap.add_argument("--cumulative", action="store_true",
+                    help="per-update window counts from each cycle's cumulative quotas (PACK_FLAG_CUMULATIVE)")
     ap.add_argument("--read-random", action="store_true",
                     help="each cycle's windows of a source read in a random order (PACK_FLAG_READ_RANDOM)")
     args = ap.parse_args()
@@ -98,7 +100,8 @@ def main():
     dp.load_library()
 
     t0 = time.time()
-    corpus = make_corpus(args.workload, args.scale).replace(wrap=args.wrap, read_random=args.read_random)
+    corpus = make_corpus(args.workload, args.scale).replace(wrap=args.wrap, read_random=args.read_random,
+                                                             cumulative=args.cumulative)
     log(f"corpus {args.workload} scale {args.scale}: {corpus.n_docs} docs, {corpus.n_tokens} tokens "
         f"({time.time() - t0:.1f}s)")
     tensors = dp.upload_corpus(corpus)
@@ -281,6 +284,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": WORKLOAD_TEXT[args.workload] + ("" if args.scale == 1.0 else f" (scale {args.scale})")
                    + (", wrap packing" if args.wrap else "") + (", random read order" if args.read_random else "")
+                   + (", per-update counts from cumulative quotas" if args.cumulative else "")
                    + (", padding-free rows" if args.packed else ""),
                    "docs": corpus.n_docs, "tokens": corpus.n_tokens, "T": T, "B": B, "updates": U,
                    "real_tokens_per_step": real, "positions_per_step": row_positions,

@@ -35,6 +35,7 @@ PACK_FLAG_TIMING = 1
 PACK_FLAG_WRAP = 2
 PACK_FLAG_HELDOUT = 4
 PACK_FLAG_READ_RANDOM = 8
+PACK_FLAG_CUMULATIVE = 16
 PHASES = ("validate", "hash", "keys", "sort", "merge", "pieces", "cut", "windows", "mixture",
           "cycle", "emit", "learned", "digest", "fingerprint")
 
@@ -46,6 +47,7 @@ INSPECT = {
     "win_first": (10, np.uint64), "src_win_start": (11, np.uint64), "win_real": (12, np.uint64),
     "win_learn": (13, np.uint64), "per_update": (14, np.uint32), "slot_src": (15, np.uint32),
     "slot_k": (16, np.uint32), "counts": (17, np.uint64),
+    "cum_taken": (18, np.uint32),
 }
 
 
@@ -230,7 +232,8 @@ class Packer:
         self.cfg = PackConfig(
             ABI_VERSION, (PACK_FLAG_TIMING if timing else 0) | (PACK_FLAG_WRAP if getattr(corpus, "wrap", False) else 0)
             | (PACK_FLAG_HELDOUT if getattr(corpus, "heldout", False) else 0)
-            | (PACK_FLAG_READ_RANDOM if getattr(corpus, "read_random", False) else 0),
+            | (PACK_FLAG_READ_RANDOM if getattr(corpus, "read_random", False) else 0)
+            | (PACK_FLAG_CUMULATIVE if getattr(corpus, "cumulative", False) else 0),
             d["tokens"].data_ptr() if d["tokens"].numel() else None, int(d["tokens"].numel()),
             d["offsets"].data_ptr(), int(d["source"].numel()),
             d["source"].data_ptr(), d["stratum"].data_ptr() if d.get("stratum") is not None else None,

@@ -162,7 +162,7 @@ struct pack_ctx {
     std::vector<uint32_t> n_upd;
     int64_t cycle = -1;
     uint32_t U = 0;
-    std::vector<uint64_t> cyc_start, cyc_next;
+    std::vector<uint64_t> cyc_start, cyc_next, taken;
     std::string err;
 };
 
@@ -234,8 +234,14 @@ size_t carve(pack_ctx& c, char* base) {
     p.wval[0] = k.take<uint32_t>(WR);
     p.wval[1] = k.take<uint32_t>(WR);
     p.wgroup = k.take<uint32_t>(WR);
+    const uint64_t CU = p.cumulative ? P / B : 0;  // most updates of a cycle: each takes B of ≤ P windows
+    p.cum_A = k.take<uint32_t>(p.cumulative ? (CU + 1) * S : 0);
+    p.cum_rem = k.take<uint64_t>(p.cumulative ? S : 0);
+    p.cum_out = k.take<uint64_t>(p.cumulative ? S + 1 : 0);
+    p.cslot_src = k.take<uint32_t>(CU * B);
+    p.cslot_i = k.take<uint32_t>(CU * B);
     c.nstart = k.take<uint32_t>(S + 1);
-    c.dig_cap = 128 + 48 * S;
+    c.dig_cap = 128 + 64 * S;  // digest message: 64 + 52·S bytes at most
     c.dig_buf = k.take<uint8_t>(c.dig_cap + 32);
     return k.off + ALIGN;
 }
@@ -250,7 +256,9 @@ void h2d(T* dst, const T* src, uint64_t count, hipStream_t st) {
 }
 
 // pinned staging: bytes for the largest set of copies between two synchronizations
-size_t pin_bytes_for(uint32_t S) { return 64ull * S + 2048; }
+// largest use: pack_cycle's cycle starts, read-order starts, sums, digest
+// message (≤ 64 + 52·S bytes) and digest, each 64-byte aligned
+size_t pin_bytes_for(uint32_t S) { return 128ull * S + 4096; }
 
 template <typename T>
 T* pin_take(pack_ctx& c, uint64_t count) {
@@ -285,7 +293,8 @@ void sync_staged(pack_ctx& c) {
 
 void check_config(const pack_config* cfg) {
     auto bad = [](const char* m) { throw InvalError{m}; };
-    if (cfg->flags & ~(PACK_FLAG_TIMING | PACK_FLAG_WRAP | PACK_FLAG_HELDOUT | PACK_FLAG_READ_RANDOM))
+    if (cfg->flags &
+        ~(PACK_FLAG_TIMING | PACK_FLAG_WRAP | PACK_FLAG_HELDOUT | PACK_FLAG_READ_RANDOM | PACK_FLAG_CUMULATIVE))
         bad("unknown flags");
     if (cfg->n_docs < 1 || cfg->n_docs >= (1ull << 31)) bad("n_docs must be in [1, 2^31)");
     if (!cfg->doc_offsets || !cfg->doc_source) bad("doc_offsets and doc_source are required");
@@ -308,6 +317,12 @@ void check_config(const pack_config* cfg) {
     unsigned __int128 W = 0;
     for (uint32_t s = 0; s < cfg->n_sources; ++s) W += cfg->share_weight[s];
     if (W == 0 || (W >> 64) != 0) bad("share weights must sum to [1, 2^64)");
+    if (cfg->flags & PACK_FLAG_CUMULATIVE) {
+        if (cfg->n_sources > 1024) bad("the cumulative mixture takes at most 1024 sources");
+        const uint64_t cap = cfg->n_docs + cfg->n_tokens / T;  // windows ≤ pieces ≤ cap
+        if ((cap / B + 1) * cfg->n_sources > (1ull << 28))
+            bad("the cumulative mixture's table (updates x sources) exceeds 2^28 entries");
+    }
 }
 
 int fail_hip(pack_ctx* c, const dp::HipError& e) {
@@ -507,6 +522,7 @@ int pack_init(const pack_config* cfg, pack_ctx** out) {
         p.wrap = (cfg->flags & PACK_FLAG_WRAP) ? 1u : 0u;
         p.heldout = (cfg->flags & PACK_FLAG_HELDOUT) ? 1u : 0u;
         p.read_random = (cfg->flags & PACK_FLAG_READ_RANDOM) ? 1u : 0u;
+        p.cumulative = (cfg->flags & PACK_FLAG_CUMULATIVE) ? 1u : 0u;
         p.cap_pieces = cfg->n_docs + cfg->n_tokens / cfg->window_tokens;
         if (p.cap_pieces >= 0xFFFFFFFFull) throw InvalError{"too many pieces for 32-bit piece indices"};
 
@@ -541,6 +557,7 @@ int pack_init(const pack_config* cfg, pack_ctx** out) {
         build_plan(*c);
         c->cyc_start.assign(S, 0);
         c->cyc_next.assign(S, 0);
+        c->taken.assign(S, 0);
         *out = c;
         return PACK_OK;
     } catch (const InvalError& e) {
@@ -567,43 +584,77 @@ int pack_cycle(pack_ctx* c, uint32_t cycle, pack_cycle_info* info) {
         return PACK_E_STATE;
     }
     try {
-        std::vector<uint64_t> start(S);
-        for (uint32_t s = 0; s < S; ++s) start[s] = cycle == 0 ? 0 : c->cyc_next[s];
+        std::vector<uint64_t> start(S), rem(S), taken(S);
+        for (uint32_t s = 0; s < S; ++s) {
+            start[s] = cycle == 0 ? 0 : c->cyc_next[s];
+            rem[s] = c->src_win_start[s + 1] - c->src_win_start[s] - start[s];
+        }
+        dp::Plan& p = c->p;
         uint64_t U = c->cfg.updates_per_cycle;
-        if (U == 0) {
-            U = ~0ull;
-            for (uint32_t s = 0; s < S; ++s) {
-                if (c->n_upd[s] == 0) continue;
-                const uint64_t M = c->src_win_start[s + 1] - c->src_win_start[s];
-                const uint64_t u = (M - start[s]) / c->n_upd[s];
-                if (u < U) U = u;
+        const uint64_t* h_sums = nullptr;
+        c->pin_off = 0;
+        if (p.cumulative) {
+            // the cycle's schedule from its cumulative quotas, on the device
+            uint64_t total = 0;
+            for (uint32_t s = 0; s < S; ++s) total += rem[s];
+            const uint64_t most = total / p.B;  // every update takes B windows
+            if (most == 0 || U > most) {
+                c->err = "a source cannot supply the cycle's windows";
+                return PACK_E_EXHAUSTED;
             }
-        }
-        bool ok = U > 0 && U <= 0xFFFFFFFFull;
-        for (uint32_t s = 0; ok && s < S; ++s) {
-            const uint64_t M = c->src_win_start[s + 1] - c->src_win_start[s];
-            if ((unsigned __int128)U * c->n_upd[s] > (unsigned __int128)(M - start[s])) ok = false;
-        }
-        if (!ok) {
-            c->err = "a source cannot supply the cycle's windows";
-            return PACK_E_EXHAUSTED;
+            const uint64_t cap = U ? U : most;
+            if (cap > p.cap_pieces / p.B) throw InvalError{"internal: cumulative table bound exceeded"};
+            c->timer.begin(PACK_PHASE_CYCLE, c->st);
+            h2d_staged(*c, p.cum_rem, rem.data(), S);
+            dp::launch_cumulative(p, c->W, U, cap, c->st);
+            c->timer.end(c->st);
+            const uint64_t* h_out = d2h_staged(*c, p.cum_out, S + 1);
+            const uint32_t* h_err = d2h_staged(*c, p.err, 1);
+            sync_staged(*c);
+            if (*h_err & dp::ERR_INTERNAL) throw InvalError{"internal: cumulative schedule"};
+            const uint64_t got = h_out[S];
+            for (uint32_t s = 0; s < S; ++s) taken[s] = h_out[s];
+            c->pin_off = 0;
+            if (got == 0 || (U && got < U)) {
+                c->err = "a source cannot supply the cycle's windows";
+                return PACK_E_EXHAUSTED;
+            }
+            U = got;
+            if (U > 0xFFFFFFFFull) throw InvalError{"internal: updates per cycle"};
+        } else {
+            if (U == 0) {
+                U = ~0ull;
+                for (uint32_t s = 0; s < S; ++s) {
+                    if (c->n_upd[s] == 0) continue;
+                    const uint64_t u = rem[s] / c->n_upd[s];
+                    if (u < U) U = u;
+                }
+            }
+            bool ok = U > 0 && U <= 0xFFFFFFFFull;
+            for (uint32_t s = 0; ok && s < S; ++s)
+                if ((unsigned __int128)U * c->n_upd[s] > (unsigned __int128)rem[s]) ok = false;
+            if (!ok) {
+                c->err = "a source cannot supply the cycle's windows";
+                return PACK_E_EXHAUSTED;
+            }
+            for (uint32_t s = 0; s < S; ++s) taken[s] = U * c->n_upd[s];
         }
         c->U = (uint32_t)U;
         c->cyc_start = start;
-        for (uint32_t s = 0; s < S; ++s) c->cyc_next[s] = start[s] + U * c->n_upd[s];
+        c->taken = taken;
+        for (uint32_t s = 0; s < S; ++s) c->cyc_next[s] = start[s] + taken[s];
         c->cycle = cycle;
-        dp::Plan& p = c->p;
         c->timer.begin(PACK_PHASE_CYCLE, c->st);
-        c->pin_off = 0;
         h2d_staged(*c, p.cyc_start, c->cyc_start.data(), S);
-        if (p.read_random) {  // each source's U·n_s cycle windows in their random read order
+        if (p.cumulative) dp::launch_cum_slots(p, c->U, c->st);
+        if (p.read_random) {  // each source's cycle windows in their random read order
             std::vector<uint64_t> ps(S + 1, 0);
-            for (uint32_t s = 0; s < S; ++s) ps[s + 1] = ps[s] + (uint64_t)c->U * c->n_upd[s];
+            for (uint32_t s = 0; s < S; ++s) ps[s + 1] = ps[s] + taken[s];
             h2d_staged(*c, p.perm_start, ps.data(), S + 1);
             dp::launch_read_order(p, cycle, ps[S], c->st);
         }
         dp::launch_cycle_sums(p, c->U, c->st);
-        const uint64_t* h_sums = d2h_staged(*c, p.cyc_sums, 2);
+        h_sums = d2h_staged(*c, p.cyc_sums, 2);
 
         // plan digest: SHA-256 of a little-endian description of the recipe,
         // stream sizes, cycle start and two order-free sums over the plan
@@ -612,6 +663,7 @@ int pack_cycle(pack_ctx* c, uint32_t cycle, pack_cycle_info* info) {
         const char magic[8] = {'D', 'P', 'A', 'C', 'K', 'P', p.wrap ? 'W' : 'D', p.heldout ? 'V' : '1'};
         msg.insert(msg.end(), magic, magic + 8);
         if (p.read_random) put(msg, 0x444E4152u, 4);  // "RAND": windows read in a random order
+        if (p.cumulative) put(msg, 0x554D5543u, 4);   // "CUMU": per-update counts from cumulative quotas
         put(msg, p.T, 4);
         put(msg, p.B, 4);
         put(msg, p.seed, 8);
@@ -651,10 +703,9 @@ int pack_cycle(pack_ctx* c, uint32_t cycle, pack_cycle_info* info) {
             std::memcpy(info->plan_digest, digest, 32);
             for (uint32_t s = 0; s < S; ++s) {
                 const uint64_t M = c->src_win_start[s + 1] - c->src_win_start[s];
-                const uint64_t taken = (uint64_t)c->U * c->n_upd[s];
                 if (info->windows_start) info->windows_start[s] = c->cyc_start[s];
-                if (info->windows_taken) info->windows_taken[s] = taken;
-                if (info->windows_remaining) info->windows_remaining[s] = M - c->cyc_start[s] - taken;
+                if (info->windows_taken) info->windows_taken[s] = c->taken[s];
+                if (info->windows_remaining) info->windows_remaining[s] = M - c->cyc_start[s] - c->taken[s];
                 if (info->kept_docs) info->kept_docs[s] = c->stats[0 * S + s];
                 if (info->kept_tokens) info->kept_tokens[s] = c->stats[1 * S + s];
                 if (info->held_docs) info->held_docs[s] = c->stats[2 * S + s];
@@ -835,6 +886,15 @@ int pack_inspect(const pack_ctx* cc, uint32_t what, void* host_dst, uint64_t cap
         case PACK_INSPECT_SLOT_SRC: src = p.slot_src; count = p.B; width = out_width = 4; break;
         case PACK_INSPECT_SLOT_K: src = p.slot_k; count = p.B; width = out_width = 4; break;
         case PACK_INSPECT_COUNTS: count = 3; width = out_width = 8; break;
+        case PACK_INSPECT_CUM_TAKEN:
+            if (!p.cumulative || c->cycle < 0) {
+                c->err = "no cumulative schedule: the context has no PACK_FLAG_CUMULATIVE or no cycle yet";
+                return PACK_E_STATE;
+            }
+            src = p.cum_A;
+            count = ((uint64_t)c->U + 1) * p.S;
+            width = out_width = 4;
+            break;
         default: c->err = "unknown inspect code"; return PACK_E_INVAL;
     }
     const uint64_t bytes = count * out_width;

@@ -86,6 +86,7 @@ struct Plan {
     uint32_t wrap;                // 1: wrap packing (cut every T tokens), 0: next-fit
     uint32_t heldout;             // 1: the stream is the held-out documents (validation)
     uint32_t read_random;         // 1: each cycle's windows of a source are read in a random order
+    uint32_t cumulative;          // 1: per-update counts from the cycle's cumulative quotas
 
     // recipe on device
     uint32_t* gbase;              // [S+1] first group of each source
@@ -145,6 +146,13 @@ struct Plan {
     uint64_t* wkey[2];            // sort workspace [cap windows]
     uint32_t* wval[2];
     uint32_t* wgroup;
+    // cumulative mixture (cumulative): windows of each source taken before each
+    // update, and every update's slot table as (source, cycle window index)
+    uint32_t* cum_A;              // [(U_cap+1)·S]
+    uint64_t* cum_rem;            // [S] windows each source has left at the cycle start
+    uint64_t* cum_out;            // [S+1] windows taken per source, then U
+    uint32_t* cslot_src;          // [U_cap·B]
+    uint32_t* cslot_i;            // [U_cap·B]
 
     // sizes known after the corresponding step (host copies)
     uint64_t n_kept, n_pieces, n_windows;
@@ -153,12 +161,21 @@ struct Plan {
 
 // Global window index of slot j of update b of the current cycle: source s
 // = slot_src[j] contributes its (slot_k[j])-th window of the update, i.e. its
-// i-th window of the cycle, i = b·n_s + slot_k[j]: window cyc_start[s] + i of
-// its stream, or cyc_start[s] + perm[perm_start[s] + i] with the random read
-// order.
+// i-th window of the cycle, i = b·n_s + slot_k[j] (with the cumulative
+// mixture, s and i come from update b's own slot table): window
+// cyc_start[s] + i of its stream, or cyc_start[s] + perm[perm_start[s] + i]
+// with the random read order.
 __device__ inline uint64_t window_of(const Plan& p, uint64_t b, uint32_t j) {
-    const uint32_t s = p.slot_src[j];
-    uint64_t i = b * p.n_upd[s] + p.slot_k[j];  // the source's i-th window of the cycle
+    uint32_t s;
+    uint64_t i;  // the source's i-th window of the cycle
+    if (p.cumulative) {
+        const uint64_t x = b * p.B + j;
+        s = p.cslot_src[x];
+        i = p.cslot_i[x];
+    } else {
+        s = p.slot_src[j];
+        i = b * p.n_upd[s] + p.slot_k[j];
+    }
     if (p.read_random) i = p.perm[p.perm_start[s] + i];
     return p.src_win_start[s] + p.cyc_start[s] + i;
 }
@@ -238,6 +255,10 @@ void launch_fill_u32(uint32_t* a, uint64_t n, uint32_t v, hipStream_t st);
 uint64_t sort_hist_words(uint64_t n_docs);
 void launch_checks(Plan& p, hipStream_t st);          // order / hash checks
 void launch_cycle_sums(Plan& p, uint32_t U, hipStream_t st);
+// cumulative mixture of a cycle: the schedule (cum_A, cum_out), then, once the
+// host has accepted U, every update's slot table
+void launch_cumulative(Plan& p, uint64_t W, uint64_t u_cfg, uint64_t cap, hipStream_t st);
+void launch_cum_slots(Plan& p, uint32_t U, hipStream_t st);
 
 struct EmitArgs {
     uint32_t* tok; int32_t* pos; int32_t* doc; uint8_t* mask;

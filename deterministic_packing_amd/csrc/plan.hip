@@ -364,11 +364,11 @@ __global__ __launch_bounds__(1024) void k_apportion(Plan p, uint64_t W, uint32_t
 // Slot order inside an update: items (s, k), k < n_s, by (2k+1)/(2n_s), ties
 // to the lower source (Sainte-Laguë order), so the sources are spread over
 // the update.  Position of (s, k) = number of items ordered before it,
-// counted in closed form per source.
-__global__ __launch_bounds__(256) void k_slots(Plan p, const uint32_t* nstart) {
-    const uint32_t u = blockIdx.x * blockDim.x + threadIdx.x;
-    if (u >= p.B) return;
-    uint32_t lo = 0, hi = p.S;  // source s with nstart[s] ≤ u < nstart[s+1]
+// counted in closed form per source.  Item u of the update (sources in
+// order, nstart = exclusive prefix of the counts) → (s, k, position).
+__device__ inline uint64_t slot_item(const uint32_t* n, const uint32_t* nstart, uint32_t S, uint32_t u,
+                                     uint32_t* s_out, uint32_t* k_out) {
+    uint32_t lo = 0, hi = S;  // source s with nstart[s] ≤ u < nstart[s+1]
     while (hi - lo > 1) {
         const uint32_t mid = (lo + hi) >> 1;
         if (nstart[mid] <= u) lo = mid;
@@ -377,10 +377,10 @@ __global__ __launch_bounds__(256) void k_slots(Plan p, const uint32_t* nstart) {
     uint32_t s = lo;
     while (nstart[s + 1] <= u) ++s;  // skip sources with n = 0
     const uint32_t k = u - nstart[s];
-    const uint64_t ns = p.n_upd[s];
+    const uint64_t ns = n[s];
     uint64_t pos = k;
-    for (uint32_t s2 = 0; s2 < p.S; ++s2) {
-        const uint64_t n2 = p.n_upd[s2];
+    for (uint32_t s2 = 0; s2 < S; ++s2) {
+        const uint64_t n2 = n[s2];
         if (s2 == s || n2 == 0) continue;
         const uint64_t X = (2ull * k + 1) * n2;   // compare (2k'+1)·n_s against X
         const uint64_t F = (s2 < s) ? X / ns : (X - 1) / ns;  // largest admissible odd bound
@@ -388,11 +388,189 @@ __global__ __launch_bounds__(256) void k_slots(Plan p, const uint32_t* nstart) {
         if (c > n2) c = n2;
         pos += c;
     }
+    *s_out = s;
+    *k_out = k;
+    return pos;
+}
+
+__global__ __launch_bounds__(256) void k_slots(Plan p, const uint32_t* nstart) {
+    const uint32_t u = blockIdx.x * blockDim.x + threadIdx.x;
+    if (u >= p.B) return;
+    uint32_t s, k;
+    const uint64_t pos = slot_item(p.n_upd, nstart, p.S, u, &s, &k);
     if (pos < p.B) {
         p.slot_src[pos] = s;
         p.slot_k[pos] = k;
     } else {
         atomicOr(p.err, ERR_INTERNAL);
+    }
+}
+
+// ------------------------------------------------------------------ cumulative mixture
+// One workgroup, thread s = source s (S ≤ CUM_MAX_S), one update after the
+// other.  After update u, source s has taken A_s with floor(q) ≤ A_s ≤ ceil(q),
+// q = (u+1)·B·w_s/W, kept as q = fl + rm/W with B·w_s = qB·W + rB added per
+// update.  The windows due by update u are those up to fl (fl − A_s of them,
+// all taken); the only other released window of s is window fl+1 when
+// rm ≠ 0 and A_s ≤ fl, due by update δ = ceil((fl+1)·W/(B·w_s)) − 1, which
+// depends on fl alone: u + 1 when B·w_s ≥ W, else u + ceil((W − rm)/(B·w_s))
+// evaluated when fl last changed.  The B − Σ(fl − A_s)⁺ remaining seats go
+// to the candidates with the smallest (δ, s) (earliest deadline first).  The
+// schedule stops before the first update after which a source would exceed
+// the windows it has left, or after cap updates.  ONE_WAVE: S ≤ 64, one
+// wavefront, exchanges by cross-lane reads instead of LDS and barriers.
+constexpr uint32_t CUM_MAX_S = 1024;
+
+template <bool ONE_WAVE>
+__global__ __launch_bounds__(ONE_WAVE ? WAVE : CUM_MAX_S) void k_cumulative(Plan p, uint64_t W, uint64_t cap) {
+    __shared__ uint64_t key[ONE_WAVE ? 1 : CUM_MAX_S];
+    __shared__ uint64_t part[3][ONE_WAVE ? 1 : CUM_MAX_S / WAVE];
+    const uint32_t s = threadIdx.x, nw = blockDim.x / WAVE;
+    const bool on = s < p.S;
+    const uint64_t w = on ? p.weight[s] : 0;
+    const uint64_t bw_hi = __umul64hi((uint64_t)p.B, w), bw = (uint64_t)p.B * w;
+    uint64_t rB = 0;
+    const uint64_t qB = w ? div128(bw_hi, bw, W, &rB) : 0;  // bw_hi < W since B·w < 2^20·W
+    const bool step_ge_W = bw_hi != 0 || bw >= W;           // fl grows every update
+    const uint64_t rem = on ? p.cum_rem[s] : ~0ull;
+    uint64_t fl = 0, rm = 0, A = 0, U = 0, due = 0;
+    bool bad = false;
+    if (on) p.cum_A[s] = 0;
+    // ONE_WAVE: Σ_s (fl − A)⁺ = Σ qB + #crossed − #ahead + #(qB = 0, not crossed, ahead), where
+    // ahead = (A = fl + 1) before the update: every term is a ballot count
+    const uint64_t QB = ONE_WAVE ? wave_sum_u64(qB) : 0;
+    for (uint64_t u = 0; u < cap; ++u) {
+        bool moved = false, crossed = false;
+        const bool ahead = A > fl;
+        if (w) {  // q ← q + B·w_s/W
+            uint64_t r2 = rm + rB;
+            const bool carry = r2 < rm;
+            fl += qB;
+            moved = qB != 0;
+            if (carry || r2 >= W) {
+                r2 -= W;
+                fl += 1;
+                moved = true;
+                crossed = true;
+            }
+            rm = r2;
+        }
+        const uint64_t m = fl > A ? fl - A : 0;
+        const bool cand = w != 0 && rm != 0 && A <= fl;
+        if (w && (moved || u == 0)) {  // the formula holds for rm = 0 too: δ of window fl+1
+            if (step_ge_W) {
+                due = u + 1;
+            } else {
+                const uint64_t gap = W - rm;
+                due = u + gap / bw + (gap % bw ? 1 : 0);
+            }
+        }
+        const uint64_t k = cand ? due : ~0ull;
+        uint64_t sm, nc;
+        uint64_t lanes = 0;
+        if (ONE_WAVE) {
+            lanes = __ballot(cand);
+            sm = QB + (uint64_t)__popcll(__ballot(crossed)) - (uint64_t)__popcll(__ballot(ahead)) +
+                 (uint64_t)__popcll(__ballot(qB == 0 && !crossed && ahead));
+            nc = (uint64_t)__popcll(lanes);
+        } else {
+            key[s] = k;
+            const uint64_t v0 = wave_sum_u64(m), v1 = wave_sum_u64(cand ? 1 : 0);
+            if ((s & (WAVE - 1)) == 0) {
+                part[0][s / WAVE] = v0;
+                part[1][s / WAVE] = v1;
+            }
+            __syncthreads();
+            sm = 0;
+            nc = 0;
+            for (uint32_t i = 0; i < nw; ++i) {
+                sm += part[0][i];
+                nc += part[1][i];
+            }
+        }
+        if (sm > p.B || nc < p.B - sm) {  // the schedule's guarantee failed
+            bad = true;
+            break;
+        }
+        const uint64_t R = p.B - sm;
+        uint64_t rank = 0;
+        if (ONE_WAVE) {
+            const uint32_t klo = (uint32_t)k, khi = (uint32_t)(k >> 32);
+            if (lanes) {
+                const int f = __builtin_ctzll(lanes);  // every candidate due in the same update: by lane
+                const uint64_t d0 = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)khi, f) << 32) |
+                                    (uint32_t)__builtin_amdgcn_readlane((int)klo, f);
+                if (__ballot(cand && k != d0) == 0) {
+                    rank = (uint64_t)__popcll(lanes & ((1ull << s) - 1ull));
+                } else {
+                    for (uint64_t rest = lanes; rest; rest &= rest - 1) {  // candidate lanes only
+                        const int t = __builtin_ctzll(rest);
+                        const uint64_t kt = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)khi, t) << 32) |
+                                            (uint32_t)__builtin_amdgcn_readlane((int)klo, t);
+                        rank += (kt < k || (kt == k && (uint32_t)t < s)) ? 1 : 0;
+                    }
+                }
+            }
+        } else if (cand) {
+            for (uint32_t t = 0; t < p.S; ++t) rank += (key[t] < k || (key[t] == k && t < s)) ? 1 : 0;
+        }
+        const uint64_t An = A + m + (cand && rank < R ? 1 : 0);
+        uint64_t ov;
+        if (ONE_WAVE) {
+            ov = __ballot(An > rem);
+        } else {
+            const uint64_t over = wave_sum_u64(An > rem ? 1 : 0);
+            __syncthreads();  // everyone has read part[] and key[]
+            if ((s & (WAVE - 1)) == 0) part[2][s / WAVE] = over;
+            __syncthreads();
+            ov = 0;
+            for (uint32_t i = 0; i < nw; ++i) ov += part[2][i];
+        }
+        if (ov) break;
+        A = An;
+        U = u + 1;
+        if (on) p.cum_A[(u + 1) * p.S + s] = (uint32_t)A;
+    }
+    if (on) p.cum_out[s] = A;
+    if (s == 0) p.cum_out[p.S] = U;
+    if (bad && s == 0) atomicOr(p.err, ERR_INTERNAL);
+}
+
+// Slot table of every update of the cycle: block u, counts
+// A(u+1) − A(u) in Sainte-Laguë order; cslot_i = A_s(u) + k.
+__global__ __launch_bounds__(256) void k_cum_slots(Plan p) {
+    extern __shared__ uint32_t csh[];  // n[S], nstart[S+1], base[S]
+    const uint32_t S = p.S;
+    uint32_t* n = csh;
+    uint32_t* ns = csh + S;
+    uint32_t* base = csh + 2 * S + 1;
+    const uint64_t u = blockIdx.x;
+    for (uint32_t s = threadIdx.x; s < S; s += blockDim.x) {
+        const uint32_t a0 = p.cum_A[u * S + s], a1 = p.cum_A[(u + 1) * S + s];
+        n[s] = a1 - a0;
+        base[s] = a0;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t run = 0;
+        for (uint32_t s = 0; s < S; ++s) {
+            ns[s] = run;
+            run += n[s];
+        }
+        ns[S] = run;
+        if (run != p.B) atomicOr(p.err, ERR_INTERNAL);
+    }
+    __syncthreads();
+    if (ns[S] != p.B) return;
+    for (uint32_t t = threadIdx.x; t < p.B; t += blockDim.x) {
+        uint32_t s, k;
+        const uint64_t pos = slot_item(n, ns, S, t, &s, &k);
+        if (pos < p.B) {
+            p.cslot_src[u * p.B + pos] = s;
+            p.cslot_i[u * p.B + pos] = base[s] + k;
+        } else {
+            atomicOr(p.err, ERR_INTERNAL);
+        }
     }
 }
 
@@ -505,6 +683,22 @@ void launch_windows(Plan& p, hipStream_t st) {
 void launch_mixture_w(Plan& p, uint64_t W, uint32_t* nstart, hipStream_t st) {
     hipLaunchKernelGGL(k_apportion, dim3(1), dim3(1024), (size_t)p.S * 12, st, p, W, nstart);
     hipLaunchKernelGGL(k_slots, dim3(blocks_for(p.B)), dim3(256), 0, st, p, (const uint32_t*)nstart);
+    DP_HIP(hipGetLastError());
+}
+
+void launch_cumulative(Plan& p, uint64_t W, uint64_t u_cfg, uint64_t cap, hipStream_t st) {
+    (void)u_cfg;  // cap already holds it when it is set
+    if (p.S <= WAVE) {
+        hipLaunchKernelGGL(k_cumulative<true>, dim3(1), dim3(WAVE), 0, st, p, W, cap);
+    } else {
+        const uint32_t threads = ((p.S + WAVE - 1) / WAVE) * WAVE;
+        hipLaunchKernelGGL(k_cumulative<false>, dim3(1), dim3(threads), 0, st, p, W, cap);
+    }
+    DP_HIP(hipGetLastError());
+}
+
+void launch_cum_slots(Plan& p, uint32_t U, hipStream_t st) {
+    if (U) hipLaunchKernelGGL(k_cum_slots, dim3(U), dim3(256), (size_t)(3 * p.S + 1) * 4, st, p);
     DP_HIP(hipGetLastError());
 }
 

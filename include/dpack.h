@@ -85,6 +85,23 @@ typedef struct pack_ctx pack_ctx;
  * key = seed), ties by i, and update b's k-th window of s is the one of rank
  * b·n_s + k.  Per-update counts, cycle ranges and sums are unchanged. */
 #define PACK_FLAG_READ_RANDOM 8u
+/* pack_config.flags: per-update window counts from the cycle's cumulative
+ * quotas instead of one fixed apportionment.  NeuronSpark-Trainer README,
+ * Concepts: every update holds each source within two samples of its recipe
+ * share, and every token is trained (max_epochs 1).  Reading taken: after u
+ * updates of a cycle, source s has taken A_s(u) windows, floor(u·B·w_s/W) ≤
+ * A_s(u) ≤ ceil(u·B·w_s/W), never fewer than after u−1; so every update holds
+ * each source within two windows of B·w_s/W and a share below one window per
+ * update still gets its windows over the cycle.  Source s's j-th window of
+ * the cycle is released in update floor((j−1)·W/(B·w_s)) and due by update
+ * ceil(j·W/(B·w_s)) − 1; each update takes the B released windows with the
+ * earliest due updates, ties to the lower source (earliest deadline first,
+ * which meets every deadline: Balinski and Young's quota method shows a
+ * schedule exists).  Each update's slots are in the Sainte-Laguë order of its
+ * own counts.  With updates_per_cycle = 0 the cycle is the longest prefix of
+ * the schedule no source runs out in.  At most 1024 sources; the table of
+ * (updates x sources) is bounded by 2^28 entries at init. */
+#define PACK_FLAG_CUMULATIVE 16u
 
 /* Kernel phases timed under PACK_FLAG_TIMING. */
 enum {
@@ -119,7 +136,7 @@ typedef struct pack_timings {
  * [64, 2^20]; 1 ≤ B ≤ 2^20; world ≥ 1 divides B; rank < world. */
 typedef struct pack_config {
     uint32_t abi_version;          /* DPACK_ABI_VERSION */
-    uint32_t flags;                /* 0 or an or of PACK_FLAG_TIMING, _WRAP, _HELDOUT, _READ_RANDOM */
+    uint32_t flags;                /* 0 or an or of PACK_FLAG_TIMING, _WRAP, _HELDOUT, _READ_RANDOM, _CUMULATIVE */
     const uint32_t *tokens;        /* device [n_tokens] token ids */
     uint64_t n_tokens;
     const uint64_t *doc_offsets;   /* device [n_docs+1]: document d is tokens[off[d], off[d+1]) */
@@ -161,19 +178,23 @@ typedef struct pack_cycle_info {
     uint64_t positions;            /* U·B·T */
     uint8_t plan_digest[32];       /* SHA-256 identifying recipe, stream sizes, cycle start and order */
     uint64_t *windows_start;       /* first window of the cycle in each source's stream */
-    uint64_t *windows_taken;       /* U·n_s */
+    uint64_t *windows_taken;       /* U·n_s (with PACK_FLAG_CUMULATIVE: A_s(U)) */
     uint64_t *windows_remaining;   /* windows left after the cycle */
     uint64_t *kept_docs, *kept_tokens, *held_docs, *held_tokens;
-    uint32_t *per_update;          /* n_s: windows of each source in every update */
+    uint32_t *per_update;          /* n_s: windows of each source in every update (the fixed
+                                    * apportionment; with PACK_FLAG_CUMULATIVE the counts vary per
+                                    * update: PACK_INSPECT_CUM_TAKEN) */
 } pack_cycle_info;
 
 /* pack_cycle — plan cycle `cycle` (must be 0, then 1, 2, …): U updates, each
  * of B windows of which n_s come from source s, taking the next U·n_s windows
  * of each source's stream.  U = updates_per_cycle, or when that is 0 the most
- * every source with n_s > 0 supports.  Synchronous.  info may be NULL.
+ * every source with n_s > 0 supports.  With PACK_FLAG_CUMULATIVE update u
+ * takes A_s(u+1) − A_s(u) windows of source s (see the flag) and the cycle
+ * A_s(U).  Synchronous.  info may be NULL.
  * Errors: PACK_E_STATE (out of order), PACK_E_EXHAUSTED (some source cannot
- * supply U·n_s windows, or U would be 0: an error, never a second pass; the
- * cycle state is unchanged), PACK_E_HIP. */
+ * supply its windows of the cycle, or U would be 0: an error, never a second
+ * pass; the cycle state is unchanged), PACK_E_HIP. */
 int pack_cycle(pack_ctx *ctx, uint32_t cycle, pack_cycle_info *info);
 
 /* Outputs of pack_batch: device buffers owned by the caller, each laid out
@@ -246,6 +267,9 @@ enum {
     PACK_INSPECT_SLOT_SRC = 15,     /* uint32 [B] */
     PACK_INSPECT_SLOT_K = 16,       /* uint32 [B] */
     PACK_INSPECT_COUNTS = 17,       /* uint64 [3]: n_kept, n_pieces, n_windows */
+    PACK_INSPECT_CUM_TAKEN = 18,    /* uint32 [(U+1)·n_sources]: with PACK_FLAG_CUMULATIVE, windows of
+                                     * each source taken before each update of the current cycle
+                                     * (row U: the cycle's totals); PACK_E_STATE otherwise */
 };
 
 /* pack_inspect — copy plan array `what` to host memory (synchronous).

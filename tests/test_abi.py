@@ -66,7 +66,7 @@ def _cfg(**kw):
     ("window_tokens", 100, dp.PACK_E_INVAL),
     ("global_batch", 0, dp.PACK_E_INVAL),
     ("n_docs", 0, dp.PACK_E_INVAL),
-    ("flags", 16, dp.PACK_E_INVAL),
+    ("flags", 32, dp.PACK_E_INVAL),
     ("n_sources", 0, dp.PACK_E_INVAL),
 ])
 def test_init_rejects_bad_config_on_host(lib, field, value, code):
@@ -86,6 +86,24 @@ def test_init_rejects_zero_weights_and_bad_holdout(lib):
         cfg.share_weight, cfg.holdout_bp = wa.ctypes.data, ba.ctypes.data
         ctx = C.c_void_p()
         assert lib.pack_init(C.byref(cfg), C.byref(ctx)) == dp.PACK_E_INVAL
+
+
+def test_cumulative_limits_on_host(lib):
+    """PACK_FLAG_CUMULATIVE: at most 1024 sources, and a bounded updates x sources table."""
+    import numpy as np
+    w = np.ones(1025, np.uint64)
+    bp = np.zeros(1025, np.uint32)
+    cfg, keep = _cfg(flags=dp.PACK_FLAG_CUMULATIVE, n_sources=1025)
+    cfg.share_weight, cfg.holdout_bp = w.ctypes.data, bp.ctypes.data
+    ctx = C.c_void_p()
+    assert lib.pack_init(C.byref(cfg), C.byref(ctx)) == dp.PACK_E_INVAL
+    assert "1024" in lib.pack_last_error(None).decode()
+    w2, bp2 = np.ones(1024, np.uint64), np.zeros(1024, np.uint32)
+    cfg, keep = _cfg(flags=dp.PACK_FLAG_CUMULATIVE, n_sources=1024, global_batch=1, window_tokens=64)
+    cfg.share_weight, cfg.holdout_bp = w2.ctypes.data, bp2.ctypes.data
+    cfg.n_tokens, cfg.n_docs = 1 << 24, (1 << 20)     # (2^20 + 2^18) updates x 1024 sources > 2^28
+    assert lib.pack_init(C.byref(cfg), C.byref(ctx)) == dp.PACK_E_INVAL
+    assert "2^28" in lib.pack_last_error(None).decode()
 
 
 def test_null_arguments_are_errors(lib):

@@ -26,7 +26,8 @@ def _setup(name):
         torch.cuda.empty_cache()
         say("generate", name)
         mode, _, base = name.partition("-") if "-" in name else ("", "", name)
-        c = make_corpus(base).replace(wrap=mode == "wrap", heldout=mode == "heldout", read_random=mode == "random")
+        c = make_corpus(base).replace(wrap=mode == "wrap", heldout=mode == "heldout", read_random=mode == "random",
+                                      cumulative=mode == "cum")
         if mode == "heldout":
             c = c.replace(updates_per_cycle=0)  # the 1-5 % held out cannot supply 200 updates
         say("oracle plan", name, c.n_docs, "docs", c.n_tokens, "tokens")
@@ -46,9 +47,10 @@ def _setup(name):
 # emission-and-digest launch takes, so it covers the two-kernel path;
 # wrap-pretrain is the pre-train workload with wrap packing, heldout-pretrain
 # its held-out (validation) stream, random-pretrain with each cycle's windows
-# read in a random order.
+# read in a random order, cum-pretrain with per-update counts from the cycle's
+# cumulative quotas.
 FULL = [("tiny", None), ("pretrain", None), ("sft", None), ("long", None), ("full", (24, 66)),
-        ("wrap-pretrain", None), ("heldout-pretrain", None), ("random-pretrain", None)]
+        ("wrap-pretrain", None), ("heldout-pretrain", None), ("random-pretrain", None), ("cum-pretrain", None)]
 
 
 @pytest.mark.parametrize("name,cap", FULL)
@@ -58,6 +60,8 @@ def test_full_size_parity(name, cap):
     say("compare plan", name)
     compare_plan(pk, op)
     compare_cycle(gi, oi, op)
+    if c.cumulative:
+        assert np.array_equal(pk.inspect("cum_taken"), op.cumulative_taken().ravel())
     U = oi.n_updates
     B, T = c.B, c.T
     r = np.random.default_rng(7)

@@ -95,6 +95,49 @@ def test_padding_free_rows_parity(kind, arg, bucket, world, wrap):
         pk.close()
 
 
+@pytest.mark.parametrize("kind,arg", SMALL_CASES)
+def test_cumulative_parity(kind, arg):
+    """The same cases with per-update counts from the cycle's cumulative quotas (PACK_FLAG_CUMULATIVE)."""
+    _parity_run(_corpus(kind, arg).replace(cumulative=True), "cumulative-" + kind, arg)
+
+
+CUM_MODES = [(s, wrap, rr, held) for s, (wrap, rr, held) in enumerate(
+    [(False, False, False), (True, False, False), (False, True, False), (False, False, True), (True, True, True),
+     (False, True, True), (True, False, False), (False, False, False)])]
+
+
+@pytest.mark.parametrize("seed,wrap,read_random,heldout", CUM_MODES)
+def test_cumulative_with_other_modes(seed, wrap, read_random, heldout):
+    """Cumulative quotas with wrap packing, the random read order and the held-out stream;
+    recipes with shares below one window per update."""
+    r = np.random.default_rng(500 + seed)
+    S = 2 + seed % 4
+    c = random_small(600 + seed, n_docs=700 + 150 * seed, n_sources=S, max_strata=1 + seed % 3, T=64,
+                     B=[1, 3, 4, 7, 8, 5, 16, 2][seed], max_len=130, prompts=bool(seed % 2),
+                     bp_max=6000 if heldout else 1500)
+    w = r.integers(1, 50, size=S).astype(np.uint64)
+    w[0] = 1 if seed % 2 else w[0]                     # a small share
+    w[-1] = 40 * int(w.sum()) if seed % 3 == 0 else w[-1]  # a dominant one
+    c = c.replace(weight=w, wrap=wrap, read_random=read_random, heldout=heldout, cumulative=True)
+    _parity_run(c, "cumulative-modes", seed)
+
+
+@pytest.mark.parametrize("S,B", [(70, 128), (130, 64)])
+def test_cumulative_many_sources(S, B):
+    """More sources than one wavefront holds: the schedule runs on a whole workgroup."""
+    c = random_small(700, n_docs=6000, n_sources=S, max_strata=2, T=64, B=B, max_len=60, bp_max=500)
+    _parity_run(c.replace(cumulative=True), "cumulative-many-sources", S)
+
+
+def test_cumulative_small_share_parity():
+    """A source below half a window per update: no windows under the fixed
+    apportionment, its windows under the cumulative quotas."""
+    c = _explicit([40, 20, 64, 10, 30] * 60, 64, 4, sources=[0, 1, 1, 1, 1] * 60, weights=[1, 60])
+    op = oracle.Plan(c.replace(cumulative=True))
+    assert op.cycle(0).taken[0] > 0
+    _parity_run(c.replace(cumulative=True), "cumulative-small-share", 0)
+
+
 PACKED_SHORT = {
     # windows of 1-3 real positions, many of them inside one 16-byte store group of the row
     "split_130": (lambda: _explicit([130] * 20, 64, 3), 1),
@@ -152,6 +195,8 @@ def _parity_run(c, kind, arg):
         return
     gi = pk.cycle(0)
     compare_cycle(gi, oi, op)
+    if getattr(c, "cumulative", False):
+        assert np.array_equal(pk.inspect("cum_taken"), op.cumulative_taken().ravel())
     U = oi.n_updates
     steps = list(range(0, U, max(1, U // 6)))[:6]
     for st in steps:
@@ -168,13 +213,14 @@ def _parity_run(c, kind, arg):
 
 @pytest.mark.parametrize("kind,arg,worlds", [("tiny", 0.5, [1, 2, 4, 8]), ("pretrain", 0.006, [1, 8, 16, 32, 64]),
                                              ("small", 4, [1, 2, 4, 8]), ("wrap-pretrain", 0.006, [1, 8, 64]),
-                                             ("heldout", 1100, [1, 2, 4, 8]), ("random-tiny", 0.5, [1, 2, 4, 8])])
+                                             ("heldout", 1100, [1, 2, 4, 8]), ("random-tiny", 0.5, [1, 2, 4, 8]),
+                                             ("cum-pretrain", 0.006, [1, 8, 64]), ("cum-tiny", 0.5, [1, 2, 8])])
 def test_elastic_rank_counts_identical(kind, arg, worlds):
     if kind == "heldout":  # a held-out stream large enough for B = 8
         c = random_small(arg, n_docs=2000, n_sources=2, T=64, B=8, max_len=60, bp_max=6000).replace(heldout=True)
     else:
         mode, _, base = kind.partition("-") if "-" in kind else ("", "", kind)
-        c = _corpus(base, arg).replace(wrap=mode == "wrap", read_random=mode == "random")
+        c = _corpus(base, arg).replace(wrap=mode == "wrap", read_random=mode == "random", cumulative=mode == "cum")
     if kind == "small":
         c = c.replace(B=8)
     if kind.endswith("pretrain"):
@@ -210,10 +256,10 @@ def test_world_not_dividing_batch_fails_at_init():
         assert e.value.code == dp.PACK_E_INVAL
 
 
-@pytest.mark.parametrize("read_random", [False, True])
-def test_cycles_until_exhausted_match_oracle(read_random):
+@pytest.mark.parametrize("read_random,cumulative", [(False, False), (True, False), (False, True), (True, True)])
+def test_cycles_until_exhausted_match_oracle(read_random, cumulative):
     c = random_small(40, n_docs=400, n_sources=3, T=64, B=6, max_len=100, prompts=True, updates_per_cycle=2)
-    c = c.replace(read_random=read_random)
+    c = c.replace(read_random=read_random, cumulative=cumulative)
     op = oracle.Plan(c)
     pk = dp.Packer(c)
     compare_plan(pk, op)
@@ -228,6 +274,8 @@ def test_cycles_until_exhausted_match_oracle(read_random):
             break
         say("cycle", cyc)
         compare_cycle(pk.cycle(cyc), oi, op)
+        if cumulative:
+            assert np.array_equal(pk.inspect("cum_taken"), op.cumulative_taken().ravel())
         compare_batch(to_np(pk.batch(0, oi.n_updates)), op.batch(0, oi.n_updates), f"cycle {cyc}")
     else:
         pytest.fail("never exhausted")
