@@ -82,6 +82,10 @@ def _load():
         lib.or_cum_export.argtypes = [vp, vp]
         lib.or_cumulative.restype = i32
         lib.or_cumulative.argtypes = [u32, u32, vp, vp, u64, u64, vp, C.POINTER(u64)]
+        lib.or_cumulative_b.restype = i32
+        lib.or_cumulative_b.argtypes = [u32, vp, u32, vp, vp, u64, u64, vp, C.POINTER(u64)]
+        lib.or_cycle_batches.restype = u64
+        lib.or_cycle_batches.argtypes = [vp, vp]
         lib.or_window_of.restype = u64
         lib.or_window_of.argtypes = [vp, u64, u32]
         lib.or_emit_window.restype = None
@@ -145,18 +149,25 @@ def apportion(B: int, weights) -> np.ndarray:
     return n
 
 
-def cumulative(B: int, weights, remaining, updates: int = 0, cap: Optional[int] = None):
-    """C6c on its own: (U, A [U+1, S]) for B windows per update, integer
-    weights and each source's remaining windows; updates = 0 takes the most
-    that fit."""
+def cumulative(B: int, weights, remaining, updates: int = 0, cap: Optional[int] = None, batches=None):
+    """C6c on its own: (U, A [U+1, S]) for B windows per update (or
+    batches[u] windows in update u), integer weights and each source's
+    remaining windows; updates = 0 takes the most that fit."""
     w = np.ascontiguousarray(weights, np.uint64)
     rem = np.ascontiguousarray(remaining, np.uint64)
     S = w.shape[0]
-    if cap is None:
+    if batches is not None:
+        bs = np.ascontiguousarray(batches, np.uint32)
+        cap = bs.shape[0] if cap is None else cap
+        assert bs.shape[0] >= cap
+    elif cap is None:
         cap = updates if updates else int(rem.sum()) // B
     A = np.zeros((cap + 1, S), np.uint32)
     U = C.c_uint64()
-    rc = _load().or_cumulative(B, S, _ptr(w), _ptr(rem), updates, cap, _ptr(A), C.byref(U))
+    if batches is not None:
+        rc = _load().or_cumulative_b(B, _ptr(bs), S, _ptr(w), _ptr(rem), updates, cap, _ptr(A), C.byref(U))
+    else:
+        rc = _load().or_cumulative(B, S, _ptr(w), _ptr(rem), updates, cap, _ptr(A), C.byref(U))
     if rc:
         raise OracleError(rc, "cumulative")
     return int(U.value), A[:U.value + 1].copy()
@@ -200,6 +211,7 @@ class _OrCorpus(C.Structure):
         ("bp", C.c_void_p), ("T", C.c_uint32), ("B", C.c_uint32), ("seed", C.c_uint64),
         ("pad_token", C.c_uint32), ("wrap", C.c_uint32), ("heldout", C.c_uint32), ("read_random", C.c_uint32),
         ("cumulative", C.c_uint32),
+        ("n_ramp", C.c_uint32), ("ramp_from", C.c_void_p), ("ramp_tokens", C.c_void_p),
     ]
 
 
@@ -214,6 +226,8 @@ class CycleInfo:
     learned_tokens: int
     positions: int
     plan_digest: bytes
+    batches: np.ndarray = None     # [U] windows of each update (B, or the ramp's batch)
+    tokens_start: int = 0          # tokens trained before the cycle
 
 
 class Plan:
@@ -234,6 +248,10 @@ class Plan:
             n_strata=np.ascontiguousarray(c.n_strata, np.uint32),
             weight=np.ascontiguousarray(c.weight, np.uint64),
             bp=np.ascontiguousarray(c.holdout_bp, np.uint32),
+            ramp_from=None if getattr(c, "ramp", None) is None else
+            np.ascontiguousarray([int(f) for f, _ in c.ramp], np.uint64),
+            ramp_tokens=None if getattr(c, "ramp", None) is None else
+            np.ascontiguousarray([int(t) for _, t in c.ramp], np.uint64),
         )
         k = self._keep
         D, S = k["source"].shape[0], k["weight"].shape[0]
@@ -249,7 +267,8 @@ class Plan:
             _ptr(k["prompt_len"]), S, _ptr(k["n_strata"]), _ptr(k["weight"]), _ptr(k["bp"]),
             c.T, c.B, c.seed & 0xFFFFFFFFFFFFFFFF, c.pad_token, 1 if getattr(c, "wrap", False) else 0,
             1 if getattr(c, "heldout", False) else 0, 1 if getattr(c, "read_random", False) else 0,
-            1 if getattr(c, "cumulative", False) else 0)
+            1 if getattr(c, "cumulative", False) else 0,
+            0 if k["ramp_from"] is None else k["ramp_from"].shape[0], _ptr(k["ramp_from"]), _ptr(k["ramp_tokens"]))
         err = C.c_int(0)
         self._p = lib.or_plan_build(C.byref(self._cs), C.byref(err))
         if not self._p:
@@ -305,7 +324,11 @@ class Plan:
         taken = np.zeros(S, np.uint64)
         U = int(lib.or_cycle_state(self._p, C.byref(cyc), _ptr(start), _ptr(taken)))
         remaining = self.windows_per_source - start - taken
-        wins = [self.window_of(b, j) for b in range(U) for j in range(self.corpus.B)] if U * self.corpus.B <= 2_000_000 else None
+        batches = np.zeros(max(U, 1), np.uint32)
+        t0 = int(lib.or_cycle_batches(self._p, _ptr(batches)))
+        batches = batches[:U]
+        nslots = int(batches.sum())
+        wins = [self.window_of(b, j) for b in range(U) for j in range(int(batches[b]))] if nslots <= 2_000_000 else None
         if wins is not None:
             wins = np.asarray(wins, dtype=np.int64)
             real = int(self.win_real[wins].sum()) if wins.size else 0
@@ -317,7 +340,7 @@ class Plan:
         if rc:
             raise OracleError(rc, "plan_digest")
         self.cycle_info = CycleInfo(c, U, start, taken, remaining, real, learned,
-                                    U * self.corpus.B * self.corpus.T, dig.tobytes())
+                                    nslots * self.corpus.T, dig.tobytes(), batches, t0)
         return self.cycle_info
 
     def cumulative_taken(self) -> np.ndarray:
@@ -344,16 +367,25 @@ class Plan:
 
     def batch(self, step: int, n_steps: int = 1, rank: int = 0, world: int = 1,
               digests: bool = True, learned: bool = True) -> dict:
+        """This rank's windows of updates [step, step+n_steps): [n, B/world, T]
+        arrays, or with a batch-size ramp [Σ B_b/world, T] (update after update)."""
         B, T = self.corpus.B, self.corpus.T
         if world <= 0 or B % world:
             raise OracleError(OR_E_INVAL, "batch world")
-        per = B // world
-        tok = np.zeros((n_steps, per, T), np.uint32)
-        pos = np.zeros((n_steps, per, T), np.int32)
-        doc = np.zeros((n_steps, per, T), np.int32)
-        mask = np.zeros((n_steps, per, T), np.uint8)
+        ramp = getattr(self.corpus, "ramp", None) is not None
+        if ramp:
+            bs = self.cycle_info.batches[step:step + n_steps]
+            if len(bs) != n_steps:
+                raise OracleError(OR_E_RANGE, "batch range")
+            shape = (int(bs.sum()) // world,)
+        else:
+            shape = (n_steps, B // world)
+        tok = np.zeros(shape + (T,), np.uint32)
+        pos = np.zeros(shape + (T,), np.int32)
+        doc = np.zeros(shape + (T,), np.int32)
+        mask = np.zeros(shape + (T,), np.uint8)
         lrn = np.zeros(n_steps, np.int64) if learned else None
-        dig = np.zeros((n_steps, per, 32), np.uint8) if digests else None
+        dig = np.zeros(shape + (32,), np.uint8) if digests else None
         rc = _load().or_batch(self._p, step, n_steps, rank, world, _ptr(tok), _ptr(pos), _ptr(doc),
                               _ptr(mask), _ptr(lrn), _ptr(dig))
         if rc:

@@ -35,6 +35,10 @@
  *     (quota at every update boundary, monotone, B per update), by exhaustive
  *     enumeration of every valid schedule on tiny cases, and by closed forms
  *     (one source; whole-window shares equal the fixed apportionment).
+ *   - batch-size ramp (C6b): batches recomputed from the definition across
+ *     cycles; each update's counts equal its batch's apportionment (fixed) or
+ *     lie within quota of the running seat count (cumulative, also against
+ *     every valid schedule on tiny cases); a one-piece ramp is the plain plan.
  *
  * All integers are unsigned unless stated; products that can exceed 64 bits
  * are taken in unsigned __int128.
@@ -338,40 +342,56 @@ static int cmp_due(const void *pa, const void *pb)
     return 0;
 }
 
-int or_cumulative(uint32_t B, uint32_t S, const uint64_t *w, const uint64_t *rem, uint64_t u_cfg,
-                  uint64_t cap, uint32_t *A, uint64_t *U_out)
+/* With a batch-size ramp (C6b) update u has Bs[u] windows and the quotas
+ * are taken at H(u) = Bs[0] + … + Bs[u−1] seats: window j of s is released in
+ * the first update u with j ≤ ceil(H(u+1)·w_s/W) and due by the first update
+ * u with H(u+1)·w_s ≥ j·W; Bs = NULL means B windows in every update. */
+int or_cumulative_b(uint32_t B, const uint32_t *Bs, uint32_t S, const uint64_t *w, const uint64_t *rem,
+                    uint64_t u_cfg, uint64_t cap, uint32_t *A, uint64_t *U_out)
 {
     u128 W = 0;
     for (uint32_t s = 0; s < S; s++) W += w[s];
-    if (W == 0 || W >> 64 || B == 0) return OR_E_INVAL;
+    if (W == 0 || W >> 64 || (!Bs && B == 0)) return OR_E_INVAL;
     *U_out = 0;
     for (uint32_t s = 0; s < S; s++) A[s] = 0;
-    due_item *it = (due_item *)malloc(sizeof(due_item) * ((uint64_t)B + S + 1));
-    if (!it) return OR_E_NOMEM;
+    uint64_t *H = (uint64_t *)malloc(sizeof(uint64_t) * (cap + 2));   /* H[u]: seats before update u */
+    uint32_t Bmax = B;
+    if (!H) return OR_E_NOMEM;
+    H[0] = 0;
+    for (uint64_t u = 0; u <= cap; u++) {
+        uint32_t Bu = Bs ? (u < cap ? Bs[u] : 0) : B;
+        if (Bs && u < cap && Bu > Bmax) Bmax = Bu;
+        H[u + 1] = H[u] + Bu;
+    }
+    due_item *it = (due_item *)malloc(sizeof(due_item) * ((uint64_t)Bmax + S + 1));
+    if (!it) { free(H); return OR_E_NOMEM; }
     uint64_t U = 0;
     for (uint64_t u = 0; u < cap && (u_cfg == 0 || u < u_cfg); u++) {
         const uint32_t *a = A + u * S;
         uint32_t *an = A + (u + 1) * S;
+        const uint64_t Bu = H[u + 1] - H[u];
         /* released, not yet taken windows of every source with their due updates */
         uint64_t m = 0;
         for (uint32_t s = 0; s < S; s++) {
             if (w[s] == 0) continue;
-            u128 q = (u128)(u + 1) * B * w[s];
-            u128 hi = (q + W - 1) / W;                    /* ceil((u+1)·B·w_s/W) */
+            u128 q = (u128)H[u + 1] * w[s];
+            u128 hi = (q + W - 1) / W;                    /* ceil(H(u+1)·w_s/W) */
             for (u128 j = (u128)a[s] + 1; j <= hi; j++) {
-                u128 num = j * W, den = (u128)B * w[s];
-                it[m].due = (num + den - 1) / den - 1;      /* ceil(j·W/(B·w_s)) − 1 */
+                /* due: the first update v with H(v+1)·w_s ≥ j·W (cap when none within the schedule) */
+                uint64_t v = u;
+                while (v < cap && (u128)H[v + 1] * w[s] < j * W) v++;
+                it[m].due = v;
                 it[m].s = s;
                 it[m].j = (uint32_t)j;
                 m++;
             }
         }
-        if (m < B) { free(it); return OR_E_INTERNAL; }
+        if (m < Bu) { free(it); free(H); return OR_E_INTERNAL; }
         qsort(it, m, sizeof(due_item), cmp_due);
         for (uint32_t s = 0; s < S; s++) an[s] = a[s];
-        for (uint64_t r = 0; r < B; r++) an[it[r].s] += 1;
-        for (uint64_t r = B; r < m; r++)
-            if (it[r].due <= u) { free(it); return OR_E_INTERNAL; }  /* deadline missed */
+        for (uint64_t r = 0; r < Bu; r++) an[it[r].s] += 1;
+        for (uint64_t r = Bu; r < m; r++)
+            if (it[r].due <= u) { free(it); free(H); return OR_E_INTERNAL; }  /* deadline missed */
         int fits = 1;
         for (uint32_t s = 0; s < S; s++)
             if (an[s] > rem[s]) fits = 0;
@@ -379,9 +399,18 @@ int or_cumulative(uint32_t B, uint32_t S, const uint64_t *w, const uint64_t *rem
         U = u + 1;
     }
     free(it);
+    free(H);
     *U_out = U;
     return OR_OK;
 }
+
+int or_cumulative(uint32_t B, uint32_t S, const uint64_t *w, const uint64_t *rem, uint64_t u_cfg,
+                  uint64_t cap, uint32_t *A, uint64_t *U_out)
+{
+    return or_cumulative_b(B, NULL, S, w, rem, u_cfg, cap, A, U_out);
+}
+
+
 
 /* ------------------------------------------------------------------------ */
 /* The plan of a corpus: C1–C6 over every document.                          */
@@ -406,6 +435,9 @@ typedef struct {
     uint32_t heldout;            /* 1: the stream is the held-out documents (C2v) */
     uint32_t read_random;        /* 1: each cycle's windows of a source read in a random order (C6r) */
     uint32_t cumulative;         /* 1: per-update counts from the cycle's cumulative quotas (C6c) */
+    uint32_t n_ramp;             /* 0: every update has B windows; else pieces of a batch-size ramp (C6b) */
+    const uint64_t *ramp_from;   /* [n_ramp] tokens trained at which each piece starts (first 0, rising) */
+    const uint64_t *ramp_tokens; /* [n_ramp] tokens per update within the piece (a multiple of T) */
 } or_corpus;
 
 typedef struct {
@@ -435,9 +467,30 @@ typedef struct {
     uint64_t *perm_start;        /* [S+1] with read_random: start of each source's part of perm */
     uint32_t *perm;              /* [U·B] with read_random: read order within each source's cycle range */
     uint64_t *taken;             /* [S] windows the current cycle takes from each source */
-    uint32_t *cum_A;             /* [(U+1)·S] with cumulative: windows of s taken before update u */
-    uint32_t *cum_src, *cum_k;   /* [U·B] with cumulative: slot table of every update */
+    uint32_t *ramp_n;            /* [n_ramp·S] with a ramp: the fixed apportionment of each piece's batch */
+    uint64_t tokens_done;        /* tokens (positions) of every update of the cycles before the current one */
+    uint32_t *upd_B;             /* [U] windows of each update of the current cycle */
+    uint64_t *upd_slot0;         /* [U+1] first slot of each update (prefix of upd_B) */
+    uint32_t *cum_A;             /* [(U+1)·S] tabled: windows of s taken before update u */
+    uint32_t *tab_src, *tab_i;   /* [Σ upd_B] tabled: each slot's source and cycle window index */
 } or_plan;
+
+/* Cycle mode: per-update tables (a ramp or the cumulative mixture) or the
+ * fixed apportionment with one slot table. */
+static int tabled(const or_corpus *c) { return c->cumulative || c->n_ramp > 0; }
+
+/* C6b. Batch-size ramp ([NS] Training, Updates: tokens_per_update is one
+ * number or pieces by the tokens trained; the batch of an update is read at
+ * the data line's token count, the cycle's start token plus its updates so
+ * far).  Reading: the tokens trained are the positions (B·T per update) of
+ * every earlier update, from 0 at cycle 0; an update starting at count t has
+ * the batch of the last piece whose start is ≤ t: tokens/T windows. */
+static uint32_t ramp_piece(const or_corpus *c, uint64_t t)
+{
+    uint32_t k = 0;
+    while (k + 1 < c->n_ramp && c->ramp_from[k + 1] <= t) k++;
+    return k;
+}
 
 typedef struct { uint32_t group; uint32_t d; uint64_t key; } sort_item;
 
@@ -687,6 +740,24 @@ or_plan *or_plan_build(const or_corpus *cin, int *err)
     if (*err) goto fail;
     *err = or_slot_table(c->B, S, p->n_upd, p->slot_src, p->slot_k);
     if (*err) goto fail;
+    if (c->n_ramp) {   /* C6b: each piece's batch B_k = tokens/T, world-independent; B is their largest */
+        uint32_t Bmax = 0;
+        for (uint32_t k = 0; k < c->n_ramp; k++) {
+            uint64_t tk = c->ramp_tokens[k];
+            if (tk == 0 || tk % T || tk / T > c->B) { *err = OR_E_INVAL; goto fail; }
+            if ((k == 0 && c->ramp_from[0] != 0) || (k > 0 && c->ramp_from[k] <= c->ramp_from[k - 1])) {
+                *err = OR_E_INVAL; goto fail;
+            }
+            if (tk / T > Bmax) Bmax = (uint32_t)(tk / T);
+        }
+        if (Bmax != c->B) { *err = OR_E_INVAL; goto fail; }
+        const uint64_t n_ramp_entries = (uint64_t)c->n_ramp * S;
+        ALLOC(p->ramp_n, n_ramp_entries);
+        for (uint32_t k = 0; k < c->n_ramp; k++) {
+            *err = or_apportion((uint32_t)(c->ramp_tokens[k] / T), S, c->weight, p->ramp_n + (uint64_t)k * S);
+            if (*err) goto fail;
+        }
+    }
 
     p->cycle = -1;
     p->U = 0;
@@ -712,7 +783,7 @@ void or_plan_free(or_plan *p)
     free(p->kept_docs); free(p->kept_tokens); free(p->held_docs); free(p->held_tokens);
     free(p->perm); free(p->perm_start);
     free(p->cyc_start); free(p->cyc_next); free(p->taken);
-    free(p->cum_A); free(p->cum_src); free(p->cum_k);
+    free(p->cum_A); free(p->tab_src); free(p->tab_i); free(p->ramp_n); free(p->upd_B); free(p->upd_slot0);
     free(p);
 }
 
@@ -727,11 +798,13 @@ void or_plan_free(or_plan *p)
 
 int or_cycle(or_plan *p, uint32_t cyc, uint32_t updates_cfg)
 {
-    const uint32_t S = p->c.n_sources, B = p->c.B;
+    const uint32_t S = p->c.n_sources, B = p->c.B, T = p->c.T;
     if ((int64_t)cyc != p->cycle + 1) return OR_E_STATE;
     uint64_t *start = calloc(S, sizeof(uint64_t)), *take = calloc(S, sizeof(uint64_t));
     uint64_t *rem = calloc(S, sizeof(uint64_t));
-    uint32_t *cA = NULL, *csrc = NULL, *ck = NULL, *cnt = NULL;
+    uint32_t *cA = NULL, *tsrc = NULL, *ti = NULL, *cnt = NULL, *Bs = NULL, *srcb = NULL, *kb = NULL;
+    uint64_t *slot0 = NULL;
+    const uint64_t t0 = (cyc == 0) ? 0 : p->tokens_done + (p->upd_slot0 ? p->upd_slot0[p->U] : (uint64_t)p->U * B) * T;
     int rc = OR_OK;
 #define CYC_FAIL(code) do { rc = (code); goto out; } while (0)
     if (!start || !take || !rem) CYC_FAIL(OR_E_NOMEM);
@@ -740,28 +813,64 @@ int or_cycle(or_plan *p, uint32_t cyc, uint32_t updates_cfg)
         rem[s] = p->src_win_start[s + 1] - p->src_win_start[s] - start[s];
     }
     uint64_t U;
-    if (p->c.cumulative) {
-        /* C6c: the cycle's schedule from its cumulative quotas */
+    if (tabled(&p->c)) {
+        /* C6b / C6c: the cycle's updates one by one, each with its own counts */
         uint64_t total = 0;
         for (uint32_t s = 0; s < S; s++) total += rem[s];
-        uint64_t cap = total / B;                    /* every update takes B windows */
-        if (updates_cfg > cap || cap == 0) CYC_FAIL(OR_E_EXHAUSTED);
+        uint32_t Bmin = B;
+        for (uint32_t k = 0; k < p->c.n_ramp; k++)
+            if (p->c.ramp_tokens[k] / T < Bmin) Bmin = (uint32_t)(p->c.ramp_tokens[k] / T);
+        uint64_t cap = total / Bmin;                 /* every update takes at least Bmin windows */
+        if (cap == 0) CYC_FAIL(OR_E_EXHAUSTED);
         if (updates_cfg) cap = updates_cfg;
         if (cap > 0xFFFFFFFFull) cap = 0xFFFFFFFFull;
+        Bs = malloc(sizeof(uint32_t) * cap);
         cA = malloc(sizeof(uint32_t) * (cap + 1) * S);
-        if (!cA) CYC_FAIL(OR_E_NOMEM);
-        rc = or_cumulative(B, S, p->c.weight, rem, updates_cfg, cap, cA, &U);
-        if (rc) goto out;
+        if (!Bs || !cA) CYC_FAIL(OR_E_NOMEM);
+        uint64_t t = t0;                             /* C6b: each update's batch at the tokens trained so far */
+        for (uint64_t u = 0; u < cap; u++) {
+            Bs[u] = p->c.n_ramp ? (uint32_t)(p->c.ramp_tokens[ramp_piece(&p->c, t)] / T) : B;
+            t += (uint64_t)Bs[u] * T;
+        }
+        if (p->c.cumulative) {
+            rc = or_cumulative_b(B, Bs, S, p->c.weight, rem, updates_cfg, cap, cA, &U);
+            if (rc) goto out;
+        } else {   /* fixed apportionment of each update's batch, until a source runs out */
+            U = 0;
+            for (uint32_t s = 0; s < S; s++) cA[s] = 0;
+            uint64_t tu = t0;                        /* tokens trained before update u */
+            for (uint64_t u = 0; u < cap; u++) {
+                const uint32_t *n = p->ramp_n + (uint64_t)ramp_piece(&p->c, tu) * S;
+                tu += (uint64_t)Bs[u] * T;
+                int fits = 1;
+                for (uint32_t s = 0; s < S; s++) {
+                    cA[(u + 1) * S + s] = cA[u * S + s] + n[s];
+                    if (cA[(u + 1) * S + s] > rem[s]) fits = 0;
+                }
+                if (!fits) break;
+                U = u + 1;
+            }
+        }
         if (U == 0 || (updates_cfg && U < updates_cfg)) CYC_FAIL(OR_E_EXHAUSTED);
         for (uint32_t s = 0; s < S; s++) take[s] = cA[U * S + s];
-        csrc = malloc(sizeof(uint32_t) * U * B);
-        ck = malloc(sizeof(uint32_t) * U * B);
+        slot0 = malloc(sizeof(uint64_t) * (U + 1));
+        if (!slot0) CYC_FAIL(OR_E_NOMEM);
+        slot0[0] = 0;
+        for (uint64_t u = 0; u < U; u++) slot0[u + 1] = slot0[u] + Bs[u];
+        tsrc = malloc(sizeof(uint32_t) * (slot0[U] ? slot0[U] : 1));
+        ti = malloc(sizeof(uint32_t) * (slot0[U] ? slot0[U] : 1));
         cnt = malloc(sizeof(uint32_t) * S);
-        if (!csrc || !ck || !cnt) CYC_FAIL(OR_E_NOMEM);
+        srcb = malloc(sizeof(uint32_t) * B);
+        kb = malloc(sizeof(uint32_t) * B);
+        if (!tsrc || !ti || !cnt || !srcb || !kb) CYC_FAIL(OR_E_NOMEM);
         for (uint64_t u = 0; u < U; u++) {   /* each update's slots interleaved as in C6 */
             for (uint32_t s = 0; s < S; s++) cnt[s] = cA[(u + 1) * S + s] - cA[u * S + s];
-            rc = or_slot_table(B, S, cnt, csrc + u * B, ck + u * B);
+            rc = or_slot_table(Bs[u], S, cnt, srcb, kb);
             if (rc) goto out;
+            for (uint32_t j = 0; j < Bs[u]; j++) {
+                tsrc[slot0[u] + j] = srcb[j];
+                ti[slot0[u] + j] = cA[u * S + srcb[j]] + kb[j];
+            }
         }
     } else {
         if (updates_cfg > 0) {
@@ -805,21 +914,30 @@ int or_cycle(or_plan *p, uint32_t cyc, uint32_t updates_cfg)
         p->perm = perm; p->perm_start = ps;
     }
     p->U = (uint32_t)U;
+    p->tokens_done = t0;
     for (uint32_t s = 0; s < S; s++) {
         p->cyc_start[s] = start[s];
         p->cyc_next[s] = start[s] + take[s];
         p->taken[s] = take[s];
     }
-    if (p->c.cumulative) {
-        free(p->cum_A); free(p->cum_src); free(p->cum_k);
-        p->cum_A = cA; p->cum_src = csrc; p->cum_k = ck;
-        cA = csrc = ck = NULL;
+    if (tabled(&p->c)) {
+        free(p->cum_A); free(p->tab_src); free(p->tab_i); free(p->upd_B); free(p->upd_slot0);
+        p->cum_A = cA; p->tab_src = tsrc; p->tab_i = ti; p->upd_B = Bs; p->upd_slot0 = slot0;
+        cA = tsrc = ti = Bs = NULL;
+        slot0 = NULL;
     }
     p->cycle = cyc;
 out:
 #undef CYC_FAIL
-    free(start); free(take); free(rem); free(cA); free(csrc); free(ck); free(cnt);
+    free(start); free(take); free(rem); free(cA); free(tsrc); free(ti); free(cnt); free(Bs); free(slot0);
+    free(srcb); free(kb);
     return rc;
+}
+
+/* Windows of update b of the current cycle. */
+static uint32_t upd_batch(const or_plan *p, uint64_t b)
+{
+    return p->upd_B ? p->upd_B[b] : p->c.B;
 }
 
 /* Global window index of slot j of update b of the current cycle. */
@@ -827,9 +945,10 @@ uint64_t or_window_of(const or_plan *p, uint64_t b, uint32_t j)
 {
     uint32_t s;
     uint64_t i;                                    /* the source's i-th window of the cycle */
-    if (p->c.cumulative) {
-        s = p->cum_src[b * p->c.B + j];
-        i = (uint64_t)p->cum_A[b * p->c.n_sources + s] + p->cum_k[b * p->c.B + j];
+    if (tabled(&p->c)) {
+        const uint64_t x = p->upd_slot0[b] + j;
+        s = p->tab_src[x];
+        i = p->tab_i[x];
     } else {
         s = p->slot_src[j];
         i = b * p->n_upd[s] + p->slot_k[j];
@@ -884,25 +1003,27 @@ int or_batch(const or_plan *p, uint32_t step, uint32_t n_steps, uint32_t rank, u
              uint32_t *tok, int32_t *pos, int32_t *doc, uint8_t *mask, int64_t *learned,
              uint8_t *digests)
 {
-    const uint32_t B = p->c.B, T = p->c.T;
+    const uint32_t T = p->c.T;
     if (p->cycle < 0) return OR_E_STATE;
-    if (world == 0 || rank >= world || B % world) return OR_E_INVAL;
+    if (world == 0 || rank >= world || p->c.B % world) return OR_E_INVAL;
     if ((uint64_t)step + n_steps > p->U) return OR_E_RANGE;
-    const uint32_t per = B / world;
+    uint64_t w = 0;   /* this rank's windows, update after update (B_b/world of update b) */
     for (uint32_t i = 0; i < n_steps; i++) {
         uint64_t b = (uint64_t)step + i;
-        for (uint32_t jj = 0; jj < per; jj++) {
+        const uint32_t Bb = upd_batch(p, b);
+        if (Bb % world) return OR_E_INVAL;
+        const uint32_t per = Bb / world;
+        for (uint32_t jj = 0; jj < per; jj++, w++) {
             uint32_t j = rank * per + jj;
             uint64_t gw = or_window_of(p, b, j);
-            uint64_t at = ((uint64_t)i * per + jj) * T;
+            uint64_t at = w * T;
             or_emit_window(p, gw, tok + at, pos + at, doc + at, mask + at);
             if (digests)
-                or_window_digest(T, tok + at, pos + at, doc + at, mask + at,
-                                 digests + ((uint64_t)i * per + jj) * 32);
+                or_window_digest(T, tok + at, pos + at, doc + at, mask + at, digests + w * 32);
         }
         if (learned) {
             int64_t sum = 0;
-            for (uint32_t j = 0; j < B; j++) sum += (int64_t)p->win_learn[or_window_of(p, b, j)];
+            for (uint32_t j = 0; j < Bb; j++) sum += (int64_t)p->win_learn[or_window_of(p, b, j)];
             learned[i] = sum;
         }
     }
@@ -918,7 +1039,10 @@ int or_batch(const or_plan *p, uint32_t step, uint32_t n_steps, uint32_t rank, u
  * where window jj begins, row_start[per] their total; the row's length is that
  * total rounded up to a multiple of bucket (none for bucket ≤ 1), at most
  * per·T, and its positions past the total are padding.  Positions of the
- * row buffer past the length are left as padding here (callers use the length). */
+ * row buffer past the length are left as padding here (callers use the length).
+ * With a batch-size ramp rows are B/world·T positions apart (B the largest
+ * batch), row_start rows B/world + 1 long; update b fills its first
+ * B_b/world + 1 entries and repeats the total in the rest. */
 int or_batch_packed(const or_plan *p, uint32_t step, uint32_t n_steps, uint32_t rank, uint32_t world,
                     uint32_t bucket, uint32_t *tok, int32_t *pos, int32_t *doc, uint8_t *mask,
                     int64_t *row_start, int64_t *length)
@@ -927,25 +1051,31 @@ int or_batch_packed(const or_plan *p, uint32_t step, uint32_t n_steps, uint32_t 
     if (p->cycle < 0) return OR_E_STATE;
     if (world == 0 || rank >= world || B % world) return OR_E_INVAL;
     if ((uint64_t)step + n_steps > p->U) return OR_E_RANGE;
-    const uint32_t per = B / world;
-    const uint64_t cap = (uint64_t)per * T;
+    const uint32_t pmax = B / world;               /* row pitch: the largest batch's windows */
+    const uint64_t pitch = (uint64_t)pmax * T;
     uint32_t *wt = malloc(4ull * T); int32_t *wp = malloc(4ull * T), *wd = malloc(4ull * T); uint8_t *wm = malloc(T);
     if (!wt || !wp || !wd || !wm) { free(wt); free(wp); free(wd); free(wm); return OR_E_NOMEM; }
     for (uint32_t i = 0; i < n_steps; i++) {
-        uint32_t *rt = tok + i * cap; int32_t *rp = pos + i * cap, *rd = doc + i * cap; uint8_t *rm = mask + i * cap;
+        const uint32_t Bb = upd_batch(p, (uint64_t)step + i);
+        if (Bb % world) { free(wt); free(wp); free(wd); free(wm); return OR_E_INVAL; }
+        const uint32_t per = Bb / world;
+        const uint64_t cap = (uint64_t)per * T;
+        uint32_t *rt = tok + i * pitch; int32_t *rp = pos + i * pitch, *rd = doc + i * pitch;
+        uint8_t *rm = mask + i * pitch;
+        int64_t *rs = row_start + (uint64_t)i * (pmax + 1);
         for (uint64_t x = 0; x < cap; x++) { rt[x] = p->c.pad_token; rp[x] = 0; rd[x] = -1; rm[x] = 0; }
         uint64_t at = 0;
         for (uint32_t jj = 0; jj < per; jj++) {
             uint64_t gw = or_window_of(p, (uint64_t)step + i, rank * per + jj);
             uint64_t real = p->win_real[gw];
-            row_start[(uint64_t)i * (per + 1) + jj] = (int64_t)at;
+            rs[jj] = (int64_t)at;
             or_emit_window(p, gw, wt, wp, wd, wm);
             for (uint64_t t = 0; t < real; t++) {
                 rt[at + t] = wt[t]; rp[at + t] = wp[t]; rd[at + t] = wd[t]; rm[at + t] = wm[t];
             }
             at += real;
         }
-        row_start[(uint64_t)i * (per + 1) + per] = (int64_t)at;
+        for (uint32_t jj = per; jj <= pmax; jj++) rs[jj] = (int64_t)at;
         uint64_t L = at;
         if (bucket > 1) L = (at + bucket - 1) / bucket * bucket;
         if (L > cap) L = cap;
@@ -971,7 +1101,8 @@ int or_plan_digest(const or_plan *p, uint8_t out[32])
     const uint32_t S = c->n_sources;
     if (p->cycle < 0) return OR_E_STATE;
     uint64_t bytes = 8 + 4 + 4 + 8 + 4 + 4 + (uint64_t)S * (8 + 4 + 4 + 4 + 8 + 8 + 8) + 4 + 4 + 8ull * S + 8 + 8
-                     + (c->read_random ? 4 : 0) + (c->cumulative ? 4 : 0);
+                     + (c->read_random ? 4 : 0) + (c->cumulative ? 4 : 0)
+                     + (c->n_ramp ? 4 + 4 + 16ull * c->n_ramp + 8 : 0);
     uint8_t *buf = (uint8_t *)malloc(bytes), *w = buf;
     if (!buf) return OR_E_NOMEM;
     /* the packing mode and the stream (training / held-out) are part of the plan */
@@ -980,6 +1111,12 @@ int or_plan_digest(const or_plan *p, uint8_t out[32])
     *w++ = c->heldout ? 'V' : '1';
     if (c->read_random) put(&w, 0x444E4152u, 4);  /* "RAND": windows read in a random order */
     if (c->cumulative) put(&w, 0x554D5543u, 4);   /* "CUMU": per-update counts from cumulative quotas */
+    if (c->n_ramp) {                               /* "RAMP": the pieces and the cycle's first token */
+        put(&w, 0x504D4152u, 4);
+        put(&w, c->n_ramp, 4);
+        for (uint32_t k = 0; k < c->n_ramp; k++) { put(&w, c->ramp_from[k], 8); put(&w, c->ramp_tokens[k], 8); }
+        put(&w, p->tokens_done, 8);
+    }
     put(&w, c->T, 4); put(&w, c->B, 4); put(&w, c->seed, 8); put(&w, S, 4); put(&w, c->pad_token, 4);
     for (uint32_t s = 0; s < S; s++) {
         put(&w, c->weight[s], 8); put(&w, c->bp[s], 4); put(&w, c->n_strata[s], 4);
@@ -1032,10 +1169,17 @@ uint32_t or_cycle_state(const or_plan *p, int64_t *cycle, uint64_t *start /*[S]*
     return p->U;
 }
 
-/* With the cumulative mixture: A [(U+1)·S] of the current cycle. */
+/* Batches of the current cycle's updates [U] and the tokens trained before it. */
+uint64_t or_cycle_batches(const or_plan *p, uint32_t *Bs)
+{
+    for (uint32_t u = 0; u < p->U; u++) Bs[u] = upd_batch(p, u);
+    return p->tokens_done;
+}
+
+/* Tabled cycles (a ramp or the cumulative mixture): A [(U+1)·S] of the current cycle. */
 int or_cum_export(const or_plan *p, uint32_t *A)
 {
-    if (!p->c.cumulative || p->cycle < 0) return OR_E_STATE;
+    if (!tabled(&p->c) || p->cycle < 0) return OR_E_STATE;
     memcpy(A, p->cum_A, sizeof(uint32_t) * ((uint64_t)p->U + 1) * p->c.n_sources);
     return OR_OK;
 }

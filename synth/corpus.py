@@ -19,7 +19,7 @@ from __future__ import annotations
 
 import dataclasses
 import math
-from typing import Dict, Optional
+from typing import Dict, Optional, Tuple
 
 import numpy as np
 
@@ -49,6 +49,7 @@ class Corpus:
     heldout: bool = False       # stream: False = training documents, True = held-out (validation)
     read_random: bool = False   # each cycle's windows of a source read in a random order
     cumulative: bool = False    # per-update counts from the cycle's cumulative quotas
+    ramp: Optional[Tuple[Tuple[int, int], ...]] = None  # batch-size ramp: ((from_tokens, tokens_per_update), ...)
 
     @property
     def n_docs(self) -> int:
