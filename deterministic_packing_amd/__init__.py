@@ -18,18 +18,19 @@ import numpy as np
 
 __all__ = [
     "DpackError", "load_library", "pack_init", "pack_cycle", "pack_batch", "pack_batch_packed", "pack_fingerprint",
-    "pack_inspect", "pack_get_timings", "pack_destroy", "pack_strerror", "Packer", "INSPECT", "SYMBOLS",
+    "pack_fingerprint_steps", "pack_inspect", "pack_get_timings", "pack_destroy", "pack_strerror", "Packer", "INSPECT", "SYMBOLS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdpack.so")
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 PACK_OK, PACK_E_ABI, PACK_E_INVAL, PACK_E_NOMEM, PACK_E_HIP = 0, -1, -2, -3, -4
 PACK_E_EXHAUSTED, PACK_E_STATE, PACK_E_RANGE = -5, -6, -7
 
-SYMBOLS = ("pack_init", "pack_cycle", "pack_batch", "pack_batch_packed", "pack_fingerprint", "pack_inspect",
-           "pack_get_timings", "pack_destroy", "pack_strerror", "pack_last_error")
+SYMBOLS = ("pack_init", "pack_cycle", "pack_batch", "pack_batch_packed", "pack_fingerprint",
+           "pack_fingerprint_steps", "pack_inspect", "pack_get_timings", "pack_destroy", "pack_strerror",
+           "pack_last_error")
 
 PACK_FLAG_TIMING = 1
 PACK_FLAG_WRAP = 2
@@ -47,7 +48,7 @@ INSPECT = {
     "win_first": (10, np.uint64), "src_win_start": (11, np.uint64), "win_real": (12, np.uint64),
     "win_learn": (13, np.uint64), "per_update": (14, np.uint32), "slot_src": (15, np.uint32),
     "slot_k": (16, np.uint32), "counts": (17, np.uint64),
-    "cum_taken": (18, np.uint32),
+    "cum_taken": (18, np.uint32), "update_batch": (19, np.uint32),
 }
 
 
@@ -67,6 +68,7 @@ class PackConfig(C.Structure):
         ("holdout_bp", C.c_void_p), ("window_tokens", C.c_uint32), ("global_batch", C.c_uint32),
         ("updates_per_cycle", C.c_uint32), ("pad_token", C.c_uint32), ("seed", C.c_uint64),
         ("rank", C.c_uint32), ("world", C.c_uint32), ("stream", C.c_void_p),
+        ("n_ramp", C.c_uint32), ("ramp_from", C.c_void_p), ("ramp_tokens", C.c_void_p),
     ]
 
 
@@ -122,6 +124,8 @@ def load_library(path: Optional[str] = None):
     lib.pack_batch_packed.argtypes = [vp, u32, u32, C.POINTER(PackOutPacked)]
     lib.pack_fingerprint.restype = i32
     lib.pack_fingerprint.argtypes = [vp, vp, u32, vp]
+    lib.pack_fingerprint_steps.restype = i32
+    lib.pack_fingerprint_steps.argtypes = [vp, u32, u32, vp, vp]
     lib.pack_inspect.restype = i32
     lib.pack_inspect.argtypes = [vp, u32, vp, C.c_uint64, C.POINTER(C.c_uint64)]
     lib.pack_get_timings.restype = i32
@@ -178,6 +182,11 @@ def pack_fingerprint(ctx: int, digests_ptr: int, n_batches: int, out_ptr: int) -
     _check(load_library().pack_fingerprint(ctx, digests_ptr, n_batches, out_ptr), "pack_fingerprint", ctx)
 
 
+def pack_fingerprint_steps(ctx: int, step: int, n_steps: int, digests_ptr: int, out_ptr: int) -> None:
+    _check(load_library().pack_fingerprint_steps(ctx, step, n_steps, digests_ptr, out_ptr),
+           "pack_fingerprint_steps", ctx)
+
+
 def pack_inspect(ctx: int, what: str) -> np.ndarray:
     code, dtype = INSPECT[what]
     lib = load_library()
@@ -228,6 +237,11 @@ class Packer:
             bp=np.ascontiguousarray(corpus.holdout_bp, np.uint32),
         )
         assert self._host["weight"].shape[0] == S
+        ramp = getattr(corpus, "ramp", None)
+        if ramp is not None:
+            self._host["ramp_from"] = np.ascontiguousarray([int(f) for f, _ in ramp], np.uint64)
+            self._host["ramp_tokens"] = np.ascontiguousarray([int(t) for _, t in ramp], np.uint64)
+        self.ramp = ramp is not None
         d = self.dev
         self.cfg = PackConfig(
             ABI_VERSION, (PACK_FLAG_TIMING if timing else 0) | (PACK_FLAG_WRAP if getattr(corpus, "wrap", False) else 0)
@@ -240,9 +254,13 @@ class Packer:
             d["prompt_len"].data_ptr() if d.get("prompt_len") is not None else None,
             S, self._host["n_strata"].ctypes.data, self._host["weight"].ctypes.data,
             self._host["bp"].ctypes.data, corpus.T, corpus.B, corpus.updates_per_cycle,
-            corpus.pad_token, corpus.seed & 0xFFFFFFFFFFFFFFFF, rank, world, self.stream.cuda_stream)
+            corpus.pad_token, corpus.seed & 0xFFFFFFFFFFFFFFFF, rank, world, self.stream.cuda_stream,
+            len(ramp) if ramp is not None else 0,
+            self._host["ramp_from"].ctypes.data if ramp is not None else None,
+            self._host["ramp_tokens"].ctypes.data if ramp is not None else None)
         self.ctx = pack_init(self.cfg)
         self.per = corpus.B // world
+        self.batches = None  # windows of each update of the current cycle (all ranks)
 
     def close(self):
         if getattr(self, "ctx", None):
@@ -264,23 +282,33 @@ class Packer:
         for k, v in arrs.items():
             setattr(info, k, v.ctypes.data)
         pack_cycle(self.ctx, c, info)
+        self.batches = pack_inspect(self.ctx, "update_batch")
         out = dict(cycle=info.cycle, n_updates=info.n_updates, real_tokens=info.real_tokens,
                    learned_tokens=info.learned_tokens, positions=info.positions,
-                   plan_digest=bytes(info.plan_digest))
+                   plan_digest=bytes(info.plan_digest), batches=self.batches)
         out.update(arrs)
         return out
 
-    def alloc_out(self, n_steps: int, digests: bool = True, learned: bool = True) -> dict:
+    def windows_of(self, step: int, n_steps: int) -> int:
+        """This rank's windows of updates [step, step+n_steps)."""
+        if not self.ramp:
+            return n_steps * self.per
+        return int(self.batches[step:step + n_steps].sum()) // self.world
+
+    def alloc_out(self, n_steps: int, digests: bool = True, learned: bool = True, step: int = 0) -> dict:
+        """Output buffers: [n_steps, B/world, ...], or with a ramp [windows, ...]
+        for the windows of updates [step, step+n_steps), update after update."""
         t = self.torch
         dev = self.dev["tokens"].device
-        shape = (n_steps, self.per, self.corpus.T)
+        lead = (self.windows_of(step, n_steps),) if self.ramp else (n_steps, self.per)
+        shape = lead + (self.corpus.T,)
         return dict(
             tokens=t.empty(shape, dtype=t.int32, device=dev),  # uint32 bits
             pos=t.empty(shape, dtype=t.int32, device=dev),
             doc=t.empty(shape, dtype=t.int32, device=dev),
             mask=t.empty(shape, dtype=t.uint8, device=dev),
             learned=t.empty((n_steps,), dtype=t.int64, device=dev) if learned else None,
-            digests=t.empty((n_steps, self.per, 32), dtype=t.uint8, device=dev) if digests else None,
+            digests=t.empty(lead + (32,), dtype=t.uint8, device=dev) if digests else None,
         )
 
     def batch_into(self, step: int, n_steps: int, out: dict) -> dict:
@@ -292,7 +320,7 @@ class Packer:
         return out
 
     def batch(self, step: int, n_steps: int = 1, digests: bool = True, learned: bool = True) -> dict:
-        return self.batch_into(step, n_steps, self.alloc_out(n_steps, digests, learned))
+        return self.batch_into(step, n_steps, self.alloc_out(n_steps, digests, learned, step))
 
     def alloc_out_packed(self, n_steps: int, learned: bool = True) -> dict:
         t = self.torch
@@ -323,6 +351,14 @@ class Packer:
         n = int(digests.shape[0])
         out = t.empty((n, 32), dtype=t.uint8, device=digests.device)
         pack_fingerprint(self.ctx, digests.data_ptr(), n, out.data_ptr())
+        return out
+
+    def fingerprint_steps(self, step: int, n_steps: int, digests) -> "torch.Tensor":
+        """digests: device uint8, the B_b digests of updates [step, step+n_steps)
+        one after another (every rank's slice of an update in rank order)."""
+        t = self.torch
+        out = t.empty((n_steps, 32), dtype=t.uint8, device=digests.device)
+        pack_fingerprint_steps(self.ctx, step, n_steps, digests.data_ptr(), out.data_ptr())
         return out
 
     def inspect(self, what: str) -> np.ndarray:

@@ -1,5 +1,6 @@
 // api.hip — the C ABI declared in include/dpack.h: context, workspace, the
 // synchronous plan (pack_init), cycles, and asynchronous batch emission.
+#include <algorithm>
 #include <cstring>
 #include <mutex>
 #include <new>
@@ -163,6 +164,16 @@ struct pack_ctx {
     int64_t cycle = -1;
     uint32_t U = 0;
     std::vector<uint64_t> cyc_start, cyc_next, taken;
+    // batch-size ramp: pieces, each piece's apportionment [K][S], the tokens
+    // trained before the current cycle and after it, the cycle's per-update
+    // batches and this rank's output prefix
+    std::vector<uint64_t> ramp_from, ramp_tokens;
+    std::vector<uint32_t> ramp_n_h;
+    uint32_t* ramp_n = nullptr;        // device [K][S]
+    dp::RampSpan* spans = nullptr;     // device [K+1]
+    uint64_t tokens_start = 0, tokens_next = 0;
+    std::vector<uint32_t> upd_B;
+    std::vector<uint64_t> upd_out0;
     std::string err;
 };
 
@@ -179,6 +190,13 @@ struct Carver {
         return p;
     }
 };
+
+// smallest batch of an update: B, or the ramp's smallest piece
+uint32_t ramp_bmin(const pack_ctx& c) {
+    uint64_t b = c.p.B;
+    for (uint64_t t : c.ramp_tokens) b = std::min<uint64_t>(b, t / c.p.T);
+    return (uint32_t)b;
+}
 
 // Lay out (or size, when base == nullptr) every device array of the plan.
 size_t carve(pack_ctx& c, char* base) {
@@ -234,14 +252,21 @@ size_t carve(pack_ctx& c, char* base) {
     p.wval[0] = k.take<uint32_t>(WR);
     p.wval[1] = k.take<uint32_t>(WR);
     p.wgroup = k.take<uint32_t>(WR);
-    const uint64_t CU = p.cumulative ? P / B : 0;  // most updates of a cycle: each takes B of ≤ P windows
-    p.cum_A = k.take<uint32_t>(p.cumulative ? (CU + 1) * S : 0);
-    p.cum_rem = k.take<uint64_t>(p.cumulative ? S : 0);
-    p.cum_out = k.take<uint64_t>(p.cumulative ? S + 1 : 0);
-    p.cslot_src = k.take<uint32_t>(CU * B);
-    p.cslot_i = k.take<uint32_t>(CU * B);
+    // per-update tables: a cycle has at most P/Bmin updates (each takes ≥ Bmin of ≤ P windows)
+    const uint64_t CU = p.tabled ? P / ramp_bmin(c) : 0;
+    const uint64_t K = c.ramp_from.size();
+    p.cum_A = k.take<uint32_t>(p.tabled ? (CU + 1) * S : 0);
+    p.cum_rem = k.take<uint64_t>(p.tabled ? S : 0);
+    p.cum_out = k.take<uint64_t>(p.tabled ? S + 1 : 0);
+    p.cslot_src = k.take<uint32_t>(p.tabled ? P : 0);
+    p.cslot_i = k.take<uint32_t>(p.tabled ? P : 0);
+    p.upd_B = k.take<uint32_t>(p.ramp ? CU + 1 : 0);
+    p.upd_slot0 = k.take<uint64_t>(p.ramp ? CU + 1 : 0);
+    p.upd_out0 = k.take<uint64_t>(p.ramp ? CU + 1 : 0);
+    c.ramp_n = k.take<uint32_t>(K * S);
+    c.spans = k.take<dp::RampSpan>(K + 1);
     c.nstart = k.take<uint32_t>(S + 1);
-    c.dig_cap = 128 + 64 * S;  // digest message: 64 + 52·S bytes at most
+    c.dig_cap = 128 + 64 * S + 16 * K + 16;  // digest message: 64 + 52·S + 16·K + 16 bytes at most
     c.dig_buf = k.take<uint8_t>(c.dig_cap + 32);
     return k.off + ALIGN;
 }
@@ -258,7 +283,7 @@ void h2d(T* dst, const T* src, uint64_t count, hipStream_t st) {
 // pinned staging: bytes for the largest set of copies between two synchronizations
 // largest use: pack_cycle's cycle starts, read-order starts, sums, digest
 // message (≤ 64 + 52·S bytes) and digest, each 64-byte aligned
-size_t pin_bytes_for(uint32_t S) { return 128ull * S + 4096; }
+size_t pin_bytes_for(uint32_t S, uint64_t K) { return 128ull * S + 112ull * K + 8192; }
 
 template <typename T>
 T* pin_take(pack_ctx& c, uint64_t count) {
@@ -317,11 +342,31 @@ void check_config(const pack_config* cfg) {
     unsigned __int128 W = 0;
     for (uint32_t s = 0; s < cfg->n_sources; ++s) W += cfg->share_weight[s];
     if (W == 0 || (W >> 64) != 0) bad("share weights must sum to [1, 2^64)");
+    uint32_t Bmin = B;
+    if (cfg->n_ramp) {
+        if (cfg->n_ramp > 4096) bad("at most 4096 ramp pieces");
+        if (!cfg->ramp_from || !cfg->ramp_tokens) bad("ramp_from and ramp_tokens are required with n_ramp > 0");
+        uint64_t Bmax = 0;
+        for (uint32_t k = 0; k < cfg->n_ramp; ++k) {
+            const uint64_t tk = cfg->ramp_tokens[k];
+            if (tk == 0 || tk % T) bad("every ramp piece's tokens per update must be a positive multiple of T");
+            const uint64_t Bk = tk / T;
+            if (Bk > (1u << 20)) bad("a ramp piece's batch must be at most 2^20 windows");
+            if (Bk % cfg->world) bad("world must divide every ramp piece's batch");
+            if (k == 0 ? cfg->ramp_from[0] != 0 : cfg->ramp_from[k] <= cfg->ramp_from[k - 1])
+                bad("ramp pieces must start at 0 tokens and rise");
+            if (Bk > Bmax) Bmax = Bk;
+            if (Bk < Bmin) Bmin = (uint32_t)Bk;
+        }
+        if (Bmax != B) bad("with a ramp, global_batch must be the largest piece's batch");
+    }
     if (cfg->flags & PACK_FLAG_CUMULATIVE) {
         if (cfg->n_sources > 1024) bad("the cumulative mixture takes at most 1024 sources");
+    }
+    if ((cfg->flags & PACK_FLAG_CUMULATIVE) || cfg->n_ramp) {
         const uint64_t cap = cfg->n_docs + cfg->n_tokens / T;  // windows ≤ pieces ≤ cap
-        if ((cap / B + 1) * cfg->n_sources > (1ull << 28))
-            bad("the cumulative mixture's table (updates x sources) exceeds 2^28 entries");
+        if ((cap / Bmin + 1) * cfg->n_sources > (1ull << 28))
+            bad("the per-update table (updates x sources) exceeds 2^28 entries");
     }
 }
 
@@ -422,6 +467,8 @@ void build_plan(pack_ctx& c) {
     c.timer.end(st);
     c.timer.begin(PACK_PHASE_MIXTURE, st);
     dp::launch_mixture_w(p, c.W, c.nstart, st);
+    for (size_t k = 0; k < c.ramp_tokens.size(); ++k)  // each ramp piece's batch apportioned the same way
+        dp::launch_apportion(p, c.W, (uint32_t)(c.ramp_tokens[k] / p.T), c.ramp_n + k * p.S, st);
     dp::launch_checks(p, st);
     c.timer.end(st);
     const uint32_t* h_upd = d2h_staged(c, p.n_upd, p.S);
@@ -436,6 +483,11 @@ void build_plan(pack_ctx& c) {
     c.src_piece_start.assign(h_sps, h_sps + p.S + 1);
     err = *h_err;
     if (err) throw dp::HipError{hipErrorUnknown, "internal plan consistency check (library bug)"};
+    if (!c.ramp_tokens.empty()) {  // K·S counts: once, at init (may exceed the staging area)
+        c.ramp_n_h.resize(c.ramp_tokens.size() * p.S);
+        d2h(c.ramp_n_h.data(), c.ramp_n, c.ramp_n_h.size(), st);
+        DP_HIP(hipStreamSynchronize(st));
+    }
 }
 
 void put(std::vector<uint8_t>& b, uint64_t v, int bytes) {
@@ -523,6 +575,11 @@ int pack_init(const pack_config* cfg, pack_ctx** out) {
         p.heldout = (cfg->flags & PACK_FLAG_HELDOUT) ? 1u : 0u;
         p.read_random = (cfg->flags & PACK_FLAG_READ_RANDOM) ? 1u : 0u;
         p.cumulative = (cfg->flags & PACK_FLAG_CUMULATIVE) ? 1u : 0u;
+        p.ramp = cfg->n_ramp ? 1u : 0u;
+        p.tabled = (p.cumulative || p.ramp) ? 1u : 0u;
+        p.world = cfg->world;
+        c->ramp_from.assign(cfg->ramp_from, cfg->ramp_from + cfg->n_ramp);
+        c->ramp_tokens.assign(cfg->ramp_tokens, cfg->ramp_tokens + cfg->n_ramp);
         p.cap_pieces = cfg->n_docs + cfg->n_tokens / cfg->window_tokens;
         if (p.cap_pieces >= 0xFFFFFFFFull) throw InvalError{"too many pieces for 32-bit piece indices"};
 
@@ -541,7 +598,7 @@ int pack_init(const pack_config* cfg, pack_ctx** out) {
         c->arena = static_cast<char*>(mem);
         c->arena_bytes = got;
         carve(*c, c->arena);
-        const size_t pbytes = pin_bytes_for(S);
+        const size_t pbytes = pin_bytes_for(S, cfg->n_ramp);
         void* pin = arena_take(c->device, pbytes, &got, true);
         if (!pin) {
             if (hipHostMalloc(&pin, pbytes, hipHostMallocDefault) != hipSuccess) {
@@ -593,34 +650,98 @@ int pack_cycle(pack_ctx* c, uint32_t cycle, pack_cycle_info* info) {
         uint64_t U = c->cfg.updates_per_cycle;
         const uint64_t* h_sums = nullptr;
         c->pin_off = 0;
-        if (p.cumulative) {
-            // the cycle's schedule from its cumulative quotas, on the device
+        const uint64_t t0 = cycle == 0 ? 0 : c->tokens_next;  // tokens trained before the cycle
+        std::vector<uint32_t> upd_B;
+        std::vector<uint64_t> upd_out0;
+        if (p.tabled) {
+            // per-update counts: the cumulative schedule and/or a batch-size ramp
             uint64_t total = 0;
             for (uint32_t s = 0; s < S; ++s) total += rem[s];
-            const uint64_t most = total / p.B;  // every update takes B windows
+            const uint32_t Bmin = ramp_bmin(*c);
+            const uint64_t most = total / Bmin;  // every update takes at least Bmin windows
             if (most == 0 || U > most) {
                 c->err = "a source cannot supply the cycle's windows";
                 return PACK_E_EXHAUSTED;
             }
             const uint64_t cap = U ? U : most;
-            if (cap > p.cap_pieces / p.B) throw InvalError{"internal: cumulative table bound exceeded"};
-            c->timer.begin(PACK_PHASE_CYCLE, c->st);
-            h2d_staged(*c, p.cum_rem, rem.data(), S);
-            dp::launch_cumulative(p, c->W, U, cap, c->st);
-            c->timer.end(c->st);
-            const uint64_t* h_out = d2h_staged(*c, p.cum_out, S + 1);
-            const uint32_t* h_err = d2h_staged(*c, p.err, 1);
-            sync_staged(*c);
-            if (*h_err & dp::ERR_INTERNAL) throw InvalError{"internal: cumulative schedule"};
-            const uint64_t got = h_out[S];
-            for (uint32_t s = 0; s < S; ++s) taken[s] = h_out[s];
-            c->pin_off = 0;
-            if (got == 0 || (U && got < U)) {
-                c->err = "a source cannot supply the cycle's windows";
-                return PACK_E_EXHAUSTED;
+            if (cap > p.cap_pieces / Bmin) throw InvalError{"internal: per-update table bound exceeded"};
+            std::vector<dp::RampSpan> spans;
+            if (p.ramp) {  // the cycle's updates by ramp piece, from the tokens trained so far
+                const uint64_t K = c->ramp_from.size();
+                uint64_t u = 0, t = t0, slot = 0, out = 0;
+                while (u < cap) {
+                    uint32_t k = (uint32_t)(std::upper_bound(c->ramp_from.begin(), c->ramp_from.end(), t) -
+                                            c->ramp_from.begin()) - 1;
+                    const uint64_t tk = c->ramp_tokens[k], Bk = tk / p.T;
+                    uint64_t n = cap - u;
+                    if (k + 1 < K) n = std::min<uint64_t>(n, (c->ramp_from[k + 1] - t + tk - 1) / tk);
+                    spans.push_back(dp::RampSpan{u, slot, out, (uint32_t)Bk, k});
+                    u += n;
+                    t += n * tk;
+                    slot += n * Bk;
+                    out += n * (Bk / c->cfg.world);
+                }
+                h2d_staged(*c, c->spans, spans.data(), spans.size());
+                dp::launch_ramp_fill(p, c->spans, (uint32_t)spans.size(), cap, c->st);
             }
-            U = got;
+            if (p.cumulative) {  // the cycle's schedule from its cumulative quotas, on the device
+                c->timer.begin(PACK_PHASE_CYCLE, c->st);
+                h2d_staged(*c, p.cum_rem, rem.data(), S);
+                dp::launch_cumulative(p, c->W, U, cap, c->st);
+                c->timer.end(c->st);
+                const uint64_t* h_out = d2h_staged(*c, p.cum_out, S + 1);
+                const uint32_t* h_err = d2h_staged(*c, p.err, 1);
+                sync_staged(*c);
+                if (*h_err & dp::ERR_INTERNAL) throw InvalError{"internal: cumulative schedule"};
+                const uint64_t got = h_out[S];
+                for (uint32_t s = 0; s < S; ++s) taken[s] = h_out[s];
+                c->pin_off = 0;
+                if (got == 0 || (U && got < U)) {
+                    c->err = "a source cannot supply the cycle's windows";
+                    return PACK_E_EXHAUSTED;
+                }
+                U = got;
+            } else {  // the fixed apportionment of each update's batch: per source, the updates it supports
+                uint64_t fit = cap;
+                for (uint32_t s = 0; s < S; ++s) {
+                    uint64_t a = 0;
+                    for (size_t x = 0; x < spans.size(); ++x) {
+                        const uint64_t end = x + 1 < spans.size() ? spans[x + 1].first : cap;
+                        const uint64_t n = c->ramp_n_h[(uint64_t)spans[x].k * S + s], len = end - spans[x].first;
+                        if (n && a + len * n > rem[s]) {
+                            fit = std::min<uint64_t>(fit, spans[x].first + (rem[s] - a) / n);
+                            break;
+                        }
+                        a += len * n;
+                    }
+                }
+                if (fit == 0 || (U && fit < U)) {
+                    c->err = "a source cannot supply the cycle's windows";
+                    return PACK_E_EXHAUSTED;
+                }
+                U = U ? U : fit;
+                for (uint32_t s = 0; s < S; ++s) {
+                    uint64_t a = 0;
+                    for (size_t x = 0; x < spans.size() && spans[x].first < U; ++x) {
+                        const uint64_t end = x + 1 < spans.size() ? std::min<uint64_t>(spans[x + 1].first, U) : U;
+                        a += (end - spans[x].first) * c->ramp_n_h[(uint64_t)spans[x].k * S + s];
+                    }
+                    taken[s] = a;
+                }
+                dp::launch_ramp_fixed_A(p, c->spans, (uint32_t)spans.size(), c->ramp_n, U, c->st);
+            }
             if (U > 0xFFFFFFFFull) throw InvalError{"internal: updates per cycle"};
+            if (p.ramp) {  // host copies of the cycle's batches and this rank's output prefix
+                upd_B.resize(U);
+                upd_out0.assign(U + 1, 0);
+                for (size_t x = 0; x < spans.size(); ++x) {
+                    const uint64_t end = x + 1 < spans.size() ? std::min<uint64_t>(spans[x + 1].first, U) : U;
+                    for (uint64_t u = spans[x].first; u < end; ++u) {
+                        upd_B[u] = spans[x].B;
+                        upd_out0[u + 1] = upd_out0[u] + spans[x].B / c->cfg.world;
+                    }
+                }
+            }
         } else {
             if (U == 0) {
                 U = ~0ull;
@@ -639,21 +760,30 @@ int pack_cycle(pack_ctx* c, uint32_t cycle, pack_cycle_info* info) {
             }
             for (uint32_t s = 0; s < S; ++s) taken[s] = U * c->n_upd[s];
         }
+        uint64_t slots = 0;  // windows of the cycle, all ranks
+        if (p.ramp)
+            for (uint32_t b : upd_B) slots += b;
+        else
+            slots = U * p.B;
         c->U = (uint32_t)U;
         c->cyc_start = start;
         c->taken = taken;
         for (uint32_t s = 0; s < S; ++s) c->cyc_next[s] = start[s] + taken[s];
         c->cycle = cycle;
+        c->tokens_start = t0;
+        c->tokens_next = t0 + slots * p.T;
+        c->upd_B = std::move(upd_B);
+        c->upd_out0 = std::move(upd_out0);
         c->timer.begin(PACK_PHASE_CYCLE, c->st);
         h2d_staged(*c, p.cyc_start, c->cyc_start.data(), S);
-        if (p.cumulative) dp::launch_cum_slots(p, c->U, c->st);
+        if (p.tabled) dp::launch_cum_slots(p, c->U, c->st);
         if (p.read_random) {  // each source's cycle windows in their random read order
             std::vector<uint64_t> ps(S + 1, 0);
             for (uint32_t s = 0; s < S; ++s) ps[s + 1] = ps[s] + taken[s];
             h2d_staged(*c, p.perm_start, ps.data(), S + 1);
             dp::launch_read_order(p, cycle, ps[S], c->st);
         }
-        dp::launch_cycle_sums(p, c->U, c->st);
+        dp::launch_cycle_sums(p, slots, c->st);
         h_sums = d2h_staged(*c, p.cyc_sums, 2);
 
         // plan digest: SHA-256 of a little-endian description of the recipe,
@@ -664,6 +794,15 @@ int pack_cycle(pack_ctx* c, uint32_t cycle, pack_cycle_info* info) {
         msg.insert(msg.end(), magic, magic + 8);
         if (p.read_random) put(msg, 0x444E4152u, 4);  // "RAND": windows read in a random order
         if (p.cumulative) put(msg, 0x554D5543u, 4);   // "CUMU": per-update counts from cumulative quotas
+        if (p.ramp) {                                  // "RAMP": the pieces and the cycle's first token
+            put(msg, 0x504D4152u, 4);
+            put(msg, c->ramp_from.size(), 4);
+            for (size_t k = 0; k < c->ramp_from.size(); ++k) {
+                put(msg, c->ramp_from[k], 8);
+                put(msg, c->ramp_tokens[k], 8);
+            }
+            put(msg, t0, 8);
+        }
         put(msg, p.T, 4);
         put(msg, p.B, 4);
         put(msg, p.seed, 8);
@@ -699,7 +838,7 @@ int pack_cycle(pack_ctx* c, uint32_t cycle, pack_cycle_info* info) {
             info->n_updates = c->U;
             info->real_tokens = sums[0];
             info->learned_tokens = sums[1];
-            info->positions = (uint64_t)c->U * p.B * p.T;
+            info->positions = slots * p.T;
             std::memcpy(info->plan_digest, digest, 32);
             for (uint32_t s = 0; s < S; ++s) {
                 const uint64_t M = c->src_win_start[s + 1] - c->src_win_start[s];
@@ -757,6 +896,7 @@ int pack_batch(pack_ctx* c, uint32_t step, uint32_t n_steps, const pack_out* out
         a.n_steps = n_steps;
         a.rank = c->cfg.rank;
         a.per = c->p.B / c->cfg.world;
+        a.n_out = c->p.ramp ? c->upd_out0[step + n_steps] - c->upd_out0[step] : (uint64_t)n_steps * a.per;
         if ((uint64_t)n_steps * a.per >= (1ull << 31)) {
             c->err = "too many windows in one call";
             return PACK_E_RANGE;
@@ -820,6 +960,7 @@ int pack_batch_packed(pack_ctx* c, uint32_t step, uint32_t n_steps, const pack_o
         a.n_steps = n_steps;
         a.rank = c->cfg.rank;
         a.per = c->p.B / c->cfg.world;
+        a.n_out = c->p.ramp ? c->upd_out0[step + n_steps] - c->upd_out0[step] : (uint64_t)n_steps * a.per;
         if ((uint64_t)n_steps * a.per >= (1ull << 31)) {
             c->err = "too many windows in one call";
             return PACK_E_RANGE;
@@ -849,10 +990,45 @@ int pack_fingerprint(pack_ctx* c, const uint8_t* digests, uint32_t n_batches, ui
         c->err = "digests must be 4-byte aligned";
         return PACK_E_INVAL;
     }
+    if (c->p.ramp) {
+        c->err = "batches of a ramp differ in size: use pack_fingerprint_steps";
+        return PACK_E_STATE;
+    }
     if (n_batches == 0) return PACK_OK;
     try {
         c->timer.begin(PACK_PHASE_FINGERPRINT, c->st);
         dp::launch_batch_fp(digests, c->p.B, n_batches, out, c->st);
+        c->timer.end(c->st);
+        return PACK_OK;
+    } catch (const dp::HipError& e) {
+        return fail_hip(c, e);
+    }
+}
+
+int pack_fingerprint_steps(pack_ctx* c, uint32_t step, uint32_t n_steps, const uint8_t* digests, uint8_t* out) {
+    if (!c) return PACK_E_INVAL;
+    c->err.clear();
+    if (!digests || !out) {
+        c->err = "digests and out are required";
+        return PACK_E_INVAL;
+    }
+    if ((uintptr_t)digests % 4) {
+        c->err = "digests must be 4-byte aligned";
+        return PACK_E_INVAL;
+    }
+    if (c->cycle < 0) {
+        c->err = "no cycle planned";
+        return PACK_E_STATE;
+    }
+    if ((uint64_t)step + n_steps > c->U) {
+        c->err = "step range outside the current cycle";
+        return PACK_E_RANGE;
+    }
+    if (n_steps == 0) return PACK_OK;
+    try {
+        c->timer.begin(PACK_PHASE_FINGERPRINT, c->st);
+        if (c->p.ramp) dp::launch_batch_fp_var(digests, c->p.upd_slot0, step, n_steps, out, c->st);
+        else dp::launch_batch_fp(digests, c->p.B, n_steps, out, c->st);
         c->timer.end(c->st);
         return PACK_OK;
     } catch (const dp::HipError& e) {
@@ -886,9 +1062,17 @@ int pack_inspect(const pack_ctx* cc, uint32_t what, void* host_dst, uint64_t cap
         case PACK_INSPECT_SLOT_SRC: src = p.slot_src; count = p.B; width = out_width = 4; break;
         case PACK_INSPECT_SLOT_K: src = p.slot_k; count = p.B; width = out_width = 4; break;
         case PACK_INSPECT_COUNTS: count = 3; width = out_width = 8; break;
+        case PACK_INSPECT_UPDATE_BATCH:
+            if (c->cycle < 0) {
+                c->err = "no cycle planned";
+                return PACK_E_STATE;
+            }
+            count = c->U;
+            width = out_width = 4;
+            break;
         case PACK_INSPECT_CUM_TAKEN:
-            if (!p.cumulative || c->cycle < 0) {
-                c->err = "no cumulative schedule: the context has no PACK_FLAG_CUMULATIVE or no cycle yet";
+            if (!p.tabled || c->cycle < 0) {
+                c->err = "no per-update schedule: neither PACK_FLAG_CUMULATIVE nor a ramp, or no cycle yet";
                 return PACK_E_STATE;
             }
             src = p.cum_A;
@@ -905,6 +1089,11 @@ int pack_inspect(const pack_ctx* cc, uint32_t what, void* host_dst, uint64_t cap
         if (what == PACK_INSPECT_COUNTS) {
             uint64_t v[3] = {p.n_kept, p.n_pieces, p.n_windows};
             std::memcpy(host_dst, v, sizeof v);
+            return PACK_OK;
+        }
+        if (what == PACK_INSPECT_UPDATE_BATCH) {  // host copy of the cycle's batches
+            uint32_t* o = static_cast<uint32_t*>(host_dst);
+            for (uint64_t u = 0; u < count; ++u) o[u] = p.ramp ? c->upd_B[u] : p.B;
             return PACK_OK;
         }
         if (width == out_width) {

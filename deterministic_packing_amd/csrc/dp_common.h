@@ -87,6 +87,9 @@ struct Plan {
     uint32_t heldout;             // 1: the stream is the held-out documents (validation)
     uint32_t read_random;         // 1: each cycle's windows of a source are read in a random order
     uint32_t cumulative;          // 1: per-update counts from the cycle's cumulative quotas
+    uint32_t ramp;                // 1: batch-size ramp (each update has its own batch)
+    uint32_t tabled;              // cumulative or ramp: windows looked up in per-update slot tables
+    uint32_t world;               // ranks sharing each update's slots
 
     // recipe on device
     uint32_t* gbase;              // [S+1] first group of each source
@@ -151,8 +154,12 @@ struct Plan {
     uint32_t* cum_A;              // [(U_cap+1)·S]
     uint64_t* cum_rem;            // [S] windows each source has left at the cycle start
     uint64_t* cum_out;            // [S+1] windows taken per source, then U
-    uint32_t* cslot_src;          // [U_cap·B]
-    uint32_t* cslot_i;            // [U_cap·B]
+    uint32_t* cslot_src;          // [slots of the cycle ≤ P]
+    uint32_t* cslot_i;            // [slots of the cycle ≤ P]
+    // batch-size ramp: per update of the cycle (U_cap+1 entries)
+    uint32_t* upd_B;              // windows of the update (all ranks)
+    uint64_t* upd_slot0;          // first slot of the update in the cycle (prefix of upd_B)
+    uint64_t* upd_out0;           // first of this rank's output windows (prefix of upd_B/world)
 
     // sizes known after the corresponding step (host copies)
     uint64_t n_kept, n_pieces, n_windows;
@@ -165,17 +172,17 @@ struct Plan {
 // mixture, s and i come from update b's own slot table): window
 // cyc_start[s] + i of its stream, or cyc_start[s] + perm[perm_start[s] + i]
 // with the random read order.
+__device__ inline uint64_t window_of_slot(const Plan& p, uint64_t x) {  // slot x of a tabled cycle
+    const uint32_t s = p.cslot_src[x];
+    uint64_t i = p.cslot_i[x];
+    if (p.read_random) i = p.perm[p.perm_start[s] + i];
+    return p.src_win_start[s] + p.cyc_start[s] + i;
+}
+
 __device__ inline uint64_t window_of(const Plan& p, uint64_t b, uint32_t j) {
-    uint32_t s;
-    uint64_t i;  // the source's i-th window of the cycle
-    if (p.cumulative) {
-        const uint64_t x = b * p.B + j;
-        s = p.cslot_src[x];
-        i = p.cslot_i[x];
-    } else {
-        s = p.slot_src[j];
-        i = b * p.n_upd[s] + p.slot_k[j];
-    }
+    if (p.tabled) return window_of_slot(p, (p.ramp ? p.upd_slot0[b] : b * p.B) + j);
+    const uint32_t s = p.slot_src[j];
+    uint64_t i = b * p.n_upd[s] + p.slot_k[j];  // the source's i-th window of the cycle
     if (p.read_random) i = p.perm[p.perm_start[s] + i];
     return p.src_win_start[s] + p.cyc_start[s] + i;
 }
@@ -249,23 +256,69 @@ void launch_lifting(Plan& p, hipStream_t st);         // jump tables
 void launch_window_count(Plan& p, hipStream_t st);    // src_win_start
 void launch_windows(Plan& p, hipStream_t st);         // win_first, pc_woff, win_real, win_learn
 void launch_mixture_w(Plan& p, uint64_t W, uint32_t* nstart, hipStream_t st);  // n_upd, slot table
+void launch_apportion(Plan& p, uint64_t W, uint32_t B, uint32_t* n_out, hipStream_t st);  // n_s of a batch B
 void launch_zero_u64(uint64_t* a, uint64_t n, hipStream_t st);
 void launch_zero_u32(uint32_t* a, uint64_t n, hipStream_t st);
 void launch_fill_u32(uint32_t* a, uint64_t n, uint32_t v, hipStream_t st);
 uint64_t sort_hist_words(uint64_t n_docs);
 void launch_checks(Plan& p, hipStream_t st);          // order / hash checks
-void launch_cycle_sums(Plan& p, uint32_t U, hipStream_t st);
+void launch_cycle_sums(Plan& p, uint64_t total_slots, hipStream_t st);
 // cumulative mixture of a cycle: the schedule (cum_A, cum_out), then, once the
 // host has accepted U, every update's slot table
 void launch_cumulative(Plan& p, uint64_t W, uint64_t u_cfg, uint64_t cap, hipStream_t st);
 void launch_cum_slots(Plan& p, uint32_t U, hipStream_t st);
+// batch-size ramp: piece spans of a cycle (host-computed) → per-update tables
+struct RampSpan {
+    uint64_t first;  // first update of the span in the cycle
+    uint64_t slot0;  // its first slot
+    uint64_t out0;   // its first output window of this rank
+    uint32_t B;      // windows per update in the span
+    uint32_t k;      // ramp piece
+};
+void launch_ramp_fill(Plan& p, const RampSpan* spans, uint32_t n_spans, uint64_t n_upd, hipStream_t st);
+// fixed apportionment with a ramp: cum_A[u][s] = Σ over spans of whole updates before u · n_s of the span's piece
+void launch_ramp_fixed_A(Plan& p, const RampSpan* spans, uint32_t n_spans, const uint32_t* ramp_n, uint64_t U,
+                         hipStream_t st);
 
 struct EmitArgs {
     uint32_t* tok; int32_t* pos; int32_t* doc; uint8_t* mask;
     int64_t* learned; uint8_t* digests;
-    uint32_t step, n_steps, rank, per;
+    uint32_t step, n_steps, rank, per;  // per: B/world, the largest batch's windows per rank
+    uint64_t n_out;                     // this rank's windows of the call
     int64_t* row_start; int64_t* length; uint32_t bucket;  // padding-free rows only
 };
+
+// Output window w of a call: update a.step + i, this rank's window jj of it,
+// and the rank's windows of that update (B_b/world with a ramp).
+__device__ inline uint64_t out_window(const Plan& p, const EmitArgs& a, uint64_t w, uint32_t* i_out,
+                                      uint32_t* jj_out, uint32_t* per_out) {
+    uint32_t i, jj, per;
+    if (!p.ramp) {
+        i = (uint32_t)(w / a.per);
+        jj = (uint32_t)(w % a.per);
+        per = a.per;
+    } else {
+        const uint64_t e = p.upd_out0[a.step] + w;
+        uint32_t lo = a.step, hi = a.step + a.n_steps;  // upd_out0[lo] ≤ e < upd_out0[hi]
+        while (hi - lo > 1) {
+            const uint32_t mid = (lo + hi) >> 1;
+            if (p.upd_out0[mid] <= e) lo = mid;
+            else hi = mid;
+        }
+        i = lo - a.step;
+        jj = (uint32_t)(e - p.upd_out0[lo]);
+        per = (uint32_t)(p.upd_out0[lo + 1] - p.upd_out0[lo]);
+    }
+    *i_out = i;
+    *jj_out = jj;
+    *per_out = per;
+    return window_of(p, (uint64_t)a.step + i, a.rank * per + jj);
+}
+
+// this rank's windows of update a.step + i
+__device__ inline uint32_t out_per(const Plan& p, const EmitArgs& a, uint32_t i) {
+    return p.ramp ? (uint32_t)(p.upd_out0[a.step + i + 1] - p.upd_out0[a.step + i]) : a.per;
+}
 void launch_emit(const Plan& p, const EmitArgs& a, hipStream_t st);
 void launch_emit_packed(const Plan& p, const EmitArgs& a, hipStream_t st);  // padding-free rows
 void launch_learned(const Plan& p, const EmitArgs& a, hipStream_t st);
@@ -273,6 +326,9 @@ void launch_window_sha(const Plan& p, const EmitArgs& a, hipStream_t st);
 bool emit_sha_fits(const EmitArgs& a);                 // launch_emit_sha applies (one workgroup per CU)
 void launch_emit_sha(const Plan& p, const EmitArgs& a, hipStream_t st);
 void launch_batch_fp(const uint8_t* digests, uint32_t B, uint32_t n_batches, uint8_t* out, hipStream_t st);
+// batches of B_b digests: batch b covers digests [slot0[step+b] − slot0[step], slot0[step+b+1] − slot0[step])
+void launch_batch_fp_var(const uint8_t* digests, const uint64_t* slot0, uint32_t step, uint32_t n_batches,
+                         uint8_t* out, hipStream_t st);
 void launch_sha_bytes(const uint8_t* msg, uint64_t len, uint8_t* out, hipStream_t st);
 
 // scans (scan.hip)

@@ -36,8 +36,8 @@ __global__ __launch_bounds__(EB) void k_emit(Plan p, EmitArgs a) {
     __shared__ uint64_t s_src[ECAP];
 
     const uint32_t widx = blockIdx.x;                  // window of this launch
-    const uint32_t i = widx / a.per, jj = widx % a.per;
-    const uint64_t gw = window_of(p, (uint64_t)a.step + i, a.rank * a.per + jj);
+    uint32_t i, jj, per_i;
+    const uint64_t gw = out_window(p, a, widx, &i, &jj, &per_i);
     const uint32_t q0 = p.win_first[gw], q1 = p.win_first[gw + 1];
     const uint32_t np = q1 - q0;
     const uint32_t real = p.win_real[gw];
@@ -151,10 +151,11 @@ __global__ __launch_bounds__(256) void k_packed_starts(Plan p, EmitArgs a) {
     __shared__ uint64_t part[256 / WAVE];
     const uint32_t i = blockIdx.x, lane = threadIdx.x % WAVE, wid = threadIdx.x / WAVE;
     int64_t* rs = a.row_start + (uint64_t)i * (a.per + 1);
+    const uint32_t per = out_per(p, a, i);  // this update's windows of the rank (≤ a.per, the row pitch)
     uint64_t carry = 0;
-    for (uint32_t c0 = 0; c0 < a.per; c0 += 256) {
+    for (uint32_t c0 = 0; c0 < per; c0 += 256) {
         const uint32_t jj = c0 + threadIdx.x;
-        const uint64_t v = jj < a.per ? p.win_real[window_of(p, (uint64_t)a.step + i, a.rank * a.per + jj)] : 0;
+        const uint64_t v = jj < per ? p.win_real[window_of(p, (uint64_t)a.step + i, a.rank * per + jj)] : 0;
         uint64_t x = v;  // inclusive scan in the wave
 #pragma unroll
         for (int o = 1; o < WAVE; o <<= 1) {
@@ -165,15 +166,15 @@ __global__ __launch_bounds__(256) void k_packed_starts(Plan p, EmitArgs a) {
         __syncthreads();
         uint64_t before = carry;
         for (uint32_t w = 0; w < wid; ++w) before += part[w];
-        if (jj < a.per) rs[jj] = (int64_t)(before + x - v);
+        if (jj < per) rs[jj] = (int64_t)(before + x - v);
         uint64_t chunk = 0;
         for (uint32_t w = 0; w < 256 / WAVE; ++w) chunk += part[w];
         __syncthreads();
         carry += chunk;
     }
+    for (uint32_t jj = per + threadIdx.x; jj <= a.per; jj += blockDim.x) rs[jj] = (int64_t)carry;
     if (threadIdx.x == 0) {
-        rs[a.per] = (int64_t)carry;
-        const uint64_t cap = (uint64_t)a.per * p.T;
+        const uint64_t cap = (uint64_t)per * p.T;
         uint64_t L = a.bucket > 1 ? (carry + a.bucket - 1) / a.bucket * a.bucket : carry;
         a.length[i] = (int64_t)(L < cap ? L : cap);
     }
@@ -198,7 +199,8 @@ __global__ __launch_bounds__(256) void k_learned(Plan p, EmitArgs a) {
     __shared__ uint64_t part[256 / WAVE];
     const uint64_t b = (uint64_t)a.step + blockIdx.x;
     uint64_t s = 0;
-    for (uint32_t j = threadIdx.x; j < p.B; j += blockDim.x) s += p.win_learn[window_of(p, b, j)];
+    const uint32_t Bb = p.ramp ? p.upd_B[b] : p.B;
+    for (uint32_t j = threadIdx.x; j < Bb; j += blockDim.x) s += p.win_learn[window_of(p, b, j)];
     s = wave_sum_u64(s);
     if ((threadIdx.x & 63) == 0) part[threadIdx.x / WAVE] = s;
     __syncthreads();
@@ -212,13 +214,13 @@ __global__ __launch_bounds__(256) void k_learned(Plan p, EmitArgs a) {
 }  // namespace
 
 void launch_emit(const Plan& p, const EmitArgs& a, hipStream_t st) {
-    const uint64_t windows = (uint64_t)a.n_steps * a.per;
+    const uint64_t windows = a.n_out;
     hipLaunchKernelGGL(k_emit<false>, dim3((uint32_t)windows), dim3(EB), 0, st, p, a);
     DP_HIP(hipGetLastError());
 }
 
 void launch_emit_packed(const Plan& p, const EmitArgs& a, hipStream_t st) {
-    const uint64_t windows = (uint64_t)a.n_steps * a.per;
+    const uint64_t windows = a.n_out;
     hipLaunchKernelGGL(k_packed_starts, dim3(a.n_steps), dim3(256), 0, st, p, a);
     hipLaunchKernelGGL(k_emit<true>, dim3((uint32_t)windows), dim3(EB), 0, st, p, a);
     hipLaunchKernelGGL(k_packed_pad, dim3(a.n_steps), dim3(256), 0, st, p, a);

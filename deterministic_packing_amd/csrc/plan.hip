@@ -326,7 +326,8 @@ __device__ inline uint64_t div128(uint64_t hi, uint64_t lo, uint64_t W, uint64_t
     return q;
 }
 
-__global__ __launch_bounds__(1024) void k_apportion(Plan p, uint64_t W, uint32_t* nstart) {
+__global__ __launch_bounds__(1024) void k_apportion(Plan p, uint64_t W, uint32_t B, uint32_t* n_out,
+                                                    uint32_t* nstart) {
     extern __shared__ uint64_t sh[];  // rem[S] then n[S] (32-bit)
     uint64_t* rem = sh;
     uint32_t* nn = reinterpret_cast<uint32_t*>(sh + p.S);
@@ -335,7 +336,7 @@ __global__ __launch_bounds__(1024) void k_apportion(Plan p, uint64_t W, uint32_t
     __syncthreads();
     for (uint32_t s = threadIdx.x; s < p.S; s += blockDim.x) {
         const uint64_t w = p.weight[s];
-        const uint64_t hi = __umul64hi((uint64_t)p.B, w), lo = (uint64_t)p.B * w;
+        const uint64_t hi = __umul64hi((uint64_t)B, w), lo = (uint64_t)B * w;
         uint64_t r;
         const uint64_t n = div128(hi, lo, W, &r);  // hi < W since B·w < B·W
         rem[s] = r;
@@ -343,19 +344,19 @@ __global__ __launch_bounds__(1024) void k_apportion(Plan p, uint64_t W, uint32_t
         atomicAdd((unsigned long long*)&given_s, (unsigned long long)n);
     }
     __syncthreads();
-    const uint64_t left = (uint64_t)p.B - given_s;
+    const uint64_t left = (uint64_t)B - given_s;
     for (uint32_t s = threadIdx.x; s < p.S; s += blockDim.x) {
         uint64_t rank = 0;
         for (uint32_t t = 0; t < p.S; ++t)
             rank += (rem[t] > rem[s] || (rem[t] == rem[s] && t < s)) ? 1 : 0;
-        p.n_upd[s] = (uint32_t)(nn[s] + (rank < left ? 1 : 0));
+        n_out[s] = (uint32_t)(nn[s] + (rank < left ? 1 : 0));
     }
     __syncthreads();
-    if (threadIdx.x == 0) {
+    if (threadIdx.x == 0 && nstart) {
         uint32_t run = 0;
         for (uint32_t s = 0; s < p.S; ++s) {
             nstart[s] = run;
-            run += p.n_upd[s];
+            run += n_out[s];
         }
         nstart[p.S] = run;
     }
@@ -428,18 +429,27 @@ __global__ __launch_bounds__(ONE_WAVE ? WAVE : CUM_MAX_S) void k_cumulative(Plan
     const uint32_t s = threadIdx.x, nw = blockDim.x / WAVE;
     const bool on = s < p.S;
     const uint64_t w = on ? p.weight[s] : 0;
-    const uint64_t bw_hi = __umul64hi((uint64_t)p.B, w), bw = (uint64_t)p.B * w;
-    uint64_t rB = 0;
-    const uint64_t qB = w ? div128(bw_hi, bw, W, &rB) : 0;  // bw_hi < W since B·w < 2^20·W
-    const bool step_ge_W = bw_hi != 0 || bw >= W;           // fl grows every update
+    // the update's step of the quota, B_u·w_s = qB·W + rB (recomputed when the batch changes)
+    uint64_t bw_hi = 0, bw = 0, rB = 0, qB = 0, QB = 0;
+    bool step_ge_W = false;  // fl grows every update
+    uint32_t Bu = 0;
     const uint64_t rem = on ? p.cum_rem[s] : ~0ull;
     uint64_t fl = 0, rm = 0, A = 0, U = 0, due = 0;
     bool bad = false;
     if (on) p.cum_A[s] = 0;
     // ONE_WAVE: Σ_s (fl − A)⁺ = Σ qB + #crossed − #ahead + #(qB = 0, not crossed, ahead), where
     // ahead = (A = fl + 1) before the update: every term is a ballot count
-    const uint64_t QB = ONE_WAVE ? wave_sum_u64(qB) : 0;
     for (uint64_t u = 0; u < cap; ++u) {
+        const uint32_t Bn = p.ramp ? p.upd_B[u] : p.B;
+        if (Bn != Bu) {  // uniform: the same batch for every source
+            Bu = Bn;
+            bw_hi = __umul64hi((uint64_t)Bu, w);
+            bw = (uint64_t)Bu * w;
+            rB = 0;
+            qB = w ? div128(bw_hi, bw, W, &rB) : 0;  // bw_hi < W since B·w < 2^20·W
+            step_ge_W = bw_hi != 0 || bw >= W;
+            if (ONE_WAVE) QB = wave_sum_u64(qB);
+        }
         bool moved = false, crossed = false;
         const bool ahead = A > fl;
         if (w) {  // q ← q + B·w_s/W
@@ -458,11 +468,32 @@ __global__ __launch_bounds__(ONE_WAVE ? WAVE : CUM_MAX_S) void k_cumulative(Plan
         const uint64_t m = fl > A ? fl - A : 0;
         const bool cand = w != 0 && rm != 0 && A <= fl;
         if (w && (moved || u == 0)) {  // the formula holds for rm = 0 too: δ of window fl+1
-            if (step_ge_W) {
-                due = u + 1;
+            if (!p.ramp) {
+                if (step_ge_W) {
+                    due = u + 1;
+                } else {
+                    const uint64_t gap = W - rm;
+                    due = u + gap / bw + (gap % bw ? 1 : 0);
+                }
             } else {
-                const uint64_t gap = W - rm;
-                due = u + gap / bw + (gap % bw ? 1 : 0);
+                // the first v > u with H(v+1)·w_s ≥ (fl+1)·W, H = upd_slot0 (seats before an
+                // update); cap when none within the schedule
+                const unsigned __int128 goal = (unsigned __int128)(fl + 1) * W;
+                auto reached = [&](uint64_t v) {  // v = cap stands for "not within the schedule"
+                    return v >= cap || (unsigned __int128)p.upd_slot0[v + 1] * w >= goal;
+                };
+                uint64_t lo = u, hi = u + 1, step = 1;  // not reached(u): fl is the quota's floor after u
+                while (!reached(hi)) {                  // gallop: ends at cap at the latest
+                    lo = hi;
+                    step *= 2;
+                    hi = lo + step < cap ? lo + step : cap;
+                }
+                while (hi - lo > 1) {  // reached(hi), not reached(lo)
+                    const uint64_t mid = lo + (hi - lo) / 2;
+                    if (reached(mid)) hi = mid;
+                    else lo = mid;
+                }
+                due = hi;
             }
         }
         const uint64_t k = cand ? due : ~0ull;
@@ -488,11 +519,11 @@ __global__ __launch_bounds__(ONE_WAVE ? WAVE : CUM_MAX_S) void k_cumulative(Plan
                 nc += part[1][i];
             }
         }
-        if (sm > p.B || nc < p.B - sm) {  // the schedule's guarantee failed
+        if (sm > Bu || nc < Bu - sm) {  // the schedule's guarantee failed
             bad = true;
             break;
         }
-        const uint64_t R = p.B - sm;
+        const uint64_t R = Bu - sm;
         uint64_t rank = 0;
         if (ONE_WAVE) {
             const uint32_t klo = (uint32_t)k, khi = (uint32_t)(k >> 32);
@@ -545,6 +576,8 @@ __global__ __launch_bounds__(256) void k_cum_slots(Plan p) {
     uint32_t* ns = csh + S;
     uint32_t* base = csh + 2 * S + 1;
     const uint64_t u = blockIdx.x;
+    const uint32_t Bu = p.ramp ? p.upd_B[u] : p.B;
+    const uint64_t x0 = p.ramp ? p.upd_slot0[u] : u * p.B;  // the update's first slot
     for (uint32_t s = threadIdx.x; s < S; s += blockDim.x) {
         const uint32_t a0 = p.cum_A[u * S + s], a1 = p.cum_A[(u + 1) * S + s];
         n[s] = a1 - a0;
@@ -558,16 +591,16 @@ __global__ __launch_bounds__(256) void k_cum_slots(Plan p) {
             run += n[s];
         }
         ns[S] = run;
-        if (run != p.B) atomicOr(p.err, ERR_INTERNAL);
+        if (run != Bu) atomicOr(p.err, ERR_INTERNAL);
     }
     __syncthreads();
-    if (ns[S] != p.B) return;
-    for (uint32_t t = threadIdx.x; t < p.B; t += blockDim.x) {
+    if (ns[S] != Bu) return;
+    for (uint32_t t = threadIdx.x; t < Bu; t += blockDim.x) {
         uint32_t s, k;
         const uint64_t pos = slot_item(n, ns, S, t, &s, &k);
-        if (pos < p.B) {
-            p.cslot_src[u * p.B + pos] = s;
-            p.cslot_i[u * p.B + pos] = base[s] + k;
+        if (pos < Bu) {
+            p.cslot_src[x0 + pos] = s;
+            p.cslot_i[x0 + pos] = base[s] + k;
         } else {
             atomicOr(p.err, ERR_INTERNAL);
         }
@@ -611,11 +644,50 @@ __global__ __launch_bounds__(256) void k_cycle_sums(Plan p, uint64_t total) {
     uint64_t real = 0, learn = 0;
     for (uint64_t idx = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
          idx += (uint64_t)gridDim.x * blockDim.x) {
-        const uint64_t gw = window_of(p, idx / p.B, (uint32_t)(idx % p.B));
+        const uint64_t gw = p.tabled ? window_of_slot(p, idx) : window_of(p, idx / p.B, (uint32_t)(idx % p.B));
         real += p.win_real[gw];
         learn += p.win_learn[gw];
     }
     block_add2(real, learn, p.cyc_sums);
+}
+
+// ------------------------------------------------------------------ batch-size ramp
+// Update u of the cycle lies in the last span whose first update is ≤ u; its
+// batch, first slot and first output window follow in closed form.
+__device__ inline uint32_t span_of(const RampSpan* sp, uint32_t n, uint64_t u) {
+    uint32_t lo = 0, hi = n;  // sp[lo].first ≤ u < sp[hi].first
+    while (hi - lo > 1) {
+        const uint32_t mid = (lo + hi) >> 1;
+        if (sp[mid].first <= u) lo = mid;
+        else hi = mid;
+    }
+    return lo;
+}
+
+__global__ __launch_bounds__(256) void k_ramp_fill(Plan p, const RampSpan* sp, uint32_t n_spans, uint64_t n_upd) {
+    const uint64_t u = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (u > n_upd) return;
+    const RampSpan r = sp[span_of(sp, n_spans, u)];
+    const uint64_t d = u - r.first;
+    if (u < n_upd) p.upd_B[u] = r.B;
+    p.upd_slot0[u] = r.slot0 + d * r.B;
+    p.upd_out0[u] = r.out0 + d * (r.B / p.world);
+}
+
+// cum_A[u][s] = Σ over spans of the updates before u in the span · the span piece's n_s
+__global__ __launch_bounds__(256) void k_ramp_fixed_A(Plan p, const RampSpan* sp, uint32_t n_spans,
+                                                      const uint32_t* ramp_n, uint64_t U) {
+    const uint64_t x = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (x >= (U + 1) * p.S) return;
+    const uint64_t u = x / p.S;
+    const uint32_t s = (uint32_t)(x % p.S);
+    uint64_t a = 0;
+    for (uint32_t k = 0; k < n_spans && sp[k].first < u; ++k) {
+        const uint64_t end = k + 1 < n_spans ? sp[k + 1].first : ~0ull;
+        const uint64_t upto = u < end ? u : end;
+        a += (upto - sp[k].first) * ramp_n[(uint64_t)sp[k].k * p.S + s];
+    }
+    p.cum_A[x] = (uint32_t)a;
 }
 
 inline uint32_t blocks_for(uint64_t n, uint32_t b = 256) { return (uint32_t)((n + b - 1) / b); }
@@ -681,7 +753,7 @@ void launch_windows(Plan& p, hipStream_t st) {
 }
 
 void launch_mixture_w(Plan& p, uint64_t W, uint32_t* nstart, hipStream_t st) {
-    hipLaunchKernelGGL(k_apportion, dim3(1), dim3(1024), (size_t)p.S * 12, st, p, W, nstart);
+    hipLaunchKernelGGL(k_apportion, dim3(1), dim3(1024), (size_t)p.S * 12, st, p, W, p.B, p.n_upd, nstart);
     hipLaunchKernelGGL(k_slots, dim3(blocks_for(p.B)), dim3(256), 0, st, p, (const uint32_t*)nstart);
     DP_HIP(hipGetLastError());
 }
@@ -702,6 +774,23 @@ void launch_cum_slots(Plan& p, uint32_t U, hipStream_t st) {
     DP_HIP(hipGetLastError());
 }
 
+void launch_apportion(Plan& p, uint64_t W, uint32_t B, uint32_t* n_out, hipStream_t st) {
+    hipLaunchKernelGGL(k_apportion, dim3(1), dim3(1024), (size_t)p.S * 12, st, p, W, B, n_out, (uint32_t*)nullptr);
+    DP_HIP(hipGetLastError());
+}
+
+void launch_ramp_fill(Plan& p, const RampSpan* spans, uint32_t n_spans, uint64_t n_upd, hipStream_t st) {
+    hipLaunchKernelGGL(k_ramp_fill, dim3(blocks_for(n_upd + 1)), dim3(256), 0, st, p, spans, n_spans, n_upd);
+    DP_HIP(hipGetLastError());
+}
+
+void launch_ramp_fixed_A(Plan& p, const RampSpan* spans, uint32_t n_spans, const uint32_t* ramp_n, uint64_t U,
+                         hipStream_t st) {
+    hipLaunchKernelGGL(k_ramp_fixed_A, dim3(blocks_for((U + 1) * p.S)), dim3(256), 0, st, p, spans, n_spans, ramp_n,
+                       U);
+    DP_HIP(hipGetLastError());
+}
+
 void launch_checks(Plan& p, hipStream_t st) {
     hipLaunchKernelGGL(k_zero_u64, dim3(1), dim3(256), 0, st, p.checks, (uint64_t)2);
     const uint64_t n = p.n_docs > p.n_kept ? p.n_docs : p.n_kept;
@@ -709,9 +798,8 @@ void launch_checks(Plan& p, hipStream_t st) {
     DP_HIP(hipGetLastError());
 }
 
-void launch_cycle_sums(Plan& p, uint32_t U, hipStream_t st) {
+void launch_cycle_sums(Plan& p, uint64_t total, hipStream_t st) {  // total: the cycle's slots
     hipLaunchKernelGGL(k_zero_u64, dim3(1), dim3(256), 0, st, p.cyc_sums, (uint64_t)2);
-    const uint64_t total = (uint64_t)U * p.B;
     if (total)
         hipLaunchKernelGGL(k_cycle_sums, dim3(std::min<uint32_t>(blocks_for(total), 512)), dim3(256), 0, st, p, total);
     DP_HIP(hipGetLastError());

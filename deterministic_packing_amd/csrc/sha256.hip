@@ -429,8 +429,8 @@ __device__ __forceinline__ void emit_lanes(const Plan& p, const EmitArgs& a, uin
                                            uint32_t lane, uint32_t* prog) {
     const bool valid = w0 + lane < n_windows;
     const uint64_t w = valid ? w0 + lane : n_windows - 1;  // lanes past the end mirror the last window
-    const uint32_t i = (uint32_t)(w / a.per), jj = (uint32_t)(w % a.per);
-    const uint64_t gw = window_of(p, (uint64_t)a.step + i, a.rank * a.per + jj);
+    uint32_t i, jj, per_i;
+    const uint64_t gw = out_window(p, a, w, &i, &jj, &per_i);
     const uint32_t q0 = p.win_first[gw], q1 = p.win_first[gw + 1], real = p.win_real[gw];
     const uint32_t T = p.T, per = T / 16, nblk = 13 * (T / 64);
     ECursor c;
@@ -513,6 +513,15 @@ __global__ __launch_bounds__(64) void k_batch_fp(const uint8_t* digests, uint32_
     sha_bytes(digests + 32ull * B * b, 32ull * B, out + 32ull * b);
 }
 
+// batch b of a ramped cycle: its B_b digests, from slot slot0[step+b] − slot0[step] on
+__global__ __launch_bounds__(64) void k_batch_fp_var(const uint8_t* digests, const uint64_t* slot0, uint32_t step,
+                                                     uint32_t n, uint8_t* out) {
+    const uint32_t b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= n) return;
+    const uint64_t x0 = slot0[step + b] - slot0[step], x1 = slot0[step + b + 1] - slot0[step];
+    sha_bytes(digests + 32ull * x0, 32ull * (x1 - x0), out + 32ull * b);
+}
+
 __global__ void k_sha_bytes(const uint8_t* msg, uint64_t len, uint8_t* out) {
     if (threadIdx.x == 0 && blockIdx.x == 0) sha_bytes(msg, len, out);
 }
@@ -520,7 +529,7 @@ __global__ void k_sha_bytes(const uint8_t* msg, uint64_t len, uint8_t* out) {
 }  // namespace
 
 void launch_window_sha(const Plan& p, const EmitArgs& a, hipStream_t st) {
-    const uint64_t n = (uint64_t)a.n_steps * a.per;
+    const uint64_t n = a.n_out;
     const uint64_t waves = (n + 63) / 64;
     const uint32_t groups = (uint32_t)((waves + SWAVES - 1) / SWAVES);
     if (waves <= 1024)  // no more waves than MI355X SIMDs (256 CUs x 4): one per SIMD
@@ -531,18 +540,25 @@ void launch_window_sha(const Plan& p, const EmitArgs& a, hipStream_t st) {
 }
 
 bool emit_sha_fits(const EmitArgs& a) {
-    const uint64_t n = (uint64_t)a.n_steps * a.per;
+    const uint64_t n = a.n_out;
     return (n + 255) / 256 <= 256;  // one workgroup (four hashing waves) per CU of MI355X's 256
 }
 
 void launch_emit_sha(const Plan& p, const EmitArgs& a, hipStream_t st) {
-    const uint64_t n = (uint64_t)a.n_steps * a.per;
+    const uint64_t n = a.n_out;
     hipLaunchKernelGGL(k_emit_sha, dim3((uint32_t)((n + 255) / 256)), dim3(64 * FWAVES), 0, st, p, a, n);
     DP_HIP(hipGetLastError());
 }
 
 void launch_batch_fp(const uint8_t* digests, uint32_t B, uint32_t n_batches, uint8_t* out, hipStream_t st) {
     hipLaunchKernelGGL(k_batch_fp, dim3((n_batches + 63) / 64), dim3(64), 0, st, digests, B, n_batches, out);
+    DP_HIP(hipGetLastError());
+}
+
+void launch_batch_fp_var(const uint8_t* digests, const uint64_t* slot0, uint32_t step, uint32_t n_batches,
+                         uint8_t* out, hipStream_t st) {
+    hipLaunchKernelGGL(k_batch_fp_var, dim3((n_batches + 63) / 64), dim3(64), 0, st, digests, slot0, step, n_batches,
+                       out);
     DP_HIP(hipGetLastError());
 }
 

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define DPACK_ABI_VERSION 1u
+#define DPACK_ABI_VERSION 2u
 
 enum {
     PACK_OK = 0,
@@ -133,7 +133,21 @@ typedef struct pack_timings {
  * monotone with doc_offsets[n_docs] ≤ n_tokens; 1 ≤ n_sources ≤ 4096;
  * source < n_sources; stratum < n_strata[source]; Σ n_strata ≤ 65536;
  * Σ share_weight in [1, 2^64); holdout_bp ≤ 10000; T a multiple of 64 in
- * [64, 2^20]; 1 ≤ B ≤ 2^20; world ≥ 1 divides B; rank < world. */
+ * [64, 2^20]; 1 ≤ B ≤ 2^20; world ≥ 1 divides B; rank < world; with a
+ * ramp: n_ramp ≤ 4096, ramp_from[0] = 0 and rising, every ramp_tokens[k] a
+ * multiple of T whose batch B_k = ramp_tokens[k]/T world divides, and B the
+ * largest B_k.
+ *
+ * Batch-size ramp (n_ramp > 0).  NeuronSpark-Trainer README, Training,
+ * Updates: tokens_per_update is one number or pieces by the tokens trained,
+ * and an update's batch is read at the data line's token count (the cycle's
+ * start token plus its updates so far).  Reading taken: the count is the
+ * positions of every earlier update (B_b·T each), from 0 at cycle 0 and
+ * across cycles; an update starting at count t has B_k = ramp_tokens[k]/T
+ * windows for the last k with ramp_from[k] ≤ t.  Each update's windows come
+ * from the apportionment of its own batch (or, with PACK_FLAG_CUMULATIVE,
+ * from quotas at the running count of windows), in the Sainte-Laguë order of
+ * its own counts; a cycle still never splits an update. */
 typedef struct pack_config {
     uint32_t abi_version;          /* DPACK_ABI_VERSION */
     uint32_t flags;                /* 0 or an or of PACK_FLAG_TIMING, _WRAP, _HELDOUT, _READ_RANDOM, _CUMULATIVE */
@@ -155,6 +169,9 @@ typedef struct pack_config {
     uint64_t seed;                 /* shuffle seed */
     uint32_t rank, world;          /* this context emits slots [rank·B/world, (rank+1)·B/world) */
     void *stream;                  /* hipStream_t for all work; NULL = default stream */
+    uint32_t n_ramp;               /* 0: every update has B windows; else the pieces below */
+    const uint64_t *ramp_from;     /* host [n_ramp]: tokens trained at which piece k starts */
+    const uint64_t *ramp_tokens;   /* host [n_ramp]: tokens per update (B_k·T) within piece k */
 } pack_config;
 
 /* pack_init — build the plan of a corpus (hash and hold-out of every
@@ -175,15 +192,15 @@ typedef struct pack_cycle_info {
     uint32_t n_updates;            /* U of this cycle */
     uint64_t real_tokens;          /* non-padding positions in the cycle (all ranks) */
     uint64_t learned_tokens;       /* positions with loss mask 1 in the cycle (all ranks) */
-    uint64_t positions;            /* U·B·T */
+    uint64_t positions;            /* U·B·T (with a ramp: Σ B_b·T) */
     uint8_t plan_digest[32];       /* SHA-256 identifying recipe, stream sizes, cycle start and order */
     uint64_t *windows_start;       /* first window of the cycle in each source's stream */
-    uint64_t *windows_taken;       /* U·n_s (with PACK_FLAG_CUMULATIVE: A_s(U)) */
+    uint64_t *windows_taken;       /* U·n_s (with PACK_FLAG_CUMULATIVE or a ramp: A_s(U)) */
     uint64_t *windows_remaining;   /* windows left after the cycle */
     uint64_t *kept_docs, *kept_tokens, *held_docs, *held_tokens;
     uint32_t *per_update;          /* n_s: windows of each source in every update (the fixed
-                                    * apportionment; with PACK_FLAG_CUMULATIVE the counts vary per
-                                    * update: PACK_INSPECT_CUM_TAKEN) */
+                                    * apportionment of B; with PACK_FLAG_CUMULATIVE or a ramp the
+                                    * counts vary per update: PACK_INSPECT_CUM_TAKEN) */
 } pack_cycle_info;
 
 /* pack_cycle — plan cycle `cycle` (must be 0, then 1, 2, …): U updates, each
@@ -198,7 +215,9 @@ typedef struct pack_cycle_info {
 int pack_cycle(pack_ctx *ctx, uint32_t cycle, pack_cycle_info *info);
 
 /* Outputs of pack_batch: device buffers owned by the caller, each laid out
- * [n_steps][B/world][T] in slot order (row-major, contiguous). */
+ * [n_steps][B/world][T] in slot order (row-major, contiguous); with a
+ * batch-size ramp update b contributes B_b/world windows, update after update
+ * ([Σ B_b/world][T], PACK_INSPECT_UPDATE_BATCH gives each B_b). */
 typedef struct pack_out {
     uint32_t *tokens;    /* token id, pad_token at padding */
     int32_t *pos;        /* offset within the piece (0 starts each piece), 0 at padding */
@@ -223,12 +242,14 @@ int pack_batch(pack_ctx *ctx, uint32_t step, uint32_t n_steps, const pack_out *o
  * Device arrays, all required but learned: */
 typedef struct pack_out_packed {
     uint32_t *tokens;    /* [n_steps][B/world · T]: update i's row; window jj's real positions
-                            (as in pack_batch) at row_start[i][jj] .. row_start[i][jj+1] */
+                            (as in pack_batch) at row_start[i][jj] .. row_start[i][jj+1]; with a
+                            ramp rows stay B/world·T apart (B the largest batch) */
     int32_t *pos;        /* same layout; 0 starts each piece */
     int32_t *doc;
     uint8_t *mask;
-    int64_t *row_start;  /* [n_steps][B/world + 1]: where each window begins; [B/world] = the total */
-    int64_t *length;     /* [n_steps]: the total rounded up to a multiple of bucket, at most B/world · T;
+    int64_t *row_start;  /* [n_steps][B/world + 1]: where each window begins; [B/world] = the total
+                            (with a ramp entries from [B_i/world] on all hold the total) */
+    int64_t *length;     /* [n_steps]: the total rounded up to a multiple of bucket, at most B_i/world · T;
                             positions from the total to the length are padding, later ones are not written */
     int64_t *learned;    /* [n_steps] or NULL: as in pack_batch */
     uint32_t bucket;     /* the rounding multiple (256 in the pages); 0 or 1: none */
@@ -244,8 +265,20 @@ int pack_batch_packed(pack_ctx *ctx, uint32_t step, uint32_t n_steps, const pack
  * its B window digests (B·32 bytes, slot order) from the device array
  * digests [n_batches][B][32], into the device array out [n_batches][32].
  * For world > 1 the caller first gathers every rank's digests in rank order.
- * Asynchronous on the context's stream.  Errors: PACK_E_INVAL (NULL), PACK_E_HIP. */
+ * Asynchronous on the context's stream.  Errors: PACK_E_INVAL (NULL),
+ * PACK_E_STATE (a context with a batch-size ramp: use pack_fingerprint_steps),
+ * PACK_E_HIP. */
 int pack_fingerprint(pack_ctx *ctx, const uint8_t *digests, uint32_t n_batches, uint8_t *out);
+
+/* pack_fingerprint_steps — fingerprints of updates [step, step+n_steps) of
+ * the current cycle, each SHA-256 over its own B_b window digests: digests is
+ * the device array of those updates' digests one after another (Σ B_b·32
+ * bytes; every rank's slice of an update in rank order), out [n_steps][32].
+ * Zephon blog post, the 16→8/32/64-GPU resume section: every global batch's
+ * SHA-256 equal byte for byte.  Any context (without a ramp it equals
+ * pack_fingerprint).  Asynchronous.  Errors: PACK_E_INVAL (NULL),
+ * PACK_E_STATE (no cycle), PACK_E_RANGE, PACK_E_HIP. */
+int pack_fingerprint_steps(pack_ctx *ctx, uint32_t step, uint32_t n_steps, const uint8_t *digests, uint8_t *out);
 
 /* Plan arrays that pack_inspect copies to the host (for checking the plan
  * against an independent implementation).  Types and lengths: */
@@ -267,9 +300,10 @@ enum {
     PACK_INSPECT_SLOT_SRC = 15,     /* uint32 [B] */
     PACK_INSPECT_SLOT_K = 16,       /* uint32 [B] */
     PACK_INSPECT_COUNTS = 17,       /* uint64 [3]: n_kept, n_pieces, n_windows */
-    PACK_INSPECT_CUM_TAKEN = 18,    /* uint32 [(U+1)·n_sources]: with PACK_FLAG_CUMULATIVE, windows of
-                                     * each source taken before each update of the current cycle
-                                     * (row U: the cycle's totals); PACK_E_STATE otherwise */
+    PACK_INSPECT_CUM_TAKEN = 18,    /* uint32 [(U+1)·n_sources]: with PACK_FLAG_CUMULATIVE or a ramp,
+                                     * windows of each source taken before each update of the current
+                                     * cycle (row U: the cycle's totals); PACK_E_STATE otherwise */
+    PACK_INSPECT_UPDATE_BATCH = 19, /* uint32 [U]: windows (all ranks) of each update of the current cycle */
 };
 
 /* pack_inspect — copy plan array `what` to host memory (synchronous).

@@ -106,9 +106,29 @@ def test_cumulative_limits_on_host(lib):
     assert "2^28" in lib.pack_last_error(None).decode()
 
 
+@pytest.mark.parametrize("frm,tok,B,world,what", [
+    ([0, 100], [128 * 2, 100], 2, 1, "multiple of T"),
+    ([5], [256], 2, 1, "start at 0"),
+    ([0, 0], [256, 512], 4, 1, "start at 0"),
+    ([0, 10], [256, 512], 8, 1, "largest"),
+    ([0, 10], [128 * 3, 128 * 4], 4, 2, "divide"),
+])
+def test_ramp_config_checked_on_host(lib, frm, tok, B, world, what):
+    """A batch-size ramp fails fast at init: pieces must start at 0 and rise, hold
+    whole windows, fit every rank count, and B must be the largest batch."""
+    import numpy as np
+    fa, ta = np.array(frm, np.uint64), np.array(tok, np.uint64)
+    cfg, keep = _cfg(global_batch=B, world=world)
+    cfg.n_ramp, cfg.ramp_from, cfg.ramp_tokens = len(frm), fa.ctypes.data, ta.ctypes.data
+    ctx = C.c_void_p()
+    assert lib.pack_init(C.byref(cfg), C.byref(ctx)) == dp.PACK_E_INVAL
+    assert what in lib.pack_last_error(None).decode()
+
+
 def test_null_arguments_are_errors(lib):
     assert lib.pack_init(None, None) == dp.PACK_E_INVAL
     assert lib.pack_cycle(None, 0, None) == dp.PACK_E_INVAL
     assert lib.pack_batch(None, 0, 1, None) == dp.PACK_E_INVAL
     assert lib.pack_batch_packed(None, 0, 1, None) == dp.PACK_E_INVAL
+    assert lib.pack_fingerprint_steps(None, 0, 1, None, None) == dp.PACK_E_INVAL
     lib.pack_destroy(None)

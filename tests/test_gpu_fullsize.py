@@ -28,6 +28,8 @@ def _setup(name):
         mode, _, base = name.partition("-") if "-" in name else ("", "", name)
         c = make_corpus(base).replace(wrap=mode == "wrap", heldout=mode == "heldout", read_random=mode == "random",
                                       cumulative=mode == "cum")
+        if mode == "ramp":  # 128 windows per update until 10^8 tokens, then 256: both within cycle 0
+            c = c.replace(ramp=((0, 128 * c.T), (100_000_000, 256 * c.T)))
         if mode == "heldout":
             c = c.replace(updates_per_cycle=0)  # the 1-5 % held out cannot supply 200 updates
         say("oracle plan", name, c.n_docs, "docs", c.n_tokens, "tokens")
@@ -107,5 +109,55 @@ def test_full_size_parity(name, cap):
             fp = pk.fingerprint(g["digests"][i:i + 1]).cpu().numpy()[0].tobytes()
             assert fp == oracle.batch_fingerprint(o["digests"][0])
     outs.clear()
+    _CACHE.clear()
+    torch.cuda.empty_cache()
+
+
+def test_full_size_ramp_parity():
+    """The pre-train workload with a batch-size ramp (128 windows per update until
+    10^8 tokens, then 256): the whole cycle in one call, ragged layout."""
+    import torch
+    name = "ramp-pretrain"
+    c, op, oi, tensors, pk, gi = _setup(name)
+    compare_plan(pk, op)
+    compare_cycle(gi, oi, op)
+    assert gi["batches"].tolist() == oi.batches.tolist()
+    assert len(set(oi.batches.tolist())) == 2, "both pieces within the cycle"
+    U, T = oi.n_updates, c.T
+    slot0 = np.concatenate([[0], np.cumsum(oi.batches.astype(np.int64))])
+    say("emit", name, "steps 0 +", U)
+    g = pk.batch(0, U)
+    torch.cuda.synchronize()
+    learned = g["learned"].cpu().numpy()
+    for b in range(U):
+        exp = sum(int(op.win_learn[op.window_of(b, j)]) for j in range(int(oi.batches[b])))
+        assert learned[b] == exp, b
+    doc = g["doc"]
+    real = doc >= 0
+    n_real = real.sum(dim=1)
+    idx = torch.arange(T, device=doc.device).view(1, T)
+    assert bool((real == (idx < n_real.unsqueeze(1))).all()), "padding only at the end of a window"
+    assert bool((g["pos"][~real] == 0).all()) and bool((g["mask"][~real] == 0).all())
+    exp_real = np.array([int(op.win_real[op.window_of(b, j)]) for b in range(U) for j in range(int(oi.batches[b]))])
+    assert np.array_equal(n_real.cpu().numpy(), exp_real)
+    r = np.random.default_rng(8)
+    picks = [(int(r.integers(U)), None) for _ in range(40)] + [(0, 0), (U - 1, None)]
+    for b, j in picks:
+        j = int(r.integers(int(oi.batches[b]))) if j is None else j
+        x = int(slot0[b]) + j
+        tok, pos, dc, mask = op.emit_window(op.window_of(b, j))
+        assert np.array_equal(g["tokens"][x].cpu().numpy().view(np.uint32), tok), (b, j)
+        assert np.array_equal(g["pos"][x].cpu().numpy(), pos)
+        assert np.array_equal(g["doc"][x].cpu().numpy(), dc)
+        assert np.array_equal(g["mask"][x].cpu().numpy(), mask)
+        assert g["digests"][x].cpu().numpy().tobytes() == oracle.window_digest(tok, pos, dc, mask)
+    switch = int(np.argmax(oi.batches != oi.batches[0]))
+    for b in sorted({0, switch - 1, switch, U - 1}):
+        o = op.batch(b, 1)
+        d = g["digests"][int(slot0[b]):int(slot0[b + 1])]
+        assert np.array_equal(d.cpu().numpy(), o["digests"]), b
+        fp = pk.fingerprint_steps(b, 1, d).cpu().numpy()[0].tobytes()
+        assert fp == oracle.batch_fingerprint(o["digests"])
+    del g
     _CACHE.clear()
     torch.cuda.empty_cache()

@@ -138,6 +138,98 @@ def test_cumulative_small_share_parity():
     _parity_run(c.replace(cumulative=True), "cumulative-small-share", 0)
 
 
+RAMP_CASES = [
+    # (seed, ramp pieces (from tokens, tokens per update), B, cumulative, read_random, wrap, updates per cycle)
+    (0, ((0, 128), (1000, 256), (3000, 512)), 8, False, False, False, 3),
+    (1, ((0, 128), (1000, 256), (3000, 512)), 8, True, False, False, 3),
+    (2, ((0, 512), (700, 64), (2000, 320)), 8, False, True, False, 0),
+    (3, ((0, 512), (700, 64), (2000, 320)), 8, True, True, True, 0),
+    (4, ((0, 64), (640, 192), (5000, 384)), 6, True, False, True, 5),
+    (5, ((0, 256),), 4, False, False, False, 4),
+    (6, ((0, 256), (900, 128), (2600, 512)), 8, True, True, True, 0),
+]
+
+
+def _ramp_corpus(seed, ramp, B, cumulative, read_random, wrap, upc):
+    c = random_small(800 + seed, n_docs=900, n_sources=2 + seed % 3, max_strata=2, T=64, B=B, max_len=150,
+                     prompts=bool(seed % 2), bp_max=1500)
+    return c.replace(ramp=ramp, cumulative=cumulative, read_random=read_random, wrap=wrap, updates_per_cycle=upc)
+
+
+@pytest.mark.parametrize("case", range(len(RAMP_CASES)))
+def test_ramp_parity(case):
+    """Batch-size ramp: every cycle's batches, counts, digest and outputs (ragged
+    layout), learned counts and fingerprints against the oracle, across cycles."""
+    seed, ramp, B, cum, rr, wrap, upc = RAMP_CASES[case]
+    c = _ramp_corpus(seed, ramp, B, cum, rr, wrap, upc)
+    op = oracle.Plan(c)
+    pk = dp.Packer(c)
+    compare_plan(pk, op)
+    for cyc in range(4):
+        try:
+            oi = op.cycle(cyc)
+        except oracle.OracleError as e:
+            with pytest.raises(dp.DpackError) as ge:
+                pk.cycle(cyc)
+            assert ge.value.code == e.code
+            break
+        say("ramp", case, "cycle", cyc, "U", oi.n_updates, "batches", oi.batches.tolist()[:8])
+        gi = pk.cycle(cyc)
+        compare_cycle(gi, oi, op)
+        assert gi["batches"].tolist() == oi.batches.tolist()
+        assert np.array_equal(pk.inspect("cum_taken"), op.cumulative_taken().ravel())
+        U = oi.n_updates
+        for st in sorted({0, max(0, U // 2 - 1), max(0, U - 2)}):
+            n = min(2, U - st)
+            o = op.batch(st, n)
+            g = to_np(pk.batch(st, n))
+            compare_batch(g, o, f"ramp{case} cycle {cyc} step {st}")
+            fp = pk.fingerprint_steps(st, n, pk.batch(st, n)["digests"]).cpu().numpy()
+            x = 0
+            for i in range(n):
+                Bb = int(oi.batches[st + i])
+                assert fp[i].tobytes() == oracle.batch_fingerprint(o["digests"][x:x + Bb])
+                x += Bb
+    pk.close()
+
+
+@pytest.mark.parametrize("case", [0, 1, 6])  # every piece's batch even: two ranks
+def test_ramp_rank_slices_and_packed_rows(case):
+    """Each rank's slice of every update (world 2) and padding-free rows of a ramped cycle."""
+    seed, ramp, B, cum, rr, wrap, upc = RAMP_CASES[case]
+    c = _ramp_corpus(seed, ramp, B, cum, rr, wrap, upc)
+    op = oracle.Plan(c)
+    oi = op.cycle(0)
+    n = min(6, oi.n_updates)
+    for rank in range(2):
+        say("ramp-ranks", case, "rank", rank)
+        pk = dp.Packer(c, rank=rank, world=2)
+        pk.cycle(0)
+        compare_batch(to_np(pk.batch(0, n)), op.batch(0, n, rank=rank, world=2), f"ramp{case} rank {rank}")
+        g = {k: (v.cpu().numpy() if v is not None else None) for k, v in pk.batch_packed(0, n, 64).items()}
+        o = op.batch_packed(0, n, rank=rank, world=2, bucket=64)
+        assert np.array_equal(g["row_start"], o["row_start"]) and np.array_equal(g["length"], o["length"])
+        for i in range(n):
+            L = int(o["length"][i])
+            for k in ("tokens", "pos", "doc", "mask"):
+                a = g[k][i, :L].view(np.uint32) if k == "tokens" else g[k][i, :L]
+                assert np.array_equal(a, o[k][i, :L]), (i, k)
+        pk.close()
+
+
+def test_ramp_fingerprint_needs_steps():
+    """pack_fingerprint cannot tell a ramp's batch sizes apart: it refuses."""
+    seed, ramp, B, cum, rr, wrap, upc = RAMP_CASES[0]
+    c = _ramp_corpus(seed, ramp, B, cum, rr, wrap, upc)
+    pk = dp.Packer(c)
+    pk.cycle(0)
+    d = pk.batch(0, 1)["digests"]
+    with pytest.raises(dp.DpackError) as e:
+        pk.fingerprint(d.reshape(1, -1, 32))
+    assert e.value.code == dp.PACK_E_STATE
+    pk.close()
+
+
 PACKED_SHORT = {
     # windows of 1-3 real positions, many of them inside one 16-byte store group of the row
     "split_130": (lambda: _explicit([130] * 20, 64, 3), 1),
