@@ -78,6 +78,8 @@ def main():
     ap.add_argument("--wrap", action="store_true", help="wrap packing (PACK_FLAG_WRAP) instead of next-fit")
     ap.add_argument("--packed", action="store_true",
                     help="emit padding-free rows (pack_batch_packed, bucket 256) instead of padded windows and digests")
+    ap.add_argument("--ramp", action="store_true",
+                    help="batch-size ramp: B/2 windows per update until 10^8 tokens, then B (pre-train: 128 -> 256)")
     ap.add_argument("--cumulative", action="store_true",
                     help="per-update window counts from each cycle's cumulative quotas (PACK_FLAG_CUMULATIVE)")
     ap.add_argument("--read-random", action="store_true",
@@ -102,6 +104,8 @@ def main():
     t0 = time.time()
     corpus = make_corpus(args.workload, args.scale).replace(wrap=args.wrap, read_random=args.read_random,
                                                              cumulative=args.cumulative)
+    if args.ramp:
+        corpus = corpus.replace(ramp=((0, corpus.B // 2 * corpus.T), (100_000_000, corpus.B * corpus.T)))
     log(f"corpus {args.workload} scale {args.scale}: {corpus.n_docs} docs, {corpus.n_tokens} tokens "
         f"({time.time() - t0:.1f}s)")
     tensors = dp.upload_corpus(corpus)
@@ -121,10 +125,11 @@ def main():
         U = probe.cycle(0)["n_updates"]
     probe.close()
     B, T = corpus.B, corpus.T
+    batches = [int(x) for x in probe.batches]  # windows of each update of cycle 0
     # output buffers outside the timed region
     out = dp.Packer.alloc_out_packed(probe, U) if args.packed else dp.Packer.alloc_out(probe, U)
     torch.cuda.synchronize()
-    log(f"cycle 0: {U} updates x {B} windows x {T} positions")
+    log(f"cycle 0: {U} updates x {B if not args.ramp else sorted(set(batches))} windows x {T} positions")
 
     def one_step():
         pk = dp.Packer(corpus, device_tensors=tensors, timing=True)
@@ -158,7 +163,7 @@ def main():
     log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step, {value:.4g} packed tokens/s")
 
     # per-kernel figures (averaged per launch over the timed steps)
-    n_windows = U * B
+    n_windows = sum(batches)
     # read every real token once, write 13 bytes per output position (padded
     # windows: U·B·T; padding-free rows: the rows' lengths, bucket padding included)
     row_positions = int(out["length"].sum().item()) if args.packed else positions
@@ -239,12 +244,12 @@ def main():
         t_c = time.perf_counter()
         ob = op.batch_packed(0, n_s) if args.packed else op.batch(0, n_s, digests=True)
         t_d = time.perf_counter()
-        est = (t_b - t_a) + (t_c - t_b) + (t_d - t_c) * U / n_s
+        est = (t_b - t_a) + (t_c - t_b) + (t_d - t_c) * sum(batches) / sum(batches[:n_s])
         cpu = {"value": round(real / est, 1), "unit": "packed tokens/s", "cores": 1, "kind": "oracle",
                "sample": (f"whole plan of the corpus ({t_b - t_a:.2f}s) + cycle ({t_c - t_b:.2f}s) + "
                           + ("padding-free rows" if args.packed else "emission with SHA-256")
-                          + f" of updates 0..{n_s - 1} of {U} ({t_d - t_c:.2f}s), scaled to {U} "
-                          f"updates: {est:.2f}s per step; single-threaded C")}
+                          + f" of updates 0..{n_s - 1} of {U} ({t_d - t_c:.2f}s), scaled to the cycle's "
+                          f"{sum(batches)} windows: {est:.2f}s per step; single-threaded C")}
         log(f"cpu baseline {cpu['value']:.4g} tokens/s ({est:.1f}s per step)")
         # bit-exactness on the sample: GPU outputs of the last timed step vs the oracle
         mism = 0
@@ -259,14 +264,15 @@ def main():
                             for i in range(n_s))
             mism += int((out["learned"][:n_s].cpu().numpy() != op.batch(0, n_s, digests=False)["learned"]).sum())
         else:
+            lead = sum(batches[:n_s]) if args.ramp else n_s  # ramp: the first updates' windows, flat
             for key in ("tokens", "pos", "doc", "mask", "digests"):
-                g = out[key][:n_s].cpu().numpy()
+                g = out[key][:lead].cpu().numpy()
                 if key == "tokens":
                     g = g.view(np.uint32)
                 mism += int((g != ob[key]).sum())
             mism += int((out["learned"][:n_s].cpu().numpy() != ob["learned"]).sum())
         mism += int(oi.plan_digest != info["plan_digest"])
-        sample_check = {"updates_compared": n_s, "windows_compared": n_s * B, "mismatches": mism}
+        sample_check = {"updates_compared": n_s, "windows_compared": sum(batches[:n_s]), "mismatches": mism}
         log(f"bit-exact check on {n_s} updates: {mism} mismatches")
 
     line = {
@@ -285,6 +291,7 @@ def main():
         "config": {"workload": WORKLOAD_TEXT[args.workload] + ("" if args.scale == 1.0 else f" (scale {args.scale})")
                    + (", wrap packing" if args.wrap else "") + (", random read order" if args.read_random else "")
                    + (", per-update counts from cumulative quotas" if args.cumulative else "")
+                   + (f", batch-size ramp {B // 2} -> {B} windows per update at 10^8 tokens" if args.ramp else "")
                    + (", padding-free rows" if args.packed else ""),
                    "docs": corpus.n_docs, "tokens": corpus.n_tokens, "T": T, "B": B, "updates": U,
                    "real_tokens_per_step": real, "positions_per_step": row_positions,
