@@ -362,6 +362,9 @@ void check_config(const pack_config* cfg) {
     }
     if (cfg->flags & PACK_FLAG_CUMULATIVE) {
         if (cfg->n_sources > 1024) bad("the cumulative mixture takes at most 1024 sources");
+        for (uint32_t s = 0; s < cfg->n_sources; ++s)  // every due update then lies within 2^62 updates
+            if (cfg->share_weight[s] && ((unsigned __int128)cfg->share_weight[s] << 62) <= W)
+                bad("the cumulative mixture needs every nonzero share to be at least 2^-62 of the weights");
     }
     if ((cfg->flags & PACK_FLAG_CUMULATIVE) || cfg->n_ramp) {
         const uint64_t cap = cfg->n_docs + cfg->n_tokens / T;  // windows ≤ pieces ≤ cap
@@ -578,6 +581,7 @@ int pack_init(const pack_config* cfg, pack_ctx** out) {
         p.ramp = cfg->n_ramp ? 1u : 0u;
         p.tabled = (p.cumulative || p.ramp) ? 1u : 0u;
         p.world = cfg->world;
+        p.lanes = 1;
         c->ramp_from.assign(cfg->ramp_from, cfg->ramp_from + cfg->n_ramp);
         c->ramp_tokens.assign(cfg->ramp_tokens, cfg->ramp_tokens + cfg->n_ramp);
         p.cap_pieces = cfg->n_docs + cfg->n_tokens / cfg->window_tokens;
@@ -666,16 +670,16 @@ int pack_cycle(pack_ctx* c, uint32_t cycle, pack_cycle_info* info) {
             const uint64_t cap = U ? U : most;
             if (cap > p.cap_pieces / Bmin) throw InvalError{"internal: per-update table bound exceeded"};
             std::vector<dp::RampSpan> spans;
-            if (p.ramp) {  // the cycle's updates by ramp piece, from the tokens trained so far
+            if (p.ramp) {  // the ramp's pieces from the tokens trained so far, the last without end
                 const uint64_t K = c->ramp_from.size();
                 uint64_t u = 0, t = t0, slot = 0, out = 0;
-                while (u < cap) {
+                for (;;) {
                     uint32_t k = (uint32_t)(std::upper_bound(c->ramp_from.begin(), c->ramp_from.end(), t) -
                                             c->ramp_from.begin()) - 1;
                     const uint64_t tk = c->ramp_tokens[k], Bk = tk / p.T;
-                    uint64_t n = cap - u;
-                    if (k + 1 < K) n = std::min<uint64_t>(n, (c->ramp_from[k + 1] - t + tk - 1) / tk);
                     spans.push_back(dp::RampSpan{u, slot, out, (uint32_t)Bk, k});
+                    if (k + 1 == K) break;
+                    const uint64_t n = (c->ramp_from[k + 1] - t + tk - 1) / tk;  // updates of piece k
                     u += n;
                     t += n * tk;
                     slot += n * Bk;
@@ -683,6 +687,8 @@ int pack_cycle(pack_ctx* c, uint32_t cycle, pack_cycle_info* info) {
                 }
                 h2d_staged(*c, c->spans, spans.data(), spans.size());
                 dp::launch_ramp_fill(p, c->spans, (uint32_t)spans.size(), cap, c->st);
+                p.spans = c->spans;
+                p.n_spans = (uint32_t)spans.size();
             }
             if (p.cumulative) {  // the cycle's schedule from its cumulative quotas, on the device
                 c->timer.begin(PACK_PHASE_CYCLE, c->st);
@@ -705,8 +711,8 @@ int pack_cycle(pack_ctx* c, uint32_t cycle, pack_cycle_info* info) {
                 uint64_t fit = cap;
                 for (uint32_t s = 0; s < S; ++s) {
                     uint64_t a = 0;
-                    for (size_t x = 0; x < spans.size(); ++x) {
-                        const uint64_t end = x + 1 < spans.size() ? spans[x + 1].first : cap;
+                    for (size_t x = 0; x < spans.size() && spans[x].first < cap; ++x) {
+                        const uint64_t end = x + 1 < spans.size() ? std::min<uint64_t>(spans[x + 1].first, cap) : cap;
                         const uint64_t n = c->ramp_n_h[(uint64_t)spans[x].k * S + s], len = end - spans[x].first;
                         if (n && a + len * n > rem[s]) {
                             fit = std::min<uint64_t>(fit, spans[x].first + (rem[s] - a) / n);

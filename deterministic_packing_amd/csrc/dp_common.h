@@ -72,6 +72,16 @@ __device__ inline uint32_t lane_id() { return __lane_id(); }
 // ---------------------------------------------------------------- plan workspace
 // Device arrays of the plan; sizes in the comments (D docs, K kept, P pieces,
 // M windows, S sources, G groups, L lifting levels).
+// A span of the batch-size ramp: from update `first` of the cycle on, B windows
+// per update, slot0 seats before it (the next span's first update ends it).
+struct RampSpan {
+    uint64_t first;  // first update of the span in the cycle
+    uint64_t slot0;  // its first slot
+    uint64_t out0;   // its first output window of this rank
+    uint32_t B;      // windows per update in the span
+    uint32_t k;      // ramp piece
+};
+
 struct Plan {
     // inputs (borrowed)
     const uint32_t* tokens;
@@ -90,6 +100,7 @@ struct Plan {
     uint32_t ramp;                // 1: batch-size ramp (each update has its own batch)
     uint32_t tabled;              // cumulative or ramp: windows looked up in per-update slot tables
     uint32_t world;               // ranks sharing each update's slots
+    uint32_t lanes;               // 1 (lanes: the schedule runs per lane over B/lanes seats)
 
     // recipe on device
     uint32_t* gbase;              // [S+1] first group of each source
@@ -160,6 +171,8 @@ struct Plan {
     uint32_t* upd_B;              // windows of the update (all ranks)
     uint64_t* upd_slot0;          // first slot of the update in the cycle (prefix of upd_B)
     uint64_t* upd_out0;           // first of this rank's output windows (prefix of upd_B/world)
+    const struct RampSpan* spans; // the ramp's pieces from the cycle's first update on (the last without end)
+    uint32_t n_spans;
 
     // sizes known after the corresponding step (host copies)
     uint64_t n_kept, n_pieces, n_windows;
@@ -267,14 +280,7 @@ void launch_cycle_sums(Plan& p, uint64_t total_slots, hipStream_t st);
 // host has accepted U, every update's slot table
 void launch_cumulative(Plan& p, uint64_t W, uint64_t u_cfg, uint64_t cap, hipStream_t st);
 void launch_cum_slots(Plan& p, uint32_t U, hipStream_t st);
-// batch-size ramp: piece spans of a cycle (host-computed) → per-update tables
-struct RampSpan {
-    uint64_t first;  // first update of the span in the cycle
-    uint64_t slot0;  // its first slot
-    uint64_t out0;   // its first output window of this rank
-    uint32_t B;      // windows per update in the span
-    uint32_t k;      // ramp piece
-};
+// batch-size ramp: piece spans of a cycle (host-computed) → per-update tables (RampSpan above)
 void launch_ramp_fill(Plan& p, const RampSpan* spans, uint32_t n_spans, uint64_t n_upd, hipStream_t st);
 // fixed apportionment with a ramp: cum_A[u][s] = Σ over spans of whole updates before u · n_s of the span's piece
 void launch_ramp_fixed_A(Plan& p, const RampSpan* spans, uint32_t n_spans, const uint32_t* ramp_n, uint64_t U,

@@ -440,7 +440,7 @@ __global__ __launch_bounds__(ONE_WAVE ? WAVE : CUM_MAX_S) void k_cumulative(Plan
     // ONE_WAVE: Σ_s (fl − A)⁺ = Σ qB + #crossed − #ahead + #(qB = 0, not crossed, ahead), where
     // ahead = (A = fl + 1) before the update: every term is a ballot count
     for (uint64_t u = 0; u < cap; ++u) {
-        const uint32_t Bn = p.ramp ? p.upd_B[u] : p.B;
+        const uint32_t Bn = (p.ramp ? p.upd_B[u] : p.B) / p.lanes;  // this lane's seats in update u
         if (Bn != Bu) {  // uniform: the same batch for every source
             Bu = Bn;
             bw_hi = __umul64hi((uint64_t)Bu, w);
@@ -476,17 +476,25 @@ __global__ __launch_bounds__(ONE_WAVE ? WAVE : CUM_MAX_S) void k_cumulative(Plan
                     due = u + gap / bw + (gap % bw ? 1 : 0);
                 }
             } else {
-                // the first v > u with H(v+1)·w_s ≥ (fl+1)·W, H = upd_slot0 (seats before an
-                // update); cap when none within the schedule
+                // the first v > u with H(v+1)·w_s ≥ (fl+1)·W, H(v) = seats before update v from the
+                // ramp's spans (the last without end, so the due does not depend on the cycle's length)
                 const unsigned __int128 goal = (unsigned __int128)(fl + 1) * W;
-                auto reached = [&](uint64_t v) {  // v = cap stands for "not within the schedule"
-                    return v >= cap || (unsigned __int128)p.upd_slot0[v + 1] * w >= goal;
+                auto reached = [&](uint64_t v) {
+                    uint32_t lo = 0, hi = p.n_spans;  // span of update v
+                    while (hi - lo > 1) {
+                        const uint32_t mid = (lo + hi) >> 1;
+                        if (p.spans[mid].first <= v) lo = mid;
+                        else hi = mid;
+                    }
+                    const RampSpan& r = p.spans[lo];
+                    const uint64_t seats = (r.slot0 + (v + 1 - r.first) * r.B) / p.lanes;  // this lane's H(v+1)
+                    return (unsigned __int128)seats * w >= goal;
                 };
                 uint64_t lo = u, hi = u + 1, step = 1;  // not reached(u): fl is the quota's floor after u
-                while (!reached(hi)) {                  // gallop: ends at cap at the latest
+                while (!reached(hi)) {                  // gallop (dues lie within 2^62 updates: shares ≥ 2^-62)
                     lo = hi;
                     step *= 2;
-                    hi = lo + step < cap ? lo + step : cap;
+                    hi = lo + step;
                 }
                 while (hi - lo > 1) {  // reached(hi), not reached(lo)
                     const uint64_t mid = lo + (hi - lo) / 2;

@@ -212,6 +212,7 @@ class _OrCorpus(C.Structure):
         ("pad_token", C.c_uint32), ("wrap", C.c_uint32), ("heldout", C.c_uint32), ("read_random", C.c_uint32),
         ("cumulative", C.c_uint32),
         ("n_ramp", C.c_uint32), ("ramp_from", C.c_void_p), ("ramp_tokens", C.c_void_p),
+        ("lanes", C.c_uint32),
     ]
 
 
@@ -255,6 +256,7 @@ class Plan:
         )
         k = self._keep
         D, S = k["source"].shape[0], k["weight"].shape[0]
+        self.lanes = max(1, int(getattr(c, "lanes", 1) or 1))
         if k["offsets"].shape[0] != D + 1 or np.any(np.diff(k["offsets"].astype(np.int64)) < 0):
             raise OracleError(OR_E_INVAL, "offsets")
         if D and (int(k["source"].max()) >= S or np.any(k["stratum"] >= k["n_strata"][k["source"]])):
@@ -268,7 +270,8 @@ class Plan:
             c.T, c.B, c.seed & 0xFFFFFFFFFFFFFFFF, c.pad_token, 1 if getattr(c, "wrap", False) else 0,
             1 if getattr(c, "heldout", False) else 0, 1 if getattr(c, "read_random", False) else 0,
             1 if getattr(c, "cumulative", False) else 0,
-            0 if k["ramp_from"] is None else k["ramp_from"].shape[0], _ptr(k["ramp_from"]), _ptr(k["ramp_tokens"]))
+            0 if k["ramp_from"] is None else k["ramp_from"].shape[0], _ptr(k["ramp_from"]), _ptr(k["ramp_tokens"]),
+            self.lanes)
         err = C.c_int(0)
         self._p = lib.or_plan_build(C.byref(self._cs), C.byref(err))
         if not self._p:
@@ -276,6 +279,7 @@ class Plan:
         nk, npc, nw = C.c_uint64(), C.c_uint64(), C.c_uint64()
         lib.or_plan_sizes(self._p, C.byref(nk), C.byref(npc), C.byref(nw))
         nk, npc, nw = nk.value, npc.value, nw.value
+        S = S * self.lanes  # with lanes every per-source array is per stream (source s, lane l) = s·L + l
         self.hash = np.zeros(D, np.uint64)
         self.keep = np.zeros(D, np.uint8)
         self.order = np.zeros(nk, np.uint32)
@@ -318,7 +322,7 @@ class Plan:
         rc = lib.or_cycle(self._p, c, U_cfg)
         if rc:
             raise OracleError(rc, "cycle")
-        S = self.corpus.n_sources
+        S = self.corpus.n_sources * self.lanes
         start = np.zeros(S, np.uint64)
         cyc = C.c_int64()
         taken = np.zeros(S, np.uint64)
@@ -346,7 +350,7 @@ class Plan:
     def cumulative_taken(self) -> np.ndarray:
         """With the cumulative mixture: A [U+1, S], windows of each source taken
         before each update of the current cycle (row U: the cycle's totals)."""
-        S = self.corpus.n_sources
+        S = self.corpus.n_sources * self.lanes
         A = np.zeros((self.cycle_info.n_updates + 1, S), np.uint32)
         rc = _load().or_cum_export(self._p, _ptr(A))
         if rc:

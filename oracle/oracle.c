@@ -342,56 +342,80 @@ static int cmp_due(const void *pa, const void *pb)
     return 0;
 }
 
-/* With a batch-size ramp (C6b) update u has Bs[u] windows and the quotas
- * are taken at H(u) = Bs[0] + … + Bs[u−1] seats: window j of s is released in
- * the first update u with j ≤ ceil(H(u+1)·w_s/W) and due by the first update
- * u with H(u+1)·w_s ≥ j·W; Bs = NULL means B windows in every update. */
-int or_cumulative_b(uint32_t B, const uint32_t *Bs, uint32_t S, const uint64_t *w, const uint64_t *rem,
+/* With a batch-size ramp (C6b) each update has its own batch and the quotas
+ * are taken at H(u) = seats (windows) before update u.  The batches continue
+ * past the cycle (the ramp's last piece forever), so a window's due update is
+ * the same whatever the cycle's length: window j of s is released in the first
+ * update u with j ≤ ceil(H(u+1)·w_s/W) and due by the first update v with
+ * H(v+1)·w_s ≥ j·W.  The batches are given as spans: from update first[k]
+ * on, batch[k] windows per update, slot0[k] seats before update first[k]; the
+ * last span has no end. */
+typedef struct { uint64_t first, slot0; uint32_t batch; } or_span;
+
+static u128 seats_before(const or_span *sp, uint32_t n, u128 v)   /* H(v) */
+{
+    uint32_t k = 0;
+    while (k + 1 < n && sp[k + 1].first <= v) k++;
+    return (u128)sp[k].slot0 + (v - sp[k].first) * (u128)sp[k].batch;
+}
+
+/* the first update v ≥ from with H(v+1) ≥ X: in span k, H(v+1) = slot0_k +
+ * (v + 1 − first_k)·batch_k, so the first such v of the span follows by a
+ * ceiling division; spans are tried in order */
+static u128 first_reaching(const or_span *sp, uint32_t n, u128 from, u128 X)
+{
+    for (uint32_t k = 0; k < n; k++) {
+        const u128 f = sp[k].first, end = (k + 1 < n) ? (u128)sp[k + 1].first : ~(u128)0;
+        if (end <= from) continue;
+        u128 v = f;                                              /* H(f+1) = slot0 + batch */
+        if (X > (u128)sp[k].slot0 + sp[k].batch) v = f + (X - sp[k].slot0 + sp[k].batch - 1) / sp[k].batch - 1;
+        if (v < from) v = from;
+        if (v < end) return v;
+    }
+    return ~(u128)0;
+}
+
+int or_cumulative_s(const or_span *sp, uint32_t n_sp, uint32_t S, const uint64_t *w, const uint64_t *rem,
                     uint64_t u_cfg, uint64_t cap, uint32_t *A, uint64_t *U_out)
 {
     u128 W = 0;
     for (uint32_t s = 0; s < S; s++) W += w[s];
-    if (W == 0 || W >> 64 || (!Bs && B == 0)) return OR_E_INVAL;
+    if (W == 0 || W >> 64 || n_sp == 0) return OR_E_INVAL;
     *U_out = 0;
     for (uint32_t s = 0; s < S; s++) A[s] = 0;
-    uint64_t *H = (uint64_t *)malloc(sizeof(uint64_t) * (cap + 2));   /* H[u]: seats before update u */
-    uint32_t Bmax = B;
-    if (!H) return OR_E_NOMEM;
-    H[0] = 0;
-    for (uint64_t u = 0; u <= cap; u++) {
-        uint32_t Bu = Bs ? (u < cap ? Bs[u] : 0) : B;
-        if (Bs && u < cap && Bu > Bmax) Bmax = Bu;
-        H[u + 1] = H[u] + Bu;
+    uint32_t Bmax = 0;
+    for (uint32_t k = 0; k < n_sp; k++) {
+        if (sp[k].batch == 0) return OR_E_INVAL;
+        if (sp[k].batch > Bmax) Bmax = sp[k].batch;
     }
     due_item *it = (due_item *)malloc(sizeof(due_item) * ((uint64_t)Bmax + S + 1));
-    if (!it) { free(H); return OR_E_NOMEM; }
+    if (!it) return OR_E_NOMEM;
     uint64_t U = 0;
     for (uint64_t u = 0; u < cap && (u_cfg == 0 || u < u_cfg); u++) {
         const uint32_t *a = A + u * S;
         uint32_t *an = A + (u + 1) * S;
-        const uint64_t Bu = H[u + 1] - H[u];
+        const u128 Hn = seats_before(sp, n_sp, (u128)u + 1);
+        const uint64_t Bu = (uint64_t)(Hn - seats_before(sp, n_sp, u));
         /* released, not yet taken windows of every source with their due updates */
         uint64_t m = 0;
         for (uint32_t s = 0; s < S; s++) {
             if (w[s] == 0) continue;
-            u128 q = (u128)H[u + 1] * w[s];
+            u128 q = Hn * w[s];
             u128 hi = (q + W - 1) / W;                    /* ceil(H(u+1)·w_s/W) */
             for (u128 j = (u128)a[s] + 1; j <= hi; j++) {
-                /* due: the first update v with H(v+1)·w_s ≥ j·W (cap when none within the schedule) */
-                uint64_t v = u;
-                while (v < cap && (u128)H[v + 1] * w[s] < j * W) v++;
-                it[m].due = v;
+                /* due: the first update v ≥ u with H(v+1)·w_s ≥ j·W, i.e. H(v+1) ≥ ceil(j·W/w_s) */
+                it[m].due = first_reaching(sp, n_sp, u, (j * W + w[s] - 1) / w[s]);
                 it[m].s = s;
                 it[m].j = (uint32_t)j;
                 m++;
             }
         }
-        if (m < Bu) { free(it); free(H); return OR_E_INTERNAL; }
+        if (m < Bu) { free(it); return OR_E_INTERNAL; }
         qsort(it, m, sizeof(due_item), cmp_due);
         for (uint32_t s = 0; s < S; s++) an[s] = a[s];
         for (uint64_t r = 0; r < Bu; r++) an[it[r].s] += 1;
         for (uint64_t r = Bu; r < m; r++)
-            if (it[r].due <= u) { free(it); free(H); return OR_E_INTERNAL; }  /* deadline missed */
+            if (it[r].due <= u) { free(it); return OR_E_INTERNAL; }  /* deadline missed */
         int fits = 1;
         for (uint32_t s = 0; s < S; s++)
             if (an[s] > rem[s]) fits = 0;
@@ -399,15 +423,34 @@ int or_cumulative_b(uint32_t B, const uint32_t *Bs, uint32_t S, const uint64_t *
         U = u + 1;
     }
     free(it);
-    free(H);
     *U_out = U;
     return OR_OK;
 }
 
+/* B windows in every update: one span. */
 int or_cumulative(uint32_t B, uint32_t S, const uint64_t *w, const uint64_t *rem, uint64_t u_cfg,
                   uint64_t cap, uint32_t *A, uint64_t *U_out)
 {
-    return or_cumulative_b(B, NULL, S, w, rem, u_cfg, cap, A, U_out);
+    const or_span sp = {0, 0, B};
+    return or_cumulative_s(&sp, 1, S, w, rem, u_cfg, cap, A, U_out);
+}
+
+/* Bs[0..cap) windows in the first updates, the last batch continuing after them. */
+int or_cumulative_b(uint32_t B, const uint32_t *Bs, uint32_t S, const uint64_t *w, const uint64_t *rem,
+                    uint64_t u_cfg, uint64_t cap, uint32_t *A, uint64_t *U_out)
+{
+    if (!Bs) return or_cumulative(B, S, w, rem, u_cfg, cap, A, U_out);
+    or_span *sp = (or_span *)malloc(sizeof(or_span) * (cap ? cap : 1));
+    if (!sp) return OR_E_NOMEM;
+    uint32_t n = 0;
+    uint64_t seats = 0;
+    for (uint64_t u = 0; u < cap; u++) {
+        if (n == 0 || sp[n - 1].batch != Bs[u]) sp[n++] = (or_span){u, seats, Bs[u]};
+        seats += Bs[u];
+    }
+    int rc = n ? or_cumulative_s(sp, n, S, w, rem, u_cfg, cap, A, U_out) : OR_E_INVAL;
+    free(sp);
+    return rc;
 }
 
 
@@ -438,6 +481,7 @@ typedef struct {
     uint32_t n_ramp;             /* 0: every update has B windows; else pieces of a batch-size ramp (C6b) */
     const uint64_t *ramp_from;   /* [n_ramp] tokens trained at which each piece starts (first 0, rising) */
     const uint64_t *ramp_tokens; /* [n_ramp] tokens per update within the piece (a multiple of T) */
+    uint32_t lanes;              /* 0 or 1: no lanes; L > 1: Zephon lanes (C2l) */
 } or_corpus;
 
 typedef struct {
@@ -473,6 +517,13 @@ typedef struct {
     uint64_t *upd_slot0;         /* [U+1] first slot of each update (prefix of upd_B) */
     uint32_t *cum_A;             /* [(U+1)·S] tabled: windows of s taken before update u */
     uint32_t *tab_src, *tab_i;   /* [Σ upd_B] tabled: each slot's source and cycle window index */
+    /* C2l lanes: the plan runs over V = S·L streams (source s, lane l) = s·L + l;
+     * the recipe's own arrays stay for the per-lane mixture */
+    uint32_t lanes, S_real;
+    const uint64_t *w_real;
+    uint16_t *v_source;
+    uint32_t *v_strata, *v_bp;
+    uint64_t *v_weight;
 } or_plan;
 
 /* Cycle mode: per-update tables (a ramp or the cumulative mixture) or the
@@ -516,13 +567,56 @@ or_plan *or_plan_build(const or_corpus *cin, int *err)
     or_plan *p = (or_plan *)calloc(1, sizeof(or_plan));
     if (!p) { *err = OR_E_NOMEM; return NULL; }
     p->c = *cin;
+    sort_item *items = NULL;
+    uint32_t *gbase = NULL;
+    /* C2l. Lanes ([ZE] "lanes instead of ranks": the data are split into a fixed
+     * number of logical streams, each with its own ordered samples and its own
+     * packing state; a rank takes whole lanes).  Reading: document d belongs to
+     * lane d mod L; each (source, lane) is a stream planned as a source is
+     * (shuffle, strata merge, cut), numbered s·L + l; each update gives lane l
+     * its B/L consecutive slots, l·B/L onwards, apportioned over the sources
+     * like a batch of B/L (C6), and the recipe's hold-out rate and weight apply
+     * to every lane of a source. */
+    p->lanes = cin->lanes > 1 ? cin->lanes : 1;
+    p->S_real = cin->n_sources;
+    p->w_real = cin->weight;
+    if (p->lanes > 1) {
+        const uint32_t L = p->lanes, V = cin->n_sources * L;
+        if (cin->B % L || V > 65535) { *err = OR_E_INVAL; free(p); return NULL; }
+        for (uint32_t k = 0; k < cin->n_ramp; k++)
+            if ((cin->ramp_tokens[k] / cin->T) % L) { *err = OR_E_INVAL; free(p); return NULL; }
+        p->v_source = calloc(cin->n_docs ? cin->n_docs : 1, sizeof(uint16_t));
+        p->v_strata = calloc(V, sizeof(uint32_t));
+        p->v_bp = calloc(V, sizeof(uint32_t));
+        p->v_weight = calloc(V, sizeof(uint64_t));
+        if (!p->v_source || !p->v_strata || !p->v_bp || !p->v_weight) {
+            free(p->v_source); free(p->v_strata); free(p->v_bp); free(p->v_weight); free(p);
+            *err = OR_E_NOMEM;
+            return NULL;
+        }
+        for (uint64_t d = 0; d < cin->n_docs; d++) p->v_source[d] = (uint16_t)(cin->source[d] * L + d % L);
+        for (uint32_t v = 0; v < V; v++) {
+            p->v_strata[v] = cin->n_strata[v / L];
+            p->v_bp[v] = cin->bp[v / L];
+            p->v_weight[v] = cin->weight[v / L];
+        }
+        p->c.source = p->v_source;
+        p->c.n_strata = p->v_strata;
+        p->c.bp = p->v_bp;
+        p->c.weight = p->v_weight;
+        p->c.n_sources = V;
+    }
     const or_corpus *c = &p->c;
     const uint64_t D = c->n_docs;
     const uint32_t S = c->n_sources, T = c->T;
-    sort_item *items = NULL;
-    uint32_t *gbase = NULL;
 
-    if (T == 0 || c->B == 0 || S == 0) { *err = OR_E_INVAL; free(p); return NULL; }
+    if (T == 0 || c->B == 0 || S == 0) { *err = OR_E_INVAL; or_plan_free(p); return NULL; }
+    if (c->cumulative) {   /* C6c: every nonzero share at least 2^-62 of the weights (due updates in 64 bits) */
+        u128 Wt = 0;
+        for (uint32_t r = 0; r < p->S_real; r++) Wt += p->w_real[r];
+        for (uint32_t r = 0; r < p->S_real; r++)
+            if (p->w_real[r] && ((u128)p->w_real[r] << 62) <= Wt) { *err = OR_E_INVAL; or_plan_free(p); return NULL; }
+    }
     ALLOC(p->hash, D); ALLOC(p->keep, D);
     ALLOC(p->src_doc_start, S + 1); ALLOC(p->src_piece_start, S + 1); ALLOC(p->src_win_start, S + 1);
     ALLOC(p->n_upd, S); ALLOC(p->slot_src, c->B); ALLOC(p->slot_k, c->B);
@@ -735,11 +829,25 @@ or_plan *or_plan_build(const or_corpus *cin, int *err)
         p->win_learn[w] = learn;
     }
 
-    /* C6: per-update counts and the slot table. */
-    *err = or_apportion(c->B, S, c->weight, p->n_upd);
-    if (*err) goto fail;
-    *err = or_slot_table(c->B, S, p->n_upd, p->slot_src, p->slot_k);
-    if (*err) goto fail;
+    /* C6: per-update counts and the slot table (with lanes: every lane's B/L
+     * slots apportioned over the sources, lane after lane). */
+    {
+        const uint32_t L = p->lanes, Sr = p->S_real, BL = c->B / L;
+        uint32_t *nr = calloc(Sr, sizeof(uint32_t)), *ts = calloc(BL, sizeof(uint32_t)), *tk = calloc(BL, 4);
+        if (!nr || !ts || !tk) { free(nr); free(ts); free(tk); goto nomem; }
+        *err = or_apportion(BL, Sr, p->w_real, nr);
+        if (!*err) *err = or_slot_table(BL, Sr, nr, ts, tk);
+        if (!*err) {
+            for (uint32_t v = 0; v < S; v++) p->n_upd[v] = nr[v / L];
+            for (uint32_t l = 0; l < L; l++)
+                for (uint32_t j = 0; j < BL; j++) {
+                    p->slot_src[l * BL + j] = ts[j] * L + l;
+                    p->slot_k[l * BL + j] = tk[j];
+                }
+        }
+        free(nr); free(ts); free(tk);
+        if (*err) goto fail;
+    }
     if (c->n_ramp) {   /* C6b: each piece's batch B_k = tokens/T, world-independent; B is their largest */
         uint32_t Bmax = 0;
         for (uint32_t k = 0; k < c->n_ramp; k++) {
@@ -753,10 +861,14 @@ or_plan *or_plan_build(const or_corpus *cin, int *err)
         if (Bmax != c->B) { *err = OR_E_INVAL; goto fail; }
         const uint64_t n_ramp_entries = (uint64_t)c->n_ramp * S;
         ALLOC(p->ramp_n, n_ramp_entries);
-        for (uint32_t k = 0; k < c->n_ramp; k++) {
-            *err = or_apportion((uint32_t)(c->ramp_tokens[k] / T), S, c->weight, p->ramp_n + (uint64_t)k * S);
-            if (*err) goto fail;
+        uint32_t *nr = calloc(p->S_real, sizeof(uint32_t));
+        if (!nr) goto nomem;
+        for (uint32_t k = 0; k < c->n_ramp; k++) {   /* each lane's share of the piece's batch */
+            *err = or_apportion((uint32_t)(c->ramp_tokens[k] / T / p->lanes), p->S_real, p->w_real, nr);
+            if (*err) { free(nr); goto fail; }
+            for (uint32_t v = 0; v < S; v++) p->ramp_n[(uint64_t)k * S + v] = nr[v / p->lanes];
         }
+        free(nr);
     }
 
     p->cycle = -1;
@@ -784,6 +896,7 @@ void or_plan_free(or_plan *p)
     free(p->perm); free(p->perm_start);
     free(p->cyc_start); free(p->cyc_next); free(p->taken);
     free(p->cum_A); free(p->tab_src); free(p->tab_i); free(p->ramp_n); free(p->upd_B); free(p->upd_slot0);
+    free(p->v_source); free(p->v_strata); free(p->v_bp); free(p->v_weight);
     free(p);
 }
 
@@ -833,7 +946,38 @@ int or_cycle(or_plan *p, uint32_t cyc, uint32_t updates_cfg)
             t += (uint64_t)Bs[u] * T;
         }
         if (p->c.cumulative) {
-            rc = or_cumulative_b(B, Bs, S, p->c.weight, rem, updates_cfg, cap, cA, &U);
+            /* every lane runs the same schedule over the sources with B/L windows
+             * per update; it must fit the lane with the fewest windows left */
+            const uint32_t L = p->lanes, Sr = p->S_real;
+            const uint32_t K = p->c.n_ramp ? p->c.n_ramp : 1;
+            or_span *sp = malloc(sizeof(or_span) * K);
+            uint32_t *Ar = malloc(sizeof(uint32_t) * (cap + 1) * Sr);
+            uint64_t *rr = malloc(sizeof(uint64_t) * Sr);
+            if (!sp || !Ar || !rr) { free(sp); free(Ar); free(rr); CYC_FAIL(OR_E_NOMEM); }
+            /* the batches of one lane from this cycle on, the ramp's last piece forever */
+            uint32_t n = 0;
+            if (!p->c.n_ramp) {
+                sp[n++] = (or_span){0, 0, B / L};
+            } else {
+                uint64_t u = 0, tt = t0, seats = 0;
+                for (;;) {
+                    const uint32_t k = ramp_piece(&p->c, tt);
+                    const uint64_t tk = p->c.ramp_tokens[k];
+                    sp[n++] = (or_span){u, seats / L, (uint32_t)(tk / T / L)};
+                    if (k + 1 == p->c.n_ramp) break;
+                    const uint64_t cnt_k = (p->c.ramp_from[k + 1] - tt + tk - 1) / tk;  /* updates in piece k */
+                    u += cnt_k; tt += cnt_k * tk; seats += cnt_k * (tk / T);
+                }
+            }
+            for (uint32_t r = 0; r < Sr; r++) {
+                rr[r] = UINT64_MAX;
+                for (uint32_t l = 0; l < L; l++) if (rem[r * L + l] < rr[r]) rr[r] = rem[r * L + l];
+            }
+            rc = or_cumulative_s(sp, n, Sr, p->w_real, rr, updates_cfg, cap, Ar, &U);
+            if (!rc)
+                for (uint64_t u = 0; u <= U; u++)
+                    for (uint32_t v = 0; v < S; v++) cA[u * S + v] = Ar[u * Sr + v / L];
+            free(sp); free(Ar); free(rr);
             if (rc) goto out;
         } else {   /* fixed apportionment of each update's batch, until a source runs out */
             U = 0;
@@ -863,13 +1007,18 @@ int or_cycle(or_plan *p, uint32_t cyc, uint32_t updates_cfg)
         srcb = malloc(sizeof(uint32_t) * B);
         kb = malloc(sizeof(uint32_t) * B);
         if (!tsrc || !ti || !cnt || !srcb || !kb) CYC_FAIL(OR_E_NOMEM);
-        for (uint64_t u = 0; u < U; u++) {   /* each update's slots interleaved as in C6 */
-            for (uint32_t s = 0; s < S; s++) cnt[s] = cA[(u + 1) * S + s] - cA[u * S + s];
-            rc = or_slot_table(Bs[u], S, cnt, srcb, kb);
-            if (rc) goto out;
-            for (uint32_t j = 0; j < Bs[u]; j++) {
-                tsrc[slot0[u] + j] = srcb[j];
-                ti[slot0[u] + j] = cA[u * S + srcb[j]] + kb[j];
+        const uint32_t L = p->lanes, Sr = p->S_real;
+        for (uint64_t u = 0; u < U; u++) {   /* each update's slots interleaved as in C6, lane after lane */
+            const uint32_t BL = Bs[u] / L;
+            for (uint32_t l = 0; l < L; l++) {
+                for (uint32_t r = 0; r < Sr; r++) cnt[r] = cA[(u + 1) * S + r * L + l] - cA[u * S + r * L + l];
+                rc = or_slot_table(BL, Sr, cnt, srcb, kb);
+                if (rc) goto out;
+                for (uint32_t j = 0; j < BL; j++) {
+                    const uint32_t v = srcb[j] * L + l;
+                    tsrc[slot0[u] + l * BL + j] = v;
+                    ti[slot0[u] + l * BL + j] = cA[u * S + v] + kb[j];
+                }
             }
         }
     } else {
@@ -1102,7 +1251,7 @@ int or_plan_digest(const or_plan *p, uint8_t out[32])
     if (p->cycle < 0) return OR_E_STATE;
     uint64_t bytes = 8 + 4 + 4 + 8 + 4 + 4 + (uint64_t)S * (8 + 4 + 4 + 4 + 8 + 8 + 8) + 4 + 4 + 8ull * S + 8 + 8
                      + (c->read_random ? 4 : 0) + (c->cumulative ? 4 : 0)
-                     + (c->n_ramp ? 4 + 4 + 16ull * c->n_ramp + 8 : 0);
+                     + (c->n_ramp ? 4 + 4 + 16ull * c->n_ramp + 8 : 0) + (p->lanes > 1 ? 8 : 0);
     uint8_t *buf = (uint8_t *)malloc(bytes), *w = buf;
     if (!buf) return OR_E_NOMEM;
     /* the packing mode and the stream (training / held-out) are part of the plan */
@@ -1117,6 +1266,7 @@ int or_plan_digest(const or_plan *p, uint8_t out[32])
         for (uint32_t k = 0; k < c->n_ramp; k++) { put(&w, c->ramp_from[k], 8); put(&w, c->ramp_tokens[k], 8); }
         put(&w, p->tokens_done, 8);
     }
+    if (p->lanes > 1) { put(&w, 0x454E414Cu, 4); put(&w, p->lanes, 4); }  /* "LANE" and the lane count */
     put(&w, c->T, 4); put(&w, c->B, 4); put(&w, c->seed, 8); put(&w, S, 4); put(&w, c->pad_token, 4);
     for (uint32_t s = 0; s < S; s++) {
         put(&w, c->weight[s], 8); put(&w, c->bp[s], 4); put(&w, c->n_strata[s], 4);

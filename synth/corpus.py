@@ -50,6 +50,7 @@ class Corpus:
     read_random: bool = False   # each cycle's windows of a source read in a random order
     cumulative: bool = False    # per-update counts from the cycle's cumulative quotas
     ramp: Optional[Tuple[Tuple[int, int], ...]] = None  # batch-size ramp: ((from_tokens, tokens_per_update), ...)
+    lanes: int = 1              # Zephon lanes: document d in lane d mod lanes
 
     @property
     def n_docs(self) -> int:

@@ -125,6 +125,16 @@ def test_ramp_config_checked_on_host(lib, frm, tok, B, world, what):
     assert what in lib.pack_last_error(None).decode()
 
 
+def test_cumulative_share_limit_on_host(lib):
+    import numpy as np
+    w, bp = np.array([1, 2**62], np.uint64), np.zeros(2, np.uint32)
+    cfg, keep = _cfg(flags=dp.PACK_FLAG_CUMULATIVE)
+    cfg.share_weight, cfg.holdout_bp = w.ctypes.data, bp.ctypes.data
+    ctx = C.c_void_p()
+    assert lib.pack_init(C.byref(cfg), C.byref(ctx)) == dp.PACK_E_INVAL
+    assert "2^-62" in lib.pack_last_error(None).decode()
+
+
 def test_null_arguments_are_errors(lib):
     assert lib.pack_init(None, None) == dp.PACK_E_INVAL
     assert lib.pack_cycle(None, 0, None) == dp.PACK_E_INVAL

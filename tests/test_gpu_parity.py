@@ -122,6 +122,31 @@ def test_cumulative_with_other_modes(seed, wrap, read_random, heldout):
     _parity_run(c, "cumulative-modes", seed)
 
 
+@pytest.mark.parametrize("upc,ramp", [(1, None), (2, None), (3, None), (2, ((0, 128), (700, 320), (2000, 64))),
+                                      (5, ((0, 128), (700, 320), (2000, 64)))])
+def test_cumulative_short_cycles(upc, ramp):
+    """Short cycles of the cumulative schedule: windows due after a cycle's last
+    update still order the seats by their true due updates, cycle after cycle."""
+    c = random_small(900 + upc, n_docs=900, n_sources=4, T=64, B=5, max_len=120, prompts=True, bp_max=1000)
+    c = c.replace(weight=np.array([1, 3, 40, 7], np.uint64), cumulative=True, updates_per_cycle=upc, ramp=ramp)
+    op = oracle.Plan(c)
+    pk = dp.Packer(c)
+    for cyc in range(6):
+        try:
+            oi = op.cycle(cyc)
+        except oracle.OracleError as e:
+            with pytest.raises(dp.DpackError) as ge:
+                pk.cycle(cyc)
+            assert ge.value.code == e.code
+            break
+        say("short cycles", upc, "cycle", cyc)
+        gi = pk.cycle(cyc)
+        compare_cycle(gi, oi, op)
+        assert np.array_equal(pk.inspect("cum_taken"), op.cumulative_taken().ravel())
+        compare_batch(to_np(pk.batch(0, oi.n_updates)), op.batch(0, oi.n_updates), f"short {upc} cycle {cyc}")
+    pk.close()
+
+
 @pytest.mark.parametrize("S,B", [(70, 128), (130, 64)])
 def test_cumulative_many_sources(S, B):
     """More sources than one wavefront holds: the schedule runs on a whole workgroup."""

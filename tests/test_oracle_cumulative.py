@@ -218,3 +218,42 @@ def test_read_random_with_cumulative():
     wb = sorted(b.window_of(u, j) for u in range(ib.n_updates) for j in range(c.B))
     assert wa == wb
     assert ia.plan_digest != ib.plan_digest
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_schedule_prefix_does_not_depend_on_length(seed):
+    """A window's due update is read from the continuing batches, not from the
+    cycle's length: a shorter schedule is a prefix of a longer one."""
+    r = np.random.default_rng(100 + seed)
+    S = int(r.integers(2, 7))
+    w = [int(x) for x in r.choice([1, 2, 3, 50, 1000], size=S)]
+    B = int(r.choice([1, 3, 8, 64]))
+    U2 = int(r.integers(20, 90))
+    _, A2 = oracle.cumulative(B, w, [10**9] * S, updates=U2)
+    for U1 in (1, 2, 5, U2 // 2):
+        _, A1 = oracle.cumulative(B, w, [10**9] * S, updates=U1)
+        assert np.array_equal(A1, A2[:U1 + 1]), U1
+
+
+@pytest.mark.parametrize("ramp", [None, ((0, 128), (700, 320), (2000, 64))])
+def test_cycle_schedule_prefix_with_updates_per_cycle(ramp):
+    """updates_per_cycle cuts the same schedule shorter (ramped or not)."""
+    base = _corpus(8, S=4, B=5 if ramp is None else 5).replace(weight=np.array([1, 3, 40, 7], np.uint64))
+    if ramp is not None:
+        base = base.replace(ramp=ramp)
+    long = oracle.Plan(base)
+    ci = long.cycle(0)
+    A_long = long.cumulative_taken()
+    for upc in (1, 2, 3, max(1, ci.n_updates // 2)):
+        short = oracle.Plan(base.replace(updates_per_cycle=upc))
+        short.cycle(0)
+        assert np.array_equal(short.cumulative_taken(), A_long[:upc + 1]), upc
+
+
+def test_tiny_share_limit_in_plans():
+    """A plan with the cumulative mixture needs every nonzero share ≥ 2^-62."""
+    c = _corpus(9, S=2, B=4).replace(weight=np.array([1, 2**62], np.uint64))
+    with pytest.raises(oracle.OracleError) as e:
+        oracle.Plan(c)
+    assert e.value.code == oracle.OR_E_INVAL
+    oracle.Plan(c.replace(weight=np.array([2, 2**62], np.uint64)))   # just above the limit
