@@ -69,6 +69,7 @@ class PackConfig(C.Structure):
         ("updates_per_cycle", C.c_uint32), ("pad_token", C.c_uint32), ("seed", C.c_uint64),
         ("rank", C.c_uint32), ("world", C.c_uint32), ("stream", C.c_void_p),
         ("n_ramp", C.c_uint32), ("ramp_from", C.c_void_p), ("ramp_tokens", C.c_void_p),
+        ("n_lanes", C.c_uint32),
     ]
 
 
@@ -242,6 +243,7 @@ class Packer:
             self._host["ramp_from"] = np.ascontiguousarray([int(f) for f, _ in ramp], np.uint64)
             self._host["ramp_tokens"] = np.ascontiguousarray([int(t) for _, t in ramp], np.uint64)
         self.ramp = ramp is not None
+        self.lanes = max(1, int(getattr(corpus, "lanes", 1) or 1))
         d = self.dev
         self.cfg = PackConfig(
             ABI_VERSION, (PACK_FLAG_TIMING if timing else 0) | (PACK_FLAG_WRAP if getattr(corpus, "wrap", False) else 0)
@@ -257,7 +259,8 @@ class Packer:
             corpus.pad_token, corpus.seed & 0xFFFFFFFFFFFFFFFF, rank, world, self.stream.cuda_stream,
             len(ramp) if ramp is not None else 0,
             self._host["ramp_from"].ctypes.data if ramp is not None else None,
-            self._host["ramp_tokens"].ctypes.data if ramp is not None else None)
+            self._host["ramp_tokens"].ctypes.data if ramp is not None else None,
+            self.lanes)
         self.ctx = pack_init(self.cfg)
         self.per = corpus.B // world
         self.batches = None  # windows of each update of the current cycle (all ranks)
@@ -274,7 +277,7 @@ class Packer:
             pass
 
     def cycle(self, c: int) -> dict:
-        S = self.corpus.n_sources
+        S = self.corpus.n_sources * self.lanes  # with lanes: one entry per stream (source, lane)
         arrs = {k: np.zeros(S, np.uint64) for k in ("windows_start", "windows_taken", "windows_remaining",
                                                      "kept_docs", "kept_tokens", "held_docs", "held_tokens")}
         arrs["per_update"] = np.zeros(S, np.uint32)

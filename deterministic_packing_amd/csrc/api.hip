@@ -174,6 +174,16 @@ struct pack_ctx {
     uint64_t tokens_start = 0, tokens_next = 0;
     std::vector<uint32_t> upd_B;
     std::vector<uint64_t> upd_out0;
+    // lanes: the plan runs over S_real·lanes streams; the mixture over the real sources
+    uint32_t lanes = 1, S_real = 0;
+    std::vector<uint64_t> weight_real;
+    uint16_t* lane_source = nullptr;   // device [n_docs]: stream of each document
+    uint32_t* n_real = nullptr;        // device [S_real]: one lane's apportionment
+    uint32_t* nstart_real = nullptr;   // device [S_real+1]
+    uint32_t* lane_src = nullptr;      // device [B/lanes]: one lane's slot table
+    uint32_t* lane_k = nullptr;
+    uint32_t* cum_Ar = nullptr;        // device [(U_cap+1)·S_real]: the per-lane schedule
+    uint32_t* ramp_n_real = nullptr;   // device [K][S_real]
     std::string err;
 };
 
@@ -205,7 +215,7 @@ size_t carve(pack_ctx& c, char* base) {
     Carver k{base};
     p.gbase = k.take<uint32_t>(S + 1);
     p.n_strata = k.take<uint32_t>(S);
-    p.weight = k.take<uint64_t>(S);
+    p.weight = k.take<uint64_t>(c.S_real);  // the recipe's weights (read by the mixture over the real sources)
     p.bp = k.take<uint32_t>(S);
     p.group = k.take<uint32_t>(D);
     p.hash = k.take<uint64_t>(D);
@@ -265,8 +275,16 @@ size_t carve(pack_ctx& c, char* base) {
     p.upd_out0 = k.take<uint64_t>(p.ramp ? CU + 1 : 0);
     c.ramp_n = k.take<uint32_t>(K * S);
     c.spans = k.take<dp::RampSpan>(K + 1);
+    const bool lanes = c.lanes > 1;
+    c.lane_source = k.take<uint16_t>(lanes ? D : 0);
+    c.n_real = k.take<uint32_t>(c.S_real);
+    c.nstart_real = k.take<uint32_t>(c.S_real + 1);
+    c.lane_src = k.take<uint32_t>(B / c.lanes);
+    c.lane_k = k.take<uint32_t>(B / c.lanes);
+    c.cum_Ar = k.take<uint32_t>(lanes && p.cumulative ? (CU + 1) * c.S_real : 0);
+    c.ramp_n_real = k.take<uint32_t>(K * c.S_real);
     c.nstart = k.take<uint32_t>(S + 1);
-    c.dig_cap = 128 + 64 * S + 16 * K + 16;  // digest message: 64 + 52·S + 16·K + 16 bytes at most
+    c.dig_cap = 128 + 64 * S + 16 * K + 24;  // digest message: 64 + 52·S + 16·K + 24 bytes at most
     c.dig_buf = k.take<uint8_t>(c.dig_cap + 32);
     return k.off + ALIGN;
 }
@@ -366,10 +384,19 @@ void check_config(const pack_config* cfg) {
             if (cfg->share_weight[s] && ((unsigned __int128)cfg->share_weight[s] << 62) <= W)
                 bad("the cumulative mixture needs every nonzero share to be at least 2^-62 of the weights");
     }
+    const uint32_t L = cfg->n_lanes > 1 ? cfg->n_lanes : 1;
+    if (L > 1) {
+        if (B % L) bad("lanes must divide global_batch");
+        for (uint32_t k = 0; k < cfg->n_ramp; ++k)
+            if ((cfg->ramp_tokens[k] / T) % L) bad("lanes must divide every ramp piece's batch");
+        if (L % cfg->world) bad("world must divide the lanes (each rank takes whole lanes)");
+        if ((uint64_t)cfg->n_sources * L > 4096) bad("n_sources x lanes must be at most 4096");
+        if (G * L > 65536) bad("(source, stratum) groups x lanes must be at most 65536");
+    }
     if ((cfg->flags & PACK_FLAG_CUMULATIVE) || cfg->n_ramp) {
         const uint64_t cap = cfg->n_docs + cfg->n_tokens / T;  // windows ≤ pieces ≤ cap
-        if ((cap / Bmin + 1) * cfg->n_sources > (1ull << 28))
-            bad("the per-update table (updates x sources) exceeds 2^28 entries");
+        if ((cap / Bmin + 1) * cfg->n_sources * L > (1ull << 28))
+            bad("the per-update table (updates x streams) exceeds 2^28 entries");
     }
 }
 
@@ -396,7 +423,7 @@ void build_plan(pack_ctx& c) {
     c.pin_off = 0;
     h2d_staged(c, p.gbase, c.gbase.data(), p.S + 1);
     h2d_staged(c, p.n_strata, c.n_strata.data(), p.S);
-    h2d_staged(c, p.weight, c.weight.data(), p.S);
+    h2d_staged(c, p.weight, c.weight_real.data(), c.S_real);
     h2d_staged(c, p.bp, c.bp.data(), p.S);
     dp::launch_zero_u32(p.err, 1, st);
     dp::launch_zero_u64(p.stats, 4ull * p.S, st);
@@ -404,6 +431,10 @@ void build_plan(pack_ctx& c) {
 
     // validation first: no kernel reads the corpus through unchecked offsets
     c.timer.begin(PACK_PHASE_VALIDATE, st);
+    if (c.lanes > 1) {  // documents to streams (source, lane); the validation then checks stream ids
+        dp::launch_lane_source(c.cfg.doc_source, p.n_docs, c.S_real, c.lanes, c.lane_source, st);
+        p.source = c.lane_source;
+    }
     dp::launch_validate(p, st);
     c.timer.end(st);
     const uint32_t* h_err = d2h_staged(c, p.err, 1);
@@ -469,9 +500,24 @@ void build_plan(pack_ctx& c) {
     dp::launch_windows(p, st);
     c.timer.end(st);
     c.timer.begin(PACK_PHASE_MIXTURE, st);
-    dp::launch_mixture_w(p, c.W, c.nstart, st);
-    for (size_t k = 0; k < c.ramp_tokens.size(); ++k)  // each ramp piece's batch apportioned the same way
-        dp::launch_apportion(p, c.W, (uint32_t)(c.ramp_tokens[k] / p.T), c.ramp_n + k * p.S, st);
+    {
+        // one lane's mixture over the recipe's sources (B/L windows), then every lane the same
+        dp::Plan pr = p;
+        pr.S = c.S_real;
+        pr.B = p.B / c.lanes;
+        if (c.lanes > 1) {
+            pr.n_upd = c.n_real;
+            pr.slot_src = c.lane_src;
+            pr.slot_k = c.lane_k;
+            dp::launch_mixture_w(pr, c.W, c.nstart_real, st);
+            dp::launch_lane_expand(p, c.n_real, c.lane_src, c.lane_k, st);
+        } else {
+            dp::launch_mixture_w(p, c.W, c.nstart, st);
+        }
+        for (size_t k = 0; k < c.ramp_tokens.size(); ++k)  // each ramp piece's lane batch apportioned the same way
+            dp::launch_apportion(pr, c.W, (uint32_t)(c.ramp_tokens[k] / p.T / c.lanes), c.ramp_n_real + k * c.S_real,
+                                 st);
+    }
     dp::launch_checks(p, st);
     c.timer.end(st);
     const uint32_t* h_upd = d2h_staged(c, p.n_upd, p.S);
@@ -487,8 +533,14 @@ void build_plan(pack_ctx& c) {
     err = *h_err;
     if (err) throw dp::HipError{hipErrorUnknown, "internal plan consistency check (library bug)"};
     if (!c.ramp_tokens.empty()) {  // K·S counts: once, at init (may exceed the staging area)
-        c.ramp_n_h.resize(c.ramp_tokens.size() * p.S);
-        d2h(c.ramp_n_h.data(), c.ramp_n, c.ramp_n_h.size(), st);
+        const uint64_t K = c.ramp_tokens.size();
+        std::vector<uint32_t> nr(K * c.S_real);
+        d2h(nr.data(), c.ramp_n_real, nr.size(), st);
+        DP_HIP(hipStreamSynchronize(st));
+        c.ramp_n_h.resize(K * p.S);  // every lane of a source the same count
+        for (uint64_t k = 0; k < K; ++k)
+            for (uint32_t v = 0; v < p.S; ++v) c.ramp_n_h[k * p.S + v] = nr[k * c.S_real + v / c.lanes];
+        h2d(c.ramp_n, c.ramp_n_h.data(), c.ramp_n_h.size(), st);
         DP_HIP(hipStreamSynchronize(st));
     }
 }
@@ -545,18 +597,24 @@ int pack_init(const pack_config* cfg, pack_ctx** out) {
         c->cfg = *cfg;
         c->st = static_cast<hipStream_t>(cfg->stream);
         c->timer.on = (cfg->flags & PACK_FLAG_TIMING) != 0;
-        const uint32_t S = cfg->n_sources;
+        // with lanes, every per-source array is per stream s·L + l (the recipe's values per source)
+        const uint32_t L = cfg->n_lanes > 1 ? cfg->n_lanes : 1, Sr = cfg->n_sources, S = Sr * L;
+        c->lanes = L;
+        c->S_real = Sr;
+        c->weight_real.assign(cfg->share_weight, cfg->share_weight + Sr);
         c->n_strata.resize(S);
         c->gbase.resize(S + 1);
-        c->bp.assign(cfg->holdout_bp, cfg->holdout_bp + S);
-        c->weight.assign(cfg->share_weight, cfg->share_weight + S);
+        c->bp.resize(S);
+        c->weight.resize(S);
         uint32_t G = 0;
         for (uint32_t s = 0; s < S; ++s) {
-            c->n_strata[s] = cfg->n_strata ? cfg->n_strata[s] : 1u;
+            c->n_strata[s] = cfg->n_strata ? cfg->n_strata[s / L] : 1u;
+            c->bp[s] = cfg->holdout_bp[s / L];
+            c->weight[s] = cfg->share_weight[s / L];
             c->gbase[s] = G;
             G += c->n_strata[s];
-            c->W += c->weight[s];
         }
+        for (uint32_t r = 0; r < Sr; ++r) c->W += c->weight_real[r];
         c->gbase[S] = G;
         DP_HIP(hipGetDevice(&c->device));
 
@@ -581,7 +639,8 @@ int pack_init(const pack_config* cfg, pack_ctx** out) {
         p.ramp = cfg->n_ramp ? 1u : 0u;
         p.tabled = (p.cumulative || p.ramp) ? 1u : 0u;
         p.world = cfg->world;
-        p.lanes = 1;
+        p.lanes = L;
+        p.S_real = Sr;
         c->ramp_from.assign(cfg->ramp_from, cfg->ramp_from + cfg->n_ramp);
         c->ramp_tokens.assign(cfg->ramp_tokens, cfg->ramp_tokens + cfg->n_ramp);
         p.cap_pieces = cfg->n_docs + cfg->n_tokens / cfg->window_tokens;
@@ -691,22 +750,31 @@ int pack_cycle(pack_ctx* c, uint32_t cycle, pack_cycle_info* info) {
                 p.n_spans = (uint32_t)spans.size();
             }
             if (p.cumulative) {  // the cycle's schedule from its cumulative quotas, on the device
+                // one schedule over the recipe's sources with B/L seats per update, which every lane
+                // follows: it must fit the lane of each source with the fewest windows left
+                const uint32_t L = c->lanes, Sr = c->S_real;
+                std::vector<uint64_t> rr(Sr, ~0ull);
+                for (uint32_t v = 0; v < S; ++v) rr[v / L] = std::min(rr[v / L], rem[v]);
+                dp::Plan pc = p;
+                pc.S = Sr;
+                if (L > 1) pc.cum_A = c->cum_Ar;
                 c->timer.begin(PACK_PHASE_CYCLE, c->st);
-                h2d_staged(*c, p.cum_rem, rem.data(), S);
-                dp::launch_cumulative(p, c->W, U, cap, c->st);
+                h2d_staged(*c, p.cum_rem, rr.data(), Sr);
+                dp::launch_cumulative(pc, c->W, U, cap, c->st);
                 c->timer.end(c->st);
-                const uint64_t* h_out = d2h_staged(*c, p.cum_out, S + 1);
+                const uint64_t* h_out = d2h_staged(*c, p.cum_out, Sr + 1);
                 const uint32_t* h_err = d2h_staged(*c, p.err, 1);
                 sync_staged(*c);
                 if (*h_err & dp::ERR_INTERNAL) throw InvalError{"internal: cumulative schedule"};
-                const uint64_t got = h_out[S];
-                for (uint32_t s = 0; s < S; ++s) taken[s] = h_out[s];
+                const uint64_t got = h_out[Sr];
+                for (uint32_t v = 0; v < S; ++v) taken[v] = h_out[v / L];
                 c->pin_off = 0;
                 if (got == 0 || (U && got < U)) {
                     c->err = "a source cannot supply the cycle's windows";
                     return PACK_E_EXHAUSTED;
                 }
                 U = got;
+                if (L > 1) dp::launch_cum_expand(p, c->cum_Ar, U, c->st);
             } else {  // the fixed apportionment of each update's batch: per source, the updates it supports
                 uint64_t fit = cap;
                 for (uint32_t s = 0; s < S; ++s) {
@@ -808,6 +876,10 @@ int pack_cycle(pack_ctx* c, uint32_t cycle, pack_cycle_info* info) {
                 put(msg, c->ramp_tokens[k], 8);
             }
             put(msg, t0, 8);
+        }
+        if (c->lanes > 1) {                            // "LANE" and the lane count
+            put(msg, 0x454E414Cu, 4);
+            put(msg, c->lanes, 4);
         }
         put(msg, p.T, 4);
         put(msg, p.B, 4);

@@ -100,7 +100,8 @@ struct Plan {
     uint32_t ramp;                // 1: batch-size ramp (each update has its own batch)
     uint32_t tabled;              // cumulative or ramp: windows looked up in per-update slot tables
     uint32_t world;               // ranks sharing each update's slots
-    uint32_t lanes;               // 1 (lanes: the schedule runs per lane over B/lanes seats)
+    uint32_t lanes;               // lanes L (1: none); streams s·L + l, the schedule per lane over B/L seats
+    uint32_t S_real;              // the recipe's sources (S = S_real·lanes streams)
 
     // recipe on device
     uint32_t* gbase;              // [S+1] first group of each source
@@ -280,6 +281,12 @@ void launch_cycle_sums(Plan& p, uint64_t total_slots, hipStream_t st);
 // host has accepted U, every update's slot table
 void launch_cumulative(Plan& p, uint64_t W, uint64_t u_cfg, uint64_t cap, hipStream_t st);
 void launch_cum_slots(Plan& p, uint32_t U, hipStream_t st);
+// lanes: stream ids of the documents, one lane's counts/slots to every lane, one lane's schedule to every lane
+void launch_lane_source(const uint16_t* source, uint64_t n_docs, uint32_t S_real, uint32_t L, uint16_t* out,
+                        hipStream_t st);
+void launch_lane_expand(Plan& p, const uint32_t* n_real, const uint32_t* lane_src, const uint32_t* lane_k,
+                        hipStream_t st);
+void launch_cum_expand(Plan& p, const uint32_t* cum_Ar, uint64_t U, hipStream_t st);
 // batch-size ramp: piece spans of a cycle (host-computed) → per-update tables (RampSpan above)
 void launch_ramp_fill(Plan& p, const RampSpan* spans, uint32_t n_spans, uint64_t n_upd, hipStream_t st);
 // fixed apportionment with a ramp: cum_A[u][s] = Σ over spans of whole updates before u · n_s of the span's piece

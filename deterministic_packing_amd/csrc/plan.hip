@@ -578,16 +578,18 @@ __global__ __launch_bounds__(ONE_WAVE ? WAVE : CUM_MAX_S) void k_cumulative(Plan
 // Slot table of every update of the cycle: block u, counts
 // A(u+1) − A(u) in Sainte-Laguë order; cslot_i = A_s(u) + k.
 __global__ __launch_bounds__(256) void k_cum_slots(Plan p) {
-    extern __shared__ uint32_t csh[];  // n[S], nstart[S+1], base[S]
-    const uint32_t S = p.S;
+    extern __shared__ uint32_t csh[];  // n[S], nstart[S+1], base[S] over the real sources
+    const uint32_t S = p.S_real, L = p.lanes;  // block (u, l): lane l's slots of update u
     uint32_t* n = csh;
     uint32_t* ns = csh + S;
     uint32_t* base = csh + 2 * S + 1;
     const uint64_t u = blockIdx.x;
-    const uint32_t Bu = p.ramp ? p.upd_B[u] : p.B;
-    const uint64_t x0 = p.ramp ? p.upd_slot0[u] : u * p.B;  // the update's first slot
+    const uint32_t l = blockIdx.y;
+    const uint32_t Bu = (p.ramp ? p.upd_B[u] : p.B) / L;
+    const uint64_t x0 = (p.ramp ? p.upd_slot0[u] : u * p.B) + (uint64_t)l * Bu;  // the lane's first slot
     for (uint32_t s = threadIdx.x; s < S; s += blockDim.x) {
-        const uint32_t a0 = p.cum_A[u * S + s], a1 = p.cum_A[(u + 1) * S + s];
+        const uint32_t v = s * L + l;  // stream (source s, lane l)
+        const uint32_t a0 = p.cum_A[u * p.S + v], a1 = p.cum_A[(u + 1) * p.S + v];
         n[s] = a1 - a0;
         base[s] = a0;
     }
@@ -607,7 +609,7 @@ __global__ __launch_bounds__(256) void k_cum_slots(Plan p) {
         uint32_t s, k;
         const uint64_t pos = slot_item(n, ns, S, t, &s, &k);
         if (pos < Bu) {
-            p.cslot_src[x0 + pos] = s;
+            p.cslot_src[x0 + pos] = s * L + l;
             p.cslot_i[x0 + pos] = base[s] + k;
         } else {
             atomicOr(p.err, ERR_INTERNAL);
@@ -698,6 +700,39 @@ __global__ __launch_bounds__(256) void k_ramp_fixed_A(Plan p, const RampSpan* sp
     p.cum_A[x] = (uint32_t)a;
 }
 
+// ------------------------------------------------------------------ lanes
+// stream of each document: (source, lane d mod L) = source·L + d mod L; an id
+// outside the sources stays invalid (0xFFFF) for the validation kernel
+__global__ __launch_bounds__(256) void k_lane_source(const uint16_t* source, uint64_t n, uint32_t S_real,
+                                                     uint32_t L, uint16_t* out) {
+    const uint64_t d = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (d >= n) return;
+    const uint32_t s = source[d];
+    out[d] = s < S_real ? (uint16_t)(s * L + (uint32_t)(d % L)) : (uint16_t)0xFFFF;
+}
+
+// every lane the same counts (n_upd of stream s·L + l = n_real[s]) and slot
+// table (lane l's slots l·B/L .. hold the one-lane table's sources in lane l)
+__global__ __launch_bounds__(256) void k_lane_expand(Plan p, const uint32_t* n_real, const uint32_t* lane_src,
+                                                     const uint32_t* lane_k) {
+    const uint32_t x = blockIdx.x * blockDim.x + threadIdx.x;
+    const uint32_t L = p.lanes, BL = p.B / L;
+    if (x < p.S) p.n_upd[x] = n_real[x / L];
+    if (x < p.B) {
+        p.slot_src[x] = lane_src[x % BL] * L + x / BL;
+        p.slot_k[x] = lane_k[x % BL];
+    }
+}
+
+// every lane follows the one-lane schedule: cum_A[u][s·L + l] = cum_Ar[u][s]
+__global__ __launch_bounds__(256) void k_cum_expand(Plan p, const uint32_t* cum_Ar, uint64_t U) {
+    const uint64_t x = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (x >= (U + 1) * p.S) return;
+    const uint64_t u = x / p.S;
+    const uint32_t v = (uint32_t)(x % p.S);
+    p.cum_A[x] = cum_Ar[u * p.S_real + v / p.lanes];
+}
+
 inline uint32_t blocks_for(uint64_t n, uint32_t b = 256) { return (uint32_t)((n + b - 1) / b); }
 
 }  // namespace
@@ -778,7 +813,25 @@ void launch_cumulative(Plan& p, uint64_t W, uint64_t u_cfg, uint64_t cap, hipStr
 }
 
 void launch_cum_slots(Plan& p, uint32_t U, hipStream_t st) {
-    if (U) hipLaunchKernelGGL(k_cum_slots, dim3(U), dim3(256), (size_t)(3 * p.S + 1) * 4, st, p);
+    if (U) hipLaunchKernelGGL(k_cum_slots, dim3(U, p.lanes), dim3(256), (size_t)(3 * p.S_real + 1) * 4, st, p);
+    DP_HIP(hipGetLastError());
+}
+
+void launch_lane_source(const uint16_t* source, uint64_t n_docs, uint32_t S_real, uint32_t L, uint16_t* out,
+                        hipStream_t st) {
+    if (n_docs) hipLaunchKernelGGL(k_lane_source, dim3(blocks_for(n_docs)), dim3(256), 0, st, source, n_docs, S_real, L, out);
+    DP_HIP(hipGetLastError());
+}
+
+void launch_lane_expand(Plan& p, const uint32_t* n_real, const uint32_t* lane_src, const uint32_t* lane_k,
+                        hipStream_t st) {
+    hipLaunchKernelGGL(k_lane_expand, dim3(blocks_for(std::max<uint64_t>(p.B, p.S))), dim3(256), 0, st, p, n_real,
+                       lane_src, lane_k);
+    DP_HIP(hipGetLastError());
+}
+
+void launch_cum_expand(Plan& p, const uint32_t* cum_Ar, uint64_t U, hipStream_t st) {
+    hipLaunchKernelGGL(k_cum_expand, dim3(blocks_for((U + 1) * p.S)), dim3(256), 0, st, p, cum_Ar, U);
     DP_HIP(hipGetLastError());
 }
 

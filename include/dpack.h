@@ -147,7 +147,21 @@ typedef struct pack_timings {
  * windows for the last k with ramp_from[k] ≤ t.  Each update's windows come
  * from the apportionment of its own batch (or, with PACK_FLAG_CUMULATIVE,
  * from quotas at the running count of windows), in the Sainte-Laguë order of
- * its own counts; a cycle still never splits an update. */
+ * its own counts; a cycle still never splits an update.
+ *
+ * Lanes (n_lanes = L > 1).  Zephon blog post, "lanes instead of ranks": the
+ * data are split into a fixed number of logical streams, each with its own
+ * ordered samples and packing state, and ranks take whole lanes; the
+ * TorchTitan integration checks that the ranks divide the lanes and the
+ * lanes every update's batch.  Reading taken: document d belongs to lane
+ * d mod L; each (source s, lane l) is a stream s·L + l planned as a source is
+ * (shuffle, strata merge, cut); update u gives lane l its B_u/L consecutive
+ * slots from l·B_u/L on, apportioned over the sources like a batch of B_u/L
+ * (every lane the same counts; with PACK_FLAG_CUMULATIVE one schedule over
+ * B_u/L seats that every lane follows).  Limits: L divides B and every ramp
+ * batch, world divides L, n_sources·L ≤ 4096, Σ n_strata·L ≤ 65536.  With
+ * lanes the per-source arrays of pack_cycle_info and of pack_inspect hold
+ * n_sources·L entries, one per stream. */
 typedef struct pack_config {
     uint32_t abi_version;          /* DPACK_ABI_VERSION */
     uint32_t flags;                /* 0 or an or of PACK_FLAG_TIMING, _WRAP, _HELDOUT, _READ_RANDOM, _CUMULATIVE */
@@ -172,6 +186,7 @@ typedef struct pack_config {
     uint32_t n_ramp;               /* 0: every update has B windows; else the pieces below */
     const uint64_t *ramp_from;     /* host [n_ramp]: tokens trained at which piece k starts */
     const uint64_t *ramp_tokens;   /* host [n_ramp]: tokens per update (B_k·T) within piece k */
+    uint32_t n_lanes;              /* 0 or 1: no lanes; L > 1: Zephon lanes (see above) */
 } pack_config;
 
 /* pack_init — build the plan of a corpus (hash and hold-out of every

@@ -135,6 +135,16 @@ def test_cumulative_share_limit_on_host(lib):
     assert "2^-62" in lib.pack_last_error(None).decode()
 
 
+@pytest.mark.parametrize("lanes,B,world,what", [(3, 8, 1, "divide global_batch"), (4, 8, 8, "whole lanes"),
+                                                (4096, 8192, 1, "4096")])
+def test_lane_config_checked_on_host(lib, lanes, B, world, what):
+    """Lanes fail fast at init: they divide the batch, the ranks divide them."""
+    cfg, keep = _cfg(n_lanes=lanes, global_batch=B, world=world)
+    ctx = C.c_void_p()
+    assert lib.pack_init(C.byref(cfg), C.byref(ctx)) == dp.PACK_E_INVAL
+    assert what in lib.pack_last_error(None).decode()
+
+
 def test_null_arguments_are_errors(lib):
     assert lib.pack_init(None, None) == dp.PACK_E_INVAL
     assert lib.pack_cycle(None, 0, None) == dp.PACK_E_INVAL

@@ -30,6 +30,8 @@ def _setup(name):
                                       cumulative=mode == "cum")
         if mode == "ramp":  # 128 windows per update until 10^8 tokens, then 256: both within cycle 0
             c = c.replace(ramp=((0, 128 * c.T), (100_000_000, 256 * c.T)))
+        if mode == "lanes":  # 8 lanes: 120 streams of (source, lane)
+            c = c.replace(lanes=8)
         if mode == "heldout":
             c = c.replace(updates_per_cycle=0)  # the 1-5 % held out cannot supply 200 updates
         say("oracle plan", name, c.n_docs, "docs", c.n_tokens, "tokens")
@@ -50,9 +52,10 @@ def _setup(name):
 # wrap-pretrain is the pre-train workload with wrap packing, heldout-pretrain
 # its held-out (validation) stream, random-pretrain with each cycle's windows
 # read in a random order, cum-pretrain with per-update counts from the cycle's
-# cumulative quotas.
+# cumulative quotas, lanes-pretrain with 8 lanes.
 FULL = [("tiny", None), ("pretrain", None), ("sft", None), ("long", None), ("full", (24, 66)),
-        ("wrap-pretrain", None), ("heldout-pretrain", None), ("random-pretrain", None), ("cum-pretrain", None)]
+        ("wrap-pretrain", None), ("heldout-pretrain", None), ("random-pretrain", None), ("cum-pretrain", None),
+        ("lanes-pretrain", None)]
 
 
 @pytest.mark.parametrize("name,cap", FULL)

@@ -255,6 +255,59 @@ def test_ramp_fingerprint_needs_steps():
     pk.close()
 
 
+LANE_CASES = [
+    # (seed, lanes, B, cumulative, ramp, wrap, read_random, heldout)
+    (0, 2, 8, False, None, False, False, False),
+    (1, 4, 8, False, None, True, False, False),
+    (2, 3, 9, True, None, False, True, False),
+    (3, 8, 16, False, None, False, False, True),
+    (4, 2, 8, True, ((0, 256), (900, 512)), False, False, False),
+    (5, 4, 8, False, ((0, 256), (600, 512), (2400, 256)), True, True, False),
+    (6, 2, 6, True, None, True, True, True),
+]
+
+
+def _lane_corpus(seed, L, B, cum, ramp, wrap, rr, held):
+    c = random_small(1200 + seed, n_docs=1200, n_sources=2 + seed % 3, max_strata=3, T=64, B=B, max_len=130,
+                     prompts=bool(seed % 2), bp_max=6000 if held else 1500)
+    return c.replace(lanes=L, cumulative=cum, ramp=ramp, wrap=wrap, read_random=rr, heldout=held)
+
+
+@pytest.mark.parametrize("case", range(len(LANE_CASES)))
+def test_lanes_parity(case):
+    """Zephon lanes: streams per (source, lane), per-lane slots, with the other modes."""
+    c = _lane_corpus(*LANE_CASES[case])
+    if c.ramp is None:
+        _parity_run(c, "lanes", case)
+        return
+    op = oracle.Plan(c)
+    pk = dp.Packer(c)
+    compare_plan(pk, op)
+    oi = op.cycle(0)
+    gi = pk.cycle(0)
+    compare_cycle(gi, oi, op)
+    assert np.array_equal(pk.inspect("cum_taken"), op.cumulative_taken().ravel())
+    n = min(4, oi.n_updates)
+    compare_batch(to_np(pk.batch(0, n)), op.batch(0, n), f"lanes{case}")
+    pk.close()
+
+
+@pytest.mark.parametrize("case", [0, 1, 4])
+def test_lanes_each_rank_takes_whole_lanes(case):
+    """Every rank count dividing the lanes gives the same global batches."""
+    c = _lane_corpus(*LANE_CASES[case])
+    op = oracle.Plan(c)
+    oi = op.cycle(0)
+    n = min(3, oi.n_updates)
+    for world in sorted({1, 2, c.lanes}):
+        for rank in sorted({0, world - 1}):
+            say("lanes-ranks", case, "world", world, "rank", rank)
+            pk = dp.Packer(c, rank=rank, world=world)
+            pk.cycle(0)
+            compare_batch(to_np(pk.batch(0, n)), op.batch(0, n, rank=rank, world=world), f"lanes{case} {rank}/{world}")
+            pk.close()
+
+
 PACKED_SHORT = {
     # windows of 1-3 real positions, many of them inside one 16-byte store group of the row
     "split_130": (lambda: _explicit([130] * 20, 64, 3), 1),
