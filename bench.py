@@ -78,6 +78,7 @@ def main():
     ap.add_argument("--wrap", action="store_true", help="wrap packing (PACK_FLAG_WRAP) instead of next-fit")
     ap.add_argument("--packed", action="store_true",
                     help="emit padding-free rows (pack_batch_packed, bucket 256) instead of padded windows and digests")
+    ap.add_argument("--lanes", type=int, default=1, help="Zephon lanes (document d in lane d mod lanes)")
     ap.add_argument("--ramp", action="store_true",
                     help="batch-size ramp: B/2 windows per update until 10^8 tokens, then B (pre-train: 128 -> 256)")
     ap.add_argument("--cumulative", action="store_true",
@@ -106,6 +107,8 @@ def main():
                                                              cumulative=args.cumulative)
     if args.ramp:
         corpus = corpus.replace(ramp=((0, corpus.B // 2 * corpus.T), (100_000_000, corpus.B * corpus.T)))
+    if args.lanes > 1:
+        corpus = corpus.replace(lanes=args.lanes)
     log(f"corpus {args.workload} scale {args.scale}: {corpus.n_docs} docs, {corpus.n_tokens} tokens "
         f"({time.time() - t0:.1f}s)")
     tensors = dp.upload_corpus(corpus)
@@ -292,6 +295,7 @@ def main():
                    + (", wrap packing" if args.wrap else "") + (", random read order" if args.read_random else "")
                    + (", per-update counts from cumulative quotas" if args.cumulative else "")
                    + (f", batch-size ramp {B // 2} -> {B} windows per update at 10^8 tokens" if args.ramp else "")
+                   + (f", {args.lanes} lanes" if args.lanes > 1 else "")
                    + (", padding-free rows" if args.packed else ""),
                    "docs": corpus.n_docs, "tokens": corpus.n_tokens, "T": T, "B": B, "updates": U,
                    "real_tokens_per_step": real, "positions_per_step": row_positions,
