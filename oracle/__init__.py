@@ -86,6 +86,8 @@ def _load():
         lib.or_cumulative_b.argtypes = [u32, vp, u32, vp, vp, u64, u64, vp, C.POINTER(u64)]
         lib.or_cycle_batches.restype = u64
         lib.or_cycle_batches.argtypes = [vp, vp]
+        lib.or_cycle_stream_next.restype = i32
+        lib.or_cycle_stream_next.argtypes = [vp, vp]
         lib.or_window_of.restype = u64
         lib.or_window_of.argtypes = [vp, u64, u32]
         lib.or_emit_window.restype = None
@@ -212,7 +214,8 @@ class _OrCorpus(C.Structure):
         ("pad_token", C.c_uint32), ("wrap", C.c_uint32), ("heldout", C.c_uint32), ("read_random", C.c_uint32),
         ("cumulative", C.c_uint32),
         ("n_ramp", C.c_uint32), ("ramp_from", C.c_void_p), ("ramp_tokens", C.c_void_p),
-        ("lanes", C.c_uint32),
+        ("lanes", C.c_uint32), ("start_tokens", C.c_void_p), ("first_cycle", C.c_uint32),
+        ("tokens_start", C.c_uint64),
     ]
 
 
@@ -229,6 +232,7 @@ class CycleInfo:
     plan_digest: bytes
     batches: np.ndarray = None     # [U] windows of each update (B, or the ramp's batch)
     tokens_start: int = 0          # tokens trained before the cycle
+    stream_next: np.ndarray = None # [streams] token where each stream's next cycle starts
 
 
 class Plan:
@@ -253,6 +257,8 @@ class Plan:
             np.ascontiguousarray([int(f) for f, _ in c.ramp], np.uint64),
             ramp_tokens=None if getattr(c, "ramp", None) is None else
             np.ascontiguousarray([int(t) for _, t in c.ramp], np.uint64),
+            start_tokens=None if getattr(c, "start_tokens", None) is None else
+            np.ascontiguousarray(c.start_tokens, np.uint64),
         )
         k = self._keep
         D, S = k["source"].shape[0], k["weight"].shape[0]
@@ -271,7 +277,8 @@ class Plan:
             1 if getattr(c, "heldout", False) else 0, 1 if getattr(c, "read_random", False) else 0,
             1 if getattr(c, "cumulative", False) else 0,
             0 if k["ramp_from"] is None else k["ramp_from"].shape[0], _ptr(k["ramp_from"]), _ptr(k["ramp_tokens"]),
-            self.lanes)
+            self.lanes, _ptr(k["start_tokens"]), int(getattr(c, "first_cycle", 0)),
+            int(getattr(c, "tokens_start", 0)))
         err = C.c_int(0)
         self._p = lib.or_plan_build(C.byref(self._cs), C.byref(err))
         if not self._p:
@@ -343,8 +350,12 @@ class Plan:
         rc = lib.or_plan_digest(self._p, _ptr(dig))
         if rc:
             raise OracleError(rc, "plan_digest")
+        nxt = np.zeros(S, np.uint64)
+        rc = lib.or_cycle_stream_next(self._p, _ptr(nxt))
+        if rc:
+            raise OracleError(rc, "stream_next")
         self.cycle_info = CycleInfo(c, U, start, taken, remaining, real, learned,
-                                    nslots * self.corpus.T, dig.tobytes(), batches, t0)
+                                    nslots * self.corpus.T, dig.tobytes(), batches, t0, nxt)
         return self.cycle_info
 
     def cumulative_taken(self) -> np.ndarray:

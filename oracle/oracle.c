@@ -39,6 +39,9 @@
  *     cycles; each update's counts equal its batch's apportionment (fixed) or
  *     lie within quota of the running seat count (cumulative, also against
  *     every valid schedule on tiny cases); a one-piece ramp is the plain plan.
+ *   - stream starts (C5s): resuming at the reported next tokens with the same T
+ *     reproduces the next cycles bit for bit in every mode; with another T
+ *     every later token is emitted once, with masks by document offset.
  *
  * All integers are unsigned unless stated; products that can exceed 64 bits
  * are taken in unsigned __int128.
@@ -482,6 +485,9 @@ typedef struct {
     const uint64_t *ramp_from;   /* [n_ramp] tokens trained at which each piece starts (first 0, rising) */
     const uint64_t *ramp_tokens; /* [n_ramp] tokens per update within the piece (a multiple of T) */
     uint32_t lanes;              /* 0 or 1: no lanes; L > 1: Zephon lanes (C2l) */
+    const uint64_t *start_tokens;/* [streams] or NULL: first token of each stream to cut (C5s) */
+    uint32_t first_cycle;        /* number of the first cycle planned */
+    uint64_t tokens_start;       /* tokens trained before the first cycle (C6b) */
 } or_corpus;
 
 typedef struct {
@@ -493,6 +499,7 @@ typedef struct {
     uint64_t *src_doc_start;     /* [S+1] */
     uint64_t n_pieces;
     uint32_t *pc_doc, *pc_off, *pc_len, *pc_woff;   /* [n_pieces] */
+    uint64_t *pc_spos;           /* [n_pieces] position of the piece's first token in its source's stream */
     uint64_t *src_piece_start;   /* [S+1] */
     uint64_t n_windows;
     uint64_t *win_first;         /* [n_windows+1] first piece of each window */
@@ -715,38 +722,51 @@ or_plan *or_plan_build(const or_corpus *cin, int *err)
      * position (its pieces restart position ids at 0, [LI] Other trainers);
      * only the stream's last window can be short, and its rest is padding.
      * A piece is a maximal run of one document inside one window. */
+    /* C5s. A stream cut from a later token ([NS] Training: a branch forks from
+     * the state after a trunk cycle; every update has one sequence length, so a
+     * new length starts a new cut).  Reading: with start_tokens, stream v's
+     * first start_tokens[v] tokens (in its merged order) are already consumed:
+     * documents wholly before that point are skipped, the one that straddles it
+     * contributes its tokens from there on, and the cut (next-fit or wrap)
+     * starts there, as if the stream began at that token. */
+#define STREAM_START(s) (c->start_tokens ? c->start_tokens[s] : 0)
     if (c->wrap) {
         uint64_t P = 0, M = 0;
         for (uint32_t s = 0; s < S; s++) {
-            uint64_t x = 0;  /* stream position of the next token */
+            uint64_t x = 0, y = 0;  /* stream position of the document; of the next token after the start */
             for (uint64_t i = p->src_doc_start[s]; i < p->src_doc_start[s + 1]; i++) {
                 uint64_t L = doc_len(c, p->order[i]);
-                for (uint64_t o = 0; o < L;) {
-                    uint64_t room = T - x % T, len = (L - o < room) ? (L - o) : room;
-                    P++; o += len; x += len;
+                uint64_t o = STREAM_START(s) > x ? STREAM_START(s) - x : 0;
+                for (; o < L;) {
+                    uint64_t room = T - y % T, len = (L - o < room) ? (L - o) : room;
+                    P++; o += len; y += len;
                 }
+                x += L;
             }
-            M += (x + T - 1) / T;
+            M += (y + T - 1) / T;
         }
         p->n_pieces = P;
         p->n_windows = M;
-        ALLOC(p->pc_doc, P); ALLOC(p->pc_off, P); ALLOC(p->pc_len, P); ALLOC(p->pc_woff, P);
+        ALLOC(p->pc_doc, P); ALLOC(p->pc_off, P); ALLOC(p->pc_len, P); ALLOC(p->pc_woff, P); ALLOC(p->pc_spos, P);
         ALLOC(p->win_first, M + 1); ALLOC(p->win_real, M); ALLOC(p->win_learn, M);
         uint64_t q = 0, w = 0;
         for (uint32_t s = 0; s < S; s++) {
             p->src_piece_start[s] = q;
             p->src_win_start[s] = w;
-            uint64_t x = 0;
+            uint64_t xd = 0, x = 0;   /* stream position of the document; of the next token after the start */
             for (uint64_t i = p->src_doc_start[s]; i < p->src_doc_start[s + 1]; i++) {
                 uint32_t d = p->order[i];
                 uint64_t L = doc_len(c, d);
-                for (uint64_t o = 0; o < L;) {
+                uint64_t o = STREAM_START(s) > xd ? STREAM_START(s) - xd : 0;
+                for (; o < L;) {
                     uint64_t room = T - x % T, len = (L - o < room) ? (L - o) : room;
                     if (x % T == 0) p->win_first[w++] = q;  /* the piece opens a window */
                     p->pc_doc[q] = d; p->pc_off[q] = (uint32_t)o; p->pc_len[q] = (uint32_t)len;
+                    p->pc_spos[q] = xd + o;
                     p->pc_woff[q] = (uint32_t)(x % T);
                     q++; o += len; x += len;
                 }
+                xd += L;
             }
         }
         p->src_piece_start[S] = q;
@@ -756,25 +776,33 @@ or_plan *or_plan_build(const or_corpus *cin, int *err)
     /* C5a: split documents into pieces: a document of L ≤ T tokens is one
      * piece; a longer one is floor(L/T) pieces of T tokens plus a tail piece
      * of the rest, if any.  Count first, then fill. */
-    {
+    {   /* with a stream start (C5s), a straddling document's rest is split the same way */
         uint64_t P = 0;
-        for (uint64_t i = 0; i < p->n_kept; i++) {
-            uint64_t L = doc_len(c, p->order[i]);
-            P += (L <= T) ? 1 : (L / T + (L % T != 0));
+        for (uint32_t s = 0; s < S; s++) {
+            uint64_t xd = 0;
+            for (uint64_t i = p->src_doc_start[s]; i < p->src_doc_start[s + 1]; i++) {
+                uint64_t L = doc_len(c, p->order[i]);
+                uint64_t o = STREAM_START(s) > xd ? STREAM_START(s) - xd : 0;
+                if (o < L) P += (L - o + T - 1) / T;
+                xd += L;
+            }
         }
         p->n_pieces = P;
-        ALLOC(p->pc_doc, P); ALLOC(p->pc_off, P); ALLOC(p->pc_len, P); ALLOC(p->pc_woff, P);
+        ALLOC(p->pc_doc, P); ALLOC(p->pc_off, P); ALLOC(p->pc_len, P); ALLOC(p->pc_woff, P); ALLOC(p->pc_spos, P);
         uint64_t q = 0;
         for (uint32_t s = 0; s < S; s++) {
             p->src_piece_start[s] = q;
+            uint64_t xd = 0;
             for (uint64_t i = p->src_doc_start[s]; i < p->src_doc_start[s + 1]; i++) {
                 uint32_t d = p->order[i];
                 uint64_t L = doc_len(c, d);
-                for (uint64_t o = 0; o < L; o += T) {
+                for (uint64_t o = STREAM_START(s) > xd ? STREAM_START(s) - xd : 0; o < L; o += T) {
                     uint64_t len = (L - o < T) ? (L - o) : T;
                     p->pc_doc[q] = d; p->pc_off[q] = (uint32_t)o; p->pc_len[q] = (uint32_t)len;
+                    p->pc_spos[q] = xd + o;
                     q++;
                 }
+                xd += L;
             }
         }
         p->src_piece_start[S] = q;
@@ -871,7 +899,7 @@ or_plan *or_plan_build(const or_corpus *cin, int *err)
         free(nr);
     }
 
-    p->cycle = -1;
+    p->cycle = (int64_t)c->first_cycle - 1;
     p->U = 0;
     free(items);
     free(gbase);
@@ -896,7 +924,7 @@ void or_plan_free(or_plan *p)
     free(p->perm); free(p->perm_start);
     free(p->cyc_start); free(p->cyc_next); free(p->taken);
     free(p->cum_A); free(p->tab_src); free(p->tab_i); free(p->ramp_n); free(p->upd_B); free(p->upd_slot0);
-    free(p->v_source); free(p->v_strata); free(p->v_bp); free(p->v_weight);
+    free(p->v_source); free(p->v_strata); free(p->v_bp); free(p->v_weight); free(p->pc_spos);
     free(p);
 }
 
@@ -917,12 +945,14 @@ int or_cycle(or_plan *p, uint32_t cyc, uint32_t updates_cfg)
     uint64_t *rem = calloc(S, sizeof(uint64_t));
     uint32_t *cA = NULL, *tsrc = NULL, *ti = NULL, *cnt = NULL, *Bs = NULL, *srcb = NULL, *kb = NULL;
     uint64_t *slot0 = NULL;
-    const uint64_t t0 = (cyc == 0) ? 0 : p->tokens_done + (p->upd_slot0 ? p->upd_slot0[p->U] : (uint64_t)p->U * B) * T;
+    const int first = (cyc == p->c.first_cycle);
+    const uint64_t t0 = first ? p->c.tokens_start
+                              : p->tokens_done + (p->upd_slot0 ? p->upd_slot0[p->U] : (uint64_t)p->U * B) * T;
     int rc = OR_OK;
 #define CYC_FAIL(code) do { rc = (code); goto out; } while (0)
     if (!start || !take || !rem) CYC_FAIL(OR_E_NOMEM);
     for (uint32_t s = 0; s < S; s++) {
-        start[s] = (cyc == 0) ? 0 : p->cyc_next[s];
+        start[s] = first ? 0 : p->cyc_next[s];
         rem[s] = p->src_win_start[s + 1] - p->src_win_start[s] - start[s];
     }
     uint64_t U;
@@ -1153,7 +1183,7 @@ int or_batch(const or_plan *p, uint32_t step, uint32_t n_steps, uint32_t rank, u
              uint8_t *digests)
 {
     const uint32_t T = p->c.T;
-    if (p->cycle < 0) return OR_E_STATE;
+    if (p->cycle < (int64_t)p->c.first_cycle) return OR_E_STATE;
     if (world == 0 || rank >= world || p->c.B % world) return OR_E_INVAL;
     if ((uint64_t)step + n_steps > p->U) return OR_E_RANGE;
     uint64_t w = 0;   /* this rank's windows, update after update (B_b/world of update b) */
@@ -1197,7 +1227,7 @@ int or_batch_packed(const or_plan *p, uint32_t step, uint32_t n_steps, uint32_t 
                     int64_t *row_start, int64_t *length)
 {
     const uint32_t B = p->c.B, T = p->c.T;
-    if (p->cycle < 0) return OR_E_STATE;
+    if (p->cycle < (int64_t)p->c.first_cycle) return OR_E_STATE;
     if (world == 0 || rank >= world || B % world) return OR_E_INVAL;
     if ((uint64_t)step + n_steps > p->U) return OR_E_RANGE;
     const uint32_t pmax = B / world;               /* row pitch: the largest batch's windows */
@@ -1248,10 +1278,11 @@ int or_plan_digest(const or_plan *p, uint8_t out[32])
 {
     const or_corpus *c = &p->c;
     const uint32_t S = c->n_sources;
-    if (p->cycle < 0) return OR_E_STATE;
+    if (p->cycle < (int64_t)p->c.first_cycle) return OR_E_STATE;
     uint64_t bytes = 8 + 4 + 4 + 8 + 4 + 4 + (uint64_t)S * (8 + 4 + 4 + 4 + 8 + 8 + 8) + 4 + 4 + 8ull * S + 8 + 8
                      + (c->read_random ? 4 : 0) + (c->cumulative ? 4 : 0)
-                     + (c->n_ramp ? 4 + 4 + 16ull * c->n_ramp + 8 : 0) + (p->lanes > 1 ? 8 : 0);
+                     + (c->n_ramp ? 4 + 4 + 16ull * c->n_ramp + 8 : 0) + (p->lanes > 1 ? 8 : 0)
+                     + (c->start_tokens ? 4 + 8ull * S : 0);
     uint8_t *buf = (uint8_t *)malloc(bytes), *w = buf;
     if (!buf) return OR_E_NOMEM;
     /* the packing mode and the stream (training / held-out) are part of the plan */
@@ -1267,6 +1298,10 @@ int or_plan_digest(const or_plan *p, uint8_t out[32])
         put(&w, p->tokens_done, 8);
     }
     if (p->lanes > 1) { put(&w, 0x454E414Cu, 4); put(&w, p->lanes, 4); }  /* "LANE" and the lane count */
+    if (c->start_tokens) {                         /* "STRT": the streams' first tokens */
+        put(&w, 0x54525453u, 4);
+        for (uint32_t s = 0; s < S; s++) put(&w, c->start_tokens[s], 8);
+    }
     put(&w, c->T, 4); put(&w, c->B, 4); put(&w, c->seed, 8); put(&w, S, 4); put(&w, c->pad_token, 4);
     for (uint32_t s = 0; s < S; s++) {
         put(&w, c->weight[s], 8); put(&w, c->bp[s], 4); put(&w, c->n_strata[s], 4);
@@ -1326,10 +1361,29 @@ uint64_t or_cycle_batches(const or_plan *p, uint32_t *Bs)
     return p->tokens_done;
 }
 
+/* C5s: each stream's token position where the next cycle's windows begin (the
+ * stream's total when it is used up): the start_tokens of a context that goes
+ * on from here, with this T or another. */
+int or_cycle_stream_next(const or_plan *p, uint64_t *out /*[S]*/)
+{
+    if (p->cycle < (int64_t)p->c.first_cycle) return OR_E_STATE;
+    for (uint32_t s = 0; s < p->c.n_sources; s++) {
+        const uint64_t M = p->src_win_start[s + 1] - p->src_win_start[s];
+        if (p->cyc_next[s] < M) {
+            out[s] = p->pc_spos[p->win_first[p->src_win_start[s] + p->cyc_next[s]]];
+        } else {
+            uint64_t tot = 0;
+            for (uint64_t i = p->src_doc_start[s]; i < p->src_doc_start[s + 1]; i++) tot += doc_len(&p->c, p->order[i]);
+            out[s] = tot;
+        }
+    }
+    return OR_OK;
+}
+
 /* Tabled cycles (a ramp or the cumulative mixture): A [(U+1)·S] of the current cycle. */
 int or_cum_export(const or_plan *p, uint32_t *A)
 {
-    if (!tabled(&p->c) || p->cycle < 0) return OR_E_STATE;
+    if (!tabled(&p->c) || p->cycle < (int64_t)p->c.first_cycle) return OR_E_STATE;
     memcpy(A, p->cum_A, sizeof(uint32_t) * ((uint64_t)p->U + 1) * p->c.n_sources);
     return OR_OK;
 }

@@ -51,6 +51,9 @@ class Corpus:
     cumulative: bool = False    # per-update counts from the cycle's cumulative quotas
     ramp: Optional[Tuple[Tuple[int, int], ...]] = None  # batch-size ramp: ((from_tokens, tokens_per_update), ...)
     lanes: int = 1              # Zephon lanes: document d in lane d mod lanes
+    start_tokens: Optional[np.ndarray] = None  # per stream: first token to cut (a resumed or re-cut stream)
+    first_cycle: int = 0        # number of the first cycle planned
+    tokens_start: int = 0       # tokens trained before the first cycle
 
     @property
     def n_docs(self) -> int:
