@@ -69,7 +69,8 @@ class PackConfig(C.Structure):
         ("updates_per_cycle", C.c_uint32), ("pad_token", C.c_uint32), ("seed", C.c_uint64),
         ("rank", C.c_uint32), ("world", C.c_uint32), ("stream", C.c_void_p),
         ("n_ramp", C.c_uint32), ("ramp_from", C.c_void_p), ("ramp_tokens", C.c_void_p),
-        ("n_lanes", C.c_uint32),
+        ("n_lanes", C.c_uint32), ("start_tokens", C.c_void_p), ("first_cycle", C.c_uint32),
+        ("tokens_start", C.c_uint64),
     ]
 
 
@@ -79,7 +80,7 @@ class PackCycleInfo(C.Structure):
         ("learned_tokens", C.c_uint64), ("positions", C.c_uint64), ("plan_digest", C.c_uint8 * 32),
         ("windows_start", C.c_void_p), ("windows_taken", C.c_void_p), ("windows_remaining", C.c_void_p),
         ("kept_docs", C.c_void_p), ("kept_tokens", C.c_void_p), ("held_docs", C.c_void_p),
-        ("held_tokens", C.c_void_p), ("per_update", C.c_void_p),
+        ("held_tokens", C.c_void_p), ("per_update", C.c_void_p), ("stream_next_token", C.c_void_p),
     ]
 
 
@@ -244,6 +245,10 @@ class Packer:
             self._host["ramp_tokens"] = np.ascontiguousarray([int(t) for _, t in ramp], np.uint64)
         self.ramp = ramp is not None
         self.lanes = max(1, int(getattr(corpus, "lanes", 1) or 1))
+        st0 = getattr(corpus, "start_tokens", None)
+        if st0 is not None:
+            self._host["start_tokens"] = np.ascontiguousarray(st0, np.uint64)
+            assert self._host["start_tokens"].shape[0] == S * self.lanes
         d = self.dev
         self.cfg = PackConfig(
             ABI_VERSION, (PACK_FLAG_TIMING if timing else 0) | (PACK_FLAG_WRAP if getattr(corpus, "wrap", False) else 0)
@@ -260,7 +265,8 @@ class Packer:
             len(ramp) if ramp is not None else 0,
             self._host["ramp_from"].ctypes.data if ramp is not None else None,
             self._host["ramp_tokens"].ctypes.data if ramp is not None else None,
-            self.lanes)
+            self.lanes, self._host["start_tokens"].ctypes.data if st0 is not None else None,
+            int(getattr(corpus, "first_cycle", 0)), int(getattr(corpus, "tokens_start", 0)))
         self.ctx = pack_init(self.cfg)
         self.per = corpus.B // world
         self.batches = None  # windows of each update of the current cycle (all ranks)
@@ -281,6 +287,7 @@ class Packer:
         arrs = {k: np.zeros(S, np.uint64) for k in ("windows_start", "windows_taken", "windows_remaining",
                                                      "kept_docs", "kept_tokens", "held_docs", "held_tokens")}
         arrs["per_update"] = np.zeros(S, np.uint32)
+        arrs["stream_next_token"] = np.zeros(S, np.uint64)
         info = PackCycleInfo()
         for k, v in arrs.items():
             setattr(info, k, v.ctypes.data)

@@ -177,6 +177,10 @@ struct pack_ctx {
     // lanes: the plan runs over S_real·lanes streams; the mixture over the real sources
     uint32_t lanes = 1, S_real = 0;
     std::vector<uint64_t> weight_real;
+    std::vector<uint64_t> start_tokens;  // [S] first token of each stream, empty: from the start
+    uint64_t* start_dev = nullptr;       // device copy
+    uint64_t* next_win = nullptr;        // device [S]: first window of each stream's next cycle (~0: none)
+    uint64_t* stream_next = nullptr;     // device [S]: its first token
     uint16_t* lane_source = nullptr;   // device [n_docs]: stream of each document
     uint32_t* n_real = nullptr;        // device [S_real]: one lane's apportionment
     uint32_t* nstart_real = nullptr;   // device [S_real+1]
@@ -283,8 +287,11 @@ size_t carve(pack_ctx& c, char* base) {
     c.lane_k = k.take<uint32_t>(B / c.lanes);
     c.cum_Ar = k.take<uint32_t>(lanes && p.cumulative ? (CU + 1) * c.S_real : 0);
     c.ramp_n_real = k.take<uint32_t>(K * c.S_real);
+    c.start_dev = k.take<uint64_t>(S);
+    c.next_win = k.take<uint64_t>(S);
+    c.stream_next = k.take<uint64_t>(S);
     c.nstart = k.take<uint32_t>(S + 1);
-    c.dig_cap = 128 + 64 * S + 16 * K + 24;  // digest message: 64 + 52·S + 16·K + 24 bytes at most
+    c.dig_cap = 128 + 72 * S + 16 * K + 28;  // digest message: 64 + 60·S + 16·K + 28 bytes at most
     c.dig_buf = k.take<uint8_t>(c.dig_cap + 32);
     return k.off + ALIGN;
 }
@@ -301,7 +308,7 @@ void h2d(T* dst, const T* src, uint64_t count, hipStream_t st) {
 // pinned staging: bytes for the largest set of copies between two synchronizations
 // largest use: pack_cycle's cycle starts, read-order starts, sums, digest
 // message (≤ 64 + 52·S bytes) and digest, each 64-byte aligned
-size_t pin_bytes_for(uint32_t S, uint64_t K) { return 128ull * S + 112ull * K + 8192; }
+size_t pin_bytes_for(uint32_t S, uint64_t K) { return 192ull * S + 112ull * K + 8192; }
 
 template <typename T>
 T* pin_take(pack_ctx& c, uint64_t count) {
@@ -424,6 +431,10 @@ void build_plan(pack_ctx& c) {
     h2d_staged(c, p.gbase, c.gbase.data(), p.S + 1);
     h2d_staged(c, p.n_strata, c.n_strata.data(), p.S);
     h2d_staged(c, p.weight, c.weight_real.data(), c.S_real);
+    if (!c.start_tokens.empty()) {
+        h2d_staged(c, c.start_dev, c.start_tokens.data(), p.S);
+        p.start_tok = c.start_dev;
+    }
     h2d_staged(c, p.bp, c.bp.data(), p.S);
     dp::launch_zero_u32(p.err, 1, st);
     dp::launch_zero_u64(p.stats, 4ull * p.S, st);
@@ -595,6 +606,10 @@ int pack_init(const pack_config* cfg, pack_ctx** out) {
             return PACK_E_NOMEM;
         }
         c->cfg = *cfg;
+        c->cycle = (int64_t)cfg->first_cycle - 1;
+        if (cfg->start_tokens)
+            c->start_tokens.assign(cfg->start_tokens, cfg->start_tokens + (uint64_t)cfg->n_sources *
+                                                                              (cfg->n_lanes > 1 ? cfg->n_lanes : 1));
         c->st = static_cast<hipStream_t>(cfg->stream);
         c->timer.on = (cfg->flags & PACK_FLAG_TIMING) != 0;
         // with lanes, every per-source array is per stream s·L + l (the recipe's values per source)
@@ -700,20 +715,21 @@ int pack_cycle(pack_ctx* c, uint32_t cycle, pack_cycle_info* info) {
     c->err.clear();
     const uint32_t S = c->p.S;
     if ((int64_t)cycle != c->cycle + 1) {
-        c->err = "cycles must be planned in order 0, 1, 2, ...";
+        c->err = "cycles must be planned in order first_cycle, first_cycle + 1, ...";
         return PACK_E_STATE;
     }
     try {
         std::vector<uint64_t> start(S), rem(S), taken(S);
         for (uint32_t s = 0; s < S; ++s) {
-            start[s] = cycle == 0 ? 0 : c->cyc_next[s];
+            start[s] = cycle == c->cfg.first_cycle ? 0 : c->cyc_next[s];
             rem[s] = c->src_win_start[s + 1] - c->src_win_start[s] - start[s];
         }
         dp::Plan& p = c->p;
         uint64_t U = c->cfg.updates_per_cycle;
         const uint64_t* h_sums = nullptr;
         c->pin_off = 0;
-        const uint64_t t0 = cycle == 0 ? 0 : c->tokens_next;  // tokens trained before the cycle
+        // tokens trained before the cycle
+        const uint64_t t0 = cycle == c->cfg.first_cycle ? c->cfg.tokens_start : c->tokens_next;
         std::vector<uint32_t> upd_B;
         std::vector<uint64_t> upd_out0;
         if (p.tabled) {
@@ -859,6 +875,16 @@ int pack_cycle(pack_ctx* c, uint32_t cycle, pack_cycle_info* info) {
         }
         dp::launch_cycle_sums(p, slots, c->st);
         h_sums = d2h_staged(*c, p.cyc_sums, 2);
+        {  // each stream's first token of the next cycle
+            std::vector<uint64_t> nw(S);
+            for (uint32_t s = 0; s < S; ++s) {
+                const uint64_t M = c->src_win_start[s + 1] - c->src_win_start[s];
+                nw[s] = c->cyc_next[s] < M ? c->src_win_start[s] + c->cyc_next[s] : ~0ull;
+            }
+            h2d_staged(*c, c->next_win, nw.data(), S);
+            dp::launch_stream_next(p, c->next_win, c->stream_next, c->st);
+        }
+        const uint64_t* h_next = d2h_staged(*c, c->stream_next, S);
 
         // plan digest: SHA-256 of a little-endian description of the recipe,
         // stream sizes, cycle start and two order-free sums over the plan
@@ -880,6 +906,10 @@ int pack_cycle(pack_ctx* c, uint32_t cycle, pack_cycle_info* info) {
         if (c->lanes > 1) {                            // "LANE" and the lane count
             put(msg, 0x454E414Cu, 4);
             put(msg, c->lanes, 4);
+        }
+        if (!c->start_tokens.empty()) {                // "STRT": the streams' first tokens
+            put(msg, 0x54525453u, 4);
+            for (uint32_t s = 0; s < S; ++s) put(msg, c->start_tokens[s], 8);
         }
         put(msg, p.T, 4);
         put(msg, p.B, 4);
@@ -907,6 +937,7 @@ int pack_cycle(pack_ctx* c, uint32_t cycle, pack_cycle_info* info) {
         const uint8_t* h_digest = d2h_staged(*c, (const uint8_t*)(c->dig_buf + c->dig_cap), 32);
         DP_HIP(hipStreamSynchronize(c->st));
         const uint64_t sums[2] = {h_sums[0], h_sums[1]};
+        std::vector<uint64_t> next_tok(h_next, h_next + S);
         uint8_t digest[32];
         std::memcpy(digest, h_digest, 32);
         c->pin_off = 0;
@@ -928,6 +959,7 @@ int pack_cycle(pack_ctx* c, uint32_t cycle, pack_cycle_info* info) {
                 if (info->held_docs) info->held_docs[s] = c->stats[2 * S + s];
                 if (info->held_tokens) info->held_tokens[s] = c->stats[3 * S + s];
                 if (info->per_update) info->per_update[s] = c->n_upd[s];
+                if (info->stream_next_token) info->stream_next_token[s] = next_tok[s];
             }
         }
         return PACK_OK;
@@ -945,7 +977,7 @@ int pack_cycle(pack_ctx* c, uint32_t cycle, pack_cycle_info* info) {
 int pack_batch(pack_ctx* c, uint32_t step, uint32_t n_steps, const pack_out* out) {
     if (!c) return PACK_E_INVAL;
     c->err.clear();
-    if (c->cycle < 0) {
+    if (c->cycle < (int64_t)c->cfg.first_cycle) {
         c->err = "no cycle planned";
         return PACK_E_STATE;
     }
@@ -1007,7 +1039,7 @@ int pack_batch(pack_ctx* c, uint32_t step, uint32_t n_steps, const pack_out* out
 int pack_batch_packed(pack_ctx* c, uint32_t step, uint32_t n_steps, const pack_out_packed* out) {
     if (!c) return PACK_E_INVAL;
     c->err.clear();
-    if (c->cycle < 0) {
+    if (c->cycle < (int64_t)c->cfg.first_cycle) {
         c->err = "no cycle planned";
         return PACK_E_STATE;
     }
@@ -1094,7 +1126,7 @@ int pack_fingerprint_steps(pack_ctx* c, uint32_t step, uint32_t n_steps, const u
         c->err = "digests must be 4-byte aligned";
         return PACK_E_INVAL;
     }
-    if (c->cycle < 0) {
+    if (c->cycle < (int64_t)c->cfg.first_cycle) {
         c->err = "no cycle planned";
         return PACK_E_STATE;
     }
@@ -1141,7 +1173,7 @@ int pack_inspect(const pack_ctx* cc, uint32_t what, void* host_dst, uint64_t cap
         case PACK_INSPECT_SLOT_K: src = p.slot_k; count = p.B; width = out_width = 4; break;
         case PACK_INSPECT_COUNTS: count = 3; width = out_width = 8; break;
         case PACK_INSPECT_UPDATE_BATCH:
-            if (c->cycle < 0) {
+            if (c->cycle < (int64_t)c->cfg.first_cycle) {
                 c->err = "no cycle planned";
                 return PACK_E_STATE;
             }
@@ -1149,7 +1181,7 @@ int pack_inspect(const pack_ctx* cc, uint32_t what, void* host_dst, uint64_t cap
             width = out_width = 4;
             break;
         case PACK_INSPECT_CUM_TAKEN:
-            if (!p.tabled || c->cycle < 0) {
+            if (!p.tabled || c->cycle < (int64_t)c->cfg.first_cycle) {
                 c->err = "no per-update schedule: neither PACK_FLAG_CUMULATIVE nor a ramp, or no cycle yet";
                 return PACK_E_STATE;
             }

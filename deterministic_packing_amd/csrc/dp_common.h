@@ -173,6 +173,7 @@ struct Plan {
     uint64_t* upd_slot0;          // first slot of the update in the cycle (prefix of upd_B)
     uint64_t* upd_out0;           // first of this rank's output windows (prefix of upd_B/world)
     const struct RampSpan* spans; // the ramp's pieces from the cycle's first update on (the last without end)
+    const uint64_t* start_tok;    // [S] first token of each stream to cut, or null (from the stream's start)
     uint32_t n_spans;
 
     // sizes known after the corresponding step (host copies)
@@ -287,6 +288,8 @@ void launch_lane_source(const uint16_t* source, uint64_t n_docs, uint32_t S_real
 void launch_lane_expand(Plan& p, const uint32_t* n_real, const uint32_t* lane_src, const uint32_t* lane_k,
                         hipStream_t st);
 void launch_cum_expand(Plan& p, const uint32_t* cum_Ar, uint64_t U, hipStream_t st);
+// each stream's first token of the window next_win[s] (~0: the stream's total)
+void launch_stream_next(Plan& p, const uint64_t* next_win, uint64_t* out, hipStream_t st);
 // batch-size ramp: piece spans of a cycle (host-computed) → per-update tables (RampSpan above)
 void launch_ramp_fill(Plan& p, const RampSpan* spans, uint32_t n_spans, uint64_t n_upd, hipStream_t st);
 // fixed apportionment with a ramp: cum_A[u][s] = Σ over spans of whole updates before u · n_s of the span's piece
@@ -352,9 +355,10 @@ void scan_u32(const uint32_t* in, uint64_t n, uint32_t* out, void* tmp, hipStrea
 void scan_len_u64(const uint32_t* ids, const uint64_t* offsets, uint64_t n, uint64_t* out, void* tmp,
                   hipStream_t st);
 void scan_wrap_pieces_u32(const uint32_t* ids, const uint64_t* offsets, const uint64_t* opre,
-                          const uint64_t* src_doc_start, const uint16_t* source, uint32_t T, uint64_t n,
-                          uint32_t* out, void* tmp, hipStream_t st);
-void scan_pieces_u32(const uint32_t* ids, const uint64_t* offsets, uint32_t T, uint64_t n, uint32_t* out,
-                     void* tmp, hipStream_t st);
+                          const uint64_t* src_doc_start, const uint16_t* source, const uint64_t* start, uint32_t T,
+                          uint64_t n, uint32_t* out, void* tmp, hipStream_t st);
+void scan_pieces_u32(const uint32_t* ids, const uint64_t* offsets, const uint64_t* opre,
+                     const uint64_t* src_doc_start, const uint16_t* source, const uint64_t* start, uint32_t T,
+                     uint64_t n, uint32_t* out, void* tmp, hipStream_t st);
 
 }  // namespace dp

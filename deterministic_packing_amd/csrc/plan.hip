@@ -131,9 +131,16 @@ __global__ __launch_bounds__(256) void k_pieces(Plan p) {
     const uint64_t L = p.offsets[d + 1] - p.offsets[d];
     const uint32_t np = p.piece_start[i + 1] - q0;
     const uint64_t pre = p.opre[i];
+    // with a stream start: the document's tokens before it are already consumed
+    uint64_t o0 = 0, cut = 0;
+    const uint64_t x0 = pre - p.opre[p.src_doc_start[p.source[d]]];  // stream position of the first token
+    if (p.start_tok) {
+        cut = p.start_tok[p.source[d]];
+        o0 = cut > x0 ? (cut - x0 < L ? cut - x0 : L) : 0;
+    }
     if (!p.wrap) {
         for (uint32_t r = 0; r < np; ++r) {
-            const uint64_t o = (uint64_t)r * p.T;
+            const uint64_t o = o0 + (uint64_t)r * p.T;
             const uint32_t q = q0 + r;
             p.pc_doc[q] = d;
             p.pc_off[q] = (uint32_t)o;
@@ -141,9 +148,9 @@ __global__ __launch_bounds__(256) void k_pieces(Plan p) {
             p.pc_pre[q] = pre + o;
         }
     } else {
-        // wrap: cut where the source's stream crosses a multiple of T
-        uint64_t x = pre - p.opre[p.src_doc_start[p.source[d]]];  // stream position of the first token
-        uint64_t o = 0;
+        // wrap: cut where the stream (from its start) crosses a multiple of T
+        uint64_t x = x0 + o0 - cut;  // stream position of the first token to cut
+        uint64_t o = o0;
         for (uint32_t r = 0; r < np; ++r) {
             const uint64_t room = p.T - x % p.T;
             const uint64_t len = (L - o) < room ? (L - o) : room;
@@ -178,12 +185,15 @@ __global__ __launch_bounds__(256) void k_next(Plan p) {
     const uint32_t s = upper_bound_u64(p.src_piece_start, p.S + 1, q) - 1;
     const uint64_t pe = p.src_piece_start[s + 1];
     const uint64_t base = p.pc_pre[q];
+    // token position where piece j starts; at the source's end, where its last piece ends (the next
+    // stream's first piece can start later in the order: documents before a stream start have none)
+    auto at = [&](uint64_t j) { return j < pe ? p.pc_pre[j] : p.pc_pre[pe - 1] + p.pc_len[pe - 1]; };
     uint64_t lo = q + 1, hi = q + p.T;  // a window holds at most T pieces
     if (hi > pe) hi = pe;
-    // largest j in [lo, hi] with pre[j] − base ≤ T  (pre[q+1] − base ≤ T always)
+    // largest j in [lo, hi] with at(j) − base ≤ T  (at(q+1) − base ≤ T always)
     while (lo < hi) {
         const uint64_t mid = (lo + hi + 1) >> 1;
-        if (p.pc_pre[mid] - base <= p.T) lo = mid;
+        if (at(mid) - base <= p.T) lo = mid;
         else hi = mid - 1;
     }
     p.jump[q] = (lo == pe) ? END : (uint32_t)lo;
@@ -253,7 +263,8 @@ __global__ __launch_bounds__(1024) void k_wrap_window_count(Plan p) {
     uint64_t run = 0;
     for (uint32_t s = 0; s < p.S; ++s) {
         p.src_win_start[s] = run;
-        const uint64_t lam = p.opre[p.src_doc_start[s + 1]] - p.opre[p.src_doc_start[s]];
+        uint64_t lam = p.opre[p.src_doc_start[s + 1]] - p.opre[p.src_doc_start[s]];
+        if (p.start_tok) lam = p.start_tok[s] < lam ? lam - p.start_tok[s] : 0;  // tokens from the stream's start
         run += (lam + p.T - 1) / p.T;
     }
     p.src_win_start[p.S] = run;
@@ -263,7 +274,8 @@ __global__ __launch_bounds__(256) void k_wrap_windows(Plan p) {
     const uint64_t q = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (q >= p.n_pieces) return;
     const uint32_t s = upper_bound_u64(p.src_piece_start, p.S + 1, q) - 1;
-    const uint64_t y = p.pc_pre[q] - p.opre[p.src_doc_start[s]];  // stream position of the piece
+    // stream position of the piece, from the stream's start
+    const uint64_t y = p.pc_pre[q] - p.opre[p.src_doc_start[s]] - (p.start_tok ? p.start_tok[s] : 0);
     if (y % p.T == 0) {
         const uint64_t gw = p.src_win_start[s] + y / p.T;
         if (gw < p.n_windows) p.win_first[gw] = (uint32_t)q;
@@ -700,6 +712,16 @@ __global__ __launch_bounds__(256) void k_ramp_fixed_A(Plan p, const RampSpan* sp
     p.cum_A[x] = (uint32_t)a;
 }
 
+// each stream's token (in its merged order) where window next_win[s] begins,
+// or its total when ~0 (used up): pc_pre holds the order's token prefix
+__global__ __launch_bounds__(256) void k_stream_next(Plan p, const uint64_t* next_win, uint64_t* out) {
+    const uint32_t s = blockIdx.x * blockDim.x + threadIdx.x;
+    if (s >= p.S) return;
+    const uint64_t base = p.opre[p.src_doc_start[s]];
+    const uint64_t w = next_win[s];
+    out[s] = w == ~0ull ? p.opre[p.src_doc_start[s + 1]] - base : p.pc_pre[p.win_first[w]] - base;
+}
+
 // ------------------------------------------------------------------ lanes
 // stream of each document: (source, lane d mod L) = source·L + d mod L; an id
 // outside the sources stays invalid (0xFFFF) for the validation kernel
@@ -756,10 +778,11 @@ void launch_merge(Plan& p, hipStream_t st) {
 void launch_piece_count(Plan& p, hipStream_t st) {
     scan_len_u64(p.order, p.offsets, p.n_kept, p.opre, p.hist, st);
     if (p.wrap)
-        scan_wrap_pieces_u32(p.order, p.offsets, p.opre, p.src_doc_start, p.source, p.T, p.n_kept, p.piece_start,
-                             p.hist, st);
+        scan_wrap_pieces_u32(p.order, p.offsets, p.opre, p.src_doc_start, p.source, p.start_tok, p.T, p.n_kept,
+                             p.piece_start, p.hist, st);
     else
-        scan_pieces_u32(p.order, p.offsets, p.T, p.n_kept, p.piece_start, p.hist, st);
+        scan_pieces_u32(p.order, p.offsets, p.opre, p.src_doc_start, p.source, p.start_tok, p.T, p.n_kept,
+                        p.piece_start, p.hist, st);
 }
 
 void launch_pieces(Plan& p, hipStream_t st) {
@@ -849,6 +872,11 @@ void launch_ramp_fixed_A(Plan& p, const RampSpan* spans, uint32_t n_spans, const
                          hipStream_t st) {
     hipLaunchKernelGGL(k_ramp_fixed_A, dim3(blocks_for((U + 1) * p.S)), dim3(256), 0, st, p, spans, n_spans, ramp_n,
                        U);
+    DP_HIP(hipGetLastError());
+}
+
+void launch_stream_next(Plan& p, const uint64_t* next_win, uint64_t* out, hipStream_t st) {
+    hipLaunchKernelGGL(k_stream_next, dim3(blocks_for(p.S)), dim3(256), 0, st, p, next_win, out);
     DP_HIP(hipGetLastError());
 }
 

@@ -99,13 +99,25 @@ struct LenIn {
         return off[d + 1] - off[d];
     }
 };
+// next-fit: T-token pieces of the document at order position i; with a
+// stream start, only of its tokens from the start on
 struct PieceCountIn {
     const uint32_t* ids;
     const uint64_t* off;
+    const uint64_t* opre;           // token prefix over the order
+    const uint64_t* src_doc_start;  // [S+1] first order position of each stream
+    const uint16_t* source;
+    const uint64_t* start;          // [S] first token of each stream, or null
     uint32_t T;
     __device__ uint32_t operator()(uint64_t i) const {
         const uint32_t d = ids[i];
-        const uint64_t L = off[d + 1] - off[d];
+        uint64_t L = off[d + 1] - off[d];
+        if (start) {
+            const uint32_t s = source[d];
+            const uint64_t x = opre[i] - opre[src_doc_start[s]], cut = start[s];
+            const uint64_t o = cut > x ? cut - x : 0;
+            L = o < L ? L - o : 0;
+        }
         return (uint32_t)((L + T - 1) / T);
     }
 };
@@ -118,12 +130,19 @@ struct WrapPieceCountIn {
     const uint64_t* opre;           // token prefix over the order
     const uint64_t* src_doc_start;  // [S+1] first order position of each source
     const uint16_t* source;
+    const uint64_t* start;          // [S] first token of each stream, or null
     uint32_t T;
     __device__ uint32_t operator()(uint64_t i) const {
         const uint32_t d = ids[i];
-        const uint64_t L = off[d + 1] - off[d];
+        uint64_t L = off[d + 1] - off[d];
+        uint64_t x = opre[i] - opre[src_doc_start[source[d]]];
+        if (start) {  // stream positions from the start on
+            const uint64_t cut = start[source[d]];
+            const uint64_t o = cut > x ? cut - x : 0;
+            L = o < L ? L - o : 0;
+            x = x + o - cut;
+        }
         if (L == 0) return 0;
-        const uint64_t x = opre[i] - opre[src_doc_start[source[d]]];
         return (uint32_t)((x + L - 1) / T - x / T + 1);
     }
 };
@@ -159,14 +178,15 @@ void scan_len_u64(const uint32_t* ids, const uint64_t* offsets, uint64_t n, uint
                   hipStream_t st) {
     scan_impl<uint64_t>(LenIn{ids, offsets}, n, out, tmp, st);
 }
-void scan_pieces_u32(const uint32_t* ids, const uint64_t* offsets, uint32_t T, uint64_t n, uint32_t* out,
-                     void* tmp, hipStream_t st) {
-    scan_impl<uint32_t>(PieceCountIn{ids, offsets, T}, n, out, tmp, st);
+void scan_pieces_u32(const uint32_t* ids, const uint64_t* offsets, const uint64_t* opre,
+                     const uint64_t* src_doc_start, const uint16_t* source, const uint64_t* start, uint32_t T,
+                     uint64_t n, uint32_t* out, void* tmp, hipStream_t st) {
+    scan_impl<uint32_t>(PieceCountIn{ids, offsets, opre, src_doc_start, source, start, T}, n, out, tmp, st);
 }
 void scan_wrap_pieces_u32(const uint32_t* ids, const uint64_t* offsets, const uint64_t* opre,
-                          const uint64_t* src_doc_start, const uint16_t* source, uint32_t T, uint64_t n,
-                          uint32_t* out, void* tmp, hipStream_t st) {
-    scan_impl<uint32_t>(WrapPieceCountIn{ids, offsets, opre, src_doc_start, source, T}, n, out, tmp, st);
+                          const uint64_t* src_doc_start, const uint16_t* source, const uint64_t* start, uint32_t T,
+                          uint64_t n, uint32_t* out, void* tmp, hipStream_t st) {
+    scan_impl<uint32_t>(WrapPieceCountIn{ids, offsets, opre, src_doc_start, source, start, T}, n, out, tmp, st);
 }
 
 }  // namespace dp

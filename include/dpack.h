@@ -161,7 +161,19 @@ typedef struct pack_timings {
  * B_u/L seats that every lane follows).  Limits: L divides B and every ramp
  * batch, world divides L, n_sources·L ≤ 4096, Σ n_strata·L ≤ 65536.  With
  * lanes the per-source arrays of pack_cycle_info and of pack_inspect hold
- * n_sources·L entries, one per stream. */
+ * n_sources·L entries, one per stream.
+ *
+ * Stream starts (start_tokens).  NeuronSpark-Trainer README, Training: every
+ * update has one sequence length and updates never span a change of length;
+ * a branch forks from the state after a trunk cycle.  Reading taken: a
+ * context may cut each stream (source, or source and lane) from a given token
+ * of its merged order: documents before it are skipped, the one it falls in
+ * contributes its tokens from there on, and next-fit or wrap starts there.
+ * pack_cycle_info.stream_next_token reports where each stream's next cycle
+ * begins; a context built with those as start_tokens (the same corpus and
+ * recipe, any T, first_cycle the next cycle's number, tokens_start the
+ * tokens trained so far) goes on from there, and with the same T its cycles
+ * are byte for byte the ones the first context would have planned. */
 typedef struct pack_config {
     uint32_t abi_version;          /* DPACK_ABI_VERSION */
     uint32_t flags;                /* 0 or an or of PACK_FLAG_TIMING, _WRAP, _HELDOUT, _READ_RANDOM, _CUMULATIVE */
@@ -187,6 +199,9 @@ typedef struct pack_config {
     const uint64_t *ramp_from;     /* host [n_ramp]: tokens trained at which piece k starts */
     const uint64_t *ramp_tokens;   /* host [n_ramp]: tokens per update (B_k·T) within piece k */
     uint32_t n_lanes;              /* 0 or 1: no lanes; L > 1: Zephon lanes (see above) */
+    const uint64_t *start_tokens;  /* host [streams] or NULL: first token of each stream to cut (below) */
+    uint32_t first_cycle;          /* number of the first cycle (pack_cycle starts there) */
+    uint64_t tokens_start;         /* tokens trained before the first cycle (the ramp's count) */
 } pack_config;
 
 /* pack_init — build the plan of a corpus (hash and hold-out of every
@@ -216,6 +231,9 @@ typedef struct pack_cycle_info {
     uint32_t *per_update;          /* n_s: windows of each source in every update (the fixed
                                     * apportionment of B; with PACK_FLAG_CUMULATIVE or a ramp the
                                     * counts vary per update: PACK_INSPECT_CUM_TAKEN) */
+    uint64_t *stream_next_token;   /* token of each stream's merged order where the next cycle's
+                                    * windows begin (its total once used up): start_tokens of a
+                                    * context that goes on after this cycle */
 } pack_cycle_info;
 
 /* pack_cycle — plan cycle `cycle` (must be 0, then 1, 2, …): U updates, each

@@ -72,3 +72,5 @@ def compare_cycle(gi: dict, oi: "oracle.CycleInfo", op: "oracle.Plan"):
         assert gi["real_tokens"] == oi.real_tokens
         assert gi["learned_tokens"] == oi.learned_tokens
     assert gi["positions"] == oi.positions
+    if getattr(oi, "stream_next", None) is not None:
+        assert gi["stream_next_token"].tolist() == oi.stream_next.tolist()

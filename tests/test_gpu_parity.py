@@ -308,6 +308,63 @@ def test_lanes_each_rank_takes_whole_lanes(case):
             pk.close()
 
 
+RESUME_MODES = [dict(), dict(wrap=True), dict(read_random=True), dict(cumulative=True),
+                dict(ramp=((0, 128), (900, 384), (2500, 192))), dict(lanes=2), dict(heldout=True, wrap=True),
+                dict(cumulative=True, lanes=3, ramp=((0, 192), (1200, 384)), read_random=True)]
+
+
+def _resume_corpus(seed, **mode):
+    held = mode.get("heldout", False)
+    c = random_small(1300 + seed, n_docs=900, n_sources=3, max_strata=2, T=64, B=6, max_len=200, prompts=True,
+                     bp_max=6000 if held else 1500)
+    return c.replace(updates_per_cycle=3, **mode)
+
+
+@pytest.mark.parametrize("mi", range(len(RESUME_MODES)))
+def test_resume_at_reported_tokens(mi):
+    """A context cut from the tokens the GPU reports after a cycle goes on where the
+    first one would have: the same T gives its next cycle byte for byte; another T
+    matches the oracle's re-cut."""
+    c = _resume_corpus(mi, **RESUME_MODES[mi])
+    op = oracle.Plan(c)
+    pk = dp.Packer(c)
+    oi0 = op.cycle(0)
+    gi0 = pk.cycle(0)
+    compare_cycle(gi0, oi0, op)
+    oi1 = op.cycle(1)
+    gi1 = pk.cycle(1)
+    nxt = gi0["stream_next_token"].copy()
+    cr = c.replace(start_tokens=nxt, first_cycle=1, tokens_start=int(gi0["positions"]))
+    say("resume", mi, "same T")
+    pb = dp.Packer(cr)
+    ob = oracle.Plan(cr)
+    compare_plan(pb, ob)
+    gb = pb.cycle(1)
+    compare_cycle(gb, ob.cycle(1), ob)
+    assert gb["n_updates"] == gi1["n_updates"] and gb["windows_taken"].tolist() == gi1["windows_taken"].tolist()
+    n = gb["n_updates"]
+    compare_batch(to_np(pb.batch(0, n)), to_np(pk.batch(0, n)), f"resume {mi}: next cycle")
+    pb.close()
+    for T2 in ((128, 320) if c.ramp is None else ()):  # a ramp's tokens per update are multiples of its T
+        say("resume", mi, "T", T2)
+        c2 = cr.replace(T=T2)
+        o2 = oracle.Plan(c2)
+        try:
+            oi2 = o2.cycle(1)
+        except oracle.OracleError as e:
+            with pytest.raises(dp.DpackError) as ge:
+                dp.Packer(c2).cycle(1)
+            assert ge.value.code == e.code
+            continue
+        p2 = dp.Packer(c2)
+        compare_plan(p2, o2)
+        compare_cycle(p2.cycle(1), oi2, o2)
+        m = min(3, oi2.n_updates)
+        compare_batch(to_np(p2.batch(0, m)), o2.batch(0, m), f"resume {mi} T {T2}")
+        p2.close()
+    pk.close()
+
+
 PACKED_SHORT = {
     # windows of 1-3 real positions, many of them inside one 16-byte store group of the row
     "split_130": (lambda: _explicit([130] * 20, 64, 3), 1),
