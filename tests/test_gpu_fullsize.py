@@ -164,3 +164,40 @@ def test_full_size_ramp_parity():
     del g
     _CACHE.clear()
     torch.cuda.empty_cache()
+
+
+def test_full_size_new_length_after_a_cycle():
+    """The pre-train workload, 100 updates in cycle 0 at T = 4096, then a context
+    that goes on at T = 8192 (128 windows per update, the same tokens) from the
+    stream tokens the GPU reports: plan, cycle and sampled windows vs the oracle."""
+    import torch
+    _CACHE.clear()
+    c = make_corpus("pretrain").replace(updates_per_cycle=100)
+    say("generate", "pretrain for the re-cut")
+    tensors = dp.upload_corpus(c)
+    pk = dp.Packer(c, device_tensors=tensors)
+    gi = pk.cycle(0)
+    pk.close()
+    c2 = c.replace(T=8192, B=128, start_tokens=gi["stream_next_token"].copy(), first_cycle=1,
+                   tokens_start=int(gi["positions"]))
+    say("oracle plan", "re-cut at T 8192")
+    op = oracle.Plan(c2)
+    oi = op.cycle(1)
+    p2 = dp.Packer(c2, device_tensors=tensors)
+    compare_plan(p2, op)
+    compare_cycle(p2.cycle(1), oi, op)
+    n = oi.n_updates
+    say("emit", "re-cut", n, "updates")
+    g = p2.batch(0, n)
+    torch.cuda.synchronize()
+    r = np.random.default_rng(9)
+    for _ in range(24):
+        i, j = int(r.integers(n)), int(r.integers(c2.B))
+        tok, pos, dc, mask = op.emit_window(op.window_of(i, j))
+        assert np.array_equal(g["tokens"][i, j].cpu().numpy().view(np.uint32), tok), (i, j)
+        assert np.array_equal(g["mask"][i, j].cpu().numpy(), mask)
+        assert g["digests"][i, j].cpu().numpy().tobytes() == oracle.window_digest(tok, pos, dc, mask)
+    o = op.batch(n - 1, 1)
+    assert np.array_equal(g["digests"][n - 1].cpu().numpy(), o["digests"][0])
+    p2.close()
+    torch.cuda.empty_cache()
