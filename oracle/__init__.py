@@ -215,7 +215,7 @@ class _OrCorpus(C.Structure):
         ("cumulative", C.c_uint32),
         ("n_ramp", C.c_uint32), ("ramp_from", C.c_void_p), ("ramp_tokens", C.c_void_p),
         ("lanes", C.c_uint32), ("start_tokens", C.c_void_p), ("first_cycle", C.c_uint32),
-        ("tokens_start", C.c_uint64),
+        ("tokens_start", C.c_uint64), ("segment", C.c_void_p), ("n_segments", C.c_uint32),
     ]
 
 
@@ -259,6 +259,7 @@ class Plan:
             np.ascontiguousarray([int(t) for _, t in c.ramp], np.uint64),
             start_tokens=None if getattr(c, "start_tokens", None) is None else
             np.ascontiguousarray(c.start_tokens, np.uint64),
+            segment=None if getattr(c, "segment", None) is None else np.ascontiguousarray(c.segment, np.uint16),
         )
         k = self._keep
         D, S = k["source"].shape[0], k["weight"].shape[0]
@@ -278,7 +279,7 @@ class Plan:
             1 if getattr(c, "cumulative", False) else 0,
             0 if k["ramp_from"] is None else k["ramp_from"].shape[0], _ptr(k["ramp_from"]), _ptr(k["ramp_tokens"]),
             self.lanes, _ptr(k["start_tokens"]), int(getattr(c, "first_cycle", 0)),
-            int(getattr(c, "tokens_start", 0)))
+            int(getattr(c, "tokens_start", 0)), _ptr(k["segment"]), int(getattr(c, "n_segments", 1) or 1))
         err = C.c_int(0)
         self._p = lib.or_plan_build(C.byref(self._cs), C.byref(err))
         if not self._p:

@@ -488,6 +488,8 @@ typedef struct {
     const uint64_t *start_tokens;/* [streams] or NULL: first token of each stream to cut (C5s) */
     uint32_t first_cycle;        /* number of the first cycle planned */
     uint64_t tokens_start;       /* tokens trained before the first cycle (C6b) */
+    const uint16_t *segment;     /* [n_docs] or NULL: arrival of each document (C3a) */
+    uint32_t n_segments;         /* arrivals (0 or 1: one) */
 } or_corpus;
 
 typedef struct {
@@ -629,7 +631,6 @@ or_plan *or_plan_build(const or_corpus *cin, int *err)
     ALLOC(p->n_upd, S); ALLOC(p->slot_src, c->B); ALLOC(p->slot_k, c->B);
     ALLOC(p->kept_docs, S); ALLOC(p->kept_tokens, S); ALLOC(p->held_docs, S); ALLOC(p->held_tokens, S);
     ALLOC(p->cyc_start, S); ALLOC(p->cyc_next, S); ALLOC(p->taken, S);
-    ALLOC(gbase, S + 1);
 
     /* C1 + C2: hash every document, decide hold-out; a kept document is one
      * that is not held out and has at least one token.
@@ -651,15 +652,29 @@ or_plan *or_plan_build(const or_corpus *cin, int *err)
     }
 
     /* C3: per (source, stratum) group, kept documents ordered by
-     * (shuffle key, input index).  Groups are numbered source-major. */
+     * (shuffle key, input index).  Groups are numbered source-major.
+     * C3a. Streamed corpora ([NS] Concepts: a data line's cycles are each
+     * downloaded, tokenized, trained on and deleted; a file's documents are
+     * shuffled at tokenization; the files left open give the rest to the next
+     * cycles).  Reading: with arrivals (segments), a document belongs to the
+     * arrival it came with; each source's documents are ordered arrival by
+     * arrival, each arrival shuffled and strata-merged on its own, so the
+     * order of the arrivals so far does not change when more arrive, and the
+     * stream of a source goes on from one arrival's rest into the next.  Groups
+     * are numbered (source, arrival, stratum). */
+    const uint32_t NSEG = c->segment && c->n_segments > 1 ? c->n_segments : 1;
+#define SEG_OF(d) (NSEG > 1 ? (uint32_t)c->segment[d] : 0u)
+    for (uint64_t d = 0; d < D; d++)
+        if (SEG_OF(d) >= NSEG) { *err = OR_E_INVAL; goto fail; }
+    ALLOC(gbase, (uint64_t)S * NSEG + 1);   /* first group of each (source, arrival) */
     gbase[0] = 0;
-    for (uint32_t s = 0; s < S; s++) gbase[s + 1] = gbase[s] + c->n_strata[s];
+    for (uint32_t u = 0; u < S * NSEG; u++) gbase[u + 1] = gbase[u] + c->n_strata[u / NSEG];
     ALLOC(items, p->n_kept);
     {
         uint64_t m = 0;
         for (uint64_t d = 0; d < D; d++) {
             if (!p->keep[d]) continue;
-            items[m].group = gbase[c->source[d]] + c->stratum[d];
+            items[m].group = gbase[c->source[d] * NSEG + SEG_OF(d)] + c->stratum[d];
             items[m].d = (uint32_t)d;
             items[m].key = or_shuffle_key(c->seed, d);
             m++;
@@ -676,17 +691,18 @@ or_plan *or_plan_build(const or_corpus *cin, int *err)
     ALLOC(p->order, p->n_kept);
     {
         uint64_t out = 0, gi = 0;
-        for (uint32_t s = 0; s < S; s++) {
+        for (uint32_t u = 0; u < S * NSEG; u++) {   /* (source, arrival) units in order */
+            const uint32_t s = u / NSEG;
             uint32_t K = c->n_strata[s];
             uint64_t *head = calloc(K ? K : 1, sizeof(uint64_t));
             uint64_t *end = calloc(K ? K : 1, sizeof(uint64_t));
             uint64_t *a = calloc(K ? K : 1, sizeof(uint64_t));
             uint64_t *A = calloc(K ? K : 1, sizeof(uint64_t));
             if (!head || !end || !a || !A) { free(head); free(end); free(a); free(A); goto nomem; }
-            p->src_doc_start[s] = out;
+            if (u % NSEG == 0) p->src_doc_start[s] = out;
             for (uint32_t k = 0; k < K; k++) {
                 head[k] = gi;
-                while (gi < p->n_kept && items[gi].group == gbase[s] + k) {
+                while (gi < p->n_kept && items[gi].group == gbase[u] + k) {
                     A[k] += doc_len(c, items[gi].d);
                     gi++;
                 }
@@ -1282,7 +1298,7 @@ int or_plan_digest(const or_plan *p, uint8_t out[32])
     uint64_t bytes = 8 + 4 + 4 + 8 + 4 + 4 + (uint64_t)S * (8 + 4 + 4 + 4 + 8 + 8 + 8) + 4 + 4 + 8ull * S + 8 + 8
                      + (c->read_random ? 4 : 0) + (c->cumulative ? 4 : 0)
                      + (c->n_ramp ? 4 + 4 + 16ull * c->n_ramp + 8 : 0) + (p->lanes > 1 ? 8 : 0)
-                     + (c->start_tokens ? 4 + 8ull * S : 0);
+                     + (c->start_tokens ? 4 + 8ull * S : 0) + (c->segment && c->n_segments > 1 ? 8 : 0);
     uint8_t *buf = (uint8_t *)malloc(bytes), *w = buf;
     if (!buf) return OR_E_NOMEM;
     /* the packing mode and the stream (training / held-out) are part of the plan */
@@ -1302,6 +1318,7 @@ int or_plan_digest(const or_plan *p, uint8_t out[32])
         put(&w, 0x54525453u, 4);
         for (uint32_t s = 0; s < S; s++) put(&w, c->start_tokens[s], 8);
     }
+    if (c->segment && c->n_segments > 1) { put(&w, 0x53474553u, 4); put(&w, c->n_segments, 4); }  /* "SEGS" */
     put(&w, c->T, 4); put(&w, c->B, 4); put(&w, c->seed, 8); put(&w, S, 4); put(&w, c->pad_token, 4);
     for (uint32_t s = 0; s < S; s++) {
         put(&w, c->weight[s], 8); put(&w, c->bp[s], 4); put(&w, c->n_strata[s], 4);

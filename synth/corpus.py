@@ -54,6 +54,8 @@ class Corpus:
     start_tokens: Optional[np.ndarray] = None  # per stream: first token to cut (a resumed or re-cut stream)
     first_cycle: int = 0        # number of the first cycle planned
     tokens_start: int = 0       # tokens trained before the first cycle
+    segment: Optional[np.ndarray] = None  # per document: the arrival it came with (streamed corpora)
+    n_segments: int = 1         # arrivals
 
     @property
     def n_docs(self) -> int:
