@@ -70,7 +70,7 @@ class PackConfig(C.Structure):
         ("rank", C.c_uint32), ("world", C.c_uint32), ("stream", C.c_void_p),
         ("n_ramp", C.c_uint32), ("ramp_from", C.c_void_p), ("ramp_tokens", C.c_void_p),
         ("n_lanes", C.c_uint32), ("start_tokens", C.c_void_p), ("first_cycle", C.c_uint32),
-        ("tokens_start", C.c_uint64),
+        ("tokens_start", C.c_uint64), ("doc_segment", C.c_void_p), ("n_segments", C.c_uint32),
     ]
 
 
@@ -266,7 +266,9 @@ class Packer:
             self._host["ramp_from"].ctypes.data if ramp is not None else None,
             self._host["ramp_tokens"].ctypes.data if ramp is not None else None,
             self.lanes, self._host["start_tokens"].ctypes.data if st0 is not None else None,
-            int(getattr(corpus, "first_cycle", 0)), int(getattr(corpus, "tokens_start", 0)))
+            int(getattr(corpus, "first_cycle", 0)), int(getattr(corpus, "tokens_start", 0)),
+            d["segment"].data_ptr() if d.get("segment") is not None else None,
+            int(getattr(corpus, "n_segments", 1) or 1))
         self.ctx = pack_init(self.cfg)
         self.per = corpus.B // world
         self.batches = None  # windows of each update of the current cycle (all ranks)
@@ -390,4 +392,5 @@ def upload_corpus(corpus, device: str = "cuda") -> dict:
 
     return dict(tokens=t(corpus.tokens, np.int32), offsets=t(corpus.offsets, np.int64),
                 source=t(corpus.source, np.int16), stratum=t(corpus.stratum, np.int16),
-                prompt_len=t(corpus.prompt_len, np.int32))
+                prompt_len=t(corpus.prompt_len, np.int32),
+                segment=t(getattr(corpus, "segment", None), np.int16))

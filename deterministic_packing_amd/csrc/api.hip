@@ -217,7 +217,7 @@ size_t carve(pack_ctx& c, char* base) {
     dp::Plan& p = c.p;
     const uint64_t D = p.n_docs, S = p.S, G = p.G, B = p.B, P = p.cap_pieces;
     Carver k{base};
-    p.gbase = k.take<uint32_t>(S + 1);
+    p.gbase = k.take<uint32_t>(S * p.n_seg + 1);
     p.n_strata = k.take<uint32_t>(S);
     p.weight = k.take<uint64_t>(c.S_real);  // the recipe's weights (read by the mixture over the real sources)
     p.bp = k.take<uint32_t>(S);
@@ -363,7 +363,9 @@ void check_config(const pack_config* cfg) {
         G += k;
         if (cfg->holdout_bp[s] > 10000) bad("holdout_bp must be <= 10000");
     }
-    if (G > 65536) bad("at most 65536 (source, stratum) groups");
+    const uint64_t NSEG = cfg->doc_segment && cfg->n_segments > 1 ? cfg->n_segments : 1;
+    if (cfg->n_segments > 65536) bad("at most 65536 arrivals");
+    if (G * NSEG > 65536) bad("at most 65536 (source, arrival, stratum) groups");
     unsigned __int128 W = 0;
     for (uint32_t s = 0; s < cfg->n_sources; ++s) W += cfg->share_weight[s];
     if (W == 0 || (W >> 64) != 0) bad("share weights must sum to [1, 2^64)");
@@ -398,7 +400,7 @@ void check_config(const pack_config* cfg) {
             if ((cfg->ramp_tokens[k] / T) % L) bad("lanes must divide every ramp piece's batch");
         if (L % cfg->world) bad("world must divide the lanes (each rank takes whole lanes)");
         if ((uint64_t)cfg->n_sources * L > 4096) bad("n_sources x lanes must be at most 4096");
-        if (G * L > 65536) bad("(source, stratum) groups x lanes must be at most 65536");
+        if (G * L * NSEG > 65536) bad("(source, arrival, stratum) groups x lanes must be at most 65536");
     }
     if ((cfg->flags & PACK_FLAG_CUMULATIVE) || cfg->n_ramp) {
         const uint64_t cap = cfg->n_docs + cfg->n_tokens / T;  // windows ≤ pieces ≤ cap
@@ -428,7 +430,7 @@ void build_plan(pack_ctx& c) {
     hipStream_t st = c.st;
     // recipe to the device
     c.pin_off = 0;
-    h2d_staged(c, p.gbase, c.gbase.data(), p.S + 1);
+    h2d_staged(c, p.gbase, c.gbase.data(), (uint64_t)p.S * p.n_seg + 1);
     h2d_staged(c, p.n_strata, c.n_strata.data(), p.S);
     h2d_staged(c, p.weight, c.weight_real.data(), c.S_real);
     if (!c.start_tokens.empty()) {
@@ -461,6 +463,7 @@ void build_plan(pack_ctx& c) {
         if (err & 4u) m += " a source id >= n_sources;";
         if (err & 8u) m += " a stratum id >= n_strata of its source;";
         if (err & 16u) m += " doc_offsets[n_docs] > n_tokens;";
+        if (err & 32u) m += " an arrival id >= n_segments;";
         throw InvalError{m};
     }
 
@@ -617,8 +620,9 @@ int pack_init(const pack_config* cfg, pack_ctx** out) {
         c->lanes = L;
         c->S_real = Sr;
         c->weight_real.assign(cfg->share_weight, cfg->share_weight + Sr);
+        const uint32_t NSEG = cfg->doc_segment && cfg->n_segments > 1 ? cfg->n_segments : 1;
         c->n_strata.resize(S);
-        c->gbase.resize(S + 1);
+        c->gbase.resize((uint64_t)S * NSEG + 1);
         c->bp.resize(S);
         c->weight.resize(S);
         uint32_t G = 0;
@@ -626,11 +630,13 @@ int pack_init(const pack_config* cfg, pack_ctx** out) {
             c->n_strata[s] = cfg->n_strata ? cfg->n_strata[s / L] : 1u;
             c->bp[s] = cfg->holdout_bp[s / L];
             c->weight[s] = cfg->share_weight[s / L];
-            c->gbase[s] = G;
-            G += c->n_strata[s];
+        }
+        for (uint32_t u = 0; u < S * NSEG; ++u) {  // groups (stream, arrival, stratum)
+            c->gbase[u] = G;
+            G += c->n_strata[u / NSEG];
         }
         for (uint32_t r = 0; r < Sr; ++r) c->W += c->weight_real[r];
-        c->gbase[S] = G;
+        c->gbase[(uint64_t)S * NSEG] = G;
         DP_HIP(hipGetDevice(&c->device));
 
         dp::Plan& p = c->p;
@@ -639,6 +645,8 @@ int pack_init(const pack_config* cfg, pack_ctx** out) {
         p.source = cfg->doc_source;
         p.stratum = cfg->doc_stratum;
         p.prompt_len = cfg->doc_prompt_len;
+        p.segment = NSEG > 1 ? cfg->doc_segment : nullptr;
+        p.n_seg = NSEG;
         p.n_tokens = cfg->n_tokens;
         p.n_docs = cfg->n_docs;
         p.S = S;
@@ -910,6 +918,10 @@ int pack_cycle(pack_ctx* c, uint32_t cycle, pack_cycle_info* info) {
         if (!c->start_tokens.empty()) {                // "STRT": the streams' first tokens
             put(msg, 0x54525453u, 4);
             for (uint32_t s = 0; s < S; ++s) put(msg, c->start_tokens[s], 8);
+        }
+        if (p.n_seg > 1) {                             // "SEGS": documents ordered arrival by arrival
+            put(msg, 0x53474553u, 4);
+            put(msg, p.n_seg, 4);
         }
         put(msg, p.T, 4);
         put(msg, p.B, 4);

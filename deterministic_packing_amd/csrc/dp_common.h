@@ -89,6 +89,8 @@ struct Plan {
     const uint16_t* source;
     const uint16_t* stratum;      // may be null
     const uint32_t* prompt_len;   // may be null
+    const uint16_t* segment;      // may be null: the arrival of each document (n_seg > 1)
+    uint32_t n_seg;               // arrivals (1: none); groups are (stream, arrival, stratum)
     uint64_t n_tokens, n_docs;
     uint32_t S, G, T, B;
     uint64_t seed;
@@ -104,7 +106,7 @@ struct Plan {
     uint32_t S_real;              // the recipe's sources (S = S_real·lanes streams)
 
     // recipe on device
-    uint32_t* gbase;              // [S+1] first group of each source
+    uint32_t* gbase;              // [S·n_seg+1] first group of each (stream, arrival)
     uint32_t* n_strata;           // [S]
     uint64_t* weight;             // [S]
     uint32_t* bp;                 // [S]

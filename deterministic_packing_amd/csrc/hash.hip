@@ -22,6 +22,7 @@ enum : uint32_t {
     ERR_SOURCE = 4u,       // source id out of range
     ERR_STRATUM = 8u,      // stratum id out of range for its source
     ERR_TOKENS = 16u,      // last offset beyond n_tokens
+    ERR_SEGMENT = 32u,     // arrival id out of range
 };
 
 __global__ __launch_bounds__(256) void k_validate(Plan p) {
@@ -32,12 +33,15 @@ __global__ __launch_bounds__(256) void k_validate(Plan p) {
     if (o1 < o0) err |= ERR_OFFSETS;
     else if (o1 - o0 > 0xFFFFFFFFull) err |= ERR_DOC_LEN;
     const uint32_t s = p.source[d];
+    const uint32_t g = p.n_seg > 1 ? p.segment[d] : 0u;
     if (s >= p.S) {
         err |= ERR_SOURCE;
+    } else if (g >= p.n_seg) {
+        err |= ERR_SEGMENT;
     } else {
         const uint32_t k = p.stratum ? p.stratum[d] : 0u;
         if (k >= p.n_strata[s]) err |= ERR_STRATUM;
-        else p.group[d] = p.gbase[s] + k;
+        else p.group[d] = p.gbase[s * p.n_seg + g] + k;  // groups (stream, arrival, stratum)
     }
     if (d == p.n_docs - 1 && o1 > p.n_tokens) err |= ERR_TOKENS;
     if (err) atomicOr(p.err, err);

@@ -83,7 +83,9 @@ __global__ __launch_bounds__(256) void k_merge(Plan p, const uint32_t* val) {
     const uint32_t d = val[i];
     const uint32_t g = p.group[d];
     const uint32_t s = p.source[d];
-    const uint32_t g0 = p.gbase[s], K = p.n_strata[s], k = g - g0;
+    // merge unit: the (stream, arrival) of the document; its strata are groups g0 .. g0+K−1
+    const uint32_t u = s * p.n_seg + (p.n_seg > 1 ? p.segment[d] : 0u);
+    const uint32_t g0 = p.gbase[u], K = p.n_strata[s], k = g - g0;
     const uint32_t b0 = p.group_start[g];
     const uint64_t a = p.gpre[i] - p.gpre[b0];
     const uint64_t A = p.gpre[p.group_start[g + 1]] - p.gpre[b0];
@@ -113,7 +115,7 @@ __global__ __launch_bounds__(256) void k_merge(Plan p, const uint32_t* val) {
 
 __global__ void k_src_doc_start(Plan p) {
     const uint32_t s = blockIdx.x * blockDim.x + threadIdx.x;
-    if (s <= p.S) p.src_doc_start[s] = p.group_start[p.gbase[s]];
+    if (s <= p.S) p.src_doc_start[s] = p.group_start[p.gbase[s * p.n_seg]];  // a stream's first arrival
 }
 
 // ------------------------------------------------------------------ A5 pieces

@@ -173,7 +173,19 @@ typedef struct pack_timings {
  * begins; a context built with those as start_tokens (the same corpus and
  * recipe, any T, first_cycle the next cycle's number, tokens_start the
  * tokens trained so far) goes on from there, and with the same T its cycles
- * are byte for byte the ones the first context would have planned. */
+ * are byte for byte the ones the first context would have planned.
+ *
+ * Streamed corpora (doc_segment, n_segments).  NeuronSpark-Trainer README,
+ * Concepts: a data line's cycles are each downloaded, tokenized, trained on
+ * and deleted; a file's documents are shuffled at tokenization; files left
+ * open give the rest to the next cycles.  Reading taken: a document belongs
+ * to the arrival it came with; each stream's documents go arrival by arrival,
+ * each arrival shuffled and strata-merged on its own, so the order of the
+ * arrivals so far does not change when more arrive.  A context per arrival
+ * over the documents so far (appended, so indices stay), with start_tokens
+ * from the previous context's stream_next_token, goes on where the previous
+ * cycle stopped: the rest of the earlier arrivals first, then the new one.
+ * Limit: Σ n_strata · lanes · n_segments ≤ 65536 groups. */
 typedef struct pack_config {
     uint32_t abi_version;          /* DPACK_ABI_VERSION */
     uint32_t flags;                /* 0 or an or of PACK_FLAG_TIMING, _WRAP, _HELDOUT, _READ_RANDOM, _CUMULATIVE */
@@ -202,6 +214,8 @@ typedef struct pack_config {
     const uint64_t *start_tokens;  /* host [streams] or NULL: first token of each stream to cut (below) */
     uint32_t first_cycle;          /* number of the first cycle (pack_cycle starts there) */
     uint64_t tokens_start;         /* tokens trained before the first cycle (the ramp's count) */
+    const uint16_t *doc_segment;   /* device [n_docs] or NULL: the arrival of each document (below) */
+    uint32_t n_segments;           /* arrivals: doc_segment < n_segments (0 or 1: one arrival) */
 } pack_config;
 
 /* pack_init — build the plan of a corpus (hash and hold-out of every

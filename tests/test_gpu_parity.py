@@ -365,6 +365,57 @@ def test_resume_at_reported_tokens(mi):
     pk.close()
 
 
+SEG_CASES = [(0, 2, dict()), (1, 3, dict(wrap=True)), (2, 5, dict(lanes=2)), (3, 3, dict(cumulative=True)),
+             (4, 4, dict(read_random=True, ramp=((0, 128), (1500, 384)))), (5, 2, dict(heldout=True))]
+
+
+@pytest.mark.parametrize("case", range(len(SEG_CASES)))
+def test_arrivals_parity(case):
+    """Streamed corpora: documents ordered arrival by arrival, with the other modes."""
+    from test_oracle_segments import _arrivals
+    seed, n_seg, mode = SEG_CASES[case]
+    c, _ = _arrivals(1400 + seed, n_seg)
+    if mode.get("heldout"):
+        c = c.replace(holdout_bp=np.full(c.n_sources, 5000, np.uint32))
+    _parity_run(c.replace(**mode), "arrivals", case)
+
+
+@pytest.mark.parametrize("wrap", [False, True])
+def test_a_context_per_arrival_on_the_gpu(wrap):
+    """A context per arrival, each going on from the tokens the previous GPU context
+    reported, plans the cycles one context over every arrival plans."""
+    from test_oracle_segments import _arrivals, _prefix
+    n_seg = 4
+    c, cuts = _arrivals(1500 + int(wrap), n_seg, n_docs=2400, even=True, updates_per_cycle=4)
+    c = c.replace(wrap=wrap)
+    full = dp.Packer(c)
+    nxt, tokens = None, 0
+    for cyc in range(n_seg):
+        fi = full.cycle(cyc)
+        cc = _prefix(c, int(cuts[cyc + 1]))
+        if cyc:
+            cc = cc.replace(start_tokens=nxt, first_cycle=cyc, tokens_start=tokens)
+        say("arrival", cyc, "wrap", wrap)
+        part = dp.Packer(cc)
+        pi = part.cycle(cyc)
+        assert pi["n_updates"] == fi["n_updates"] and pi["windows_taken"].tolist() == fi["windows_taken"].tolist()
+        compare_batch(to_np(part.batch(0, pi["n_updates"])), to_np(full.batch(0, fi["n_updates"])), f"arrival {cyc}")
+        assert pi["stream_next_token"].tolist() == fi["stream_next_token"].tolist()
+        nxt, tokens = pi["stream_next_token"].copy(), int(tokens + pi["positions"])
+        part.close()
+    full.close()
+
+
+def test_bad_arrival_id_is_an_error():
+    from test_oracle_segments import _arrivals
+    c, _ = _arrivals(1600, 2)
+    seg = c.segment.copy()
+    seg[3] = 7
+    with pytest.raises(dp.DpackError) as e:
+        dp.Packer(c.replace(segment=seg))
+    assert e.value.code == dp.PACK_E_INVAL and "arrival" in str(e.value)
+
+
 PACKED_SHORT = {
     # windows of 1-3 real positions, many of them inside one 16-byte store group of the row
     "split_130": (lambda: _explicit([130] * 20, 64, 3), 1),
@@ -432,9 +483,17 @@ def _parity_run(c, kind, arg):
         o = op.batch(st, n)
         g = to_np(pk.batch(st, n))
         compare_batch(g, o, f"{kind}{arg} step {st}")
-        fp = pk.fingerprint(pk.batch(st, n)["digests"]).cpu().numpy()
-        for i in range(n):
-            assert fp[i].tobytes() == oracle.batch_fingerprint(o["digests"][i])
+        if getattr(c, "ramp", None) is None:
+            fp = pk.fingerprint(pk.batch(st, n)["digests"]).cpu().numpy()
+            for i in range(n):
+                assert fp[i].tobytes() == oracle.batch_fingerprint(o["digests"][i])
+        else:  # batches of a ramp: each update's own digests
+            fp = pk.fingerprint_steps(st, n, pk.batch(st, n)["digests"]).cpu().numpy()
+            x = 0
+            for i in range(n):
+                Bb = int(oi.batches[st + i])
+                assert fp[i].tobytes() == oracle.batch_fingerprint(o["digests"][x:x + Bb])
+                x += Bb
     pk.close()
 
 

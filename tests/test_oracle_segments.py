@@ -18,16 +18,31 @@ import oracle
 from synth.corpus import Corpus, random_small
 
 
-def _arrivals(seed, n_seg, n_docs=1600, **kw):
-    """A corpus whose documents are sorted by arrival (indices grow with it)."""
+def _arrivals(seed, n_seg, n_docs=1600, even=False, **kw):
+    """A corpus whose documents are sorted by arrival (indices grow with it); the
+    arrivals are of random sizes, or of equal ones with `even`."""
     c = random_small(seed, n_docs=n_docs, n_sources=kw.pop("S", 3), max_strata=2, T=64, B=kw.pop("B", 6),
                      max_len=150, prompts=True, bp_max=1500)
     r = np.random.default_rng(seed + 7)
-    cuts = np.sort(r.choice(np.arange(1, c.n_docs), size=n_seg - 1, replace=False))
+    c = _permuted(c, r.permutation(c.n_docs))   # the sources arrive mixed
+    if even:
+        cuts = np.arange(1, n_seg) * (c.n_docs // n_seg)
+    else:
+        cuts = np.sort(r.choice(np.arange(1, c.n_docs), size=n_seg - 1, replace=False))
     seg = np.zeros(c.n_docs, np.uint16)
     for k, x in enumerate(cuts):
         seg[x:] = k + 1
     return c.replace(segment=seg, n_segments=n_seg, **kw), np.concatenate([[0], cuts, [c.n_docs]])
+
+
+def _permuted(c, perm):
+    """The same documents, document i of the result being document perm[i]."""
+    L = c.lengths()[perm]
+    offsets = np.concatenate([[0], np.cumsum(L)]).astype(c.offsets.dtype)
+    tokens = np.concatenate([c.tokens[int(c.offsets[d]):int(c.offsets[d + 1])] for d in perm]).astype(c.tokens.dtype)
+    return Corpus(c.name, tokens, offsets, c.source[perm], c.stratum[perm],
+                  None if c.prompt_len is None else c.prompt_len[perm], c.n_strata, c.weight, c.holdout_bp,
+                  T=c.T, B=c.B, updates_per_cycle=c.updates_per_cycle, seed=c.seed, pad_token=c.pad_token)
 
 
 def _prefix(c, n):
@@ -91,7 +106,7 @@ def test_a_context_per_arrival_plans_the_same_cycles(wrap):
     context's stream tokens, equals cycle c of one context over every arrival (the
     cycles here never reach a stream's still open last window)."""
     n_seg = 4
-    c, cuts = _arrivals(6, n_seg, n_docs=2400, updates_per_cycle=4)
+    c, cuts = _arrivals(6, n_seg, n_docs=2400, even=True, updates_per_cycle=4)
     c = c.replace(wrap=wrap)
     full = oracle.Plan(c)
     nxt, tokens = None, 0
