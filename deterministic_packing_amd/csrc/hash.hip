@@ -109,23 +109,53 @@ __device__ __forceinline__ void load_tokens(const uint32_t* tokens, uint64_t t0,
     x[TPT] = tokens[t0 + TPT];
 }
 
+// A tile's documents [lo, hi] (from the tile table) and this thread's entry of
+// their offsets, offsets[lo + threadIdx.x] (loaded ahead of the tile, so the
+// staging below waits on no global load; entries past the first 256 are read
+// at staging time).
+struct TileMeta {
+    uint64_t lo, hi, o;
+};
+
+__device__ __forceinline__ void meta_first(const uint32_t* first, uint64_t tile, TileMeta& m) {
+    m.lo = first[tile];
+    m.hi = first[tile + 1];
+}
+
+__device__ __forceinline__ void meta_offset(const Plan& p, TileMeta& m) {
+    m.o = threadIdx.x < m.hi - m.lo + 2 ? p.offsets[m.lo + threadIdx.x] : 0;
+}
+
 // One tile: the tile's document offsets into LDS, each thread's documents and
 // NH terms, and the per-document sums into S (see above).  x holds the
-// thread's tokens from t0 (zeros past end).
-__device__ __forceinline__ void hash_tile(const Plan& p, const uint32_t* first, uint64_t base, uint64_t end,
-                                          uint64_t tile, const uint32_t (&x)[TPT + 1], uint64_t* s_off,
+// thread's tokens from t0 (zeros past end).  FULL: every thread's TPT + 1
+// tokens lie below end.
+//
+// A wavefront whose tokens and last partner lie in one document (most of them:
+// a wavefront spans 1,025 tokens, documents average about 1,200) takes a
+// branch-free path: the thread's pairs start at the positions whose offset in
+// the document is even, TPT/2 products accumulated with 32x32→64 multiply-adds,
+// then one wavefront sum and one atomic.  Other wavefronts walk the thread's
+// positions with document offsets kept in 32 bits: only r mod 2^32 enters a
+// key, and a thread's positions are within TPT + 1 of its document's end.
+template <bool FULL>
+__device__ __forceinline__ void hash_tile(const Plan& p, uint64_t base, uint64_t end, uint64_t tile,
+                                          const uint32_t (&x)[TPT + 1], const TileMeta& m, uint64_t* s_off,
                                           uint64_t* S) {
     const uint32_t lane = lane_id();
     const uint64_t t0 = base + tile * HT + (uint64_t)TPT * threadIdx.x;  // this thread's first token
-    const uint64_t d_lo = first[tile], d_hi = first[tile + 1];  // documents of the tile
-    Offs off{p.offsets, s_off, d_lo, d_hi - d_lo + 2 <= OCAP + 1};
+    const uint64_t d_lo = m.lo, d_hi = m.hi;  // documents of the tile
+    const uint64_t n_off = d_hi - d_lo + 2;
+    Offs off{p.offsets, s_off, d_lo, n_off <= OCAP + 1};
     __syncthreads();  // the previous tile's readers are done with s_off
-    if (off.staged)
-        for (uint64_t i = threadIdx.x; i < d_hi - d_lo + 2; i += blockDim.x) s_off[i] = p.offsets[d_lo + i];
+    if (off.staged) {
+        if (threadIdx.x < n_off) s_off[threadIdx.x] = m.o;
+        for (uint64_t i = threadIdx.x + blockDim.x; i < n_off; i += blockDim.x) s_off[i] = p.offsets[d_lo + i];
+    }
     __syncthreads();
-    const bool active = t0 < end;
-    uint32_t fd = 0xFFFFFFFFu, ld = 0xFFFFFFFFu;
-    uint64_t v1 = 0, v2 = 0;
+    const bool active = FULL || t0 < end;
+    uint32_t cur = 0;
+    uint64_t ob = 0, nb = 0;
     if (active) {
         // document of t0: search between the tile's first document and the next tile's
         uint64_t lo = d_lo, hi = d_hi + 1;  // d in [lo, hi)
@@ -134,15 +164,44 @@ __device__ __forceinline__ void hash_tile(const Plan& p, const uint32_t* first, 
             if (off[mid] <= t0) lo = mid;
             else hi = mid;
         }
-        uint32_t cur = (uint32_t)lo;
+        cur = (uint32_t)lo;
+        ob = off[cur];
+        nb = off[cur + 1];
+    }
+    if (__all(active && t0 + TPT < nb)) {
+        // one document under the whole wavefront: offsets r = rb + j, pairs at
+        // j = par, par + 2, ..., keys k = (r + 1)·φ32 and k + φ32
+        const uint32_t rb = (uint32_t)(t0 - ob);
+        const uint32_t par = rb & 1u;
+        const uint32_t kp = (rb + 1u + par) * PHI32;
+        uint64_t acc = 0;
+#pragma unroll
+        for (uint32_t i = 0; i < TPT / 2; ++i) {
+            const uint32_t a = par ? x[2 * i + 1] : x[2 * i];
+            const uint32_t b = par ? x[2 * i + 2] : x[2 * i + 1];
+            const uint32_t k0 = kp + 2u * i * PHI32;
+            acc += (uint64_t)(a + k0) * (uint64_t)(b + k0 + PHI32);
+        }
+        acc = wave_sum_u64(acc);
+        if (lane == 0) atomicAdd((unsigned long long*)&S[cur], (unsigned long long)acc);
+        return;
+    }
+    uint32_t fd = 0xFFFFFFFFu, ld = 0xFFFFFFFFu;
+    uint64_t v1 = 0, v2 = 0;
+    if (active) {
         fd = cur;
-        uint64_t ob = off[cur], nb = off[cur + 1];
+        // rem: positions from t0 before the document's end, capped at TPT + 1;
+        // kb: the key of offset rb, (rb + 1)·φ32, so offset rb + j has kb + j·φ32
+        uint32_t rem = (uint32_t)std::min<uint64_t>(nb - t0, TPT + 1);
+        uint32_t rb = (uint32_t)(t0 - ob);
+        uint32_t kb = (rb + 1u) * PHI32;
+        bool e0 = (rb & 1u) == 0;  // offset rb + j is even iff e0 == (j even)
+        const uint32_t n_in = FULL ? TPT : (uint32_t)std::min<uint64_t>(end - t0, TPT);
         uint64_t acc = 0;
 #pragma unroll
         for (uint32_t j = 0; j < TPT; ++j) {
-            const uint64_t pos = t0 + j;
-            if (pos < end) {
-                if (pos >= nb) {  // the next document starts: flush the finished one
+            if (FULL || j < n_in) {
+                if (j >= rem) {  // the next document starts: flush the finished one
                     if (cur == fd) v1 = acc;
                     else atomicAdd((unsigned long long*)&S[cur], (unsigned long long)acc);
                     acc = 0;
@@ -150,10 +209,17 @@ __device__ __forceinline__ void hash_tile(const Plan& p, const uint32_t* first, 
                         ++cur;
                         ob = nb;
                         nb = off[cur + 1];
-                    } while (pos >= nb);
+                    } while (t0 + j >= nb);
+                    rem = (uint32_t)std::min<uint64_t>(nb - t0, TPT + 1);
+                    rb = (uint32_t)(t0 - ob);  // the offset of t0, mod 2^32
+                    kb = (rb + 1u) * PHI32;
+                    e0 = (rb & 1u) == 0;
                 }
-                const uint64_t r = pos - ob;
-                if ((r & 1) == 0) acc += pair_term(x[j], pos + 1 < nb ? x[j + 1] : 0u, r);
+                // a term at even offsets only: its first factor is zeroed at odd ones
+                const uint32_t k0 = kb + j * PHI32;
+                const uint32_t b = j + 1 < rem ? x[j + 1] : 0u;
+                const uint32_t a = (e0 == ((j & 1u) == 0)) ? x[j] + k0 : 0u;
+                acc += (uint64_t)a * (uint64_t)(b + k0 + PHI32);
             }
         }
         if (cur == fd) v1 = acc;
@@ -181,9 +247,11 @@ __device__ __forceinline__ void hash_tile(const Plan& p, const uint32_t* first, 
 }
 
 // Tiles [0, nfast) have every thread's TPT + 1 tokens inside [base, end):
-// they run two at a time, the next tile's loads issued (unconditionally, at a
-// clamped tile) before the current tile is hashed.  The last tiles load
-// element by element with bounds checks.
+// they run two at a time in a software pipeline whose loads are issued (at a
+// clamped tile, unconditionally) before the current tile is hashed: the next
+// tile's tokens and offset entries, and the tile table two tiles ahead.  A
+// tile's hashing then waits on no global load.  The last tiles load element
+// by element with bounds checks.
 __global__ __launch_bounds__(256) void k_hash_flat(Plan p, const uint32_t* first, uint64_t base, uint64_t end,
                                                    uint64_t ntiles, uint64_t nfast, uint64_t* S) {
     __shared__ uint64_t s_off[OCAP + 1];
@@ -192,16 +260,32 @@ __global__ __launch_bounds__(256) void k_hash_flat(Plan p, const uint32_t* first
     uint64_t ta = blockIdx.x;
     if (ta < nfast) {
         uint32_t xa[TPT + 1], xb[TPT + 1];
+        TileMeta ma, mb, mc;
+        meta_first(first, ta, ma);
+        meta_offset(p, ma);
         load_tokens(tok, base + ta * HT + (uint64_t)TPT * threadIdx.x, xa);
+        uint64_t tb = ta + step, cb = tb < nfast ? tb : ta;  // cb: a tile below nfast to load from
+        meta_first(first, cb, mb);
         while (true) {
-            const uint64_t tb = ta + step;
-            load_tokens(tok, base + (tb < nfast ? tb : ta) * HT + (uint64_t)TPT * threadIdx.x, xb);
-            hash_tile(p, first, base, end, ta, xa, s_off, S);
+            // ta ready (xa, ma); tb's table entries ready (mb)
+            load_tokens(tok, base + cb * HT + (uint64_t)TPT * threadIdx.x, xb);
+            meta_offset(p, mb);
+            const uint64_t tc = tb + step, cc = tc < nfast ? tc : cb;
+            meta_first(first, cc, mc);
+            hash_tile<true>(p, base, end, ta, xa, ma, s_off, S);
             if (tb >= nfast) break;
-            ta = tb + step;
-            load_tokens(tok, base + (ta < nfast ? ta : tb) * HT + (uint64_t)TPT * threadIdx.x, xa);
-            hash_tile(p, first, base, end, tb, xb, s_off, S);
-            if (ta >= nfast) break;
+            // tb ready (xb, mb); tc's table entries ready (mc)
+            load_tokens(tok, base + cc * HT + (uint64_t)TPT * threadIdx.x, xa);
+            ma = mc;
+            meta_offset(p, ma);
+            const uint64_t td = tc + step, cd = td < nfast ? td : cc;
+            meta_first(first, cd, mc);
+            hash_tile<true>(p, base, end, tb, xb, mb, s_off, S);
+            if (tc >= nfast) break;
+            ta = tc;
+            tb = td;
+            cb = cd;
+            mb = mc;
         }
     }
     for (uint64_t tile = nfast + blockIdx.x; tile < ntiles; tile += step) {
@@ -209,7 +293,10 @@ __global__ __launch_bounds__(256) void k_hash_flat(Plan p, const uint32_t* first
         uint32_t x[TPT + 1];
 #pragma unroll
         for (uint32_t j = 0; j <= TPT; ++j) x[j] = (t0 + j < end) ? tok[t0 + j] : 0u;
-        hash_tile(p, first, base, end, tile, x, s_off, S);
+        TileMeta m;
+        meta_first(first, tile, m);
+        meta_offset(p, m);
+        hash_tile<false>(p, base, end, tile, x, m, s_off, S);
     }
 }
 
