@@ -85,6 +85,12 @@ def main():
                     help="per-update window counts from each cycle's cumulative quotas (PACK_FLAG_CUMULATIVE)")
     ap.add_argument("--read-random", action="store_true",
                     help="each cycle's windows of a source read in a random order (PACK_FLAG_READ_RANDOM)")
+    ap.add_argument("--heldout", action="store_true",
+                    help="the held-out (validation) stream instead of the training one, cycle of maximal length")
+    ap.add_argument("--arrivals", type=int, default=1,
+                    help="streamed corpus: each document carries one of N arrivals (seeded uniform labels)")
+    ap.add_argument("--resume", action="store_true",
+                    help="time cycle 1 of a context that starts each stream at the token cycle 0 reported")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -109,15 +115,29 @@ def main():
         corpus = corpus.replace(ramp=((0, corpus.B // 2 * corpus.T), (100_000_000, corpus.B * corpus.T)))
     if args.lanes > 1:
         corpus = corpus.replace(lanes=args.lanes)
+    if args.heldout:
+        corpus = corpus.replace(heldout=True, updates_per_cycle=0)
+    if args.arrivals > 1:
+        r = np.random.default_rng(np.random.SeedSequence([7, args.arrivals]))
+        corpus = corpus.replace(segment=r.integers(0, args.arrivals, size=corpus.n_docs).astype(np.uint16),
+                                n_segments=args.arrivals)
     log(f"corpus {args.workload} scale {args.scale}: {corpus.n_docs} docs, {corpus.n_tokens} tokens "
         f"({time.time() - t0:.1f}s)")
     tensors = dp.upload_corpus(corpus)
     torch.cuda.synchronize()
     log("corpus resident in HBM")
 
+    if args.resume:
+        # each stream from the token where cycle 0 left it: a context for cycle 1 on
+        first = dp.Packer(corpus, device_tensors=tensors)
+        i0 = first.cycle(0)
+        corpus = corpus.replace(start_tokens=i0["stream_next_token"].copy(), first_cycle=1,
+                                tokens_start=int(i0["positions"]))
+        first.close()
+    cyc = corpus.first_cycle
     probe = dp.Packer(corpus, device_tensors=tensors)
     try:
-        U = probe.cycle(0)["n_updates"]
+        U = probe.cycle(cyc)["n_updates"]
     except dp.DpackError as e:
         if e.code != dp.PACK_E_EXHAUSTED or args.scale == 1.0:
             raise
@@ -125,18 +145,18 @@ def main():
         probe.close()
         corpus = corpus.replace(updates_per_cycle=0)
         probe = dp.Packer(corpus, device_tensors=tensors)
-        U = probe.cycle(0)["n_updates"]
+        U = probe.cycle(cyc)["n_updates"]
     probe.close()
     B, T = corpus.B, corpus.T
-    batches = [int(x) for x in probe.batches]  # windows of each update of cycle 0
+    batches = [int(x) for x in probe.batches]  # windows of each update of the timed cycle
     # output buffers outside the timed region
     out = dp.Packer.alloc_out_packed(probe, U) if args.packed else dp.Packer.alloc_out(probe, U)
     torch.cuda.synchronize()
-    log(f"cycle 0: {U} updates x {B if not args.ramp else sorted(set(batches))} windows x {T} positions")
+    log(f"cycle {cyc}: {U} updates x {B if not args.ramp else sorted(set(batches))} windows x {T} positions")
 
     def one_step():
         pk = dp.Packer(corpus, device_tensors=tensors, timing=True)
-        info = pk.cycle(0)
+        info = pk.cycle(cyc)
         if args.packed:
             pk.batch_packed_into(0, info["n_updates"], out)
         else:
@@ -243,7 +263,7 @@ def main():
         t_a = time.perf_counter()
         op = oracle.Plan(corpus)
         t_b = time.perf_counter()
-        oi = op.cycle(0)
+        oi = op.cycle(cyc)
         t_c = time.perf_counter()
         ob = op.batch_packed(0, n_s) if args.packed else op.batch(0, n_s, digests=True)
         t_d = time.perf_counter()
@@ -296,6 +316,9 @@ def main():
                    + (", per-update counts from cumulative quotas" if args.cumulative else "")
                    + (f", batch-size ramp {B // 2} -> {B} windows per update at 10^8 tokens" if args.ramp else "")
                    + (f", {args.lanes} lanes" if args.lanes > 1 else "")
+                   + (", held-out (validation) stream, cycle of maximal length" if args.heldout else "")
+                   + (f", {args.arrivals} arrivals" if args.arrivals > 1 else "")
+                   + (", cycle 1 of a context resumed at cycle 0's stream tokens" if args.resume else "")
                    + (", padding-free rows" if args.packed else ""),
                    "docs": corpus.n_docs, "tokens": corpus.n_tokens, "T": T, "B": B, "updates": U,
                    "real_tokens_per_step": real, "positions_per_step": row_positions,
