@@ -32,6 +32,9 @@ def _setup(name):
             c = c.replace(ramp=((0, 128 * c.T), (100_000_000, 256 * c.T)))
         if mode == "lanes":  # 8 lanes: 120 streams of (source, lane)
             c = c.replace(lanes=8)
+        if mode == "arrivals":  # 8 arrivals, seeded uniform labels: 480 (source, arrival, stratum) groups
+            r = np.random.default_rng(np.random.SeedSequence([7, 8]))
+            c = c.replace(segment=r.integers(0, 8, size=c.n_docs).astype(np.uint16), n_segments=8)
         if mode == "heldout":
             c = c.replace(updates_per_cycle=0)  # the 1-5 % held out cannot supply 200 updates
         say("oracle plan", name, c.n_docs, "docs", c.n_tokens, "tokens")
@@ -52,10 +55,11 @@ def _setup(name):
 # wrap-pretrain is the pre-train workload with wrap packing, heldout-pretrain
 # its held-out (validation) stream, random-pretrain with each cycle's windows
 # read in a random order, cum-pretrain with per-update counts from the cycle's
-# cumulative quotas, lanes-pretrain with 8 lanes.
+# cumulative quotas, lanes-pretrain with 8 lanes, arrivals-pretrain with its
+# documents labelled with 8 arrivals.
 FULL = [("tiny", None), ("pretrain", None), ("sft", None), ("long", None), ("full", (24, 66)),
         ("wrap-pretrain", None), ("heldout-pretrain", None), ("random-pretrain", None), ("cum-pretrain", None),
-        ("lanes-pretrain", None)]
+        ("lanes-pretrain", None), ("arrivals-pretrain", None)]
 
 
 @pytest.mark.parametrize("name,cap", FULL)
