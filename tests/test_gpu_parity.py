@@ -686,6 +686,53 @@ def _edge_run(c, name):
     compare_batch(to_np(pk.batch(0, n)), op.batch(0, n), name)
 
 
+def _max_case(name):
+    """Corpora at the limits the library documents (sources, groups, token ids,
+    window length, windows per update), small enough for the oracle."""
+    r = np.random.default_rng(np.random.SeedSequence([31, len(name)]))
+    vocab = 50000
+    if name == "max_sources":  # 4,096 sources: per-source statistics past the LDS bins
+        S, D, T, B = 4096, 60000, 64, 64
+        L = r.integers(1, 200, size=D)
+        src = r.integers(0, S, size=D).astype(np.uint16)
+        st, ns = np.zeros(D, np.uint16), np.ones(S, np.uint32)
+        w, bp = r.integers(1, 1000, size=S).astype(np.uint64), r.integers(0, 3000, size=S).astype(np.uint32)
+    elif name == "max_groups":  # 16 sources x 4,096 strata = 65,536 groups, most of them empty
+        S, D, T, B = 16, 40000, 64, 16
+        L = r.integers(1, 150, size=D)
+        src, st = r.integers(0, S, size=D).astype(np.uint16), r.integers(0, 4096, size=D).astype(np.uint16)
+        ns = np.full(S, 4096, np.uint32)
+        w, bp = r.integers(1, 100, size=S).astype(np.uint64), np.full(S, 100, np.uint32)
+    elif name == "full_range_tokens":  # token ids over all of [0, 2^32)
+        S, D, T, B = 3, 3000, 128, 4
+        L = r.integers(0, 700, size=D)
+        src, st, ns = r.integers(0, S, size=D).astype(np.uint16), np.zeros(D, np.uint16), np.ones(S, np.uint32)
+        w, bp = np.array([5, 3, 2], np.uint64), np.array([500, 100, 2000], np.uint32)
+        vocab = 2**32
+    elif name == "long_windows":  # T = 65,536: 13,313 compressions per window record
+        S, D, T, B = 2, 400, 65536, 2
+        L = r.integers(1, 150000, size=D)
+        src, st, ns = r.integers(0, S, size=D).astype(np.uint16), np.zeros(D, np.uint16), np.ones(S, np.uint32)
+        w, bp = np.array([1, 1], np.uint64), np.array([100, 100], np.uint32)
+    else:  # wide_update: 65,536 windows in one update, the most one emission-and-digest launch takes
+        S, D, T, B = 2, 90000, 64, 65536
+        L = r.integers(20, 64, size=D)
+        src, st, ns = r.integers(0, S, size=D).astype(np.uint16), np.zeros(D, np.uint16), np.ones(S, np.uint32)
+        w, bp = np.array([1, 1], np.uint64), np.zeros(S, np.uint32)
+    order = np.lexsort((st, src))
+    src, st, L = src[order], st[order], L[order]
+    off = np.zeros(D + 1, np.uint64)
+    np.cumsum(L, out=off[1:])
+    tok = r.integers(0, vocab, size=int(off[-1]), dtype=np.uint64).astype(np.uint32)
+    pl = np.minimum(r.integers(0, 100, size=D), L).astype(np.uint32)
+    return Corpus(name, tok, off, src, st, pl, ns, w, bp, T=T, B=B, updates_per_cycle=0, seed=11, pad_token=7)
+
+
+@pytest.mark.parametrize("name", ["max_sources", "max_groups", "full_range_tokens", "long_windows", "wide_update"])
+def test_maximum_sizes(name):
+    _edge_run(_max_case(name), name)
+
+
 def test_reemission_and_reinit_are_bytewise_identical():
     c = make_corpus("sft", 0.002)
     a = dp.Packer(c)
