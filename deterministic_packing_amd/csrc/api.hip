@@ -233,7 +233,7 @@ size_t carve(pack_ctx& c, char* base) {
     p.val[0] = k.take<uint32_t>(D);
     p.val[1] = k.take<uint32_t>(D);
     const uint64_t WR = p.read_random ? P : 0;  // cycle windows ≤ windows ≤ pieces
-    p.hist = k.take<uint32_t>(dp::sort_hist_words(D > WR ? D : WR));
+    p.hist = k.take<uint32_t>(dp::sort_hist_words(D > WR ? D : WR, G > S ? G : S));
     p.group_start = k.take<uint32_t>(G + 1);
     p.gpre = k.take<uint64_t>(D + 1);
     p.order = k.take<uint32_t>(D);

@@ -262,7 +262,7 @@ void launch_validate(const Plan& p, hipStream_t st);
 void launch_hash(const Plan& p, uint64_t base, uint64_t end, uint64_t* S, uint32_t* first, hipStream_t st);
 uint64_t hash_tile_count(uint64_t n_tokens);
 void launch_keep_scan(Plan& p, hipStream_t st);       // kept_pos + compaction into val[0], keys
-void launch_sort(Plan& p, hipStream_t st);            // LSD radix by (group, key64); sets sort_buf
+void launch_sort(Plan& p, hipStream_t st);            // by (group, key64, d); sets sort_buf
 uint32_t sort_pairs(uint64_t* const key[2], uint32_t* const val[2], const uint32_t* group, uint64_t n, uint32_t G,
                     uint32_t* hist_ws, uint32_t* err, hipStream_t st);
 void launch_read_order(Plan& p, uint32_t cycle, uint64_t total, hipStream_t st);  // perm of each source's cycle windows
@@ -277,7 +277,7 @@ void launch_apportion(Plan& p, uint64_t W, uint32_t B, uint32_t* n_out, hipStrea
 void launch_zero_u64(uint64_t* a, uint64_t n, hipStream_t st);
 void launch_zero_u32(uint32_t* a, uint64_t n, hipStream_t st);
 void launch_fill_u32(uint32_t* a, uint64_t n, uint32_t v, hipStream_t st);
-uint64_t sort_hist_words(uint64_t n_docs);
+uint64_t sort_hist_words(uint64_t n, uint64_t G);
 void launch_checks(Plan& p, hipStream_t st);          // order / hash checks
 void launch_cycle_sums(Plan& p, uint64_t total_slots, hipStream_t st);
 // cumulative mixture of a cycle: the schedule (cum_A, cum_out), then, once the

@@ -1,24 +1,23 @@
 // sort.hip — compaction of kept documents, Philox4x32-10 shuffle keys, and a
-// stable LSD radix sort of the kept documents by (group, key64).
+// sort of the kept documents by (group, key64, input index).
 //
 // NeuronSpark-Trainer README, Concepts: a file's documents are shuffled.  The
 // shuffle here is counter-based: key64(d) = x1·2^32 + x0 of
 // Philox4x32-10(counter = (d lo, d hi, 0x53485546, 0), key = (seed lo, seed hi))
 // (Salmon et al., SC'11), so it depends only on the seed and the input index d,
-// never on rank, world or launch shape.  Kept documents enter the sort in
-// input order and every pass is stable.  The radix passes order by
-// (group, key64 >> 32) only; runs that tie there (rare: about n²/2^33 pairs
-// for n documents of a group) are then ordered by the low 32 key bits with a
-// stable insertion sort, which leaves ties of key64 in input order, so the
-// result is the order by (group, key64, d).
+// never on rank, world or launch shape.
+//
+// The sort is a distribution sort that relies on the keys' high bits being
+// uniform (they are Philox outputs): a group of n elements is cut into 2^b
+// buckets by the top b key bits, b the least with n >> b <= 4, so a bucket
+// holds about two to four elements; elements reach their bucket through
+// atomic tickets (in no particular order) and one thread per bucket then
+// orders it by (key64, input index) with an insertion sort.  The result is the
+// unique order by (group, key64, input index), whatever the tickets were.
 #include "dp_common.h"
 
 namespace dp {
 namespace {
-
-constexpr int RB = 256;             // threads per block
-constexpr int RI = 8;               // rounds per tile
-constexpr int RTILE = RB * RI;      // elements per tile
 
 __global__ __launch_bounds__(256) void k_compact_keys(Plan p, uint64_t* key, uint32_t* val) {
     const uint64_t d = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -29,92 +28,148 @@ __global__ __launch_bounds__(256) void k_compact_keys(Plan p, uint64_t* key, uin
                            (uint32_t)(p.seed >> 32));
 }
 
-template <bool GROUP>
-__device__ inline uint32_t digit_of(uint64_t key, uint32_t val, const uint32_t* group, int shift) {
-    if (GROUP) return (group[val] >> shift) & 0xFFu;
-    return (uint32_t)(key >> shift) & 0xFFu;
+// buckets of a group of n elements: 2^b, b the least with n >> b <= 4
+__device__ __forceinline__ uint32_t bucket_bits(uint32_t n) {
+    uint32_t b = 0;
+    while ((n >> b) > 4u) ++b;
+    return b;
 }
 
-template <bool GROUP>
-__global__ __launch_bounds__(RB) void k_hist(const uint64_t* key, const uint32_t* val, const uint32_t* group,
-                                             uint64_t n, int shift, uint32_t* hist, uint32_t nb) {
-    __shared__ uint32_t h[256];
-    h[threadIdx.x] = 0;
-    __syncthreads();
-    const uint64_t base = (uint64_t)blockIdx.x * RTILE;
-    for (int r = 0; r < RI; ++r) {
-        const uint64_t i = base + (uint64_t)r * RB + threadIdx.x;
-        if (i < n) atomicAdd(&h[digit_of<GROUP>(GROUP ? 0 : key[i], GROUP ? val[i] : 0, group, shift)], 1u);
-    }
-    __syncthreads();
-    hist[(uint64_t)threadIdx.x * nb + blockIdx.x] = h[threadIdx.x];
-}
+constexpr uint32_t LDS_GROUPS = 8192;  // group counts kept in LDS up to this many groups
 
-// Stable scatter: element i of the tile lands at
-//   offset[digit][tile] + (# earlier elements of the tile with the same digit).
-// Within a round of 256 elements the earlier same-digit lanes of a wave come
-// from ballots over the 8 digit bits; earlier waves and rounds from LDS counts.
-template <bool GROUP>
-__global__ __launch_bounds__(RB) void k_scatter(const uint64_t* key_in, const uint32_t* val_in,
-                                                const uint32_t* group, uint64_t n, int shift,
-                                                const uint32_t* hofs, uint32_t nb, uint64_t* key_out,
-                                                uint32_t* val_out, uint32_t* err) {
-    __shared__ uint32_t running[256];
-    __shared__ uint32_t wcount[RB / WAVE][256];
-    const int t = threadIdx.x, wid = t / WAVE, lane = t & (WAVE - 1);
-    running[t] = hofs[(uint64_t)t * nb + blockIdx.x];
-#pragma unroll
-    for (int w = 0; w < RB / WAVE; ++w) wcount[w][t] = 0;
-    __syncthreads();
-    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (WAVE - lane));
-    const uint64_t base = (uint64_t)blockIdx.x * RTILE;
-    for (int r = 0; r < RI; ++r) {
-        const uint64_t i = base + (uint64_t)r * RB + t;
-        const bool valid = i < n;
-        uint64_t k = 0;
-        uint32_t v = 0, dg = 0;
-        if (valid) {
-            k = key_in[i];
-            v = val_in[i];
-            dg = digit_of<GROUP>(k, v, group, shift);
-        }
-        uint64_t peers = __ballot(valid);
-#pragma unroll
-        for (int b = 0; b < 8; ++b) {
-            const bool bit = (dg >> b) & 1u;
-            const uint64_t m = __ballot(bit);
-            peers &= bit ? m : ~m;
-        }
-        const uint32_t rank = (uint32_t)__popcll(peers & lt_mask);
-        if (valid && rank == 0) wcount[wid][dg] = (uint32_t)__popcll(peers);
+// gcount[g] += elements of group g (gcount zeroed before)
+__global__ __launch_bounds__(256) void k_group_count(const uint32_t* val, const uint32_t* group, uint64_t n,
+                                                     uint32_t G, uint32_t* gcount) {
+    __shared__ uint32_t h[LDS_GROUPS];
+    const bool lds = G <= LDS_GROUPS;
+    if (lds) {
+        for (uint32_t g = threadIdx.x; g < G; g += blockDim.x) h[g] = 0;
         __syncthreads();
-        if (valid) {
-            uint32_t dst = running[dg] + rank;
-            for (int w = 0; w < wid; ++w) dst += wcount[w][dg];
-            if (dst < n) {
-                key_out[dst] = k;
-                val_out[dst] = v;
-            } else {
-                atomicOr(err, ERR_INTERNAL);
+    }
+    const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+    for (uint64_t i0 = (uint64_t)blockIdx.x * blockDim.x; i0 < n; i0 += stride) {
+        const uint64_t i = i0 + threadIdx.x;
+        const uint32_t g = i < n ? group[val[i]] : 0xFFFFFFFFu;
+        // kept documents come grouped: a wavefront of one group adds once
+        const uint32_t g0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)g);
+        const bool one_group = __all(g == g0);  // every lane below n (g0 is then a group)
+        if (one_group && g0 != 0xFFFFFFFFu) {
+            if (lane_id() == 0) {
+                if (lds) atomicAdd(&h[g0], (uint32_t)WAVE);
+                else atomicAdd(&gcount[g0], (uint32_t)WAVE);
             }
+        } else if (i < n) {
+            if (lds) atomicAdd(&h[g], 1u);
+            else atomicAdd(&gcount[g], 1u);
         }
+    }
+    if (lds) {
         __syncthreads();
-        uint32_t add = 0;
-#pragma unroll
-        for (int w = 0; w < RB / WAVE; ++w) {
-            add += wcount[w][t];
-            wcount[w][t] = 0;
-        }
-        running[t] += add;
-        __syncthreads();
+        for (uint32_t g = threadIdx.x; g < G; g += blockDim.x)
+            if (h[g]) atomicAdd(&gcount[g], h[g]);
     }
 }
 
-// Random read order of each source's cycle windows (NeuronSpark-Trainer
-// README, Concepts: the trainer reads each source's windows of a segment in a
-// random order; a segment read as a cycle).  Element e of the cycle's windows
-// is source s's i-th window; key64 = x1·2^32 + x0 of Philox4x32-10(counter =
-// (i, s, cycle, 0x57494E44), key = seed); sorted by (s, key64, e).
+// gbase[g] = first bucket of group g (exclusive prefix of 2^b_g), gbase[G] =
+// the buckets in use; one block of 1,024 threads, each over a run of groups
+__global__ __launch_bounds__(1024) void k_bucket_base(const uint32_t* gcount, uint32_t G, uint32_t* gbase) {
+    __shared__ uint32_t part[1024];
+    const uint32_t per = (G + 1023) / 1024, g0 = threadIdx.x * per, g1 = min(G, g0 + per);
+    uint32_t sum = 0;
+    for (uint32_t g = g0; g < g1; ++g) sum += 1u << bucket_bits(gcount[g]);
+    part[threadIdx.x] = sum;
+    __syncthreads();
+    for (uint32_t o = 1; o < 1024; o <<= 1) {  // inclusive scan of the runs' sums
+        const uint32_t y = threadIdx.x >= o ? part[threadIdx.x - o] : 0u;
+        __syncthreads();
+        part[threadIdx.x] += y;
+        __syncthreads();
+    }
+    uint32_t at = part[threadIdx.x] - sum;
+    for (uint32_t g = g0; g < g1; ++g) {
+        gbase[g] = at;
+        at += 1u << bucket_bits(gcount[g]);
+    }
+    if (threadIdx.x == 1023) gbase[G] = part[1023];
+}
+
+// element i's bucket and its ticket in it (bcount zeroed before)
+__global__ __launch_bounds__(256) void k_bucket_count(const uint64_t* key, const uint32_t* val, const uint32_t* group,
+                                                      uint64_t n, const uint32_t* gcount, const uint32_t* gbase,
+                                                      uint32_t* bcount, uint32_t* bucket, uint32_t* ticket) {
+    const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    const uint32_t g = group[val[i]];
+    const uint32_t b = bucket_bits(gcount[g]);
+    const uint32_t hi = (uint32_t)(key[i] >> 32);
+    const uint32_t bk = gbase[g] + (b ? hi >> (32u - b) : 0u);
+    bucket[i] = bk;
+    ticket[i] = atomicAdd(&bcount[bk], 1u);
+}
+
+__global__ __launch_bounds__(256) void k_bucket_scatter(const uint64_t* key, const uint32_t* val, uint64_t n,
+                                                        const uint32_t* bucket, const uint32_t* ticket,
+                                                        const uint32_t* boff, uint64_t* key_out, uint32_t* val_out) {
+    const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    const uint32_t at = boff[bucket[i]] + ticket[i];
+    key_out[at] = key[i];
+    val_out[at] = val[i];
+}
+
+constexpr uint32_t BMAX = 16;  // bucket sizes sorted in registers
+
+__device__ __forceinline__ void cmpx(uint64_t& ka, uint32_t& va, uint64_t& kb, uint32_t& vb) {
+    const bool sw = ka > kb || (ka == kb && va > vb);
+    const uint64_t k = sw ? kb : ka, k2 = sw ? ka : kb;
+    const uint32_t v = sw ? vb : va, v2 = sw ? va : vb;
+    ka = k; kb = k2; va = v; vb = v2;
+}
+
+// one thread per bucket: [boff[b], boff[b+1]) ordered by (key64, val).  Up to
+// BMAX elements are loaded at once, padded with the largest pair and sorted by
+// an odd-even transposition network in registers; a larger bucket (rare: a
+// bucket averages 2-4 elements) is sorted in place by insertion.
+__global__ __launch_bounds__(256) void k_bucket_sort(uint64_t* key, uint32_t* val, const uint32_t* boff, uint64_t nb) {
+    const uint64_t b = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= nb) return;
+    const uint32_t lo = boff[b], hi = boff[b + 1];
+    const uint32_t m = hi - lo;
+    if (m < 2) return;
+    if (m <= BMAX) {
+        uint64_t k[BMAX];
+        uint32_t v[BMAX];
+#pragma unroll
+        for (uint32_t j = 0; j < BMAX; ++j) {
+            k[j] = j < m ? key[lo + j] : ~0ull;
+            v[j] = j < m ? val[lo + j] : ~0u;
+        }
+#pragma unroll
+        for (uint32_t r = 0; r < BMAX; ++r)
+#pragma unroll
+            for (uint32_t j = r & 1u; j + 1 < BMAX; j += 2) cmpx(k[j], v[j], k[j + 1], v[j + 1]);
+#pragma unroll
+        for (uint32_t j = 0; j < BMAX; ++j)
+            if (j < m) {
+                key[lo + j] = k[j];
+                val[lo + j] = v[j];
+            }
+        return;
+    }
+    for (uint32_t a = lo + 1; a < hi; ++a) {
+        const uint64_t k = key[a];
+        const uint32_t v = val[a];
+        uint32_t c = a;
+        while (c > lo && (key[c - 1] > k || (key[c - 1] == k && val[c - 1] > v))) {
+            key[c] = key[c - 1];
+            val[c] = val[c - 1];
+            --c;
+        }
+        key[c] = k;
+        val[c] = v;
+    }
+}
+
 __global__ __launch_bounds__(256) void k_window_keys(Plan p, uint32_t cycle, uint64_t total) {
     const uint64_t e = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (e >= total) return;
@@ -138,33 +193,6 @@ __global__ __launch_bounds__(256) void k_perm_out(Plan p, const uint32_t* sorted
     p.perm[r] = (uint32_t)(e - p.perm_start[p.wgroup[e]]);
 }
 
-// Orders each run of equal (group, key64 >> 32) by the low 32 key bits; the
-// thread at a run's first element sorts the run (insertion sort, stable).
-// Other threads only read the high key bits and groups, which the sort of a
-// run does not change.
-__global__ __launch_bounds__(256) void k_tie_fix(uint64_t* key, uint32_t* val, const uint32_t* group, uint64_t n) {
-    const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= n) return;
-    const uint32_t hi = (uint32_t)(key[i] >> 32), g = group[val[i]];
-    auto same = [&](uint64_t j) { return (uint32_t)(key[j] >> 32) == hi && group[val[j]] == g; };
-    if (i > 0 && same(i - 1)) return;     // not the first element of its run
-    if (i + 1 >= n || !same(i + 1)) return;  // a run of one
-    uint64_t end = i + 2;
-    while (end < n && same(end)) ++end;
-    for (uint64_t a = i + 1; a < end; ++a) {
-        const uint64_t k = key[a];
-        const uint32_t v = val[a];
-        uint64_t b = a;
-        while (b > i && (uint32_t)key[b - 1] > (uint32_t)k) {
-            key[b] = key[b - 1];
-            val[b] = val[b - 1];
-            --b;
-        }
-        key[b] = k;
-        val[b] = v;
-    }
-}
-
 }  // namespace
 
 void launch_keep_scan(Plan& p, hipStream_t st) {
@@ -174,42 +202,37 @@ void launch_keep_scan(Plan& p, hipStream_t st) {
     DP_HIP(hipGetLastError());
 }
 
-// Stable sort of n (key64, val) pairs by (group[val], key64, input order),
-// ping-ponging between buffers 0 and 1; returns the buffer that holds the
-// result.  group values are < G.
+// Sort of n (key64, val) pairs by (group[val], key64, val) into buffer 1 (the
+// input is buffer 0); returns 1.  group values are < G; keys' high 32 bits
+// uniform.  Launches are sized by the bucket bound n/2 + G + 1 (a group of
+// n_g > 4 elements takes 2^b < n_g/2 buckets), so nothing is read back.
 uint32_t sort_pairs(uint64_t* const key[2], uint32_t* const val[2], const uint32_t* group, uint64_t n, uint32_t G,
-                    uint32_t* hist_ws, uint32_t* err, hipStream_t st) {
-    const uint32_t nb = (uint32_t)((n + RTILE - 1) / RTILE);
-    // hist holds [256·nb] counts followed by [256·nb + 1] scanned offsets and the scan's temp
-    uint32_t* hist = hist_ws;
-    uint32_t* hofs = hist_ws + 256ull * nb + 1;
-    void* tmp = hofs + 256ull * nb + 2;
-    int cur = 0;
-    auto pass = [&](bool group_pass, int shift) {
-        if (nb == 0) return;
-        if (group_pass)
-            hipLaunchKernelGGL(k_hist<true>, dim3(nb), dim3(RB), 0, st, key[cur], val[cur], group, n, shift, hist, nb);
-        else
-            hipLaunchKernelGGL(k_hist<false>, dim3(nb), dim3(RB), 0, st, key[cur], val[cur], group, n, shift, hist,
-                               nb);
-        scan_u32(hist, 256ull * nb, hofs, tmp, st);
-        if (group_pass)
-            hipLaunchKernelGGL(k_scatter<true>, dim3(nb), dim3(RB), 0, st, key[cur], val[cur], group, n, shift, hofs,
-                               nb, key[cur ^ 1], val[cur ^ 1], err);
-        else
-            hipLaunchKernelGGL(k_scatter<false>, dim3(nb), dim3(RB), 0, st, key[cur], val[cur], group, n, shift, hofs,
-                               nb, key[cur ^ 1], val[cur ^ 1], err);
-        DP_HIP(hipGetLastError());
-        cur ^= 1;
-    };
-    for (int shift = 32; shift < 64; shift += 8) pass(false, shift);
-    for (int shift = 0; G > 1 && shift < 32 && ((G - 1) >> shift) != 0; shift += 8) pass(true, shift);
-    if (n > 1) {
-        hipLaunchKernelGGL(k_tie_fix, dim3((uint32_t)((n + 255) / 256)), dim3(256), 0, st, key[cur], val[cur], group,
-                           n);
-        DP_HIP(hipGetLastError());
-    }
-    return (uint32_t)cur;
+                    uint32_t* ws, uint32_t* err, hipStream_t st) {
+    (void)err;
+    if (n == 0) return 0;
+    const uint64_t NB = n / 2 + G + 1;  // bucket bound
+    uint32_t* gcount = ws;                 // [G]
+    uint32_t* bcount = gcount + G;         // [NB], zeroed with gcount
+    uint32_t* gbase = bcount + NB;         // [G + 1]
+    uint32_t* boff = gbase + G + 1;        // [NB + 1]
+    uint32_t* bucket = boff + NB + 1;      // [n]
+    uint32_t* ticket = bucket + n;         // [n]
+    void* tmp = ticket + n + 1;            // scan temp (8-byte aligned below)
+    tmp = reinterpret_cast<void*>((reinterpret_cast<uintptr_t>(tmp) + 7) & ~uintptr_t(7));
+    launch_fill_u32(gcount, G + NB, 0u, st);
+    const uint32_t blocks = (uint32_t)((n + 255) / 256);
+    hipLaunchKernelGGL(k_group_count, dim3(std::min<uint32_t>(blocks, 16384)), dim3(256), 0, st, val[0], group, n, G,
+                       gcount);
+    hipLaunchKernelGGL(k_bucket_base, dim3(1), dim3(1024), 0, st, (const uint32_t*)gcount, G, gbase);
+    hipLaunchKernelGGL(k_bucket_count, dim3(blocks), dim3(256), 0, st, key[0], val[0], group, n,
+                       (const uint32_t*)gcount, (const uint32_t*)gbase, bcount, bucket, ticket);
+    scan_u32(bcount, NB, boff, tmp, st);
+    hipLaunchKernelGGL(k_bucket_scatter, dim3(blocks), dim3(256), 0, st, key[0], val[0], n, (const uint32_t*)bucket,
+                       (const uint32_t*)ticket, (const uint32_t*)boff, key[1], val[1]);
+    hipLaunchKernelGGL(k_bucket_sort, dim3((uint32_t)((NB + 255) / 256)), dim3(256), 0, st, key[1], val[1],
+                       (const uint32_t*)boff, NB);
+    DP_HIP(hipGetLastError());
+    return 1;
 }
 
 // requires p.n_kept (host) to be set
@@ -228,10 +251,10 @@ void launch_read_order(Plan& p, uint32_t cycle, uint64_t total, hipStream_t st) 
     DP_HIP(hipGetLastError());
 }
 
-// workspace for the sort's histogram, offsets and scan temp, in uint32 words
-uint64_t sort_hist_words(uint64_t n_docs) {
-    const uint64_t nb = (n_docs + RTILE - 1) / RTILE + 1;
-    return 256ull * nb * 2 + 4 + (scan_temp_bytes(256ull * nb) + 3) / 4 + 16;
+// workspace of sort_pairs for n pairs in G groups, in uint32 words
+uint64_t sort_hist_words(uint64_t n, uint64_t G) {
+    const uint64_t NB = n / 2 + G + 1;
+    return G + NB + (G + 1) + (NB + 1) + 2 * n + 1 + 2 + (scan_temp_bytes(NB) + 3) / 4 + 16;
 }
 
 }  // namespace dp
