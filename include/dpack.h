@@ -108,7 +108,7 @@ enum {
     PACK_PHASE_VALIDATE = 0, /* corpus validation kernel */
     PACK_PHASE_HASH,         /* per-document hash and hold-out */
     PACK_PHASE_KEYS,         /* compaction of kept documents and Philox keys */
-    PACK_PHASE_SORT,         /* radix sort by (group, key) */
+    PACK_PHASE_SORT,         /* sort by (group, key, document) */
     PACK_PHASE_MERGE,        /* strata merge */
     PACK_PHASE_PIECES,       /* piece counts, prefix sums and piece table */
     PACK_PHASE_CUT,          /* next-fit: next pointers, lifting, windows per source */
