@@ -450,12 +450,20 @@ void build_plan(pack_ctx& c) {
     }
     dp::launch_validate(p, st);
     c.timer.end(st);
+
+    // A1 hash + hold-out, A2 compaction, A3 keys; after an invalid corpus the
+    // hash kernels return at once (they read the error flag) and the error is
+    // raised below, before any later kernel runs
+    c.timer.begin(PACK_PHASE_HASH, st);
+    dp::launch_hash(p, p.gpre /* per-document sums; gpre is free until the merge */, c.hash_first, st);
+    c.timer.end(st);
+    c.timer.begin(PACK_PHASE_KEYS, st);
+    dp::launch_keep_scan(p, st);
+    c.timer.end(st);
     const uint32_t* h_err = d2h_staged(c, p.err, 1);
-    const uint64_t* h_lo = d2h_staged(c, p.offsets, 1);  // offsets[0] and offsets[n_docs]:
-    const uint64_t* h_hi = d2h_staged(c, p.offsets + p.n_docs, 1);  // the tokens the documents cover
+    const uint32_t* h_kept = d2h_staged(c, p.kept_pos + p.n_docs, 1);
     sync_staged(c);
     uint32_t err = *h_err;
-    const uint64_t span[2] = {*h_lo, *h_hi};
     if (err) {
         std::string m = "invalid corpus:";
         if (err & 1u) m += " offsets decrease;";
@@ -466,17 +474,6 @@ void build_plan(pack_ctx& c) {
         if (err & 32u) m += " an arrival id >= n_segments;";
         throw InvalError{m};
     }
-
-    // A1 hash + hold-out, A2 compaction, A3 keys
-    c.timer.begin(PACK_PHASE_HASH, st);
-    dp::launch_hash(p, span[0], span[1], p.gpre /* per-document sums; gpre is free until the merge */,
-                    c.hash_first, st);
-    c.timer.end(st);
-    c.timer.begin(PACK_PHASE_KEYS, st);
-    dp::launch_keep_scan(p, st);
-    c.timer.end(st);
-    const uint32_t* h_kept = d2h_staged(c, p.kept_pos + p.n_docs, 1);
-    sync_staged(c);
     p.n_kept = *h_kept;
 
     // A3 sort, A4 merge, A5 piece counts

@@ -63,7 +63,10 @@ constexpr uint32_t HT = 256 * TPT;   // tokens per tile (one 256-thread block)
 typedef uint32_t u32x4a4 __attribute__((ext_vector_type(4), aligned(4)));
 
 // first[t] = the document containing token base + t·HT (clamped to D−1)
-__global__ __launch_bounds__(256) void k_tile_first_doc(Plan p, uint64_t base, uint64_t ntiles, uint32_t* first) {
+__global__ __launch_bounds__(256) void k_tile_first_doc(Plan p, uint32_t* first) {
+    if (*p.err) return;  // an invalid corpus: nothing reads its offsets
+    const uint64_t base = p.offsets[0], end = p.offsets[p.n_docs];
+    const uint64_t ntiles = (end - base + HT - 1) / HT;
     const uint64_t t = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (t > ntiles) return;
     const uint64_t x = base + t * HT;
@@ -252,8 +255,12 @@ __device__ __forceinline__ void hash_tile(const Plan& p, uint64_t base, uint64_t
 // tile's tokens and offset entries, and the tile table two tiles ahead.  A
 // tile's hashing then waits on no global load.  The last tiles load element
 // by element with bounds checks.
-__global__ __launch_bounds__(256) void k_hash_flat(Plan p, const uint32_t* first, uint64_t base, uint64_t end,
-                                                   uint64_t ntiles, uint64_t nfast, uint64_t* S) {
+__global__ __launch_bounds__(256) void k_hash_flat(Plan p, const uint32_t* first, uint64_t* S) {
+    if (*p.err) return;  // an invalid corpus: nothing reads its offsets
+    const uint64_t base = p.offsets[0], end = p.offsets[p.n_docs];
+    if (end == base) return;
+    const uint64_t ntiles = (end - base + HT - 1) / HT;
+    const uint64_t nfast = (end - base - 1) / HT;  // tiles whose every thread reads TPT + 1 tokens below end
     __shared__ uint64_t s_off[OCAP + 1];
     const uint32_t* tok = p.tokens;
     const uint64_t step = gridDim.x;
@@ -304,6 +311,7 @@ __global__ __launch_bounds__(256) void k_hash_flat(Plan p, const uint32_t* first
 // and non-empty (with the held-out stream: iff held and non-empty); per-source
 // statistics in LDS, one atomic per block and bin.
 __global__ __launch_bounds__(256) void k_hash_final(Plan p, const uint64_t* S, uint32_t lds_bins) {
+    if (*p.err) return;  // an invalid corpus: source ids may be out of range
     extern __shared__ unsigned long long bins[];  // [4][S] when lds_bins
     if (lds_bins) {
         for (uint32_t i = threadIdx.x; i < 4 * p.S; i += blockDim.x) bins[i] = 0;
@@ -352,17 +360,18 @@ void launch_validate(const Plan& p, hipStream_t st) {
 
 // base/end: offsets[0] and offsets[n_docs] (read back after validation);
 // S: [n_docs] sums, first: [ntiles + 1] tile table (workspace)
-void launch_hash(const Plan& p, uint64_t base, uint64_t end, uint64_t* S, uint32_t* first, hipStream_t st) {
-    const uint64_t ntiles = end > base ? (end - base + HT - 1) / HT : 0;
+// The span [offsets[0], offsets[n_docs]) is read on the device and the
+// grids are sized by n_tokens, so nothing waits for the validation: after an
+// invalid corpus the kernels return at once and the error is read with the
+// kept count.  S: [n_docs] sums, first: [hash_tile_count(n_tokens) + 2]
+void launch_hash(const Plan& p, uint64_t* S, uint32_t* first, hipStream_t st) {
+    const uint64_t ntiles = (p.n_tokens + HT - 1) / HT;  // a bound: the documents cover at most n_tokens
     hipLaunchKernelGGL(k_zero, dim3((uint32_t)std::min<uint64_t>((p.n_docs + 255) / 256, 2048)), dim3(256), 0, st, S,
                        p.n_docs);
     if (ntiles) {
-        hipLaunchKernelGGL(k_tile_first_doc, dim3((uint32_t)((ntiles + 1 + 255) / 256)), dim3(256), 0, st, p, base,
-                           ntiles, first);
-        // tiles whose every thread reads TPT + 1 tokens below end
-        const uint64_t nfast = (end - base - 1) / HT;
+        hipLaunchKernelGGL(k_tile_first_doc, dim3((uint32_t)((ntiles + 1 + 255) / 256)), dim3(256), 0, st, p, first);
         hipLaunchKernelGGL(k_hash_flat, dim3((uint32_t)std::min<uint64_t>(ntiles, 16384)), dim3(256), 0, st, p,
-                           (const uint32_t*)first, base, end, ntiles, nfast, S);
+                           (const uint32_t*)first, S);
     }
     const uint32_t lds_bins = p.S <= 256 ? 1u : 0u;
     const size_t lds = lds_bins ? 4ull * p.S * sizeof(uint64_t) : 0;
