@@ -462,16 +462,27 @@ __global__ __launch_bounds__(64 * FWAVES) void k_emit_sha(Plan p, EmitArgs a, ui
     else emit_lanes(p, a, n_windows, w0, lane, prog + e);
 }
 
-// SHA-256 of an arbitrary byte string (4-byte aligned start), one lane.
+// SHA-256 of an arbitrary byte string (4-byte aligned start), one lane.  The
+// next block's words are loaded before the current block is compressed, so
+// the chain does not wait on a load per block.
 __device__ __forceinline__ void sha_bytes(const uint8_t* msg, uint64_t len, uint8_t* out) {
     uint32_t H[8];
     sha256_init(H);
     const uint64_t full = len / 64;
+    const uint32_t* wp = reinterpret_cast<const uint32_t*>(msg);
+    uint32_t nx[16];
+    if (full) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) nx[i] = wp[i];
+    }
     for (uint64_t b = 0; b < full; ++b) {
         uint32_t W[16];
-        const uint32_t* wp = reinterpret_cast<const uint32_t*>(msg + 64 * b);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) W[i] = bswap32(wp[i]);
+        for (int i = 0; i < 16; ++i) W[i] = bswap32(nx[i]);
+        if (b + 1 < full) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) nx[i] = wp[16 * (b + 1) + i];
+        }
         sha256_compress(H, W);
     }
     const uint64_t rem = len - 64 * full;
