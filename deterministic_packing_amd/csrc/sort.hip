@@ -37,10 +37,11 @@ __device__ __forceinline__ uint32_t bucket_bits(uint32_t n) {
 
 constexpr uint32_t LDS_GROUPS = 8192;  // group counts kept in LDS up to this many groups
 
-// gcount[g] += elements of group g (gcount zeroed before)
+// gcount[g] += elements of group g (gcount zeroed before); with G <=
+// LDS_GROUPS the block counts in LDS first (G words of dynamic LDS)
 __global__ __launch_bounds__(256) void k_group_count(const uint32_t* val, const uint32_t* group, uint64_t n,
                                                      uint32_t G, uint32_t* gcount) {
-    __shared__ uint32_t h[LDS_GROUPS];
+    extern __shared__ uint32_t h[];
     const bool lds = G <= LDS_GROUPS;
     if (lds) {
         for (uint32_t g = threadIdx.x; g < G; g += blockDim.x) h[g] = 0;
@@ -221,8 +222,9 @@ uint32_t sort_pairs(uint64_t* const key[2], uint32_t* const val[2], const uint32
     tmp = reinterpret_cast<void*>((reinterpret_cast<uintptr_t>(tmp) + 7) & ~uintptr_t(7));
     launch_fill_u32(gcount, G + NB, 0u, st);
     const uint32_t blocks = (uint32_t)((n + 255) / 256);
-    hipLaunchKernelGGL(k_group_count, dim3(std::min<uint32_t>(blocks, 16384)), dim3(256), 0, st, val[0], group, n, G,
-                       gcount);
+    const size_t glds = G <= LDS_GROUPS ? sizeof(uint32_t) * G : 0;
+    hipLaunchKernelGGL(k_group_count, dim3(std::min<uint32_t>(blocks, 1024)), dim3(256), glds, st, val[0], group, n,
+                       G, gcount);
     hipLaunchKernelGGL(k_bucket_base, dim3(1), dim3(1024), 0, st, (const uint32_t*)gcount, G, gbase);
     hipLaunchKernelGGL(k_bucket_count, dim3(blocks), dim3(256), 0, st, key[0], val[0], group, n,
                        (const uint32_t*)gcount, (const uint32_t*)gbase, bcount, bucket, ticket);
