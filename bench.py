@@ -233,6 +233,34 @@ def main():
             side[k] = {"kernel": k, "bound": "hbm", "achieved": e["achieved"], "peak": HBM_PEAK_GBPS,
                        "unit": "GB/s", "frac": e["frac"], "traffic": traffic_from_profile(k, args.workload)}
 
+    # latency of one update per call (pack_batch of a single update), with and
+    # without the window digests, on a context whose cycle is planned: GPU time
+    # between events on the context's stream, and host wall time to completion
+    per_call = None
+    if not args.packed and not args.ramp:
+        pk1 = dp.Packer(corpus, device_tensors=tensors)
+        pk1.cycle(cyc)
+        n_calls = min(20, U)
+        per_call = {"calls": n_calls, "windows_per_call": B}
+        for dg in (False, True):
+            o1 = pk1.alloc_out(1, digests=dg)
+            gpu, wall = [], []
+            for s_ in range(n_calls):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                torch.cuda.synchronize()
+                t_a = time.perf_counter()
+                e0.record()
+                pk1.batch_into(s_, 1, o1)
+                e1.record()
+                torch.cuda.synchronize()
+                wall.append((time.perf_counter() - t_a) * 1e3)
+                gpu.append(e0.elapsed_time(e1))
+            tag = "with_digests" if dg else "without_digests"
+            per_call[tag + "_gpu_ms"] = round(float(np.median(gpu)), 4)
+            per_call[tag + "_wall_ms"] = round(float(np.median(wall)), 4)
+        pk1.close()
+        log(f"one update per call: {per_call}")
+
     # plain device-to-device copy of 1 GiB: practical HBM ceiling and the
     # known-size kernel the PMC byte counters are calibrated against
     copy = None
@@ -331,6 +359,7 @@ def main():
         "cpu_baseline": cpu,
         "kernels": kernels,
         "copy_ceiling": copy,
+        "per_call_batch": per_call,
         "bit_exact_sample": sample_check,
     }
     print(json.dumps(line), flush=True)
