@@ -380,26 +380,27 @@ def test_arrivals_parity(case):
     _parity_run(c.replace(**mode), "arrivals", case)
 
 
-@pytest.mark.parametrize("wrap", [False, True])
-def test_a_context_per_arrival_on_the_gpu(wrap):
+@pytest.mark.parametrize("mi", range(7))
+def test_a_context_per_arrival_on_the_gpu(mi):
     """A context per arrival, each going on from the tokens the previous GPU context
-    reported, plans the cycles one context over every arrival plans."""
-    from test_oracle_segments import _arrivals, _prefix
-    n_seg = 4
-    c, cuts = _arrivals(1500 + int(wrap), n_seg, n_docs=2400, even=True, updates_per_cycle=4)
-    c = c.replace(wrap=wrap)
+    reported, plans the cycles one context over every arrival plans, in every mode."""
+    from test_oracle_segments import ARRIVAL_MODES, _prefix, arrival_corpus
+    mode = ARRIVAL_MODES[mi]
+    c, cuts = arrival_corpus(1500 + mi, mode)
     full = dp.Packer(c)
     nxt, tokens = None, 0
-    for cyc in range(n_seg):
+    for cyc in range(4):
         fi = full.cycle(cyc)
-        cc = _prefix(c, int(cuts[cyc + 1]))
+        cc = _prefix(c, int(cuts[cyc + 1])).replace(**mode)
         if cyc:
             cc = cc.replace(start_tokens=nxt, first_cycle=cyc, tokens_start=tokens)
-        say("arrival", cyc, "wrap", wrap)
+        say("arrival", cyc, "mode", mode)
         part = dp.Packer(cc)
         pi = part.cycle(cyc)
         assert pi["n_updates"] == fi["n_updates"] and pi["windows_taken"].tolist() == fi["windows_taken"].tolist()
-        compare_batch(to_np(part.batch(0, pi["n_updates"])), to_np(full.batch(0, fi["n_updates"])), f"arrival {cyc}")
+        assert pi["batches"].tolist() == fi["batches"].tolist()
+        n = pi["n_updates"]
+        compare_batch(to_np(part.batch(0, n)), to_np(full.batch(0, n)), f"arrival {cyc}")
         assert pi["stream_next_token"].tolist() == fi["stream_next_token"].tolist()
         nxt, tokens = pi["stream_next_token"].copy(), int(tokens + pi["positions"])
         part.close()

@@ -100,26 +100,37 @@ def test_earlier_arrivals_keep_their_order(seed, n_seg):
             assert b[:len(a)] == a
 
 
-@pytest.mark.parametrize("wrap", [False, True])
-def test_a_context_per_arrival_plans_the_same_cycles(wrap):
+ARRIVAL_MODES = [dict(), dict(wrap=True), dict(cumulative=True), dict(lanes=2), dict(read_random=True),
+                 dict(ramp=((0, 256), (1500, 512))), dict(cumulative=True, lanes=2, read_random=True, wrap=True)]
+
+
+def arrival_corpus(seed, mode):
+    """Four equal arrivals; B = 8 (the ramp's largest batch, two lanes of four)."""
+    c, cuts = _arrivals(seed, 4, n_docs=2400, even=True, updates_per_cycle=4, B=8)
+    return c.replace(**mode), cuts
+
+
+@pytest.mark.parametrize("mi", range(len(ARRIVAL_MODES)))
+def test_a_context_per_arrival_plans_the_same_cycles(mi):
     """Cycle c planned by a context over arrivals 0..c, going on from the previous
-    context's stream tokens, equals cycle c of one context over every arrival (the
-    cycles here never reach a stream's still open last window)."""
-    n_seg = 4
-    c, cuts = _arrivals(6, n_seg, n_docs=2400, even=True, updates_per_cycle=4)
-    c = c.replace(wrap=wrap)
+    context's stream tokens, next cycle number and tokens trained, equals cycle c
+    of one context over every arrival, in every mode (the cycles here never reach
+    a stream's still open last window)."""
+    mode = ARRIVAL_MODES[mi]
+    c, cuts = arrival_corpus(6, mode)
     full = oracle.Plan(c)
     nxt, tokens = None, 0
-    for cyc in range(n_seg):
+    for cyc in range(4):
         fi = full.cycle(cyc)
-        cc = _prefix(c, int(cuts[cyc + 1]))
+        cc = _prefix(c, int(cuts[cyc + 1])).replace(**mode)
         if cyc:
             cc = cc.replace(start_tokens=nxt, first_cycle=cyc, tokens_start=tokens)
         part = oracle.Plan(cc)
         pi = part.cycle(cyc)
         # the cycle stays clear of each stream's last (still open) window
-        assert all(int(pi.remaining[s]) >= 1 for s in range(c.n_sources))
+        assert all(int(x) >= 1 for x in pi.remaining)
         assert pi.n_updates == fi.n_updates and pi.taken.tolist() == fi.taken.tolist()
+        assert pi.batches.tolist() == fi.batches.tolist()
         a, b = full.batch(0, fi.n_updates), part.batch(0, pi.n_updates)
         for key in ("tokens", "pos", "doc", "mask", "digests", "learned"):
             assert np.array_equal(a[key], b[key]), (cyc, key)
