@@ -734,6 +734,41 @@ def test_maximum_sizes(name):
     _edge_run(_max_case(name), name)
 
 
+def test_two_contexts_on_two_streams():
+    """Two contexts alive at once, each on its own stream, their batches issued
+    interleaved: each equals what a context alone emits (own workspace each,
+    stream-ordered work only)."""
+    import torch
+    ca, cb = make_corpus("sft", 0.003), random_small(77, n_docs=900, n_sources=3, max_strata=2, T=128, B=4,
+                                                      max_len=300, prompts=True, bp_max=1500)
+    ref = {}
+    for name, c in (("a", ca), ("b", cb)):
+        pk = dp.Packer(c)
+        n = min(pk.cycle(0)["n_updates"], 6)
+        ref[name] = (n, to_np(pk.batch(0, n)))
+        pk.close()
+    sa, sb = torch.cuda.Stream(), torch.cuda.Stream()
+    ta, tb = dp.upload_corpus(ca), dp.upload_corpus(cb)
+    torch.cuda.synchronize()  # the corpora are resident before other streams read them
+    pa, pb = dp.Packer(ca, stream=sa, device_tensors=ta), dp.Packer(cb, stream=sb, device_tensors=tb)
+    pa.cycle(0)
+    pb.cycle(0)
+    outs = {"a": pa.alloc_out(ref["a"][0]), "b": pb.alloc_out(ref["b"][0])}
+    torch.cuda.synchronize()
+    for i in range(max(ref["a"][0], ref["b"][0])):  # one update at a time, alternating streams
+        for name, pk in (("a", pa), ("b", pb)):
+            if i < ref[name][0]:
+                one = {k: (v[i:i + 1] if v is not None else None) for k, v in outs[name].items()}
+                pk.batch_into(i, 1, one)
+    torch.cuda.synchronize()
+    for name in ("a", "b"):
+        got = to_np(outs[name])
+        for k, v in ref[name][1].items():
+            assert np.array_equal(got[k], v), (name, k)
+    pa.close()
+    pb.close()
+
+
 def test_reemission_and_reinit_are_bytewise_identical():
     c = make_corpus("sft", 0.002)
     a = dp.Packer(c)
