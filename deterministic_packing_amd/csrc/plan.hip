@@ -303,16 +303,33 @@ __global__ __launch_bounds__(256) void k_window_stats(Plan p) {
         return;
     }
     uint32_t f = 0, learn = 0;
-    for (uint32_t q = q0; q < q1; ++q) {
-        p.pc_woff[q] = f;
-        const uint32_t o = p.pc_off[q], len = p.pc_len[q], d = p.pc_doc[q];
-        const uint32_t pl = p.prompt_len ? p.prompt_len[d] : 0u;
-        const uint64_t from = o > pl ? o : pl;
-        if ((uint64_t)o + len > from) learn += (uint32_t)((uint64_t)o + len - from);
-        const uint64_t base = p.offsets[d] + o - f;
-        const uint32_t lead = (uint32_t)(from - o < len ? from - o : len);  // prompt positions of the piece
-        p.pc_emit[q] = make_uint4((uint32_t)base, (uint32_t)(base >> 32), d, f + lead);
-        f += len;
+    for (uint32_t q = q0; q < q1; q += 4) {  // four pieces at a time, every load before any store
+        uint32_t o[4], len[4], d[4], pl[4];
+        uint64_t od[4];
+#pragma unroll
+        for (uint32_t u = 0; u < 4; ++u) {
+            const bool in = q + u < q1;
+            o[u] = in ? p.pc_off[q + u] : 0u;
+            len[u] = in ? p.pc_len[q + u] : 0u;
+            d[u] = in ? p.pc_doc[q + u] : 0u;
+        }
+#pragma unroll
+        for (uint32_t u = 0; u < 4; ++u) {
+            const bool in = q + u < q1;
+            pl[u] = in && p.prompt_len ? p.prompt_len[d[u]] : 0u;
+            od[u] = in ? p.offsets[d[u]] : 0ull;
+        }
+#pragma unroll
+        for (uint32_t u = 0; u < 4; ++u) {
+            if (q + u >= q1) break;
+            p.pc_woff[q + u] = f;
+            const uint64_t from = o[u] > pl[u] ? o[u] : pl[u];
+            if ((uint64_t)o[u] + len[u] > from) learn += (uint32_t)((uint64_t)o[u] + len[u] - from);
+            const uint64_t base = od[u] + o[u] - f;
+            const uint32_t lead = (uint32_t)(from - o[u] < len[u] ? from - o[u] : len[u]);  // prompt positions
+            p.pc_emit[q + u] = make_uint4((uint32_t)base, (uint32_t)(base >> 32), d[u], f + lead);
+            f += len[u];
+        }
     }
     p.win_real[gw] = f;
     p.win_learn[gw] = learn;
