@@ -311,9 +311,9 @@ struct EmitArgs {
 __device__ inline uint64_t out_window(const Plan& p, const EmitArgs& a, uint64_t w, uint32_t* i_out,
                                       uint32_t* jj_out, uint32_t* per_out) {
     uint32_t i, jj, per;
-    if (!p.ramp) {
-        i = (uint32_t)(w / a.per);
-        jj = (uint32_t)(w % a.per);
+    if (!p.ramp) {  // a launch's window index fits 32 bits: 32-bit division
+        i = (uint32_t)w / a.per;
+        jj = (uint32_t)w - i * a.per;
         per = a.per;
     } else {
         const uint64_t e = p.upd_out0[a.step] + w;

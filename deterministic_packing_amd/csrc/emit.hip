@@ -80,65 +80,109 @@ __global__ __launch_bounds__(EB) void k_emit(Plan p, EmitArgs a) {
         return piece(q);
     };
 
-    const uint64_t out0 = PACKED ? (uint64_t)i * a.per * p.T + (uint64_t)a.row_start[(uint64_t)i * (a.per + 1) + jj]
-                                 : (uint64_t)widx * p.T;
-    // Store groups are 4 destination elements aligned to 16 bytes.  A packed
-    // window may start mid-group: `lead` elements of that group belong to the
-    // previous window, and groups that straddle the window's ends are written
-    // element by element so that neighbouring windows never overwrite each other.
-    const uint32_t lead = PACKED ? (uint32_t)(out0 & 3u) : 0u;
-    const uint64_t base = out0 - lead;
-    const uint32_t span = PACKED ? lead + real : p.T;
-    uint4* tok4 = reinterpret_cast<uint4*>(a.tok + base);
-    int4* pos4 = reinterpret_cast<int4*>(a.pos + base);
-    int4* doc4 = reinterpret_cast<int4*>(a.doc + base);
-    uint32_t* mask4 = reinterpret_cast<uint32_t*>(a.mask + base);
     const uint32_t pad = p.pad_token;
-
-    for (uint32_t g = threadIdx.x; g < (span + 3) / 4; g += EB) {
-        const int32_t tb = (int32_t)(4 * g) - (int32_t)lead;  // window position of the group's first element
-        const uint32_t tf = tb < 0 ? 0u : (uint32_t)tb;       // first position inside the window
-        uint32_t tk[4];
-        int32_t ps[4], dc[4];
-        uint32_t mk = 0;
+    if constexpr (!PACKED) {
+        // padded windows: window widx is [widx·T, (widx+1)·T) of the outputs
+        const uint64_t out0 = (uint64_t)widx * p.T;
+        uint4* tok4 = reinterpret_cast<uint4*>(a.tok + out0);
+        int4* pos4 = reinterpret_cast<int4*>(a.pos + out0);
+        int4* doc4 = reinterpret_cast<int4*>(a.doc + out0);
+        uint32_t* mask4 = reinterpret_cast<uint32_t*>(a.mask + out0);
+        for (uint32_t g = threadIdx.x; g < p.T / 4; g += EB) {
+            const uint32_t t0 = 4 * g;
+            uint32_t tk[4];
+            int32_t ps[4], dc[4];
+            uint32_t mk = 0;
+            if (t0 >= real) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) { tk[e] = pad; ps[e] = 0; dc[e] = -1; }
-        if (tf < real) {
-            uint32_t q = find(tf);
-            PieceView v = get(q);
-            uint32_t next_woff = (q + 1 < np) ? (staged ? s_woff[q + 1] : p.pc_woff[q0 + q + 1]) : real;
+                for (int e = 0; e < 4; ++e) { tk[e] = pad; ps[e] = 0; dc[e] = -1; }
+            } else {
+                uint32_t q = find(t0);
+                PieceView v = get(q);
+                uint32_t next_woff = (q + 1 < np) ? (staged ? s_woff[q + 1] : p.pc_woff[q0 + q + 1]) : real;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int32_t ts = tb + e;
-                if (ts < 0 || (uint32_t)ts >= real) continue;
-                const uint32_t t = (uint32_t)ts;
-                while (t >= next_woff && q + 1 < np) {  // next piece (contiguous up to `real`)
-                    ++q;
-                    v = get(q);
-                    next_woff = (q + 1 < np) ? (staged ? s_woff[q + 1] : p.pc_woff[q0 + q + 1]) : real;
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t t = t0 + e;
+                    if (t >= real) {
+                        tk[e] = pad; ps[e] = 0; dc[e] = -1;
+                        continue;
+                    }
+                    while (t >= next_woff && q + 1 < np) {  // next piece (contiguous up to `real`)
+                        ++q;
+                        v = get(q);
+                        next_woff = (q + 1 < np) ? (staged ? s_woff[q + 1] : p.pc_woff[q0 + q + 1]) : real;
+                    }
+                    const uint32_t u = t - v.woff;
+                    tk[e] = (v.src + u < p.n_tokens) ? p.tokens[v.src + u] : pad;  // guard: never read past the corpus
+                    ps[e] = (int32_t)u;
+                    dc[e] = (int32_t)v.doc;
+                    mk |= (t >= v.mfrom ? 1u : 0u) << (8 * e);
                 }
-                const uint32_t u = t - v.woff;
-                tk[e] = (v.src + u < p.n_tokens) ? p.tokens[v.src + u] : pad;  // guard: never read past the corpus
-                ps[e] = (int32_t)u;
-                dc[e] = (int32_t)v.doc;
-                mk |= (t >= v.mfrom ? 1u : 0u) << (8 * e);
             }
-        }
-        if (!PACKED || (tb >= 0 && (uint32_t)tb + 4 <= real)) {
             tok4[g] = make_uint4(tk[0], tk[1], tk[2], tk[3]);
             pos4[g] = make_int4(ps[0], ps[1], ps[2], ps[3]);
             doc4[g] = make_int4(dc[0], dc[1], dc[2], dc[3]);
             mask4[g] = mk;
-        } else {
+        }
+    } else {
+        // padding-free rows: window jj of update i from row position row_start[i][jj]
+        const uint64_t out0 = (uint64_t)i * a.per * p.T + (uint64_t)a.row_start[(uint64_t)i * (a.per + 1) + jj];
+        // Store groups are 4 destination elements aligned to 16 bytes.  A packed
+        // window may start mid-group: `lead` elements of that group belong to the
+        // previous window, and groups that straddle the window's ends are written
+        // element by element so that neighbouring windows never overwrite each other.
+        const uint32_t lead = (uint32_t)(out0 & 3u);
+        const uint64_t base = out0 - lead;
+        const uint32_t span = lead + real;
+        uint4* tok4 = reinterpret_cast<uint4*>(a.tok + base);
+        int4* pos4 = reinterpret_cast<int4*>(a.pos + base);
+        int4* doc4 = reinterpret_cast<int4*>(a.doc + base);
+        uint32_t* mask4 = reinterpret_cast<uint32_t*>(a.mask + base);
+        for (uint32_t g = threadIdx.x; g < (span + 3) / 4; g += EB) {
+            const int32_t tb = (int32_t)(4 * g) - (int32_t)lead;  // window position of the group's first element
+            const uint32_t tf = tb < 0 ? 0u : (uint32_t)tb;       // first position inside the window
+            uint32_t tk[4];
+            int32_t ps[4], dc[4];
+            uint32_t mk = 0;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int32_t ts = tb + e;
-                if (ts < 0 || (uint32_t)ts >= real) continue;
-                const uint64_t o = base + 4 * (uint64_t)g + e;
-                a.tok[o] = tk[e];
-                a.pos[o] = ps[e];
-                a.doc[o] = dc[e];
-                a.mask[o] = (uint8_t)(mk >> (8 * e));
+            for (int e = 0; e < 4; ++e) { tk[e] = pad; ps[e] = 0; dc[e] = -1; }
+            if (tf < real) {
+                uint32_t q = find(tf);
+                PieceView v = get(q);
+                uint32_t next_woff = (q + 1 < np) ? (staged ? s_woff[q + 1] : p.pc_woff[q0 + q + 1]) : real;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int32_t ts = tb + e;
+                    if (ts < 0 || (uint32_t)ts >= real) continue;
+                    const uint32_t t = (uint32_t)ts;
+                    while (t >= next_woff && q + 1 < np) {  // next piece (contiguous up to `real`)
+                        ++q;
+                        v = get(q);
+                        next_woff = (q + 1 < np) ? (staged ? s_woff[q + 1] : p.pc_woff[q0 + q + 1]) : real;
+                    }
+                    const uint32_t u = t - v.woff;
+                    tk[e] = (v.src + u < p.n_tokens) ? p.tokens[v.src + u] : pad;  // guard: never read past the corpus
+                    ps[e] = (int32_t)u;
+                    dc[e] = (int32_t)v.doc;
+                    mk |= (t >= v.mfrom ? 1u : 0u) << (8 * e);
+                }
+            }
+            if (tb >= 0 && (uint32_t)tb + 4 <= real) {
+                tok4[g] = make_uint4(tk[0], tk[1], tk[2], tk[3]);
+                pos4[g] = make_int4(ps[0], ps[1], ps[2], ps[3]);
+                doc4[g] = make_int4(dc[0], dc[1], dc[2], dc[3]);
+                mask4[g] = mk;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int32_t ts = tb + e;
+                    if (ts < 0 || (uint32_t)ts >= real) continue;
+                    const uint64_t o = base + 4 * (uint64_t)g + e;
+                    a.tok[o] = tk[e];
+                    a.pos[o] = ps[e];
+                    a.doc[o] = dc[e];
+                    a.mask[o] = (uint8_t)(mk >> (8 * e));
+                }
             }
         }
     }
