@@ -1,0 +1,40 @@
+"""Seeded random combinations of every mode on small corpora (wrap packing,
+random read order, cumulative mixture, lanes, batch-size ramp, held-out
+stream, arrivals, stream starts), for parity between the GPU and the oracle."""
+import numpy as np
+
+import oracle
+from synth.corpus import random_small
+
+
+def combo_corpus(seed):
+    """(corpus, description): the modes drawn from the seed; with stream starts,
+    the corpus goes on from the oracle's cycle 0 (first cycle 1)."""
+    r = np.random.default_rng(np.random.SeedSequence([4242, seed]))
+    L = int(r.choice([1, 1, 2, 3]))
+    ramp = r.random() < 0.3
+    heldout = r.random() < 0.2
+    T = 64 * int(r.choice([1, 2]))
+    b = [L * int(x) for x in r.integers(1, 4, size=2)]
+    B = max(b) if ramp else L * int(r.integers(1, 4))
+    c = random_small(seed, n_docs=int(r.integers(400, 1400)), n_sources=int(r.integers(1, 5)),
+                     max_strata=int(r.integers(1, 4)), T=T, B=B, max_len=int(r.integers(40, 400)),
+                     prompts=bool(r.random() < 0.5), bp_max=6000 if heldout else 1500)
+    mode = dict(wrap=bool(r.random() < 0.4), read_random=bool(r.random() < 0.4),
+                cumulative=bool(r.random() < 0.4), heldout=heldout, lanes=L,
+                updates_per_cycle=0 if heldout else int(r.choice([0, 2, 3, 5])))
+    if ramp:
+        mode["ramp"] = ((0, b[0] * T), (int(r.integers(T, 40 * T)), b[1] * T))
+    if r.random() < 0.3:
+        n_seg = int(r.integers(2, 4))
+        mode.update(segment=r.integers(0, n_seg, size=c.n_docs).astype(np.uint16), n_segments=n_seg)
+    c = c.replace(**mode)
+    desc = {k: v for k, v in mode.items() if k not in ("segment",) and v not in (False, None)}
+    if r.random() < 0.25:
+        try:
+            ci = oracle.Plan(c).cycle(0)
+            c = c.replace(start_tokens=ci.stream_next.copy(), first_cycle=1, tokens_start=ci.tokens_start + ci.positions)
+            desc["resumed"] = True
+        except oracle.OracleError:
+            pass
+    return c, desc

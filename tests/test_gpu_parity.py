@@ -462,17 +462,18 @@ def test_heldout_stream_parity(seed, wrap):
 
 def _parity_run(c, kind, arg):
     say("plan/cycle/batch", kind, arg, "docs", c.n_docs, "T", c.T, "B", c.B)
+    cyc = int(getattr(c, "first_cycle", 0))  # the first cycle the context plans
     op = oracle.Plan(c)
     pk = dp.Packer(c)
     compare_plan(pk, op)
     try:
-        oi = op.cycle(0)
+        oi = op.cycle(cyc)
     except oracle.OracleError as e:
         with pytest.raises(dp.DpackError) as ge:
-            pk.cycle(0)
+            pk.cycle(cyc)
         assert ge.value.code == e.code
         return
-    gi = pk.cycle(0)
+    gi = pk.cycle(cyc)
     compare_cycle(gi, oi, op)
     if getattr(c, "cumulative", False):
         assert np.array_equal(pk.inspect("cum_taken"), op.cumulative_taken().ravel())
@@ -496,6 +497,18 @@ def _parity_run(c, kind, arg):
                 assert fp[i].tobytes() == oracle.batch_fingerprint(o["digests"][x:x + Bb])
                 x += Bb
     pk.close()
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_mode_combinations(seed):
+    """Seeded random combinations of every mode (wrap, random read order,
+    cumulative mixture, lanes, batch-size ramp, held-out stream, arrivals,
+    stream starts) on small corpora: plan, cycle, batches and fingerprints
+    against the oracle."""
+    from _combos import combo_corpus
+    c, desc = combo_corpus(seed)
+    say("combination", seed, desc)
+    _parity_run(c, "combo", seed)
 
 
 @pytest.mark.parametrize("kind,arg,worlds", [("tiny", 0.5, [1, 2, 4, 8]), ("pretrain", 0.006, [1, 8, 16, 32, 64]),
