@@ -511,6 +511,48 @@ def test_mode_combinations(seed):
     _parity_run(c, "combo", seed)
 
 
+@pytest.mark.parametrize("seed", range(24))
+def test_mode_combinations_two_ranks(seed):
+    """The combinations with even batches at world 2 (with lanes, where 2 divides
+    them): each rank's slice equals the oracle's, and the two slices side by
+    side equal the world-1 batch."""
+    from _combos import combo_corpus
+    c, desc = combo_corpus(seed, even=True)
+    ramp = getattr(c, "ramp", None)
+    L = max(1, int(getattr(c, "lanes", 1) or 1))
+    if L > 1 and L % 2:
+        pytest.skip("ranks take whole lanes: world 2 does not divide 3 lanes")
+    cyc = int(getattr(c, "first_cycle", 0))
+    op = oracle.Plan(c)
+    try:
+        oi = op.cycle(cyc)
+    except oracle.OracleError:
+        pytest.skip("the combination runs out of data before its cycle: no batches to split")
+    n = min(3, oi.n_updates)
+    whole = op.batch(0, n)
+    parts = []
+    for r in range(2):
+        say("combination", seed, desc, "rank", r)
+        pk = dp.Packer(c, rank=r, world=2)
+        pk.cycle(cyc)
+        g = to_np(pk.batch(0, n))
+        compare_batch(g, op.batch(0, n, rank=r, world=2), f"combo {seed} rank {r}")
+        parts.append(g)
+        pk.close()
+    if ramp is None:  # [n, B/2, T] side by side
+        for k in ("tokens", "doc", "digests"):
+            assert np.array_equal(np.concatenate([x[k] for x in parts], axis=1), whole[k])
+    else:  # each update's windows: rank 0's half, then rank 1's
+        off, offs = 0, [0, 0]
+        for b in range(n):
+            Bb = int(oi.batches[b])
+            for r in range(2):
+                seg = parts[r]["tokens"][offs[r]:offs[r] + Bb // 2]
+                assert np.array_equal(seg, whole["tokens"][off + r * (Bb // 2):off + (r + 1) * (Bb // 2)])
+                offs[r] += Bb // 2
+            off += Bb
+
+
 @pytest.mark.parametrize("kind,arg,worlds", [("tiny", 0.5, [1, 2, 4, 8]), ("pretrain", 0.006, [1, 8, 16, 32, 64]),
                                              ("small", 4, [1, 2, 4, 8]), ("wrap-pretrain", 0.006, [1, 8, 64]),
                                              ("heldout", 1100, [1, 2, 4, 8]), ("random-tiny", 0.5, [1, 2, 4, 8]),
