@@ -75,6 +75,8 @@ def main():
                     help="updates the oracle emits for the CPU baseline (the plan is always whole)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-copy", action="store_true", help="skip the plain D2D copy used as calibration/ceiling")
+    ap.add_argument("--no-per-call", action="store_true",
+                    help="skip the latency of one update per pack_batch call (kernel traces of the step alone)")
     ap.add_argument("--wrap", action="store_true", help="wrap packing (PACK_FLAG_WRAP) instead of next-fit")
     ap.add_argument("--packed", action="store_true",
                     help="emit padding-free rows (pack_batch_packed, bucket 256) instead of padded windows and digests")
@@ -237,7 +239,7 @@ def main():
     # without the window digests, on a context whose cycle is planned: GPU time
     # between events on the context's stream, and host wall time to completion
     per_call = None
-    if not args.packed and not args.ramp:
+    if not args.packed and not args.ramp and not args.no_per_call:
         pk1 = dp.Packer(corpus, device_tensors=tensors)
         pk1.cycle(cyc)
         n_calls = min(20, U)
