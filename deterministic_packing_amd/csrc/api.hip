@@ -221,13 +221,17 @@ size_t carve(pack_ctx& c, char* base) {
     p.n_strata = k.take<uint32_t>(S);
     p.weight = k.take<uint64_t>(c.S_real);  // the recipe's weights (read by the mixture over the real sources)
     p.bp = k.take<uint32_t>(S);
+    // with the recipe (one staged copy at init): stream starts, zeroed statistics
+    // and error flag, the pad row
+    c.start_dev = k.take<uint64_t>(S);
+    p.stats = k.take<uint64_t>(4 * S);
+    p.err = k.take<uint32_t>(1);
+    p.pad16 = k.take<uint32_t>(16);
     p.group = k.take<uint32_t>(D);
     p.hash = k.take<uint64_t>(D);
     c.hash_first = k.take<uint32_t>(dp::hash_tile_count(p.n_tokens) + 2);
     p.keep = k.take<uint8_t>(D);
     p.kept_pos = k.take<uint32_t>(D + 1);
-    p.stats = k.take<uint64_t>(4 * S);
-    p.err = k.take<uint32_t>(1);
     p.key[0] = k.take<uint64_t>(D);
     p.key[1] = k.take<uint64_t>(D);
     p.val[0] = k.take<uint32_t>(D);
@@ -258,7 +262,6 @@ size_t carve(pack_ctx& c, char* base) {
     p.cyc_start = k.take<uint64_t>(S);
     p.checks = k.take<uint64_t>(2);
     p.cyc_sums = k.take<uint64_t>(2);
-    p.pad16 = k.take<uint32_t>(16);
     p.perm_start = k.take<uint64_t>(S + 1);
     p.perm = k.take<uint32_t>(WR);
     p.wkey[0] = k.take<uint64_t>(WR);
@@ -287,7 +290,6 @@ size_t carve(pack_ctx& c, char* base) {
     c.lane_k = k.take<uint32_t>(B / c.lanes);
     c.cum_Ar = k.take<uint32_t>(lanes && p.cumulative ? (CU + 1) * c.S_real : 0);
     c.ramp_n_real = k.take<uint32_t>(K * c.S_real);
-    c.start_dev = k.take<uint64_t>(S);
     c.next_win = k.take<uint64_t>(S);
     c.stream_next = k.take<uint64_t>(S);
     c.nstart = k.take<uint32_t>(S + 1);
@@ -306,9 +308,13 @@ void h2d(T* dst, const T* src, uint64_t count, hipStream_t st) {
 }
 
 // pinned staging: bytes for the largest set of copies between two synchronizations
-// largest use: pack_cycle's cycle starts, read-order starts, sums, digest
-// message (≤ 64 + 52·S bytes) and digest, each 64-byte aligned
-size_t pin_bytes_for(uint32_t S, uint64_t K) { return 192ull * S + 112ull * K + 8192; }
+// largest uses: pack_cycle's cycle starts, read-order starts, sums, digest
+// message (≤ 64 + 52·S bytes) and digest, each 64-byte aligned; pack_init's
+// first block (recipe with the arrival bases gbase, 4·(S·n_seg + 1) bytes,
+// starts, statistics, pad row: ≤ 56·S + 4·S·n_seg bytes plus alignment)
+size_t pin_bytes_for(uint32_t S, uint64_t K, uint64_t n_seg) {
+    return 192ull * S + 112ull * K + 4ull * S * n_seg + 8192;
+}
 
 template <typename T>
 T* pin_take(pack_ctx& c, uint64_t count) {
@@ -428,19 +434,30 @@ void release(pack_ctx* c) {
 void build_plan(pack_ctx& c) {
     dp::Plan& p = c.p;
     hipStream_t st = c.st;
-    // recipe to the device
+    // the recipe, stream starts, zeroed statistics and error flag and the pad
+    // row lie together at the start of the workspace: laid out in the pinned
+    // staging area as on the device and sent with one copy
     c.pin_off = 0;
-    h2d_staged(c, p.gbase, c.gbase.data(), (uint64_t)p.S * p.n_seg + 1);
-    h2d_staged(c, p.n_strata, c.n_strata.data(), p.S);
-    h2d_staged(c, p.weight, c.weight_real.data(), c.S_real);
-    if (!c.start_tokens.empty()) {
-        h2d_staged(c, c.start_dev, c.start_tokens.data(), p.S);
-        p.start_tok = c.start_dev;
+    {
+        uint8_t* const dbase = reinterpret_cast<uint8_t*>(p.gbase);
+        const size_t span = static_cast<size_t>(reinterpret_cast<uint8_t*>(p.pad16 + 16) - dbase);
+        uint8_t* const h = pin_take<uint8_t>(c, span);
+        std::memset(h, 0, span);
+        auto place = [&](const void* dev, const void* src, size_t bytes) {
+            if (bytes) std::memcpy(h + (static_cast<const uint8_t*>(dev) - dbase), src, bytes);
+        };
+        place(p.gbase, c.gbase.data(), 4ull * ((uint64_t)p.S * p.n_seg + 1));
+        place(p.n_strata, c.n_strata.data(), 4ull * p.S);
+        place(p.weight, c.weight_real.data(), 8ull * c.S_real);
+        place(p.bp, c.bp.data(), 4ull * p.S);
+        if (!c.start_tokens.empty()) {
+            place(c.start_dev, c.start_tokens.data(), 8ull * p.S);
+            p.start_tok = c.start_dev;
+        }
+        uint32_t* const pad = reinterpret_cast<uint32_t*>(h + (reinterpret_cast<uint8_t*>(p.pad16) - dbase));
+        for (int i = 0; i < 16; ++i) pad[i] = p.pad_token;
+        h2d(dbase, h, span, st);
     }
-    h2d_staged(c, p.bp, c.bp.data(), p.S);
-    dp::launch_zero_u32(p.err, 1, st);
-    dp::launch_zero_u64(p.stats, 4ull * p.S, st);
-    dp::launch_fill_u32(p.pad16, 16, p.pad_token, st);
 
     // validation first: no kernel reads the corpus through unchecked offsets
     c.timer.begin(PACK_PHASE_VALIDATE, st);
@@ -681,7 +698,7 @@ int pack_init(const pack_config* cfg, pack_ctx** out) {
         c->arena = static_cast<char*>(mem);
         c->arena_bytes = got;
         carve(*c, c->arena);
-        const size_t pbytes = pin_bytes_for(S, cfg->n_ramp);
+        const size_t pbytes = pin_bytes_for(S, cfg->n_ramp, c->p.n_seg);
         void* pin = arena_take(c->device, pbytes, &got, true);
         if (!pin) {
             if (hipHostMalloc(&pin, pbytes, hipHostMallocDefault) != hipSuccess) {

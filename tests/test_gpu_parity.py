@@ -770,6 +770,11 @@ def _max_case(name):
         L = r.integers(1, 150000, size=D)
         src, st, ns = r.integers(0, S, size=D).astype(np.uint16), np.zeros(D, np.uint16), np.ones(S, np.uint32)
         w, bp = np.array([1, 1], np.uint64), np.array([100, 100], np.uint32)
+    elif name == "max_arrivals":  # 30,000 arrivals of one source: 30,001 group bases staged at init
+        S, D, T, B = 1, 60000, 64, 8
+        L = r.integers(1, 120, size=D)
+        src, st, ns = np.zeros(D, np.uint16), np.zeros(D, np.uint16), np.ones(S, np.uint32)
+        w, bp = np.array([1], np.uint64), np.array([300], np.uint32)
     else:  # wide_update: 65,536 windows in one update, the most one emission-and-digest launch takes
         S, D, T, B = 2, 90000, 64, 65536
         L = r.integers(20, 64, size=D)
@@ -781,10 +786,14 @@ def _max_case(name):
     np.cumsum(L, out=off[1:])
     tok = r.integers(0, vocab, size=int(off[-1]), dtype=np.uint64).astype(np.uint32)
     pl = np.minimum(r.integers(0, 100, size=D), L).astype(np.uint32)
-    return Corpus(name, tok, off, src, st, pl, ns, w, bp, T=T, B=B, updates_per_cycle=0, seed=11, pad_token=7)
+    c = Corpus(name, tok, off, src, st, pl, ns, w, bp, T=T, B=B, updates_per_cycle=0, seed=11, pad_token=7)
+    if name == "max_arrivals":
+        c = c.replace(segment=r.integers(0, 30000, size=D).astype(np.uint16), n_segments=30000)
+    return c
 
 
-@pytest.mark.parametrize("name", ["max_sources", "max_groups", "full_range_tokens", "long_windows", "wide_update"])
+@pytest.mark.parametrize("name", ["max_sources", "max_groups", "max_arrivals", "full_range_tokens", "long_windows",
+                                  "wide_update"])
 def test_maximum_sizes(name):
     _edge_run(_max_case(name), name)
 
