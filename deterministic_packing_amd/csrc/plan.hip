@@ -77,37 +77,74 @@ __global__ __launch_bounds__(1024) void k_group_suffix_min(uint32_t* gs, uint32_
     }
 }
 
+// Number of elements of stratum k2 (documents [c0, c1) of the group order,
+// prefix gpre) that come before an element of stratum k at consumed fraction
+// a/A: a2/A2 < a/A, or equal and k2 < k; searched in [lo, hi).
+__device__ __forceinline__ uint32_t count_before(const Plan& p, uint32_t c0, uint32_t c1, bool earlier, uint64_t a,
+                                                 uint64_t A, uint32_t lo, uint32_t hi) {
+    const uint64_t base = p.gpre[c0];
+    const uint64_t A2 = p.gpre[c1] - base;
+    while (lo < hi) {
+        const uint32_t mid = (lo + hi) >> 1;
+        const uint64_t a2 = p.gpre[c0 + mid] - base;
+        const int c = cmp_mul128(a2, A, a, A2);
+        const bool before = earlier ? (c <= 0) : (c < 0);
+        if (before) lo = mid + 1;
+        else hi = mid;
+    }
+    return lo;
+}
+
+constexpr uint32_t MERGE_K = 128;  // other strata bracketed per block at once (two threads each)
+
+// A block whose documents all lie in one group first finds, for every other
+// stratum, the counts before its first and its last document (they bound
+// every count in between: the fraction grows with the position in the group);
+// each thread then searches only between them.  Blocks across a group
+// boundary search every stratum in full.
 __global__ __launch_bounds__(256) void k_merge(Plan p, const uint32_t* val) {
-    const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= p.n_kept) return;
-    const uint32_t d = val[i];
+    __shared__ uint32_t s_lo[MERGE_K], s_hi[MERGE_K];
+    const uint64_t i0 = (uint64_t)blockIdx.x * blockDim.x;
+    const uint64_t i = i0 + threadIdx.x;
+    const uint64_t ilast = min((uint64_t)p.n_kept, i0 + blockDim.x) - 1;  // the block's last document
+    const uint32_t gf = p.group[val[i0]], gl = p.group[val[ilast]];
+    const bool one_group = gf == gl;  // uniform across the block
+    const bool active = i < p.n_kept;
+    const uint32_t d = active ? val[i] : val[ilast];
     const uint32_t g = p.group[d];
     const uint32_t s = p.source[d];
     // merge unit: the (stream, arrival) of the document; its strata are groups g0 .. g0+K−1
     const uint32_t u = s * p.n_seg + (p.n_seg > 1 ? p.segment[d] : 0u);
     const uint32_t g0 = p.gbase[u], K = p.n_strata[s], k = g - g0;
     const uint32_t b0 = p.group_start[g];
-    const uint64_t a = p.gpre[i] - p.gpre[b0];
     const uint64_t A = p.gpre[p.group_start[g + 1]] - p.gpre[b0];
-    uint64_t rank = i - b0;
-    for (uint32_t k2 = 0; k2 < K; ++k2) {
-        if (k2 == k) continue;
-        const uint32_t c0 = p.group_start[g0 + k2], c1 = p.group_start[g0 + k2 + 1];
-        if (c0 == c1) continue;
-        const uint64_t base = p.gpre[c0];
-        const uint64_t A2 = p.gpre[c1] - base;
-        // elements (k2, j2) before (k, j):  a2/A2 < a/A, or equal and k2 < k
-        uint32_t lo = 0, hi = c1 - c0;
-        while (lo < hi) {
-            const uint32_t mid = (lo + hi) >> 1;
-            const uint64_t a2 = p.gpre[c0 + mid] - base;
-            const int c = cmp_mul128(a2, A, a, A2);
-            const bool before = (k2 < k) ? (c <= 0) : (c < 0);
-            if (before) lo = mid + 1;
-            else hi = mid;
+    auto frac = [&](uint64_t j) { return p.gpre[j] - p.gpre[b0]; };  // consumed tokens before element j
+    const uint64_t a = frac(active ? i : ilast);
+    uint64_t rank = (active ? i : ilast) - b0;
+    for (uint32_t kb = 0; kb < K; kb += MERGE_K) {
+        if (one_group) {
+            __syncthreads();  // the previous chunk's bounds are read
+            const uint32_t t = threadIdx.x >> 1, end = threadIdx.x & 1u;
+            const uint32_t k2 = kb + t;
+            if (t < MERGE_K && k2 < K && k2 != k) {
+                const uint32_t c0 = p.group_start[g0 + k2], c1 = p.group_start[g0 + k2 + 1];
+                const uint32_t r = c0 == c1 ? 0u
+                                            : count_before(p, c0, c1, k2 < k, frac(end ? ilast : i0), A, 0u, c1 - c0);
+                if (end) s_hi[t] = r;
+                else s_lo[t] = r;
+            }
+            __syncthreads();
         }
-        rank += lo;
+        const uint32_t kend = min(K, kb + MERGE_K);
+        for (uint32_t k2 = kb; k2 < kend; ++k2) {
+            if (k2 == k) continue;
+            const uint32_t c0 = p.group_start[g0 + k2], c1 = p.group_start[g0 + k2 + 1];
+            if (c0 == c1) continue;
+            const uint32_t lo = one_group ? s_lo[k2 - kb] : 0u, hi = one_group ? s_hi[k2 - kb] : c1 - c0;
+            rank += count_before(p, c0, c1, k2 < k, a, A, lo, hi);
+        }
     }
+    if (!active) return;
     const uint64_t at = p.group_start[g0] + rank;
     if (at < p.n_kept) p.order[at] = d;
     else atomicOr(p.err, ERR_INTERNAL);
