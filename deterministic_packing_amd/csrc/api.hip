@@ -293,7 +293,7 @@ size_t carve(pack_ctx& c, char* base) {
     c.next_win = k.take<uint64_t>(S);
     c.stream_next = k.take<uint64_t>(S);
     c.nstart = k.take<uint32_t>(S + 1);
-    c.dig_cap = 128 + 72 * S + 16 * K + 28;  // digest message: 64 + 60·S + 16·K + 28 bytes at most
+    c.dig_cap = 128 + 72 * S + 16 * K + 28;  // records 60·S, header ≤ 100 + 16·K, leaves 32·⌈S/16⌉
     c.dig_buf = k.take<uint8_t>(c.dig_cap + 32);
     return k.off + ALIGN;
 }
@@ -908,9 +908,26 @@ int pack_cycle(pack_ctx* c, uint32_t cycle, pack_cycle_info* info) {
         }
         const uint64_t* h_next = d2h_staged(*c, c->stream_next, S);
 
-        // plan digest: SHA-256 of a little-endian description of the recipe,
-        // stream sizes, cycle start and two order-free sums over the plan
+        // plan digest: SHA-256 of a little-endian header (mode, the recipe's
+        // scalars, the cycle, its updates, two order-free sums over the plan)
+        // followed by the digests of the streams' 60-byte records, 16 streams
+        // to a leaf (one lane each), so the serial chain stays short for many
+        // streams.  The records, then the header, go to the device in one copy;
+        // the leaf digests are written after the header there.
+        constexpr uint32_t REC = 60, LEAF = 16;
         std::vector<uint8_t> msg;
+        for (uint32_t s = 0; s < S; ++s) {
+            put(msg, c->weight[s], 8);
+            put(msg, c->bp[s], 4);
+            put(msg, c->n_strata[s], 4);
+            put(msg, c->n_upd[s], 4);
+            put(msg, c->src_win_start[s + 1] - c->src_win_start[s], 8);
+            put(msg, c->stats[0 * S + s], 8);
+            put(msg, c->stats[1 * S + s], 8);
+            put(msg, c->cyc_start[s], 8);
+            put(msg, c->start_tokens.empty() ? 0 : c->start_tokens[s], 8);
+        }
+        const size_t rec_bytes = msg.size();  // REC · S
         // the packing mode (D next-fit, W wrap) and the stream (1 training, V held-out) are part of the plan
         const char magic[8] = {'D', 'P', 'A', 'C', 'K', 'P', p.wrap ? 'W' : 'D', p.heldout ? 'V' : '1'};
         msg.insert(msg.end(), magic, magic + 8);
@@ -929,10 +946,7 @@ int pack_cycle(pack_ctx* c, uint32_t cycle, pack_cycle_info* info) {
             put(msg, 0x454E414Cu, 4);
             put(msg, c->lanes, 4);
         }
-        if (!c->start_tokens.empty()) {                // "STRT": the streams' first tokens
-            put(msg, 0x54525453u, 4);
-            for (uint32_t s = 0; s < S; ++s) put(msg, c->start_tokens[s], 8);
-        }
+        if (!c->start_tokens.empty()) put(msg, 0x54525453u, 4);  // "STRT": streams cut from given tokens
         if (p.n_seg > 1) {                             // "SEGS": documents ordered arrival by arrival
             put(msg, 0x53474553u, 4);
             put(msg, p.n_seg, 4);
@@ -942,23 +956,17 @@ int pack_cycle(pack_ctx* c, uint32_t cycle, pack_cycle_info* info) {
         put(msg, p.seed, 8);
         put(msg, S, 4);
         put(msg, p.pad_token, 4);
-        for (uint32_t s = 0; s < S; ++s) {
-            put(msg, c->weight[s], 8);
-            put(msg, c->bp[s], 4);
-            put(msg, c->n_strata[s], 4);
-            put(msg, c->n_upd[s], 4);
-            put(msg, c->src_win_start[s + 1] - c->src_win_start[s], 8);
-            put(msg, c->stats[0 * S + s], 8);
-            put(msg, c->stats[1 * S + s], 8);
-        }
         put(msg, cycle, 4);
         put(msg, c->U, 4);
-        for (uint32_t s = 0; s < S; ++s) put(msg, c->cyc_start[s], 8);
         put(msg, c->checks[0], 8);
         put(msg, c->checks[1], 8);
-        if (msg.size() > c->dig_cap) throw InvalError{"internal: digest buffer"};
+        const size_t head_bytes = msg.size() - rec_bytes;
+        const uint32_t leaves = (S + LEAF - 1) / LEAF;
+        if (rec_bytes + head_bytes + 32ull * leaves > c->dig_cap) throw InvalError{"internal: digest buffer"};
         h2d_staged(*c, c->dig_buf, msg.data(), msg.size());
-        dp::launch_sha_bytes(c->dig_buf, msg.size(), c->dig_buf + c->dig_cap, c->st);
+        uint8_t* const head = c->dig_buf + rec_bytes;
+        dp::launch_sha_chunks(c->dig_buf, rec_bytes, REC * LEAF, head + head_bytes, c->st);
+        dp::launch_sha_bytes(head, head_bytes + 32ull * leaves, c->dig_buf + c->dig_cap, c->st);
         c->timer.end(c->st);
         const uint8_t* h_digest = d2h_staged(*c, (const uint8_t*)(c->dig_buf + c->dig_cap), 32);
         DP_HIP(hipStreamSynchronize(c->st));

@@ -347,6 +347,7 @@ void launch_batch_fp(const uint8_t* digests, uint32_t B, uint32_t n_batches, uin
 // batches of B_b digests: batch b covers digests [slot0[step+b] − slot0[step], slot0[step+b+1] − slot0[step])
 void launch_batch_fp_var(const uint8_t* digests, const uint64_t* slot0, uint32_t step, uint32_t n_batches,
                          uint8_t* out, hipStream_t st);
+void launch_sha_chunks(const uint8_t* msg, uint64_t len, uint32_t chunk, uint8_t* out, hipStream_t st);
 void launch_sha_bytes(const uint8_t* msg, uint64_t len, uint8_t* out, hipStream_t st);
 
 // scans (scan.hip)

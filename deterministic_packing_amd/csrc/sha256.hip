@@ -537,6 +537,15 @@ __global__ void k_sha_bytes(const uint8_t* msg, uint64_t len, uint8_t* out) {
     if (threadIdx.x == 0 && blockIdx.x == 0) sha_bytes(msg, len, out);
 }
 
+// lane j: SHA-256 of msg[j·chunk, min((j+1)·chunk, len)) into out + 32·j
+__global__ __launch_bounds__(64) void k_sha_chunks(const uint8_t* msg, uint64_t len, uint32_t chunk, uint8_t* out) {
+    const uint64_t j = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const uint64_t x0 = j * chunk;
+    if (x0 >= len) return;
+    const uint64_t x1 = x0 + chunk < len ? x0 + chunk : len;
+    sha_bytes(msg + x0, x1 - x0, out + 32 * j);
+}
+
 }  // namespace
 
 void launch_window_sha(const Plan& p, const EmitArgs& a, hipStream_t st) {
@@ -570,6 +579,12 @@ void launch_batch_fp_var(const uint8_t* digests, const uint64_t* slot0, uint32_t
                          uint8_t* out, hipStream_t st) {
     hipLaunchKernelGGL(k_batch_fp_var, dim3((n_batches + 63) / 64), dim3(64), 0, st, digests, slot0, step, n_batches,
                        out);
+    DP_HIP(hipGetLastError());
+}
+
+void launch_sha_chunks(const uint8_t* msg, uint64_t len, uint32_t chunk, uint8_t* out, hipStream_t st) {
+    const uint64_t n = (len + chunk - 1) / chunk;
+    if (n) hipLaunchKernelGGL(k_sha_chunks, dim3((uint32_t)((n + 63) / 64)), dim3(64), 0, st, msg, len, chunk, out);
     DP_HIP(hipGetLastError());
 }
 

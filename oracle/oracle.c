@@ -1280,11 +1280,18 @@ int or_batch_packed(const or_plan *p, uint32_t step, uint32_t n_steps, uint32_t 
     return OR_OK;
 }
 
-/* Plan digest of the current cycle: SHA-256 over a little-endian byte string
- * of the recipe, the per-source stream sizes and cycle ranges, and two
- * order-free sums that change with the document order and content.  A resume
- * whose digest differs was planned from another recipe or order ([NS]
- * Training: a resume with another sample order is refused). */
+/* Plan digest of the current cycle: SHA-256 over a little-endian header (the
+ * mode, the recipe's scalars, the cycle, its updates and two order-free sums
+ * that change with the document order and content) followed by the digests of
+ * the streams' records, 16 streams to a leaf.  A stream's record (60 bytes):
+ * weight, hold-out rate, strata, windows per update, windows in the stream,
+ * kept documents and tokens, the cycle's first window, the stream's first
+ * token (0 without stream starts).  A resume whose digest differs was planned
+ * from another recipe or order ([NS] Training: a resume with another sample
+ * order is refused). */
+#define OR_DIGEST_RECORD 60u
+#define OR_DIGEST_LEAF 16u
+
 static void put(uint8_t **w, uint64_t v, int bytes)
 {
     for (int i = 0; i < bytes; i++) *(*w)++ = (uint8_t)(v >> (8 * i));
@@ -1295,12 +1302,19 @@ int or_plan_digest(const or_plan *p, uint8_t out[32])
     const or_corpus *c = &p->c;
     const uint32_t S = c->n_sources;
     if (p->cycle < (int64_t)p->c.first_cycle) return OR_E_STATE;
-    uint64_t bytes = 8 + 4 + 4 + 8 + 4 + 4 + (uint64_t)S * (8 + 4 + 4 + 4 + 8 + 8 + 8) + 4 + 4 + 8ull * S + 8 + 8
-                     + (c->read_random ? 4 : 0) + (c->cumulative ? 4 : 0)
-                     + (c->n_ramp ? 4 + 4 + 16ull * c->n_ramp + 8 : 0) + (p->lanes > 1 ? 8 : 0)
-                     + (c->start_tokens ? 4 + 8ull * S : 0) + (c->segment && c->n_segments > 1 ? 8 : 0);
+    const uint32_t leaves = (S + OR_DIGEST_LEAF - 1) / OR_DIGEST_LEAF;
+    uint8_t *rec = (uint8_t *)malloc((uint64_t)S * OR_DIGEST_RECORD + 1), *r = rec;
+    uint64_t bytes = 8 + 4 + 4 + (16ull * c->n_ramp + 16) + 8 + 4 + 8 + 4 + 4 + 8 + 4 + 4 + 4 + 4 + 8 + 8 + 32ull * leaves;
     uint8_t *buf = (uint8_t *)malloc(bytes), *w = buf;
-    if (!buf) return OR_E_NOMEM;
+    if (!rec || !buf) { free(rec); free(buf); return OR_E_NOMEM; }
+    for (uint32_t s = 0; s < S; s++) {
+        put(&r, c->weight[s], 8); put(&r, c->bp[s], 4); put(&r, c->n_strata[s], 4);
+        put(&r, p->n_upd[s], 4);
+        put(&r, p->src_win_start[s + 1] - p->src_win_start[s], 8);
+        put(&r, p->kept_docs[s], 8); put(&r, p->kept_tokens[s], 8);
+        put(&r, p->cyc_start[s], 8);
+        put(&r, c->start_tokens ? c->start_tokens[s] : 0, 8);
+    }
     /* the packing mode and the stream (training / held-out) are part of the plan */
     memcpy(w, "DPACKP", 6); w += 6;
     *w++ = c->wrap ? 'W' : 'D';
@@ -1314,22 +1328,18 @@ int or_plan_digest(const or_plan *p, uint8_t out[32])
         put(&w, p->tokens_done, 8);
     }
     if (p->lanes > 1) { put(&w, 0x454E414Cu, 4); put(&w, p->lanes, 4); }  /* "LANE" and the lane count */
-    if (c->start_tokens) {                         /* "STRT": the streams' first tokens */
-        put(&w, 0x54525453u, 4);
-        for (uint32_t s = 0; s < S; s++) put(&w, c->start_tokens[s], 8);
-    }
+    if (c->start_tokens) put(&w, 0x54525453u, 4);  /* "STRT": streams cut from given tokens (in the records) */
     if (c->segment && c->n_segments > 1) { put(&w, 0x53474553u, 4); put(&w, c->n_segments, 4); }  /* "SEGS" */
     put(&w, c->T, 4); put(&w, c->B, 4); put(&w, c->seed, 8); put(&w, S, 4); put(&w, c->pad_token, 4);
-    for (uint32_t s = 0; s < S; s++) {
-        put(&w, c->weight[s], 8); put(&w, c->bp[s], 4); put(&w, c->n_strata[s], 4);
-        put(&w, p->n_upd[s], 4);
-        put(&w, p->src_win_start[s + 1] - p->src_win_start[s], 8);
-        put(&w, p->kept_docs[s], 8); put(&w, p->kept_tokens[s], 8);
-    }
     put(&w, (uint64_t)p->cycle, 4); put(&w, p->U, 4);
-    for (uint32_t s = 0; s < S; s++) put(&w, p->cyc_start[s], 8);
     put(&w, p->order_check, 8); put(&w, p->hash_check, 8);
+    for (uint32_t j = 0; j < leaves; j++) {  /* the records' digests, 16 streams to a leaf */
+        const uint32_t s0 = j * OR_DIGEST_LEAF, s1 = s0 + OR_DIGEST_LEAF < S ? s0 + OR_DIGEST_LEAF : S;
+        or_sha256(rec + (uint64_t)s0 * OR_DIGEST_RECORD, (uint64_t)(s1 - s0) * OR_DIGEST_RECORD, w);
+        w += 32;
+    }
     or_sha256(buf, (uint64_t)(w - buf), out);
+    free(rec);
     free(buf);
     return OR_OK;
 }
