@@ -711,6 +711,9 @@ EDGE = {
     "tiny_share_zero_seats": lambda: _explicit([30] * 200, 64, 4, sources=[0, 1] * 100, weights=[1000, 1]),
     "prompt_beyond_doc": lambda: _explicit([10, 100, 200] * 30, 64, 2, prompts=[50, 3, 150] * 30),
     "many_pieces_window": lambda: _explicit([1] * 5000, 4096, 1),
+    "single_document": lambda: _explicit([37], 64, 1),
+    "one_nonempty_among_empty": lambda: _explicit([0, 0, 0, 130, 0, 0], 64, 1),
+    "prompts_cover_everything": lambda: _explicit([10, 70, 200, 3] * 20, 64, 2, prompts=[10, 80, 200, 9] * 20),
 }
 
 
