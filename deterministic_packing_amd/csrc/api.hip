@@ -308,10 +308,14 @@ void h2d(T* dst, const T* src, uint64_t count, hipStream_t st) {
 }
 
 // pinned staging: bytes for the largest set of copies between two synchronizations
-// largest uses: pack_cycle's cycle starts, read-order starts, sums, digest
-// message (≤ 64 + 52·S bytes) and digest, each 64-byte aligned; pack_init's
-// first block (recipe with the arrival bases gbase, 4·(S·n_seg + 1) bytes,
-// starts, statistics, pad row: ≤ 56·S + 4·S·n_seg bytes plus alignment)
+// largest uses: pack_cycle's copies, each 64-byte aligned: cycle starts,
+// read-order starts, the cumulative schedule's remaining windows and totals,
+// next windows and next tokens (8·S bytes each, about 48·S in all), the ramp's
+// spans (40 bytes per piece), sums, error flag, the plan digest's message (60·S
+// bytes of stream records, then a header of at most 100 + 16·K bytes) and the
+// digest; pack_init's first block (recipe with the arrival bases gbase,
+// 4·(S·n_seg + 1) bytes, starts, statistics, pad row: ≤ 56·S + 4·S·n_seg bytes
+// plus alignment)
 size_t pin_bytes_for(uint32_t S, uint64_t K, uint64_t n_seg) {
     return 192ull * S + 112ull * K + 4ull * S * n_seg + 8192;
 }
