@@ -2,17 +2,21 @@
 """Packed tokens/s of the whole deterministic-packing path on one MI355X.
 
 One step = one pass of the whole path over the resident synthetic corpus:
-pack_init (validation, hash + hold-out, keys, radix sort, strata merge,
-pieces, next-fit cut, window table, mixture) + pack_cycle(0) + pack_batch of
-every update of the cycle with learned counts and per-window SHA-256 digests
-+ pack_destroy.  The corpus is in HBM and the output buffers are allocated
+pack_init (validation, hash + hold-out, keys, sort, strata merge, pieces,
+next-fit cut, window table, mixture) + pack_cycle(0) + pack_batch of every
+update of the cycle with learned counts and per-window SHA-256 digests +
+pack_destroy.  The corpus is in HBM and the output buffers are allocated
 before the timed region.  value = real (non-padding) tokens emitted per second.
+The default workload is the full cycle: 2·10^9 tokens resident, 15 sources x
+8 strata, T = 4096, B = 1024, every update of the longest cycle.
 
 Per-kernel times come from HIP events the library records on its stream
 (PACK_FLAG_TIMING) inside the timed steps; the roofline object is reported for
 the kernel that takes the most time, and every phase is listed under
-"kernels".  The CPU baseline is the oracle (plain sequential C) timed on this
-host on a bounded sample of the same workload.
+"kernels".  The emission kernel without digests (the packing kernel on its
+own, HBM-bound) is timed the same way in a separate pass over the same cycle
+and reported as roofline_emit.  The CPU baseline is the oracle (plain
+sequential C) timed on this host on a bounded sample of the same workload.
 """
 import argparse
 import json
@@ -69,10 +73,13 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", default="pretrain", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--workload", default="full", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--scale", type=float, default=1.0, help="fraction of the workload (1.0 = as specified)")
-    ap.add_argument("--cpu-sample-updates", type=int, default=10,
-                    help="updates the oracle emits for the CPU baseline (the plan is always whole)")
+    ap.add_argument("--cpu-sample-seconds", type=float, default=12.0,
+                    help="the oracle emits (with digests) whole updates from update 0 until this much time has "
+                         "passed, for the CPU baseline (the plan is always whole)")
+    ap.add_argument("--cpu-sample-updates", type=int, default=0,
+                    help="emit exactly this many updates for the CPU baseline instead (0: by time)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-copy", action="store_true", help="skip the plain D2D copy used as calibration/ceiling")
     ap.add_argument("--no-per-call", action="store_true",
@@ -164,6 +171,7 @@ def main():
         else:
             pk.batch_into(0, info["n_updates"], out)
         tm = pk.timings(reset=True)
+        pk.status()  # a failure inside the batch kernels raises here
         pk.close()
         return info, tm
 
@@ -234,6 +242,28 @@ def main():
         if "achieved" in e:
             side[k] = {"kernel": k, "bound": "hbm", "achieved": e["achieved"], "peak": HBM_PEAK_GBPS,
                        "unit": "GB/s", "frac": e["frac"], "traffic": traffic_from_profile(k, args.workload)}
+    if "emit" not in side:
+        # the emission kernel on its own (pack_batch without digests over the
+        # same cycle, into the same buffers), timed by the library's events
+        pk2 = dp.Packer(corpus, device_tensors=tensors, timing=True)
+        pk2.cycle(cyc)
+        nod = dict(out, digests=None)
+        pk2.batch_into(0, U, nod)  # warm-up
+        pk2.timings(reset=True)
+        reps = 3
+        for _ in range(reps):
+            pk2.batch_into(0, U, nod)
+        ms_e, n_e = pk2.timings(reset=True)["emit"]
+        pk2.status()
+        pk2.close()
+        per_launch_ms = ms_e / n_e
+        ach = emit_bytes / (per_launch_ms / 1e3) / 1e9
+        side["emit"] = {"kernel": "emit", "bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBPS,
+                        "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
+                        "traffic": traffic_from_profile("emit", args.workload),
+                        "ms_per_launch": round(per_launch_ms, 4), "work_per_launch": emit_bytes,
+                        "measured": f"pack_batch without digests over the whole cycle, {reps} launches"}
+        log(f"emission alone: {per_launch_ms:.3f} ms per cycle, {ach:.1f} GB/s")
 
     # latency of one update per call (pack_batch of a single update), with and
     # without the window digests, on a context whose cycle is planned: GPU time
@@ -283,49 +313,60 @@ def main():
         copy = {"bytes_per_copy": 2 * 4 * n, "ms": round(ms, 4), "GBps": round(2 * 4 * n / (ms / 1e3) / 1e9, 1)}
         del a, b
 
-    # CPU baseline: the oracle on this host (whole plan, sampled updates)
+    # CPU baseline: the oracle on this host (whole plan, then whole updates
+    # from update 0 until the time budget is spent), and a bit-exact check of
+    # the GPU's outputs of the last timed step on every sampled update
     cpu = None
     sample_check = None
     if not args.no_cpu_baseline:
+        import platform
         import oracle
         oracle.build()
-        n_s = max(1, min(args.cpu_sample_updates, U))
         t_a = time.perf_counter()
         op = oracle.Plan(corpus)
         t_b = time.perf_counter()
         oi = op.cycle(cyc)
         t_c = time.perf_counter()
-        ob = op.batch_packed(0, n_s) if args.packed else op.batch(0, n_s, digests=True)
-        t_d = time.perf_counter()
-        est = (t_b - t_a) + (t_c - t_b) + (t_d - t_c) * sum(batches) / sum(batches[:n_s])
+        first_win = np.concatenate([[0], np.cumsum(batches)]).astype(np.int64)
+        n_s, t_emit, mism = 0, 0.0, 0
+        while n_s < U and ((args.cpu_sample_updates == 0 and t_emit < args.cpu_sample_seconds)
+                           or n_s < args.cpu_sample_updates):
+            t_x = time.perf_counter()
+            ob = op.batch_packed(n_s, 1) if args.packed else op.batch(n_s, 1, digests=True)
+            t_emit += time.perf_counter() - t_x
+            if args.packed:
+                ln = int(ob["length"][0])
+                mism += int(int(out["length"][n_s].item()) != ln)
+                mism += int((out["row_start"][n_s].cpu().numpy() != ob["row_start"][0]).sum())
+                for key in ("tokens", "pos", "doc", "mask"):
+                    g = out[key][n_s, :ln].cpu().numpy()
+                    if key == "tokens":
+                        g = g.view(np.uint32)
+                    mism += int((g != ob[key][0, :ln]).sum())
+                mism += int(int(out["learned"][n_s].item()) != int(op.batch(n_s, 1, digests=False)["learned"][0]))
+            else:
+                for key in ("tokens", "pos", "doc", "mask", "digests"):
+                    if args.ramp:  # flat [windows, ...]: this update's windows
+                        g = out[key][int(first_win[n_s]):int(first_win[n_s + 1])].cpu().numpy()
+                    else:
+                        g = out[key][n_s].cpu().numpy()
+                    if key == "tokens":
+                        g = g.view(np.uint32)
+                    mism += int((g != ob[key].reshape(g.shape)).sum())
+                mism += int(int(out["learned"][n_s].item()) != int(ob["learned"][0]))
+            n_s += 1
+        est = (t_b - t_a) + (t_c - t_b) + t_emit * sum(batches) / sum(batches[:n_s])
+        model = next((ln.split(":", 1)[1].strip() for ln in open("/proc/cpuinfo") if ln.startswith("model name")),
+                     platform.processor())
         cpu = {"value": round(real / est, 1), "unit": "packed tokens/s", "cores": 1, "kind": "oracle",
+               "host": {"nproc": os.cpu_count(), "usable_cpus": len(os.sched_getaffinity(0)), "cpu_model": model},
                "sample": (f"whole plan of the corpus ({t_b - t_a:.2f}s) + cycle ({t_c - t_b:.2f}s) + "
                           + ("padding-free rows" if args.packed else "emission with SHA-256")
-                          + f" of updates 0..{n_s - 1} of {U} ({t_d - t_c:.2f}s), scaled to the cycle's "
-                          f"{sum(batches)} windows: {est:.2f}s per step; single-threaded C")}
-        log(f"cpu baseline {cpu['value']:.4g} tokens/s ({est:.1f}s per step)")
-        # bit-exactness on the sample: GPU outputs of the last timed step vs the oracle
-        mism = 0
-        if args.packed:
-            lens = out["length"][:n_s].cpu().numpy()
-            mism += int((lens != ob["length"]).sum()) + int((out["row_start"][:n_s].cpu().numpy() != ob["row_start"]).sum())
-            for key in ("tokens", "pos", "doc", "mask"):
-                g = out[key][:n_s].cpu().numpy()
-                if key == "tokens":
-                    g = g.view(np.uint32)
-                mism += sum(int((g[i, :int(ob["length"][i])] != ob[key][i, :int(ob["length"][i])]).sum())
-                            for i in range(n_s))
-            mism += int((out["learned"][:n_s].cpu().numpy() != op.batch(0, n_s, digests=False)["learned"]).sum())
-        else:
-            lead = sum(batches[:n_s]) if args.ramp else n_s  # ramp: the first updates' windows, flat
-            for key in ("tokens", "pos", "doc", "mask", "digests"):
-                g = out[key][:lead].cpu().numpy()
-                if key == "tokens":
-                    g = g.view(np.uint32)
-                mism += int((g != ob[key]).sum())
-            mism += int((out["learned"][:n_s].cpu().numpy() != ob["learned"]).sum())
+                          + f" of updates 0..{n_s - 1} of {U} ({t_emit:.2f}s), scaled to the cycle's "
+                          f"{sum(batches)} windows: {est:.2f}s per step; single-threaded C on one core")}
+        log(f"cpu baseline {cpu['value']:.4g} tokens/s ({est:.1f}s per step) on {model}")
         mism += int(oi.plan_digest != info["plan_digest"])
-        sample_check = {"updates_compared": n_s, "windows_compared": sum(batches[:n_s]), "mismatches": mism}
+        sample_check = {"updates_compared": n_s, "windows_compared": int(sum(batches[:n_s])), "mismatches": mism}
         log(f"bit-exact check on {n_s} updates: {mism} mismatches")
 
     line = {

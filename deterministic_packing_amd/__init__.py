@@ -18,7 +18,8 @@ import numpy as np
 
 __all__ = [
     "DpackError", "load_library", "pack_init", "pack_cycle", "pack_batch", "pack_batch_packed", "pack_fingerprint",
-    "pack_fingerprint_steps", "pack_inspect", "pack_get_timings", "pack_destroy", "pack_strerror", "Packer", "INSPECT", "SYMBOLS",
+    "pack_fingerprint_steps", "pack_inspect", "pack_get_timings", "pack_status", "pack_test_option", "pack_destroy",
+    "pack_strerror", "Packer", "INSPECT", "SYMBOLS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -26,11 +27,12 @@ LIB_PATH = os.path.join(_HERE, "libdpack.so")
 ABI_VERSION = 2
 
 PACK_OK, PACK_E_ABI, PACK_E_INVAL, PACK_E_NOMEM, PACK_E_HIP = 0, -1, -2, -3, -4
-PACK_E_EXHAUSTED, PACK_E_STATE, PACK_E_RANGE = -5, -6, -7
+PACK_E_EXHAUSTED, PACK_E_STATE, PACK_E_RANGE, PACK_E_INTERNAL = -5, -6, -7, -8
+PACK_TEST_WAIT_GIVE_UP, PACK_TEST_CYCLE_FAULT = 1, 2
 
 SYMBOLS = ("pack_init", "pack_cycle", "pack_batch", "pack_batch_packed", "pack_fingerprint",
-           "pack_fingerprint_steps", "pack_inspect", "pack_get_timings", "pack_destroy", "pack_strerror",
-           "pack_last_error")
+           "pack_fingerprint_steps", "pack_inspect", "pack_get_timings", "pack_status", "pack_test_option",
+           "pack_destroy", "pack_strerror", "pack_last_error")
 
 PACK_FLAG_TIMING = 1
 PACK_FLAG_WRAP = 2
@@ -132,6 +134,10 @@ def load_library(path: Optional[str] = None):
     lib.pack_inspect.argtypes = [vp, u32, vp, C.c_uint64, C.POINTER(C.c_uint64)]
     lib.pack_get_timings.restype = i32
     lib.pack_get_timings.argtypes = [vp, C.POINTER(PackTimings), i32]
+    lib.pack_status.restype = i32
+    lib.pack_status.argtypes = [vp]
+    lib.pack_test_option.restype = i32
+    lib.pack_test_option.argtypes = [vp, u32, u32]
     lib.pack_destroy.restype = None
     lib.pack_destroy.argtypes = [vp]
     lib.pack_strerror.restype = C.c_char_p
@@ -206,6 +212,15 @@ def pack_get_timings(ctx: int, reset: bool = False) -> dict:
     t = PackTimings()
     _check(load_library().pack_get_timings(ctx, C.byref(t), 1 if reset else 0), "pack_get_timings", ctx)
     return {name: (t.ms[i], int(t.calls[i])) for i, name in enumerate(PHASES)}
+
+
+def pack_status(ctx: int) -> None:
+    """Synchronize and raise if a kernel of an earlier asynchronous call failed."""
+    _check(load_library().pack_status(ctx), "pack_status", ctx)
+
+
+def pack_test_option(ctx: int, what: int, value: int) -> None:
+    _check(load_library().pack_test_option(ctx, what, value), "pack_test_option", ctx)
 
 
 def pack_destroy(ctx: int) -> None:
@@ -332,7 +347,10 @@ class Packer:
         return out
 
     def batch(self, step: int, n_steps: int = 1, digests: bool = True, learned: bool = True) -> dict:
-        return self.batch_into(step, n_steps, self.alloc_out(n_steps, digests, learned, step))
+        """pack_batch into new buffers, then pack_status (synchronous)."""
+        out = self.batch_into(step, n_steps, self.alloc_out(n_steps, digests, learned, step))
+        pack_status(self.ctx)
+        return out
 
     def alloc_out_packed(self, n_steps: int, learned: bool = True) -> dict:
         t = self.torch
@@ -378,6 +396,12 @@ class Packer:
 
     def timings(self, reset: bool = False) -> dict:
         return pack_get_timings(self.ctx, reset)
+
+    def status(self) -> None:
+        pack_status(self.ctx)
+
+    def test_option(self, what: int, value: int) -> None:
+        pack_test_option(self.ctx, what, value)
 
 
 def upload_corpus(corpus, device: str = "cuda") -> dict:

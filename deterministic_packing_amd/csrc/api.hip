@@ -76,6 +76,11 @@ struct InvalError {
     std::string msg;
 };
 
+// a kernel flagged ERR_INTERNAL: a library bug or a bounded wait that gave up
+struct InternalError {
+    std::string msg;
+};
+
 }  // namespace
 
 // HIP events around kernel phases, recorded on the context's stream when the
@@ -162,6 +167,7 @@ struct pack_ctx {
     std::vector<uint64_t> src_win_start, stats, checks, src_piece_start;
     std::vector<uint32_t> n_upd;
     int64_t cycle = -1;
+    bool ready = false;  // a cycle is current: its device tables are valid for pack_batch
     uint32_t U = 0;
     std::vector<uint64_t> cyc_start, cyc_next, taken;
     // batch-size ramp: pieces, each piece's apportionment [K][S], the tokens
@@ -222,10 +228,11 @@ size_t carve(pack_ctx& c, char* base) {
     p.weight = k.take<uint64_t>(c.S_real);  // the recipe's weights (read by the mixture over the real sources)
     p.bp = k.take<uint32_t>(S);
     // with the recipe (one staged copy at init): stream starts, zeroed statistics
-    // and error flag, the pad row
+    // and error flags, the pad row
     c.start_dev = k.take<uint64_t>(S);
     p.stats = k.take<uint64_t>(4 * S);
     p.err = k.take<uint32_t>(1);
+    p.err_batch = k.take<uint32_t>(1);
     p.pad16 = k.take<uint32_t>(16);
     p.group = k.take<uint32_t>(D);
     p.hash = k.take<uint64_t>(D);
@@ -563,7 +570,7 @@ void build_plan(pack_ctx& c) {
     c.checks.assign(h_checks, h_checks + 2);
     c.src_piece_start.assign(h_sps, h_sps + p.S + 1);
     err = *h_err;
-    if (err) throw dp::HipError{hipErrorUnknown, "internal plan consistency check (library bug)"};
+    if (err) throw InternalError{"internal plan consistency check failed (library bug)"};
     if (!c.ramp_tokens.empty()) {  // K·S counts: once, at init (may exceed the staging area)
         const uint64_t K = c.ramp_tokens.size();
         std::vector<uint32_t> nr(K * c.S_real);
@@ -595,6 +602,7 @@ const char* pack_strerror(int code) {
         case PACK_E_EXHAUSTED: return "a source cannot supply the cycle (data exhausted)";
         case PACK_E_STATE: return "call out of order";
         case PACK_E_RANGE: return "step range outside the current cycle";
+        case PACK_E_INTERNAL: return "internal failure inside a kernel (library bug); results not valid";
         default: return "unknown error";
     }
 }
@@ -725,6 +733,10 @@ int pack_init(const pack_config* cfg, pack_ctx** out) {
         g_init_error = e.msg;
         release(c);
         return PACK_E_INVAL;
+    } catch (const InternalError& e) {
+        g_init_error = e.msg;
+        release(c);
+        return PACK_E_INTERNAL;
     } catch (const dp::HipError& e) {
         fail_hip(nullptr, e);
         release(c);
@@ -744,6 +756,10 @@ int pack_cycle(pack_ctx* c, uint32_t cycle, pack_cycle_info* info) {
         c->err = "cycles must be planned in order first_cycle, first_cycle + 1, ...";
         return PACK_E_STATE;
     }
+    // From here the cycle's device tables are rewritten: until this call
+    // succeeds no cycle is current.  Host state is committed only after the
+    // final synchronization, so on any error the same cycle can be planned again.
+    c->ready = false;
     try {
         std::vector<uint64_t> start(S), rem(S), taken(S);
         for (uint32_t s = 0; s < S; ++s) {
@@ -758,6 +774,7 @@ int pack_cycle(pack_ctx* c, uint32_t cycle, pack_cycle_info* info) {
         const uint64_t t0 = cycle == c->cfg.first_cycle ? c->cfg.tokens_start : c->tokens_next;
         std::vector<uint32_t> upd_B;
         std::vector<uint64_t> upd_out0;
+        dp::launch_zero_u32(p.err, 1, c->st);  // cycle kernels flag internal failures here
         if (p.tabled) {
             // per-update counts: the cumulative schedule and/or a batch-size ramp
             uint64_t total = 0;
@@ -807,7 +824,7 @@ int pack_cycle(pack_ctx* c, uint32_t cycle, pack_cycle_info* info) {
                 const uint64_t* h_out = d2h_staged(*c, p.cum_out, Sr + 1);
                 const uint32_t* h_err = d2h_staged(*c, p.err, 1);
                 sync_staged(*c);
-                if (*h_err & dp::ERR_INTERNAL) throw InvalError{"internal: cumulative schedule"};
+                if (*h_err & dp::ERR_INTERNAL) throw InternalError{"internal: cumulative schedule (library bug)"};
                 const uint64_t got = h_out[Sr];
                 for (uint32_t v = 0; v < S; ++v) taken[v] = h_out[v / L];
                 c->pin_off = 0;
@@ -881,18 +898,12 @@ int pack_cycle(pack_ctx* c, uint32_t cycle, pack_cycle_info* info) {
             for (uint32_t b : upd_B) slots += b;
         else
             slots = U * p.B;
-        c->U = (uint32_t)U;
-        c->cyc_start = start;
-        c->taken = taken;
-        for (uint32_t s = 0; s < S; ++s) c->cyc_next[s] = start[s] + taken[s];
-        c->cycle = cycle;
-        c->tokens_start = t0;
-        c->tokens_next = t0 + slots * p.T;
-        c->upd_B = std::move(upd_B);
-        c->upd_out0 = std::move(upd_out0);
+        const uint32_t U32 = (uint32_t)U;
+        std::vector<uint64_t> next(S);
+        for (uint32_t s = 0; s < S; ++s) next[s] = start[s] + taken[s];
         c->timer.begin(PACK_PHASE_CYCLE, c->st);
-        h2d_staged(*c, p.cyc_start, c->cyc_start.data(), S);
-        if (p.tabled) dp::launch_cum_slots(p, c->U, c->st);
+        h2d_staged(*c, p.cyc_start, start.data(), S);
+        if (p.tabled) dp::launch_cum_slots(p, U32, c->st);
         if (p.read_random) {  // each source's cycle windows in their random read order
             std::vector<uint64_t> ps(S + 1, 0);
             for (uint32_t s = 0; s < S; ++s) ps[s + 1] = ps[s] + taken[s];
@@ -905,7 +916,7 @@ int pack_cycle(pack_ctx* c, uint32_t cycle, pack_cycle_info* info) {
             std::vector<uint64_t> nw(S);
             for (uint32_t s = 0; s < S; ++s) {
                 const uint64_t M = c->src_win_start[s + 1] - c->src_win_start[s];
-                nw[s] = c->cyc_next[s] < M ? c->src_win_start[s] + c->cyc_next[s] : ~0ull;
+                nw[s] = next[s] < M ? c->src_win_start[s] + next[s] : ~0ull;
             }
             h2d_staged(*c, c->next_win, nw.data(), S);
             dp::launch_stream_next(p, c->next_win, c->stream_next, c->st);
@@ -928,7 +939,7 @@ int pack_cycle(pack_ctx* c, uint32_t cycle, pack_cycle_info* info) {
             put(msg, c->src_win_start[s + 1] - c->src_win_start[s], 8);
             put(msg, c->stats[0 * S + s], 8);
             put(msg, c->stats[1 * S + s], 8);
-            put(msg, c->cyc_start[s], 8);
+            put(msg, start[s], 8);
             put(msg, c->start_tokens.empty() ? 0 : c->start_tokens[s], 8);
         }
         const size_t rec_bytes = msg.size();  // REC · S
@@ -961,7 +972,7 @@ int pack_cycle(pack_ctx* c, uint32_t cycle, pack_cycle_info* info) {
         put(msg, S, 4);
         put(msg, p.pad_token, 4);
         put(msg, cycle, 4);
-        put(msg, c->U, 4);
+        put(msg, U32, 4);
         put(msg, c->checks[0], 8);
         put(msg, c->checks[1], 8);
         const size_t head_bytes = msg.size() - rec_bytes;
@@ -973,12 +984,27 @@ int pack_cycle(pack_ctx* c, uint32_t cycle, pack_cycle_info* info) {
         dp::launch_sha_bytes(head, head_bytes + 32ull * leaves, c->dig_buf + c->dig_cap, c->st);
         c->timer.end(c->st);
         const uint8_t* h_digest = d2h_staged(*c, (const uint8_t*)(c->dig_buf + c->dig_cap), 32);
+        const uint32_t* h_cerr = d2h_staged(*c, p.err, 1);
         DP_HIP(hipStreamSynchronize(c->st));
         const uint64_t sums[2] = {h_sums[0], h_sums[1]};
         std::vector<uint64_t> next_tok(h_next, h_next + S);
         uint8_t digest[32];
         std::memcpy(digest, h_digest, 32);
+        const uint32_t cerr = *h_cerr;
         c->pin_off = 0;
+        if (cerr & dp::ERR_INTERNAL) throw InternalError{"internal: a cycle kernel found the plan inconsistent (library bug)"};
+
+        // commit the cycle
+        c->U = U32;
+        c->cyc_start = start;
+        c->taken = taken;
+        c->cyc_next = next;
+        c->cycle = cycle;
+        c->tokens_start = t0;
+        c->tokens_next = t0 + slots * p.T;
+        c->upd_B = std::move(upd_B);
+        c->upd_out0 = std::move(upd_out0);
+        c->ready = true;
 
         if (info) {
             info->cycle = cycle;
@@ -1003,20 +1029,65 @@ int pack_cycle(pack_ctx* c, uint32_t cycle, pack_cycle_info* info) {
         return PACK_OK;
     } catch (const InvalError& e) {
         c->err = e.msg;
+        c->pin_off = 0;
         return PACK_E_INVAL;
+    } catch (const InternalError& e) {
+        c->err = e.msg;
+        c->pin_off = 0;
+        return PACK_E_INTERNAL;
     } catch (const dp::HipError& e) {
+        c->pin_off = 0;
         return fail_hip(c, e);
     } catch (const std::bad_alloc&) {
         c->err = "host allocation failed";
+        c->pin_off = 0;
         return PACK_E_NOMEM;
     }
+}
+
+int pack_status(pack_ctx* c) {
+    if (!c) return PACK_E_INVAL;
+    c->err.clear();
+    try {
+        // the staging area is free between calls: every call resets it after its synchronization
+        c->pin_off = 0;
+        const uint32_t* h = d2h_staged(*c, c->p.err_batch, 1);
+        DP_HIP(hipStreamSynchronize(c->st));
+        const uint32_t e = *h;
+        c->pin_off = 0;
+        if (e & dp::ERR_INTERNAL) {
+            dp::launch_zero_u32(c->p.err_batch, 1, c->st);
+            DP_HIP(hipStreamSynchronize(c->st));
+            c->err = "internal: a batch kernel's bounded wait gave up; the digests of the calls since the last "
+                     "pack_status are not valid (library bug)";
+            return PACK_E_INTERNAL;
+        }
+        return PACK_OK;
+    } catch (const dp::HipError& e) {
+        c->pin_off = 0;
+        return fail_hip(c, e);
+    }
+}
+
+int pack_test_option(pack_ctx* c, uint32_t what, uint32_t value) {
+    if (!c) return PACK_E_INVAL;
+    c->err.clear();
+    uint32_t bit = 0;
+    switch (what) {
+        case PACK_TEST_WAIT_GIVE_UP: bit = dp::TEST_WAIT_GIVE_UP; break;
+        case PACK_TEST_CYCLE_FAULT: bit = dp::TEST_CYCLE_FAULT; break;
+        default: c->err = "unknown test option"; return PACK_E_INVAL;
+    }
+    if (value) c->p.test_opts |= bit;
+    else c->p.test_opts &= ~bit;
+    return PACK_OK;
 }
 
 int pack_batch(pack_ctx* c, uint32_t step, uint32_t n_steps, const pack_out* out) {
     if (!c) return PACK_E_INVAL;
     c->err.clear();
-    if (c->cycle < (int64_t)c->cfg.first_cycle) {
-        c->err = "no cycle planned";
+    if (!c->ready) {
+        c->err = "no cycle planned (or the last pack_cycle failed)";
         return PACK_E_STATE;
     }
     if (n_steps == 0 || (uint64_t)step + n_steps > c->U) {
@@ -1049,7 +1120,7 @@ int pack_batch(pack_ctx* c, uint32_t step, uint32_t n_steps, const pack_out* out
             c->err = "too many windows in one call";
             return PACK_E_RANGE;
         }
-        if (a.digests && dp::emit_sha_fits(a)) {  // emission beside the digests, one kernel
+        if (a.digests) {  // emission beside the digests, one kernel
             c->timer.begin(PACK_PHASE_DIGEST, c->st);
             dp::launch_emit_sha(c->p, a, c->st);
             c->timer.end(c->st);
@@ -1057,11 +1128,6 @@ int pack_batch(pack_ctx* c, uint32_t step, uint32_t n_steps, const pack_out* out
             c->timer.begin(PACK_PHASE_EMIT, c->st);
             dp::launch_emit(c->p, a, c->st);
             c->timer.end(c->st);
-            if (a.digests) {
-                c->timer.begin(PACK_PHASE_DIGEST, c->st);
-                dp::launch_window_sha(c->p, a, c->st);
-                c->timer.end(c->st);
-            }
         }
         if (a.learned) {
             c->timer.begin(PACK_PHASE_LEARNED, c->st);
@@ -1077,8 +1143,8 @@ int pack_batch(pack_ctx* c, uint32_t step, uint32_t n_steps, const pack_out* out
 int pack_batch_packed(pack_ctx* c, uint32_t step, uint32_t n_steps, const pack_out_packed* out) {
     if (!c) return PACK_E_INVAL;
     c->err.clear();
-    if (c->cycle < (int64_t)c->cfg.first_cycle) {
-        c->err = "no cycle planned";
+    if (!c->ready) {
+        c->err = "no cycle planned (or the last pack_cycle failed)";
         return PACK_E_STATE;
     }
     if (n_steps == 0 || (uint64_t)step + n_steps > c->U) {
@@ -1164,8 +1230,8 @@ int pack_fingerprint_steps(pack_ctx* c, uint32_t step, uint32_t n_steps, const u
         c->err = "digests must be 4-byte aligned";
         return PACK_E_INVAL;
     }
-    if (c->cycle < (int64_t)c->cfg.first_cycle) {
-        c->err = "no cycle planned";
+    if (!c->ready) {
+        c->err = "no cycle planned (or the last pack_cycle failed)";
         return PACK_E_STATE;
     }
     if ((uint64_t)step + n_steps > c->U) {
@@ -1211,15 +1277,15 @@ int pack_inspect(const pack_ctx* cc, uint32_t what, void* host_dst, uint64_t cap
         case PACK_INSPECT_SLOT_K: src = p.slot_k; count = p.B; width = out_width = 4; break;
         case PACK_INSPECT_COUNTS: count = 3; width = out_width = 8; break;
         case PACK_INSPECT_UPDATE_BATCH:
-            if (c->cycle < (int64_t)c->cfg.first_cycle) {
-                c->err = "no cycle planned";
+            if (!c->ready) {
+                c->err = "no cycle planned (or the last pack_cycle failed)";
                 return PACK_E_STATE;
             }
             count = c->U;
             width = out_width = 4;
             break;
         case PACK_INSPECT_CUM_TAKEN:
-            if (!p.tabled || c->cycle < (int64_t)c->cfg.first_cycle) {
+            if (!p.tabled || !c->ready) {
                 c->err = "no per-update schedule: neither PACK_FLAG_CUMULATIVE nor a ramp, or no cycle yet";
                 return PACK_E_STATE;
             }

@@ -9,9 +9,13 @@ namespace dp {
 
 constexpr int WAVE = 64;
 constexpr uint32_t END = 0xFFFFFFFFu;  // "past the end of the source" in jump tables
-// error bit set by a kernel that finds the plan inconsistent (a library bug):
-// the access is skipped and pack_init reports the failure instead
+// error bit set by a kernel that finds the plan inconsistent (a library bug)
+// or whose bounded wait gives up: the access is skipped and the calling
+// function (pack_init, pack_cycle) or pack_status reports PACK_E_INTERNAL
 constexpr uint32_t ERR_INTERNAL = 0x100u;
+// test options (the PACK_TEST_* values of dpack.h)
+constexpr uint32_t TEST_WAIT_GIVE_UP = 1u;
+constexpr uint32_t TEST_CYCLE_FAULT = 2u;
 
 // ---------------------------------------------------------------- errors
 struct HipError {
@@ -117,7 +121,9 @@ struct Plan {
     uint8_t* keep;                // [D]
     uint32_t* kept_pos;           // [D+1] exclusive scan of keep
     uint64_t* stats;              // [4][S] kept docs, kept tokens, held docs, held tokens
-    uint32_t* err;                // [1] validation error flags
+    uint32_t* err;                // [1] validation and plan/cycle error flags (cleared by each synchronous call)
+    uint32_t* err_batch;          // [1] error flags of the asynchronous batch kernels (cleared by pack_status)
+    uint32_t test_opts;           // test options (PACK_TEST_*): 0 in normal use
 
     // A3 sort
     uint64_t* key[2];             // [D]
@@ -340,9 +346,7 @@ __device__ inline uint32_t out_per(const Plan& p, const EmitArgs& a, uint32_t i)
 void launch_emit(const Plan& p, const EmitArgs& a, hipStream_t st);
 void launch_emit_packed(const Plan& p, const EmitArgs& a, hipStream_t st);  // padding-free rows
 void launch_learned(const Plan& p, const EmitArgs& a, hipStream_t st);
-void launch_window_sha(const Plan& p, const EmitArgs& a, hipStream_t st);
-bool emit_sha_fits(const EmitArgs& a);                 // launch_emit_sha applies (one workgroup per CU)
-void launch_emit_sha(const Plan& p, const EmitArgs& a, hipStream_t st);
+void launch_emit_sha(const Plan& p, const EmitArgs& a, hipStream_t st);  // emission and window digests
 void launch_batch_fp(const uint8_t* digests, uint32_t B, uint32_t n_batches, uint8_t* out, hipStream_t st);
 // batches of B_b digests: batch b covers digests [slot0[step+b] − slot0[step], slot0[step+b+1] − slot0[step])
 void launch_batch_fp_var(const uint8_t* digests, const uint64_t* slot0, uint32_t step, uint32_t n_batches,

@@ -719,6 +719,8 @@ __global__ __launch_bounds__(256) void k_checks(Plan p) {
 }
 
 __global__ __launch_bounds__(256) void k_cycle_sums(Plan p, uint64_t total) {
+    // test option: report an internal failure of the cycle (pack_cycle must fail)
+    if ((p.test_opts & TEST_CYCLE_FAULT) && blockIdx.x == 0 && threadIdx.x == 0) atomicOr(p.err, ERR_INTERNAL);
     uint64_t real = 0, learn = 0;
     for (uint64_t idx = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
          idx += (uint64_t)gridDim.x * blockDim.x) {

@@ -91,42 +91,45 @@ __device__ __forceinline__ void load_chunk(u32x4 (&stage)[SLOADS], const EmitArg
     }
 }
 
-// Placement: each wave hashes 64 windows and is pure VALU work, so a SIMD
-// that holds two of them takes twice as long, and with fewer waves than SIMDs
-// the kernel's time is that of the most loaded SIMD.  A workgroup is four
-// independent waves (one per SIMD of its CU); the SPREAD variant reserves
-// 96 KB of LDS (16 KB used per wave, the rest unused), more than half of a
-// CU's 160 KB, so no CU holds two workgroups and no SIMD two waves.  Launches
-// with more waves than SIMDs use the 64 KB variant instead.
-constexpr uint32_t SWAVES = 4;  // waves per workgroup
+// Placement: each hashing wave digests 64 windows and is pure VALU work, so a
+// SIMD that holds two of them takes twice as long.  The emission-and-digest
+// kernel below therefore gives each SIMD of a CU exactly one hashing wave:
+// its workgroups reserve 96 KB of LDS (16 KB used per hashing wave, the rest
+// unused), more than half of a CU's 160 KB, so no CU holds two workgroups.
 
 // Waits until the emitting wave of the same workgroup has published at least
 // `need` record blocks of its 64 windows (workgroup-scope acquire).  The
 // emitting wave never waits on anything, so the wait ends; the spin limit is
-// a safety net only (the digests are then wrong and err is flagged).
-__device__ __forceinline__ void wait_progress(const uint32_t* prog, uint32_t need, uint32_t* err) {
+// a safety net only: the wave then flags ERR_INTERNAL in err (the batch error
+// word that pack_status reports) and goes on, so every wave still exits and
+// the kernel completes.  With the test option TEST_WAIT_GIVE_UP the wait asks
+// for a count no wave publishes and gives up after one poll.
+__device__ __forceinline__ void wait_progress(const uint32_t* prog, uint32_t need, uint32_t* err, uint32_t opts) {
+    const bool give_up = (opts & TEST_WAIT_GIVE_UP) != 0;
+    const uint32_t target = give_up ? 0xFFFFFFFFu : need;
+    const uint32_t limit = give_up ? 1u : (1u << 24);
     uint32_t spins = 0;
-    while (__hip_atomic_load(prog, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < need) {
-        __builtin_amdgcn_s_sleep(2);
-        if (++spins == (1u << 24)) {
+    while (__hip_atomic_load(prog, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < target) {
+        if (++spins >= limit) {
             atomicOr(err, ERR_INTERNAL);
             break;
         }
+        __builtin_amdgcn_s_sleep(2);
     }
 }
 
 // Hashes windows w0 .. w0+63 of the outputs (one lane per window), reading
 // each 256-byte chunk cooperatively and transposing it through this wave's
-// 16 KB of LDS.  With prog set, chunk c is read only once the emitting wave
-// has published its blocks.
-template <bool WAIT>
+// 16 KB of LDS.  Chunk c is read only once the emitting wave has published
+// its blocks in prog.
 __device__ __forceinline__ void hash_outputs(uint32_t T, const EmitArgs& a, uint64_t n_windows, uint64_t w0,
-                                             uint32_t lane, u32x4* lds, const uint32_t* prog, uint32_t* err) {
+                                             uint32_t lane, u32x4* lds, const uint32_t* prog, uint32_t* err,
+                                             uint32_t opts) {
     const uint32_t nblk = 13 * (T / 64);   // blocks in the record
     const uint32_t nch = (nblk + SCH - 1) / SCH;
     const uint32_t my_piece = lane % SPIECES, my_grp = lane / SPIECES;
     u32x4 stage[SLOADS];
-    if (WAIT) wait_progress(prog, SCH < nblk ? SCH : nblk, err);
+    wait_progress(prog, SCH < nblk ? SCH : nblk, err, opts);
     load_chunk(stage, a, T, w0, n_windows, 0, my_grp, my_piece);
     uint32_t H[8];
     sha256_init(H);
@@ -143,7 +146,7 @@ __device__ __forceinline__ void hash_outputs(uint32_t T, const EmitArgs& a, uint
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        if (WAIT && c + 1 < nch) wait_progress(prog, (c + 2) * SCH < nblk ? (c + 2) * SCH : nblk, err);
+        if (c + 1 < nch) wait_progress(prog, (c + 2) * SCH < nblk ? (c + 2) * SCH : nblk, err, opts);
         // the last iteration reloads its own chunk (harmless) so the loop has no branch around the loads
         load_chunk(stage, a, T, w0, n_windows, c + 1 < nch ? c + 1 : c, my_grp, my_piece);
         const uint32_t nb = (c + 1) * SCH <= nblk ? SCH : nblk - c * SCH;
@@ -173,25 +176,18 @@ __device__ __forceinline__ void hash_outputs(uint32_t T, const EmitArgs& a, uint
     if (w0 + lane < n_windows) store_digest(H, a.digests + 32 * (w0 + lane));
 }
 
-template <bool SPREAD>
-__global__ __launch_bounds__(64 * SWAVES) void k_window_sha(uint32_t T, EmitArgs a, uint64_t n_windows) {
-    __shared__ u32x4 lds_all[(SPREAD ? 6 : 4) * 64 * SPIECES];  // 96 KB or 64 KB
-    const uint32_t wave = threadIdx.x / 64, lane = threadIdx.x % 64;
-    const uint64_t w0 = ((uint64_t)blockIdx.x * SWAVES + wave) * 64;
-    if (w0 >= n_windows) return;  // whole wave past the end
-    hash_outputs<false>(T, a, n_windows, w0, lane, lds_all + wave * 64 * SPIECES, nullptr, nullptr);
-}
-
 // ---------------------------------------------------------------- emission beside the digest
-// With digests requested and at most one hashing wave per SIMD, pack_batch
-// runs one kernel whose workgroups pair four emitting waves with four hashing
-// waves (one per SIMD).  Emitting wave e writes the record of its 64 windows
-// (one lane per window) block by block in record order and publishes, in LDS,
-// how many blocks are complete; hashing wave e hashes the same windows from
-// the outputs exactly as k_window_sha does, reading a chunk only once it is
-// published.  Emission is memory traffic and a little integer work, so it
-// hides under the hashing waves' SHA-256 chains, the step's longest serial
-// dependency, instead of running as a kernel of its own before them.
+// With digests requested, pack_batch runs one kernel whose workgroups pair
+// four emitting waves with four hashing waves (one of each per SIMD).
+// Emitting wave e writes the record of its 64 windows (one lane per window)
+// block by block in record order and publishes, in LDS, how many blocks are
+// complete; hashing wave e digests the same windows from the outputs
+// (hash_outputs), reading a chunk only once it is published.  Emission is
+// memory traffic and a little integer work, so it hides under the hashing
+// waves' SHA-256 chains, the step's longest serial dependency, instead of
+// running as a kernel of its own before them.  A launch of more than 256
+// workgroups (65,536 windows) runs them one CU-load after another: each
+// workgroup's waves finish together, and the next one takes the CU.
 //
 // Piece view (plan array pc_emit, written with the window offsets): position
 // t of piece q holds token base_q + t, position id t − f_q, document id d_q,
@@ -458,7 +454,8 @@ __global__ __launch_bounds__(64 * FWAVES) void k_emit_sha(Plan p, EmitArgs a, ui
     const uint32_t e = wave & 3;
     const uint64_t w0 = ((uint64_t)blockIdx.x * 4 + e) * 64;
     if (w0 >= n_windows) return;
-    if (wave < 4) hash_outputs<true>(p.T, a, n_windows, w0, lane, lds_all + e * 64 * SPIECES, prog + e, p.err);
+    if (wave < 4)
+        hash_outputs(p.T, a, n_windows, w0, lane, lds_all + e * 64 * SPIECES, prog + e, p.err_batch, p.test_opts);
     else emit_lanes(p, a, n_windows, w0, lane, prog + e);
 }
 
@@ -548,25 +545,9 @@ __global__ __launch_bounds__(64) void k_sha_chunks(const uint8_t* msg, uint64_t 
 
 }  // namespace
 
-void launch_window_sha(const Plan& p, const EmitArgs& a, hipStream_t st) {
-    const uint64_t n = a.n_out;
-    const uint64_t waves = (n + 63) / 64;
-    const uint32_t groups = (uint32_t)((waves + SWAVES - 1) / SWAVES);
-    if (waves <= 1024)  // no more waves than MI355X SIMDs (256 CUs x 4): one per SIMD
-        hipLaunchKernelGGL(k_window_sha<true>, dim3(groups), dim3(64 * SWAVES), 0, st, p.T, a, n);
-    else
-        hipLaunchKernelGGL(k_window_sha<false>, dim3(groups), dim3(64 * SWAVES), 0, st, p.T, a, n);
-    DP_HIP(hipGetLastError());
-}
-
-bool emit_sha_fits(const EmitArgs& a) {
-    const uint64_t n = a.n_out;
-    return (n + 255) / 256 <= 256;  // one workgroup (four hashing waves) per CU of MI355X's 256
-}
-
 void launch_emit_sha(const Plan& p, const EmitArgs& a, hipStream_t st) {
-    const uint64_t n = a.n_out;
-    hipLaunchKernelGGL(k_emit_sha, dim3((uint32_t)((n + 255) / 256)), dim3(64 * FWAVES), 0, st, p, a, n);
+    const uint64_t n = a.n_out;  // < 2^31 windows: at most 2^23 workgroups
+    if (n) hipLaunchKernelGGL(k_emit_sha, dim3((uint32_t)((n + 255) / 256)), dim3(64 * FWAVES), 0, st, p, a, n);
     DP_HIP(hipGetLastError());
 }
 

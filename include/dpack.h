@@ -54,6 +54,8 @@ enum {
     PACK_E_EXHAUSTED = -5, /* a source cannot supply the cycle's windows */
     PACK_E_STATE = -6,     /* calls out of order (cycle skipped, batch before cycle) */
     PACK_E_RANGE = -7,     /* step range beyond the current cycle */
+    PACK_E_INTERNAL = -8,  /* a kernel found the plan inconsistent or a bounded wait gave up (a
+                              library bug): the call's results are not valid */
 };
 
 typedef struct pack_ctx pack_ctx;
@@ -117,8 +119,8 @@ enum {
     PACK_PHASE_CYCLE,        /* cycle sums and plan digest */
     PACK_PHASE_EMIT,         /* emission kernel of pack_batch (when not timed under DIGEST) */
     PACK_PHASE_LEARNED,      /* per-update learned counts of pack_batch */
-    PACK_PHASE_DIGEST,       /* per-window SHA-256 of pack_batch; with at most 65536 windows
-                              * in the call, emission runs inside the same kernel and is timed here */
+    PACK_PHASE_DIGEST,       /* per-window SHA-256 of pack_batch with digests; the emission runs
+                              * inside the same kernel and is timed here */
     PACK_PHASE_FINGERPRINT,  /* pack_fingerprint */
     PACK_N_PHASES
 };
@@ -221,12 +223,17 @@ typedef struct pack_config {
 /* pack_init — build the plan of a corpus (hash and hold-out of every
  * document, grouping, shuffle keys and sort, strata merge, pieces, next-fit
  * windows, per-update apportionment and slot table) on cfg->stream.
+ * NeuronSpark-Trainer README, Concepts: documents held out by a hash of their
+ * text (the same in every line, each source at its own rate), shuffled, each
+ * source's strata at their share of its tokens, windows cut at document
+ * ends; Zephon blog post, TorchTitan integration: configuration errors such
+ * as a rank count that does not divide the batch fail at start.
  * Synchronous: returns once the plan is on the device; reads back only the
  * per-source window counts and statistics.  The plan is independent of rank
  * and world, which only select the emitted slice.
  * Errors: PACK_E_ABI, PACK_E_INVAL (limits above, checked on the host and,
- * for device arrays, by a validation kernel), PACK_E_NOMEM, PACK_E_HIP.
- * On error *out is NULL and nothing is leaked. */
+ * for device arrays, by a validation kernel), PACK_E_NOMEM, PACK_E_HIP,
+ * PACK_E_INTERNAL.  On error *out is NULL and nothing is leaked. */
 int pack_init(const pack_config *cfg, pack_ctx **out);
 
 /* Per-cycle information, filled by pack_cycle.  The per-source arrays are
@@ -250,15 +257,20 @@ typedef struct pack_cycle_info {
                                     * context that goes on after this cycle */
 } pack_cycle_info;
 
-/* pack_cycle — plan cycle `cycle` (must be 0, then 1, 2, …): U updates, each
- * of B windows of which n_s come from source s, taking the next U·n_s windows
- * of each source's stream.  U = updates_per_cycle, or when that is 0 the most
- * every source with n_s > 0 supports.  With PACK_FLAG_CUMULATIVE update u
- * takes A_s(u+1) − A_s(u) windows of source s (see the flag) and the cycle
- * A_s(U).  Synchronous.  info may be NULL.
+/* pack_cycle — plan cycle `cycle` (must be first_cycle, then the next, …):
+ * U updates, each of B windows of which n_s come from source s, taking the
+ * next U·n_s windows of each source's stream.  U = updates_per_cycle, or
+ * when that is 0 the most every source with n_s > 0 supports.  With
+ * PACK_FLAG_CUMULATIVE update u takes A_s(u+1) − A_s(u) windows of source s
+ * (see the flag) and the cycle A_s(U).  NeuronSpark-Trainer README, Concepts
+ * and Training: a data line is consumed in cycles, updates never span a
+ * cycle end, every token is trained once and running out is an error.
+ * Synchronous.  info may be NULL.
  * Errors: PACK_E_STATE (out of order), PACK_E_EXHAUSTED (some source cannot
  * supply its windows of the cycle, or U would be 0: an error, never a second
- * pass; the cycle state is unchanged), PACK_E_HIP. */
+ * pass), PACK_E_INTERNAL, PACK_E_HIP.  On any error no cycle is current
+ * afterwards (pack_batch and the cycle's inspections return PACK_E_STATE)
+ * and the same cycle number is the one to plan next. */
 int pack_cycle(pack_ctx *ctx, uint32_t cycle, pack_cycle_info *info);
 
 /* Outputs of pack_batch: device buffers owned by the caller, each laid out
@@ -276,8 +288,13 @@ typedef struct pack_out {
 } pack_out;
 
 /* pack_batch — emit updates [step, step+n_steps) of the current cycle for
- * this context's rank.  Asynchronous on cfg->stream; a pure function of
- * (corpus, config, cycle, step), so re-emitting a step reproduces it exactly.
+ * this context's rank.  Linnet "Training", Supervised fine-tuning: rows of
+ * exactly T positions with the rest padded, loss on completions only, each
+ * update weighed by its learned positions; Zephon blog post, resume section:
+ * every global batch byte-identical (and its SHA-256 equal) at any rank count.
+ * Asynchronous on cfg->stream; a pure function of (corpus, config, cycle,
+ * step), so re-emitting a step reproduces it exactly.  A failure inside its
+ * kernels (PACK_E_INTERNAL) is reported by the next pack_status.
  * Errors: PACK_E_STATE (no cycle planned), PACK_E_RANGE (step + n_steps > U
  * or n_steps = 0), PACK_E_INVAL (a NULL output array), PACK_E_HIP. */
 int pack_batch(pack_ctx *ctx, uint32_t step, uint32_t n_steps, const pack_out *out);
@@ -359,6 +376,27 @@ enum {
  * PACK_E_RANGE (capacity too small), PACK_E_HIP. */
 int pack_inspect(const pack_ctx *ctx, uint32_t what, void *host_dst, uint64_t capacity_bytes,
                  uint64_t *needed);
+
+/* pack_status — synchronize the context's stream and report whether a
+ * kernel of an asynchronous call made since the last pack_status (the window
+ * digests of pack_batch wait, boundedly, for the emission beside them)
+ * flagged an internal failure; if so, the outputs of those calls are not
+ * valid, and the flag is cleared.  Returns PACK_OK, PACK_E_INTERNAL (message
+ * in pack_last_error), PACK_E_INVAL (NULL) or PACK_E_HIP. */
+int pack_status(pack_ctx *ctx);
+
+/* Test options for pack_test_option.  They exist so that the error paths
+ * above can be exercised on a GPU with every kernel still running to its
+ * end; with every option 0 (the default) no output byte changes. */
+enum {
+    PACK_TEST_WAIT_GIVE_UP = 1, /* the digest waves' bounded waits give up after one poll:
+                                   the batch's digests are invalid, pack_status reports it */
+    PACK_TEST_CYCLE_FAULT = 2,  /* a cycle kernel reports an internal failure: pack_cycle fails */
+};
+
+/* pack_test_option — set test option `what` on (value != 0) or off for the
+ * calls that follow.  Errors: PACK_E_INVAL (NULL ctx, unknown option). */
+int pack_test_option(pack_ctx *ctx, uint32_t what, uint32_t value);
 
 /* pack_get_timings — synchronize the context's stream and return the phase
  * times recorded since the last reset (all zero unless the context was made

@@ -10,16 +10,33 @@ from synth.corpus import random_small
 def combo_corpus(seed, even=False):
     """(corpus, description): the modes drawn from the seed; with stream starts,
     the corpus goes on from the oracle's cycle 0 (first cycle 1).  even: every
-    update's batch a multiple of 2·lanes (two ranks can split it)."""
-    r = np.random.default_rng(np.random.SeedSequence([4242, seed]))
-    L = int(r.choice([1, 1, 2, 3]))
+    update's batch a multiple of 2·lanes and an even lane count (two ranks can
+    split it), and a combination that runs out of data before its first cycle
+    is drawn again (from the seed and the attempt), so every seed has batches."""
+    if not even:
+        return _draw(seed, seed, [4242, seed], False)
+    for attempt in range(32):
+        c, desc = _draw(seed + 10000 * attempt, seed, [4242, seed] + ([attempt] if attempt else []), True)
+        try:
+            oracle.Plan(c).cycle(int(c.first_cycle))
+        except oracle.OracleError:
+            continue
+        if attempt:
+            desc["redrawn"] = attempt
+        return c, desc
+    raise RuntimeError(f"no combination with batches for seed {seed}")
+
+
+def _draw(corpus_seed, seed, seq, even):
+    r = np.random.default_rng(np.random.SeedSequence(seq))
+    L = int(r.choice([1, 1, 2, 4] if even else [1, 1, 2, 3]))
     ramp = r.random() < 0.3
     heldout = r.random() < 0.2
     T = 64 * int(r.choice([1, 2]))
     m = 2 * L if even else L
     b = [m * int(x) for x in r.integers(1, 4, size=2)]
     B = max(b) if ramp else m * int(r.integers(1, 4))
-    c = random_small(seed, n_docs=int(r.integers(400, 1400)), n_sources=int(r.integers(1, 5)),
+    c = random_small(corpus_seed, n_docs=int(r.integers(400, 1400)), n_sources=int(r.integers(1, 5)),
                      max_strata=int(r.integers(1, 4)), T=T, B=B, max_len=int(r.integers(40, 400)),
                      prompts=bool(r.random() < 0.5), bp_max=6000 if heldout else 1500)
     mode = dict(wrap=bool(r.random() < 0.4), read_random=bool(r.random() < 0.4),

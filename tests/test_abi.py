@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_strerror_covers_every_code(lib):
-    for code in range(-7, 1):
+    for code in range(-8, 1):
         assert dp.pack_strerror(code) not in ("", "unknown error")
     assert dp.pack_strerror(-99) == "unknown error"
 
@@ -151,4 +151,6 @@ def test_null_arguments_are_errors(lib):
     assert lib.pack_batch(None, 0, 1, None) == dp.PACK_E_INVAL
     assert lib.pack_batch_packed(None, 0, 1, None) == dp.PACK_E_INVAL
     assert lib.pack_fingerprint_steps(None, 0, 1, None, None) == dp.PACK_E_INVAL
+    assert lib.pack_status(None) == dp.PACK_E_INVAL
+    assert lib.pack_test_option(None, dp.PACK_TEST_WAIT_GIVE_UP, 1) == dp.PACK_E_INVAL
     lib.pack_destroy(None)
