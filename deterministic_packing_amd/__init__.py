@@ -17,7 +17,7 @@ from typing import Optional
 import numpy as np
 
 __all__ = [
-    "DpackError", "load_library", "pack_init", "pack_cycle", "pack_batch", "pack_batch_packed", "pack_fingerprint",
+    "DpackError", "load_library", "pack_init", "pack_init_noalloc", "pack_cycle", "pack_batch", "pack_batch_packed", "pack_fingerprint",
     "pack_fingerprint_steps", "pack_inspect", "pack_get_timings", "pack_status", "pack_test_option", "pack_destroy",
     "pack_strerror", "Packer", "INSPECT", "SYMBOLS",
 ]
@@ -30,7 +30,7 @@ PACK_OK, PACK_E_ABI, PACK_E_INVAL, PACK_E_NOMEM, PACK_E_HIP = 0, -1, -2, -3, -4
 PACK_E_EXHAUSTED, PACK_E_STATE, PACK_E_RANGE, PACK_E_INTERNAL = -5, -6, -7, -8
 PACK_TEST_WAIT_GIVE_UP, PACK_TEST_CYCLE_FAULT = 1, 2
 
-SYMBOLS = ("pack_init", "pack_cycle", "pack_batch", "pack_batch_packed", "pack_fingerprint",
+SYMBOLS = ("pack_init", "pack_init_noalloc", "pack_cycle", "pack_batch", "pack_batch_packed", "pack_fingerprint",
            "pack_fingerprint_steps", "pack_inspect", "pack_get_timings", "pack_status", "pack_test_option",
            "pack_destroy", "pack_strerror", "pack_last_error")
 
@@ -120,6 +120,8 @@ def load_library(path: Optional[str] = None):
     vp, i32, u32 = C.c_void_p, C.c_int, C.c_uint32
     lib.pack_init.restype = i32
     lib.pack_init.argtypes = [C.POINTER(PackConfig), C.POINTER(vp)]
+    lib.pack_init_noalloc.restype = i32
+    lib.pack_init_noalloc.argtypes = [C.POINTER(PackConfig), C.POINTER(vp)]
     lib.pack_cycle.restype = i32
     lib.pack_cycle.argtypes = [vp, u32, C.POINTER(PackCycleInfo)]
     lib.pack_batch.restype = i32
@@ -169,6 +171,12 @@ def _check(rc: int, call: str, ctx=None):
 def pack_init(cfg: PackConfig) -> int:
     ctx = C.c_void_p()
     _check(load_library().pack_init(C.byref(cfg), C.byref(ctx)), "pack_init")
+    return ctx.value
+
+
+def pack_init_noalloc(cfg: PackConfig) -> int:
+    ctx = C.c_void_p()
+    _check(load_library().pack_init_noalloc(C.byref(cfg), C.byref(ctx)), "pack_init_noalloc")
     return ctx.value
 
 
@@ -237,7 +245,8 @@ class Packer:
     (or pass ``device_tensors`` to reuse resident ones)."""
 
     def __init__(self, corpus, rank: int = 0, world: int = 1, device: str = "cuda",
-                 device_tensors: Optional[dict] = None, stream=None, timing: bool = False):
+                 device_tensors: Optional[dict] = None, stream=None, timing: bool = False,
+                 noalloc: bool = False):
         import torch
 
         self.torch = torch
@@ -284,7 +293,7 @@ class Packer:
             int(getattr(corpus, "first_cycle", 0)), int(getattr(corpus, "tokens_start", 0)),
             d["segment"].data_ptr() if d.get("segment") is not None else None,
             int(getattr(corpus, "n_segments", 1) or 1))
-        self.ctx = pack_init(self.cfg)
+        self.ctx = pack_init_noalloc(self.cfg) if noalloc else pack_init(self.cfg)
         self.per = corpus.B // world
         self.batches = None  # windows of each update of the current cycle (all ranks)
 

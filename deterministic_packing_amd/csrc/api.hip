@@ -10,6 +10,11 @@
 #include "dp_common.h"
 #include "dpack.h"
 
+// The device workspace of pack_init_noalloc (see NoallocSlot below).  Host code
+// never passes this name to a kernel or a copy: it uses the address that
+// hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) uint8_t scratch[64ull << 20];
+
 namespace {
 
 constexpr size_t ALIGN = 256;
@@ -60,6 +65,26 @@ void arena_give(int dev, void* ptr, size_t bytes, bool pinned = false) {
         cache_free(c, ptr);
     }
 }
+
+// Memory of pack_init_noalloc, for callers that cannot allocate.  The device
+// workspace of such a context is carved from `scratch`, a file-scope device
+// array that each GPU holds from the library's first use on it until the
+// process ends; its pinned-staging role is taken by a static host buffer per
+// device.  One such context may be alive per device at a time (a slot's
+// in_use flag, under a mutex); its workspace keeps the previous context's
+// bytes, and the plan clears what must start at zero exactly as it does in a
+// workspace reused from the arena cache.
+constexpr size_t NOALLOC_DEVICE_BYTES = 64ull << 20;  // 64 MiB per device
+constexpr size_t NOALLOC_HOST_BYTES = 1ull << 20;     // 1 MiB of host staging per device
+constexpr int NOALLOC_MAX_DEVICES = 16;
+
+struct NoallocSlot {
+    void* dev = nullptr;  // the device address of `scratch` on this device (hipGetSymbolAddress)
+    bool in_use = false;
+    alignas(256) uint8_t host[NOALLOC_HOST_BYTES];
+};
+std::mutex g_noalloc_mu;
+NoallocSlot g_noalloc[NOALLOC_MAX_DEVICES];
 
 thread_local std::string g_init_error;
 
@@ -156,6 +181,7 @@ struct pack_ctx {
     dp::Plan p{};
     char* arena = nullptr;
     size_t arena_bytes = 0;
+    bool noalloc = false;  // arena and staging are the device's static scratch and host buffer
     uint32_t* nstart = nullptr;
     uint32_t* hash_first = nullptr;  // tile -> first document table of the hash
     uint8_t* dig_buf = nullptr;
@@ -436,8 +462,13 @@ int fail_hip(pack_ctx* c, const dp::HipError& e) {
 void release(pack_ctx* c) {
     if (!c) return;
     if (c->arena || c->pin) (void)hipStreamSynchronize(c->st);
-    if (c->arena) arena_give(c->device, c->arena, c->arena_bytes);
-    if (c->pin) arena_give(c->device, c->pin, c->pin_bytes, true);
+    if (c->noalloc) {  // static memory: hand the device's slot back, never to the arena cache
+        std::lock_guard<std::mutex> lk(g_noalloc_mu);
+        g_noalloc[c->device].in_use = false;
+    } else {
+        if (c->arena) arena_give(c->device, c->arena, c->arena_bytes);
+        if (c->pin) arena_give(c->device, c->pin, c->pin_bytes, true);
+    }
     c->timer.destroy();
     delete c;
 }
@@ -590,28 +621,9 @@ void put(std::vector<uint8_t>& b, uint64_t v, int bytes) {
 
 }  // namespace
 
-extern "C" {
+namespace {
 
-const char* pack_strerror(int code) {
-    switch (code) {
-        case PACK_OK: return "ok";
-        case PACK_E_ABI: return "ABI version mismatch";
-        case PACK_E_INVAL: return "invalid argument or corpus";
-        case PACK_E_NOMEM: return "out of memory";
-        case PACK_E_HIP: return "HIP runtime error";
-        case PACK_E_EXHAUSTED: return "a source cannot supply the cycle (data exhausted)";
-        case PACK_E_STATE: return "call out of order";
-        case PACK_E_RANGE: return "step range outside the current cycle";
-        case PACK_E_INTERNAL: return "internal failure inside a kernel (library bug); results not valid";
-        default: return "unknown error";
-    }
-}
-
-const char* pack_last_error(const pack_ctx* ctx) {
-    return ctx ? ctx->err.c_str() : g_init_error.c_str();
-}
-
-int pack_init(const pack_config* cfg, pack_ctx** out) {
+int init_context(const pack_config* cfg, pack_ctx** out, bool noalloc) {
     g_init_error.clear();
     if (!out) {
         g_init_error = "out is NULL";
@@ -625,6 +637,10 @@ int pack_init(const pack_config* cfg, pack_ctx** out) {
     if (cfg->abi_version != DPACK_ABI_VERSION) {
         g_init_error = "abi_version mismatch";
         return PACK_E_ABI;
+    }
+    if (noalloc && (cfg->flags & PACK_FLAG_TIMING)) {  // timing events would be created per context
+        g_init_error = "pack_init_noalloc does not take PACK_FLAG_TIMING";
+        return PACK_E_INVAL;
     }
     pack_ctx* c = nullptr;
     try {
@@ -663,7 +679,6 @@ int pack_init(const pack_config* cfg, pack_ctx** out) {
         }
         for (uint32_t r = 0; r < Sr; ++r) c->W += c->weight_real[r];
         c->gbase[(uint64_t)S * NSEG] = G;
-        DP_HIP(hipGetDevice(&c->device));
 
         dp::Plan& p = c->p;
         p.tokens = cfg->tokens;
@@ -696,33 +711,77 @@ int pack_init(const pack_config* cfg, pack_ctx** out) {
         if (p.cap_pieces >= 0xFFFFFFFFull) throw InvalError{"too many pieces for 32-bit piece indices"};
 
         const size_t bytes = carve(*c, nullptr);
-        size_t got = 0;
-        void* mem = arena_take(c->device, bytes, &got);
-        if (!mem) {
-            if (hipMalloc(&mem, bytes) != hipSuccess) {
-                (void)hipGetLastError();
-                g_init_error = "device workspace allocation failed (" + std::to_string(bytes) + " bytes)";
-                delete c;
-                return PACK_E_NOMEM;
-            }
-            got = bytes;
-        }
-        c->arena = static_cast<char*>(mem);
-        c->arena_bytes = got;
-        carve(*c, c->arena);
         const size_t pbytes = pin_bytes_for(S, cfg->n_ramp, c->p.n_seg);
-        void* pin = arena_take(c->device, pbytes, &got, true);
-        if (!pin) {
-            if (hipHostMalloc(&pin, pbytes, hipHostMallocDefault) != hipSuccess) {
-                (void)hipGetLastError();
-                g_init_error = "pinned host staging allocation failed";
-                release(c);
-                return PACK_E_NOMEM;
-            }
-            got = pbytes;
+        if (noalloc && (bytes > NOALLOC_DEVICE_BYTES || pbytes > NOALLOC_HOST_BYTES)) {
+            // the static workspace's limits, before any device work
+            g_init_error = "pack_init_noalloc: the plan needs " + std::to_string(bytes) +
+                           " bytes of device workspace and " + std::to_string(pbytes) +
+                           " bytes of staging; the static scratch holds " +
+                           std::to_string(NOALLOC_DEVICE_BYTES) + " and " + std::to_string(NOALLOC_HOST_BYTES);
+            delete c;
+            return PACK_E_INVAL;
         }
-        c->pin = static_cast<uint8_t*>(pin);
-        c->pin_bytes = got;
+        DP_HIP(hipGetDevice(&c->device));
+        if (noalloc) {
+            if (c->device < 0 || c->device >= NOALLOC_MAX_DEVICES) {
+                g_init_error = "pack_init_noalloc: device index beyond the static slots";
+                delete c;
+                return PACK_E_INVAL;
+            }
+            std::lock_guard<std::mutex> lk(g_noalloc_mu);
+            NoallocSlot& slot = g_noalloc[c->device];
+            if (slot.in_use) {
+                g_init_error = "pack_init_noalloc: a context made by it is still alive on this device";
+                delete c;
+                return PACK_E_STATE;
+            }
+            if (!slot.dev) {  // once per device, with that device current
+                void* ptr = nullptr;
+                const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+                if (e != hipSuccess || !ptr) {
+                    (void)hipGetLastError();
+                    g_init_error = std::string("pack_init_noalloc: hipGetSymbolAddress(scratch): ") +
+                                   hipGetErrorString(e);
+                    delete c;
+                    return PACK_E_HIP;
+                }
+                slot.dev = ptr;
+            }
+            slot.in_use = true;
+            c->noalloc = true;
+            c->arena = static_cast<char*>(slot.dev);
+            c->arena_bytes = NOALLOC_DEVICE_BYTES;
+            c->pin = slot.host;
+            c->pin_bytes = NOALLOC_HOST_BYTES;
+            carve(*c, c->arena);
+        } else {
+            size_t got = 0;
+            void* mem = arena_take(c->device, bytes, &got);
+            if (!mem) {
+                if (hipMalloc(&mem, bytes) != hipSuccess) {
+                    (void)hipGetLastError();
+                    g_init_error = "device workspace allocation failed (" + std::to_string(bytes) + " bytes)";
+                    delete c;
+                    return PACK_E_NOMEM;
+                }
+                got = bytes;
+            }
+            c->arena = static_cast<char*>(mem);
+            c->arena_bytes = got;
+            carve(*c, c->arena);
+            void* pin = arena_take(c->device, pbytes, &got, true);
+            if (!pin) {
+                if (hipHostMalloc(&pin, pbytes, hipHostMallocDefault) != hipSuccess) {
+                    (void)hipGetLastError();
+                    g_init_error = "pinned host staging allocation failed";
+                    release(c);
+                    return PACK_E_NOMEM;
+                }
+                got = pbytes;
+            }
+            c->pin = static_cast<uint8_t*>(pin);
+            c->pin_bytes = got;
+        }
         build_plan(*c);
         c->cyc_start.assign(S, 0);
         c->cyc_next.assign(S, 0);
@@ -747,6 +806,33 @@ int pack_init(const pack_config* cfg, pack_ctx** out) {
         return PACK_E_NOMEM;
     }
 }
+
+}  // namespace
+
+extern "C" {
+
+const char* pack_strerror(int code) {
+    switch (code) {
+        case PACK_OK: return "ok";
+        case PACK_E_ABI: return "ABI version mismatch";
+        case PACK_E_INVAL: return "invalid argument or corpus";
+        case PACK_E_NOMEM: return "out of memory";
+        case PACK_E_HIP: return "HIP runtime error";
+        case PACK_E_EXHAUSTED: return "a source cannot supply the cycle (data exhausted)";
+        case PACK_E_STATE: return "call out of order";
+        case PACK_E_RANGE: return "step range outside the current cycle";
+        case PACK_E_INTERNAL: return "internal failure inside a kernel (library bug); results not valid";
+        default: return "unknown error";
+    }
+}
+
+const char* pack_last_error(const pack_ctx* ctx) {
+    return ctx ? ctx->err.c_str() : g_init_error.c_str();
+}
+
+int pack_init(const pack_config* cfg, pack_ctx** out) { return init_context(cfg, out, false); }
+
+int pack_init_noalloc(const pack_config* cfg, pack_ctx** out) { return init_context(cfg, out, true); }
 
 int pack_cycle(pack_ctx* c, uint32_t cycle, pack_cycle_info* info) {
     if (!c) return PACK_E_INVAL;

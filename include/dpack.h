@@ -236,6 +236,25 @@ typedef struct pack_config {
  * PACK_E_INTERNAL.  On error *out is NULL and nothing is leaked. */
 int pack_init(const pack_config *cfg, pack_ctx **out);
 
+/* pack_init_noalloc — pack_init for callers that cannot allocate memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same plan, byte for byte, built without hipMalloc, hipFree,
+ * hipHostMalloc or any other allocating HIP call.  The device workspace is a
+ * static array of 64 MiB that each GPU the library runs on holds until the
+ * process ends; the staging of host<->device copies is a static host buffer of
+ * 1 MiB per device (ordinary memory, so the plan's few small copies are
+ * pageable).  The context object itself is ordinary host memory.  Limits, on
+ * top of pack_init's: the plan's workspace must fit 64 MiB and its staging
+ * 1 MiB (PACK_E_INVAL with both sizes in pack_last_error otherwise, checked
+ * before any device work; roughly 250,000 documents of a few hundred tokens),
+ * no PACK_FLAG_TIMING (PACK_E_INVAL), at most 16 devices.  One context made by
+ * pack_init_noalloc may be alive per device at a time: while it is, another
+ * pack_init_noalloc on that device returns PACK_E_STATE (pack_destroy frees
+ * the slot).  The workspace keeps the previous context's bytes; the plan
+ * clears what must start at zero.  The returned context takes every other
+ * call as a pack_init context does.  Errors: as pack_init, and PACK_E_STATE. */
+int pack_init_noalloc(const pack_config *cfg, pack_ctx **out);
+
 /* Per-cycle information, filled by pack_cycle.  The per-source arrays are
  * optional host buffers of n_sources entries owned by the caller. */
 typedef struct pack_cycle_info {

@@ -154,3 +154,18 @@ def test_null_arguments_are_errors(lib):
     assert lib.pack_status(None) == dp.PACK_E_INVAL
     assert lib.pack_test_option(None, dp.PACK_TEST_WAIT_GIVE_UP, 1) == dp.PACK_E_INVAL
     lib.pack_destroy(None)
+
+
+def test_noalloc_limits_checked_before_device_work(lib):
+    """pack_init_noalloc: a plan whose workspace exceeds the static scratch, or
+    PACK_FLAG_TIMING, is refused on the host (no GPU call is made)."""
+    cfg, keep = _cfg(n_docs=1 << 22, n_tokens=1 << 32)  # ~4 M documents: hundreds of MB of workspace
+    ctx = C.c_void_p()
+    assert lib.pack_init_noalloc(C.byref(cfg), C.byref(ctx)) == dp.PACK_E_INVAL
+    msg = lib.pack_last_error(None).decode()
+    assert "static scratch holds 67108864" in msg, msg
+    assert ctx.value is None
+    cfg, keep = _cfg(flags=dp.PACK_FLAG_TIMING)
+    assert lib.pack_init_noalloc(C.byref(cfg), C.byref(ctx)) == dp.PACK_E_INVAL
+    assert "PACK_FLAG_TIMING" in lib.pack_last_error(None).decode()
+    assert lib.pack_init_noalloc(None, C.byref(ctx)) == dp.PACK_E_INVAL
