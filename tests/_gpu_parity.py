@@ -74,3 +74,20 @@ def compare_cycle(gi: dict, oi: "oracle.CycleInfo", op: "oracle.Plan"):
     assert gi["positions"] == oi.positions
     if getattr(oi, "stream_next", None) is not None:
         assert gi["stream_next_token"].tolist() == oi.stream_next.tolist()
+
+
+def oracle_digests(op: "oracle.Plan", steps, rank: int = 0, world: int = 1, threads: int = 0) -> np.ndarray:
+    """The oracle's window digests of the given updates, [len(steps), B/world, 32]
+    (updates of B windows each).  Each update is one call of the oracle's batch
+    function; the calls run on a thread pool (the C oracle keeps no shared
+    mutable state and ctypes releases the interpreter lock during a call)."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+    steps = list(steps)
+    n = threads or min(16, len(os.sched_getaffinity(0)))
+
+    def one(b):
+        return op.batch(b, 1, rank=rank, world=world, digests=True, learned=False)["digests"][0]
+
+    with ThreadPoolExecutor(max_workers=max(1, n)) as ex:
+        return np.stack(list(ex.map(one, steps))) if steps else np.zeros((0, 0, 32), np.uint8)

@@ -1,10 +1,12 @@
 """Parity at the workloads' full sizes, in the launch configuration bench.py
 times (every update of the cycle emitted by one pack_batch call with learned
 counts and digests).  The oracle computes the whole plan; outputs are compared
-on sampled windows (content and digests), whole sampled batches
-(fingerprints), every learned count, and checked on the GPU for properties that
-hold everywhere (padding at the end, position ids, masks agreeing with the
-learned counts)."""
+on every window's digest of the cycle (the SHA-256 of its whole record, so
+every output byte), sampled windows' contents, whole sampled batches
+(fingerprints) and every learned count, and checked on the GPU for properties
+that hold everywhere (padding at the end, position ids, masks agreeing with the
+learned counts).  The full-cycle workload is also re-derived at emulated rank
+counts 1/8/16/32/64, one fresh context per rank."""
 import numpy as np
 import pytest
 
@@ -12,7 +14,7 @@ import deterministic_packing_amd as dp
 import oracle
 from synth import make_corpus
 
-from _gpu_parity import compare_cycle, compare_plan, say
+from _gpu_parity import compare_cycle, compare_plan, oracle_digests, say
 
 pytestmark = pytest.mark.gpu
 
@@ -50,14 +52,14 @@ def _setup(name):
 
 # (workload, updates emitted per call: None = the whole cycle in one call, as the
 # bench does; else the first a and the last b updates of the cycle).  The full
-# workload's second call holds 67,584 windows, more than the one-kernel
-# emission-and-digest launch takes, so it covers the two-kernel path;
-# wrap-pretrain is the pre-train workload with wrap packing, heldout-pretrain
-# its held-out (validation) stream, random-pretrain with each cycle's windows
-# read in a random order, cum-pretrain with per-update counts from the cycle's
-# cumulative quotas, lanes-pretrain with 8 lanes, arrivals-pretrain with its
-# documents labelled with 8 arrivals.
-FULL = [("tiny", None), ("pretrain", None), ("sft", None), ("long", None), ("full", (24, 66)),
+# workload's call holds 581,632 windows (2,272 workgroups of the emission-and-
+# digest kernel, nine CU-loads); wrap-pretrain is the pre-train workload with
+# wrap packing, heldout-pretrain its held-out (validation) stream,
+# random-pretrain with each cycle's windows read in a random order,
+# cum-pretrain with per-update counts from the cycle's cumulative quotas,
+# lanes-pretrain with 8 lanes, arrivals-pretrain with its documents labelled
+# with 8 arrivals.
+FULL = [("tiny", None), ("pretrain", None), ("sft", None), ("long", None), ("full", None),
         ("wrap-pretrain", None), ("heldout-pretrain", None), ("random-pretrain", None), ("cum-pretrain", None),
         ("lanes-pretrain", None), ("arrivals-pretrain", None)]
 
@@ -83,6 +85,13 @@ def test_full_size_parity(name, cap):
     torch.cuda.synchronize()
     for s0, g in outs:
         cnt = g["tokens"].shape[0]
+        # every window digest of the call against the oracle's
+        say("oracle digests", name, cnt, "updates")
+        exp = oracle_digests(op, range(s0, s0 + cnt))
+        got = g["digests"].cpu().numpy()
+        if not np.array_equal(got, exp):
+            bad = np.argwhere((got != exp).any(axis=2))
+            raise AssertionError(f"{name}: {len(bad)} window digests differ, first (update, slot) {bad[:3].tolist()}")
         # learned counts of every update in the call
         learned = g["learned"].cpu().numpy()
         for i in range(cnt):
@@ -94,7 +103,8 @@ def test_full_size_parity(name, cap):
         n_real = real.sum(dim=2)
         idx = torch.arange(T, device=doc.device).view(1, 1, T)
         assert bool((real == (idx < n_real.unsqueeze(2))).all()), "padding only at the end of a window"
-        assert bool((g["pos"][~real] == 0).all()) and bool((g["mask"][~real] == 0).all())
+        # (no boolean-mask indexing: the full cycle has more than 2^31 positions)
+        assert bool(((g["pos"] == 0) | real).all()) and bool(((g["mask"] == 0) | real).all())
         assert bool(((g["tokens"] == c.pad_token) | real).all())
         assert bool((g["mask"].sum(dim=(1, 2)).cpu() == g["learned"].cpu()).all()), "learned = sum of mask"
         exp_real = np.array([[int(op.win_real[op.window_of(s0 + i, j)]) for j in range(B)] for i in range(cnt)])
@@ -144,7 +154,7 @@ def test_full_size_ramp_parity():
     n_real = real.sum(dim=1)
     idx = torch.arange(T, device=doc.device).view(1, T)
     assert bool((real == (idx < n_real.unsqueeze(1))).all()), "padding only at the end of a window"
-    assert bool((g["pos"][~real] == 0).all()) and bool((g["mask"][~real] == 0).all())
+    assert bool(((g["pos"] == 0) | real).all()) and bool(((g["mask"] == 0) | real).all())
     exp_real = np.array([int(op.win_real[op.window_of(b, j)]) for b in range(U) for j in range(int(oi.batches[b]))])
     assert np.array_equal(n_real.cpu().numpy(), exp_real)
     r = np.random.default_rng(8)
@@ -204,4 +214,43 @@ def test_full_size_new_length_after_a_cycle():
     o = op.batch(n - 1, 1)
     assert np.array_equal(g["digests"][n - 1].cpu().numpy(), o["digests"][0])
     p2.close()
+    torch.cuda.empty_cache()
+
+
+def test_full_cycle_fingerprints_at_emulated_rank_counts():
+    """The full-cycle workload at full size (2·10^9 tokens, B = 1024): for each
+    rank count R in 1, 8, 16, 32, 64, every rank's slice of the cycle's first,
+    middle and last update is emitted by a fresh context of its own over the
+    resident corpus; the slices side by side must give the oracle's window
+    digests, and the batch fingerprint the oracle's (Zephon blog post, resume
+    of a 16-GPU run on 8/32/64 GPUs: every global batch's SHA-256 equal byte
+    for byte)."""
+    import torch
+    c, op, oi, tensors, pk, gi = _setup("full")
+    U, B = oi.n_updates, c.B
+    steps = [0, U // 2, U - 1]
+    say("oracle digests", "full", steps)
+    exp = oracle_digests(op, steps)
+    exp_fp = [oracle.batch_fingerprint(exp[k]) for k in range(len(steps))]
+    for R in (1, 8, 16, 32, 64):
+        per = B // R
+        dig = torch.empty((len(steps), B, 32), dtype=torch.uint8, device=tensors["tokens"].device)
+        say("emulated ranks", R)
+        for r in range(R):
+            p = dp.Packer(c, rank=r, world=R, device_tensors=tensors)
+            info = p.cycle(0)
+            assert info["plan_digest"] == oi.plan_digest and info["n_updates"] == U, (R, r)
+            for k, b in enumerate(steps):
+                out = p.alloc_out(1)
+                p.batch_into(b, 1, out)
+                dig[k, r * per:(r + 1) * per] = out["digests"][0]
+            p.status()
+            p.close()
+        got = dig.cpu().numpy()
+        for k, b in enumerate(steps):
+            assert np.array_equal(got[k], exp[k]), (R, b)
+        fps = pk.fingerprint(dig).cpu().numpy()
+        for k, b in enumerate(steps):
+            assert fps[k].tobytes() == exp_fp[k], (R, b)
+    _CACHE.clear()
     torch.cuda.empty_cache()
