@@ -48,8 +48,9 @@ def log(*a):
 
 def traffic_from_profile(kernel: str, workload: str):
     """HBM bytes per launch measured by rocprofv3 PMC runs, if a committed
-    summary exists for this kernel and workload and the kernel's source is
-    unchanged since (else None)."""
+    summary exists for this kernel and workload (profiles/<kernel>_<workload>
+    _pmc.md, the workload with a _packed suffix for padding-free rows) and the
+    kernel's source is unchanged since (else None)."""
     import hashlib
     path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_pmc.md")
     if not os.path.exists(path):
@@ -228,11 +229,13 @@ def main():
                 entry.update(emission_inside=fused, bytes_per_launch=digest_bytes,
                              achieved_GBps=round(digest_bytes / (per_launch_ms / 1e3) / 1e9, 1))
         kernels[k] = entry
+    # profiles are taken per kernel and workload, with and without padding-free rows
+    prof_tag = args.workload + ("_packed" if args.packed else "")
     dominant = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
     dom = kernels[dominant]
     roofline = None
     if "bound" in dom:
-        traffic = traffic_from_profile(dominant, args.workload)
+        traffic = traffic_from_profile(dominant, prof_tag)
         roofline = {"kernel": dominant, "bound": dom["bound"], "achieved": dom["achieved"], "peak": dom["peak"],
                     "unit": dom["unit"], "frac": dom["frac"], "traffic": traffic}
     # the HBM-bound kernels, each against the HBM roofline
@@ -241,7 +244,7 @@ def main():
         e = kernels.get(k, {})
         if "achieved" in e:
             side[k] = {"kernel": k, "bound": "hbm", "achieved": e["achieved"], "peak": HBM_PEAK_GBPS,
-                       "unit": "GB/s", "frac": e["frac"], "traffic": traffic_from_profile(k, args.workload)}
+                       "unit": "GB/s", "frac": e["frac"], "traffic": traffic_from_profile(k, prof_tag)}
     if "emit" not in side:
         # the emission kernel on its own (pack_batch without digests over the
         # same cycle, into the same buffers), timed by the library's events
@@ -260,7 +263,7 @@ def main():
         ach = emit_bytes / (per_launch_ms / 1e3) / 1e9
         side["emit"] = {"kernel": "emit", "bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBPS,
                         "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
-                        "traffic": traffic_from_profile("emit", args.workload),
+                        "traffic": traffic_from_profile("emit", prof_tag),
                         "ms_per_launch": round(per_launch_ms, 4), "work_per_launch": emit_bytes,
                         "measured": f"pack_batch without digests over the whole cycle, {reps} launches"}
         log(f"emission alone: {per_launch_ms:.3f} ms per cycle, {ach:.1f} GB/s")
