@@ -185,9 +185,9 @@ __device__ __forceinline__ void hash_outputs(uint32_t T, const EmitArgs& a, uint
 // (hash_outputs), reading a chunk only once it is published.  Emission is
 // memory traffic and a little integer work, so it hides under the hashing
 // waves' SHA-256 chains, the step's longest serial dependency, instead of
-// running as a kernel of its own before them.  A launch of more than 256
-// workgroups (65,536 windows) runs them one CU-load after another: each
-// workgroup's waves finish together, and the next one takes the CU.
+// running as a kernel of its own before them.  It serves launches of at most
+// 256 workgroups (65,536 windows, one hashing wave per SIMD); larger launches
+// use k_emit_digest below.
 //
 // Piece view (plan array pc_emit, written with the window offsets): position
 // t of piece q holds token base_q + t, position id t − f_q, document id d_q,
@@ -459,6 +459,203 @@ __global__ __launch_bounds__(64 * FWAVES) void k_emit_sha(Plan p, EmitArgs a, ui
     else emit_lanes(p, a, n_windows, w0, lane, prog + e);
 }
 
+// ---------------------------------------------------------------- emission and digest in one lane
+// For launches of more than 1,024 waves (more windows than one wave per SIMD
+// covers), each lane makes its window's record itself, 64-byte block by
+// 64-byte block in record order: token ids gathered from the corpus through the
+// window's pieces, position ids, document ids and loss-mask bytes computed
+// from them.  It stores the blocks to the outputs and compresses them, so
+// nothing is read back and no lane waits for another; without LDS and at 168
+// VGPRs a SIMD holds three such waves, which keeps the SHA-256 rounds'
+// dependent instructions issuing.  (With one wave per SIMD the paired kernel
+// above is faster: its emitting wave runs beside the chain instead of in it.)
+constexpr uint32_t GWAVES = 4;  // waves (of 64 windows) per workgroup
+
+__device__ __forceinline__ uint32_t pos_of(const EPiece& P, uint32_t t) { return (t - P.woff) & P.pm; }
+
+// Loads for the token block at window positions t0 .. t0+15: va gets the
+// 16-token run of the piece holding t0, vb that of the next piece (the block's
+// words are va below window position bw, vb from it).  Both loads are
+// unconditional (a run that does not lie wholly in the corpus reads the pad
+// buffer), so no loaded value crosses a branch; a lane whose block needs more
+// (a third piece starts in it, or a run it needs crosses the corpus end) gets
+// its words one by one instead, rarely.
+__device__ __forceinline__ void issue_tokens(const Plan& p, ECursor& c, uint32_t t0, uint32_t q1, uint32_t real,
+                                             uint32_t (&va)[16], uint32_t (&vb)[16], uint32_t& bw) {
+    c.seek(p, t0, q1, real);
+    const EPiece& A = c.cur;
+    const EPiece& B = c.nxt;
+    const uint64_t n = p.n_tokens;
+    const uint64_t lim = n >= 16 ? n - 16 : 0;
+    const bool okA = A.pm && n >= 16 && A.base + t0 <= lim;
+    const bool cross = t0 + 16 > B.woff;
+    const bool okB = B.pm && n >= 16 && B.base + t0 <= lim;
+    const bool exact = (A.pm && !okA) || (cross && B.pm && !okB) || t0 + 16 > c.nn.woff;
+    load16(va, okA ? p.tokens + A.base + t0 : p.pad16);
+    load16(vb, cross && okB ? p.tokens + B.base + t0 : p.pad16);
+    bw = B.woff;
+    if (wave_any(exact) && exact) {
+        ECursor x = c;
+#pragma unroll
+        for (uint32_t e = 0; e < 16; ++e) {
+            const uint32_t t = t0 + e;
+            x.seek(p, t, q1, real);
+            va[e] = x.cur.pm ? p.tokens[x.cur.base + t] : p.pad_token;
+        }
+        bw = NEVER;
+    }
+}
+
+// Position ids (S = 1) or document ids (S = 2) of window positions t0 .. t0+15.
+template <uint32_t S>
+__device__ __forceinline__ void id_block(const Plan& p, ECursor& c, uint32_t t0, uint32_t q1, uint32_t real,
+                                         uint32_t (&W)[16]) {
+    c.seek(p, t0, q1, real);
+    const EPiece& A = c.cur;
+    const EPiece& B = c.nxt;
+    if (!wave_any(t0 + 16 > c.nn.woff)) {  // at most one piece boundary in every lane's block
+#pragma unroll
+        for (uint32_t e = 0; e < 16; ++e) {
+            const uint32_t t = t0 + e;
+            const bool inB = t >= B.woff;
+            W[e] = S == 1 ? (inB ? pos_of(B, t) : pos_of(A, t)) : (inB ? B.doc : A.doc);
+        }
+    } else {
+        ECursor x = c;
+#pragma unroll
+        for (uint32_t e = 0; e < 16; ++e) {
+            const uint32_t t = t0 + e;
+            x.seek(p, t, q1, real);
+            W[e] = S == 1 ? pos_of(x.cur, t) : x.cur.doc;
+        }
+    }
+}
+
+// Loss-mask bytes of window positions t0 .. t0+63 as 16 little-endian words:
+// position t learns iff t is at or past the first learned position of the
+// piece holding it.  With at most one boundary (A to B) in the block, the
+// learned positions are [A.mfrom, B.woff) and [B.mfrom, ...), word by word.
+__device__ __forceinline__ void mask_block(const Plan& p, ECursor& c, uint32_t t0, uint32_t q1, uint32_t real,
+                                           uint32_t (&W)[16]) {
+    c.seek(p, t0, q1, real);
+    const EPiece& A = c.cur;
+    const EPiece& B = c.nxt;
+    if (!wave_any(t0 + 64 > c.nn.woff)) {
+        const int ma = (int)A.mfrom - (int)t0, wb = (int)B.woff - (int)t0, mb = (int)B.mfrom - (int)t0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            W[i] = __builtin_amdgcn_bitop3_b32(ones_le(clamp4(ma - 4 * i)), ones_le(clamp4(wb - 4 * i)),
+                                               ones_le(clamp4(mb - 4 * i)), 0xBA);  // (x & ~y) | z
+    } else {
+        ECursor x = c;
+#pragma unroll 1
+        for (uint32_t i = 0; i < 16; ++i) {
+            uint32_t w = 0;
+#pragma unroll
+            for (uint32_t k = 0; k < 4; ++k) {
+                const uint32_t t = t0 + 4 * i + k;
+                x.seek(p, t, q1, real);
+                w |= (t >= x.cur.mfrom ? 1u : 0u) << (8 * k);
+            }
+            W[i] = w;
+        }
+    }
+}
+
+__device__ __forceinline__ void compress_le(uint32_t H[8], uint32_t (&W)[16]) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) W[e] = bswap32(W[e]);
+    sha256_compress(H, W);
+}
+
+__global__ __launch_bounds__(64 * GWAVES) __attribute__((amdgpu_waves_per_eu(3)))
+void k_emit_digest(Plan p, EmitArgs a, uint64_t n_windows) {
+    const uint32_t wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+    const uint64_t w0 = ((uint64_t)blockIdx.x * GWAVES + wave) * 64;
+    if (w0 >= n_windows) return;  // whole wave past the end
+    const bool valid = w0 + lane < n_windows;
+    const uint64_t w = valid ? w0 + lane : n_windows - 1;  // lanes past the end mirror the last window
+    uint32_t i_, jj_, per_;
+    const uint64_t gw = out_window(p, a, w, &i_, &jj_, &per_);
+    const uint32_t q0 = p.win_first[gw], q1 = p.win_first[gw + 1], real = p.win_real[gw];
+    const uint32_t T = p.T;
+    if (q1 <= q0 || real > T) {  // every window holds a piece and at most T positions (else a library bug)
+        atomicOr(p.err_batch, ERR_INTERNAL);
+        return;
+    }
+    uint32_t H[8];
+    sha256_init(H);
+    ECursor c;
+    // One loop over the record's 13·T/64 blocks, so the compression is one
+    // copy of code: blocks [0, T/16) are token ids (the next block's runs
+    // loaded before the current one is compressed), then position ids and
+    // document ids (T/16 blocks each), then the mask (T/64 blocks of 64
+    // positions).  The block's array is uniform across the wave.
+    const uint32_t nb = T / 16, nblk = 13 * (T / 64);
+    uint32_t va[16], vb[16], bw;
+    // A block is half of a 128-byte line of its array: an even block's words
+    // wait in P and are stored with the next block's, eight 16-byte stores in a
+    // row, so no line is left half-written in L2 for a whole compression (only
+    // a last mask block of an odd count goes out alone).
+    uint32_t P[16];
+    c.restart(p, q0, q1, real);
+    issue_tokens(p, c, 0, q1, real, va, vb, bw);
+#pragma unroll 1
+    for (uint32_t blk = 0; blk < nblk; ++blk) {
+        uint32_t W[16];
+        uint8_t* dst;
+        uint32_t k, n_arr;  // the block's index in its array, the array's blocks
+        if (blk < nb) {
+            const uint32_t t0 = 16 * blk;
+#pragma unroll
+            for (uint32_t e = 0; e < 16; ++e) W[e] = t0 + e >= bw ? vb[e] : va[e];
+            if (blk + 1 < nb) issue_tokens(p, c, t0 + 16, q1, real, va, vb, bw);
+            dst = reinterpret_cast<uint8_t*>(a.tok + w * T + t0);
+            k = blk;
+            n_arr = nb;
+        } else if (blk < 2 * nb) {
+            const uint32_t t0 = 16 * (blk - nb);
+            if (t0 == 0) c.restart(p, q0, q1, real);
+            id_block<1>(p, c, t0, q1, real, W);
+            dst = reinterpret_cast<uint8_t*>(a.pos + w * T + t0);
+            k = blk - nb;
+            n_arr = nb;
+        } else if (blk < 3 * nb) {
+            const uint32_t t0 = 16 * (blk - 2 * nb);
+            if (t0 == 0) c.restart(p, q0, q1, real);
+            id_block<2>(p, c, t0, q1, real, W);
+            dst = reinterpret_cast<uint8_t*>(a.doc + w * T + t0);
+            k = blk - 2 * nb;
+            n_arr = nb;
+        } else {
+            const uint32_t t0 = 64 * (blk - 3 * nb);
+            if (t0 == 0) c.restart(p, q0, q1, real);
+            mask_block(p, c, t0, q1, real, W);
+            dst = a.mask + w * T + t0;
+            k = blk - 3 * nb;
+            n_arr = T / 64;
+        }
+        if ((k & 1) == 0 && k + 1 < n_arr) {  // first half of a line: wait for the second
+#pragma unroll
+            for (int e = 0; e < 16; ++e) P[e] = W[e];
+        } else if (valid) {
+            if (k & 1) store16(dst - 64, P);
+            store16(dst, W);
+        }
+        compress_le(H, W);
+    }
+    // 13·T bytes is a multiple of 64: one padding block
+    uint32_t W[16];
+    W[0] = 0x80000000u;
+#pragma unroll
+    for (int i = 1; i < 14; ++i) W[i] = 0;
+    const uint64_t bits = 13ull * T * 8ull;
+    W[14] = (uint32_t)(bits >> 32);
+    W[15] = (uint32_t)bits;
+    sha256_compress(H, W);
+    if (valid) store_digest(H, a.digests + 32 * w);
+}
+
 // SHA-256 of an arbitrary byte string (4-byte aligned start), one lane.  The
 // next block's words are loaded before the current block is compressed, so
 // the chain does not wait on a load per block.
@@ -547,7 +744,13 @@ __global__ __launch_bounds__(64) void k_sha_chunks(const uint8_t* msg, uint64_t 
 
 void launch_emit_sha(const Plan& p, const EmitArgs& a, hipStream_t st) {
     const uint64_t n = a.n_out;  // < 2^31 windows: at most 2^23 workgroups
-    if (n) hipLaunchKernelGGL(k_emit_sha, dim3((uint32_t)((n + 255) / 256)), dim3(64 * FWAVES), 0, st, p, a, n);
+    const uint64_t waves = (n + 63) / 64;
+    if (!n) return;
+    if (waves <= 1024)  // no more windows than one hashing wave per SIMD (256 CUs x 4) covers
+        hipLaunchKernelGGL(k_emit_sha, dim3((uint32_t)((n + 255) / 256)), dim3(64 * FWAVES), 0, st, p, a, n);
+    else
+        hipLaunchKernelGGL(k_emit_digest, dim3((uint32_t)((waves + GWAVES - 1) / GWAVES)), dim3(64 * GWAVES), 0, st,
+                           p, a, n);
     DP_HIP(hipGetLastError());
 }
 

@@ -409,7 +409,8 @@ int pack_status(pack_ctx *ctx);
  * end; with every option 0 (the default) no output byte changes. */
 enum {
     PACK_TEST_WAIT_GIVE_UP = 1, /* the digest waves' bounded waits give up after one poll:
-                                   the batch's digests are invalid, pack_status reports it */
+                                   the batch's digests are invalid, pack_status reports it
+                                   (calls of at most 65,536 windows; larger ones have no wait) */
     PACK_TEST_CYCLE_FAULT = 2,  /* a cycle kernel reports an internal failure: pack_cycle fails */
 };
 
