@@ -507,14 +507,16 @@ void build_plan(pack_ctx& c) {
         dp::launch_lane_source(c.cfg.doc_source, p.n_docs, c.S_real, c.lanes, c.lane_source, st);
         p.source = c.lane_source;
     }
-    dp::launch_validate(p, st);
+    // the validation also zeroes the hash's per-document sums (gpre, free
+    // until the merge) and writes its tile table
+    dp::launch_validate(p, p.gpre, c.hash_first, st);
     c.timer.end(st);
 
     // A1 hash + hold-out, A2 compaction, A3 keys; after an invalid corpus the
     // hash kernels return at once (they read the error flag) and the error is
     // raised below, before any later kernel runs
     c.timer.begin(PACK_PHASE_HASH, st);
-    dp::launch_hash(p, p.gpre /* per-document sums; gpre is free until the merge */, c.hash_first, st);
+    dp::launch_hash(p, p.gpre, c.hash_first, st);
     c.timer.end(st);
     c.timer.begin(PACK_PHASE_KEYS, st);
     dp::launch_keep_scan(p, st);

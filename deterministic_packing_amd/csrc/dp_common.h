@@ -264,7 +264,7 @@ __device__ inline uint32_t bswap32(uint32_t x) { return __builtin_bswap32(x); }
 
 // ---------------------------------------------------------------- launchers
 // (each defined in the translation unit that holds the kernels)
-void launch_validate(const Plan& p, hipStream_t st);
+void launch_validate(const Plan& p, uint64_t* S, uint32_t* first, hipStream_t st);  // also zeroes S, fills first
 void launch_hash(const Plan& p, uint64_t* S, uint32_t* first, hipStream_t st);
 uint64_t hash_tile_count(uint64_t n_tokens);
 void launch_keep_scan(Plan& p, hipStream_t st);       // kept_pos + compaction into val[0], keys

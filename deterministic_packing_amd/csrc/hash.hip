@@ -25,13 +25,35 @@ enum : uint32_t {
     ERR_SEGMENT = 32u,     // arrival id out of range
 };
 
-__global__ __launch_bounds__(256) void k_validate(Plan p) {
+constexpr uint32_t TPT = 16;         // contiguous tokens per thread of the hash
+constexpr uint32_t HT = 256 * TPT;   // tokens per tile (one 256-thread block)
+
+// One thread per document: the corpus checks, and two preparations of the
+// hash (the validation visits every document anyway): the document's NH sum
+// S[d] = 0, and the tile table first[t] = d for every tile whose first token
+// base + t·HT lies in the document (each token belongs to one non-empty
+// document, so every tile below ntiles gets exactly one writer; the last
+// document also writes the sentinel first[ntiles] = D − 1).  A document whose
+// own offsets are invalid writes no table entry, and entries stay below
+// n_first, so an invalid corpus writes nothing out of place; the hash kernels
+// then return at once on the error flag.
+__global__ __launch_bounds__(256) void k_validate(Plan p, uint64_t* S, uint32_t* first, uint64_t n_first) {
     const uint64_t d = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (d >= p.n_docs) return;
     uint32_t err = 0;
     const uint64_t o0 = p.offsets[d], o1 = p.offsets[d + 1];
+    S[d] = 0;
     if (o1 < o0) err |= ERR_OFFSETS;
     else if (o1 - o0 > 0xFFFFFFFFull) err |= ERR_DOC_LEN;
+    const uint64_t base = p.offsets[0];
+    if (!err && o1 > o0 && o0 >= base && o1 <= p.n_tokens) {
+        for (uint64_t t = (o0 - base + HT - 1) / HT; t <= (o1 - 1 - base) / HT && t < n_first; ++t)
+            first[t] = (uint32_t)d;
+    }
+    if (d == p.n_docs - 1 && o1 >= base) {
+        const uint64_t ntiles = (o1 - base + HT - 1) / HT;
+        if (ntiles < n_first) first[ntiles] = (uint32_t)d;
+    }
     const uint32_t s = p.source[d];
     const uint32_t g = p.n_seg > 1 ? p.segment[d] : 0u;
     if (s >= p.S) {
@@ -57,30 +79,7 @@ __global__ __launch_bounds__(256) void k_validate(Plan p) {
 // by a segmented scan (documents are in token order) and added to S[d] with one
 // 64-bit atomic per document and wavefront: integer addition is order-free, so
 // the sum is exact.  k_hash_final then mixes and decides the hold-out.
-constexpr uint32_t TPT = 16;         // contiguous tokens per thread
-constexpr uint32_t HT = 256 * TPT;   // tokens per tile (one 256-thread block)
-
 typedef uint32_t u32x4a4 __attribute__((ext_vector_type(4), aligned(4)));
-
-// first[t] = the document containing token base + t·HT (clamped to D−1)
-__global__ __launch_bounds__(256) void k_tile_first_doc(Plan p, uint32_t* first) {
-    if (*p.err) return;  // an invalid corpus: nothing reads its offsets
-    const uint64_t base = p.offsets[0], end = p.offsets[p.n_docs];
-    const uint64_t ntiles = (end - base + HT - 1) / HT;
-    const uint64_t t = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (t > ntiles) return;
-    const uint64_t x = base + t * HT;
-    // number of j in [1, D] with off[j] <= x: the containing document (empty ones skipped)
-    uint64_t lo = 1, hi = p.n_docs + 1;
-    while (lo < hi) {
-        const uint64_t mid = (lo + hi) >> 1;
-        if (p.offsets[mid] <= x) lo = mid + 1;
-        else hi = mid;
-    }
-    uint64_t d = lo - 1;
-    if (d > p.n_docs - 1) d = p.n_docs - 1;
-    first[t] = (uint32_t)d;
-}
 
 __device__ inline uint64_t pair_term(uint32_t a, uint32_t b, uint64_t r) {
     const uint32_t k0 = (uint32_t)(r + 1) * PHI32;
@@ -345,34 +344,25 @@ __global__ __launch_bounds__(256) void k_hash_final(Plan p, const uint64_t* S, u
     }
 }
 
-__global__ __launch_bounds__(256) void k_zero(uint64_t* a, uint64_t n) {
-    for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (uint64_t)gridDim.x * blockDim.x)
-        a[i] = 0;
-}
-
 }  // namespace
 
-void launch_validate(const Plan& p, hipStream_t st) {
+void launch_validate(const Plan& p, uint64_t* S, uint32_t* first, hipStream_t st) {
     const uint64_t blocks = (p.n_docs + 255) / 256;
-    hipLaunchKernelGGL(k_validate, dim3((uint32_t)blocks), dim3(256), 0, st, p);
+    hipLaunchKernelGGL(k_validate, dim3((uint32_t)blocks), dim3(256), 0, st, p, S, first,
+                       hash_tile_count(p.n_tokens) + 2);
     DP_HIP(hipGetLastError());
 }
 
-// base/end: offsets[0] and offsets[n_docs] (read back after validation);
-// S: [n_docs] sums, first: [ntiles + 1] tile table (workspace)
-// The span [offsets[0], offsets[n_docs]) is read on the device and the
-// grids are sized by n_tokens, so nothing waits for the validation: after an
-// invalid corpus the kernels return at once and the error is read with the
-// kept count.  S: [n_docs] sums, first: [hash_tile_count(n_tokens) + 2]
+// S: [n_docs] sums, zeroed by the validation kernel; first: the tile table it
+// wrote ([hash_tile_count(n_tokens) + 2]).  The span [offsets[0],
+// offsets[n_docs]) is read on the device and the grid is sized by n_tokens, so
+// nothing waits for the validation: after an invalid corpus the kernels return
+// at once and the error is read with the kept count.
 void launch_hash(const Plan& p, uint64_t* S, uint32_t* first, hipStream_t st) {
     const uint64_t ntiles = (p.n_tokens + HT - 1) / HT;  // a bound: the documents cover at most n_tokens
-    hipLaunchKernelGGL(k_zero, dim3((uint32_t)std::min<uint64_t>((p.n_docs + 255) / 256, 2048)), dim3(256), 0, st, S,
-                       p.n_docs);
-    if (ntiles) {
-        hipLaunchKernelGGL(k_tile_first_doc, dim3((uint32_t)((ntiles + 1 + 255) / 256)), dim3(256), 0, st, p, first);
+    if (ntiles)
         hipLaunchKernelGGL(k_hash_flat, dim3((uint32_t)std::min<uint64_t>(ntiles, 16384)), dim3(256), 0, st, p,
                            (const uint32_t*)first, S);
-    }
     const uint32_t lds_bins = p.S <= 256 ? 1u : 0u;
     const size_t lds = lds_bins ? 4ull * p.S * sizeof(uint64_t) : 0;
     hipLaunchKernelGGL(k_hash_final, dim3((uint32_t)std::min<uint64_t>((p.n_docs + 255) / 256, 1024)), dim3(256), lds,
