@@ -586,55 +586,12 @@ void k_emit_digest(Plan p, EmitArgs a, uint64_t n_windows) {
     uint32_t H[8];
     sha256_init(H);
     ECursor c;
-    // One loop over the record's 13·T/64 blocks, so the compression is one
-    // copy of code: blocks [0, T/16) are token ids (the next block's runs
-    // loaded before the current one is compressed), then position ids and
-    // document ids (T/16 blocks each), then the mask (T/64 blocks of 64
-    // positions).  The block's array is uniform across the wave.
-    const uint32_t nb = T / 16, nblk = 13 * (T / 64);
-    uint32_t va[16], vb[16], bw;
     // A block is half of a 128-byte line of its array: an even block's words
     // wait in P and are stored with the next block's, eight 16-byte stores in a
     // row, so no line is left half-written in L2 for a whole compression (only
     // a last mask block of an odd count goes out alone).
     uint32_t P[16];
-    c.restart(p, q0, q1, real);
-    issue_tokens(p, c, 0, q1, real, va, vb, bw);
-#pragma unroll 1
-    for (uint32_t blk = 0; blk < nblk; ++blk) {
-        uint32_t W[16];
-        uint8_t* dst;
-        uint32_t k, n_arr;  // the block's index in its array, the array's blocks
-        if (blk < nb) {
-            const uint32_t t0 = 16 * blk;
-#pragma unroll
-            for (uint32_t e = 0; e < 16; ++e) W[e] = t0 + e >= bw ? vb[e] : va[e];
-            if (blk + 1 < nb) issue_tokens(p, c, t0 + 16, q1, real, va, vb, bw);
-            dst = reinterpret_cast<uint8_t*>(a.tok + w * T + t0);
-            k = blk;
-            n_arr = nb;
-        } else if (blk < 2 * nb) {
-            const uint32_t t0 = 16 * (blk - nb);
-            if (t0 == 0) c.restart(p, q0, q1, real);
-            id_block<1>(p, c, t0, q1, real, W);
-            dst = reinterpret_cast<uint8_t*>(a.pos + w * T + t0);
-            k = blk - nb;
-            n_arr = nb;
-        } else if (blk < 3 * nb) {
-            const uint32_t t0 = 16 * (blk - 2 * nb);
-            if (t0 == 0) c.restart(p, q0, q1, real);
-            id_block<2>(p, c, t0, q1, real, W);
-            dst = reinterpret_cast<uint8_t*>(a.doc + w * T + t0);
-            k = blk - 2 * nb;
-            n_arr = nb;
-        } else {
-            const uint32_t t0 = 64 * (blk - 3 * nb);
-            if (t0 == 0) c.restart(p, q0, q1, real);
-            mask_block(p, c, t0, q1, real, W);
-            dst = a.mask + w * T + t0;
-            k = blk - 3 * nb;
-            n_arr = T / 64;
-        }
+    auto finish = [&](uint32_t (&W)[16], uint8_t* dst, uint32_t k, uint32_t n_arr) {
         if ((k & 1) == 0 && k + 1 < n_arr) {  // first half of a line: wait for the second
 #pragma unroll
             for (int e = 0; e < 16; ++e) P[e] = W[e];
@@ -643,6 +600,46 @@ void k_emit_digest(Plan p, EmitArgs a, uint64_t n_windows) {
             store16(dst, W);
         }
         compress_le(H, W);
+    };
+    const uint32_t nb = T / 16;
+    // token ids: the next block's runs are loaded before the current one is compressed
+    uint32_t va[16], vb[16], bw;
+    c.restart(p, q0, q1, real);
+    issue_tokens(p, c, 0, q1, real, va, vb, bw);
+    uint8_t* const tok = reinterpret_cast<uint8_t*>(a.tok + w * T);
+#pragma unroll 1
+    for (uint32_t k = 0; k < nb; ++k) {
+        uint32_t W[16];
+#pragma unroll
+        for (uint32_t e = 0; e < 16; ++e) W[e] = 16 * k + e >= bw ? vb[e] : va[e];
+        if (k + 1 < nb) issue_tokens(p, c, 16 * (k + 1), q1, real, va, vb, bw);
+        finish(W, tok + 64 * k, k, nb);
+    }
+    // position ids, document ids
+    uint8_t* const pos = reinterpret_cast<uint8_t*>(a.pos + w * T);
+    c.restart(p, q0, q1, real);
+#pragma unroll 1
+    for (uint32_t k = 0; k < nb; ++k) {
+        uint32_t W[16];
+        id_block<1>(p, c, 16 * k, q1, real, W);
+        finish(W, pos + 64 * k, k, nb);
+    }
+    uint8_t* const doc = reinterpret_cast<uint8_t*>(a.doc + w * T);
+    c.restart(p, q0, q1, real);
+#pragma unroll 1
+    for (uint32_t k = 0; k < nb; ++k) {
+        uint32_t W[16];
+        id_block<2>(p, c, 16 * k, q1, real, W);
+        finish(W, doc + 64 * k, k, nb);
+    }
+    // loss mask, 64 positions per block
+    uint8_t* const mask = a.mask + w * T;
+    c.restart(p, q0, q1, real);
+#pragma unroll 1
+    for (uint32_t k = 0; k < T / 64; ++k) {
+        uint32_t W[16];
+        mask_block(p, c, 64 * k, q1, real, W);
+        finish(W, mask + 64 * k, k, T / 64);
     }
     // 13·T bytes is a multiple of 64: one padding block
     uint32_t W[16];
