@@ -905,9 +905,20 @@ int pack_cycle(pack_ctx* c, uint32_t cycle, pack_cycle_info* info) {
                 dp::Plan pc = p;
                 pc.S = Sr;
                 if (L > 1) pc.cum_A = c->cum_Ar;
+                // integral quotas (every update's seats times every weight a multiple of W):
+                // the schedule has a closed form
+                bool integral = true;
+                for (uint32_t r = 0; r < Sr && integral; ++r) {
+                    const unsigned __int128 w = c->weight_real[r];
+                    if (p.ramp) {
+                        for (const dp::RampSpan& sp : spans) integral = integral && (sp.B / L) * w % c->W == 0;
+                    } else {
+                        integral = (p.B / L) * w % c->W == 0;
+                    }
+                }
                 c->timer.begin(PACK_PHASE_CYCLE, c->st);
                 h2d_staged(*c, p.cum_rem, rr.data(), Sr);
-                dp::launch_cumulative(pc, c->W, U, cap, c->st);
+                dp::launch_cumulative(pc, c->W, cap, integral, c->st);
                 c->timer.end(c->st);
                 const uint64_t* h_out = d2h_staged(*c, p.cum_out, Sr + 1);
                 const uint32_t* h_err = d2h_staged(*c, p.err, 1);

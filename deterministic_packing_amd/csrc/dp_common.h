@@ -287,8 +287,9 @@ uint64_t sort_hist_words(uint64_t n, uint64_t G);
 void launch_checks(Plan& p, hipStream_t st);          // order / hash checks
 void launch_cycle_sums(Plan& p, uint64_t total_slots, hipStream_t st);
 // cumulative mixture of a cycle: the schedule (cum_A, cum_out), then, once the
-// host has accepted U, every update's slot table
-void launch_cumulative(Plan& p, uint64_t W, uint64_t u_cfg, uint64_t cap, hipStream_t st);
+// host has accepted U, every update's slot table.  integral: every update's
+// seats times every weight is a multiple of W (the schedule has a closed form)
+void launch_cumulative(Plan& p, uint64_t W, uint64_t cap, bool integral, hipStream_t st);
 void launch_cum_slots(Plan& p, uint32_t U, hipStream_t st);
 // lanes: stream ids of the documents, one lane's counts/slots to every lane, one lane's schedule to every lane
 void launch_lane_source(const uint16_t* source, uint64_t n_docs, uint32_t S_real, uint32_t L, uint16_t* out,

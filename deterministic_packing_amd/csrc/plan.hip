@@ -643,6 +643,60 @@ __global__ __launch_bounds__(ONE_WAVE ? WAVE : CUM_MAX_S) void k_cumulative(Plan
     if (bad && s == 0) atomicOr(p.err, ERR_INTERNAL);
 }
 
+// Integral quotas: when every update's seats times every weight is a multiple
+// of W (one source, or shares that divide the batch), every quota is an
+// integer, no window is ever taken ahead of its quota, and the schedule above
+// is A_s(u) = H(u)·w_s/W exactly, H(u) being the lane's seats before update u.
+// Then no update-by-update loop is needed: one thread per source finds the
+// last update its windows cover (A_s is nondecreasing in u), the minimum over
+// sources (at most cap) is the cycle's U, and a grid writes the table.
+__device__ inline uint64_t lane_seats_before(const Plan& p, uint64_t u) {
+    if (!p.ramp) return u * (uint64_t)(p.B / p.lanes);
+    uint32_t lo = 0, hi = p.n_spans;  // span of update u
+    while (hi - lo > 1) {
+        const uint32_t mid = (lo + hi) >> 1;
+        if (p.spans[mid].first <= u) lo = mid;
+        else hi = mid;
+    }
+    const RampSpan& r = p.spans[lo];
+    return (r.slot0 + (u - r.first) * r.B) / p.lanes;
+}
+
+__device__ inline uint64_t integral_quota(const Plan& p, uint64_t u, uint64_t w, uint64_t W) {
+    const uint64_t H = lane_seats_before(p, u);
+    uint64_t r;
+    return w ? div128(__umul64hi(H, w), H * w, W, &r) : 0;  // the quotient is at most H: hi < W
+}
+
+__global__ __launch_bounds__(1024) void k_cum_integral_U(Plan p, uint64_t W, uint64_t cap) {
+    __shared__ unsigned long long U;
+    if (threadIdx.x == 0) U = cap;
+    __syncthreads();
+    for (uint32_t s = threadIdx.x; s < p.S; s += blockDim.x) {
+        const uint64_t w = p.weight[s], rem = p.cum_rem[s];
+        if (w == 0 || integral_quota(p, cap, w, W) <= rem) continue;
+        uint64_t lo = 0, hi = cap;  // A_s(lo) ≤ rem < A_s(hi)
+        while (hi - lo > 1) {
+            const uint64_t mid = lo + (hi - lo) / 2;
+            if (integral_quota(p, mid, w, W) <= rem) lo = mid;
+            else hi = mid;
+        }
+        atomicMin(&U, (unsigned long long)lo);
+    }
+    __syncthreads();
+    for (uint32_t s = threadIdx.x; s < p.S; s += blockDim.x) p.cum_out[s] = integral_quota(p, U, p.weight[s], W);
+    if (threadIdx.x == 0) p.cum_out[p.S] = U;
+}
+
+__global__ __launch_bounds__(256) void k_cum_integral_A(Plan p, uint64_t W, uint64_t cap) {
+    const uint64_t x = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (x >= (cap + 1) * p.S) return;
+    const uint64_t u = x / p.S;
+    const uint32_t s = (uint32_t)(x - u * p.S);
+    if (u > p.cum_out[p.S]) return;
+    p.cum_A[x] = (uint32_t)integral_quota(p, u, p.weight[s], W);
+}
+
 // Slot table of every update of the cycle: block u, counts
 // A(u+1) − A(u) in Sainte-Laguë order; cslot_i = A_s(u) + k.
 __global__ __launch_bounds__(256) void k_cum_slots(Plan p) {
@@ -882,9 +936,11 @@ void launch_mixture_w(Plan& p, uint64_t W, uint32_t* nstart, hipStream_t st) {
     DP_HIP(hipGetLastError());
 }
 
-void launch_cumulative(Plan& p, uint64_t W, uint64_t u_cfg, uint64_t cap, hipStream_t st) {
-    (void)u_cfg;  // cap already holds it when it is set
-    if (p.S <= WAVE) {
+void launch_cumulative(Plan& p, uint64_t W, uint64_t cap, bool integral, hipStream_t st) {
+    if (integral) {
+        hipLaunchKernelGGL(k_cum_integral_U, dim3(1), dim3(1024), 0, st, p, W, cap);
+        hipLaunchKernelGGL(k_cum_integral_A, dim3(blocks_for((cap + 1) * p.S)), dim3(256), 0, st, p, W, cap);
+    } else if (p.S <= WAVE) {
         hipLaunchKernelGGL(k_cumulative<true>, dim3(1), dim3(WAVE), 0, st, p, W, cap);
     } else {
         const uint32_t threads = ((p.S + WAVE - 1) / WAVE) * WAVE;

@@ -163,6 +163,46 @@ def test_cumulative_small_share_parity():
     _parity_run(c.replace(cumulative=True), "cumulative-small-share", 0)
 
 
+INTEGRAL_CASES = [
+    # (seed, sources, weights, B, ramp, lanes, updates per cycle): every update's seats times every weight
+    # a multiple of the weights' sum, so every cumulative quota is an integer
+    (0, 1, [5], 5, None, 1, 0),
+    (1, 3, [1, 1, 2], 8, None, 1, 0),
+    (2, 2, [1, 3], 16, ((0, 256), (700, 512), (2000, 1024)), 1, 0),
+    (3, 2, [1, 1], 8, None, 2, 0),
+    (4, 2, [1, 1], 6, None, 1, 3),
+    (5, 3, [0, 2, 2], 4, None, 1, 2),
+    (6, 1, [7], 3, ((0, 192), (900, 64)), 1, 4),
+]
+
+
+@pytest.mark.parametrize("case", range(len(INTEGRAL_CASES)))
+def test_cumulative_integral_quotas(case):
+    """Cumulative quotas that are integers every update (one source, or shares
+    dividing every batch): the schedule's closed form, cycle after cycle until
+    a source runs out, with a ramp, lanes and fixed cycle lengths."""
+    seed, S, w, B, ramp, L, upc = INTEGRAL_CASES[case]
+    c = random_small(950 + seed, n_docs=800, n_sources=S, max_strata=2, T=64, B=B, max_len=150,
+                     prompts=bool(seed % 2), bp_max=1000)
+    c = c.replace(weight=np.array(w, np.uint64), cumulative=True, ramp=ramp, lanes=L, updates_per_cycle=upc)
+    op = oracle.Plan(c)
+    pk = dp.Packer(c)
+    for cyc in range(4):
+        try:
+            oi = op.cycle(cyc)
+        except oracle.OracleError as e:
+            with pytest.raises(dp.DpackError) as ge:
+                pk.cycle(cyc)
+            assert ge.value.code == e.code
+            break
+        say("integral quotas", case, "cycle", cyc, "updates", oi.n_updates)
+        compare_cycle(pk.cycle(cyc), oi, op)
+        assert np.array_equal(pk.inspect("cum_taken"), op.cumulative_taken().ravel())
+        n = oi.n_updates
+        compare_batch(to_np(pk.batch(0, n)), op.batch(0, n), f"integral {case} cycle {cyc}")
+    pk.close()
+
+
 RAMP_CASES = [
     # (seed, ramp pieces (from tokens, tokens per update), B, cumulative, read_random, wrap, updates per cycle)
     (0, ((0, 128), (1000, 256), (3000, 512)), 8, False, False, False, 3),
