@@ -184,6 +184,9 @@ struct pack_ctx {
     bool noalloc = false;  // arena and staging are the device's static scratch and host buffer
     uint32_t* nstart = nullptr;
     uint32_t* hash_first = nullptr;  // tile -> first document table of the hash
+    uint32_t* scan_base = nullptr;   // the scans' workspace (zeroed once at init)
+    uint64_t scan_words = 0;
+    uint32_t scan_epoch = 0;         // the last scan epoch (host)
     uint8_t* dig_buf = nullptr;
     size_t dig_cap = 0;
     // pinned host staging for every host<->device copy (asynchronous copies,
@@ -271,6 +274,12 @@ size_t carve(pack_ctx& c, char* base) {
     p.val[1] = k.take<uint32_t>(D);
     const uint64_t WR = p.read_random ? P : 0;  // cycle windows ≤ windows ≤ pieces
     p.hist = k.take<uint32_t>(dp::sort_hist_words(D > WR ? D : WR, G > S ? G : S));
+    {  // scans: kept flags (D), the sorts' bucket counts, lengths and pieces (≤ D)
+        const uint64_t n_max = std::max<uint64_t>(D + 1, (D > WR ? D : WR) / 2 + (G > S ? G : S) + 1);
+        c.scan_words = dp::scan_ws_bytes(n_max) / 4;
+        c.scan_base = k.take<uint32_t>(c.scan_words);
+        p.scan = dp::scan_ws_at(c.scan_base, n_max, p.err, &c.scan_epoch);
+    }
     p.group_start = k.take<uint32_t>(G + 1);
     p.gpre = k.take<uint64_t>(D + 1);
     p.order = k.take<uint32_t>(D);
@@ -392,6 +401,7 @@ void check_config(const pack_config* cfg) {
     if (cfg->n_docs < 1 || cfg->n_docs >= (1ull << 31)) bad("n_docs must be in [1, 2^31)");
     if (!cfg->doc_offsets || !cfg->doc_source) bad("doc_offsets and doc_source are required");
     if (cfg->n_tokens && !cfg->tokens) bad("tokens is NULL with n_tokens > 0");
+    if (cfg->n_tokens >= (1ull << dp::SCAN_VALUE_BITS)) bad("n_tokens must be below 2^40");
     if (cfg->n_sources < 1 || cfg->n_sources > 4096) bad("n_sources must be in [1, 4096]");
     if (!cfg->share_weight || !cfg->holdout_bp) bad("share_weight and holdout_bp are required");
     const uint32_t T = cfg->window_tokens, B = cfg->global_batch;
@@ -503,6 +513,8 @@ void build_plan(pack_ctx& c) {
 
     // validation first: no kernel reads the corpus through unchecked offsets
     c.timer.begin(PACK_PHASE_VALIDATE, st);
+    dp::launch_zero_u32(c.scan_base, c.scan_words, st);  // no tile ticket taken, no status published
+    c.scan_epoch = 0;
     if (c.lanes > 1) {  // documents to streams (source, lane); the validation then checks stream ids
         dp::launch_lane_source(c.cfg.doc_source, p.n_docs, c.S_real, c.lanes, c.lane_source, st);
         p.source = c.lane_source;
@@ -525,6 +537,7 @@ void build_plan(pack_ctx& c) {
     const uint32_t* h_kept = d2h_staged(c, p.kept_pos + p.n_docs, 1);
     sync_staged(c);
     uint32_t err = *h_err;
+    if (err & dp::ERR_INTERNAL) throw InternalError{"internal: a scan's bounded wait gave up (library bug)"};
     if (err) {
         std::string m = "invalid corpus:";
         if (err & 1u) m += " offsets decrease;";

@@ -86,6 +86,23 @@ struct RampSpan {
     uint32_t k;      // ramp piece
 };
 
+// Workspace of the single-pass scans: a tile ticket (zero between scans) and
+// one status word per tile: state (bits 63..62: 1 the tile's sum, 2 its
+// inclusive prefix), the scan's epoch (61..40; words of other epochs count as
+// nothing published) and the value (39..0), in one word so that a relaxed
+// device-scope atomic load sees value and state together (no fence, which
+// would write back the whole L2 of the publishing XCD).  err receives
+// ERR_INTERNAL if a look-back's bounded wait gives up.  epoch (host) is the
+// last epoch used; at its wrap the workspace is zeroed again.
+struct ScanWs {
+    uint32_t* ticket;
+    uint64_t* status;
+    uint32_t* err;
+    uint32_t* epoch;  // host
+    uint64_t words;   // 32-bit words of the workspace, ticket first
+};
+constexpr uint64_t SCAN_VALUE_BITS = 40;  // scanned totals stay below 2^40 (n_tokens < 2^40)
+
 struct Plan {
     // inputs (borrowed)
     const uint32_t* tokens;
@@ -128,7 +145,8 @@ struct Plan {
     // A3 sort
     uint64_t* key[2];             // [D]
     uint32_t* val[2];             // [D]
-    uint32_t* hist;               // [256 * NB + 1]
+    uint32_t* hist;               // sort workspace
+    ScanWs scan;                  // single-pass scan workspace
     uint32_t sort_buf;            // which buffer holds the sorted result
 
     // A4
@@ -270,7 +288,7 @@ uint64_t hash_tile_count(uint64_t n_tokens);
 void launch_keep_scan(Plan& p, hipStream_t st);       // kept_pos + compaction into val[0], keys
 void launch_sort(Plan& p, hipStream_t st);            // by (group, key64, d); sets sort_buf
 uint32_t sort_pairs(uint64_t* const key[2], uint32_t* const val[2], const uint32_t* group, uint64_t n, uint32_t G,
-                    uint32_t* hist_ws, uint32_t* err, hipStream_t st);
+                    uint32_t* hist_ws, const ScanWs& scan, hipStream_t st);
 void launch_read_order(Plan& p, uint32_t cycle, uint64_t total, hipStream_t st);  // perm of each source's cycle windows
 void launch_merge(Plan& p, hipStream_t st);           // group_start, gpre, order, src_doc_start
 void launch_piece_count(Plan& p, hipStream_t st);     // piece_start, opre
@@ -355,18 +373,21 @@ void launch_batch_fp_var(const uint8_t* digests, const uint64_t* slot0, uint32_t
 void launch_sha_chunks(const uint8_t* msg, uint64_t len, uint32_t chunk, uint8_t* out, hipStream_t st);
 void launch_sha_bytes(const uint8_t* msg, uint64_t len, uint8_t* out, hipStream_t st);
 
-// scans (scan.hip)
-size_t scan_temp_bytes(uint64_t n);
+// scans (scan.hip): single pass, tiles in ticket order, each tile's prefix
+// from its predecessors' published aggregates (decoupled look-back)
+uint64_t scan_ws_tiles(uint64_t n_max);          // tiles of the largest scan
+size_t scan_ws_bytes(uint64_t n_max);            // workspace bytes for scans of up to n_max items
+ScanWs scan_ws_at(void* base, uint64_t n_max, uint32_t* err, uint32_t* host_epoch);  // zeroed by the caller once, epoch 0
 // exclusive scans writing out[0..n] (out[n] = total)
-void scan_keep_u32(const uint8_t* flags, uint64_t n, uint32_t* out, void* tmp, hipStream_t st);
-void scan_u32(const uint32_t* in, uint64_t n, uint32_t* out, void* tmp, hipStream_t st);
-void scan_len_u64(const uint32_t* ids, const uint64_t* offsets, uint64_t n, uint64_t* out, void* tmp,
+void scan_keep_u32(const uint8_t* flags, uint64_t n, uint32_t* out, const ScanWs& ws, hipStream_t st);
+void scan_u32(const uint32_t* in, uint64_t n, uint32_t* out, const ScanWs& ws, hipStream_t st);
+void scan_len_u64(const uint32_t* ids, const uint64_t* offsets, uint64_t n, uint64_t* out, const ScanWs& ws,
                   hipStream_t st);
 void scan_wrap_pieces_u32(const uint32_t* ids, const uint64_t* offsets, const uint64_t* opre,
                           const uint64_t* src_doc_start, const uint16_t* source, const uint64_t* start, uint32_t T,
-                          uint64_t n, uint32_t* out, void* tmp, hipStream_t st);
+                          uint64_t n, uint32_t* out, const ScanWs& ws, hipStream_t st);
 void scan_pieces_u32(const uint32_t* ids, const uint64_t* offsets, const uint64_t* opre,
                      const uint64_t* src_doc_start, const uint16_t* source, const uint64_t* start, uint32_t T,
-                     uint64_t n, uint32_t* out, void* tmp, hipStream_t st);
+                     uint64_t n, uint32_t* out, const ScanWs& ws, hipStream_t st);
 
 }  // namespace dp

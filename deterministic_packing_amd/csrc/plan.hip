@@ -879,7 +879,7 @@ void launch_merge(Plan& p, hipStream_t st) {
         hipLaunchKernelGGL(k_group_bounds, dim3(blocks_for(p.n_kept)), dim3(256), 0, st, val, p.group, p.n_kept,
                            p.group_start);
     hipLaunchKernelGGL(k_group_suffix_min, dim3(1), dim3(1024), 0, st, p.group_start, p.G);
-    scan_len_u64(val, p.offsets, p.n_kept, p.gpre, p.hist, st);
+    scan_len_u64(val, p.offsets, p.n_kept, p.gpre, p.scan, st);
     // holes (which a correct merge never leaves) would read document 0
     if (p.n_kept) hipLaunchKernelGGL(k_fill_u32, dim3(blocks_for(p.n_kept)), dim3(256), 0, st, p.order, p.n_kept, 0u);
     if (p.n_kept) hipLaunchKernelGGL(k_merge, dim3(blocks_for(p.n_kept)), dim3(256), 0, st, p, val);
@@ -888,13 +888,13 @@ void launch_merge(Plan& p, hipStream_t st) {
 }
 
 void launch_piece_count(Plan& p, hipStream_t st) {
-    scan_len_u64(p.order, p.offsets, p.n_kept, p.opre, p.hist, st);
+    scan_len_u64(p.order, p.offsets, p.n_kept, p.opre, p.scan, st);
     if (p.wrap)
         scan_wrap_pieces_u32(p.order, p.offsets, p.opre, p.src_doc_start, p.source, p.start_tok, p.T, p.n_kept,
-                             p.piece_start, p.hist, st);
+                             p.piece_start, p.scan, st);
     else
         scan_pieces_u32(p.order, p.offsets, p.opre, p.src_doc_start, p.source, p.start_tok, p.T, p.n_kept,
-                        p.piece_start, p.hist, st);
+                        p.piece_start, p.scan, st);
 }
 
 void launch_pieces(Plan& p, hipStream_t st) {

@@ -1,5 +1,10 @@
-// scan.hip — device-wide exclusive prefix sums (three passes: tile sums,
-// scan of tile sums, tile scan plus offset).  Integer sums are exact and
+// scan.hip — device-wide exclusive prefix sums in one pass.  Tiles take
+// tickets in the order they start; a tile sums its items, publishes the sum,
+// and one wavefront looks back over the preceding tiles' published sums (64
+// at a time) until it meets a published inclusive prefix (decoupled
+// look-back); the tile then publishes its own inclusive prefix and writes its
+// items.  Status words pack state, epoch and value into 64 bits (ScanWs).  A tile only waits for tiles with lower tickets, which have started
+// and never wait for it, so every wait ends.  Integer sums are exact and
 // order-free, so the result does not depend on the launch shape.
 #include "dp_common.h"
 
@@ -7,7 +12,7 @@ namespace dp {
 namespace {
 
 constexpr int SB = 256;          // threads per block
-constexpr int SI = 8;            // items per thread
+constexpr int SI = 16;           // items per thread
 constexpr int STILE = SB * SI;   // items per tile
 
 template <typename T>
@@ -34,53 +39,81 @@ __device__ T block_exclusive(T v, T* lds_wave, T* total) {
     return before + x - v;
 }
 
-template <typename T, typename In>
-__global__ __launch_bounds__(SB) void k_tile_sums(In in, uint64_t n, T* sums) {
-    __shared__ T lw[SB / WAVE];
-    const uint64_t base = (uint64_t)blockIdx.x * STILE + (uint64_t)threadIdx.x * SI;
-    T s = 0;
-#pragma unroll
-    for (int j = 0; j < SI; ++j)
-        if (base + j < n) s += in(base + j);
-    T tot;
-    block_exclusive<T>(s, lw, &tot);
-    if (threadIdx.x == 0) sums[blockIdx.x] = tot;
+__device__ __forceinline__ uint64_t status_load(const uint64_t* w) {
+    return __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <typename T>
-__global__ __launch_bounds__(SB) void k_scan_sums(T* sums, uint64_t nb) {
+__device__ __forceinline__ void status_store(uint64_t* w, uint64_t v) {
+    __hip_atomic_store(w, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+constexpr uint64_t VALUE = (1ull << SCAN_VALUE_BITS) - 1;
+constexpr uint32_t LOOKBACK_POLLS = 1u << 20;  // far beyond any real wait: the tiles waited for are running
+
+template <typename T, typename In>
+__global__ __launch_bounds__(SB) void k_scan(In in, uint64_t n, T* out, ScanWs ws, uint32_t epoch) {
     __shared__ T lw[SB / WAVE];
-    T carry = 0;
-    for (uint64_t c = 0; c < nb; c += SB) {
-        const uint64_t i = c + threadIdx.x;
-        const T v = i < nb ? sums[i] : T(0);
-        T tot;
-        const T ex = block_exclusive<T>(v, lw, &tot);
-        if (i < nb) sums[i] = carry + ex;
-        carry += tot;
+    __shared__ uint64_t s_tile, s_prefix;
+    if (threadIdx.x == 0) {
+        const uint32_t t = atomicAdd(ws.ticket, 1u);
+        if (t == gridDim.x - 1) atomicExch(ws.ticket, 0u);  // every ticket handed out: zero for the next scan
+        s_tile = t;
     }
-    if (threadIdx.x == 0) sums[nb] = carry;
-}
-
-template <typename T, typename In>
-__global__ __launch_bounds__(SB) void k_tile_scan(In in, uint64_t n, const T* sums, T* out, uint64_t nb) {
-    __shared__ T lw[SB / WAVE];
-    const uint64_t base = (uint64_t)blockIdx.x * STILE + (uint64_t)threadIdx.x * SI;
+    __syncthreads();
+    const uint64_t tile = s_tile;
+    const uint64_t base = tile * STILE + (uint64_t)threadIdx.x * SI;
     T v[SI];
+#pragma unroll
+    for (int j = 0; j < SI; ++j) v[j] = (base + j < n) ? in(base + j) : T(0);  // every load issued first
     T s = 0;
 #pragma unroll
-    for (int j = 0; j < SI; ++j) {
-        v[j] = (base + j < n) ? in(base + j) : T(0);
-        s += v[j];
-    }
+    for (int j = 0; j < SI; ++j) s += v[j];
     T tot;
-    T run = block_exclusive<T>(s, lw, &tot) + sums[blockIdx.x];
+    const T ex = block_exclusive<T>(s, lw, &tot);
+    const uint64_t tag = (uint64_t)epoch << SCAN_VALUE_BITS;
+    const uint64_t AGG = (1ull << 62) | tag, INC = (2ull << 62) | tag;
+    if (threadIdx.x == 0) {
+        status_store(&ws.status[tile], (tile == 0 ? INC : AGG) | ((uint64_t)tot & VALUE));
+        if (tile == 0) s_prefix = 0;
+    }
+    if (tile > 0 && threadIdx.x < WAVE) {
+        // lane l reads tile j − l; lanes up to the first (nearest) tile with an
+        // inclusive prefix add their values: sums, then that prefix
+        const uint32_t lane = threadIdx.x;
+        uint64_t prefix = 0;
+        int64_t j = (int64_t)tile - 1;
+        uint32_t polls = 0;
+        while (true) {
+            const int64_t q = j - (int64_t)lane;
+            const uint64_t w = q >= 0 ? status_load(&ws.status[q]) : INC;  // before tile 0: a prefix of 0
+            const uint64_t state = w & ~VALUE;
+            if (!__all(state == AGG || state == INC)) {
+                if (++polls > LOOKBACK_POLLS) {
+                    if (lane == 0) atomicOr(ws.err, ERR_INTERNAL);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+                continue;
+            }
+            const uint64_t inc = __ballot(state == INC);
+            const uint32_t k = inc ? (uint32_t)__builtin_ctzll(inc) : WAVE;
+            prefix += wave_sum_u64(lane <= k ? (w & VALUE) : 0);
+            if (inc) break;
+            j -= WAVE;
+        }
+        if (lane == 0) {
+            status_store(&ws.status[tile], INC | ((prefix + (uint64_t)tot) & VALUE));
+            s_prefix = prefix;
+        }
+    }
+    __syncthreads();
+    T run = (T)s_prefix + ex;
 #pragma unroll
     for (int j = 0; j < SI; ++j) {
         if (base + j < n) out[base + j] = run;
         run += v[j];
     }
-    if (blockIdx.x == 0 && threadIdx.x == 0) out[n] = sums[nb];
+    if (tile == gridDim.x - 1 && threadIdx.x == 0) out[n] = (T)s_prefix + tot;
 }
 
 struct KeepIn {
@@ -148,45 +181,52 @@ struct WrapPieceCountIn {
 };
 
 template <typename T, typename In>
-void scan_impl(In in, uint64_t n, T* out, void* tmp, hipStream_t st) {
-    const uint64_t nb = (n + STILE - 1) / STILE;
-    T* sums = static_cast<T*>(tmp);
-    if (nb == 0) {
-        hipLaunchKernelGGL(k_scan_sums<T>, dim3(1), dim3(SB), 0, st, sums, (uint64_t)0);
-        hipLaunchKernelGGL((k_tile_scan<T, In>), dim3(1), dim3(SB), 0, st, in, (uint64_t)0,
-                           (const T*)sums, out, (uint64_t)0);
-        DP_HIP(hipGetLastError());
-        return;
+void scan_impl(In in, uint64_t n, T* out, const ScanWs& ws, hipStream_t st) {
+    const uint64_t tiles = n ? (n + STILE - 1) / STILE : 1;  // n = 0: one tile writes out[0] = 0
+    uint32_t epoch = ++*ws.epoch;  // a new epoch for every scan of this workspace
+    if (epoch >= (1u << (62 - SCAN_VALUE_BITS))) {  // wrapped: no stale status word may carry a reused epoch
+        launch_zero_u32(ws.ticket, ws.words, st);
+        epoch = *ws.epoch = 1;
     }
-    hipLaunchKernelGGL((k_tile_sums<T, In>), dim3(nb), dim3(SB), 0, st, in, n, sums);
-    hipLaunchKernelGGL(k_scan_sums<T>, dim3(1), dim3(SB), 0, st, sums, nb);
-    hipLaunchKernelGGL((k_tile_scan<T, In>), dim3(nb), dim3(SB), 0, st, in, n, (const T*)sums, out, nb);
+    hipLaunchKernelGGL((k_scan<T, In>), dim3((uint32_t)tiles), dim3(SB), 0, st, in, n, out, ws, epoch);
     DP_HIP(hipGetLastError());
 }
 
 }  // namespace
 
-size_t scan_temp_bytes(uint64_t n) { return ((n + STILE - 1) / STILE + 2) * sizeof(uint64_t); }
+uint64_t scan_ws_tiles(uint64_t n_max) { return (n_max + STILE - 1) / STILE + 1; }
 
-void scan_keep_u32(const uint8_t* flags, uint64_t n, uint32_t* out, void* tmp, hipStream_t st) {
-    scan_impl<uint32_t>(KeepIn{flags}, n, out, tmp, st);
+size_t scan_ws_bytes(uint64_t n_max) { return 8 + 8 * scan_ws_tiles(n_max); }  // [ticket, pad][status × tiles]
+
+ScanWs scan_ws_at(void* base, uint64_t n_max, uint32_t* err, uint32_t* host_epoch) {
+    ScanWs ws{};
+    ws.ticket = static_cast<uint32_t*>(base);
+    ws.status = base ? reinterpret_cast<uint64_t*>(static_cast<uint8_t*>(base) + 8) : nullptr;
+    ws.err = err;
+    ws.epoch = host_epoch;
+    ws.words = scan_ws_bytes(n_max) / 4;
+    return ws;
 }
-void scan_u32(const uint32_t* in, uint64_t n, uint32_t* out, void* tmp, hipStream_t st) {
-    scan_impl<uint32_t>(U32In{in}, n, out, tmp, st);
+
+void scan_keep_u32(const uint8_t* flags, uint64_t n, uint32_t* out, const ScanWs& ws, hipStream_t st) {
+    scan_impl<uint32_t>(KeepIn{flags}, n, out, ws, st);
 }
-void scan_len_u64(const uint32_t* ids, const uint64_t* offsets, uint64_t n, uint64_t* out, void* tmp,
+void scan_u32(const uint32_t* in, uint64_t n, uint32_t* out, const ScanWs& ws, hipStream_t st) {
+    scan_impl<uint32_t>(U32In{in}, n, out, ws, st);
+}
+void scan_len_u64(const uint32_t* ids, const uint64_t* offsets, uint64_t n, uint64_t* out, const ScanWs& ws,
                   hipStream_t st) {
-    scan_impl<uint64_t>(LenIn{ids, offsets}, n, out, tmp, st);
+    scan_impl<uint64_t>(LenIn{ids, offsets}, n, out, ws, st);
 }
 void scan_pieces_u32(const uint32_t* ids, const uint64_t* offsets, const uint64_t* opre,
                      const uint64_t* src_doc_start, const uint16_t* source, const uint64_t* start, uint32_t T,
-                     uint64_t n, uint32_t* out, void* tmp, hipStream_t st) {
-    scan_impl<uint32_t>(PieceCountIn{ids, offsets, opre, src_doc_start, source, start, T}, n, out, tmp, st);
+                     uint64_t n, uint32_t* out, const ScanWs& ws, hipStream_t st) {
+    scan_impl<uint32_t>(PieceCountIn{ids, offsets, opre, src_doc_start, source, start, T}, n, out, ws, st);
 }
 void scan_wrap_pieces_u32(const uint32_t* ids, const uint64_t* offsets, const uint64_t* opre,
                           const uint64_t* src_doc_start, const uint16_t* source, const uint64_t* start, uint32_t T,
-                          uint64_t n, uint32_t* out, void* tmp, hipStream_t st) {
-    scan_impl<uint32_t>(WrapPieceCountIn{ids, offsets, opre, src_doc_start, source, start, T}, n, out, tmp, st);
+                          uint64_t n, uint32_t* out, const ScanWs& ws, hipStream_t st) {
+    scan_impl<uint32_t>(WrapPieceCountIn{ids, offsets, opre, src_doc_start, source, start, T}, n, out, ws, st);
 }
 
 }  // namespace dp

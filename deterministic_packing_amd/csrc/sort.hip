@@ -197,7 +197,7 @@ __global__ __launch_bounds__(256) void k_perm_out(Plan p, const uint32_t* sorted
 }  // namespace
 
 void launch_keep_scan(Plan& p, hipStream_t st) {
-    scan_keep_u32(p.keep, p.n_docs, p.kept_pos, p.hist, st);
+    scan_keep_u32(p.keep, p.n_docs, p.kept_pos, p.scan, st);
     const uint64_t blocks = (p.n_docs + 255) / 256;
     hipLaunchKernelGGL(k_compact_keys, dim3((uint32_t)blocks), dim3(256), 0, st, p, p.key[0], p.val[0]);
     DP_HIP(hipGetLastError());
@@ -208,8 +208,7 @@ void launch_keep_scan(Plan& p, hipStream_t st) {
 // uniform.  Launches are sized by the bucket bound n/2 + G + 1 (a group of
 // n_g > 4 elements takes 2^b < n_g/2 buckets), so nothing is read back.
 uint32_t sort_pairs(uint64_t* const key[2], uint32_t* const val[2], const uint32_t* group, uint64_t n, uint32_t G,
-                    uint32_t* ws, uint32_t* err, hipStream_t st) {
-    (void)err;
+                    uint32_t* ws, const ScanWs& scan, hipStream_t st) {
     if (n == 0) return 0;
     const uint64_t NB = n / 2 + G + 1;  // bucket bound
     uint32_t* gcount = ws;                 // [G]
@@ -218,8 +217,6 @@ uint32_t sort_pairs(uint64_t* const key[2], uint32_t* const val[2], const uint32
     uint32_t* boff = gbase + G + 1;        // [NB + 1]
     uint32_t* bucket = boff + NB + 1;      // [n]
     uint32_t* ticket = bucket + n;         // [n]
-    void* tmp = ticket + n + 1;            // scan temp (8-byte aligned below)
-    tmp = reinterpret_cast<void*>((reinterpret_cast<uintptr_t>(tmp) + 7) & ~uintptr_t(7));
     launch_fill_u32(gcount, G + NB, 0u, st);
     const uint32_t blocks = (uint32_t)((n + 255) / 256);
     const size_t glds = G <= LDS_GROUPS ? sizeof(uint32_t) * G : 0;
@@ -228,7 +225,7 @@ uint32_t sort_pairs(uint64_t* const key[2], uint32_t* const val[2], const uint32
     hipLaunchKernelGGL(k_bucket_base, dim3(1), dim3(1024), 0, st, (const uint32_t*)gcount, G, gbase);
     hipLaunchKernelGGL(k_bucket_count, dim3(blocks), dim3(256), 0, st, key[0], val[0], group, n,
                        (const uint32_t*)gcount, (const uint32_t*)gbase, bcount, bucket, ticket);
-    scan_u32(bcount, NB, boff, tmp, st);
+    scan_u32(bcount, NB, boff, scan, st);
     hipLaunchKernelGGL(k_bucket_scatter, dim3(blocks), dim3(256), 0, st, key[0], val[0], n, (const uint32_t*)bucket,
                        (const uint32_t*)ticket, (const uint32_t*)boff, key[1], val[1]);
     hipLaunchKernelGGL(k_bucket_sort, dim3((uint32_t)((NB + 255) / 256)), dim3(256), 0, st, key[1], val[1],
@@ -239,7 +236,7 @@ uint32_t sort_pairs(uint64_t* const key[2], uint32_t* const val[2], const uint32
 
 // requires p.n_kept (host) to be set
 void launch_sort(Plan& p, hipStream_t st) {
-    p.sort_buf = sort_pairs(p.key, p.val, p.group, p.n_kept, p.G, p.hist, p.err, st);
+    p.sort_buf = sort_pairs(p.key, p.val, p.group, p.n_kept, p.G, p.hist, p.scan, st);
 }
 
 // requires perm_start (device) for the cycle; total = U·B
@@ -248,7 +245,7 @@ void launch_read_order(Plan& p, uint32_t cycle, uint64_t total, hipStream_t st) 
     const uint32_t blocks = (uint32_t)((total + 255) / 256);
     hipLaunchKernelGGL(k_window_keys, dim3(blocks), dim3(256), 0, st, p, cycle, total);
     DP_HIP(hipGetLastError());
-    const uint32_t buf = sort_pairs(p.wkey, p.wval, p.wgroup, total, p.S, p.hist, p.err, st);
+    const uint32_t buf = sort_pairs(p.wkey, p.wval, p.wgroup, total, p.S, p.hist, p.scan, st);
     hipLaunchKernelGGL(k_perm_out, dim3(blocks), dim3(256), 0, st, p, (const uint32_t*)p.wval[buf], total);
     DP_HIP(hipGetLastError());
 }
@@ -256,7 +253,7 @@ void launch_read_order(Plan& p, uint32_t cycle, uint64_t total, hipStream_t st) 
 // workspace of sort_pairs for n pairs in G groups, in uint32 words
 uint64_t sort_hist_words(uint64_t n, uint64_t G) {
     const uint64_t NB = n / 2 + G + 1;
-    return G + NB + (G + 1) + (NB + 1) + 2 * n + 1 + 2 + (scan_temp_bytes(NB) + 3) / 4 + 16;
+    return G + NB + (G + 1) + (NB + 1) + 2 * n + 1 + 16;
 }
 
 }  // namespace dp

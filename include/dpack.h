@@ -131,8 +131,9 @@ typedef struct pack_timings {
 } pack_timings;
 
 /* Configuration of a packing context.  Limits (PACK_E_INVAL otherwise):
- * 1 ≤ n_docs < 2^31; every document shorter than 2^32 tokens; offsets
- * monotone with doc_offsets[n_docs] ≤ n_tokens; 1 ≤ n_sources ≤ 4096;
+ * 1 ≤ n_docs < 2^31; n_tokens < 2^40; every document shorter than 2^32
+ * tokens; offsets monotone with doc_offsets[n_docs] ≤ n_tokens;
+ * 1 ≤ n_sources ≤ 4096;
  * source < n_sources; stratum < n_strata[source]; Σ n_strata ≤ 65536;
  * Σ share_weight in [1, 2^64); holdout_bp ≤ 10000; T a multiple of 64 in
  * [64, 2^20]; 1 ≤ B ≤ 2^20; world ≥ 1 divides B; rank < world; with a

@@ -68,6 +68,7 @@ def _cfg(**kw):
     ("n_docs", 0, dp.PACK_E_INVAL),
     ("flags", 32, dp.PACK_E_INVAL),
     ("n_sources", 0, dp.PACK_E_INVAL),
+    ("n_tokens", 1 << 40, dp.PACK_E_INVAL),  # scanned token totals stay below 2^40
 ])
 def test_init_rejects_bad_config_on_host(lib, field, value, code):
     cfg, keep = _cfg(**{field: value})
