@@ -560,11 +560,12 @@ void build_plan(pack_ctx& c) {
     c.timer.begin(PACK_PHASE_PIECES, st);
     dp::launch_piece_count(p, st);
     c.timer.end(st);
-    const uint32_t* h_pieces = d2h_staged(c, p.piece_start + p.n_kept, 1);
-    sync_staged(c);
-    p.n_pieces = *h_pieces;
-    if (p.n_pieces > p.cap_pieces) throw InvalError{"internal: piece bound exceeded"};
-    p.levels = bitlen(p.n_pieces) ? bitlen(p.n_pieces) : 1;
+    // the piece and window counts stay on the device until the end: the
+    // launches below are sized by their bound and the kernels read the counts
+    p.n_pieces_dev = p.piece_start + p.n_kept;
+    p.n_windows_dev = p.src_win_start + p.S;
+    p.n_pieces = p.n_windows = p.cap_pieces;
+    p.levels = bitlen(p.cap_pieces) ? bitlen(p.cap_pieces) : 1;
 
     // A5 pieces, next-fit by lifting, windows per source
     c.timer.begin(PACK_PHASE_PIECES, st);
@@ -574,10 +575,6 @@ void build_plan(pack_ctx& c) {
     dp::launch_lifting(p, st);
     dp::launch_window_count(p, st);
     c.timer.end(st);
-    const uint64_t* h_sws = d2h_staged(c, p.src_win_start, p.S + 1);
-    sync_staged(c);
-    c.src_win_start.assign(h_sws, h_sws + p.S + 1);
-    p.n_windows = c.src_win_start[p.S];
 
     // window table, A6 mixture, checks
     c.timer.begin(PACK_PHASE_WINDOWS, st);
@@ -609,8 +606,16 @@ void build_plan(pack_ctx& c) {
     const uint64_t* h_stats = d2h_staged(c, p.stats, 4ull * p.S);
     const uint64_t* h_checks = d2h_staged(c, p.checks, 2);
     const uint64_t* h_sps = d2h_staged(c, p.src_piece_start, p.S + 1);
+    const uint32_t* h_pieces = d2h_staged(c, p.piece_start + p.n_kept, 1);
+    const uint64_t* h_sws = d2h_staged(c, p.src_win_start, p.S + 1);
     h_err = d2h_staged(c, p.err, 1);
     sync_staged(c);
+    p.n_pieces_dev = nullptr;  // host counts from here on
+    p.n_windows_dev = nullptr;
+    p.n_pieces = *h_pieces;
+    if (p.n_pieces > p.cap_pieces) throw InvalError{"internal: piece bound exceeded"};
+    c.src_win_start.assign(h_sws, h_sws + p.S + 1);
+    p.n_windows = c.src_win_start[p.S];
     c.n_upd.assign(h_upd, h_upd + p.S);
     c.stats.assign(h_stats, h_stats + 4ull * p.S);
     c.checks.assign(h_checks, h_checks + 2);

@@ -205,7 +205,22 @@ struct Plan {
     // sizes known after the corresponding step (host copies)
     uint64_t n_kept, n_pieces, n_windows;
     uint64_t cap_pieces;          // allocation bound for pieces
+    // while pack_init runs, the piece and window counts stay on the device
+    // (n_pieces and n_windows then hold the bound cap_pieces); null afterwards
+    const uint32_t* n_pieces_dev;
+    const uint64_t* n_windows_dev;
 };
+
+// the plan's piece and window counts (from the device while pack_init runs),
+// never above the allocation bound
+__device__ inline uint64_t plan_pieces(const Plan& p) {
+    const uint64_t n = p.n_pieces_dev ? *p.n_pieces_dev : p.n_pieces;
+    return n < p.cap_pieces ? n : p.cap_pieces;
+}
+__device__ inline uint64_t plan_windows(const Plan& p) {
+    const uint64_t n = p.n_windows_dev ? *p.n_windows_dev : p.n_windows;
+    return n < p.cap_pieces ? n : p.cap_pieces;
+}
 
 // Global window index of slot j of update b of the current cycle: source s
 // = slot_src[j] contributes its (slot_k[j])-th window of the update, i.e. its

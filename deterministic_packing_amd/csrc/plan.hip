@@ -163,7 +163,8 @@ __global__ __launch_bounds__(256) void k_pieces(Plan p) {
     if (i >= p.n_kept) return;
     const uint32_t d = p.order[i];
     const uint32_t q0 = p.piece_start[i];
-    if (d >= p.n_docs || p.piece_start[i + 1] > p.n_pieces) {
+    const uint64_t n_pieces = p.n_pieces_dev ? *p.n_pieces_dev : p.n_pieces;
+    if (d >= p.n_docs || n_pieces > p.cap_pieces || p.piece_start[i + 1] > n_pieces) {
         atomicOr(p.err, ERR_INTERNAL);
         return;
     }
@@ -203,7 +204,7 @@ __global__ __launch_bounds__(256) void k_pieces(Plan p) {
         }
         if (o != L) atomicOr(p.err, ERR_INTERNAL);  // piece count and cut disagree
     }
-    if (i == p.n_kept - 1) p.pc_pre[p.n_pieces] = p.opre[p.n_kept];
+    if (i == p.n_kept - 1) p.pc_pre[n_pieces] = p.opre[p.n_kept];
 }
 
 __global__ void k_src_piece_start(Plan p) {
@@ -220,7 +221,7 @@ __global__ void k_src_piece_start(Plan p) {
 // lifting: jump[l][q] = next^(2^l)(q), END once past the source.
 __global__ __launch_bounds__(256) void k_next(Plan p) {
     const uint64_t q = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (q >= p.n_pieces) return;
+    if (q >= plan_pieces(p)) return;
     const uint32_t s = upper_bound_u64(p.src_piece_start, p.S + 1, q) - 1;
     const uint64_t pe = p.src_piece_start[s + 1];
     const uint64_t base = p.pc_pre[q];
@@ -241,10 +242,10 @@ __global__ __launch_bounds__(256) void k_next(Plan p) {
 // Levels l+1 .. l+k (k <= 3) from level l in one launch: level l+i is
 // next^(2^(l+i)) = level l applied 2^i times, so a thread follows level l
 // from q and records every power-of-two step (2, 4, 8 lookups).
-__global__ __launch_bounds__(256) void k_lift(const uint32_t* lev, uint32_t* out, uint64_t stride, uint32_t k,
-                                              uint64_t n) {
+__global__ __launch_bounds__(256) void k_lift(Plan p, const uint32_t* lev, uint32_t* out, uint64_t stride,
+                                              uint32_t k) {
     const uint64_t q = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (q >= n) return;
+    if (q >= plan_pieces(p)) return;
     uint32_t x = (uint32_t)q;
     uint32_t steps = 0;
     for (uint32_t i = 1; i <= k; ++i) {
@@ -285,14 +286,15 @@ __global__ __launch_bounds__(1024) void k_window_count(Plan p) {
 
 __global__ __launch_bounds__(256) void k_windows(Plan p) {
     const uint64_t gw = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (gw >= p.n_windows) return;
+    const uint64_t n_windows = plan_windows(p);
+    if (gw >= n_windows) return;
     const uint32_t s = upper_bound_u64(p.src_win_start, p.S + 1, gw) - 1;
     const uint64_t w = gw - p.src_win_start[s];
     uint32_t cur = (uint32_t)p.src_piece_start[s];
     for (uint32_t l = 0; l < p.levels; ++l)
         if ((w >> l) & 1) cur = p.jump[(uint64_t)l * p.cap_pieces + cur];
     p.win_first[gw] = cur;
-    if (gw == p.n_windows - 1) p.win_first[p.n_windows] = (uint32_t)p.n_pieces;
+    if (gw == n_windows - 1) p.win_first[n_windows] = (uint32_t)plan_pieces(p);
 }
 
 // Wrap packing: source s has ceil(Λ_s / T) windows (Λ_s its kept tokens), and
@@ -311,16 +313,17 @@ __global__ __launch_bounds__(1024) void k_wrap_window_count(Plan p) {
 
 __global__ __launch_bounds__(256) void k_wrap_windows(Plan p) {
     const uint64_t q = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (q >= p.n_pieces) return;
+    const uint64_t n_pieces = plan_pieces(p), n_windows = plan_windows(p);
+    if (q >= n_pieces) return;
     const uint32_t s = upper_bound_u64(p.src_piece_start, p.S + 1, q) - 1;
     // stream position of the piece, from the stream's start
     const uint64_t y = p.pc_pre[q] - p.opre[p.src_doc_start[s]] - (p.start_tok ? p.start_tok[s] : 0);
     if (y % p.T == 0) {
         const uint64_t gw = p.src_win_start[s] + y / p.T;
-        if (gw < p.n_windows) p.win_first[gw] = (uint32_t)q;
+        if (gw < n_windows) p.win_first[gw] = (uint32_t)q;
         else atomicOr(p.err, ERR_INTERNAL);
     }
-    if (q == p.n_pieces - 1) p.win_first[p.n_windows] = (uint32_t)p.n_pieces;
+    if (q == n_pieces - 1) p.win_first[n_windows] = (uint32_t)n_pieces;
 }
 
 // offsets of pieces in their window; real and learned positions per window
@@ -331,9 +334,9 @@ __global__ __launch_bounds__(256) void k_wrap_windows(Plan p) {
 // when the prompt covers the piece).
 __global__ __launch_bounds__(256) void k_window_stats(Plan p) {
     const uint64_t gw = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (gw >= p.n_windows) return;
+    if (gw >= plan_windows(p)) return;
     const uint32_t q0 = p.win_first[gw], q1 = p.win_first[gw + 1];
-    if (q0 >= q1 || q1 > p.n_pieces) {
+    if (q0 >= q1 || q1 > plan_pieces(p)) {
         atomicOr(p.err, ERR_INTERNAL);
         p.win_real[gw] = 0;
         p.win_learn[gw] = 0;
@@ -903,14 +906,15 @@ void launch_pieces(Plan& p, hipStream_t st) {
     DP_HIP(hipGetLastError());
 }
 
+// p.n_pieces: the piece count or its bound (the kernels read the count itself)
 void launch_lifting(Plan& p, hipStream_t st) {
     if (p.n_pieces == 0 || p.wrap) return;  // wrap packing cuts by position, no next-fit
     hipLaunchKernelGGL(k_next, dim3(blocks_for(p.n_pieces)), dim3(256), 0, st, p);
     for (uint32_t l = 1; l < p.levels;) {  // levels l .. l+k-1 from level l-1
         const uint32_t k = p.levels - l < 3 ? p.levels - l : 3;
-        hipLaunchKernelGGL(k_lift, dim3(blocks_for(p.n_pieces)), dim3(256), 0, st,
+        hipLaunchKernelGGL(k_lift, dim3(blocks_for(p.n_pieces)), dim3(256), 0, st, p,
                            (const uint32_t*)(p.jump + (uint64_t)(l - 1) * p.cap_pieces),
-                           p.jump + (uint64_t)l * p.cap_pieces, p.cap_pieces, k, p.n_pieces);
+                           p.jump + (uint64_t)l * p.cap_pieces, p.cap_pieces, k);
         l += k;
     }
     DP_HIP(hipGetLastError());
@@ -922,6 +926,7 @@ void launch_window_count(Plan& p, hipStream_t st) {
     DP_HIP(hipGetLastError());
 }
 
+// p.n_pieces, p.n_windows: the counts or their bound (the kernels read the counts)
 void launch_windows(Plan& p, hipStream_t st) {
     if (p.n_windows == 0) return;
     if (p.wrap) hipLaunchKernelGGL(k_wrap_windows, dim3(blocks_for(p.n_pieces)), dim3(256), 0, st, p);
