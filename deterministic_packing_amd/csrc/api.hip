@@ -335,7 +335,7 @@ size_t carve(pack_ctx& c, char* base) {
     c.next_win = k.take<uint64_t>(S);
     c.stream_next = k.take<uint64_t>(S);
     c.nstart = k.take<uint32_t>(S + 1);
-    c.dig_cap = 128 + 72 * S + 16 * K + 28;  // records 60·S, header ≤ 100 + 16·K, leaves 32·⌈S/16⌉
+    c.dig_cap = 128 + 72 * S + 16 * K + 28;  // records 60·S, header ≤ 100 + 16·K, leaves 32·⌈S/8⌉
     c.dig_buf = k.take<uint8_t>(c.dig_cap + 32);
     return k.off + ALIGN;
 }
@@ -1042,11 +1042,12 @@ int pack_cycle(pack_ctx* c, uint32_t cycle, pack_cycle_info* info) {
 
         // plan digest: SHA-256 of a little-endian header (mode, the recipe's
         // scalars, the cycle, its updates, two order-free sums over the plan)
-        // followed by the digests of the streams' 60-byte records, 16 streams
-        // to a leaf (one lane each), so the serial chain stays short for many
-        // streams.  The records, then the header, go to the device in one copy;
-        // the leaf digests are written after the header there.
-        constexpr uint32_t REC = 60, LEAF = 16;
+        // followed by the digests of the streams' 60-byte records, 8 streams
+        // to a leaf (one wavefront each), so the serial chain stays short: a
+        // leaf is 8 blocks, and the top hash grows by one block per 2 leaves.
+        // The records, then the header, go to the device in one copy; the
+        // leaf digests are written after the header there.
+        constexpr uint32_t REC = 60, LEAF = 8;
         std::vector<uint8_t> msg;
         for (uint32_t s = 0; s < S; ++s) {
             put(msg, c->weight[s], 8);

@@ -21,29 +21,6 @@ __device__ inline void store_digest(const uint32_t H[8], uint8_t* out) {
     o[1] = make_uint4(bswap32(H[4]), bswap32(H[5]), bswap32(H[6]), bswap32(H[7]));
 }
 
-struct Block {
-    uint4 v[4];
-};
-
-__device__ inline Block load_block(const uint4* p) {
-    Block b;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) b.v[i] = p[i];
-    return b;
-}
-
-__device__ inline void compress_block(uint32_t H[8], const Block& b) {
-    uint32_t W[16];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        W[4 * q + 0] = bswap32(b.v[q].x);
-        W[4 * q + 1] = bswap32(b.v[q].y);
-        W[4 * q + 2] = bswap32(b.v[q].z);
-        W[4 * q + 3] = bswap32(b.v[q].w);
-    }
-    sha256_compress(H, W);
-}
-
 // One lane per window (64 windows per wave, one wave per workgroup).  The
 // record is T words of tok, T of pos, T of doc, then T/4 words of mask bytes;
 // with T a multiple of 64 every 64-byte block lies in one array, and so does
@@ -724,17 +701,92 @@ __global__ __launch_bounds__(64) void k_batch_fp_var(const uint8_t* digests, con
     sha_bytes(digests + 32ull * x0, 32ull * (x1 - x0), out + 32ull * b);
 }
 
-__global__ void k_sha_bytes(const uint8_t* msg, uint64_t len, uint8_t* out) {
-    if (threadIdx.x == 0 && blockIdx.x == 0) sha_bytes(msg, len, out);
+// SHA-256 of a byte string (4-byte aligned start) by one whole wavefront,
+// for the plan digest's chains: lane l builds padded block b0 + l (64 blocks
+// at a time), expands its message schedule and stores the 64 words with the
+// round constants added to LDS (kw, 64 × 65 words: a padded row per lane);
+// lane 0 then runs the compressions on those words, so the serial chain holds
+// only the round function (about 14 of the 22 instructions of a round).
+constexpr uint32_t KW_ROW = 65;
+
+__device__ __forceinline__ void sha256_compress_kw(uint32_t H[8], const uint32_t* kw) {
+    uint32_t a = H[0], b = H[1], c = H[2], d = H[3], e = H[4], f = H[5], g = H[6], h = H[7];
+#pragma unroll
+    for (int t = 0; t < 64; ++t) {
+        const uint32_t S1 = __builtin_amdgcn_bitop3_b32(rotr32(e, 6), rotr32(e, 11), rotr32(e, 25), 0x96);
+        const uint32_t ch = __builtin_amdgcn_bitop3_b32(e, f, g, 0xCA);
+        const uint32_t T1 = h + kw[t] + ch + S1;
+        const uint32_t S0 = __builtin_amdgcn_bitop3_b32(rotr32(a, 2), rotr32(a, 13), rotr32(a, 22), 0x96);
+        const uint32_t mj = __builtin_amdgcn_bitop3_b32(a, b, c, 0xE8);
+        h = g; g = f; f = e; e = d + T1;
+        d = c; c = b; b = a; a = T1 + S0 + mj;
+    }
+    H[0] += a; H[1] += b; H[2] += c; H[3] += d;
+    H[4] += e; H[5] += f; H[6] += g; H[7] += h;
 }
 
-// lane j: SHA-256 of msg[j·chunk, min((j+1)·chunk, len)) into out + 32·j
-__global__ __launch_bounds__(64) void k_sha_chunks(const uint8_t* msg, uint64_t len, uint32_t chunk, uint8_t* out) {
-    const uint64_t j = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const uint64_t x0 = j * chunk;
-    if (x0 >= len) return;
+// Word i of padded block b of an len-byte message (big-endian).
+__device__ __forceinline__ uint32_t padded_word(const uint8_t* msg, uint64_t len, uint64_t nblk, uint64_t b,
+                                                uint32_t i) {
+    if (b == nblk - 1 && i >= 14) return i == 14 ? (uint32_t)((len * 8) >> 32) : (uint32_t)(len * 8);
+    const uint64_t x = 64 * b + 4 * i;
+    if (x + 4 <= len) return bswap32(reinterpret_cast<const uint32_t*>(msg)[x / 4]);
+    uint32_t word = 0;
+    for (uint32_t k = 0; k < 4; ++k) {
+        const uint64_t at = x + k;
+        word = (word << 8) | (at < len ? msg[at] : (at == len ? 0x80u : 0u));
+    }
+    return word;
+}
+
+__device__ void sha_bytes_wave(const uint8_t* msg, uint64_t len, uint8_t* out, uint32_t* kw) {
+    const uint32_t lane = lane_id();
+    const uint64_t nblk = (len + 9 + 63) / 64;
+    uint32_t H[8];
+    sha256_init(H);
+    for (uint64_t b0 = 0; b0 < nblk; b0 += WAVE) {
+        const uint64_t b = b0 + lane;
+        if (b < nblk) {
+            uint32_t W[16];
+#pragma unroll
+            for (uint32_t i = 0; i < 16; ++i) W[i] = padded_word(msg, len, nblk, b, i);
+            uint32_t* row = kw + lane * KW_ROW;
+#pragma unroll
+            for (int t = 0; t < 64; ++t) {
+                uint32_t w;
+                if (t < 16) {
+                    w = W[t];
+                } else {
+                    const uint32_t w15 = W[(t + 1) & 15], w2 = W[(t + 14) & 15];
+                    const uint32_t s0 = __builtin_amdgcn_bitop3_b32(rotr32(w15, 7), rotr32(w15, 18), w15 >> 3, 0x96);
+                    const uint32_t s1 = __builtin_amdgcn_bitop3_b32(rotr32(w2, 17), rotr32(w2, 19), w2 >> 10, 0x96);
+                    w = W[t & 15] + s0 + W[(t + 9) & 15] + s1;
+                    W[t & 15] = w;
+                }
+                row[t] = w + sha_k(t);
+            }
+        }
+        __syncthreads();  // one wavefront per workgroup: its schedule rows are in LDS
+        if (lane == 0) {
+            const uint64_t n = nblk - b0 < WAVE ? nblk - b0 : WAVE;
+            for (uint64_t k = 0; k < n; ++k) sha256_compress_kw(H, kw + k * KW_ROW);
+        }
+        __syncthreads();  // the rows are consumed before the next group overwrites them
+    }
+    if (lane == 0) store_digest(H, out);
+}
+
+__global__ __launch_bounds__(WAVE) void k_sha_bytes(const uint8_t* msg, uint64_t len, uint8_t* out) {
+    __shared__ uint32_t kw[WAVE * KW_ROW];
+    sha_bytes_wave(msg, len, out, kw);
+}
+
+// workgroup j (one wavefront): SHA-256 of msg[j·chunk, min((j+1)·chunk, len)) into out + 32·j
+__global__ __launch_bounds__(WAVE) void k_sha_chunks(const uint8_t* msg, uint64_t len, uint32_t chunk, uint8_t* out) {
+    __shared__ uint32_t kw[WAVE * KW_ROW];
+    const uint64_t x0 = (uint64_t)blockIdx.x * chunk;
     const uint64_t x1 = x0 + chunk < len ? x0 + chunk : len;
-    sha_bytes(msg + x0, x1 - x0, out + 32 * j);
+    sha_bytes_wave(msg + x0, x1 - x0, out + 32ull * blockIdx.x, kw);
 }
 
 }  // namespace
@@ -764,8 +816,8 @@ void launch_batch_fp_var(const uint8_t* digests, const uint64_t* slot0, uint32_t
 }
 
 void launch_sha_chunks(const uint8_t* msg, uint64_t len, uint32_t chunk, uint8_t* out, hipStream_t st) {
-    const uint64_t n = (len + chunk - 1) / chunk;
-    if (n) hipLaunchKernelGGL(k_sha_chunks, dim3((uint32_t)((n + 63) / 64)), dim3(64), 0, st, msg, len, chunk, out);
+    const uint64_t n = (len + chunk - 1) / chunk;  // one workgroup per chunk
+    if (n) hipLaunchKernelGGL(k_sha_chunks, dim3((uint32_t)n), dim3(WAVE), 0, st, msg, len, chunk, out);
     DP_HIP(hipGetLastError());
 }
 

@@ -1283,14 +1283,14 @@ int or_batch_packed(const or_plan *p, uint32_t step, uint32_t n_steps, uint32_t 
 /* Plan digest of the current cycle: SHA-256 over a little-endian header (the
  * mode, the recipe's scalars, the cycle, its updates and two order-free sums
  * that change with the document order and content) followed by the digests of
- * the streams' records, 16 streams to a leaf.  A stream's record (60 bytes):
+ * the streams' records, 8 streams to a leaf.  A stream's record (60 bytes):
  * weight, hold-out rate, strata, windows per update, windows in the stream,
  * kept documents and tokens, the cycle's first window, the stream's first
  * token (0 without stream starts).  A resume whose digest differs was planned
  * from another recipe or order ([NS] Training: a resume with another sample
  * order is refused). */
 #define OR_DIGEST_RECORD 60u
-#define OR_DIGEST_LEAF 16u
+#define OR_DIGEST_LEAF 8u
 
 static void put(uint8_t **w, uint64_t v, int bytes)
 {
@@ -1333,7 +1333,7 @@ int or_plan_digest(const or_plan *p, uint8_t out[32])
     put(&w, c->T, 4); put(&w, c->B, 4); put(&w, c->seed, 8); put(&w, S, 4); put(&w, c->pad_token, 4);
     put(&w, (uint64_t)p->cycle, 4); put(&w, p->U, 4);
     put(&w, p->order_check, 8); put(&w, p->hash_check, 8);
-    for (uint32_t j = 0; j < leaves; j++) {  /* the records' digests, 16 streams to a leaf */
+    for (uint32_t j = 0; j < leaves; j++) {  /* the records' digests, 8 streams to a leaf */
         const uint32_t s0 = j * OR_DIGEST_LEAF, s1 = s0 + OR_DIGEST_LEAF < S ? s0 + OR_DIGEST_LEAF : S;
         or_sha256(rec + (uint64_t)s0 * OR_DIGEST_RECORD, (uint64_t)(s1 - s0) * OR_DIGEST_RECORD, w);
         w += 32;

@@ -22,7 +22,7 @@ is the library's own definition, stated here field by field and rebuilt with
   trained before the cycle u64; "LANE" + lanes u32; "STRT"; "SEGS" +
   arrivals u32; then T u32, B u32, seed u64, streams u32, pad token u32,
   cycle u32, updates u32, order check u64, hash check u64; then one 32-byte
-  leaf per 16 streams: SHA-256 of those streams' records.
+  leaf per 8 streams: SHA-256 of those streams' records.
 
 A one-byte change to a record field's width or order, to a mode word, or to
 the leaf grouping in the oracle fails here.
@@ -94,7 +94,7 @@ def rebuild(plan: "oracle.Plan", info: "oracle.CycleInfo") -> bytes:
         head += b"SEGS" + struct.pack("<I", c.n_segments)
     head += struct.pack("<IIQIIIIQQ", c.T, c.B, c.seed, S, c.pad_token, info.cycle, info.n_updates,
                         order_check, hash_check)
-    leaves = b"".join(hashlib.sha256(records[60 * s0:60 * min(s0 + 16, S)]).digest() for s0 in range(0, S, 16))
+    leaves = b"".join(hashlib.sha256(records[60 * s0:60 * min(s0 + 8, S)]).digest() for s0 in range(0, S, 8))
     return hashlib.sha256(head + leaves).digest()
 
 
@@ -114,7 +114,7 @@ def _cases():
     yield "lanes", _base(4, B=8).replace(lanes=4)
     seg = _base(5)
     yield "arrivals", seg.replace(segment=(np.arange(seg.n_docs) % 3).astype(np.uint16), n_segments=3)
-    # more than 16 streams: several leaves, the last one partial
+    # more than 8 streams: several leaves, the last one partial
     yield "many_streams", _base(6, n_sources=37, n_docs=1500, B=40)
     yield "lanes_many_streams", _base(7, n_sources=9, n_docs=1500, B=16).replace(lanes=4, cumulative=True)
     # stream starts: go on from the tokens the first cycle reported
