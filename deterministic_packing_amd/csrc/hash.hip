@@ -158,7 +158,8 @@ constexpr uint32_t NO_END = 0xFFFFFFFFu;  // no further document start within re
 
 // What a wave-tile needs besides its tokens: the documents lo and hi holding
 // its first token and the next tile's (tile table), off[lo], and lane k's
-// offset off[lo + k] (clamped to off[D]), which serves tiles of hi − lo < WAVE.
+// offset off[lo + k] for k ≤ hi − lo (clamped to off[D]), which serves tiles
+// of hi − lo < WAVE.
 // Every load is a vector load (lane 0 and 1 read the two table entries; lane
 // 0's offset is off[lo]), counted in order with the token loads, so waiting
 // for one tile's entries never waits for loads issued after them.
@@ -174,7 +175,8 @@ __device__ __forceinline__ void tile_table(const uint32_t* first, uint64_t t, Ti
 __device__ __forceinline__ void tile_offsets(const Plan& p, TileDocs& m) {
     m.lo = (uint32_t)__builtin_amdgcn_readlane((int)m.tv, 0);
     m.hi = (uint32_t)__builtin_amdgcn_readlane((int)m.tv, 1);
-    m.o = p.offsets[std::min<uint64_t>(m.lo + lane_id(), p.n_docs)];
+    // only the lanes of the tile's documents load (a tile inside one document: lane 0 alone)
+    m.o = lane_id() <= m.hi - m.lo ? p.offsets[std::min<uint64_t>(m.lo + lane_id(), p.n_docs)] : 0;
 }
 
 __device__ __forceinline__ void tile_ready(TileDocs& m) { m.olo = readlane64(m.o, 0); }
