@@ -162,9 +162,9 @@ __device__ __forceinline__ void hash_outputs(uint32_t T, const EmitArgs& a, uint
 // (hash_outputs), reading a chunk only once it is published.  Emission is
 // memory traffic and a little integer work, so it hides under the hashing
 // waves' SHA-256 chains, the step's longest serial dependency, instead of
-// running as a kernel of its own before them.  It serves launches of at most
-// 256 workgroups (65,536 windows, one hashing wave per SIMD); larger launches
-// use k_emit_digest below.
+// running as a kernel of its own before them.  It serves launches of 513 to
+// 1,024 waves (one hashing wave per SIMD); smaller launches use the ring
+// pairs and larger ones k_emit_digest below.
 //
 // Piece view (plan array pc_emit, written with the window offsets): position
 // t of piece q holds token base_q + t, position id t − f_q, document id d_q,
@@ -686,6 +686,184 @@ __device__ __forceinline__ void sha_bytes(const uint8_t* msg, uint64_t len, uint
     }
 }
 
+// ---------------------------------------------------------------- emission with the schedule beside the rounds
+// For launches of at most 1,024 waves (a hashing wave's chain is then the
+// step's critical path): pairs of waves.  The emitting wave of a pair makes
+// its 64 windows' records itself, block by block (as k_emit_digest does),
+// stores them, and for each block also expands the SHA-256 message schedule
+// and writes its 64 words, round constants added, to a ring of RING slots in
+// LDS; the hashing wave runs only the rounds, reading each round's word from
+// its row, and hands the slot back.  A lone wavefront runs the rounds alone
+// at about 1.7 µs per 64-byte block against 2.5 µs for the whole compression
+// (the message schedule is a third of it), and neither wave reads a record
+// back.  PAIRS = 1 or 2: one workgroup per CU (it reserves more than half of
+// the LDS), waves 0 .. PAIRS−1 hash, the next PAIRS emit, so with waves placed
+// on SIMDs in turn every wave has a SIMD of its own (launches of at most 256
+// and 512 waves).  (Four pairs per CU, one hashing and one emitting wave per
+// SIMD, measured slower than the paired kernel above.)
+constexpr uint32_t RING = 2;          // schedule slots per pair
+constexpr uint32_t RING_ROW = 65;     // words per lane's row (64, padded: no bank conflicts)
+constexpr uint32_t RING_SLOT = 64 * RING_ROW;
+
+__device__ __forceinline__ void publish_count(uint32_t* c, uint32_t v) {
+    __hip_atomic_store(c, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// The message schedule of block X (16 big-endian words), round constants added, into row[0..63].
+__device__ __forceinline__ void schedule_row(uint32_t (&X)[16], uint32_t* row) {
+#pragma unroll
+    for (int t = 0; t < 64; ++t) {
+        uint32_t w;
+        if (t < 16) {
+            w = X[t];
+        } else {
+            const uint32_t w15 = X[(t + 1) & 15], w2 = X[(t + 14) & 15];
+            const uint32_t s0 = __builtin_amdgcn_bitop3_b32(rotr32(w15, 7), rotr32(w15, 18), w15 >> 3, 0x96);
+            const uint32_t s1 = __builtin_amdgcn_bitop3_b32(rotr32(w2, 17), rotr32(w2, 19), w2 >> 10, 0x96);
+            w = X[t & 15] + s0 + X[(t + 9) & 15] + s1;
+            X[t & 15] = w;
+        }
+        row[t] = w + sha_k(t);
+    }
+}
+
+__device__ __forceinline__ void rounds_from_row(uint32_t H[8], const uint32_t* row) {
+    uint32_t a = H[0], b = H[1], c = H[2], d = H[3], e = H[4], f = H[5], g = H[6], h = H[7];
+#pragma unroll
+    for (int t = 0; t < 64; ++t) {
+        const uint32_t S1 = __builtin_amdgcn_bitop3_b32(rotr32(e, 6), rotr32(e, 11), rotr32(e, 25), 0x96);
+        const uint32_t ch = __builtin_amdgcn_bitop3_b32(e, f, g, 0xCA);
+        const uint32_t T1 = h + row[t] + ch + S1;
+        const uint32_t S0 = __builtin_amdgcn_bitop3_b32(rotr32(a, 2), rotr32(a, 13), rotr32(a, 22), 0x96);
+        const uint32_t mj = __builtin_amdgcn_bitop3_b32(a, b, c, 0xE8);
+        h = g; g = f; f = e; e = d + T1;
+        d = c; c = b; b = a; a = T1 + S0 + mj;
+    }
+    H[0] += a; H[1] += b; H[2] += c; H[3] += d;
+    H[4] += e; H[5] += f; H[6] += g; H[7] += h;
+}
+
+// Hashing wave of a pair: block b's row is ready once prod ≥ b + 1; the slot
+// goes back (cons = b + 1) when the rounds have read it.
+__device__ __forceinline__ void ring_hash(const EmitArgs& a, uint64_t n_windows, uint64_t w0, uint32_t lane,
+                                          uint32_t nblk, const uint32_t* ring, uint32_t* prod, uint32_t* cons,
+                                          uint32_t* err, uint32_t opts) {
+    uint32_t H[8];
+    sha256_init(H);
+#pragma unroll 1
+    for (uint32_t b = 0; b < nblk; ++b) {
+        wait_progress(prod, b + 1, err, opts);
+        rounds_from_row(H, ring + (b % RING) * RING_SLOT + lane * RING_ROW);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");  // the row's reads are complete
+        if (lane == 0) publish_count(cons, b + 1);
+    }
+    if (w0 + lane < n_windows) store_digest(H, a.digests + 32 * (w0 + lane));
+}
+
+// Emitting wave of a pair: the records of windows w0 .. w0+63 (one lane each),
+// stored like k_emit_digest's, each block's schedule into the ring.
+__device__ __forceinline__ void ring_emit(const Plan& p, const EmitArgs& a, uint64_t n_windows, uint64_t w0,
+                                          uint32_t lane, uint32_t* ring, uint32_t* prod, const uint32_t* cons,
+                                          uint32_t* err, uint32_t opts) {
+    const bool valid = w0 + lane < n_windows;
+    const uint64_t w = valid ? w0 + lane : n_windows - 1;  // lanes past the end mirror the last window
+    uint32_t i_, jj_, per_;
+    const uint64_t gw = out_window(p, a, w, &i_, &jj_, &per_);
+    const uint32_t q0 = p.win_first[gw], q1 = p.win_first[gw + 1], real = p.win_real[gw];
+    const uint32_t T = p.T;
+    const bool ok = q1 > q0 && real <= T;  // every window holds a piece and at most T positions (else a library bug)
+    if (!ok) atomicOr(p.err_batch, ERR_INTERNAL);
+    uint32_t blk = 0;  // blocks handed to the hashing wave
+    auto to_ring = [&](uint32_t (&X)[16]) {  // X: big-endian words of the next block
+        if (blk >= RING) wait_progress(cons, blk + 1 - RING, err, opts);  // its slot is free
+        schedule_row(X, ring + (blk % RING) * RING_SLOT + lane * RING_ROW);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        ++blk;
+        if (lane == 0) publish_count(prod, blk);
+    };
+    ECursor c;
+    uint32_t P[16];
+    auto finish = [&](uint32_t (&W)[16], uint8_t* dst, uint32_t k, uint32_t n_arr) {
+        if ((k & 1) == 0 && k + 1 < n_arr) {  // first half of a 128-byte line: stored with the second
+#pragma unroll
+            for (int e = 0; e < 16; ++e) P[e] = W[e];
+        } else if (valid && ok) {
+            if (k & 1) store16(dst - 64, P);
+            store16(dst, W);
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) W[e] = bswap32(W[e]);
+        to_ring(W);
+    };
+    const uint32_t nb = T / 16;
+    const uint32_t q0c = ok ? q0 : 0, q1c = ok ? q1 : 1, realc = ok ? real : 0;  // a window that fails the check is
+    uint32_t va[16], vb[16], bw;                                                // made as padding (never stored)
+    c.restart(p, q0c, q1c, realc);
+    issue_tokens(p, c, 0, q1c, realc, va, vb, bw);
+    uint8_t* const tok = reinterpret_cast<uint8_t*>(a.tok + w * T);
+#pragma unroll 1
+    for (uint32_t k = 0; k < nb; ++k) {
+        uint32_t W[16];
+#pragma unroll
+        for (uint32_t e = 0; e < 16; ++e) W[e] = 16 * k + e >= bw ? vb[e] : va[e];
+        if (k + 1 < nb) issue_tokens(p, c, 16 * (k + 1), q1c, realc, va, vb, bw);
+        finish(W, tok + 64 * k, k, nb);
+    }
+    uint8_t* const pos = reinterpret_cast<uint8_t*>(a.pos + w * T);
+    c.restart(p, q0c, q1c, realc);
+#pragma unroll 1
+    for (uint32_t k = 0; k < nb; ++k) {
+        uint32_t W[16];
+        id_block<1>(p, c, 16 * k, q1c, realc, W);
+        finish(W, pos + 64 * k, k, nb);
+    }
+    uint8_t* const doc = reinterpret_cast<uint8_t*>(a.doc + w * T);
+    c.restart(p, q0c, q1c, realc);
+#pragma unroll 1
+    for (uint32_t k = 0; k < nb; ++k) {
+        uint32_t W[16];
+        id_block<2>(p, c, 16 * k, q1c, realc, W);
+        finish(W, doc + 64 * k, k, nb);
+    }
+    uint8_t* const mask = a.mask + w * T;
+    c.restart(p, q0c, q1c, realc);
+#pragma unroll 1
+    for (uint32_t k = 0; k < T / 64; ++k) {
+        uint32_t W[16];
+        mask_block(p, c, 64 * k, q1c, realc, W);
+        finish(W, mask + 64 * k, k, T / 64);
+    }
+    // 13·T bytes is a multiple of 64: one padding block
+    uint32_t X[16];
+    X[0] = 0x80000000u;
+#pragma unroll
+    for (int i = 1; i < 14; ++i) X[i] = 0;
+    const uint64_t bits = 13ull * T * 8ull;
+    X[14] = (uint32_t)(bits >> 32);
+    X[15] = (uint32_t)bits;
+    to_ring(X);
+}
+
+template <uint32_t PAIRS>
+__global__ __launch_bounds__(128 * PAIRS) void k_emit_ring(Plan p, EmitArgs a, uint64_t n_windows) {
+    static_assert(PAIRS <= 2, "at most two pairs: every wave on a SIMD of its own");
+    // [PAIRS][RING] slots, then prod[PAIRS], cons[PAIRS], padded to 96 KB (one workgroup per CU)
+    __shared__ uint32_t ring_lds[96 * 1024 / 4];
+    const uint32_t wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+    const bool hasher = wave < PAIRS;  // waves 0 .. PAIRS−1 hash, the next PAIRS emit (wave i on SIMD i mod 4)
+    const uint32_t pair = hasher ? wave : wave - PAIRS;
+    uint32_t* ring = ring_lds + pair * RING * RING_SLOT;
+    uint32_t* prod = ring_lds + PAIRS * RING * RING_SLOT;
+    uint32_t* cons = prod + PAIRS;
+    if (threadIdx.x < 2 * PAIRS) prod[threadIdx.x] = 0;
+    __syncthreads();
+    const uint64_t w0 = ((uint64_t)blockIdx.x * PAIRS + pair) * 64;
+    if (w0 >= n_windows) return;  // both waves of the pair
+    const uint32_t nblk = 13 * (p.T / 64) + 1;
+    if (hasher) ring_hash(a, n_windows, w0, lane, nblk, ring, prod + pair, cons + pair, p.err_batch, p.test_opts);
+    else ring_emit(p, a, n_windows, w0, lane, ring, prod + pair, cons + pair, p.err_batch, p.test_opts);
+}
+
 __global__ __launch_bounds__(64) void k_batch_fp(const uint8_t* digests, uint32_t B, uint32_t n, uint8_t* out) {
     const uint32_t b = blockIdx.x * blockDim.x + threadIdx.x;
     if (b >= n) return;
@@ -791,11 +969,21 @@ __global__ __launch_bounds__(WAVE) void k_sha_chunks(const uint8_t* msg, uint64_
 
 }  // namespace
 
+// Launch shape by the number of waves of 64 windows (each a chain of 13·T/64 + 1
+// compressions): at most 256, one ring pair per CU; at most 512, two (the
+// hashing waves alone on their SIMDs); at most 1,024, the paired kernel with
+// one hashing wave per SIMD (measured faster there than four ring pairs per
+// CU, whose emitting waves share the hashing waves' SIMDs); above, each lane
+// its own record (throughput-bound).
 void launch_emit_sha(const Plan& p, const EmitArgs& a, hipStream_t st) {
     const uint64_t n = a.n_out;  // < 2^31 windows: at most 2^23 workgroups
     const uint64_t waves = (n + 63) / 64;
     if (!n) return;
-    if (waves <= 1024)  // no more windows than one hashing wave per SIMD (256 CUs x 4) covers
+    if (waves <= 256)
+        hipLaunchKernelGGL(k_emit_ring<1>, dim3((uint32_t)waves), dim3(128), 0, st, p, a, n);
+    else if (waves <= 512)
+        hipLaunchKernelGGL(k_emit_ring<2>, dim3((uint32_t)((waves + 1) / 2)), dim3(256), 0, st, p, a, n);
+    else if (waves <= 1024)
         hipLaunchKernelGGL(k_emit_sha, dim3((uint32_t)((n + 255) / 256)), dim3(64 * FWAVES), 0, st, p, a, n);
     else
         hipLaunchKernelGGL(k_emit_digest, dim3((uint32_t)((waves + GWAVES - 1) / GWAVES)), dim3(64 * GWAVES), 0, st,

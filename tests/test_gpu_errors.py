@@ -34,13 +34,23 @@ def _corpus(seed, **mode):
     return c.replace(**mode)
 
 
-@pytest.mark.parametrize("mode", [{}, {"wrap": True, "read_random": True}])
-def test_digest_wait_that_gives_up_is_reported(mode):
-    c = _corpus(501, **mode)
-    say("digest wait give-up", mode)
+def _large_corpus(seed, **mode):  # a launch of 513 to 1,024 waves: the paired kernel
+    c = random_small(seed, n_docs=40000, n_sources=3, max_strata=2, T=64, B=640, max_len=120, bp_max=500)
+    return c.replace(**mode)
+
+
+@pytest.mark.parametrize("mode,large", [({}, False), ({"wrap": True, "read_random": True}, False), ({}, True)])
+def test_digest_wait_that_gives_up_is_reported(mode, large):
+    """Both kernels with bounded waits: the ring pairs (launches of at most 512
+    waves) and the paired kernel (513 to 1,024 waves, here 600)."""
+    c = _large_corpus(505, **mode) if large else _corpus(501, **mode)
+    upc = 60 if large else 3
+    say("digest wait give-up", mode, "large" if large else "small")
     op = oracle.Plan(c)
-    oi = op.cycle(0, updates_per_cycle=3)
-    pk = dp.Packer(c.replace(updates_per_cycle=3))
+    oi = op.cycle(0, updates_per_cycle=upc)
+    if large:
+        assert 512 * 64 < oi.n_updates * c.B <= 1024 * 64
+    pk = dp.Packer(c.replace(updates_per_cycle=upc))
     pk.cycle(0)
     n = oi.n_updates
     good = to_np(pk.batch(0, n))  # batch() ends with pack_status: no failure
