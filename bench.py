@@ -210,8 +210,12 @@ def main():
         # window SHA-256: (13T/64 + 1) compressions per window
         "digest": ("alu", SHA_OPS_PER_BLOCK * n_windows * (13 * T // 64 + 1), "TOP/s"),
     }
-    # bytes the digest kernel moves: its 13T-byte records read back, plus the emission when fused
-    digest_bytes = 13.0 * positions + (emit_bytes if fused else 0.0)
+    # bytes the digest kernel moves: the emission when fused, a 32-byte digest per window, and the
+    # 13T-byte records read back where the paired kernel hashes them from the outputs (launches of
+    # 513 to 1,024 waves of 64 windows; the ring pairs and the own-record kernel read nothing back)
+    waves = (n_windows + 63) // 64
+    read_back = 512 < waves <= 1024
+    digest_bytes = (13.0 * positions if read_back else 0.0) + (emit_bytes if fused else 0.0) + 32.0 * n_windows
     kernels = {}
     for k in phase_ms:
         if phase_calls[k] == 0:
