@@ -41,40 +41,22 @@ __global__ __launch_bounds__(256) void k_zero_u64(uint64_t* a, uint64_t n) {
     if (i < n) a[i] = 0;
 }
 
+// group_start[g] for every group: the sorted documents come group by group,
+// so the element where the group changes writes the start of its group and of
+// the empty groups just before it (the first element from group 0 on, the last
+// one the empty groups after it, up to group_start[G] = n).  Each entry has
+// one writer.  Also clears the merged order (holes, which a correct merge
+// never leaves, would then read document 0).
 __global__ __launch_bounds__(256) void k_group_bounds(const uint32_t* val, const uint32_t* group, uint64_t n,
-                                                      uint32_t* gs) {
+                                                      uint32_t G, uint32_t* gs, uint32_t* order) {
     const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n) return;
+    order[i] = 0;
     const uint32_t g = group[val[i]];
-    if (i == 0 || group[val[i - 1]] != g) gs[g] = (uint32_t)i;
-}
-
-// gs[g] = min(gs[g], gs[g+1], …): empty groups start where the next non-empty
-// one does.  One block, chunks from the top.
-__global__ __launch_bounds__(1024) void k_group_suffix_min(uint32_t* gs, uint32_t G) {
-    __shared__ uint32_t lw[16];
-    __shared__ uint32_t carry_s;
-    if (threadIdx.x == 0) carry_s = gs[G];
-    __syncthreads();
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-    for (int64_t top = (int64_t)G - 1; top >= 0; top -= 1024) {
-        const int64_t i = top - (int64_t)threadIdx.x;  // thread 0 takes the highest index
-        uint32_t x = i >= 0 ? gs[i] : 0xFFFFFFFFu;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const uint32_t y = __shfl_up(x, o, 64);
-            if (lane >= o) x = min(x, y);
-        }
-        if (lane == 63) lw[wid] = x;
-        __syncthreads();
-        uint32_t before = carry_s;
-        for (int w = 0; w < wid; ++w) before = min(before, lw[w]);
-        x = min(x, before);
-        if (i >= 0) gs[i] = x;
-        __syncthreads();
-        if (threadIdx.x == 1023) carry_s = x;
-        __syncthreads();
-    }
+    const uint32_t from = i == 0 ? 0u : group[val[i - 1]] + 1;  // groups from .. g start here
+    for (uint32_t x = from; x <= g && x < G; ++x) gs[x] = (uint32_t)i;
+    if (i == n - 1)
+        for (uint32_t x = g + 1; x <= G; ++x) gs[x] = (uint32_t)n;
 }
 
 // Number of elements of stratum k2 (documents [c0, c1) of the group order,
@@ -144,6 +126,8 @@ __global__ __launch_bounds__(256) void k_merge(Plan p, const uint32_t* val) {
             rank += count_before(p, c0, c1, k2 < k, a, A, lo, hi);
         }
     }
+    if (blockIdx.x == 0)  // each stream's first position in the merged order (a stream's first arrival)
+        for (uint32_t x = threadIdx.x; x <= p.S; x += blockDim.x) p.src_doc_start[x] = p.group_start[p.gbase[x * p.n_seg]];
     if (!active) return;
     const uint64_t at = p.group_start[g0] + rank;
     if (at < p.n_kept) p.order[at] = d;
@@ -160,6 +144,8 @@ __global__ void k_src_doc_start(Plan p) {
 // and a tail piece (config "long-context branch": split at T).
 __global__ __launch_bounds__(256) void k_pieces(Plan p) {
     const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (blockIdx.x == 0)  // each stream's first piece
+        for (uint32_t x = threadIdx.x; x <= p.S; x += blockDim.x) p.src_piece_start[x] = p.piece_start[p.src_doc_start[x]];
     if (i >= p.n_kept) return;
     const uint32_t d = p.order[i];
     const uint32_t q0 = p.piece_start[i];
@@ -876,17 +862,16 @@ inline uint32_t blocks_for(uint64_t n, uint32_t b = 256) { return (uint32_t)((n 
 
 void launch_merge(Plan& p, hipStream_t st) {
     const uint32_t* val = p.val[p.sort_buf];
-    hipLaunchKernelGGL(k_fill_u32, dim3(blocks_for(p.G + 1)), dim3(256), 0, st, p.group_start, (uint64_t)p.G + 1,
-                       (uint32_t)p.n_kept);
-    if (p.n_kept)
-        hipLaunchKernelGGL(k_group_bounds, dim3(blocks_for(p.n_kept)), dim3(256), 0, st, val, p.group, p.n_kept,
-                           p.group_start);
-    hipLaunchKernelGGL(k_group_suffix_min, dim3(1), dim3(1024), 0, st, p.group_start, p.G);
+    if (p.n_kept) {
+        hipLaunchKernelGGL(k_group_bounds, dim3(blocks_for(p.n_kept)), dim3(256), 0, st, val, p.group, p.n_kept, p.G,
+                           p.group_start, p.order);
+    } else {  // no document: every group starts (and ends) at 0
+        hipLaunchKernelGGL(k_fill_u32, dim3(blocks_for(p.G + 1)), dim3(256), 0, st, p.group_start,
+                           (uint64_t)p.G + 1, 0u);
+    }
     scan_len_u64(val, p.offsets, p.n_kept, p.gpre, p.scan, st);
-    // holes (which a correct merge never leaves) would read document 0
-    if (p.n_kept) hipLaunchKernelGGL(k_fill_u32, dim3(blocks_for(p.n_kept)), dim3(256), 0, st, p.order, p.n_kept, 0u);
     if (p.n_kept) hipLaunchKernelGGL(k_merge, dim3(blocks_for(p.n_kept)), dim3(256), 0, st, p, val);
-    hipLaunchKernelGGL(k_src_doc_start, dim3(blocks_for(p.S + 1)), dim3(256), 0, st, p);
+    else hipLaunchKernelGGL(k_src_doc_start, dim3(blocks_for(p.S + 1)), dim3(256), 0, st, p);
     DP_HIP(hipGetLastError());
 }
 
@@ -902,7 +887,7 @@ void launch_piece_count(Plan& p, hipStream_t st) {
 
 void launch_pieces(Plan& p, hipStream_t st) {
     if (p.n_kept) hipLaunchKernelGGL(k_pieces, dim3(blocks_for(p.n_kept)), dim3(256), 0, st, p);
-    hipLaunchKernelGGL(k_src_piece_start, dim3(blocks_for(p.S + 1)), dim3(256), 0, st, p);
+    else hipLaunchKernelGGL(k_src_piece_start, dim3(blocks_for(p.S + 1)), dim3(256), 0, st, p);
     DP_HIP(hipGetLastError());
 }
 
