@@ -28,9 +28,10 @@ enum : uint32_t {
 constexpr uint32_t TPT = 16;          // contiguous tokens per lane of the hash
 constexpr uint32_t WT = WAVE * TPT;   // tokens per wave-tile (one wavefront's share)
 
-// One thread per document: the corpus checks, and two preparations of the
-// hash (the validation visits every document anyway): the document's NH sum
-// S[d] = 0, and the tile table first[t] = d for every wave-tile whose first
+// One thread per document: the corpus checks, and preparations of later steps
+// (the validation visits every document anyway): zero the plan's two sums
+// (added to at the end of the plan), the document's NH sum S[d] = 0, and the
+// hash's tile table first[t] = d for every wave-tile whose first
 // token base + t·WT lies in the document (each token belongs to one non-empty
 // document, so every tile below ntiles gets exactly one writer; the last
 // document also writes the sentinel first[ntiles] = D − 1).  A document whose
@@ -43,6 +44,7 @@ __global__ __launch_bounds__(256) void k_validate(Plan p, uint64_t* S, uint32_t*
     uint32_t err = 0;
     const uint64_t o0 = p.offsets[d], o1 = p.offsets[d + 1];
     S[d] = 0;
+    if (d == 0) p.checks[0] = p.checks[1] = 0;  // the plan's two sums, added to at the end of the plan
     if (o1 < o0) err |= ERR_OFFSETS;
     else if (o1 - o0 > 0xFFFFFFFFull) err |= ERR_DOC_LEN;
     const uint64_t base = p.offsets[0];

@@ -984,8 +984,8 @@ void launch_stream_next(Plan& p, const uint64_t* next_win, uint64_t* out, hipStr
     DP_HIP(hipGetLastError());
 }
 
+// p.checks was zeroed by the validation kernel
 void launch_checks(Plan& p, hipStream_t st) {
-    hipLaunchKernelGGL(k_zero_u64, dim3(1), dim3(256), 0, st, p.checks, (uint64_t)2);
     const uint64_t n = p.n_docs > p.n_kept ? p.n_docs : p.n_kept;
     hipLaunchKernelGGL(k_checks, dim3(std::min<uint32_t>(blocks_for(n), 512)), dim3(256), 0, st, p);
     DP_HIP(hipGetLastError());
