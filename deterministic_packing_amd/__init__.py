@@ -28,7 +28,7 @@ ABI_VERSION = 2
 
 PACK_OK, PACK_E_ABI, PACK_E_INVAL, PACK_E_NOMEM, PACK_E_HIP = 0, -1, -2, -3, -4
 PACK_E_EXHAUSTED, PACK_E_STATE, PACK_E_RANGE, PACK_E_INTERNAL = -5, -6, -7, -8
-PACK_TEST_WAIT_GIVE_UP, PACK_TEST_CYCLE_FAULT = 1, 2
+PACK_TEST_WAIT_GIVE_UP, PACK_TEST_CYCLE_FAULT, PACK_TEST_SORT_INSERTION = 1, 2, 3
 
 SYMBOLS = ("pack_init", "pack_init_noalloc", "pack_cycle", "pack_batch", "pack_batch_packed", "pack_fingerprint",
            "pack_fingerprint_steps", "pack_inspect", "pack_get_timings", "pack_status", "pack_test_option",

@@ -1194,6 +1194,7 @@ int pack_test_option(pack_ctx* c, uint32_t what, uint32_t value) {
     switch (what) {
         case PACK_TEST_WAIT_GIVE_UP: bit = dp::TEST_WAIT_GIVE_UP; break;
         case PACK_TEST_CYCLE_FAULT: bit = dp::TEST_CYCLE_FAULT; break;
+        case PACK_TEST_SORT_INSERTION: bit = dp::TEST_SORT_INSERTION; break;
         default: c->err = "unknown test option"; return PACK_E_INVAL;
     }
     if (value) c->p.test_opts |= bit;

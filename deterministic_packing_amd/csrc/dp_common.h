@@ -16,6 +16,7 @@ constexpr uint32_t ERR_INTERNAL = 0x100u;
 // test options (the PACK_TEST_* values of dpack.h)
 constexpr uint32_t TEST_WAIT_GIVE_UP = 1u;
 constexpr uint32_t TEST_CYCLE_FAULT = 2u;
+constexpr uint32_t TEST_SORT_INSERTION = 4u;
 
 // ---------------------------------------------------------------- errors
 struct HipError {
@@ -303,7 +304,7 @@ uint64_t hash_tile_count(uint64_t n_tokens);
 void launch_keep_scan(Plan& p, hipStream_t st);       // kept_pos + compaction into val[0], keys
 void launch_sort(Plan& p, hipStream_t st);            // by (group, key64, d); sets sort_buf
 uint32_t sort_pairs(uint64_t* const key[2], uint32_t* const val[2], const uint32_t* group, uint64_t n, uint32_t G,
-                    uint32_t* hist_ws, const ScanWs& scan, hipStream_t st);
+                    uint32_t* hist_ws, const ScanWs& scan, uint32_t test_opts, hipStream_t st);
 void launch_read_order(Plan& p, uint32_t cycle, uint64_t total, hipStream_t st);  // perm of each source's cycle windows
 void launch_merge(Plan& p, hipStream_t st);           // group_start, gpre, order, src_doc_start
 void launch_piece_count(Plan& p, hipStream_t st);     // piece_start, opre

@@ -130,14 +130,16 @@ __device__ __forceinline__ void cmpx(uint64_t& ka, uint32_t& va, uint64_t& kb, u
 // one thread per bucket: [boff[b], boff[b+1]) ordered by (key64, val).  Up to
 // BMAX elements are loaded at once, padded with the largest pair and sorted by
 // an odd-even transposition network in registers; a larger bucket (rare: a
-// bucket averages 2-4 elements) is sorted in place by insertion.
-__global__ __launch_bounds__(256) void k_bucket_sort(uint64_t* key, uint32_t* val, const uint32_t* boff, uint64_t nb) {
+// bucket averages 2-4 elements) is sorted in place by insertion, as is every
+// bucket with insertion_only (a test option, so that path is exercised).
+__global__ __launch_bounds__(256) void k_bucket_sort(uint64_t* key, uint32_t* val, const uint32_t* boff, uint64_t nb,
+                                                     uint32_t insertion_only) {
     const uint64_t b = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (b >= nb) return;
     const uint32_t lo = boff[b], hi = boff[b + 1];
     const uint32_t m = hi - lo;
     if (m < 2) return;
-    if (m <= BMAX) {
+    if (m <= BMAX && !insertion_only) {
         uint64_t k[BMAX];
         uint32_t v[BMAX];
 #pragma unroll
@@ -208,7 +210,7 @@ void launch_keep_scan(Plan& p, hipStream_t st) {
 // uniform.  Launches are sized by the bucket bound n/2 + G + 1 (a group of
 // n_g > 4 elements takes 2^b < n_g/2 buckets), so nothing is read back.
 uint32_t sort_pairs(uint64_t* const key[2], uint32_t* const val[2], const uint32_t* group, uint64_t n, uint32_t G,
-                    uint32_t* ws, const ScanWs& scan, hipStream_t st) {
+                    uint32_t* ws, const ScanWs& scan, uint32_t test_opts, hipStream_t st) {
     if (n == 0) return 0;
     const uint64_t NB = n / 2 + G + 1;  // bucket bound
     uint32_t* gcount = ws;                 // [G]
@@ -229,14 +231,14 @@ uint32_t sort_pairs(uint64_t* const key[2], uint32_t* const val[2], const uint32
     hipLaunchKernelGGL(k_bucket_scatter, dim3(blocks), dim3(256), 0, st, key[0], val[0], n, (const uint32_t*)bucket,
                        (const uint32_t*)ticket, (const uint32_t*)boff, key[1], val[1]);
     hipLaunchKernelGGL(k_bucket_sort, dim3((uint32_t)((NB + 255) / 256)), dim3(256), 0, st, key[1], val[1],
-                       (const uint32_t*)boff, NB);
+                       (const uint32_t*)boff, NB, (test_opts & TEST_SORT_INSERTION) ? 1u : 0u);
     DP_HIP(hipGetLastError());
     return 1;
 }
 
 // requires p.n_kept (host) to be set
 void launch_sort(Plan& p, hipStream_t st) {
-    p.sort_buf = sort_pairs(p.key, p.val, p.group, p.n_kept, p.G, p.hist, p.scan, st);
+    p.sort_buf = sort_pairs(p.key, p.val, p.group, p.n_kept, p.G, p.hist, p.scan, p.test_opts, st);
 }
 
 // requires perm_start (device) for the cycle; total = U·B
@@ -245,7 +247,7 @@ void launch_read_order(Plan& p, uint32_t cycle, uint64_t total, hipStream_t st) 
     const uint32_t blocks = (uint32_t)((total + 255) / 256);
     hipLaunchKernelGGL(k_window_keys, dim3(blocks), dim3(256), 0, st, p, cycle, total);
     DP_HIP(hipGetLastError());
-    const uint32_t buf = sort_pairs(p.wkey, p.wval, p.wgroup, total, p.S, p.hist, p.scan, st);
+    const uint32_t buf = sort_pairs(p.wkey, p.wval, p.wgroup, total, p.S, p.hist, p.scan, p.test_opts, st);
     hipLaunchKernelGGL(k_perm_out, dim3(blocks), dim3(256), 0, st, p, (const uint32_t*)p.wval[buf], total);
     DP_HIP(hipGetLastError());
 }

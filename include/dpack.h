@@ -406,13 +406,17 @@ int pack_inspect(const pack_ctx *ctx, uint32_t what, void *host_dst, uint64_t ca
 int pack_status(pack_ctx *ctx);
 
 /* Test options for pack_test_option.  They exist so that the error paths
- * above can be exercised on a GPU with every kernel still running to its
- * end; with every option 0 (the default) no output byte changes. */
+ * above, and code paths that real inputs almost never take, can be exercised
+ * on a GPU with every kernel still running to its end; with every option 0
+ * (the default) no output byte changes, and PACK_TEST_SORT_INSERTION changes
+ * none either. */
 enum {
     PACK_TEST_WAIT_GIVE_UP = 1, /* the digest waves' bounded waits give up after one poll:
                                    the batch's digests are invalid, pack_status reports it
                                    (calls of at most 65,536 windows; larger ones have no wait) */
     PACK_TEST_CYCLE_FAULT = 2,  /* a cycle kernel reports an internal failure: pack_cycle fails */
+    PACK_TEST_SORT_INSERTION = 3, /* the sort of a cycle's random read order orders every bucket
+                                     by insertion, the path of buckets above 16 elements */
 };
 
 /* pack_test_option — set test option `what` on (value != 0) or off for the

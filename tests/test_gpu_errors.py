@@ -1,4 +1,5 @@
-"""Internal failures inside the kernels reach the caller (GPU).
+"""Internal failures inside the kernels reach the caller, and rare code paths
+run, forced by the library's test options (GPU).
 
 The window digests of pack_batch wait, boundedly, for the emitting waves
 beside them; if such a wait gives up, the call's digests are not valid and
@@ -129,4 +130,22 @@ def test_test_options_change_no_output_byte_when_off():
     with pytest.raises(dp.DpackError) as e:
         pk.test_option(99, 1)
     assert e.value.code == dp.PACK_E_INVAL
+    pk.close()
+
+
+@pytest.mark.parametrize("mode", [{}, {"cumulative": True}, {"lanes": 2}])
+def test_sort_insertion_path_gives_the_same_read_order(mode):
+    """The sort's insertion path (buckets above 16 elements, which uniform keys
+    almost never fill) forced for every bucket of the cycles' random read order:
+    the read order, and so every batch, still equal the oracle's."""
+    c = _corpus(506, read_random=True, **mode).replace(updates_per_cycle=3)
+    say("sort insertion path", mode)
+    op = oracle.Plan(c)
+    pk = dp.Packer(c)
+    pk.test_option(dp.PACK_TEST_SORT_INSERTION, 1)
+    for cyc in range(3):
+        oi = op.cycle(cyc)
+        compare_cycle(pk.cycle(cyc), oi, op)
+        n = oi.n_updates
+        compare_batch(to_np(pk.batch(0, n)), op.batch(0, n), f"insertion sort cycle {cyc}")
     pk.close()
