@@ -20,6 +20,13 @@ namespace {
 constexpr int EB = 256;      // threads per window
 constexpr int ECAP = 512;    // pieces staged in LDS
 
+typedef uint32_t u32x4a4 __attribute__((ext_vector_type(4), aligned(4)));  // 16-byte load, 4-byte aligned
+
+__device__ __forceinline__ void load4(const uint32_t* src, uint32_t (&tk)[4]) {
+    const u32x4a4 x = *reinterpret_cast<const u32x4a4*>(src);
+    tk[0] = x.x; tk[1] = x.y; tk[2] = x.z; tk[3] = x.w;
+}
+
 struct PieceView {
     uint32_t woff, doc, mfrom;
     uint64_t src;
@@ -100,23 +107,35 @@ __global__ __launch_bounds__(EB) void k_emit(Plan p, EmitArgs a) {
                 uint32_t q = find(t0);
                 PieceView v = get(q);
                 uint32_t next_woff = (q + 1 < np) ? (staged ? s_woff[q + 1] : p.pc_woff[q0 + q + 1]) : real;
+                const uint32_t u0 = t0 - v.woff;
+                if (t0 + 4 <= next_woff && t0 + 4 <= real && v.src + u0 + 4 <= p.n_tokens) {
+                    // the four positions in one piece: one 16-byte load of their tokens
+                    load4(p.tokens + v.src + u0, tk);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const uint32_t t = t0 + e;
-                    if (t >= real) {
-                        tk[e] = pad; ps[e] = 0; dc[e] = -1;
-                        continue;
+                    for (int e = 0; e < 4; ++e) {
+                        ps[e] = (int32_t)(u0 + e);
+                        dc[e] = (int32_t)v.doc;
+                        mk |= (t0 + e >= v.mfrom ? 1u : 0u) << (8 * e);
                     }
-                    while (t >= next_woff && q + 1 < np) {  // next piece (contiguous up to `real`)
-                        ++q;
-                        v = get(q);
-                        next_woff = (q + 1 < np) ? (staged ? s_woff[q + 1] : p.pc_woff[q0 + q + 1]) : real;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const uint32_t t = t0 + e;
+                        if (t >= real) {
+                            tk[e] = pad; ps[e] = 0; dc[e] = -1;
+                            continue;
+                        }
+                        while (t >= next_woff && q + 1 < np) {  // next piece (contiguous up to `real`)
+                            ++q;
+                            v = get(q);
+                            next_woff = (q + 1 < np) ? (staged ? s_woff[q + 1] : p.pc_woff[q0 + q + 1]) : real;
+                        }
+                        const uint32_t u = t - v.woff;
+                        tk[e] = (v.src + u < p.n_tokens) ? p.tokens[v.src + u] : pad;  // guard: never read past the corpus
+                        ps[e] = (int32_t)u;
+                        dc[e] = (int32_t)v.doc;
+                        mk |= (t >= v.mfrom ? 1u : 0u) << (8 * e);
                     }
-                    const uint32_t u = t - v.woff;
-                    tk[e] = (v.src + u < p.n_tokens) ? p.tokens[v.src + u] : pad;  // guard: never read past the corpus
-                    ps[e] = (int32_t)u;
-                    dc[e] = (int32_t)v.doc;
-                    mk |= (t >= v.mfrom ? 1u : 0u) << (8 * e);
                 }
             }
             tok4[g] = make_uint4(tk[0], tk[1], tk[2], tk[3]);
@@ -150,21 +169,33 @@ __global__ __launch_bounds__(EB) void k_emit(Plan p, EmitArgs a) {
                 uint32_t q = find(tf);
                 PieceView v = get(q);
                 uint32_t next_woff = (q + 1 < np) ? (staged ? s_woff[q + 1] : p.pc_woff[q0 + q + 1]) : real;
+                const uint32_t u0 = tf - v.woff;
+                if (tb >= 0 && tf + 4 <= next_woff && tf + 4 <= real && v.src + u0 + 4 <= p.n_tokens) {
+                    // the four positions in one piece: one 16-byte load of their tokens
+                    load4(p.tokens + v.src + u0, tk);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int32_t ts = tb + e;
-                    if (ts < 0 || (uint32_t)ts >= real) continue;
-                    const uint32_t t = (uint32_t)ts;
-                    while (t >= next_woff && q + 1 < np) {  // next piece (contiguous up to `real`)
-                        ++q;
-                        v = get(q);
-                        next_woff = (q + 1 < np) ? (staged ? s_woff[q + 1] : p.pc_woff[q0 + q + 1]) : real;
+                    for (int e = 0; e < 4; ++e) {
+                        ps[e] = (int32_t)(u0 + e);
+                        dc[e] = (int32_t)v.doc;
+                        mk |= (tf + e >= v.mfrom ? 1u : 0u) << (8 * e);
                     }
-                    const uint32_t u = t - v.woff;
-                    tk[e] = (v.src + u < p.n_tokens) ? p.tokens[v.src + u] : pad;  // guard: never read past the corpus
-                    ps[e] = (int32_t)u;
-                    dc[e] = (int32_t)v.doc;
-                    mk |= (t >= v.mfrom ? 1u : 0u) << (8 * e);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int32_t ts = tb + e;
+                        if (ts < 0 || (uint32_t)ts >= real) continue;
+                        const uint32_t t = (uint32_t)ts;
+                        while (t >= next_woff && q + 1 < np) {  // next piece (contiguous up to `real`)
+                            ++q;
+                            v = get(q);
+                            next_woff = (q + 1 < np) ? (staged ? s_woff[q + 1] : p.pc_woff[q0 + q + 1]) : real;
+                        }
+                        const uint32_t u = t - v.woff;
+                        tk[e] = (v.src + u < p.n_tokens) ? p.tokens[v.src + u] : pad;  // guard: never read past the corpus
+                        ps[e] = (int32_t)u;
+                        dc[e] = (int32_t)v.doc;
+                        mk |= (t >= v.mfrom ? 1u : 0u) << (8 * e);
+                    }
                 }
             }
             if (tb >= 0 && (uint32_t)tb + 4 <= real) {

@@ -66,6 +66,29 @@ PACKED_CASES = ([("small", s, b, w, False) for s, b, w in [(0, 256, 1), (1, 64, 
                    ("long", 0.01, 256, 2, False)])
 
 
+NODIG_CASES = [("small", s) for s in range(8)] + [("tinydocs", 3), ("sft", 0.004), ("long", 0.01), ("full", 0.002)]
+
+
+@pytest.mark.parametrize("kind,arg", NODIG_CASES)
+@pytest.mark.parametrize("wrap", [False, True])
+def test_batch_without_digests_parity(kind, arg, wrap):
+    """pack_batch without digests (the emission kernel alone): padded windows whose
+    four-position groups lie in one piece take one 16-byte token load, the others
+    (piece ends, padding, the corpus end) go element by element."""
+    c = _corpus(kind, arg).replace(wrap=wrap)
+    op = oracle.Plan(c)
+    try:
+        oi = op.cycle(0)
+    except oracle.OracleError:
+        pytest.skip("corpus exhausted at this size")
+    n = min(4, oi.n_updates)
+    say("no digests", kind, arg, "wrap", wrap)
+    pk = dp.Packer(c)
+    pk.cycle(0)
+    compare_batch(to_np(pk.batch(0, n, digests=False)), op.batch(0, n, digests=False), f"{kind}{arg} no digests")
+    pk.close()
+
+
 @pytest.mark.parametrize("kind,arg,bucket,world,wrap", PACKED_CASES)
 def test_padding_free_rows_parity(kind, arg, bucket, world, wrap):
     """pack_batch_packed against the oracle's padding-free rows (rank 0 and the last rank).
