@@ -10,12 +10,15 @@ before the timed region.  value = real (non-padding) tokens emitted per second.
 The default workload is the full cycle: 2·10^9 tokens resident, 15 sources x
 8 strata, T = 4096, B = 1024, every update of the longest cycle.
 
-Per-kernel times come from HIP events the library records on its stream
-(PACK_FLAG_TIMING) inside the timed steps; the roofline object is reported for
-the kernel that takes the most time, and every phase is listed under
-"kernels".  The emission kernel without digests (the packing kernel on its
-own, HBM-bound) is timed the same way in a separate pass over the same cycle
-and reported as roofline_emit.  The CPU baseline is the oracle (plain
+Per-kernel times come from HIP events the library records on its stream.
+Inside the timed steps only the batch's kernels are timed
+(PACK_FLAG_TIMING_BATCH: two events around the dominant kernel per step); the
+plan's phases are timed in a second pass of the same steps after the timed
+region (PACK_FLAG_TIMING), since an event costs several microseconds of stream
+time.  The roofline object is reported for the kernel that takes the most
+time, and every phase is listed under "kernels".  The emission kernel without
+digests (the packing kernel on its own, HBM-bound) is timed the same way in a
+separate pass over the same cycle and reported as roofline_emit.  The CPU baseline is the oracle (plain
 sequential C) timed on this host on a bounded sample of the same workload.
 """
 import argparse
@@ -164,8 +167,8 @@ def main():
     torch.cuda.synchronize()
     log(f"cycle {cyc}: {U} updates x {B if not args.ramp else sorted(set(batches))} windows x {T} positions")
 
-    def one_step():
-        pk = dp.Packer(corpus, device_tensors=tensors, timing=True)
+    def one_step(timing):
+        pk = dp.Packer(corpus, device_tensors=tensors, timing=timing)
         info = pk.cycle(cyc)
         if args.packed:
             pk.batch_packed_into(0, info["n_updates"], out)
@@ -176,27 +179,38 @@ def main():
         pk.close()
         return info, tm
 
+    # the timed steps record events only around the batch's kernels (the
+    # dominant kernel's launch time): an event costs several microseconds of
+    # stream time, which the plan's dozen phases would add to every step
     for w in range(args.warmup):
-        one_step()
+        one_step("batch")
         log(f"warmup {w + 1}/{args.warmup} done")
     torch.cuda.synchronize()
     phase_ms = {}
     phase_calls = {}
     t_start = time.perf_counter()
     for s in range(args.steps):
-        info, tm = one_step()
+        info, tm = one_step("batch")
         for k, (ms, n) in tm.items():
             phase_ms[k] = phase_ms.get(k, 0.0) + ms
             phase_calls[k] = phase_calls.get(k, 0) + n
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
     ms_per_step = elapsed * 1e3 / args.steps
+    # the plan's phases: the same steps again after the timed region, every phase timed
+    for s in range(args.steps):
+        _, tm = one_step(True)
+        for k, (ms, n) in tm.items():
+            if k not in ("emit", "learned", "digest", "fingerprint"):
+                phase_ms[k] = phase_ms.get(k, 0.0) + ms
+                phase_calls[k] = phase_calls.get(k, 0) + n
     real = info["real_tokens"]
     positions = info["positions"]
     value = real / (ms_per_step / 1e3)
     log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step, {value:.4g} packed tokens/s")
 
-    # per-kernel figures (averaged per launch over the timed steps)
+    # per-kernel figures (averaged per launch: the batch's over the timed steps,
+    # the plan's over the instrumented pass)
     n_windows = sum(batches)
     # read every real token once, write 13 bytes per output position (padded
     # windows: U·B·T; padding-free rows: the rows' lengths, bucket padding included)
@@ -252,7 +266,7 @@ def main():
     if "emit" not in side:
         # the emission kernel on its own (pack_batch without digests over the
         # same cycle, into the same buffers), timed by the library's events
-        pk2 = dp.Packer(corpus, device_tensors=tensors, timing=True)
+        pk2 = dp.Packer(corpus, device_tensors=tensors, timing="batch")
         pk2.cycle(cyc)
         nod = dict(out, digests=None)
         pk2.batch_into(0, U, nod)  # warm-up

@@ -39,6 +39,7 @@ PACK_FLAG_WRAP = 2
 PACK_FLAG_HELDOUT = 4
 PACK_FLAG_READ_RANDOM = 8
 PACK_FLAG_CUMULATIVE = 16
+PACK_FLAG_TIMING_BATCH = 32
 PHASES = ("validate", "hash", "keys", "sort", "merge", "pieces", "cut", "windows", "mixture",
           "cycle", "emit", "learned", "digest", "fingerprint")
 
@@ -242,10 +243,12 @@ class Packer:
     ``corpus`` provides numpy arrays (tokens, offsets, source, stratum,
     prompt_len) and the recipe (n_strata, weight, holdout_bp, T, B,
     updates_per_cycle, seed, pad_token); they are copied to ``device`` once
-    (or pass ``device_tensors`` to reuse resident ones)."""
+    (or pass ``device_tensors`` to reuse resident ones).  ``timing``: True
+    times every kernel phase, "batch" only the phases of batch and
+    fingerprint calls (read with ``timings``)."""
 
     def __init__(self, corpus, rank: int = 0, world: int = 1, device: str = "cuda",
-                 device_tensors: Optional[dict] = None, stream=None, timing: bool = False,
+                 device_tensors: Optional[dict] = None, stream=None, timing=False,
                  noalloc: bool = False):
         import torch
 
@@ -275,7 +278,8 @@ class Packer:
             assert self._host["start_tokens"].shape[0] == S * self.lanes
         d = self.dev
         self.cfg = PackConfig(
-            ABI_VERSION, (PACK_FLAG_TIMING if timing else 0) | (PACK_FLAG_WRAP if getattr(corpus, "wrap", False) else 0)
+            ABI_VERSION, (PACK_FLAG_TIMING_BATCH if timing == "batch" else PACK_FLAG_TIMING if timing else 0)
+            | (PACK_FLAG_WRAP if getattr(corpus, "wrap", False) else 0)
             | (PACK_FLAG_HELDOUT if getattr(corpus, "heldout", False) else 0)
             | (PACK_FLAG_READ_RANDOM if getattr(corpus, "read_random", False) else 0)
             | (PACK_FLAG_CUMULATIVE if getattr(corpus, "cumulative", False) else 0),

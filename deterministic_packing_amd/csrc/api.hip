@@ -109,9 +109,11 @@ struct InternalError {
 }  // namespace
 
 // HIP events around kernel phases, recorded on the context's stream when the
-// context is made with PACK_FLAG_TIMING; resolved in pack_get_timings.
+// context is made with PACK_FLAG_TIMING (every phase) or PACK_FLAG_TIMING_BATCH
+// (the phases of pack_batch and pack_fingerprint); resolved in pack_get_timings.
 struct PhaseTimer {
     bool on = false;
+    uint32_t phases = 0;  // bit k: phase k is timed
     std::vector<hipEvent_t> pool;
     struct Pending {
         int phase;
@@ -129,12 +131,14 @@ struct PhaseTimer {
             pool.pop_back();
             return e;
         }
+        // timestamps only: no system-scope fence (a fence writes back and invalidates the
+        // caches at every phase boundary, about 10 µs each, and slows the work after it)
         hipEvent_t e;
-        DP_HIP(hipEventCreate(&e));
+        DP_HIP(hipEventCreateWithFlags(&e, hipEventDisableSystemFence));
         return e;
     }
     void begin(int phase, hipStream_t st) {
-        if (!on) return;
+        if (!on || !(phases >> phase & 1u)) return;
         open_phase = phase;
         open_a = get();
         DP_HIP(hipEventRecord(open_a, st));
@@ -396,7 +400,8 @@ void sync_staged(pack_ctx& c) {
 void check_config(const pack_config* cfg) {
     auto bad = [](const char* m) { throw InvalError{m}; };
     if (cfg->flags &
-        ~(PACK_FLAG_TIMING | PACK_FLAG_WRAP | PACK_FLAG_HELDOUT | PACK_FLAG_READ_RANDOM | PACK_FLAG_CUMULATIVE))
+        ~(PACK_FLAG_TIMING | PACK_FLAG_TIMING_BATCH | PACK_FLAG_WRAP | PACK_FLAG_HELDOUT | PACK_FLAG_READ_RANDOM |
+          PACK_FLAG_CUMULATIVE))
         bad("unknown flags");
     if (cfg->n_docs < 1 || cfg->n_docs >= (1ull << 31)) bad("n_docs must be in [1, 2^31)");
     if (!cfg->doc_offsets || !cfg->doc_source) bad("doc_offsets and doc_source are required");
@@ -658,8 +663,8 @@ int init_context(const pack_config* cfg, pack_ctx** out, bool noalloc) {
         g_init_error = "abi_version mismatch";
         return PACK_E_ABI;
     }
-    if (noalloc && (cfg->flags & PACK_FLAG_TIMING)) {  // timing events would be created per context
-        g_init_error = "pack_init_noalloc does not take PACK_FLAG_TIMING";
+    if (noalloc && (cfg->flags & (PACK_FLAG_TIMING | PACK_FLAG_TIMING_BATCH))) {  // events are created per context
+        g_init_error = "pack_init_noalloc does not take PACK_FLAG_TIMING or PACK_FLAG_TIMING_BATCH";
         return PACK_E_INVAL;
     }
     pack_ctx* c = nullptr;
@@ -676,7 +681,11 @@ int init_context(const pack_config* cfg, pack_ctx** out, bool noalloc) {
             c->start_tokens.assign(cfg->start_tokens, cfg->start_tokens + (uint64_t)cfg->n_sources *
                                                                               (cfg->n_lanes > 1 ? cfg->n_lanes : 1));
         c->st = static_cast<hipStream_t>(cfg->stream);
-        c->timer.on = (cfg->flags & PACK_FLAG_TIMING) != 0;
+        c->timer.on = (cfg->flags & (PACK_FLAG_TIMING | PACK_FLAG_TIMING_BATCH)) != 0;
+        c->timer.phases = (cfg->flags & PACK_FLAG_TIMING) ? (1u << PACK_N_PHASES) - 1u
+                                                           : (1u << PACK_PHASE_EMIT) | (1u << PACK_PHASE_LEARNED) |
+                                                                 (1u << PACK_PHASE_DIGEST) |
+                                                                 (1u << PACK_PHASE_FINGERPRINT);
         // with lanes, every per-source array is per stream s·L + l (the recipe's values per source)
         const uint32_t L = cfg->n_lanes > 1 ? cfg->n_lanes : 1, Sr = cfg->n_sources, S = Sr * L;
         c->lanes = L;

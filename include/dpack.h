@@ -104,8 +104,16 @@ typedef struct pack_ctx pack_ctx;
  * the schedule no source runs out in.  At most 1024 sources; the table of
  * (updates x sources) is bounded by 2^28 entries at init. */
 #define PACK_FLAG_CUMULATIVE 16u
+/* pack_config.flags: record HIP events only around the kernels of pack_batch,
+ * pack_batch_packed and pack_fingerprint (phases EMIT, LEARNED, DIGEST,
+ * FINGERPRINT); pack_init and pack_cycle record none, so their kernels run as
+ * in an untimed context (each event costs several microseconds of stream
+ * time).  With PACK_FLAG_TIMING as well, every phase is timed.  Changes no
+ * output byte. */
+#define PACK_FLAG_TIMING_BATCH 32u
 
-/* Kernel phases timed under PACK_FLAG_TIMING. */
+/* Kernel phases timed under PACK_FLAG_TIMING (EMIT to FINGERPRINT also under
+ * PACK_FLAG_TIMING_BATCH). */
 enum {
     PACK_PHASE_VALIDATE = 0, /* corpus validation kernel */
     PACK_PHASE_HASH,         /* per-document hash and hold-out */
@@ -191,7 +199,8 @@ typedef struct pack_timings {
  * Limit: Σ n_strata · lanes · n_segments ≤ 65536 groups. */
 typedef struct pack_config {
     uint32_t abi_version;          /* DPACK_ABI_VERSION */
-    uint32_t flags;                /* 0 or an or of PACK_FLAG_TIMING, _WRAP, _HELDOUT, _READ_RANDOM, _CUMULATIVE */
+    uint32_t flags;                /* 0 or an or of PACK_FLAG_TIMING, _TIMING_BATCH, _WRAP, _HELDOUT, _READ_RANDOM,
+                                      _CUMULATIVE */
     const uint32_t *tokens;        /* device [n_tokens] token ids */
     uint64_t n_tokens;
     const uint64_t *doc_offsets;   /* device [n_docs+1]: document d is tokens[off[d], off[d+1]) */

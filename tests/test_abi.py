@@ -66,7 +66,7 @@ def _cfg(**kw):
     ("window_tokens", 100, dp.PACK_E_INVAL),
     ("global_batch", 0, dp.PACK_E_INVAL),
     ("n_docs", 0, dp.PACK_E_INVAL),
-    ("flags", 32, dp.PACK_E_INVAL),
+    ("flags", 64, dp.PACK_E_INVAL),
     ("n_sources", 0, dp.PACK_E_INVAL),
     ("n_tokens", 1 << 40, dp.PACK_E_INVAL),  # scanned token totals stay below 2^40
 ])
@@ -159,14 +159,19 @@ def test_null_arguments_are_errors(lib):
 
 def test_noalloc_limits_checked_before_device_work(lib):
     """pack_init_noalloc: a plan whose workspace exceeds the static scratch, or
-    PACK_FLAG_TIMING, is refused on the host (no GPU call is made)."""
+    PACK_FLAG_TIMING or PACK_FLAG_TIMING_BATCH, is refused on the host (no GPU
+    call is made)."""
     cfg, keep = _cfg(n_docs=1 << 22, n_tokens=1 << 32)  # ~4 M documents: hundreds of MB of workspace
     ctx = C.c_void_p()
     assert lib.pack_init_noalloc(C.byref(cfg), C.byref(ctx)) == dp.PACK_E_INVAL
     msg = lib.pack_last_error(None).decode()
     assert "static scratch holds 67108864" in msg, msg
     assert ctx.value is None
-    cfg, keep = _cfg(flags=dp.PACK_FLAG_TIMING)
-    assert lib.pack_init_noalloc(C.byref(cfg), C.byref(ctx)) == dp.PACK_E_INVAL
-    assert "PACK_FLAG_TIMING" in lib.pack_last_error(None).decode()
+    for flag in (dp.PACK_FLAG_TIMING, dp.PACK_FLAG_TIMING_BATCH):
+        cfg, keep = _cfg(flags=flag)
+        assert lib.pack_init_noalloc(C.byref(cfg), C.byref(ctx)) == dp.PACK_E_INVAL
+        assert "PACK_FLAG_TIMING" in lib.pack_last_error(None).decode()
     assert lib.pack_init_noalloc(None, C.byref(ctx)) == dp.PACK_E_INVAL
+    cfg, keep = _cfg(flags=64)  # no such flag
+    assert lib.pack_init_noalloc(C.byref(cfg), C.byref(ctx)) == dp.PACK_E_INVAL
+    assert "unknown flags" in lib.pack_last_error(None).decode()

@@ -908,3 +908,24 @@ def test_reemission_and_reinit_are_bytewise_identical():
     z = to_np(b.batch(1, 3))
     for k in x:
         assert np.array_equal(x[k], y[k]) and np.array_equal(x[k], z[k]), k
+
+
+def test_timing_flags_change_no_output():
+    """PACK_FLAG_TIMING times every phase, PACK_FLAG_TIMING_BATCH only the batch
+    and fingerprint calls' phases; neither changes an output byte."""
+    c = make_corpus("sft", 0.002)
+    outs, tms = {}, {}
+    for timing in (False, True, "batch"):
+        pk = dp.Packer(c, timing=timing)
+        pk.cycle(0)
+        outs[timing] = to_np(pk.batch(0, 2))
+        tms[timing] = pk.timings(reset=True)
+        pk.close()
+    for k in outs[False]:
+        assert np.array_equal(outs[False][k], outs[True][k]) and np.array_equal(outs[False][k], outs["batch"][k]), k
+    plan = ("validate", "hash", "keys", "sort", "merge", "pieces", "cut", "windows", "mixture", "cycle")
+    assert all(tms[True][p][1] > 0 for p in plan), tms[True]
+    assert all(tms["batch"][p][1] == 0 for p in plan), tms["batch"]
+    for t in (True, "batch"):
+        ms, n = tms[t]["digest"]
+        assert n == 1 and ms > 0, tms[t]
