@@ -197,6 +197,17 @@ struct pack_ctx {
     // no pageable bounce); a bump allocator reset after each synchronization
     uint8_t* pin = nullptr;
     size_t pin_bytes = 0, pin_off = 0;
+    // device mailbox mirroring the staging byte for byte: a batch of uploads
+    // (downloads) is one copy of the staged span and one kernel that moves each
+    // array to (from) its place
+    uint8_t* mbox = nullptr;
+    size_t mbox_bytes = 0;
+    struct Moved {
+        const uint8_t* src;
+        uint8_t* dst;
+        size_t off, bytes;  // staging offset and size
+    };
+    std::vector<Moved> upq, downq;
     std::vector<uint64_t> src_win_start, stats, checks, src_piece_start;
     std::vector<uint32_t> n_upd;
     int64_t cycle = -1;
@@ -243,6 +254,8 @@ struct Carver {
         return p;
     }
 };
+
+size_t pin_bytes_for(uint32_t S, uint64_t K, uint64_t n_seg);
 
 // smallest batch of an update: B, or the ramp's smallest piece
 uint32_t ramp_bmin(const pack_ctx& c) {
@@ -341,6 +354,8 @@ size_t carve(pack_ctx& c, char* base) {
     c.nstart = k.take<uint32_t>(S + 1);
     c.dig_cap = 128 + 72 * S + 16 * K + 28;  // records 60·S, header ≤ 100 + 16·K, leaves 32·⌈S/8⌉
     c.dig_buf = k.take<uint8_t>(c.dig_cap + 32);
+    c.mbox_bytes = pin_bytes_for((uint32_t)S, K, p.n_seg);
+    c.mbox = k.take<uint8_t>(c.mbox_bytes);
     return k.off + ALIGN;
 }
 
@@ -392,9 +407,62 @@ T* d2h_staged(pack_ctx& c, const T* src, uint64_t count) {
     return h;
 }
 
-void sync_staged(pack_ctx& c) {
-    DP_HIP(hipStreamSynchronize(c.st));
+void flush_moved(pack_ctx& c, std::vector<pack_ctx::Moved>& q, bool upload) {
+    if (q.empty()) return;
+    size_t lo = ~size_t(0), hi = 0;
+    dp::XferList l{};
+    l.n = (uint32_t)q.size();
+    for (uint32_t i = 0; i < l.n; ++i) {
+        lo = std::min(lo, q[i].off);
+        hi = std::max(hi, q[i].off + q[i].bytes);
+        l.x[i] = dp::Xfer{q[i].src, q[i].dst, q[i].bytes};
+    }
+    q.clear();
+    if (hi > c.mbox_bytes) throw dp::HipError{hipErrorOutOfMemory, "internal: transfer mailbox exhausted"};
+    if (upload) {
+        h2d(c.mbox + lo, c.pin + lo, hi - lo, c.st);
+        dp::launch_xfer(l, c.st);
+    } else {
+        dp::launch_xfer(l, c.st);
+        d2h(c.pin + lo, c.mbox + lo, hi - lo, c.st);
+    }
+}
+
+// host array -> staging, queued; sent by up_flush (call it before the kernels that read dst)
+template <typename T>
+void up(pack_ctx& c, T* dst, const T* src, uint64_t count) {
+    if (!count) return;
+    T* h = pin_take<T>(c, count);
+    std::memcpy(h, src, sizeof(T) * count);
+    const size_t off = static_cast<size_t>(reinterpret_cast<uint8_t*>(h) - c.pin);
+    c.upq.push_back({c.mbox + off, reinterpret_cast<uint8_t*>(dst), off, sizeof(T) * count});
+    if (c.upq.size() == dp::XFER_MAX) flush_moved(c, c.upq, true);
+}
+void up_flush(pack_ctx& c) { flush_moved(c, c.upq, true); }
+
+// device range -> staging, queued; read the returned pointer after sync_staged
+template <typename T>
+const T* down(pack_ctx& c, const T* src, uint64_t count) {
+    T* h = pin_take<T>(c, count);
+    if (!count) return h;
+    const size_t off = static_cast<size_t>(reinterpret_cast<uint8_t*>(h) - c.pin);
+    c.downq.push_back({reinterpret_cast<const uint8_t*>(src), c.mbox + off, off, sizeof(T) * count});
+    if (c.downq.size() == dp::XFER_MAX) flush_moved(c, c.downq, false);
+    return h;
+}
+
+void reset_staging(pack_ctx& c) {
     c.pin_off = 0;
+    c.upq.clear();
+    c.downq.clear();
+}
+
+// the queued downloads, then a synchronization; the staging is free again afterwards
+void sync_staged(pack_ctx& c) {
+    if (!c.upq.empty()) throw dp::HipError{hipErrorInvalidValue, "internal: uploads staged but not sent"};
+    flush_moved(c, c.downq, false);
+    DP_HIP(hipStreamSynchronize(c.st));
+    reset_staging(c);
 }
 
 void check_config(const pack_config* cfg) {
@@ -494,7 +562,7 @@ void build_plan(pack_ctx& c) {
     // the recipe, stream starts, zeroed statistics and error flag and the pad
     // row lie together at the start of the workspace: laid out in the pinned
     // staging area as on the device and sent with one copy
-    c.pin_off = 0;
+    reset_staging(c);
     {
         uint8_t* const dbase = reinterpret_cast<uint8_t*>(p.gbase);
         const size_t span = static_cast<size_t>(reinterpret_cast<uint8_t*>(p.pad16 + 16) - dbase);
@@ -538,8 +606,8 @@ void build_plan(pack_ctx& c) {
     c.timer.begin(PACK_PHASE_KEYS, st);
     dp::launch_keep_scan(p, st);
     c.timer.end(st);
-    const uint32_t* h_err = d2h_staged(c, p.err, 1);
-    const uint32_t* h_kept = d2h_staged(c, p.kept_pos + p.n_docs, 1);
+    const uint32_t* h_err = down(c, p.err, 1);
+    const uint32_t* h_kept = down(c, p.kept_pos + p.n_docs, 1);
     sync_staged(c);
     uint32_t err = *h_err;
     if (err & dp::ERR_INTERNAL) throw InternalError{"internal: a scan's bounded wait gave up (library bug)"};
@@ -607,13 +675,14 @@ void build_plan(pack_ctx& c) {
     }
     dp::launch_checks(p, st);
     c.timer.end(st);
-    const uint32_t* h_upd = d2h_staged(c, p.n_upd, p.S);
-    const uint64_t* h_stats = d2h_staged(c, p.stats, 4ull * p.S);
-    const uint64_t* h_checks = d2h_staged(c, p.checks, 2);
-    const uint64_t* h_sps = d2h_staged(c, p.src_piece_start, p.S + 1);
-    const uint32_t* h_pieces = d2h_staged(c, p.piece_start + p.n_kept, 1);
-    const uint64_t* h_sws = d2h_staged(c, p.src_win_start, p.S + 1);
-    h_err = d2h_staged(c, p.err, 1);
+    // the plan's counts back to the host: one gather kernel and one copy
+    const uint32_t* h_upd = down(c, p.n_upd, p.S);
+    const uint64_t* h_stats = down(c, p.stats, 4ull * p.S);
+    const uint64_t* h_checks = down(c, p.checks, 2);
+    const uint64_t* h_sps = down(c, p.src_piece_start, p.S + 1);
+    const uint32_t* h_pieces = down(c, p.piece_start + p.n_kept, 1);
+    const uint64_t* h_sws = down(c, p.src_win_start, p.S + 1);
+    h_err = down(c, p.err, 1);
     sync_staged(c);
     p.n_pieces_dev = nullptr;  // host counts from here on
     p.n_windows_dev = nullptr;
@@ -884,7 +953,7 @@ int pack_cycle(pack_ctx* c, uint32_t cycle, pack_cycle_info* info) {
         dp::Plan& p = c->p;
         uint64_t U = c->cfg.updates_per_cycle;
         const uint64_t* h_sums = nullptr;
-        c->pin_off = 0;
+        reset_staging(*c);
         // tokens trained before the cycle
         const uint64_t t0 = cycle == c->cfg.first_cycle ? c->cfg.tokens_start : c->tokens_next;
         std::vector<uint32_t> upd_B;
@@ -953,7 +1022,7 @@ int pack_cycle(pack_ctx* c, uint32_t cycle, pack_cycle_info* info) {
                 if (*h_err & dp::ERR_INTERNAL) throw InternalError{"internal: cumulative schedule (library bug)"};
                 const uint64_t got = h_out[Sr];
                 for (uint32_t v = 0; v < S; ++v) taken[v] = h_out[v / L];
-                c->pin_off = 0;
+                reset_staging(*c);
                 if (got == 0 || (U && got < U)) {
                     c->err = "a source cannot supply the cycle's windows";
                     return PACK_E_EXHAUSTED;
@@ -1027,35 +1096,27 @@ int pack_cycle(pack_ctx* c, uint32_t cycle, pack_cycle_info* info) {
         const uint32_t U32 = (uint32_t)U;
         std::vector<uint64_t> next(S);
         for (uint32_t s = 0; s < S; ++s) next[s] = start[s] + taken[s];
-        c->timer.begin(PACK_PHASE_CYCLE, c->st);
-        h2d_staged(*c, p.cyc_start, start.data(), S);
-        if (p.tabled) dp::launch_cum_slots(p, U32, c->st);
+        // every upload of the cycle is computed on the host first: the stream
+        // starts, the read order's source starts, each stream's next window
+        // and the plan digest's message go to the device together
+        std::vector<uint64_t> ps;
         if (p.read_random) {  // each source's cycle windows in their random read order
-            std::vector<uint64_t> ps(S + 1, 0);
+            ps.assign(S + 1, 0);
             for (uint32_t s = 0; s < S; ++s) ps[s + 1] = ps[s] + taken[s];
-            h2d_staged(*c, p.perm_start, ps.data(), S + 1);
-            dp::launch_read_order(p, cycle, ps[S], c->st);
         }
-        dp::launch_cycle_sums(p, slots, c->st);
-        h_sums = d2h_staged(*c, p.cyc_sums, 2);
-        {  // each stream's first token of the next cycle
-            std::vector<uint64_t> nw(S);
-            for (uint32_t s = 0; s < S; ++s) {
-                const uint64_t M = c->src_win_start[s + 1] - c->src_win_start[s];
-                nw[s] = next[s] < M ? c->src_win_start[s] + next[s] : ~0ull;
-            }
-            h2d_staged(*c, c->next_win, nw.data(), S);
-            dp::launch_stream_next(p, c->next_win, c->stream_next, c->st);
+        std::vector<uint64_t> nw(S);  // each stream's first window of the next cycle
+        for (uint32_t s = 0; s < S; ++s) {
+            const uint64_t M = c->src_win_start[s + 1] - c->src_win_start[s];
+            nw[s] = next[s] < M ? c->src_win_start[s] + next[s] : ~0ull;
         }
-        const uint64_t* h_next = d2h_staged(*c, c->stream_next, S);
 
         // plan digest: SHA-256 of a little-endian header (mode, the recipe's
         // scalars, the cycle, its updates, two order-free sums over the plan)
         // followed by the digests of the streams' 60-byte records, 8 streams
         // to a leaf (one wavefront each), so the serial chain stays short: a
         // leaf is 8 blocks, and the top hash grows by one block per 2 leaves.
-        // The records, then the header, go to the device in one copy; the
-        // leaf digests are written after the header there.
+        // The records, then the header, go to the device with the cycle's
+        // other uploads; the leaf digests are written after the header there.
         constexpr uint32_t REC = 60, LEAF = 8;
         std::vector<uint8_t> msg;
         for (uint32_t s = 0; s < S; ++s) {
@@ -1105,20 +1166,32 @@ int pack_cycle(pack_ctx* c, uint32_t cycle, pack_cycle_info* info) {
         const size_t head_bytes = msg.size() - rec_bytes;
         const uint32_t leaves = (S + LEAF - 1) / LEAF;
         if (rec_bytes + head_bytes + 32ull * leaves > c->dig_cap) throw InvalError{"internal: digest buffer"};
-        h2d_staged(*c, c->dig_buf, msg.data(), msg.size());
+
+        c->timer.begin(PACK_PHASE_CYCLE, c->st);
+        up(*c, p.cyc_start, start.data(), S);
+        if (p.read_random) up(*c, p.perm_start, ps.data(), S + 1);
+        up(*c, c->next_win, nw.data(), S);
+        up(*c, c->dig_buf, msg.data(), msg.size());
+        up_flush(*c);
+        if (p.tabled) dp::launch_cum_slots(p, U32, c->st);
+        if (p.read_random) dp::launch_read_order(p, cycle, ps[S], c->st);
+        dp::launch_cycle_sums(p, slots, c->st);
+        dp::launch_stream_next(p, c->next_win, c->stream_next, c->st);  // each stream's first token of the next cycle
         uint8_t* const head = c->dig_buf + rec_bytes;
         dp::launch_sha_chunks(c->dig_buf, rec_bytes, REC * LEAF, head + head_bytes, c->st);
         dp::launch_sha_bytes(head, head_bytes + 32ull * leaves, c->dig_buf + c->dig_cap, c->st);
         c->timer.end(c->st);
-        const uint8_t* h_digest = d2h_staged(*c, (const uint8_t*)(c->dig_buf + c->dig_cap), 32);
-        const uint32_t* h_cerr = d2h_staged(*c, p.err, 1);
-        DP_HIP(hipStreamSynchronize(c->st));
+        h_sums = down(*c, p.cyc_sums, 2);
+        const uint64_t* h_next = down(*c, c->stream_next, S);
+        const uint8_t* h_digest = down(*c, (const uint8_t*)(c->dig_buf + c->dig_cap), 32);
+        const uint32_t* h_cerr = down(*c, p.err, 1);
+        sync_staged(*c);
         const uint64_t sums[2] = {h_sums[0], h_sums[1]};
         std::vector<uint64_t> next_tok(h_next, h_next + S);
         uint8_t digest[32];
         std::memcpy(digest, h_digest, 32);
         const uint32_t cerr = *h_cerr;
-        c->pin_off = 0;
+        reset_staging(*c);
         if (cerr & dp::ERR_INTERNAL) throw InternalError{"internal: a cycle kernel found the plan inconsistent (library bug)"};
 
         // commit the cycle
@@ -1156,18 +1229,18 @@ int pack_cycle(pack_ctx* c, uint32_t cycle, pack_cycle_info* info) {
         return PACK_OK;
     } catch (const InvalError& e) {
         c->err = e.msg;
-        c->pin_off = 0;
+        reset_staging(*c);
         return PACK_E_INVAL;
     } catch (const InternalError& e) {
         c->err = e.msg;
-        c->pin_off = 0;
+        reset_staging(*c);
         return PACK_E_INTERNAL;
     } catch (const dp::HipError& e) {
-        c->pin_off = 0;
+        reset_staging(*c);
         return fail_hip(c, e);
     } catch (const std::bad_alloc&) {
         c->err = "host allocation failed";
-        c->pin_off = 0;
+        reset_staging(*c);
         return PACK_E_NOMEM;
     }
 }
@@ -1177,11 +1250,11 @@ int pack_status(pack_ctx* c) {
     c->err.clear();
     try {
         // the staging area is free between calls: every call resets it after its synchronization
-        c->pin_off = 0;
+        reset_staging(*c);
         const uint32_t* h = d2h_staged(*c, c->p.err_batch, 1);
         DP_HIP(hipStreamSynchronize(c->st));
         const uint32_t e = *h;
-        c->pin_off = 0;
+        reset_staging(*c);
         if (e & dp::ERR_INTERNAL) {
             dp::launch_zero_u32(c->p.err_batch, 1, c->st);
             DP_HIP(hipStreamSynchronize(c->st));
@@ -1191,7 +1264,7 @@ int pack_status(pack_ctx* c) {
         }
         return PACK_OK;
     } catch (const dp::HipError& e) {
-        c->pin_off = 0;
+        reset_staging(*c);
         return fail_hip(c, e);
     }
 }

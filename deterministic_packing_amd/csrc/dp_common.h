@@ -317,6 +317,21 @@ void launch_apportion(Plan& p, uint64_t W, uint32_t B, uint32_t* n_out, hipStrea
 void launch_zero_u64(uint64_t* a, uint64_t n, hipStream_t st);
 void launch_zero_u32(uint32_t* a, uint64_t n, hipStream_t st);
 void launch_fill_u32(uint32_t* a, uint64_t n, uint32_t v, hipStream_t st);
+
+// up to XFER_MAX device-to-device copies of small ranges in one launch (the
+// host's uploads and downloads pass through a contiguous mailbox, so a batch of
+// them costs one copy and this kernel); pointers 4-byte aligned
+constexpr uint32_t XFER_MAX = 16;
+struct Xfer {
+    const uint8_t* src;
+    uint8_t* dst;
+    uint64_t bytes;
+};
+struct XferList {
+    Xfer x[XFER_MAX];
+    uint32_t n;
+};
+void launch_xfer(const XferList& l, hipStream_t st);
 uint64_t sort_hist_words(uint64_t n, uint64_t G);
 void launch_checks(Plan& p, hipStream_t st);          // order / hash checks
 void launch_cycle_sums(Plan& p, uint64_t total_slots, hipStream_t st);

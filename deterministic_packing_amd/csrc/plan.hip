@@ -36,6 +36,16 @@ __global__ __launch_bounds__(256) void k_fill_u32(uint32_t* a, uint64_t n, uint3
     if (i < n) a[i] = v;
 }
 
+// one block per range: 4-byte words, then the last bytes
+__global__ __launch_bounds__(256) void k_xfer(XferList l) {
+    const Xfer x = l.x[blockIdx.x];
+    const uint64_t words = x.bytes / 4;
+    const uint32_t* s = reinterpret_cast<const uint32_t*>(x.src);
+    uint32_t* d = reinterpret_cast<uint32_t*>(x.dst);
+    for (uint64_t i = threadIdx.x; i < words; i += blockDim.x) d[i] = s[i];
+    for (uint64_t i = 4 * words + threadIdx.x; i < x.bytes; i += blockDim.x) x.dst[i] = x.src[i];
+}
+
 __global__ __launch_bounds__(256) void k_zero_u64(uint64_t* a, uint64_t n) {
     const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n) a[i] = 0;
@@ -1007,6 +1017,16 @@ void launch_zero_u32(uint32_t* a, uint64_t n, hipStream_t st) { launch_fill_u32(
 
 void launch_fill_u32(uint32_t* a, uint64_t n, uint32_t v, hipStream_t st) {
     if (n) hipLaunchKernelGGL(k_fill_u32, dim3(blocks_for(n)), dim3(256), 0, st, a, n, v);
+    DP_HIP(hipGetLastError());
+}
+
+void launch_xfer(const XferList& l, hipStream_t st) {
+    if (l.n == 0) return;
+    if (l.n > XFER_MAX) throw HipError{hipErrorInvalidValue, "internal: transfer list"};
+    for (uint32_t i = 0; i < l.n; ++i)
+        if ((reinterpret_cast<uintptr_t>(l.x[i].src) | reinterpret_cast<uintptr_t>(l.x[i].dst)) & 3u)
+            throw HipError{hipErrorInvalidValue, "internal: unaligned transfer"};
+    hipLaunchKernelGGL(k_xfer, dim3(l.n), dim3(256), 0, st, l);
     DP_HIP(hipGetLastError());
 }
 
