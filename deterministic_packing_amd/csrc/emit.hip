@@ -11,7 +11,14 @@
 //
 // One workgroup per window.  The window's piece table is staged in LDS; each
 // thread produces 4 consecutive positions and writes them with one 16-byte
-// store per int32 array and one 4-byte store of the mask.
+// store per int32 array and one 4-byte store of the mask.  In padded windows
+// these stores are non-temporal: the outputs stream to HBM without taking
+// cache lines (about 4 % faster, and the kernels after the batch find no dirty
+// output lines to write back).  Padding-free rows keep ordinary stores: their
+// edge groups are written element by element into lines that neighbouring
+// windows share, and mixing the two kinds there made the rows about 10 %
+// slower.  So do the digest kernels, which store the same arrays: non-temporal
+// stores from their few, long-running waves made them 2-3x slower.
 #include "dp_common.h"
 
 namespace dp {
@@ -25,6 +32,33 @@ typedef uint32_t u32x4a4 __attribute__((ext_vector_type(4), aligned(4)));  // 16
 __device__ __forceinline__ void load4(const uint32_t* src, uint32_t (&tk)[4]) {
     const u32x4a4 x = *reinterpret_cast<const u32x4a4*>(src);
     tk[0] = x.x; tk[1] = x.y; tk[2] = x.z; tk[3] = x.w;
+}
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// one group of 4 positions: 16 bytes of each int32 array, 4 mask bytes
+template <bool NT>
+__device__ __forceinline__ void store_group(uint32_t* tok, int32_t* pos, int32_t* doc, uint8_t* mask, uint64_t g,
+                                           const uint32_t (&tk)[4], const int32_t (&ps)[4], const int32_t (&dc)[4],
+                                           uint32_t mk) {
+    const u32x4 t{tk[0], tk[1], tk[2], tk[3]};
+    const u32x4 o{(uint32_t)ps[0], (uint32_t)ps[1], (uint32_t)ps[2], (uint32_t)ps[3]};
+    const u32x4 d{(uint32_t)dc[0], (uint32_t)dc[1], (uint32_t)dc[2], (uint32_t)dc[3]};
+    u32x4* const t4 = reinterpret_cast<u32x4*>(tok) + g;
+    u32x4* const o4 = reinterpret_cast<u32x4*>(pos) + g;
+    u32x4* const d4 = reinterpret_cast<u32x4*>(doc) + g;
+    uint32_t* const m4 = reinterpret_cast<uint32_t*>(mask) + g;
+    if constexpr (NT) {
+        __builtin_nontemporal_store(t, t4);
+        __builtin_nontemporal_store(o, o4);
+        __builtin_nontemporal_store(d, d4);
+        __builtin_nontemporal_store(mk, m4);
+    } else {
+        *t4 = t;
+        *o4 = o;
+        *d4 = d;
+        *m4 = mk;
+    }
 }
 
 struct PieceView {
@@ -91,10 +125,6 @@ __global__ __launch_bounds__(EB) void k_emit(Plan p, EmitArgs a) {
     if constexpr (!PACKED) {
         // padded windows: window widx is [widx·T, (widx+1)·T) of the outputs
         const uint64_t out0 = (uint64_t)widx * p.T;
-        uint4* tok4 = reinterpret_cast<uint4*>(a.tok + out0);
-        int4* pos4 = reinterpret_cast<int4*>(a.pos + out0);
-        int4* doc4 = reinterpret_cast<int4*>(a.doc + out0);
-        uint32_t* mask4 = reinterpret_cast<uint32_t*>(a.mask + out0);
         for (uint32_t g = threadIdx.x; g < p.T / 4; g += EB) {
             const uint32_t t0 = 4 * g;
             uint32_t tk[4];
@@ -138,10 +168,7 @@ __global__ __launch_bounds__(EB) void k_emit(Plan p, EmitArgs a) {
                     }
                 }
             }
-            tok4[g] = make_uint4(tk[0], tk[1], tk[2], tk[3]);
-            pos4[g] = make_int4(ps[0], ps[1], ps[2], ps[3]);
-            doc4[g] = make_int4(dc[0], dc[1], dc[2], dc[3]);
-            mask4[g] = mk;
+            store_group<true>(a.tok + out0, a.pos + out0, a.doc + out0, a.mask + out0, g, tk, ps, dc, mk);
         }
     } else {
         // padding-free rows: window jj of update i from row position row_start[i][jj]
@@ -153,10 +180,6 @@ __global__ __launch_bounds__(EB) void k_emit(Plan p, EmitArgs a) {
         const uint32_t lead = (uint32_t)(out0 & 3u);
         const uint64_t base = out0 - lead;
         const uint32_t span = lead + real;
-        uint4* tok4 = reinterpret_cast<uint4*>(a.tok + base);
-        int4* pos4 = reinterpret_cast<int4*>(a.pos + base);
-        int4* doc4 = reinterpret_cast<int4*>(a.doc + base);
-        uint32_t* mask4 = reinterpret_cast<uint32_t*>(a.mask + base);
         for (uint32_t g = threadIdx.x; g < (span + 3) / 4; g += EB) {
             const int32_t tb = (int32_t)(4 * g) - (int32_t)lead;  // window position of the group's first element
             const uint32_t tf = tb < 0 ? 0u : (uint32_t)tb;       // first position inside the window
@@ -199,10 +222,7 @@ __global__ __launch_bounds__(EB) void k_emit(Plan p, EmitArgs a) {
                 }
             }
             if (tb >= 0 && (uint32_t)tb + 4 <= real) {
-                tok4[g] = make_uint4(tk[0], tk[1], tk[2], tk[3]);
-                pos4[g] = make_int4(ps[0], ps[1], ps[2], ps[3]);
-                doc4[g] = make_int4(dc[0], dc[1], dc[2], dc[3]);
-                mask4[g] = mk;
+                store_group<false>(a.tok + base, a.pos + base, a.doc + base, a.mask + base, g, tk, ps, dc, mk);
             } else {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
