@@ -478,7 +478,7 @@ void check_config(const pack_config* cfg) {
     if (cfg->n_sources < 1 || cfg->n_sources > 4096) bad("n_sources must be in [1, 4096]");
     if (!cfg->share_weight || !cfg->holdout_bp) bad("share_weight and holdout_bp are required");
     const uint32_t T = cfg->window_tokens, B = cfg->global_batch;
-    if (T < 64 || T > (1u << 20) || T % 64) bad("window_tokens must be a multiple of 64 in [64, 2^20]");
+    if (T < 1 || T > (1u << 20)) bad("window_tokens must be in [1, 2^20]");
     if (B < 1 || B > (1u << 20)) bad("global_batch must be in [1, 2^20]");
     if (cfg->world < 1 || cfg->rank >= cfg->world) bad("need world >= 1 and rank < world");
     if (B % cfg->world) bad("world must divide global_batch");

@@ -68,7 +68,7 @@ struct PieceView {
 
 // PACKED: padding-free rows (Linnet Training, the transformers Trainer path):
 // window jj of update i writes only its real positions, at row position
-// a.row_start[i][jj] of update i's row (stride B/world·T), one element at a time.
+// a.row_start[i][jj] of update i's row (stride B/world·T), through emit_span.
 template <bool PACKED>
 __global__ __launch_bounds__(EB) void k_emit(Plan p, EmitArgs a) {
     __shared__ uint32_t s_woff[ECAP];
@@ -122,7 +122,80 @@ __global__ __launch_bounds__(EB) void k_emit(Plan p, EmitArgs a) {
     };
 
     const uint32_t pad = p.pad_token;
+    // Window positions [0, len) at output element out0, which need not be a
+    // multiple of 4 (padding-free rows start anywhere; padded windows when T is
+    // not): positions from `real` on are padding.  Store groups are 4
+    // destination elements aligned to 16 bytes; the window may start mid-group
+    // (`lead` elements of that group belong to the previous window), and groups
+    // that straddle the window's ends are written element by element so that
+    // neighbouring windows never overwrite each other.
+    auto emit_span = [&](uint64_t out0, uint32_t len) {
+        const uint32_t lead = (uint32_t)(out0 & 3u);
+        const uint64_t base = out0 - lead;
+        const uint32_t span = lead + len;
+        for (uint32_t g = threadIdx.x; g < (span + 3) / 4; g += EB) {
+            const int32_t tb = (int32_t)(4 * g) - (int32_t)lead;  // window position of the group's first element
+            const uint32_t tf = tb < 0 ? 0u : (uint32_t)tb;       // first position inside the window
+            uint32_t tk[4];
+            int32_t ps[4], dc[4];
+            uint32_t mk = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { tk[e] = pad; ps[e] = 0; dc[e] = -1; }
+            if (tf < real) {
+                uint32_t q = find(tf);
+                PieceView v = get(q);
+                uint32_t next_woff = (q + 1 < np) ? (staged ? s_woff[q + 1] : p.pc_woff[q0 + q + 1]) : real;
+                const uint32_t u0 = tf - v.woff;
+                if (tb >= 0 && tf + 4 <= next_woff && tf + 4 <= real && v.src + u0 + 4 <= p.n_tokens) {
+                    // the four positions in one piece: one 16-byte load of their tokens
+                    load4(p.tokens + v.src + u0, tk);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        ps[e] = (int32_t)(u0 + e);
+                        dc[e] = (int32_t)v.doc;
+                        mk |= (tf + e >= v.mfrom ? 1u : 0u) << (8 * e);
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int32_t ts = tb + e;
+                        if (ts < 0 || (uint32_t)ts >= real) continue;
+                        const uint32_t t = (uint32_t)ts;
+                        while (t >= next_woff && q + 1 < np) {  // next piece (contiguous up to `real`)
+                            ++q;
+                            v = get(q);
+                            next_woff = (q + 1 < np) ? (staged ? s_woff[q + 1] : p.pc_woff[q0 + q + 1]) : real;
+                        }
+                        const uint32_t u = t - v.woff;
+                        tk[e] = (v.src + u < p.n_tokens) ? p.tokens[v.src + u] : pad;  // guard: never read past the corpus
+                        ps[e] = (int32_t)u;
+                        dc[e] = (int32_t)v.doc;
+                        mk |= (t >= v.mfrom ? 1u : 0u) << (8 * e);
+                    }
+                }
+            }
+            if (tb >= 0 && (uint32_t)tb + 4 <= len) {
+                store_group<false>(a.tok + base, a.pos + base, a.doc + base, a.mask + base, g, tk, ps, dc, mk);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int32_t ts = tb + e;
+                    if (ts < 0 || (uint32_t)ts >= len) continue;
+                    const uint64_t o = base + 4 * (uint64_t)g + e;
+                    a.tok[o] = tk[e];
+                    a.pos[o] = ps[e];
+                    a.doc[o] = dc[e];
+                    a.mask[o] = (uint8_t)(mk >> (8 * e));
+                }
+            }
+        }
+    };
+
     if constexpr (!PACKED) {
+        if (p.T % 4) {  // window widx is [widx·T, (widx+1)·T) of the outputs, not on 16-byte boundaries
+            emit_span((uint64_t)widx * p.T, p.T);
+            return;
+        }
         // padded windows: window widx is [widx·T, (widx+1)·T) of the outputs
         const uint64_t out0 = (uint64_t)widx * p.T;
         for (uint32_t g = threadIdx.x; g < p.T / 4; g += EB) {
@@ -172,70 +245,7 @@ __global__ __launch_bounds__(EB) void k_emit(Plan p, EmitArgs a) {
         }
     } else {
         // padding-free rows: window jj of update i from row position row_start[i][jj]
-        const uint64_t out0 = (uint64_t)i * a.per * p.T + (uint64_t)a.row_start[(uint64_t)i * (a.per + 1) + jj];
-        // Store groups are 4 destination elements aligned to 16 bytes.  A packed
-        // window may start mid-group: `lead` elements of that group belong to the
-        // previous window, and groups that straddle the window's ends are written
-        // element by element so that neighbouring windows never overwrite each other.
-        const uint32_t lead = (uint32_t)(out0 & 3u);
-        const uint64_t base = out0 - lead;
-        const uint32_t span = lead + real;
-        for (uint32_t g = threadIdx.x; g < (span + 3) / 4; g += EB) {
-            const int32_t tb = (int32_t)(4 * g) - (int32_t)lead;  // window position of the group's first element
-            const uint32_t tf = tb < 0 ? 0u : (uint32_t)tb;       // first position inside the window
-            uint32_t tk[4];
-            int32_t ps[4], dc[4];
-            uint32_t mk = 0;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) { tk[e] = pad; ps[e] = 0; dc[e] = -1; }
-            if (tf < real) {
-                uint32_t q = find(tf);
-                PieceView v = get(q);
-                uint32_t next_woff = (q + 1 < np) ? (staged ? s_woff[q + 1] : p.pc_woff[q0 + q + 1]) : real;
-                const uint32_t u0 = tf - v.woff;
-                if (tb >= 0 && tf + 4 <= next_woff && tf + 4 <= real && v.src + u0 + 4 <= p.n_tokens) {
-                    // the four positions in one piece: one 16-byte load of their tokens
-                    load4(p.tokens + v.src + u0, tk);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        ps[e] = (int32_t)(u0 + e);
-                        dc[e] = (int32_t)v.doc;
-                        mk |= (tf + e >= v.mfrom ? 1u : 0u) << (8 * e);
-                    }
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int32_t ts = tb + e;
-                        if (ts < 0 || (uint32_t)ts >= real) continue;
-                        const uint32_t t = (uint32_t)ts;
-                        while (t >= next_woff && q + 1 < np) {  // next piece (contiguous up to `real`)
-                            ++q;
-                            v = get(q);
-                            next_woff = (q + 1 < np) ? (staged ? s_woff[q + 1] : p.pc_woff[q0 + q + 1]) : real;
-                        }
-                        const uint32_t u = t - v.woff;
-                        tk[e] = (v.src + u < p.n_tokens) ? p.tokens[v.src + u] : pad;  // guard: never read past the corpus
-                        ps[e] = (int32_t)u;
-                        dc[e] = (int32_t)v.doc;
-                        mk |= (t >= v.mfrom ? 1u : 0u) << (8 * e);
-                    }
-                }
-            }
-            if (tb >= 0 && (uint32_t)tb + 4 <= real) {
-                store_group<false>(a.tok + base, a.pos + base, a.doc + base, a.mask + base, g, tk, ps, dc, mk);
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int32_t ts = tb + e;
-                    if (ts < 0 || (uint32_t)ts >= real) continue;
-                    const uint64_t o = base + 4 * (uint64_t)g + e;
-                    a.tok[o] = tk[e];
-                    a.pos[o] = ps[e];
-                    a.doc[o] = dc[e];
-                    a.mask[o] = (uint8_t)(mk >> (8 * e));
-                }
-            }
-        }
+        emit_span((uint64_t)i * a.per * p.T + (uint64_t)a.row_start[(uint64_t)i * (a.per + 1) + jj], real);
     }
 }
 

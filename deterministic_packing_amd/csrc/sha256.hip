@@ -967,6 +967,48 @@ __global__ __launch_bounds__(WAVE) void k_sha_chunks(const uint8_t* msg, uint64_
     sha_bytes_wave(msg + x0, x1 - x0, out + 32ull * blockIdx.x, kw);
 }
 
+// ---------------------------------------------------------------- any window length
+// T not a multiple of 64: the emission kernel writes the windows first, then
+// this kernel hashes each window's record from the outputs, one lane per
+// window.  Word j of the padded message (its bytes 4j .. 4j+3, big-endian for
+// the compression) is element j of tok, pos, doc for j < 3T (each array is 4T
+// bytes, so no word straddles two of them); from byte 12T on come the T mask
+// bytes, the byte 0x80, zeros, and the message's bit length 104·T as 8
+// big-endian bytes that end the last block (FIPS 180-4, section 5.1.1).
+__global__ __launch_bounds__(256) void k_window_digest_any(Plan p, EmitArgs a) {
+    const uint64_t w = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (w >= a.n_out) return;
+    const uint64_t T = p.T, o = w * T;
+    const uint32_t* tok = a.tok + o;
+    const int32_t* pos = a.pos + o;
+    const int32_t* doc = a.doc + o;
+    const uint8_t* mask = a.mask + o;
+    const uint64_t L = 13 * T;              // message bytes
+    const uint64_t nb = (L + 72) / 64;      // blocks: L + 1 + 8 bytes rounded up to 64
+    const uint64_t tail = 64 * nb - 8, bits = 8 * L;
+    auto byte_at = [&](uint64_t i) -> uint32_t {  // byte i ≥ 12T of the padded message
+        if (i < L) return mask[i - 12 * T];
+        if (i == L) return 0x80u;
+        if (i >= tail) return (uint32_t)(bits >> (8 * (7 - (i - tail)))) & 0xFFu;
+        return 0u;
+    };
+    uint32_t H[8];
+    sha256_init(H);
+    for (uint64_t b = 0; b < nb; ++b) {
+        uint32_t W[16];
+#pragma unroll
+        for (uint32_t e = 0; e < 16; ++e) {
+            const uint64_t j = 16 * b + e;
+            if (j < T) W[e] = bswap32(tok[j]);
+            else if (j < 2 * T) W[e] = bswap32((uint32_t)pos[j - T]);
+            else if (j < 3 * T) W[e] = bswap32((uint32_t)doc[j - 2 * T]);
+            else W[e] = byte_at(4 * j) << 24 | byte_at(4 * j + 1) << 16 | byte_at(4 * j + 2) << 8 | byte_at(4 * j + 3);
+        }
+        sha256_compress(H, W);
+    }
+    store_digest(H, a.digests + 32 * w);
+}
+
 }  // namespace
 
 // Launch shape by the number of waves of 64 windows (each a chain of 13·T/64 + 1
@@ -979,7 +1021,10 @@ void launch_emit_sha(const Plan& p, const EmitArgs& a, hipStream_t st) {
     const uint64_t n = a.n_out;  // < 2^31 windows: at most 2^23 workgroups
     const uint64_t waves = (n + 63) / 64;
     if (!n) return;
-    if (waves <= 256)
+    if (p.T % 64) {  // records not made of whole 64-byte blocks per array: emission, then digests from the outputs
+        launch_emit(p, a, st);
+        hipLaunchKernelGGL(k_window_digest_any, dim3((uint32_t)((n + 255) / 256)), dim3(256), 0, st, p, a);
+    } else if (waves <= 256)
         hipLaunchKernelGGL(k_emit_ring<1>, dim3((uint32_t)waves), dim3(128), 0, st, p, a, n);
     else if (waves <= 512)
         hipLaunchKernelGGL(k_emit_ring<2>, dim3((uint32_t)((waves + 1) / 2)), dim3(256), 0, st, p, a, n);

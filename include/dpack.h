@@ -143,8 +143,9 @@ typedef struct pack_timings {
  * tokens; offsets monotone with doc_offsets[n_docs] ≤ n_tokens;
  * 1 ≤ n_sources ≤ 4096;
  * source < n_sources; stratum < n_strata[source]; Σ n_strata ≤ 65536;
- * Σ share_weight in [1, 2^64); holdout_bp ≤ 10000; T a multiple of 64 in
- * [64, 2^20]; 1 ≤ B ≤ 2^20; world ≥ 1 divides B; rank < world; with a
+ * Σ share_weight in [1, 2^64); holdout_bp ≤ 10000; 1 ≤ T ≤ 2^20 (any T;
+ * with T a multiple of 64 the window digests are computed beside the
+ * emission, otherwise from the emitted outputs after it); 1 ≤ B ≤ 2^20; world ≥ 1 divides B; rank < world; with a
  * ramp: n_ramp ≤ 4096, ramp_from[0] = 0 and rising, every ramp_tokens[k] a
  * multiple of T whose batch B_k = ramp_tokens[k]/T world divides, and B the
  * largest B_k.

@@ -63,7 +63,8 @@ def _cfg(**kw):
     ("abi_version", 99, dp.PACK_E_ABI),
     ("world", 3, dp.PACK_E_INVAL),          # world must divide B (fail fast, as the pages require)
     ("rank", 5, dp.PACK_E_INVAL),
-    ("window_tokens", 100, dp.PACK_E_INVAL),
+    ("window_tokens", 0, dp.PACK_E_INVAL),
+    ("window_tokens", (1 << 20) + 1, dp.PACK_E_INVAL),
     ("global_batch", 0, dp.PACK_E_INVAL),
     ("n_docs", 0, dp.PACK_E_INVAL),
     ("flags", 64, dp.PACK_E_INVAL),

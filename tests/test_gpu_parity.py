@@ -926,3 +926,47 @@ def test_timing_flags_change_no_output():
     for t in (True, "batch"):
         ms, n = tms[t]["digest"]
         assert n == 1 and ms > 0, tms[t]
+
+
+# Window lengths that are not multiples of 64 (1, 3 and 17 not even of 4):
+# padded windows that start off 16-byte boundaries go through the span writer,
+# and the digests come from the emitted outputs, hashed by their own kernel.
+ANY_T_CASES = [(1, 4), (3, 3), (17, 5), (60, 4), (100, 4), (130, 2), (1000, 3), (4095, 2), (4097, 2)]
+
+
+def _any_t(T, B, wrap):
+    return random_small(80 + T % 97, n_docs=90, n_sources=2, max_strata=2, T=T, B=B, max_len=max(3, 2 * T),
+                        prompts=True, bp_max=1500).replace(wrap=wrap)
+
+
+@pytest.mark.parametrize("T,B", ANY_T_CASES)
+@pytest.mark.parametrize("wrap", [False, True])
+def test_any_window_length_parity(T, B, wrap):
+    _parity_run(_any_t(T, B, wrap), ("wrap-" if wrap else "") + f"T{T}", B)
+
+
+@pytest.mark.parametrize("T,B", [(3, 4), (100, 4), (4095, 2)])
+def test_any_window_length_without_digests_and_padding_free(T, B):
+    """The emission kernel alone, padded and in padding-free rows of two ranks."""
+    c = _any_t(T, B, False)
+    op = oracle.Plan(c)
+    oi = op.cycle(0)
+    n = min(4, oi.n_updates)
+    say("any T, no digests", T, B)
+    pk = dp.Packer(c)
+    pk.cycle(0)
+    compare_batch(to_np(pk.batch(0, n, digests=False)), op.batch(0, n, digests=False), f"T{T} no digests")
+    pk.close()
+    for rank in (0, 1):
+        say("any T, padding-free rows", T, B, "rank", rank)
+        pk = dp.Packer(c, rank=rank, world=2)
+        pk.cycle(0)
+        g = {k: (v.cpu().numpy() if v is not None else None) for k, v in pk.batch_packed(0, n, 8).items()}
+        o = op.batch_packed(0, n, rank=rank, world=2, bucket=8)
+        assert np.array_equal(g["row_start"], o["row_start"]) and np.array_equal(g["length"], o["length"])
+        for i in range(n):
+            L = int(o["length"][i])
+            for k in ("tokens", "pos", "doc", "mask"):
+                a = g[k][i, :L].view(np.uint32) if k == "tokens" else g[k][i, :L]
+                assert np.array_equal(a, o[k][i, :L]), (i, k)
+        pk.close()

@@ -35,9 +35,9 @@ def test_sha256_random_lengths():
         assert oracle.sha256(data) == hashlib.sha256(data).digest()
 
 
-def test_window_digest_is_sha256_of_record():
-    r = np.random.default_rng(6)
-    T = 64
+@pytest.mark.parametrize("T", [1, 3, 17, 60, 64, 100, 4095])
+def test_window_digest_is_sha256_of_record(T):
+    r = np.random.default_rng(6 + T)
     tok = r.integers(0, 2**32, size=T, dtype=np.uint32)
     pos = r.integers(-5, 100, size=T).astype(np.int32)
     doc = r.integers(-1, 1000, size=T).astype(np.int32)
