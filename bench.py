@@ -247,13 +247,24 @@ def main():
                 entry.update(emission_inside=fused, bytes_per_launch=digest_bytes,
                              achieved_GBps=round(digest_bytes / (per_launch_ms / 1e3) / 1e9, 1))
         kernels[k] = entry
-    # profiles are taken per kernel and workload, with and without padding-free rows
-    prof_tag = args.workload + ("_packed" if args.packed else "")
+    # profiles are taken per kernel and workload, with and without padding-free rows, in the
+    # plain mode only: another mode can run another kernel (the held-out stream's few windows
+    # take the ring kernel) or other bytes, so it reports no traffic; the hash does not depend
+    # on how the windows are emitted
+    moded = (args.wrap or args.lanes > 1 or args.ramp or args.cumulative or args.read_random or args.heldout
+             or args.arrivals > 1 or args.resume or args.scale != 1.0)
+
+    def traffic_of(k):
+        if moded:
+            return None
+        return traffic_from_profile(k, args.workload if k == "hash" else
+                                    args.workload + ("_packed" if args.packed else ""))
+
     dominant = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
     dom = kernels[dominant]
     roofline = None
     if "bound" in dom:
-        traffic = traffic_from_profile(dominant, prof_tag)
+        traffic = traffic_of(dominant)
         roofline = {"kernel": dominant, "bound": dom["bound"], "achieved": dom["achieved"], "peak": dom["peak"],
                     "unit": dom["unit"], "frac": dom["frac"], "traffic": traffic}
     # the HBM-bound kernels, each against the HBM roofline
@@ -262,7 +273,7 @@ def main():
         e = kernels.get(k, {})
         if "achieved" in e:
             side[k] = {"kernel": k, "bound": "hbm", "achieved": e["achieved"], "peak": HBM_PEAK_GBPS,
-                       "unit": "GB/s", "frac": e["frac"], "traffic": traffic_from_profile(k, prof_tag)}
+                       "unit": "GB/s", "frac": e["frac"], "traffic": traffic_of(k)}
     if "emit" not in side:
         # the emission kernel on its own (pack_batch without digests over the
         # same cycle, into the same buffers), timed by the library's events
@@ -281,7 +292,7 @@ def main():
         ach = emit_bytes / (per_launch_ms / 1e3) / 1e9
         side["emit"] = {"kernel": "emit", "bound": "hbm", "achieved": round(ach, 2), "peak": HBM_PEAK_GBPS,
                         "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4),
-                        "traffic": traffic_from_profile("emit", prof_tag),
+                        "traffic": traffic_of("emit"),
                         "ms_per_launch": round(per_launch_ms, 4), "work_per_launch": emit_bytes,
                         "measured": f"pack_batch without digests over the whole cycle, {reps} launches"}
         log(f"emission alone: {per_launch_ms:.3f} ms per cycle, {ach:.1f} GB/s")
