@@ -42,7 +42,8 @@ int main(void)
     int bad = 0;
 
     c.abi_version = 1; bad |= expect(pack_init(&c, &ctx), PACK_E_ABI, "abi"); c = base;
-    c.window_tokens = 100; bad |= expect(pack_init(&c, &ctx), PACK_E_INVAL, "T not a multiple of 64"); c = base;
+    c.window_tokens = 0; bad |= expect(pack_init(&c, &ctx), PACK_E_INVAL, "T = 0"); c = base;
+    c.window_tokens = (1u << 20) + 1; bad |= expect(pack_init(&c, &ctx), PACK_E_INVAL, "T above 2^20"); c = base;
     c.global_batch = 0; bad |= expect(pack_init(&c, &ctx), PACK_E_INVAL, "B = 0"); c = base;
     c.world = 3; bad |= expect(pack_init(&c, &ctx), PACK_E_INVAL, "world does not divide B"); c = base;
     c.rank = 1; bad |= expect(pack_init(&c, &ctx), PACK_E_INVAL, "rank >= world"); c = base;
@@ -59,6 +60,8 @@ int main(void)
     c.n_docs = 1u << 22; c.n_tokens = 1ull << 32;
     bad |= expect(pack_init_noalloc(&c, &ctx), PACK_E_INVAL, "no-alloc workspace limit"); c = base;
     c.flags = PACK_FLAG_TIMING; bad |= expect(pack_init_noalloc(&c, &ctx), PACK_E_INVAL, "no-alloc timing"); c = base;
+    c.flags = PACK_FLAG_TIMING_BATCH;
+    bad |= expect(pack_init_noalloc(&c, &ctx), PACK_E_INVAL, "no-alloc batch timing"); c = base;
     bad |= ctx != NULL;
     for (int k = -9; k <= 0; ++k) bad |= pack_strerror(k) == NULL || pack_strerror(k)[0] == 0;
     bad |= pack_last_error(NULL) == NULL;
