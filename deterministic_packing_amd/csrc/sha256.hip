@@ -887,7 +887,9 @@ __global__ __launch_bounds__(64) void k_batch_fp_var(const uint8_t* digests, con
 // only the round function (about 14 of the 22 instructions of a round).
 constexpr uint32_t KW_ROW = 65;
 
-__device__ __forceinline__ void sha256_compress_kw(uint32_t H[8], const uint32_t* kw) {
+// kw: the block's 64 round words K[t] + W[t], in registers (loaded from LDS
+// before the rounds, so the chain waits for LDS once per block, not per round)
+__device__ __forceinline__ void sha256_compress_kw(uint32_t H[8], const uint32_t (&kw)[64]) {
     uint32_t a = H[0], b = H[1], c = H[2], d = H[3], e = H[4], f = H[5], g = H[6], h = H[7];
 #pragma unroll
     for (int t = 0; t < 64; ++t) {
@@ -917,7 +919,7 @@ __device__ __forceinline__ uint32_t padded_word(const uint8_t* msg, uint64_t len
     return word;
 }
 
-__device__ void sha_bytes_wave(const uint8_t* msg, uint64_t len, uint8_t* out, uint32_t* kw) {
+__device__ __forceinline__ void sha_bytes_wave(const uint8_t* msg, uint64_t len, uint8_t* out, uint32_t* kw) {
     const uint32_t lane = lane_id();
     const uint64_t nblk = (len + 9 + 63) / 64;
     uint32_t H[8];
@@ -947,7 +949,12 @@ __device__ void sha_bytes_wave(const uint8_t* msg, uint64_t len, uint8_t* out, u
         __syncthreads();  // one wavefront per workgroup: its schedule rows are in LDS
         if (lane == 0) {
             const uint64_t n = nblk - b0 < WAVE ? nblk - b0 : WAVE;
-            for (uint64_t k = 0; k < n; ++k) sha256_compress_kw(H, kw + k * KW_ROW);
+            for (uint64_t k = 0; k < n; ++k) {
+                uint32_t r[64];
+#pragma unroll
+                for (int t = 0; t < 64; ++t) r[t] = kw[k * KW_ROW + t];
+                sha256_compress_kw(H, r);
+            }
         }
         __syncthreads();  // the rows are consumed before the next group overwrites them
     }
