@@ -958,7 +958,9 @@ int pack_cycle(pack_ctx* c, uint32_t cycle, pack_cycle_info* info) {
         const uint64_t t0 = cycle == c->cfg.first_cycle ? c->cfg.tokens_start : c->tokens_next;
         std::vector<uint32_t> upd_B;
         std::vector<uint64_t> upd_out0;
-        dp::launch_zero_u32(p.err, 1, c->st);  // cycle kernels flag internal failures here
+        // cycle kernels flag internal failures in err: zeroed here when kernels run before the
+        // uploads below (ramp, cumulative schedule), else with the uploads
+        if (p.tabled) dp::launch_zero_u32(p.err, 1, c->st);
         if (p.tabled) {
             // per-update counts: the cumulative schedule and/or a batch-size ramp
             uint64_t total = 0;
@@ -1168,6 +1170,10 @@ int pack_cycle(pack_ctx* c, uint32_t cycle, pack_cycle_info* info) {
         if (rec_bytes + head_bytes + 32ull * leaves > c->dig_cap) throw InvalError{"internal: digest buffer"};
 
         c->timer.begin(PACK_PHASE_CYCLE, c->st);
+        const uint32_t zero_err = 0;
+        const uint64_t zero_sums[2] = {0, 0};
+        if (!p.tabled) up(*c, p.err, &zero_err, 1);
+        up(*c, p.cyc_sums, zero_sums, 2);
         up(*c, p.cyc_start, start.data(), S);
         if (p.read_random) up(*c, p.perm_start, ps.data(), S + 1);
         up(*c, c->next_win, nw.data(), S);
@@ -1175,8 +1181,7 @@ int pack_cycle(pack_ctx* c, uint32_t cycle, pack_cycle_info* info) {
         up_flush(*c);
         if (p.tabled) dp::launch_cum_slots(p, U32, c->st);
         if (p.read_random) dp::launch_read_order(p, cycle, ps[S], c->st);
-        dp::launch_cycle_sums(p, slots, c->st);
-        dp::launch_stream_next(p, c->next_win, c->stream_next, c->st);  // each stream's first token of the next cycle
+        dp::launch_cycle_sums(p, slots, c->next_win, c->stream_next, c->st);  // and each stream's next first token
         uint8_t* const head = c->dig_buf + rec_bytes;
         dp::launch_sha_chunks(c->dig_buf, rec_bytes, REC * LEAF, head + head_bytes, c->st);
         dp::launch_sha_bytes(head, head_bytes + 32ull * leaves, c->dig_buf + c->dig_cap, c->st);

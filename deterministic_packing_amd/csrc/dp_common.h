@@ -334,7 +334,10 @@ struct XferList {
 void launch_xfer(const XferList& l, hipStream_t st);
 uint64_t sort_hist_words(uint64_t n, uint64_t G);
 void launch_checks(Plan& p, hipStream_t st);          // order / hash checks
-void launch_cycle_sums(Plan& p, uint64_t total_slots, hipStream_t st);
+// the cycle's real and learned sums into cyc_sums (zeroed before), and each
+// stream's first token of the window next_win[s] (~0: the stream's total)
+void launch_cycle_sums(Plan& p, uint64_t total_slots, const uint64_t* next_win, uint64_t* stream_next,
+                       hipStream_t st);
 // cumulative mixture of a cycle: the schedule (cum_A, cum_out), then, once the
 // host has accepted U, every update's slot table.  integral: every update's
 // seats times every weight is a multiple of W (the schedule has a closed form)
@@ -346,8 +349,6 @@ void launch_lane_source(const uint16_t* source, uint64_t n_docs, uint32_t S_real
 void launch_lane_expand(Plan& p, const uint32_t* n_real, const uint32_t* lane_src, const uint32_t* lane_k,
                         hipStream_t st);
 void launch_cum_expand(Plan& p, const uint32_t* cum_Ar, uint64_t U, hipStream_t st);
-// each stream's first token of the window next_win[s] (~0: the stream's total)
-void launch_stream_next(Plan& p, const uint64_t* next_win, uint64_t* out, hipStream_t st);
 // batch-size ramp: piece spans of a cycle (host-computed) → per-update tables (RampSpan above)
 void launch_ramp_fill(Plan& p, const RampSpan* spans, uint32_t n_spans, uint64_t n_upd, hipStream_t st);
 // fixed apportionment with a ramp: cum_A[u][s] = Σ over spans of whole updates before u · n_s of the span's piece

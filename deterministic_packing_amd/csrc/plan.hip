@@ -771,9 +771,20 @@ __global__ __launch_bounds__(256) void k_checks(Plan p) {
     block_add2(oc, hc, p.checks);
 }
 
-__global__ __launch_bounds__(256) void k_cycle_sums(Plan p, uint64_t total) {
+// The cycle's sums over its slots (cyc_sums zeroed before); block 0 also
+// writes each stream's token, in its merged order, where window next_win[s]
+// begins (pc_pre holds the order's token prefix), or the stream's total when
+// next_win[s] = ~0 (used up): where the next cycle starts.
+__global__ __launch_bounds__(256) void k_cycle_sums(Plan p, uint64_t total, const uint64_t* next_win,
+                                                    uint64_t* stream_next) {
     // test option: report an internal failure of the cycle (pack_cycle must fail)
     if ((p.test_opts & TEST_CYCLE_FAULT) && blockIdx.x == 0 && threadIdx.x == 0) atomicOr(p.err, ERR_INTERNAL);
+    if (blockIdx.x == 0)
+        for (uint32_t s = threadIdx.x; s < p.S; s += blockDim.x) {
+            const uint64_t base = p.opre[p.src_doc_start[s]];
+            const uint64_t w = next_win[s];
+            stream_next[s] = w == ~0ull ? p.opre[p.src_doc_start[s + 1]] - base : p.pc_pre[p.win_first[w]] - base;
+        }
     uint64_t real = 0, learn = 0;
     for (uint64_t idx = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
          idx += (uint64_t)gridDim.x * blockDim.x) {
@@ -821,16 +832,6 @@ __global__ __launch_bounds__(256) void k_ramp_fixed_A(Plan p, const RampSpan* sp
         a += (upto - sp[k].first) * ramp_n[(uint64_t)sp[k].k * p.S + s];
     }
     p.cum_A[x] = (uint32_t)a;
-}
-
-// each stream's token (in its merged order) where window next_win[s] begins,
-// or its total when ~0 (used up): pc_pre holds the order's token prefix
-__global__ __launch_bounds__(256) void k_stream_next(Plan p, const uint64_t* next_win, uint64_t* out) {
-    const uint32_t s = blockIdx.x * blockDim.x + threadIdx.x;
-    if (s >= p.S) return;
-    const uint64_t base = p.opre[p.src_doc_start[s]];
-    const uint64_t w = next_win[s];
-    out[s] = w == ~0ull ? p.opre[p.src_doc_start[s + 1]] - base : p.pc_pre[p.win_first[w]] - base;
 }
 
 // ------------------------------------------------------------------ lanes
@@ -989,11 +990,6 @@ void launch_ramp_fixed_A(Plan& p, const RampSpan* spans, uint32_t n_spans, const
     DP_HIP(hipGetLastError());
 }
 
-void launch_stream_next(Plan& p, const uint64_t* next_win, uint64_t* out, hipStream_t st) {
-    hipLaunchKernelGGL(k_stream_next, dim3(blocks_for(p.S)), dim3(256), 0, st, p, next_win, out);
-    DP_HIP(hipGetLastError());
-}
-
 // p.checks was zeroed by the validation kernel
 void launch_checks(Plan& p, hipStream_t st) {
     const uint64_t n = p.n_docs > p.n_kept ? p.n_docs : p.n_kept;
@@ -1001,10 +997,10 @@ void launch_checks(Plan& p, hipStream_t st) {
     DP_HIP(hipGetLastError());
 }
 
-void launch_cycle_sums(Plan& p, uint64_t total, hipStream_t st) {  // total: the cycle's slots
-    hipLaunchKernelGGL(k_zero_u64, dim3(1), dim3(256), 0, st, p.cyc_sums, (uint64_t)2);
-    if (total)
-        hipLaunchKernelGGL(k_cycle_sums, dim3(std::min<uint32_t>(blocks_for(total), 512)), dim3(256), 0, st, p, total);
+void launch_cycle_sums(Plan& p, uint64_t total, const uint64_t* next_win, uint64_t* stream_next,
+                       hipStream_t st) {  // total: the cycle's slots
+    const uint32_t blocks = total ? std::min<uint32_t>(blocks_for(total), 512) : 1u;
+    hipLaunchKernelGGL(k_cycle_sums, dim3(blocks), dim3(256), 0, st, p, total, next_win, stream_next);
     DP_HIP(hipGetLastError());
 }
 
