@@ -314,7 +314,6 @@ void launch_window_count(Plan& p, hipStream_t st);    // src_win_start
 void launch_windows(Plan& p, hipStream_t st);         // win_first, pc_woff, win_real, win_learn
 void launch_mixture_w(Plan& p, uint64_t W, uint32_t* nstart, hipStream_t st);  // n_upd, slot table
 void launch_apportion(Plan& p, uint64_t W, uint32_t B, uint32_t* n_out, hipStream_t st);  // n_s of a batch B
-void launch_zero_u64(uint64_t* a, uint64_t n, hipStream_t st);
 void launch_zero_u32(uint32_t* a, uint64_t n, hipStream_t st);
 void launch_fill_u32(uint32_t* a, uint64_t n, uint32_t v, hipStream_t st);
 

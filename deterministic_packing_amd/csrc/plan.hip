@@ -46,11 +46,6 @@ __global__ __launch_bounds__(256) void k_xfer(XferList l) {
     for (uint64_t i = 4 * words + threadIdx.x; i < x.bytes; i += blockDim.x) x.dst[i] = x.src[i];
 }
 
-__global__ __launch_bounds__(256) void k_zero_u64(uint64_t* a, uint64_t n) {
-    const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n) a[i] = 0;
-}
-
 // group_start[g] for every group: the sorted documents come group by group,
 // so the element where the group changes writes the start of its group and of
 // the empty groups just before it (the first element from group 0 on, the last
@@ -1001,11 +996,6 @@ void launch_cycle_sums(Plan& p, uint64_t total, const uint64_t* next_win, uint64
                        hipStream_t st) {  // total: the cycle's slots
     const uint32_t blocks = total ? std::min<uint32_t>(blocks_for(total), 512) : 1u;
     hipLaunchKernelGGL(k_cycle_sums, dim3(blocks), dim3(256), 0, st, p, total, next_win, stream_next);
-    DP_HIP(hipGetLastError());
-}
-
-void launch_zero_u64(uint64_t* a, uint64_t n, hipStream_t st) {
-    if (n) hipLaunchKernelGGL(k_zero_u64, dim3(blocks_for(n)), dim3(256), 0, st, a, n);
     DP_HIP(hipGetLastError());
 }
 
