@@ -1,6 +1,7 @@
 """Seeded random combinations of every mode on small corpora (wrap packing,
 random read order, cumulative mixture, lanes, batch-size ramp, held-out
-stream, arrivals, stream starts), for parity between the GPU and the oracle."""
+stream, arrivals, stream starts, window lengths that are not multiples of
+64), for parity between the GPU and the oracle."""
 import numpy as np
 
 import oracle
@@ -33,6 +34,11 @@ def _draw(corpus_seed, seed, seq, even):
     ramp = r.random() < 0.3
     heldout = r.random() < 0.2
     T = 64 * int(r.choice([1, 2]))
+    # about a third of the combinations take a window length that is not a multiple of 64 (nor of 4),
+    # drawn from a stream of its own so the other draws stay as they were
+    t_alt = np.random.default_rng(np.random.SeedSequence(seq + [77]))
+    if t_alt.random() < 0.35:
+        T = int(t_alt.choice([37, 100]))
     m = 2 * L if even else L
     b = [m * int(x) for x in r.integers(1, 4, size=2)]
     B = max(b) if ramp else m * int(r.integers(1, 4))
