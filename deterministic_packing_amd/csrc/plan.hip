@@ -29,7 +29,9 @@ __device__ inline uint32_t upper_bound_u64(const uint64_t* a, uint32_t n, uint64
 // result is the merge of the strata by (a/A, k) and the output position of
 // element (k, j) is j plus, for every other stratum k', the number of its
 // elements ordered before it — counted by binary search with exact 128-bit
-// cross-multiplication.
+// cross-multiplication.  The merged order's token prefix comes the same way:
+// the element's stratum's tokens before it plus, for every other stratum, the
+// tokens of the elements counted before it (and the units before its own).
 
 __global__ __launch_bounds__(256) void k_fill_u32(uint32_t* a, uint64_t n, uint32_t v) {
     const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -108,6 +110,7 @@ __global__ __launch_bounds__(256) void k_merge(Plan p, const uint32_t* val) {
     auto frac = [&](uint64_t j) { return p.gpre[j] - p.gpre[b0]; };  // consumed tokens before element j
     const uint64_t a = frac(active ? i : ilast);
     uint64_t rank = (active ? i : ilast) - b0;
+    uint64_t before = a;  // tokens of the unit's documents merged before this one: own stratum first
     for (uint32_t kb = 0; kb < K; kb += MERGE_K) {
         if (one_group) {
             __syncthreads();  // the previous chunk's bounds are read
@@ -128,20 +131,30 @@ __global__ __launch_bounds__(256) void k_merge(Plan p, const uint32_t* val) {
             const uint32_t c0 = p.group_start[g0 + k2], c1 = p.group_start[g0 + k2 + 1];
             if (c0 == c1) continue;
             const uint32_t lo = one_group ? s_lo[k2 - kb] : 0u, hi = one_group ? s_hi[k2 - kb] : c1 - c0;
-            rank += count_before(p, c0, c1, k2 < k, a, A, lo, hi);
+            const uint32_t n = count_before(p, c0, c1, k2 < k, a, A, lo, hi);
+            rank += n;
+            before += p.gpre[c0 + n] - p.gpre[c0];
         }
     }
     if (blockIdx.x == 0)  // each stream's first position in the merged order (a stream's first arrival)
         for (uint32_t x = threadIdx.x; x <= p.S; x += blockDim.x) p.src_doc_start[x] = p.group_start[p.gbase[x * p.n_seg]];
     if (!active) return;
     const uint64_t at = p.group_start[g0] + rank;
-    if (at < p.n_kept) p.order[at] = d;
-    else atomicOr(p.err, ERR_INTERNAL);
+    if (at < p.n_kept) {
+        p.order[at] = d;
+        // the token prefix of the merged order: the units before this one (their groups come first in
+        // the sorted order, so gpre counts them), then this unit's documents merged before this one
+        p.opre[at] = p.gpre[p.group_start[g0]] + before;
+    } else {
+        atomicOr(p.err, ERR_INTERNAL);
+    }
+    if (i == p.n_kept - 1) p.opre[p.n_kept] = p.gpre[p.n_kept];
 }
 
 __global__ void k_src_doc_start(Plan p) {
     const uint32_t s = blockIdx.x * blockDim.x + threadIdx.x;
     if (s <= p.S) p.src_doc_start[s] = p.group_start[p.gbase[s * p.n_seg]];  // a stream's first arrival
+    if (s == 0) p.opre[0] = 0;  // no kept document
 }
 
 // ------------------------------------------------------------------ A5 pieces
@@ -881,8 +894,8 @@ void launch_merge(Plan& p, hipStream_t st) {
     DP_HIP(hipGetLastError());
 }
 
+// p.opre, the token prefix of the merged order, was written by the merge
 void launch_piece_count(Plan& p, hipStream_t st) {
-    scan_len_u64(p.order, p.offsets, p.n_kept, p.opre, p.scan, st);
     if (p.wrap)
         scan_wrap_pieces_u32(p.order, p.offsets, p.opre, p.src_doc_start, p.source, p.start_tok, p.T, p.n_kept,
                              p.piece_start, p.scan, st);
