@@ -66,11 +66,60 @@ __host__ __device__ inline int cmp_mul128(uint64_t a, uint64_t b, uint64_t c, ui
 }
 
 // ---------------------------------------------------------------- wave helpers
-__device__ inline uint64_t wave_sum_u64(uint64_t v) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);
+// Cross-lane moves by DPP, in registers (no LDS crossbar): row_shr:n (lane i
+// reads lane i − n of its row of 16), row_bcast:15 / row_bcast:31 (lane 15 /
+// 31 to the next row / rows), wave_shr:1 (lane i reads lane i − 1),
+// wave_shl:1 (lane i reads lane i + 1).  A lane whose source lies outside the
+// pattern, or whose row is masked off, keeps `old`.  Every lane of the
+// wavefront must be active.
+enum : int {
+    DPP_ROW_SHR1 = 0x111, DPP_ROW_SHR2 = 0x112, DPP_ROW_SHR4 = 0x114, DPP_ROW_SHR8 = 0x118,
+    DPP_WAVE_SHL1 = 0x130, DPP_WAVE_SHR1 = 0x138, DPP_BCAST15 = 0x142, DPP_BCAST31 = 0x143,
+};
+
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp32(uint32_t old, uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, ROWS, 0xF, false);
+}
+
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint64_t dpp64(uint64_t old, uint64_t v) {
+    const uint32_t lo = dpp32<CTRL, ROWS>((uint32_t)old, (uint32_t)v);
+    const uint32_t hi = dpp32<CTRL, ROWS>((uint32_t)(old >> 32), (uint32_t)(v >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Inclusive sum over lanes 0 .. l, in lane l: within rows of 16 by shifts of
+// 1, 2, 4, 8, then row 0's total into row 1 and row 2's into row 3, then
+// lane 31's into rows 2 and 3.  Every lane must be active.
+__device__ __forceinline__ uint64_t wave_incl_u64(uint64_t v) {
+    v += dpp64<DPP_ROW_SHR1, 0xF>(0, v);
+    v += dpp64<DPP_ROW_SHR2, 0xF>(0, v);
+    v += dpp64<DPP_ROW_SHR4, 0xF>(0, v);
+    v += dpp64<DPP_ROW_SHR8, 0xF>(0, v);
+    v += dpp64<DPP_BCAST15, 0xA>(0, v);
+    v += dpp64<DPP_BCAST31, 0xC>(0, v);
     return v;
 }
+
+__device__ __forceinline__ uint32_t wave_incl_u32(uint32_t v) {
+    v += dpp32<DPP_ROW_SHR1, 0xF>(0, v);
+    v += dpp32<DPP_ROW_SHR2, 0xF>(0, v);
+    v += dpp32<DPP_ROW_SHR4, 0xF>(0, v);
+    v += dpp32<DPP_ROW_SHR8, 0xF>(0, v);
+    v += dpp32<DPP_BCAST15, 0xA>(0, v);
+    v += dpp32<DPP_BCAST31, 0xC>(0, v);
+    return v;
+}
+
+__device__ __forceinline__ uint64_t readlane64(uint64_t v, uint32_t k) {
+    const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, (int)k);
+    const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), (int)k);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// The sum of v over the wavefront, in every lane.  Every lane must be active.
+__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) { return readlane64(wave_incl_u64(v), WAVE - 1); }
 
 __device__ inline uint32_t lane_id() { return __lane_id(); }
 

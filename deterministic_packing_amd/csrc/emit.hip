@@ -261,12 +261,7 @@ __global__ __launch_bounds__(256) void k_packed_starts(Plan p, EmitArgs a) {
     for (uint32_t c0 = 0; c0 < per; c0 += 256) {
         const uint32_t jj = c0 + threadIdx.x;
         const uint64_t v = jj < per ? p.win_real[window_of(p, (uint64_t)a.step + i, a.rank * per + jj)] : 0;
-        uint64_t x = v;  // inclusive scan in the wave
-#pragma unroll
-        for (int o = 1; o < WAVE; o <<= 1) {
-            const uint64_t y = __shfl_up(x, o, WAVE);
-            if (lane >= (uint32_t)o) x += y;
-        }
+        const uint64_t x = wave_incl_u64(v);  // inclusive scan in the wave (every thread takes part)
         if (lane == WAVE - 1) part[wid] = x;
         __syncthreads();
         uint64_t before = carry;

@@ -99,28 +99,6 @@ __device__ __forceinline__ void load_tokens(const uint32_t* tokens, uint64_t t0,
     x[TPT] = tokens[t0 + TPT];
 }
 
-// Cross-lane moves by DPP: row_shr:n (lane i reads lane i − n of its row of
-// 16), row_bcast:15 / row_bcast:31 (lane 15 / 31 to the next row / rows),
-// wave_shr:1 (lane i reads lane i − 1), wave_shl:1 (lane i reads lane i + 1).
-// A lane whose source lies outside the pattern, or whose row is masked off,
-// keeps `old`.  Every lane of the wavefront must be active.
-enum : int {
-    DPP_ROW_SHR1 = 0x111, DPP_ROW_SHR2 = 0x112, DPP_ROW_SHR4 = 0x114, DPP_ROW_SHR8 = 0x118,
-    DPP_WAVE_SHL1 = 0x130, DPP_WAVE_SHR1 = 0x138, DPP_BCAST15 = 0x142, DPP_BCAST31 = 0x143,
-};
-
-template <int CTRL, int ROWS>
-__device__ __forceinline__ uint32_t dpp32(uint32_t old, uint32_t v) {
-    return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, ROWS, 0xF, false);
-}
-
-template <int CTRL, int ROWS>
-__device__ __forceinline__ uint64_t dpp64(uint64_t old, uint64_t v) {
-    const uint32_t lo = dpp32<CTRL, ROWS>((uint32_t)old, (uint32_t)v);
-    const uint32_t hi = dpp32<CTRL, ROWS>((uint32_t)(old >> 32), (uint32_t)(v >> 32));
-    return ((uint64_t)hi << 32) | lo;
-}
-
 // One step of an inclusive scan of v segmented by the key f (nondecreasing
 // across lanes): the source lane's partial is added when its key is the same.
 template <int CTRL, int ROWS>
@@ -137,23 +115,6 @@ __device__ __forceinline__ void seg_scan(uint64_t& v, uint32_t f) {
     seg_step<DPP_ROW_SHR8, 0xF>(v, f);
     seg_step<DPP_BCAST15, 0xA>(v, f);
     seg_step<DPP_BCAST31, 0xC>(v, f);
-}
-
-// The sum of v over the wavefront, in lane WAVE − 1.
-__device__ __forceinline__ uint64_t wave_total(uint64_t v) {
-    v += dpp64<DPP_ROW_SHR1, 0xF>(0, v);
-    v += dpp64<DPP_ROW_SHR2, 0xF>(0, v);
-    v += dpp64<DPP_ROW_SHR4, 0xF>(0, v);
-    v += dpp64<DPP_ROW_SHR8, 0xF>(0, v);
-    v += dpp64<DPP_BCAST15, 0xA>(0, v);
-    v += dpp64<DPP_BCAST31, 0xC>(0, v);
-    return v;
-}
-
-__device__ __forceinline__ uint64_t readlane64(uint64_t v, uint32_t k) {
-    const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, (int)k);
-    const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), (int)k);
-    return ((uint64_t)hi << 32) | lo;
 }
 
 constexpr uint32_t NO_END = 0xFFFFFFFFu;  // no further document start within reach of the lane
@@ -210,7 +171,7 @@ __device__ __forceinline__ void hash_wave_tile(const Plan& p, uint64_t end, uint
             const uint32_t k0 = kp + 2u * i * PHI32;
             acc += (uint64_t)(a + k0) * (uint64_t)(b + k0 + PHI32);
         }
-        acc = wave_total(acc);
+        acc = wave_incl_u64(acc);
         if (lane == WAVE - 1) atomicAdd((unsigned long long*)&S[m.lo], (unsigned long long)acc);
         return;
     }
@@ -424,7 +385,7 @@ __global__ __launch_bounds__(256) void k_hash_final(Plan p, const uint64_t* S, u
             const uint32_t s0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)s);  // lane 0 is valid
             if (__all(!valid || s == s0)) {
                 const uint64_t kc = __popcll(__ballot(keep)), hc = __popcll(__ballot(held));
-                const uint64_t kl = wave_total(keep ? L : 0), hl = wave_total(held ? L : 0);
+                const uint64_t kl = wave_incl_u64(keep ? L : 0), hl = wave_incl_u64(held ? L : 0);
                 if (lane == WAVE - 1) {
                     if (kc) {
                         add_bin(bins, p.stats, s0, kc, lds_bins);

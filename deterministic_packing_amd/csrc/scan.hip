@@ -17,14 +17,11 @@ constexpr int STILE = SB * SI;   // items per tile
 
 template <typename T>
 __device__ T block_exclusive(T v, T* lds_wave, T* total) {
-    // inclusive wave scan
+    // inclusive wave scan (every thread of the block takes part)
     const int lane = threadIdx.x & (WAVE - 1), wid = threadIdx.x / WAVE;
-    T x = v;
-#pragma unroll
-    for (int o = 1; o < WAVE; o <<= 1) {
-        T y = __shfl_up(x, o, WAVE);
-        if (lane >= o) x += y;
-    }
+    T x;
+    if constexpr (sizeof(T) == 8) x = (T)wave_incl_u64((uint64_t)v);
+    else x = (T)wave_incl_u32((uint32_t)v);
     if (lane == WAVE - 1) lds_wave[wid] = x;
     __syncthreads();
     T before = 0, all = 0;
