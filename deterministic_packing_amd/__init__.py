@@ -322,7 +322,9 @@ class Packer:
         for k, v in arrs.items():
             setattr(info, k, v.ctypes.data)
         pack_cycle(self.ctx, c, info)
-        self.batches = pack_inspect(self.ctx, "update_batch")
+        # each update's batch: B without a ramp, else the library's per-update table
+        self.batches = (pack_inspect(self.ctx, "update_batch") if self.ramp
+                        else np.full(info.n_updates, self.corpus.B, np.uint32))
         out = dict(cycle=info.cycle, n_updates=info.n_updates, real_tokens=info.real_tokens,
                    learned_tokens=info.learned_tokens, positions=info.positions,
                    plan_digest=bytes(info.plan_digest), batches=self.batches)

@@ -72,6 +72,7 @@ def compare_cycle(gi: dict, oi: "oracle.CycleInfo", op: "oracle.Plan"):
         assert gi["real_tokens"] == oi.real_tokens
         assert gi["learned_tokens"] == oi.learned_tokens
     assert gi["positions"] == oi.positions
+    assert np.asarray(gi["batches"]).tolist() == [int(x) for x in oi.batches]
     if getattr(oi, "stream_next", None) is not None:
         assert gi["stream_next_token"].tolist() == oi.stream_next.tolist()
 

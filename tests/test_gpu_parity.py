@@ -535,6 +535,8 @@ def _parity_run(c, kind, arg):
         return
     gi = pk.cycle(cyc)
     compare_cycle(gi, oi, op)
+    # the library's per-update batches (the binding reads them only with a ramp)
+    assert pk.inspect("update_batch").tolist() == [int(x) for x in oi.batches]
     if getattr(c, "cumulative", False):
         assert np.array_equal(pk.inspect("cum_taken"), op.cumulative_taken().ravel())
     U = oi.n_updates
