@@ -972,3 +972,24 @@ def test_any_window_length_without_digests_and_padding_free(T, B):
                 a = g[k][i, :L].view(np.uint32) if k == "tokens" else g[k][i, :L]
                 assert np.array_equal(a, o[k][i, :L]), (i, k)
         pk.close()
+
+
+@pytest.mark.parametrize("T", [4000, 4100])
+@pytest.mark.parametrize("wrap", [False, True])
+def test_any_window_length_every_digest_of_a_cycle(T, wrap):
+    """The pre-train mix at 20,000 documents with T not a multiple of 64: every
+    window digest of the cycle (the emission, then the digests from the
+    outputs) against the oracle's, and the first and last updates whole."""
+    from _gpu_parity import oracle_digests
+    c = make_corpus("pretrain", 0.02, T=T, updates_per_cycle=0).replace(wrap=wrap)
+    op = oracle.Plan(c)
+    oi = op.cycle(0)
+    say("any T, whole cycle", T, "wrap", wrap, "updates", oi.n_updates)
+    pk = dp.Packer(c)
+    compare_cycle(pk.cycle(0), oi, op)
+    U = oi.n_updates
+    got = pk.batch(0, U)["digests"].cpu().numpy()
+    assert np.array_equal(got, oracle_digests(op, range(U)))
+    for st in sorted({0, U - 1}):
+        compare_batch(to_np(pk.batch(st, 1)), op.batch(st, 1), f"T{T} update {st}")
+    pk.close()
