@@ -490,31 +490,42 @@ __global__ __launch_bounds__(256) void k_slots(Plan p, const uint32_t* nstart) {
 // all taken); the only other released window of s is window fl+1 when
 // rm ≠ 0 and A_s ≤ fl, due by update δ = ceil((fl+1)·W/(B·w_s)) − 1, which
 // depends on fl alone: u + 1 when B·w_s ≥ W, else u + ceil((W − rm)/(B·w_s))
-// evaluated when fl last changed.  The B − Σ(fl − A_s)⁺ remaining seats go
-// to the candidates with the smallest (δ, s) (earliest deadline first).  The
-// schedule stops before the first update after which a source would exceed
-// the windows it has left, or after cap updates.  ONE_WAVE: S ≤ 64, one
-// wavefront, exchanges by cross-lane reads instead of LDS and barriers.
+// evaluated when fl last changed.  The B − Σ(fl − A_s)⁺ remaining seats R go
+// to the candidates with the smallest (δ, s) (earliest deadline first): every
+// wave finds the threshold key κ, the smallest with at least R candidates at
+// or below it, by galloping and bisecting over the due update with ballot
+// counts of the ROWS key rows (a row = the keys of 64 consecutive sources),
+// and a candidate takes a seat when its key is below κ or equals κ within
+// the first R − #(keys < κ) of those ties by source.  The schedule stops
+// before the first update after which a source would exceed the windows it
+// has left, or after cap updates.
+// ROWS = 1 (S ≤ 64): one wavefront, no LDS and no barrier.  ROWS > 1: each
+// update publishes the keys and the waves' sums in LDS behind one barrier
+// (double-buffered by the update's parity, so no second barrier guards their
+// reuse); whether an update fits the windows left is read at the next
+// update's barrier, and an update that does not fit is undone (its table row
+// lies past the cycle's U).
 constexpr uint32_t CUM_MAX_S = 1024;
 
-template <bool ONE_WAVE>
-__global__ __launch_bounds__(ONE_WAVE ? WAVE : CUM_MAX_S) void k_cumulative(Plan p, uint64_t W, uint64_t cap) {
-    __shared__ uint64_t key[ONE_WAVE ? 1 : CUM_MAX_S];
-    __shared__ uint64_t part[3][ONE_WAVE ? 1 : CUM_MAX_S / WAVE];
-    const uint32_t s = threadIdx.x, nw = blockDim.x / WAVE;
+template <uint32_t ROWS>
+__global__ __launch_bounds__(ROWS * WAVE) void k_cumulative(Plan p, uint64_t W, uint64_t cap) {
+    constexpr bool ONE = ROWS == 1;
+    __shared__ uint64_t key[ONE ? 1 : 2][ONE ? 1 : ROWS * WAVE];
+    __shared__ uint64_t part[ONE ? 1 : 2][3][ONE ? 1 : ROWS];
+    const uint32_t s = threadIdx.x, lane = s & (WAVE - 1), wv = s / WAVE;
     const bool on = s < p.S;
     const uint64_t w = on ? p.weight[s] : 0;
     // the update's step of the quota, B_u·w_s = qB·W + rB (recomputed when the batch changes)
-    uint64_t bw_hi = 0, bw = 0, rB = 0, qB = 0, QB = 0;
+    uint64_t bw_hi = 0, bw = 0, rB = 0, qB = 0;
     bool step_ge_W = false;  // fl grows every update
     uint32_t Bu = 0;
     const uint64_t rem = on ? p.cum_rem[s] : ~0ull;
     uint64_t fl = 0, rm = 0, A = 0, U = 0, due = 0;
-    bool bad = false;
+    uint64_t A_prev = 0;  // ROWS > 1: A before the update whose fit is not yet known
+    bool bad = false, over_prev = false, undone = false;
     if (on) p.cum_A[s] = 0;
-    // ONE_WAVE: Σ_s (fl − A)⁺ = Σ qB + #crossed − #ahead + #(qB = 0, not crossed, ahead), where
-    // ahead = (A = fl + 1) before the update: every term is a ballot count
-    for (uint64_t u = 0; u < cap; ++u) {
+    uint64_t u = 0;
+    for (; u < cap; ++u) {
         const uint32_t Bn = (p.ramp ? p.upd_B[u] : p.B) / p.lanes;  // this lane's seats in update u
         if (Bn != Bu) {  // uniform: the same batch for every source
             Bu = Bn;
@@ -523,10 +534,8 @@ __global__ __launch_bounds__(ONE_WAVE ? WAVE : CUM_MAX_S) void k_cumulative(Plan
             rB = 0;
             qB = w ? div128(bw_hi, bw, W, &rB) : 0;  // bw_hi < W since B·w < 2^20·W
             step_ge_W = bw_hi != 0 || bw >= W;
-            if (ONE_WAVE) QB = wave_sum_u64(qB);
         }
-        bool moved = false, crossed = false;
-        const bool ahead = A > fl;
+        bool moved = false;
         if (w) {  // q ← q + B·w_s/W
             uint64_t r2 = rm + rB;
             const bool carry = r2 < rm;
@@ -536,7 +545,6 @@ __global__ __launch_bounds__(ONE_WAVE ? WAVE : CUM_MAX_S) void k_cumulative(Plan
                 r2 -= W;
                 fl += 1;
                 moved = true;
-                crossed = true;
             }
             rm = r2;
         }
@@ -580,70 +588,99 @@ __global__ __launch_bounds__(ONE_WAVE ? WAVE : CUM_MAX_S) void k_cumulative(Plan
             }
         }
         const uint64_t k = cand ? due : ~0ull;
-        uint64_t sm, nc;
-        uint64_t lanes = 0;
-        if (ONE_WAVE) {
-            lanes = __ballot(cand);
-            sm = QB + (uint64_t)__popcll(__ballot(crossed)) - (uint64_t)__popcll(__ballot(ahead)) +
-                 (uint64_t)__popcll(__ballot(qB == 0 && !crossed && ahead));
-            nc = (uint64_t)__popcll(lanes);
-        } else {
-            key[s] = k;
-            const uint64_t v0 = wave_sum_u64(m), v1 = wave_sum_u64(cand ? 1 : 0);
-            if ((s & (WAVE - 1)) == 0) {
-                part[0][s / WAVE] = v0;
-                part[1][s / WAVE] = v1;
+        uint64_t sm = wave_sum_u64(m), nc = (uint64_t)__popcll(__ballot(cand));
+        const uint32_t par = (uint32_t)(u & 1);
+        if (!ONE) {
+            key[par][s] = k;
+            if (lane == 0) {
+                part[par][0][wv] = sm;
+                part[par][1][wv] = nc;
+                part[par][2][wv] = over_prev ? 1 : 0;  // the previous update took more than a source has
             }
             __syncthreads();
             sm = 0;
             nc = 0;
-            for (uint32_t i = 0; i < nw; ++i) {
-                sm += part[0][i];
-                nc += part[1][i];
+            uint64_t ovp = 0;
+#pragma unroll
+            for (uint32_t i = 0; i < ROWS; ++i) {
+                sm += part[par][0][i];
+                nc += part[par][1][i];
+                ovp += part[par][2][i];
             }
+            if (ovp) {  // update u − 1 does not fit: the cycle ends after u − 1 updates
+                A = A_prev;
+                undone = true;
+                break;
+            }
+            U = u;
         }
         if (sm > Bu || nc < Bu - sm) {  // the schedule's guarantee failed
             bad = true;
             break;
         }
         const uint64_t R = Bu - sm;
-        uint64_t rank = 0;
-        if (ONE_WAVE) {
-            const uint32_t klo = (uint32_t)k, khi = (uint32_t)(k >> 32);
-            if (lanes) {
-                const int f = __builtin_ctzll(lanes);  // every candidate due in the same update: by lane
-                const uint64_t d0 = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)khi, f) << 32) |
-                                    (uint32_t)__builtin_amdgcn_readlane((int)klo, f);
-                if (__ballot(cand && k != d0) == 0) {
-                    rank = (uint64_t)__popcll(lanes & ((1ull << s) - 1ull));
+        bool take = false;
+        if (R) {
+            uint64_t kr[ROWS];  // every wave holds all key rows (non-candidates ~0) and finds the same κ
+#pragma unroll
+            for (uint32_t r = 0; r < ROWS; ++r) kr[r] = ONE ? k : key[par][r * WAVE + lane];
+            auto count_le = [&](uint64_t thr) {
+                uint64_t c = 0;
+#pragma unroll
+                for (uint32_t r = 0; r < ROWS; ++r) c += (uint64_t)__popcll(__ballot(kr[r] <= thr));
+                return c;
+            };
+            // A candidate's window fl+1 is due after update u (fl would have moved in its due
+            // update), so no key is at most u: count_le(u) = 0 < R.  Keys stay below 2^64 − 1
+            // (dues lie within 2^62 updates), where the count is nc ≥ R.
+            constexpr uint64_t TOP = ~0ull - 1;
+            uint64_t lo = u, hi = u, below = 0, step = 1;
+            for (;;) {  // gallop: count_le(lo) = below < R
+                hi = step > TOP - lo ? TOP : lo + step;
+                const uint64_t c = count_le(hi);
+                if (c >= R) break;
+                lo = hi;
+                below = c;
+                step <<= 1;
+            }
+            while (hi - lo > 1) {  // count_le(lo) = below < R ≤ count_le(hi)
+                const uint64_t mid = lo + (hi - lo) / 2;
+                const uint64_t c = count_le(mid);
+                if (c >= R) {
+                    hi = mid;
                 } else {
-                    for (uint64_t rest = lanes; rest; rest &= rest - 1) {  // candidate lanes only
-                        const int t = __builtin_ctzll(rest);
-                        const uint64_t kt = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)khi, t) << 32) |
-                                            (uint32_t)__builtin_amdgcn_readlane((int)klo, t);
-                        rank += (kt < k || (kt == k && (uint32_t)t < s)) ? 1 : 0;
-                    }
+                    lo = mid;
+                    below = c;
                 }
             }
-        } else if (cand) {
-            for (uint32_t t = 0; t < p.S; ++t) rank += (key[t] < k || (key[t] == k && t < s)) ? 1 : 0;
+            // κ = hi; the ties at κ take the R − below seats left, lower sources first
+            const bool tie = cand && k == hi;
+            uint64_t rank = (uint64_t)__popcll(__ballot(tie) & ((1ull << lane) - 1ull));
+#pragma unroll
+            for (uint32_t r = 0; r + 1 < ROWS; ++r) rank += r < wv ? (uint64_t)__popcll(__ballot(kr[r] == hi)) : 0;
+            take = cand && (k < hi || (tie && rank < R - below));
         }
-        const uint64_t An = A + m + (cand && rank < R ? 1 : 0);
-        uint64_t ov;
-        if (ONE_WAVE) {
-            ov = __ballot(An > rem);
-        } else {
-            const uint64_t over = wave_sum_u64(An > rem ? 1 : 0);
-            __syncthreads();  // everyone has read part[] and key[]
-            if ((s & (WAVE - 1)) == 0) part[2][s / WAVE] = over;
-            __syncthreads();
-            ov = 0;
-            for (uint32_t i = 0; i < nw; ++i) ov += part[2][i];
+        const uint64_t An = A + m + (take ? 1 : 0);
+        if (ONE) {
+            if (__ballot(An > rem)) break;
+            A = An;
+            U = u + 1;
+        } else {  // the fit is read at the next update's barrier (or after the loop)
+            over_prev = __ballot(An > rem) != 0;
+            A_prev = A;
+            A = An;
         }
-        if (ov) break;
-        A = An;
-        U = u + 1;
-        if (on) p.cum_A[(u + 1) * p.S + s] = (uint32_t)A;
+        if (on) p.cum_A[(u + 1) * p.S + s] = (uint32_t)An;
+    }
+    if (!ONE && !bad && !undone && u == cap && cap) {  // the last update's fit
+        const uint32_t par = (uint32_t)(cap & 1);
+        if (lane == 0) part[par][2][wv] = over_prev ? 1 : 0;
+        __syncthreads();
+        uint64_t ovp = 0;
+#pragma unroll
+        for (uint32_t i = 0; i < ROWS; ++i) ovp += part[par][2][i];
+        if (ovp) A = A_prev;
+        else U = cap;
     }
     if (on) p.cum_out[s] = A;
     if (s == 0) p.cum_out[p.S] = U;
@@ -949,11 +986,14 @@ void launch_cumulative(Plan& p, uint64_t W, uint64_t cap, bool integral, hipStre
     if (integral) {
         hipLaunchKernelGGL(k_cum_integral_U, dim3(1), dim3(1024), 0, st, p, W, cap);
         hipLaunchKernelGGL(k_cum_integral_A, dim3(blocks_for((cap + 1) * p.S)), dim3(256), 0, st, p, W, cap);
-    } else if (p.S <= WAVE) {
-        hipLaunchKernelGGL(k_cumulative<true>, dim3(1), dim3(WAVE), 0, st, p, W, cap);
-    } else {
-        const uint32_t threads = ((p.S + WAVE - 1) / WAVE) * WAVE;
-        hipLaunchKernelGGL(k_cumulative<false>, dim3(1), dim3(threads), 0, st, p, W, cap);
+    } else {  // rows of 64 sources, a power of two
+        if (p.S > CUM_MAX_S) throw HipError{hipErrorInvalidValue, "internal: cumulative schedule over more than 1024 sources"};
+        const uint32_t rows = (p.S + WAVE - 1) / WAVE;
+        if (rows <= 1) hipLaunchKernelGGL(k_cumulative<1>, dim3(1), dim3(WAVE), 0, st, p, W, cap);
+        else if (rows <= 2) hipLaunchKernelGGL(k_cumulative<2>, dim3(1), dim3(2 * WAVE), 0, st, p, W, cap);
+        else if (rows <= 4) hipLaunchKernelGGL(k_cumulative<4>, dim3(1), dim3(4 * WAVE), 0, st, p, W, cap);
+        else if (rows <= 8) hipLaunchKernelGGL(k_cumulative<8>, dim3(1), dim3(8 * WAVE), 0, st, p, W, cap);
+        else hipLaunchKernelGGL(k_cumulative<16>, dim3(1), dim3(16 * WAVE), 0, st, p, W, cap);
     }
     DP_HIP(hipGetLastError());
 }

@@ -174,6 +174,37 @@ def test_cumulative_many_sources(S, B):
     _parity_run(c.replace(cumulative=True), "cumulative-many-sources", S)
 
 
+MANY_SOURCE_SCHEDULES = [
+    # (S, B, ramp, updates per cycle, tiny shares): schedules of many updates on the several-wavefront path
+    (70, 50, None, 0, False),
+    (130, 96, None, 0, True),
+    (257, 200, ((0, 120 * 64), (40 * 120 * 64, 200 * 64)), 0, True),
+    (1024, 300, None, 0, True),
+    (1024, 1500, None, 12, False),
+]
+
+
+@pytest.mark.parametrize("case", range(len(MANY_SOURCE_SCHEDULES)))
+def test_cumulative_many_sources_long_schedules(case):
+    """More sources than a wavefront over a cycle of many updates: weights near
+    each source's share of the tokens (so the schedule runs until the corpus is
+    nearly used), some of them tiny (windows due thousands of updates ahead),
+    with a batch-size ramp, up to 1,024 sources, and a cycle cut by its update
+    count; the per-update table, batches and fingerprints equal the oracle's."""
+    S, B, ramp, upc, tiny = MANY_SOURCE_SCHEDULES[case]
+    c = random_small(800 + case, n_docs=min(200 * S, 100000), n_sources=S, max_strata=2, T=64, B=B, max_len=100,
+                     bp_max=300, updates_per_cycle=upc)
+    r = np.random.default_rng(810 + case)
+    L = np.diff(c.offsets.astype(np.int64))
+    tok = np.bincount(c.source.astype(np.int64), weights=L, minlength=S)
+    w = np.round(tok * r.uniform(0.8, 1.2, size=S)).astype(np.uint64)
+    if tiny:
+        w[r.choice(S, size=max(2, S // 16), replace=False)] = 1
+    w[tok == 0] = 0
+    c = c.replace(weight=w, cumulative=True, ramp=ramp)
+    _parity_run(c, "cumulative-many-sources-long", case)
+
+
 def test_cumulative_small_share_parity():
     """A source below half a window per update: no windows under the fixed
     apportionment, its windows under the cumulative quotas."""
