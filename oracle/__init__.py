@@ -94,6 +94,8 @@ def _load():
         lib.or_emit_window.argtypes = [vp, u64, vp, vp, vp, vp]
         lib.or_window_digest.restype = None
         lib.or_window_digest.argtypes = [u32, vp, vp, vp, vp, vp]
+        lib.or_window_digests_chunked.restype = i32
+        lib.or_window_digests_chunked.argtypes = [u32, u64, vp, vp, vp, vp, vp]
         lib.or_batch.restype = i32
         lib.or_batch.argtypes = [vp, u32, u32, u32, u32, vp, vp, vp, vp, vp, vp]
         lib.or_batch_packed.restype = i32
@@ -194,6 +196,22 @@ def window_digest(tok, pos, doc, mask) -> bytes:
     mask = np.ascontiguousarray(mask, np.uint8)
     _load().or_window_digest(T, _ptr(tok), _ptr(pos), _ptr(doc), _ptr(mask), _ptr(out))
     return out.tobytes()
+
+
+def window_digests_chunked(tok, pos, doc, mask) -> np.ndarray:
+    """Chunked window digests of windows laid out [..., T]: [..., 32]."""
+    T = tok.shape[-1]
+    lead = tok.shape[:-1]
+    n = int(np.prod(lead)) if lead else 1
+    out = np.zeros(lead + (32,), dtype=np.uint8)
+    tok = np.ascontiguousarray(tok, np.uint32)
+    pos = np.ascontiguousarray(pos, np.int32)
+    doc = np.ascontiguousarray(doc, np.int32)
+    mask = np.ascontiguousarray(mask, np.uint8)
+    rc = _load().or_window_digests_chunked(T, n, _ptr(tok), _ptr(pos), _ptr(doc), _ptr(mask), _ptr(out))
+    if rc:
+        raise OracleError(rc, "window_digests_chunked")
+    return out
 
 
 def batch_fingerprint(window_digests: np.ndarray) -> bytes:
@@ -402,10 +420,13 @@ class Plan:
         mask = np.zeros(shape + (T,), np.uint8)
         lrn = np.zeros(n_steps, np.int64) if learned else None
         dig = np.zeros(shape + (32,), np.uint8) if digests else None
+        chunked = digests and getattr(self.corpus, "digest_chunked", False)
         rc = _load().or_batch(self._p, step, n_steps, rank, world, _ptr(tok), _ptr(pos), _ptr(doc),
-                              _ptr(mask), _ptr(lrn), _ptr(dig))
+                              _ptr(mask), _ptr(lrn), _ptr(None if chunked else dig))
         if rc:
             raise OracleError(rc, "batch")
+        if chunked:  # the same records, digested chunk by chunk
+            dig = window_digests_chunked(tok, pos, doc, mask)
         return dict(tokens=tok, pos=pos, doc=doc, mask=mask, learned=lrn, digests=dig)
 
     def batch_packed(self, step: int, n_steps: int = 1, rank: int = 0, world: int = 1, bucket: int = 256) -> dict:

@@ -30,6 +30,9 @@
  *   - Philox4x32-10: Salmon et al., SC'11; pinned against rocRAND's open
  *     implementation.
  *   - SHA-256: FIPS 180-4; pinned against Python's hashlib.
+ *   - window digests, whole-record (C8) and chunked: rebuilt from the record
+ *     bytes with Python's hashlib; a record of one chunk gives the double
+ *     SHA-256 of the record.
  *   - the sort uses the C library's qsort with a total order as comparator.
  *   - cumulative mixture (C6c): pinned by its requirements in exact integers
  *     (quota at every update boundary, monotone, B per update), by exhaustive
@@ -1188,6 +1191,49 @@ void or_window_digest(uint32_t T, const uint32_t *tok, const int32_t *pos, const
     memcpy(rec + 12ull * T, mask, T);
     or_sha256(rec, 13ull * T, out);
     free(rec);
+}
+
+/* Chunked window digest (PACK_FLAG_DIGEST_CHUNKED), a second reading of the
+ * window digest above, chosen so that one window's hashing is not one serial
+ * chain of 13·T/64 blocks: the same 13·T-byte record is cut into chunks of
+ * OR_DIGEST_CHUNK bytes (the last one shorter when 13·T is not a multiple),
+ * each chunk is hashed with SHA-256, and the window digest is the SHA-256 of
+ * the chunk digests concatenated in record order (32 bytes each).  A record
+ * of one chunk (T ≤ 315) thus has SHA-256(SHA-256(record)).  Returns OR_OK or
+ * OR_E_NOMEM. */
+#define OR_DIGEST_CHUNK 4096u
+
+int or_window_digest_chunked(uint32_t T, const uint32_t *tok, const int32_t *pos, const int32_t *doc,
+                             const uint8_t *mask, uint8_t out[32])
+{
+    const uint64_t n = 13ull * T, nc = (n + OR_DIGEST_CHUNK - 1) / OR_DIGEST_CHUNK;
+    uint8_t *rec = (uint8_t *)malloc(n ? n : 1);
+    uint8_t *cd = (uint8_t *)malloc(32 * (nc ? nc : 1));
+    if (!rec || !cd) { free(rec); free(cd); return OR_E_NOMEM; }
+    memcpy(rec, tok, 4ull * T);
+    memcpy(rec + 4ull * T, pos, 4ull * T);
+    memcpy(rec + 8ull * T, doc, 4ull * T);
+    memcpy(rec + 12ull * T, mask, T);
+    for (uint64_t i = 0; i < nc; i++) {
+        const uint64_t at = i * OR_DIGEST_CHUNK;
+        or_sha256(rec + at, n - at < OR_DIGEST_CHUNK ? n - at : OR_DIGEST_CHUNK, cd + 32 * i);
+    }
+    or_sha256(cd, 32 * nc, out);
+    free(rec);
+    free(cd);
+    return OR_OK;
+}
+
+/* The chunked digests of n windows laid out [n][T] each array ([n][32] out). */
+int or_window_digests_chunked(uint32_t T, uint64_t n, const uint32_t *tok, const int32_t *pos,
+                              const int32_t *doc, const uint8_t *mask, uint8_t *out)
+{
+    for (uint64_t w = 0; w < n; w++) {
+        const uint64_t at = w * T;
+        const int rc = or_window_digest_chunked(T, tok + at, pos + at, doc + at, mask + at, out + 32 * w);
+        if (rc) return rc;
+    }
+    return OR_OK;
 }
 
 /* One call of the batch entry: updates [step, step+n_steps) of the current

@@ -5,7 +5,8 @@
  * point of the oracle over seeded random small corpora in every mode: plain,
  * wrap, held-out stream, random read order, cumulative mixture, batch-size
  * ramp, lanes, arrivals, stream starts, prompts, several cycles, rank slices,
- * padding-free rows, plan digests and the exported arrays.  Output buffers are
+ * padding-free rows, window digests (whole and chunked), plan digests and the
+ * exported arrays.  Output buffers are
  * allocated to their exact sizes, so a write one element past any of them is
  * reported.  The driver computes nothing of the method itself: it draws inputs
  * with its own SplitMix64 stream and checks return codes.
@@ -78,6 +79,7 @@ static int check_cycle(or_plan *p, uint32_t world, uint32_t lanes)
             uint8_t *mask = NEW(uint8_t, T), d[32];
             or_emit_window(p, or_window_of(p, b, j), tok, pos, doc, mask);
             or_window_digest(T, tok, pos, doc, mask, d);
+            if (or_window_digests_chunked(T, 1, tok, pos, doc, mask, d) != OR_OK) bad = 1;
             free(tok); free(pos); free(doc); free(mask);
         }
     free(start); free(taken); free(next); free(Bs);
@@ -175,10 +177,38 @@ static int run_case(uint32_t seed)
     return bad;
 }
 
+/* chunked window digests of records of several chunks, the last one partial
+ * or whole, over windows laid out back to back */
+static int check_chunked_digests(void)
+{
+    static const uint32_t Ts[] = {315, 316, 1024, 1500, 5000};
+    int bad = 0;
+    for (uint32_t i = 0; i < sizeof Ts / sizeof Ts[0]; i++) {
+        const uint32_t T = Ts[i], n = 3;
+        uint32_t *tok = NEW(uint32_t, (uint64_t)n * T);
+        int32_t *pos = NEW(int32_t, (uint64_t)n * T), *doc = NEW(int32_t, (uint64_t)n * T);
+        uint8_t *mask = NEW(uint8_t, (uint64_t)n * T), *d = NEW(uint8_t, 32 * n);
+        for (uint64_t j = 0; j < (uint64_t)n * T; j++) {
+            tok[j] = (uint32_t)rnd();
+            pos[j] = (int32_t)rnd_below(T);
+            doc[j] = (int32_t)rnd_below(1000);
+            mask[j] = (uint8_t)rnd_below(2);
+        }
+        if (or_window_digests_chunked(T, n, tok, pos, doc, mask, d) != OR_OK) bad = 1;
+        free(tok); free(pos); free(doc); free(mask); free(d);
+    }
+    return bad;
+}
+
 int main(int argc, char **argv)
 {
     const uint32_t cases = argc > 1 ? (uint32_t)strtoul(argv[1], NULL, 10) : 96;
     uint32_t failed = 0;
+    g_rng = 0xC4u;
+    if (check_chunked_digests()) {
+        fprintf(stderr, "chunked window digests: an oracle call returned an unexpected error\n");
+        failed++;
+    }
     for (uint32_t s = 0; s < cases; s++)
         if (run_case(s)) {
             fprintf(stderr, "case %u: an oracle call returned an unexpected error\n", s);

@@ -56,6 +56,7 @@ class Corpus:
     tokens_start: int = 0       # tokens trained before the first cycle
     segment: Optional[np.ndarray] = None  # per document: the arrival it came with (streamed corpora)
     n_segments: int = 1         # arrivals
+    digest_chunked: bool = False  # window digests chunk by chunk (4,096-byte chunks of the record)
 
     @property
     def n_docs(self) -> int:

@@ -48,6 +48,59 @@ def test_window_digest_is_sha256_of_record(T):
     assert oracle.window_digest(tok, pos, doc, mask) == hashlib.sha256(record).digest()
 
 
+def _record(T, seed):
+    r = np.random.default_rng(seed)
+    tok = r.integers(0, 2**32, size=T, dtype=np.uint32)
+    pos = r.integers(-5, 100, size=T).astype(np.int32)
+    doc = r.integers(-1, 1000, size=T).astype(np.int32)
+    mask = r.integers(0, 2, size=T).astype(np.uint8)
+    record = (tok.astype("<u4").tobytes() + pos.astype("<i4").tobytes() +
+              doc.astype("<i4").tobytes() + mask.tobytes())
+    return tok, pos, doc, mask, record
+
+
+# one chunk (13·T ≤ 4096), one byte past a chunk, chunks straddling the record's
+# arrays, exact multiples of a chunk (T = 1024·k: 13·T = 4096·13k/4) and a long record
+@pytest.mark.parametrize("T", [1, 3, 64, 315, 316, 1000, 1024, 2048, 4095, 4096, 5000])
+def test_chunked_window_digest_rebuilt_with_hashlib(T):
+    """The chunked window digest: SHA-256 of the SHA-256 digests of the record's
+    4,096-byte chunks in order, the last chunk shorter."""
+    tok, pos, doc, mask, record = _record(T, 70 + T)
+    chunks = [record[i:i + 4096] for i in range(0, len(record), 4096)]
+    assert sum(map(len, chunks)) == 13 * T and all(len(c) == 4096 for c in chunks[:-1])
+    want = hashlib.sha256(b"".join(hashlib.sha256(c).digest() for c in chunks)).digest()
+    got = oracle.window_digests_chunked(tok[None], pos[None], doc[None], mask[None])
+    assert got.shape == (1, 32) and got[0].tobytes() == want
+
+
+def test_chunked_window_digest_of_one_chunk_is_double_sha256():
+    """A record of at most 4,096 bytes is one chunk: its digest is SHA-256 applied
+    twice, and it differs from the whole-record digest."""
+    for T in (1, 100, 315):
+        tok, pos, doc, mask, record = _record(T, 90 + T)
+        got = oracle.window_digests_chunked(tok, pos, doc, mask).tobytes()
+        assert got == hashlib.sha256(hashlib.sha256(record).digest()).digest()
+        assert got != oracle.window_digest(tok, pos, doc, mask)
+
+
+def test_chunked_window_digests_batch_layout_and_one_byte():
+    """[n, T] windows give [n, 32] digests, window by window; one changed byte in
+    any chunk changes that window's digest only."""
+    T, n = 700, 5
+    rows = [_record(T, 110 + w) for w in range(n)]
+    tok, pos, doc, mask = (np.stack([r[k] for r in rows]) for k in range(4))
+    d = oracle.window_digests_chunked(tok, pos, doc, mask)
+    assert d.shape == (n, 32)
+    for w in range(n):
+        assert d[w].tobytes() == oracle.window_digests_chunked(tok[w], pos[w], doc[w], mask[w]).tobytes()
+    for k, arr in enumerate((tok, pos, doc)):  # chunks 0, 2 and 1 (4·T bytes an array)
+        a2 = [tok.copy(), pos.copy(), doc.copy(), mask.copy()]
+        a2[k][3, T - 1] ^= 1
+        d2 = oracle.window_digests_chunked(*a2)
+        assert d2[3].tobytes() != d[3].tobytes()
+        assert np.array_equal(np.delete(d2, 3, 0), np.delete(d, 3, 0))
+
+
 # --------------------------------------------------------------- Philox vs rocRAND
 
 @pytest.fixture(scope="module")
@@ -186,3 +239,24 @@ def test_holdout_rate_within_four_sigma():
         q = c.holdout_bp[s] / 1e4
         mu, sd = n[s] * q, (n[s] * q * (1 - q)) ** 0.5
         assert abs(int(p.held_docs[s]) - mu) <= 4 * sd + 1, (s, p.held_docs[s], mu, sd)
+
+
+def test_batch_with_chunked_digests():
+    """With digest_chunked the oracle's batches keep every array and learned count,
+    and each window digest is the hashlib rebuild of its record's chunks."""
+    from synth.corpus import random_small
+    c = random_small(7, n_docs=300, n_sources=2, T=400, B=3, max_len=900)
+    a = oracle.Plan(c)
+    a.cycle(0)
+    b = oracle.Plan(c.replace(digest_chunked=True))
+    b.cycle(0)
+    x, y = a.batch(0, 2), b.batch(0, 2)
+    for k in ("tokens", "pos", "doc", "mask", "learned"):
+        assert np.array_equal(x[k], y[k]), k
+    for s in range(2):
+        for w in range(3):
+            rec = (y["tokens"][s, w].astype("<u4").tobytes() + y["pos"][s, w].astype("<i4").tobytes() +
+                   y["doc"][s, w].astype("<i4").tobytes() + y["mask"][s, w].tobytes())
+            inner = b"".join(hashlib.sha256(rec[i:i + 4096]).digest() for i in range(0, len(rec), 4096))
+            assert y["digests"][s, w].tobytes() == hashlib.sha256(inner).digest()
+            assert x["digests"][s, w].tobytes() == hashlib.sha256(rec).digest()
