@@ -28,7 +28,7 @@ ABI_VERSION = 2
 
 PACK_OK, PACK_E_ABI, PACK_E_INVAL, PACK_E_NOMEM, PACK_E_HIP = 0, -1, -2, -3, -4
 PACK_E_EXHAUSTED, PACK_E_STATE, PACK_E_RANGE, PACK_E_INTERNAL = -5, -6, -7, -8
-PACK_TEST_WAIT_GIVE_UP, PACK_TEST_CYCLE_FAULT, PACK_TEST_SORT_INSERTION = 1, 2, 3
+PACK_TEST_WAIT_GIVE_UP, PACK_TEST_CYCLE_FAULT, PACK_TEST_SORT_INSERTION, PACK_TEST_DIGEST_SLICES = 1, 2, 3, 4
 
 SYMBOLS = ("pack_init", "pack_init_noalloc", "pack_cycle", "pack_batch", "pack_batch_packed", "pack_fingerprint",
            "pack_fingerprint_steps", "pack_inspect", "pack_get_timings", "pack_status", "pack_test_option",
@@ -40,6 +40,7 @@ PACK_FLAG_HELDOUT = 4
 PACK_FLAG_READ_RANDOM = 8
 PACK_FLAG_CUMULATIVE = 16
 PACK_FLAG_TIMING_BATCH = 32
+PACK_FLAG_DIGEST_CHUNKED = 64
 PHASES = ("validate", "hash", "keys", "sort", "merge", "pieces", "cut", "windows", "mixture",
           "cycle", "emit", "learned", "digest", "fingerprint")
 
@@ -282,7 +283,8 @@ class Packer:
             | (PACK_FLAG_WRAP if getattr(corpus, "wrap", False) else 0)
             | (PACK_FLAG_HELDOUT if getattr(corpus, "heldout", False) else 0)
             | (PACK_FLAG_READ_RANDOM if getattr(corpus, "read_random", False) else 0)
-            | (PACK_FLAG_CUMULATIVE if getattr(corpus, "cumulative", False) else 0),
+            | (PACK_FLAG_CUMULATIVE if getattr(corpus, "cumulative", False) else 0)
+            | (PACK_FLAG_DIGEST_CHUNKED if getattr(corpus, "digest_chunked", False) else 0),
             d["tokens"].data_ptr() if d["tokens"].numel() else None, int(d["tokens"].numel()),
             d["offsets"].data_ptr(), int(d["source"].numel()),
             d["source"].data_ptr(), d["stratum"].data_ptr() if d.get("stratum") is not None else None,

@@ -356,6 +356,10 @@ size_t carve(pack_ctx& c, char* base) {
     c.dig_buf = k.take<uint8_t>(c.dig_cap + 32);
     c.mbox_bytes = pin_bytes_for((uint32_t)S, K, p.n_seg);
     c.mbox = k.take<uint8_t>(c.mbox_bytes);
+    // chunked window digests: 16 MiB of chunk digests, or those of a call's most windows (P ≥ a cycle's)
+    p.chunk_cd_words = p.digest_chunked ? std::min<uint64_t>(4ull << 20, 8 * dp::digest_chunks(p.T) * std::max(P, B))
+                                        : 0;
+    p.chunk_cd = k.take<uint32_t>(p.chunk_cd_words);
     return k.off + ALIGN;
 }
 
@@ -469,7 +473,7 @@ void check_config(const pack_config* cfg) {
     auto bad = [](const char* m) { throw InvalError{m}; };
     if (cfg->flags &
         ~(PACK_FLAG_TIMING | PACK_FLAG_TIMING_BATCH | PACK_FLAG_WRAP | PACK_FLAG_HELDOUT | PACK_FLAG_READ_RANDOM |
-          PACK_FLAG_CUMULATIVE))
+          PACK_FLAG_CUMULATIVE | PACK_FLAG_DIGEST_CHUNKED))
         bad("unknown flags");
     if (cfg->n_docs < 1 || cfg->n_docs >= (1ull << 31)) bad("n_docs must be in [1, 2^31)");
     if (!cfg->doc_offsets || !cfg->doc_source) bad("doc_offsets and doc_source are required");
@@ -798,6 +802,7 @@ int init_context(const pack_config* cfg, pack_ctx** out, bool noalloc) {
         p.heldout = (cfg->flags & PACK_FLAG_HELDOUT) ? 1u : 0u;
         p.read_random = (cfg->flags & PACK_FLAG_READ_RANDOM) ? 1u : 0u;
         p.cumulative = (cfg->flags & PACK_FLAG_CUMULATIVE) ? 1u : 0u;
+        p.digest_chunked = (cfg->flags & PACK_FLAG_DIGEST_CHUNKED) ? 1u : 0u;
         p.ramp = cfg->n_ramp ? 1u : 0u;
         p.tabled = (p.cumulative || p.ramp) ? 1u : 0u;
         p.world = cfg->world;
@@ -1282,6 +1287,7 @@ int pack_test_option(pack_ctx* c, uint32_t what, uint32_t value) {
         case PACK_TEST_WAIT_GIVE_UP: bit = dp::TEST_WAIT_GIVE_UP; break;
         case PACK_TEST_CYCLE_FAULT: bit = dp::TEST_CYCLE_FAULT; break;
         case PACK_TEST_SORT_INSERTION: bit = dp::TEST_SORT_INSERTION; break;
+        case PACK_TEST_DIGEST_SLICES: bit = dp::TEST_DIGEST_SLICES; break;
         default: c->err = "unknown test option"; return PACK_E_INVAL;
     }
     if (value) c->p.test_opts |= bit;

@@ -17,6 +17,7 @@ constexpr uint32_t ERR_INTERNAL = 0x100u;
 constexpr uint32_t TEST_WAIT_GIVE_UP = 1u;
 constexpr uint32_t TEST_CYCLE_FAULT = 2u;
 constexpr uint32_t TEST_SORT_INSERTION = 4u;
+constexpr uint32_t TEST_DIGEST_SLICES = 8u;
 
 // ---------------------------------------------------------------- errors
 struct HipError {
@@ -175,6 +176,9 @@ struct Plan {
     uint32_t world;               // ranks sharing each update's slots
     uint32_t lanes;               // lanes L (1: none); streams s·L + l, the schedule per lane over B/L seats
     uint32_t S_real;              // the recipe's sources (S = S_real·lanes streams)
+    uint32_t digest_chunked;      // 1: window digests over the digests of 4,096-byte chunks of the record
+    uint32_t* chunk_cd;           // digest_chunked: the chunk digests of one slice of windows (8 words each)
+    uint64_t chunk_cd_words;      // its size in words
 
     // recipe on device
     uint32_t* gbase;              // [S·n_seg+1] first group of each (stream, arrival)
@@ -445,6 +449,9 @@ __device__ inline uint32_t out_per(const Plan& p, const EmitArgs& a, uint32_t i)
 void launch_emit(const Plan& p, const EmitArgs& a, hipStream_t st);
 void launch_emit_packed(const Plan& p, const EmitArgs& a, hipStream_t st);  // padding-free rows
 void launch_learned(const Plan& p, const EmitArgs& a, hipStream_t st);
+// chunked window digests: chunks of DIGEST_CHUNK bytes of a window's 13·T-byte record
+constexpr uint32_t DIGEST_CHUNK = 4096;
+__host__ __device__ inline uint64_t digest_chunks(uint64_t T) { return (13 * T + DIGEST_CHUNK - 1) / DIGEST_CHUNK; }
 void launch_emit_sha(const Plan& p, const EmitArgs& a, hipStream_t st);  // emission and window digests
 void launch_batch_fp(const uint8_t* digests, uint32_t B, uint32_t n_batches, uint8_t* out, hipStream_t st);
 // batches of B_b digests: batch b covers digests [slot0[step+b] − slot0[step], slot0[step+b+1] − slot0[step])

@@ -1016,6 +1016,171 @@ __global__ __launch_bounds__(256) void k_window_digest_any(Plan p, EmitArgs a) {
     store_digest(H, a.digests + 32 * w);
 }
 
+// ---------------------------------------------------------------- chunked window digests
+// PACK_FLAG_DIGEST_CHUNKED: a window's digest is the SHA-256 of the SHA-256
+// digests of its record's chunks of DIGEST_CHUNK bytes (the last chunk
+// shorter), in record order.  The chunks are independent chains, so one lane
+// hashes one chunk and a window's chunks run side by side.  The emission
+// kernel writes the windows first and these kernels read each record from the
+// outputs, one slice of windows [w0, w0 + nw) at a time: lane g hashes chunk
+// g mod nc of window w0 + g / nc (nc chunks a window) into cd[8g .. 8g+8)
+// (the final state words, which are the chunk digest's big-endian words, so
+// they are the next message's words as they stand), then one lane per window
+// hashes its nc chunk digests.
+//
+// Byte x of a record lies in tok (x < 4T), pos (x < 8T), doc (x < 12T) as
+// 4-byte little-endian elements, or in mask (x ≥ 12T).
+__device__ __forceinline__ const uint8_t* record_at(const EmitArgs& a, uint64_t T, uint64_t w, uint64_t x) {
+    if (x < 4 * T) return reinterpret_cast<const uint8_t*>(a.tok + w * T) + x;
+    if (x < 8 * T) return reinterpret_cast<const uint8_t*>(a.pos + w * T) + (x - 4 * T);
+    if (x < 12 * T) return reinterpret_cast<const uint8_t*>(a.doc + w * T) + (x - 8 * T);
+    return a.mask + w * T + (x - 12 * T);
+}
+
+// The padding block that ends a message of len bytes, len a multiple of 64
+// (FIPS 180-4, section 5.1.1: the byte 0x80, zeros, the bit length).
+__device__ __forceinline__ void final_pad_block(uint32_t H[8], uint64_t len) {
+    uint32_t W[16];
+    W[0] = 0x80000000u;
+#pragma unroll
+    for (uint32_t e = 1; e < 14; ++e) W[e] = 0u;
+    W[14] = (uint32_t)((8 * len) >> 32);
+    W[15] = (uint32_t)(8 * len);
+    sha256_compress(H, W);
+}
+
+__device__ __forceinline__ void store_state(const uint32_t H[8], uint32_t* out) {
+    uint4* o = reinterpret_cast<uint4*>(out);
+    o[0] = make_uint4(H[0], H[1], H[2], H[3]);
+    o[1] = make_uint4(H[4], H[5], H[6], H[7]);
+}
+
+// T a multiple of 1,024: 4T and 12T are multiples of DIGEST_CHUNK, so every
+// chunk lies in one array, and every chunk length (4,096, or T mod 4,096 for
+// the last mask chunk) is a multiple of 1,024.  A lane takes its chunk one
+// 128-byte line (two blocks, eight 16-byte loads) at a time and loads the
+// next line before compressing the current one (the last line is loaded
+// twice, so every load is unconditional).
+__global__ __launch_bounds__(256) void k_chunk_sha_lines(Plan p, EmitArgs a, uint64_t w0, uint64_t n_lanes,
+                                                         uint32_t nc, uint32_t* cd) {
+    const uint64_t g = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (g >= n_lanes) return;
+    const uint64_t T = p.T, w = w0 + g / nc, x0 = (uint64_t)DIGEST_CHUNK * (g % nc);
+    const uint64_t len = 13 * T - x0 < DIGEST_CHUNK ? 13 * T - x0 : DIGEST_CHUNK;
+    const u32x4a4* src = reinterpret_cast<const u32x4a4*>(record_at(a, T, w, x0));
+    const uint32_t lines = (uint32_t)(len / 128);
+    u32x4 nx[8];
+#pragma unroll
+    for (uint32_t e = 0; e < 8; ++e) nx[e] = src[e];
+    uint32_t H[8];
+    sha256_init(H);
+    for (uint32_t l = 0; l < lines; ++l) {
+        u32x4 cur[8];
+#pragma unroll
+        for (uint32_t e = 0; e < 8; ++e) cur[e] = nx[e];
+        const uint32_t ln = l + 1 < lines ? l + 1 : l;
+#pragma unroll
+        for (uint32_t e = 0; e < 8; ++e) nx[e] = src[8 * ln + e];
+#pragma unroll
+        for (uint32_t h = 0; h < 2; ++h) {
+            uint32_t W[16];
+#pragma unroll
+            for (uint32_t e = 0; e < 4; ++e) {
+                W[4 * e + 0] = bswap32(cur[4 * h + e].x);
+                W[4 * e + 1] = bswap32(cur[4 * h + e].y);
+                W[4 * e + 2] = bswap32(cur[4 * h + e].z);
+                W[4 * e + 3] = bswap32(cur[4 * h + e].w);
+            }
+            sha256_compress(H, W);
+        }
+    }
+    final_pad_block(H, len);
+    store_state(H, cd + 8 * g);
+}
+
+// Any T: word j of a chunk's padded message is a whole element of tok, pos
+// or doc while its 4 bytes lie before byte 12T of the record (chunk starts and
+// 12T are multiples of 4, and a chunk ends at a multiple of 4 there); from
+// there on the words are assembled byte by byte from mask, the byte 0x80,
+// zeros and the chunk's bit length.
+__global__ __launch_bounds__(256) void k_chunk_sha_any(Plan p, EmitArgs a, uint64_t w0, uint64_t n_lanes,
+                                                       uint32_t nc, uint32_t* cd) {
+    const uint64_t g = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (g >= n_lanes) return;
+    const uint64_t T = p.T, w = w0 + g / nc, x0 = (uint64_t)DIGEST_CHUNK * (g % nc);
+    const uint64_t len = 13 * T - x0 < DIGEST_CHUNK ? 13 * T - x0 : DIGEST_CHUNK;
+    const uint64_t nb = (len + 72) / 64, tail = 64 * nb - 8, bits = 8 * len;
+    const uint8_t* mask = a.mask + w * T;
+    auto byte_at = [&](uint64_t q) -> uint32_t {  // byte q of the padded chunk, x0 + q ≥ 12T when q < len
+        if (q < len) return mask[x0 + q - 12 * T];
+        if (q == len) return 0x80u;
+        if (q >= tail) return (uint32_t)(bits >> (8 * (7 - (q - tail)))) & 0xFFu;
+        return 0u;
+    };
+    uint32_t H[8];
+    sha256_init(H);
+    for (uint64_t b = 0; b < nb; ++b) {
+        uint32_t W[16];
+#pragma unroll
+        for (uint32_t e = 0; e < 16; ++e) {
+            const uint64_t q = 64 * b + 4 * e, x = x0 + q;
+            if (q + 4 <= len && x + 4 <= 12 * T)
+                W[e] = bswap32(*reinterpret_cast<const uint32_t*>(record_at(a, T, w, x)));
+            else
+                W[e] = byte_at(q) << 24 | byte_at(q + 1) << 16 | byte_at(q + 2) << 8 | byte_at(q + 3);
+        }
+        sha256_compress(H, W);
+    }
+    store_state(H, cd + 8 * g);
+}
+
+// One lane per window of the slice: SHA-256 of its nc chunk digests (8·nc
+// message words, then 0x80000000, zeros and the bit length 256·nc).
+__global__ __launch_bounds__(256) void k_chunk_final(EmitArgs a, uint64_t w0, uint64_t nw, uint32_t nc,
+                                                     const uint32_t* cd) {
+    const uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= nw) return;
+    const uint32_t* m = cd + 8ull * nc * i;
+    const uint64_t words = 8ull * nc, nb = (32ull * nc + 72) / 64, bits = 256ull * nc;
+    uint32_t H[8];
+    sha256_init(H);
+    for (uint64_t b = 0; b < nb; ++b) {
+        uint32_t W[16];
+#pragma unroll
+        for (uint32_t e = 0; e < 16; ++e) {
+            const uint64_t j = 16 * b + e;
+            W[e] = j < words ? m[j]
+                   : j == words ? 0x80000000u
+                   : j == 16 * nb - 2 ? (uint32_t)(bits >> 32)
+                   : j == 16 * nb - 1 ? (uint32_t)bits
+                   : 0u;
+        }
+        sha256_compress(H, W);
+    }
+    store_digest(H, a.digests + 32 * (w0 + i));
+}
+
+// Emission, then the chunk digests slice by slice (p.chunk_cd holds at least
+// one window's nc chunk digests: checked at init).
+void launch_chunked_digests(const Plan& p, const EmitArgs& a, hipStream_t st) {
+    const uint64_t n = a.n_out, nc = digest_chunks(p.T);
+    launch_emit(p, a, st);
+    uint64_t slice = p.chunk_cd_words / (8 * nc);
+    if (slice == 0) throw HipError{hipErrorInvalidValue, "internal: chunk digest scratch"};
+    if ((p.test_opts & TEST_DIGEST_SLICES) && slice > 3) slice = 3;  // test option: many slices a call
+    for (uint64_t w0 = 0; w0 < n; w0 += slice) {
+        const uint64_t nw = n - w0 < slice ? n - w0 : slice, lanes = nw * nc;
+        const dim3 grid((uint32_t)((lanes + 255) / 256));
+        if (p.T % 1024 == 0)
+            hipLaunchKernelGGL(k_chunk_sha_lines, grid, dim3(256), 0, st, p, a, w0, lanes, (uint32_t)nc, p.chunk_cd);
+        else
+            hipLaunchKernelGGL(k_chunk_sha_any, grid, dim3(256), 0, st, p, a, w0, lanes, (uint32_t)nc, p.chunk_cd);
+        hipLaunchKernelGGL(k_chunk_final, dim3((uint32_t)((nw + 255) / 256)), dim3(256), 0, st, a, w0, nw,
+                           (uint32_t)nc, (const uint32_t*)p.chunk_cd);
+    }
+    DP_HIP(hipGetLastError());
+}
+
 }  // namespace
 
 // Launch shape by the number of waves of 64 windows (each a chain of 13·T/64 + 1
@@ -1028,6 +1193,10 @@ void launch_emit_sha(const Plan& p, const EmitArgs& a, hipStream_t st) {
     const uint64_t n = a.n_out;  // < 2^31 windows: at most 2^23 workgroups
     const uint64_t waves = (n + 63) / 64;
     if (!n) return;
+    if (p.digest_chunked) {
+        launch_chunked_digests(p, a, st);
+        return;
+    }
     if (p.T % 64) {  // records not made of whole 64-byte blocks per array: emission, then digests from the outputs
         launch_emit(p, a, st);
         hipLaunchKernelGGL(k_window_digest_any, dim3((uint32_t)((n + 255) / 256)), dim3(256), 0, st, p, a);

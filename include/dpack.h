@@ -111,6 +111,21 @@ typedef struct pack_ctx pack_ctx;
  * time).  With PACK_FLAG_TIMING as well, every phase is timed.  Changes no
  * output byte. */
 #define PACK_FLAG_TIMING_BATCH 32u
+/* pack_config.flags: chunked window digests.  Zephon blog post, resume
+ * section, fixes only that every global batch's SHA-256 is equal at any rank
+ * count; how a window is digested is this library's reading.  Without the
+ * flag a window's digest is one SHA-256 over its 13·T-byte record (pack_out),
+ * a serial chain of about 13·T/64 compressions.  With it the record is cut
+ * into chunks of 4,096 bytes (the last one shorter when 13·T is not a
+ * multiple), each chunk is hashed with SHA-256, and the window's digest is
+ * the SHA-256 of those chunk digests in record order, 32 bytes each (a
+ * record of one chunk, T ≤ 315, gets SHA-256(SHA-256(record))).  The chunks
+ * of a window hash side by side, so few windows take far less time; the
+ * digests differ from those without the flag, and batch fingerprints are
+ * taken over them as before.  Changes no other output byte; the context's
+ * device memory grows by at most 16 MiB (the chunk digests of one slice of
+ * windows at a time). */
+#define PACK_FLAG_DIGEST_CHUNKED 64u
 
 /* Kernel phases timed under PACK_FLAG_TIMING (EMIT to FINGERPRINT also under
  * PACK_FLAG_TIMING_BATCH). */
@@ -314,7 +329,8 @@ typedef struct pack_out {
     uint8_t *mask;       /* 1 iff the token is learned (at or after the prompt) */
     int64_t *learned;    /* device [n_steps]: global learned positions of each update; NULL = skip */
     uint8_t *digests;    /* device [n_steps][B/world][32]: SHA-256 of each window's record
-                            tok‖pos‖doc‖mask (little-endian, 13·T bytes); NULL = skip */
+                            tok‖pos‖doc‖mask (little-endian, 13·T bytes), or of its chunks'
+                            digests under PACK_FLAG_DIGEST_CHUNKED; NULL = skip */
 } pack_out;
 
 /* pack_batch — emit updates [step, step+n_steps) of the current cycle for
@@ -418,8 +434,8 @@ int pack_status(pack_ctx *ctx);
 /* Test options for pack_test_option.  They exist so that the error paths
  * above, and code paths that real inputs almost never take, can be exercised
  * on a GPU with every kernel still running to its end; with every option 0
- * (the default) no output byte changes, and PACK_TEST_SORT_INSERTION changes
- * none either. */
+ * (the default) no output byte changes, and PACK_TEST_SORT_INSERTION and
+ * PACK_TEST_DIGEST_SLICES change none either. */
 enum {
     PACK_TEST_WAIT_GIVE_UP = 1, /* the digest waves' bounded waits give up after one poll:
                                    the batch's digests are invalid, pack_status reports it
@@ -427,6 +443,8 @@ enum {
     PACK_TEST_CYCLE_FAULT = 2,  /* a cycle kernel reports an internal failure: pack_cycle fails */
     PACK_TEST_SORT_INSERTION = 3, /* the sort of a cycle's random read order orders every bucket
                                      by insertion, the path of buckets above 16 elements */
+    PACK_TEST_DIGEST_SLICES = 4,  /* chunked window digests in slices of 3 windows (many slices
+                                     and a partial last one per call); no output byte changes */
 };
 
 /* pack_test_option — set test option `what` on (value != 0) or off for the

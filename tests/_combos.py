@@ -1,7 +1,7 @@
 """Seeded random combinations of every mode on small corpora (wrap packing,
 random read order, cumulative mixture, lanes, batch-size ramp, held-out
 stream, arrivals, stream starts, window lengths that are not multiples of
-64), for parity between the GPU and the oracle."""
+64, chunked window digests), for parity between the GPU and the oracle."""
 import numpy as np
 
 import oracle
@@ -39,13 +39,15 @@ def _draw(corpus_seed, seed, seq, even):
     t_alt = np.random.default_rng(np.random.SeedSequence(seq + [77]))
     if t_alt.random() < 0.35:
         T = int(t_alt.choice([37, 100]))
+    # about a third take chunked window digests, from a stream of their own as well
+    chunked = bool(np.random.default_rng(np.random.SeedSequence(seq + [78])).random() < 0.35)
     m = 2 * L if even else L
     b = [m * int(x) for x in r.integers(1, 4, size=2)]
     B = max(b) if ramp else m * int(r.integers(1, 4))
     c = random_small(corpus_seed, n_docs=int(r.integers(400, 1400)), n_sources=int(r.integers(1, 5)),
                      max_strata=int(r.integers(1, 4)), T=T, B=B, max_len=int(r.integers(40, 400)),
                      prompts=bool(r.random() < 0.5), bp_max=6000 if heldout else 1500)
-    mode = dict(wrap=bool(r.random() < 0.4), read_random=bool(r.random() < 0.4),
+    mode = dict(digest_chunked=chunked, wrap=bool(r.random() < 0.4), read_random=bool(r.random() < 0.4),
                 cumulative=bool(r.random() < 0.4), heldout=heldout, lanes=L,
                 updates_per_cycle=0 if heldout else int(r.choice([0, 2, 3, 5])))
     if ramp:

@@ -67,7 +67,7 @@ def _cfg(**kw):
     ("window_tokens", (1 << 20) + 1, dp.PACK_E_INVAL),
     ("global_batch", 0, dp.PACK_E_INVAL),
     ("n_docs", 0, dp.PACK_E_INVAL),
-    ("flags", 64, dp.PACK_E_INVAL),
+    ("flags", 128, dp.PACK_E_INVAL),
     ("n_sources", 0, dp.PACK_E_INVAL),
     ("n_tokens", 1 << 40, dp.PACK_E_INVAL),  # scanned token totals stay below 2^40
 ])
@@ -173,6 +173,6 @@ def test_noalloc_limits_checked_before_device_work(lib):
         assert lib.pack_init_noalloc(C.byref(cfg), C.byref(ctx)) == dp.PACK_E_INVAL
         assert "PACK_FLAG_TIMING" in lib.pack_last_error(None).decode()
     assert lib.pack_init_noalloc(None, C.byref(ctx)) == dp.PACK_E_INVAL
-    cfg, keep = _cfg(flags=64)  # no such flag
+    cfg, keep = _cfg(flags=128)  # no such flag
     assert lib.pack_init_noalloc(C.byref(cfg), C.byref(ctx)) == dp.PACK_E_INVAL
     assert "unknown flags" in lib.pack_last_error(None).decode()

@@ -1024,3 +1024,67 @@ def test_any_window_length_every_digest_of_a_cycle(T, wrap):
     for st in sorted({0, U - 1}):
         compare_batch(to_np(pk.batch(st, 1)), op.batch(st, 1), f"T{T} update {st}")
     pk.close()
+
+
+# ---------------------------------------------------------------- chunked window digests
+CHUNKED_CASES = [("small", 0), ("small", 3), ("small", 5), ("tinydocs", 2), ("sft", 0.004), ("long", 0.01),
+                 ("pretrain", 0.006), ("full", 0.002)]
+
+
+@pytest.mark.parametrize("kind,arg", CHUNKED_CASES)
+def test_chunked_digest_parity(kind, arg):
+    """PACK_FLAG_DIGEST_CHUNKED: every output and each window's digest over its
+    record's 4,096-byte chunk digests equal the oracle's, and so do the batch
+    fingerprints taken over them."""
+    _parity_run(_corpus(kind, arg).replace(digest_chunked=True), "chunked-" + kind, arg)
+
+
+@pytest.mark.parametrize("T", [1, 37, 100, 315, 316, 1000, 1024, 1500, 3072, 5000])
+def test_chunked_digest_any_window_length(T):
+    """Window lengths whose records are one chunk (T ≤ 315), one byte more, whose
+    chunks straddle tok, pos, doc and mask (T not a multiple of 1,024: the word by
+    word kernel) or lie in one array each (1,024, 3,072: the line kernel)."""
+    c = random_small(1200 + T, n_docs=200, n_sources=2, max_strata=2, T=T, B=3, max_len=max(8, 2 * T),
+                     prompts=True, bp_max=1000)
+    _parity_run(c.replace(digest_chunked=True), "chunked-T", T)
+
+
+@pytest.mark.parametrize("T", [2048, 1000])
+def test_chunked_digests_in_slices(T):
+    """With PACK_TEST_DIGEST_SLICES the chunk digests go through slices of three
+    windows (a partial last one): the digests are those of one slice and the
+    oracle's; the same context without digests emits the same arrays."""
+    c = random_small(1300 + T, n_docs=400, n_sources=3, T=T, B=4, max_len=3 * T, bp_max=500).replace(
+        digest_chunked=True)
+    op = oracle.Plan(c)
+    oi = op.cycle(0)
+    n = min(4, oi.n_updates)
+    o = op.batch(0, n)
+    pk = dp.Packer(c)
+    pk.cycle(0)
+    one = to_np(pk.batch(0, n))
+    pk.test_option(dp.PACK_TEST_DIGEST_SLICES, 1)
+    sliced = to_np(pk.batch(0, n))
+    pk.test_option(dp.PACK_TEST_DIGEST_SLICES, 0)
+    plain = to_np(pk.batch(0, n, digests=False))
+    assert np.array_equal(one["digests"], sliced["digests"])
+    compare_batch(sliced, o, f"chunked slices T={T}")
+    for k in ("tokens", "pos", "doc", "mask"):
+        assert np.array_equal(plain[k], one[k]), k
+    pk.close()
+
+
+def test_chunked_and_whole_record_digests_differ_arrays_equal():
+    """The flag changes the digests only: the same corpus with and without it
+    emits the same arrays, and every digest differs."""
+    c = _corpus("small", 1)
+    a, b = dp.Packer(c), dp.Packer(c.replace(digest_chunked=True))
+    a.cycle(0)
+    b.cycle(0)
+    x, y = to_np(a.batch(0, 2)), to_np(b.batch(0, 2))
+    for k in ("tokens", "pos", "doc", "mask", "learned"):
+        assert np.array_equal(x[k], y[k]), k
+    dx, dy = x["digests"].reshape(-1, 32), y["digests"].reshape(-1, 32)
+    assert all(dx[i].tobytes() != dy[i].tobytes() for i in range(dx.shape[0]))
+    a.close()
+    b.close()
