@@ -49,6 +49,18 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
+def digest_blocks(T: int, chunked: bool) -> int:
+    """SHA-256 compressions per window digest: the record's 13·T bytes and their
+    padding, or, chunked, every 4,096-byte chunk with its padding and then the
+    digest of the chunk digests (32 bytes each)."""
+    n = 13 * T
+    if not chunked:
+        return (n + 72) // 64
+    full, last = divmod(n, 4096)
+    blocks = full * ((4096 + 72) // 64) + ((last + 72) // 64 if last else 0)
+    return blocks + (32 * (full + (1 if last else 0)) + 72) // 64
+
+
 def traffic_from_profile(kernel: str, workload: str):
     """HBM bytes per launch measured by rocprofv3 PMC runs, if a committed
     summary exists for this kernel and workload (profiles/<kernel>_<workload>
@@ -104,6 +116,9 @@ def main():
                     help="streamed corpus: each document carries one of N arrivals (seeded uniform labels)")
     ap.add_argument("--resume", action="store_true",
                     help="time cycle 1 of a context that starts each stream at the token cycle 0 reported")
+    ap.add_argument("--digest-chunked", action="store_true",
+                    help="window digests over the digests of 4,096-byte chunks of each record "
+                         "(PACK_FLAG_DIGEST_CHUNKED)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -123,7 +138,8 @@ def main():
 
     t0 = time.time()
     corpus = make_corpus(args.workload, args.scale).replace(wrap=args.wrap, read_random=args.read_random,
-                                                             cumulative=args.cumulative)
+                                                             cumulative=args.cumulative,
+                                                             digest_chunked=args.digest_chunked)
     if args.ramp:
         corpus = corpus.replace(ramp=((0, corpus.B // 2 * corpus.T), (100_000_000, corpus.B * corpus.T)))
     if args.lanes > 1:
@@ -221,14 +237,15 @@ def main():
         "emit": ("hbm", emit_bytes, "GB/s"),
         # hash: read every token once + per document offsets/source in, hash/keep out
         "hash": ("hbm", 4.0 * corpus.n_tokens + 19.0 * corpus.n_docs, "GB/s"),
-        # window SHA-256: (13T/64 + 1) compressions per window
-        "digest": ("alu", SHA_OPS_PER_BLOCK * n_windows * (13 * T // 64 + 1), "TOP/s"),
+        # window SHA-256: (13T/64 + 1) compressions per window; chunked, each chunk's blocks and
+        # padding, then the SHA-256 of the chunk digests
+        "digest": ("alu", SHA_OPS_PER_BLOCK * n_windows * digest_blocks(T, args.digest_chunked), "TOP/s"),
     }
     # bytes the digest kernel moves: the emission when fused, a 32-byte digest per window, and the
     # 13T-byte records read back where the paired kernel hashes them from the outputs (launches of
     # 513 to 1,024 waves of 64 windows; the ring pairs and the own-record kernel read nothing back)
     waves = (n_windows + 63) // 64
-    read_back = 512 < waves <= 1024
+    read_back = 512 < waves <= 1024 or args.digest_chunked
     digest_bytes = (13.0 * positions if read_back else 0.0) + (emit_bytes if fused else 0.0) + 32.0 * n_windows
     kernels = {}
     for k in phase_ms:
@@ -252,7 +269,7 @@ def main():
     # take the ring kernel) or other bytes, so it reports no traffic; the hash does not depend
     # on how the windows are emitted
     moded = (args.wrap or args.lanes > 1 or args.ramp or args.cumulative or args.read_random or args.heldout
-             or args.arrivals > 1 or args.resume or args.scale != 1.0)
+             or args.arrivals > 1 or args.resume or args.digest_chunked or args.scale != 1.0)
 
     def traffic_of(k):
         if moded:
@@ -422,7 +439,8 @@ def main():
                    + (", held-out (validation) stream, cycle of maximal length" if args.heldout else "")
                    + (f", {args.arrivals} arrivals" if args.arrivals > 1 else "")
                    + (", cycle 1 of a context resumed at cycle 0's stream tokens" if args.resume else "")
-                   + (", padding-free rows" if args.packed else ""),
+                   + (", padding-free rows" if args.packed else "")
+                   + (", chunked window digests (4,096-byte chunks)" if args.digest_chunked else ""),
                    "docs": corpus.n_docs, "tokens": corpus.n_tokens, "T": T, "B": B, "updates": U,
                    "real_tokens_per_step": real, "positions_per_step": row_positions,
                    "step": ("pack_init + pack_cycle + pack_batch_packed(all updates, learned, bucket 256) + pack_destroy"

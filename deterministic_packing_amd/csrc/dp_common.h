@@ -453,6 +453,8 @@ void launch_learned(const Plan& p, const EmitArgs& a, hipStream_t st);
 constexpr uint32_t DIGEST_CHUNK = 4096;
 __host__ __device__ inline uint64_t digest_chunks(uint64_t T) { return (13 * T + DIGEST_CHUNK - 1) / DIGEST_CHUNK; }
 void launch_emit_sha(const Plan& p, const EmitArgs& a, hipStream_t st);  // emission and window digests
+uint64_t chunk_slice_windows(const Plan& p);  // chunked digests: windows of one slice of the scratch
+void launch_chunk_hash(const Plan& p, const EmitArgs& a, uint64_t w0, uint64_t nw, hipStream_t st);
 void launch_batch_fp(const uint8_t* digests, uint32_t B, uint32_t n_batches, uint8_t* out, hipStream_t st);
 // batches of B_b digests: batch b covers digests [slot0[step+b] − slot0[step], slot0[step+b+1] − slot0[step])
 void launch_batch_fp_var(const uint8_t* digests, const uint64_t* slot0, uint32_t step, uint32_t n_batches,

@@ -1160,27 +1160,6 @@ __global__ __launch_bounds__(256) void k_chunk_final(EmitArgs a, uint64_t w0, ui
     store_digest(H, a.digests + 32 * (w0 + i));
 }
 
-// Emission, then the chunk digests slice by slice (p.chunk_cd holds at least
-// one window's nc chunk digests: checked at init).
-void launch_chunked_digests(const Plan& p, const EmitArgs& a, hipStream_t st) {
-    const uint64_t n = a.n_out, nc = digest_chunks(p.T);
-    launch_emit(p, a, st);
-    uint64_t slice = p.chunk_cd_words / (8 * nc);
-    if (slice == 0) throw HipError{hipErrorInvalidValue, "internal: chunk digest scratch"};
-    if ((p.test_opts & TEST_DIGEST_SLICES) && slice > 3) slice = 3;  // test option: many slices a call
-    for (uint64_t w0 = 0; w0 < n; w0 += slice) {
-        const uint64_t nw = n - w0 < slice ? n - w0 : slice, lanes = nw * nc;
-        const dim3 grid((uint32_t)((lanes + 255) / 256));
-        if (p.T % 1024 == 0)
-            hipLaunchKernelGGL(k_chunk_sha_lines, grid, dim3(256), 0, st, p, a, w0, lanes, (uint32_t)nc, p.chunk_cd);
-        else
-            hipLaunchKernelGGL(k_chunk_sha_any, grid, dim3(256), 0, st, p, a, w0, lanes, (uint32_t)nc, p.chunk_cd);
-        hipLaunchKernelGGL(k_chunk_final, dim3((uint32_t)((nw + 255) / 256)), dim3(256), 0, st, a, w0, nw,
-                           (uint32_t)nc, (const uint32_t*)p.chunk_cd);
-    }
-    DP_HIP(hipGetLastError());
-}
-
 }  // namespace
 
 // Launch shape by the number of waves of 64 windows (each a chain of 13·T/64 + 1
@@ -1193,8 +1172,10 @@ void launch_emit_sha(const Plan& p, const EmitArgs& a, hipStream_t st) {
     const uint64_t n = a.n_out;  // < 2^31 windows: at most 2^23 workgroups
     const uint64_t waves = (n + 63) / 64;
     if (!n) return;
-    if (p.digest_chunked) {
-        launch_chunked_digests(p, a, st);
+    if (p.digest_chunked) {  // one stream: the emission, then the chunk digests slice by slice
+        launch_emit(p, a, st);
+        const uint64_t slice = chunk_slice_windows(p);
+        for (uint64_t w0 = 0; w0 < n; w0 += slice) launch_chunk_hash(p, a, w0, n - w0 < slice ? n - w0 : slice, st);
         return;
     }
     if (p.T % 64) {  // records not made of whole 64-byte blocks per array: emission, then digests from the outputs
@@ -1209,6 +1190,30 @@ void launch_emit_sha(const Plan& p, const EmitArgs& a, hipStream_t st) {
     else
         hipLaunchKernelGGL(k_emit_digest, dim3((uint32_t)((waves + GWAVES - 1) / GWAVES)), dim3(64 * GWAVES), 0, st,
                            p, a, n);
+    DP_HIP(hipGetLastError());
+}
+
+// Windows whose chunk digests p.chunk_cd holds at once (at least one: the
+// scratch is sized at init for one window's chunks or more).
+uint64_t chunk_slice_windows(const Plan& p) {
+    const uint64_t slice = p.chunk_cd_words / (8 * digest_chunks(p.T));
+    if (slice == 0) throw HipError{hipErrorInvalidValue, "internal: chunk digest scratch"};
+    return (p.test_opts & TEST_DIGEST_SLICES) && slice > 3 ? 3 : slice;  // test option: many slices a call
+}
+
+// Chunk digests of windows [w0, w0 + nw) of a call's outputs (nw at most
+// chunk_slice_windows), then their window digests into a.digests.
+void launch_chunk_hash(const Plan& p, const EmitArgs& a, uint64_t w0, uint64_t nw, hipStream_t st) {
+    const uint64_t nc = digest_chunks(p.T), lanes = nw * nc;
+    if (!nw) return;
+    if (nw > chunk_slice_windows(p)) throw HipError{hipErrorInvalidValue, "internal: chunk digest slice"};
+    const dim3 grid((uint32_t)((lanes + 255) / 256));
+    if (p.T % 1024 == 0)
+        hipLaunchKernelGGL(k_chunk_sha_lines, grid, dim3(256), 0, st, p, a, w0, lanes, (uint32_t)nc, p.chunk_cd);
+    else
+        hipLaunchKernelGGL(k_chunk_sha_any, grid, dim3(256), 0, st, p, a, w0, lanes, (uint32_t)nc, p.chunk_cd);
+    hipLaunchKernelGGL(k_chunk_final, dim3((uint32_t)((nw + 255) / 256)), dim3(256), 0, st, a, w0, nw, (uint32_t)nc,
+                       (const uint32_t*)p.chunk_cd);
     DP_HIP(hipGetLastError());
 }
 

@@ -77,3 +77,13 @@ def test_noalloc_equals_pack_init_twice_smaller_second():
     assert second.n_docs < first.n_docs and second.n_tokens < first.n_tokens
     _check("tiny, cumulative, random read order", first)
     _check("smaller, wrap, batch-size ramp", second)
+
+
+def test_noalloc_chunked_digests_one_stream():
+    """Chunked window digests (the emission, then the chunk digests from the
+    outputs) in the static scratch: the no-alloc context equals a pack_init
+    context and the oracle, across a batch-size ramp."""
+    c = random_small(405, n_docs=900, n_sources=3, max_strata=2, T=1024, B=4, max_len=2500, prompts=True,
+                     bp_max=800).replace(digest_chunked=True, ramp=((0, 2 * 1024), (6 * 2 * 1024, 4 * 1024)),
+                                         updates_per_cycle=4)
+    _check("chunked digests, batch-size ramp", c)
