@@ -1,8 +1,8 @@
 """Parity at the workloads' full sizes, in the launch configuration bench.py
 times (every update of the cycle emitted by one pack_batch call with learned
 counts and digests).  The oracle computes the whole plan; outputs are compared
-on every window's digest of the cycle (the SHA-256 of its whole record, so
-every output byte), sampled windows' contents, whole sampled batches
+on every window's digest of the cycle (the SHA-256 of its whole record, or
+with chunked digests of its chunks' digests, so every output byte), sampled windows' contents, whole sampled batches
 (fingerprints) and every learned count, and checked on the GPU for properties
 that hold everywhere (padding at the end, position ids, masks agreeing with the
 learned counts).  The full-cycle workload is also re-derived at emulated rank
@@ -39,6 +39,8 @@ def _setup(name):
             c = c.replace(segment=r.integers(0, 8, size=c.n_docs).astype(np.uint16), n_segments=8)
         if mode == "heldout":
             c = c.replace(updates_per_cycle=0)  # the 1-5 % held out cannot supply 200 updates
+        if mode == "chunked":  # window digests over 4,096-byte chunks of each record
+            c = c.replace(digest_chunked=True)
         say("oracle plan", name, c.n_docs, "docs", c.n_tokens, "tokens")
         op = oracle.Plan(c)
         oi = op.cycle(0)
@@ -58,10 +60,16 @@ def _setup(name):
 # random-pretrain with each cycle's windows read in a random order,
 # cum-pretrain with per-update counts from the cycle's cumulative quotas,
 # lanes-pretrain with 8 lanes, arrivals-pretrain with its documents labelled
-# with 8 arrivals.
+# with 8 arrivals, chunked-pretrain and chunked-long with chunked window digests.
 FULL = [("tiny", None), ("pretrain", None), ("sft", None), ("long", None), ("full", None),
         ("wrap-pretrain", None), ("heldout-pretrain", None), ("random-pretrain", None), ("cum-pretrain", None),
-        ("lanes-pretrain", None), ("arrivals-pretrain", None)]
+        ("lanes-pretrain", None), ("arrivals-pretrain", None), ("chunked-pretrain", None), ("chunked-long", None)]
+
+
+def _window_digest(c, tok, pos, dc, mask):
+    if c.digest_chunked:
+        return oracle.window_digests_chunked(tok, pos, dc, mask).tobytes()
+    return oracle.window_digest(tok, pos, dc, mask)
 
 
 @pytest.mark.parametrize("name,cap", FULL)
@@ -118,7 +126,7 @@ def test_full_size_parity(name, cap):
             assert np.array_equal(g["pos"][i, j].cpu().numpy(), pos)
             assert np.array_equal(g["doc"][i, j].cpu().numpy(), dc)
             assert np.array_equal(g["mask"][i, j].cpu().numpy(), mask)
-            assert g["digests"][i, j].cpu().numpy().tobytes() == oracle.window_digest(tok, pos, dc, mask)
+            assert g["digests"][i, j].cpu().numpy().tobytes() == _window_digest(c, tok, pos, dc, mask)
         # whole sampled batches: every window digest and the batch fingerprint
         for i in sorted({0, cnt - 1}):
             o = op.batch(s0 + i, 1)
