@@ -290,13 +290,15 @@ size_t carve(pack_ctx& c, char* base) {
     p.val[0] = k.take<uint32_t>(D);
     p.val[1] = k.take<uint32_t>(D);
     const uint64_t WR = p.read_random ? P : 0;  // cycle windows ≤ windows ≤ pieces
-    p.hist = k.take<uint32_t>(dp::sort_hist_words(D > WR ? D : WR, G > S ? G : S));
     {  // scans: kept flags (D), the sorts' bucket counts, lengths and pieces (≤ D)
         const uint64_t n_max = std::max<uint64_t>(D + 1, (D > WR ? D : WR) / 2 + (G > S ? G : S) + 1);
         c.scan_words = dp::scan_ws_bytes(n_max) / 4;
         c.scan_base = k.take<uint32_t>(c.scan_words);
         p.scan = dp::scan_ws_at(c.scan_base, n_max, p.err, &c.scan_epoch);
     }
+    // right after the scan's words: build_plan zeroes both (and the padding
+    // between) with one fill, the sort's counts for the compaction to count into
+    p.hist = k.take<uint32_t>(dp::sort_hist_words(D > WR ? D : WR, G > S ? G : S));
     p.group_start = k.take<uint32_t>(G + 1);
     p.gpre = k.take<uint64_t>(D + 1);
     p.order = k.take<uint32_t>(D);
@@ -590,7 +592,10 @@ void build_plan(pack_ctx& c) {
 
     // validation first: no kernel reads the corpus through unchecked offsets
     c.timer.begin(PACK_PHASE_VALIDATE, st);
-    dp::launch_zero_u32(c.scan_base, c.scan_words, st);  // no tile ticket taken, no status published
+    // no tile ticket taken, no status published; the plan sort's group and
+    // bucket counts zeroed (they lie right after the scan's words)
+    dp::launch_zero_u32(c.scan_base, static_cast<uint64_t>(p.hist - c.scan_base) + dp::sort_count_words(p.n_docs, p.G),
+                        st);
     c.scan_epoch = 0;
     if (c.lanes > 1) {  // documents to streams (source, lane); the validation then checks stream ids
         dp::launch_lane_source(c.cfg.doc_source, p.n_docs, c.S_real, c.lanes, c.lane_source, st);

@@ -354,10 +354,13 @@ __device__ inline uint32_t bswap32(uint32_t x) { return __builtin_bswap32(x); }
 void launch_validate(const Plan& p, uint64_t* S, uint32_t* first, hipStream_t st);  // also zeroes S, fills first
 void launch_hash(const Plan& p, uint64_t* S, uint32_t* first, hipStream_t st);
 uint64_t hash_tile_count(uint64_t n_tokens);
-void launch_keep_scan(Plan& p, hipStream_t st);       // kept_pos + compaction into val[0], keys
+void launch_keep_scan(Plan& p, hipStream_t st);       // kept_pos + compaction into val[0], keys, group counts
 void launch_sort(Plan& p, hipStream_t st);            // by (group, key64, d); sets sort_buf
+// counted: the workspace's first sort_count_words(n, G) words were zeroed and
+// its first G hold each group's element count (else the sort does both)
 uint32_t sort_pairs(uint64_t* const key[2], uint32_t* const val[2], const uint32_t* group, uint64_t n, uint32_t G,
-                    uint32_t* hist_ws, const ScanWs& scan, uint32_t test_opts, hipStream_t st);
+                    uint32_t* hist_ws, const ScanWs& scan, uint32_t test_opts, bool counted, hipStream_t st);
+uint64_t sort_count_words(uint64_t n, uint64_t G);  // group and bucket counts of a sort of n pairs
 void launch_read_order(Plan& p, uint32_t cycle, uint64_t total, hipStream_t st);  // perm of each source's cycle windows
 void launch_merge(Plan& p, hipStream_t st);           // group_start, gpre, order, src_doc_start
 void launch_piece_count(Plan& p, hipStream_t st);     // piece_start, opre
