@@ -539,10 +539,12 @@ __device__ __forceinline__ void mask_block(const Plan& p, ECursor& c, uint32_t t
     }
 }
 
-__device__ __forceinline__ void compress_le(uint32_t H[8], uint32_t (&W)[16]) {
+// Compresses the block from a byte-swapped copy, so W stays as stored.
+__device__ __forceinline__ void compress_copy(uint32_t H[8], const uint32_t (&W)[16]) {
+    uint32_t B[16];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) W[e] = bswap32(W[e]);
-    sha256_compress(H, W);
+    for (int e = 0; e < 16; ++e) B[e] = bswap32(W[e]);
+    sha256_compress(H, B);
 }
 
 __global__ __launch_bounds__(64 * GWAVES) __attribute__((amdgpu_waves_per_eu(3)))
@@ -555,7 +557,7 @@ void k_emit_digest(Plan p, EmitArgs a, uint64_t n_windows) {
     uint32_t i_, jj_, per_;
     const uint64_t gw = out_window(p, a, w, &i_, &jj_, &per_);
     const uint32_t q0 = p.win_first[gw], q1 = p.win_first[gw + 1], real = p.win_real[gw];
-    const uint32_t T = p.T;
+    const uint32_t T = p.T;  // a multiple of 64 here: each array is a whole number of 128-byte lines
     if (q1 <= q0 || real > T) {  // every window holds a piece and at most T positions (else a library bug)
         atomicOr(p.err_batch, ERR_INTERNAL);
         return;
@@ -563,60 +565,77 @@ void k_emit_digest(Plan p, EmitArgs a, uint64_t n_windows) {
     uint32_t H[8];
     sha256_init(H);
     ECursor c;
-    // A block is half of a 128-byte line of its array: an even block's words
-    // wait in P and are stored with the next block's, eight 16-byte stores in a
-    // row, so no line is left half-written in L2 for a whole compression (only
-    // a last mask block of an odd count goes out alone).
-    uint32_t P[16];
-    auto finish = [&](uint32_t (&W)[16], uint8_t* dst, uint32_t k, uint32_t n_arr) {
-        if ((k & 1) == 0 && k + 1 < n_arr) {  // first half of a line: wait for the second
-#pragma unroll
-            for (int e = 0; e < 16; ++e) P[e] = W[e];
-        } else if (valid) {
-            if (k & 1) store16(dst - 64, P);
-            store16(dst, W);
+    // Blocks go in pairs, the two halves of a 128-byte line of their array:
+    // the pair is stored with eight 16-byte stores in a row (no line left
+    // half-written in L2 for a whole compression), each block compressed from
+    // a byte-swapped copy; every loop takes two blocks per turn, so no block's
+    // words are copied to other registers at a turn's end.
+    auto store_pair = [&](uint8_t* dst, const uint32_t (&W0)[16], const uint32_t (&W1)[16]) {
+        if (valid) {
+            store16(dst, W0);
+            store16(dst + 64, W1);
         }
-        compress_le(H, W);
     };
-    const uint32_t nb = T / 16;
-    // token ids: the next block's runs are loaded before the current one is compressed
-    uint32_t va[16], vb[16], bw;
+    const uint32_t nb = T / 16;  // blocks of tok, pos and doc: a multiple of 4
+    // token ids: two prefetch buffers in turn, each block's runs loaded before the previous block is compressed
+    uint32_t va0[16], vb0[16], bw0, va1[16], vb1[16], bw1;
     c.restart(p, q0, q1, real);
-    issue_tokens(p, c, 0, q1, real, va, vb, bw);
+    issue_tokens(p, c, 0, q1, real, va0, vb0, bw0);
     uint8_t* const tok = reinterpret_cast<uint8_t*>(a.tok + w * T);
 #pragma unroll 1
-    for (uint32_t k = 0; k < nb; ++k) {
-        uint32_t W[16];
+    for (uint32_t k = 0; k < nb; k += 2) {
+        uint32_t W0[16], W1[16];
 #pragma unroll
-        for (uint32_t e = 0; e < 16; ++e) W[e] = 16 * k + e >= bw ? vb[e] : va[e];
-        if (k + 1 < nb) issue_tokens(p, c, 16 * (k + 1), q1, real, va, vb, bw);
-        finish(W, tok + 64 * k, k, nb);
+        for (uint32_t e = 0; e < 16; ++e) W0[e] = 16 * k + e >= bw0 ? vb0[e] : va0[e];
+        issue_tokens(p, c, 16 * (k + 1), q1, real, va1, vb1, bw1);
+        compress_copy(H, W0);
+#pragma unroll
+        for (uint32_t e = 0; e < 16; ++e) W1[e] = 16 * (k + 1) + e >= bw1 ? vb1[e] : va1[e];
+        if (k + 2 < nb) issue_tokens(p, c, 16 * (k + 2), q1, real, va0, vb0, bw0);
+        store_pair(tok + 64 * k, W0, W1);
+        compress_copy(H, W1);
     }
     // position ids, document ids
     uint8_t* const pos = reinterpret_cast<uint8_t*>(a.pos + w * T);
     c.restart(p, q0, q1, real);
 #pragma unroll 1
-    for (uint32_t k = 0; k < nb; ++k) {
-        uint32_t W[16];
-        id_block<1>(p, c, 16 * k, q1, real, W);
-        finish(W, pos + 64 * k, k, nb);
+    for (uint32_t k = 0; k < nb; k += 2) {
+        uint32_t W0[16], W1[16];
+        id_block<1>(p, c, 16 * k, q1, real, W0);
+        compress_copy(H, W0);
+        id_block<1>(p, c, 16 * (k + 1), q1, real, W1);
+        store_pair(pos + 64 * k, W0, W1);
+        compress_copy(H, W1);
     }
     uint8_t* const doc = reinterpret_cast<uint8_t*>(a.doc + w * T);
     c.restart(p, q0, q1, real);
 #pragma unroll 1
-    for (uint32_t k = 0; k < nb; ++k) {
-        uint32_t W[16];
-        id_block<2>(p, c, 16 * k, q1, real, W);
-        finish(W, doc + 64 * k, k, nb);
+    for (uint32_t k = 0; k < nb; k += 2) {
+        uint32_t W0[16], W1[16];
+        id_block<2>(p, c, 16 * k, q1, real, W0);
+        compress_copy(H, W0);
+        id_block<2>(p, c, 16 * (k + 1), q1, real, W1);
+        store_pair(doc + 64 * k, W0, W1);
+        compress_copy(H, W1);
     }
-    // loss mask, 64 positions per block
+    // loss mask, 64 positions per block; with an odd count the last block goes out alone
     uint8_t* const mask = a.mask + w * T;
+    const uint32_t nm = T / 64;
     c.restart(p, q0, q1, real);
 #pragma unroll 1
-    for (uint32_t k = 0; k < T / 64; ++k) {
+    for (uint32_t k = 0; k + 1 < nm; k += 2) {
+        uint32_t W0[16], W1[16];
+        mask_block(p, c, 64 * k, q1, real, W0);
+        compress_copy(H, W0);
+        mask_block(p, c, 64 * (k + 1), q1, real, W1);
+        store_pair(mask + 64 * k, W0, W1);
+        compress_copy(H, W1);
+    }
+    if (nm & 1) {
         uint32_t W[16];
-        mask_block(p, c, 64 * k, q1, real, W);
-        finish(W, mask + 64 * k, k, T / 64);
+        mask_block(p, c, 64 * (nm - 1), q1, real, W);
+        if (valid) store16(mask + 64 * (nm - 1), W);
+        compress_copy(H, W);
     }
     // 13·T bytes is a multiple of 64: one padding block
     uint32_t W[16];
